@@ -1,0 +1,458 @@
+// C ABI of the tkv library (include/tkv.h): handle lifetime, prefill,
+// append, decode attention, statistics and inspection hooks.  Reassignment
+// lives in reassign.cpp.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "handle.hpp"
+#include "host_util.hpp"
+
+using namespace tkvd;
+
+static thread_local std::string g_create_err;
+
+int tkv_fail(tkv* t, int code, const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (t)
+    t->err = buf;
+  else
+    g_create_err = buf;
+  return code;
+}
+
+static int device_alloc(tkv* t, void** p, size_t bytes) {
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    return tkv_fail(t, TKV_ENOMEM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+  }
+  t->device_allocs.push_back(*p);
+  return TKV_OK;
+}
+
+static int host_alloc(tkv* t, void** p, size_t bytes) {
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipHostMalloc(p, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    return tkv_fail(t, TKV_ENOMEM, "hipHostMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+  }
+  t->host_allocs.push_back(*p);
+  return TKV_OK;
+}
+
+static void release(tkv* t) {
+  for (void* p : t->device_allocs) (void)hipFree(p);
+  for (void* p : t->host_allocs) (void)hipHostFree(p);
+  for (hipEvent_t e : t->ev_free) (void)hipEventDestroy(e);
+  for (auto& pr : t->ev_pending) {
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  t->device_allocs.clear();
+  t->host_allocs.clear();
+}
+
+extern "C" const char* tkv_last_error(const tkv_t* t) { return t ? t->err.c_str() : g_create_err.c_str(); }
+
+extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_ratio, double evict_ratio,
+                          tkv_protect protect, const tkv_options* opts, tkv_t** out) {
+  if (!out) return tkv_fail(nullptr, TKV_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!shape) return tkv_fail(nullptr, TKV_EINVAL, "shape is NULL");
+  const tkv_shape& s = *shape;
+  if (s.layers < 1 || s.q_heads < 1 || s.kv_heads < 1 || s.batch < 1 || s.max_tokens < 1)
+    return tkv_fail(nullptr, TKV_EINVAL, "shape fields must be positive");
+  if (s.q_heads % s.kv_heads) return tkv_fail(nullptr, TKV_EINVAL, "q_heads must be a multiple of kv_heads");
+  const int group = s.q_heads / s.kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 5 && group != 8)
+    return tkv_fail(nullptr, TKV_EINVAL, "q_heads/kv_heads = %d not supported (1, 2, 4, 5, 8)", group);
+  if (s.head_dim != 64 && s.head_dim != 128) return tkv_fail(nullptr, TKV_EINVAL, "head_dim must be 64 or 128");
+  if (s.batch > kMaxBatch) return tkv_fail(nullptr, TKV_EINVAL, "batch > %d", kMaxBatch);
+  if (s.q_heads > kMaxQHeads) return tkv_fail(nullptr, TKV_EINVAL, "q_heads > %d", kMaxQHeads);
+  if (s.max_tokens > (1 << 30)) return tkv_fail(nullptr, TKV_EINVAL, "max_tokens too large");
+  if (s.dtype != TKV_BF16 && s.dtype != TKV_F32) return tkv_fail(nullptr, TKV_EINVAL, "unknown dtype");
+  if (delta <= 0) return tkv_fail(nullptr, TKV_EINVAL, "delta must be > 0");
+  auto ratio_ok = [](double r) { return std::isfinite(r) && r >= 0.0 && r <= 1.0; };
+  if (!ratio_ok(hbm_ratio) || !ratio_ok(evict_ratio))
+    return tkv_fail(nullptr, TKV_EINVAL, "hbm_ratio and evict_ratio must be in [0, 1]");
+  if (protect.prompt < 0 || protect.sinks < 0 || protect.recent < 0)
+    return tkv_fail(nullptr, TKV_EINVAL, "protect fields must be >= 0");
+  tkv_options o{};
+  if (opts) o = *opts;
+  if (!ratio_ok(o.t2_ratio)) return tkv_fail(nullptr, TKV_EINVAL, "t2_ratio must be in [0, 1]");
+  if (o.chunk == 0) o.chunk = 256;
+  if (o.chunk != 128 && o.chunk != 256 && o.chunk != 512)
+    return tkv_fail(nullptr, TKV_EINVAL, "chunk must be 128, 256 or 512");
+  if (o.staging_layers < 0 || o.staging_layers == 1)
+    return tkv_fail(nullptr, TKV_EINVAL, "staging_layers must be 0 or >= 2");
+  const bool resident = o.staging_layers == 0 || o.staging_layers >= s.layers;
+  if (!resident) return tkv_fail(nullptr, TKV_EINVAL, "stream staging (staging_layers < layers) is not available yet");
+  if (o.t2_ratio > 0) return tkv_fail(nullptr, TKV_EINVAL, "the 8-bit host tier is not available yet");
+
+  tkv* t = new tkv();
+  t->L = s.layers;
+  t->Hq = s.q_heads;
+  t->Hkv = s.kv_heads;
+  t->D = s.head_dim;
+  t->B = s.batch;
+  t->nmax = s.max_tokens;
+  t->dtype = s.dtype;
+  t->esz = s.dtype == TKV_BF16 ? 2 : 4;
+  t->group = group;
+  t->delta = delta;
+  t->chunk = o.chunk;
+  t->resident = resident;
+  t->S = resident ? s.layers : o.staging_layers;
+  t->hbm = hbm_ratio;
+  t->evict = evict_ratio;
+  t->t2 = o.t2_ratio;
+  t->prompt = protect.prompt;
+  t->sinks = protect.sinks;
+  t->recent = protect.recent;
+  t->flags = o.flags;
+  t->row_elems = (int64_t)s.kv_heads * s.head_dim;
+  t->row_bytes = t->row_elems * t->esz;
+
+  const int64_t nmax = s.max_tokens;
+  const int64_t pmax = std::min<int64_t>(nmax, (int64_t)std::max(protect.prompt, protect.sinks) + protect.recent);
+  const int64_t h_at_max = floor_ratio(hbm_ratio, nmax);
+  t->cap0 = (int)std::min<int64_t>(nmax, std::max(pmax, h_at_max) + delta + 1);
+  t->cap1 = (int)std::max<int64_t>(1, std::min<int64_t>(nmax, nmax - h_at_max + 1));
+  t->cap2 = o.t2_ratio > 0 ? (int)std::min<int64_t>(nmax, floor_ratio(o.t2_ratio, nmax) + 1) : 0;
+  t->capS = t->cap1 + t->cap2;
+  t->max_chunks = (int)((nmax + t->chunk - 1) / t->chunk);
+
+  const size_t L = t->L, B = t->B, Hq = t->Hq;
+  int rc = TKV_OK;
+  auto dev = [&](void** p, size_t bytes) {
+    if (rc == TKV_OK) rc = device_alloc(t, p, bytes);
+  };
+  dev(&t->pool_k, L * B * t->cap0 * t->row_bytes);
+  dev(&t->pool_v, L * B * t->cap0 * t->row_bytes);
+  dev(&t->stage_k, (size_t)t->S * B * t->capS * t->row_bytes);
+  dev(&t->stage_v, (size_t)t->S * B * t->capS * t->row_bytes);
+  dev((void**)&t->live_loc, B * nmax * 4);
+  dev((void**)&t->live_pos, B * nmax * 4);
+  dev((void**)&t->tier, B * nmax);
+  dev((void**)&t->loc, B * nmax * 4);
+  dev((void**)&t->s, B * nmax * 4);
+  dev((void**)&t->logits, L * B * Hq * nmax * 4);
+  dev((void**)&t->part_ml, L * B * Hq * t->max_chunks * 2 * 4);
+  dev((void**)&t->part_o, L * B * Hq * t->max_chunks * t->D * 4);
+  dev((void**)&t->layer_score, L * B * nmax * 4);
+  if (rc == TKV_OK) rc = host_alloc(t, &t->arena1_k, L * B * t->cap1 * t->row_bytes);
+  if (rc == TKV_OK) rc = host_alloc(t, &t->arena1_v, L * B * t->cap1 * t->row_bytes);
+  if (rc == TKV_OK) {
+    hipError_t e = hipSuccess;
+    if (e == hipSuccess) e = hipMemset(t->tier, kUnused, B * nmax);
+    if (e == hipSuccess) e = hipMemset(t->loc, 0xFF, B * nmax * 4);
+    if (e == hipSuccess) e = hipMemset(t->s, 0, B * nmax * 4);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) rc = tkv_fail(t, TKV_EHIP, "initialising device state: %s", hipGetErrorString(e));
+  }
+  if (rc != TKV_OK) {
+    g_create_err = t->err;
+    release(t);
+    delete t;
+    return rc;
+  }
+  t->nlive.assign(B, 0);
+  t->free0.resize(B);
+  for (auto& f : t->free0) {
+    f.resize(t->cap0);
+    for (int i = 0; i < t->cap0; ++i) f[i] = t->cap0 - 1 - i;  // back() = lowest free slot
+  }
+  t->h_tier.assign(B * nmax, kUnused);
+  t->h_loc.assign(B * nmax, kNoLoc);
+  t->t1_owner.resize(B);
+  t->last_promote.assign(B * nmax, tkv_delta{});
+  t->last_demote.assign(B * nmax, tkv_delta{});
+  t->last_counts.assign(B * 2, 0);
+  t->st.hbm_bytes = (int64_t)(2 * L * B * t->cap0 + 2 * (size_t)t->S * B * t->capS) * t->row_bytes;
+  t->st.host_bytes = (int64_t)(2 * L * B * t->cap1) * t->row_bytes;
+  t->st.full_cache_bytes = (int64_t)(2 * L * B * nmax) * t->row_bytes;
+  *out = t;
+  return TKV_OK;
+}
+
+extern "C" int tkv_destroy(tkv_t* t) {
+  if (!t) return TKV_OK;
+  (void)hipDeviceSynchronize();
+  release(t);
+  delete t;
+  return TKV_OK;
+}
+
+extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tokens, tkv_stream_t stream) {
+  if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  if (t->state != TkvState::Empty || t->n != 0) return tkv_fail(t, TKV_ESTATE, "prefill needs an empty cache");
+  if (!k || !v) return tkv_fail(t, TKV_EINVAL, "k/v is NULL");
+  if (n_tokens < 1) return tkv_fail(t, TKV_EINVAL, "n_tokens must be >= 1");
+  if (n_tokens > t->nmax) return tkv_fail(t, TKV_ECAPACITY, "n_tokens %d > max_tokens %d", n_tokens, t->nmax);
+  hipStream_t st = (hipStream_t)stream;
+  const int n0 = n_tokens;
+
+  // first placement: every score is 0, so candidates rank by position
+  std::vector<uint8_t> first = first_placement(*t, n0);
+  const int nt0 = (int)std::count(first.begin(), first.end(), (uint8_t)TKV_T0);
+  const int nt1 = n0 - nt0;
+  if (nt0 > t->cap0 || nt1 > t->cap1)
+    return tkv_fail(t, TKV_ECAPACITY, "first placement does not fit (T0 %d/%d, T1 %d/%d)", nt0, t->cap0, nt1, t->cap1);
+
+  std::vector<uint32_t> codes((size_t)t->B * n0);
+  for (int b = 0; b < t->B; ++b) {
+    auto& own = t->t1_owner[b];
+    own.clear();
+    for (int p = 0; p < n0; ++p) {
+      uint32_t code;
+      if (first[p] == TKV_T0) {
+        code = (uint32_t)t->free0[b].back();
+        t->free0[b].pop_back();
+      } else {
+        code = (uint32_t)(t->cap0 + own.size());
+        own.push_back(p);
+      }
+      codes[(size_t)b * n0 + p] = code;
+      t->h_tier[(size_t)b * t->nmax + p] = first[p];
+      t->h_loc[(size_t)b * t->nmax + p] = code;
+    }
+    t->nlive[b] = n0;
+  }
+
+  void* d_codes = nullptr;
+  HIP_TRY(t, hipMallocAsync(&d_codes, codes.size() * 4, st));
+  HIP_TRY(t, hipMemcpyAsync(d_codes, codes.data(), codes.size() * 4, hipMemcpyHostToDevice, st));
+  PlaceArgs pa{};
+  pa.rows = t->rowspace();
+  pa.k = k;
+  pa.v = v;
+  pa.codes = (const uint32_t*)d_codes;
+  pa.row_bytes = t->row_bytes;
+  pa.batch = t->B;
+  pa.n_tokens = n0;
+  pa.elem_bytes = t->esz;
+  HIP_TRY(t, launch_place_rows(pa, t->L, st));
+  // T1 rows also go to their home in pinned host memory
+  if (nt1 > 0) {
+    const size_t width = (size_t)nt1 * t->row_bytes;
+    for (int which = 0; which < 2; ++which) {
+      HIP_TRY(t, hipMemcpy2DAsync(which ? t->arena1_v : t->arena1_k, (size_t)t->cap1 * t->row_bytes,
+                                  which ? t->stage_v : t->stage_k, (size_t)t->capS * t->row_bytes, width,
+                                  (size_t)t->L * t->B, hipMemcpyDeviceToHost, st));
+    }
+    t->st.d2h_bytes += 2 * (int64_t)width * t->L * t->B;
+  }
+  // per-position tables and the live list (every prefilled position is live)
+  std::vector<int32_t> pos((size_t)t->B * n0);
+  for (int b = 0; b < t->B; ++b)
+    for (int p = 0; p < n0; ++p) pos[(size_t)b * n0 + p] = p;
+  for (int b = 0; b < t->B; ++b) {
+    const size_t off = (size_t)b * t->nmax;
+    HIP_TRY(t, hipMemcpyAsync(t->tier + off, &t->h_tier[off], n0, hipMemcpyHostToDevice, st));
+    HIP_TRY(t, hipMemcpyAsync(t->loc + off, &t->h_loc[off], (size_t)n0 * 4, hipMemcpyHostToDevice, st));
+    HIP_TRY(t, hipMemcpyAsync(t->live_loc + off, &t->h_loc[off], (size_t)n0 * 4, hipMemcpyHostToDevice, st));
+    HIP_TRY(t, hipMemcpyAsync(t->live_pos + off, &pos[(size_t)b * n0], (size_t)n0 * 4, hipMemcpyHostToDevice, st));
+  }
+  HIP_TRY(t, hipFreeAsync(d_codes, st));
+  HIP_TRY(t, hipStreamSynchronize(st));
+  t->n = n0;
+  t->state = TkvState::Ready;
+  return TKV_OK;
+}
+
+extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream) {
+  if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "previous step has layers left");
+  if (!k || !v) return tkv_fail(t, TKV_EINVAL, "k/v is NULL");
+  if (t->n >= t->nmax) return tkv_fail(t, TKV_ECAPACITY, "max_tokens (%d) reached", t->nmax);
+  for (int b = 0; b < t->B; ++b)
+    if (t->free0[b].empty()) return tkv_fail(t, TKV_ECAPACITY, "T0 pool full (sequence %d): reassign first", b);
+  AppendArgs a{};
+  a.rows = t->rowspace();
+  a.k = k;
+  a.v = v;
+  a.live_loc = t->live_loc;
+  a.live_pos = t->live_pos;
+  a.tier = t->tier;
+  a.loc = t->loc;
+  a.s = t->s;
+  a.layers = t->L;
+  a.batch = t->B;
+  a.kv_heads = t->Hkv;
+  a.head_dim = t->D;
+  a.elem_bytes = t->esz;
+  a.nmax = t->nmax;
+  a.pos = t->n;
+  for (int b = 0; b < t->B; ++b) {
+    a.slot[b] = t->free0[b].back();
+    a.nlive[b] = t->nlive[b];
+  }
+  HIP_TRY(t, launch_append(a, (hipStream_t)stream));
+  for (int b = 0; b < t->B; ++b) {
+    t->free0[b].pop_back();
+    const size_t off = (size_t)b * t->nmax + t->n;
+    t->h_tier[off] = TKV_T0;
+    t->h_loc[off] = (uint32_t)a.slot[b];
+    t->nlive[b] += 1;
+  }
+  t->n += 1;
+  t->layers_done = 0;
+  t->state = TkvState::InStep;
+  return TKV_OK;
+}
+
+static int record_event(tkv* t, hipEvent_t* e, hipStream_t st) {
+  if (t->ev_free.empty()) {
+    hipEvent_t x;
+    HIP_TRY(t, hipEventCreate(&x));
+    t->ev_free.push_back(x);
+  }
+  *e = t->ev_free.back();
+  t->ev_free.pop_back();
+  HIP_TRY(t, hipEventRecord(*e, st));
+  return TKV_OK;
+}
+
+static int drain_events(tkv* t) {
+  for (auto& pr : t->ev_pending) {
+    HIP_TRY(t, hipEventSynchronize(pr.second));
+    float ms = 0.f;
+    HIP_TRY(t, hipEventElapsedTime(&ms, pr.first, pr.second));
+    t->st.attn_kernel_ms += ms;
+    t->st.attn_kernel_launches += 1;
+    t->ev_free.push_back(pr.first);
+    t->ev_free.push_back(pr.second);
+  }
+  t->ev_pending.clear();
+  return TKV_OK;
+}
+
+extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
+                               tkv_stream_t stream) {
+  if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  if (t->state != TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "no step in progress (append first)");
+  if (!q || !out) return tkv_fail(t, TKV_EINVAL, "q/out is NULL");
+  if (layer_begin != t->layers_done)
+    return tkv_fail(t, TKV_ESTATE, "layer groups must come in order: expected layer %d", t->layers_done);
+  if (layer_count < 1 || layer_begin + layer_count > t->L) return tkv_fail(t, TKV_EINVAL, "bad layer range");
+  hipStream_t st = (hipStream_t)stream;
+  int max_live = 0;
+  for (int b = 0; b < t->B; ++b) max_live = std::max(max_live, t->nlive[b]);
+
+  AttnArgs a{};
+  a.rows = t->rowspace();
+  a.live_loc = t->live_loc;
+  a.q = q;
+  a.logits = t->logits;
+  a.part_ml = t->part_ml;
+  a.part_o = t->part_o;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)t->D));
+  a.layer_begin = layer_begin;
+  a.batch = t->B;
+  a.q_heads = t->Hq;
+  a.kv_heads = t->Hkv;
+  a.nmax = t->nmax;
+  a.max_chunks = t->max_chunks;
+  for (int b = 0; b < t->B; ++b) a.nlive[b] = t->nlive[b];
+  const int chunks_now = (max_live + t->chunk - 1) / t->chunk;
+  const bool timed = (t->flags & TKV_FLAG_TIME_KERNELS) != 0;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (timed) {
+    int rc = record_event(t, &e0, st);
+    if (rc) return rc;
+  }
+  if (chunks_now > 0) HIP_TRY(t, launch_attn(a, t->dtype, t->D, t->group, t->chunk, layer_count, chunks_now, st));
+  if (timed) {
+    int rc = record_event(t, &e1, st);
+    if (rc) return rc;
+    t->ev_pending.emplace_back(e0, e1);
+  }
+
+  FinalizeArgs f{};
+  f.logits = t->logits;
+  f.part_ml = t->part_ml;
+  f.part_o = t->part_o;
+  f.out = out;
+  f.layer_score = t->layer_score;
+  f.layer_begin = layer_begin;
+  f.batch = t->B;
+  f.q_heads = t->Hq;
+  f.nmax = t->nmax;
+  f.max_chunks = t->max_chunks;
+  f.chunk = t->chunk;
+  for (int b = 0; b < t->B; ++b) f.nlive[b] = t->nlive[b];
+  const int tiles_now = (max_live + 255) / 256;
+  if (tiles_now > 0) HIP_TRY(t, launch_finalize(f, t->D, layer_count, tiles_now, st));
+
+  t->layers_done += layer_count;
+  if (t->layers_done == t->L) {
+    ScoreArgs sa{};
+    sa.layer_score = t->layer_score;
+    sa.live_pos = t->live_pos;
+    sa.s = t->s;
+    sa.inv_lh = (float)(1.0 / ((double)t->L * t->Hq));
+    sa.layers = t->L;
+    sa.batch = t->B;
+    sa.nmax = t->nmax;
+    for (int b = 0; b < t->B; ++b) sa.nlive[b] = t->nlive[b];
+    if (tiles_now > 0) HIP_TRY(t, launch_score(sa, tiles_now, st));
+    t->step += 1;
+    t->state = TkvState::Ready;
+  }
+  return TKV_OK;
+}
+
+extern "C" int tkv_stats(tkv_t* t, tkv_stats_t* out) {
+  if (!t || !out) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  int rc = drain_events(t);
+  if (rc) return rc;
+  t->st.step = t->step;
+  t->st.n_tokens = t->n;
+  for (int i = 0; i < 4; ++i) t->st.tier_count[i] = 0;
+  for (int b = 0; b < t->B; ++b)
+    for (int p = 0; p < t->n; ++p) {
+      const uint8_t x = t->h_tier[(size_t)b * t->nmax + p];
+      if (x < 4) t->st.tier_count[x] += 1;
+    }
+  *out = t->st;
+  return TKV_OK;
+}
+
+extern "C" int tkv_read_scores(tkv_t* t, float* scores, tkv_stream_t stream) {
+  if (!t || !scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  HIP_TRY(t, hipMemcpyAsync(scores, t->s, (size_t)t->B * t->nmax * 4, hipMemcpyDeviceToHost, (hipStream_t)stream));
+  HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
+  return TKV_OK;
+}
+
+extern "C" int tkv_write_scores(tkv_t* t, const float* scores, tkv_stream_t stream) {
+  if (!t || !scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "step in progress");
+  HIP_TRY(t, hipMemcpyAsync(t->s, scores, (size_t)t->B * t->nmax * 4, hipMemcpyHostToDevice, (hipStream_t)stream));
+  HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
+  return TKV_OK;
+}
+
+extern "C" int tkv_read_tiers(tkv_t* t, uint8_t* tiers, tkv_stream_t stream) {
+  if (!t || !tiers) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  HIP_TRY(t, hipMemcpyAsync(tiers, t->tier, (size_t)t->B * t->nmax, hipMemcpyDeviceToHost, (hipStream_t)stream));
+  HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
+  return TKV_OK;
+}
+
+extern "C" int tkv_read_deltas(tkv_t* t, tkv_delta* promote, tkv_delta* demote, int32_t* counts) {
+  if (!t || !promote || !demote || !counts) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  std::memcpy(promote, t->last_promote.data(), t->last_promote.size() * sizeof(tkv_delta));
+  std::memcpy(demote, t->last_demote.data(), t->last_demote.size() * sizeof(tkv_delta));
+  std::memcpy(counts, t->last_counts.data(), t->last_counts.size() * sizeof(int32_t));
+  return TKV_OK;
+}

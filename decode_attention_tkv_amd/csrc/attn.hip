@@ -1,0 +1,404 @@
+// Decode-step kernels: append, split-K attention over the tiered cache,
+// chunk merge + per-layer score sums, and the Eq. 1 score update.
+//
+// "Not All Thoughts Need HBM" (gist.science technical summary):
+//   Method §3 -- every live row (T0 pool or T1/T2 staging) contributes
+//   exactly the same terms; rows are walked in logical-position order through
+//   a location table, so the arithmetic never depends on where a row sits.
+//   Method §2, Eq. 1 -- s_i += (1/|L|) sum_l (1/H) sum_h alpha_{l,h}[i].
+//
+// Work decomposition (gfx950, wave64):
+//   k_attn_chunk  one work-group (4 waves) per (chunk of CHUNK live rows,
+//                 kv head, layer x sequence).  A K or V row of head_dim
+//                 elements is read as 16-byte pieces by LPR consecutive lanes,
+//                 so a wave covers 64/LPR rows per load instruction.  Each row
+//                 is loaded once for all G query heads of its kv head.  The
+//                 dot products reduce over the LPR lanes with DPP butterflies
+//                 (quad_perm, row_half_mirror, row_mirror), the chunk max and
+//                 sums with DPP + LDS in a fixed order.  Phase 1 writes the
+//                 log2-scaled logits; phase 2 forms p = 2^(z - m_chunk) once
+//                 per (head, row) in LDS and accumulates p * V.
+//   k_finalize    one work-group per (256 live rows, sequence, layer): merges
+//                 the chunk partials in chunk order into M, 1/sum and out, and
+//                 sums alpha over the layer's heads for its rows.
+//   k_score       one thread per live row: adds the layers' sums (layer
+//                 order) times 1/(L*H) to s.  No atomics anywhere, so every
+//                 result is bitwise reproducible.
+#include "tkv_internal.hpp"
+
+namespace tkvd {
+namespace {
+
+typedef uint16_t bf16_t;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N in 1..64); every lane of a group
+// gets the identical value (each step adds a pair in both orders).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<0xB1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<0x4E>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<0x141>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<0x140>(x));
+  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+template <typename T>
+__device__ __forceinline__ void unpack(const uint4& u, float* f);
+
+template <>
+__device__ __forceinline__ void unpack<bf16_t>(const uint4& u, float* f) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void unpack<float>(const uint4& u, float* f) {
+  f[0] = __uint_as_float(u.x);
+  f[1] = __uint_as_float(u.y);
+  f[2] = __uint_as_float(u.z);
+  f[3] = __uint_as_float(u.w);
+}
+
+// ---------------------------------------------------------------------------
+// Append: copy the new token's K/V rows of every (layer, sequence) into its
+// T0 slot and extend the live list.  grid (layers*batch, 2), block 256.
+__global__ __launch_bounds__(256) void k_append(const AppendArgs a) {
+  const int lb = blockIdx.x;
+  const int b = lb % a.batch;
+  const int l = lb / a.batch;
+  const int which = blockIdx.y;
+  const int64_t row_bytes = (int64_t)a.kv_heads * a.head_dim * a.elem_bytes;
+  const char* src = (const char*)(which ? a.v : a.k) + (int64_t)lb * row_bytes;
+  char* dst = (char*)(which ? a.rows.pool_v : a.rows.pool_k) +
+              ((int64_t)l * a.rows.pool_lstride + (int64_t)b * a.rows.pool_bstride) * a.elem_bytes +
+              (int64_t)a.slot[b] * row_bytes;
+  for (int64_t off = (int64_t)threadIdx.x * 16; off < row_bytes; off += 256 * 16)
+    *reinterpret_cast<uint4*>(dst + off) = load16(src + off);
+  if (l == 0 && which == 0 && threadIdx.x == 0) {
+    const int64_t j = (int64_t)b * a.nmax + a.nlive[b];
+    const int64_t p = (int64_t)b * a.nmax + a.pos;
+    a.live_loc[j] = (uint32_t)a.slot[b];
+    a.live_pos[j] = a.pos;
+    a.tier[p] = 0;
+    a.loc[p] = (uint32_t)a.slot[b];
+    a.s[p] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K attention, pass 1.  grid (chunks, kv_heads, layer_count*batch).
+template <typename T, int D, int G, int CHUNK>
+__global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
+  constexpr int LPR = D * (int)sizeof(T) / 16;  // lanes per row
+  constexpr int EPL = 16 / (int)sizeof(T);      // elements per lane
+  constexpr int RPI = 64 / LPR;                 // rows per wave load
+  constexpr int NW = 4;
+  constexpr int RPW = CHUNK / NW;               // rows per wave
+  constexpr int ITERS = RPW / RPI;
+  constexpr int UB = (G <= 2) ? 8 : 4;
+  constexpr int U = ITERS < UB ? ITERS : UB;    // loads in flight per lane per batch
+  static_assert(RPW % RPI == 0 && ITERS % U == 0, "chunk shape");
+
+  __shared__ float zs[G][CHUNK];
+  __shared__ float red[NW][G];
+  __shared__ float osum[NW][G][D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int part = lane % LPR, rg = lane / LPR;
+  const int c = blockIdx.x, kvh = blockIdx.y;
+  const int b = blockIdx.z % a.batch, ll = blockIdx.z / a.batch;
+  const int l = a.layer_begin + ll;
+  const int nl = a.nlive[b];
+  const int j0 = c * CHUNK;
+  if (j0 >= nl) return;
+  const int nrows = min(CHUNK, nl - j0);
+
+  const int64_t rs = (int64_t)a.kv_heads * D;  // elements between consecutive rows
+  const int64_t poff = (int64_t)l * a.rows.pool_lstride + (int64_t)b * a.rows.pool_bstride +
+                       (int64_t)kvh * D + part * EPL;
+  const int64_t soff = (int64_t)(l % a.rows.stage_slots) * a.rows.stage_lstride +
+                       (int64_t)b * a.rows.stage_bstride + (int64_t)kvh * D + part * EPL;
+  const T* poolK = (const T*)a.rows.pool_k + poff;
+  const T* poolV = (const T*)a.rows.pool_v + poff;
+  const T* stageK = (const T*)a.rows.stage_k + soff;
+  const T* stageV = (const T*)a.rows.stage_v + soff;
+  const uint32_t cap0 = (uint32_t)a.rows.cap0;
+  const uint32_t* locs = a.live_loc + (int64_t)b * a.nmax + j0;
+
+  float qv[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const T* qp = (const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + g) * D + part * EPL;
+    unpack<T>(load16(qp), qv[g]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[g][e] *= a.qscale;
+  }
+
+  // ---- phase 1: logits and the chunk max
+  float mx[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) mx[g] = -INFINITY;
+  for (int it0 = 0; it0 < ITERS; it0 += U) {
+    uint4 kd[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = wave * RPW + (it0 + u) * RPI + rg;
+      kd[u] = make_uint4(0, 0, 0, 0);
+      if (r < nrows) {
+        const uint32_t code = locs[r];
+        const T* p = code < cap0 ? poolK + (int64_t)code * rs : stageK + (int64_t)(code - cap0) * rs;
+        kd[u] = load16(p);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = wave * RPW + (it0 + u) * RPI + rg;
+      float kf[EPL];
+      unpack<T>(kd[u], kf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(qv[g][e], kf[e], acc);
+        const float z = group_sum<LPR>(acc);
+        if (r < nrows) {
+          if (part == 0) zs[g][r] = z;
+          mx[g] = fmaxf(mx[g], z);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float m = mx[g];
+    for (int off = LPR; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) red[wave][g] = m;
+  }
+  __syncthreads();
+  float mc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) mc[g] = fmaxf(fmaxf(red[0][g], red[1][g]), fmaxf(red[2][g], red[3][g]));
+
+  // ---- logits out; p = 2^(z - m) in place; chunk sums
+  float ls[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    ls[g] = 0.f;
+    float* lg = a.logits + (((int64_t)l * a.batch + b) * a.q_heads + kvh * G + g) * a.nmax + j0;
+    for (int r = tid; r < CHUNK; r += 256) {
+      float p = 0.f;
+      if (r < nrows) {
+        const float z = zs[g][r];
+        lg[r] = z;
+        p = exp2f(z - mc[g]);
+      }
+      zs[g][r] = p;
+      ls[g] += p;
+    }
+  }
+  __syncthreads();  // all reads of red[] (maxima) done before it is reused below
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float s = group_sum<64>(ls[g]);
+    if (lane == 0) red[wave][g] = s;
+  }
+
+  // ---- phase 2: o = sum_r p_r * v_r
+  float o[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
+  for (int it0 = 0; it0 < ITERS; it0 += U) {
+    uint4 vd[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = wave * RPW + (it0 + u) * RPI + rg;
+      vd[u] = make_uint4(0, 0, 0, 0);
+      if (r < nrows) {
+        const uint32_t code = locs[r];
+        const T* p = code < cap0 ? poolV + (int64_t)code * rs : stageV + (int64_t)(code - cap0) * rs;
+        vd[u] = load16(p);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = wave * RPW + (it0 + u) * RPI + rg;
+      if (r < nrows) {
+        float vf[EPL];
+        unpack<T>(vd[u], vf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float pg = zs[g][r];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(pg, vf[e], o[g][e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = o[g][e];
+      for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
+      if (rg == 0) osum[wave][g][part * EPL + e] = x;
+    }
+  __syncthreads();
+  const int64_t hbase = ((int64_t)l * a.batch + b) * a.q_heads + kvh * G;
+  for (int t = tid; t < G * D; t += 256) {
+    const int g = t / D, e = t % D;
+    const float x = ((osum[0][g][e] + osum[1][g][e]) + osum[2][g][e]) + osum[3][g][e];
+    a.part_o[((hbase + g) * a.max_chunks + c) * D + e] = x;
+  }
+  if (tid < G) {
+    const float s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    float* ml = a.part_ml + ((hbase + tid) * a.max_chunks + c) * 2;
+    ml[0] = mc[tid];
+    ml[1] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge chunk partials and sum alpha over heads.  grid (tiles, batch,
+// layer_count), block 256; tile t covers live rows [256t, 256t+256).
+template <int D>
+__global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
+  __shared__ float Ms[kMaxQHeads];
+  __shared__ float iLs[kMaxQHeads];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x, b = blockIdx.y, ll = blockIdx.z;
+  const int l = a.layer_begin + ll;
+  const int nl = a.nlive[b];
+  const int tiles = (nl + 255) / 256;
+  if (tile >= tiles) return;
+  const int nch = (nl + a.chunk - 1) / a.chunk;
+  const int64_t hbase = ((int64_t)l * a.batch + b) * a.q_heads;
+
+  for (int h = tid; h < a.q_heads; h += 256) {
+    const float* ml = a.part_ml + (hbase + h) * a.max_chunks * 2;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[2 * c]);
+    float L = 0.f;
+    for (int c = 0; c < nch; ++c) L += ml[2 * c + 1] * exp2f(ml[2 * c] - M);
+    Ms[h] = M;
+    iLs[h] = 1.f / L;
+  }
+  __syncthreads();
+
+  // output rows of the heads assigned to this tile
+  for (int h = tile; h < a.q_heads; h += tiles) {
+    const float* ml = a.part_ml + (hbase + h) * a.max_chunks * 2;
+    const float* po = a.part_o + (hbase + h) * a.max_chunks * D;
+    for (int e = tid; e < D; e += 256) {
+      float acc = 0.f;
+      for (int c = 0; c < nch; ++c) acc += po[(int64_t)c * D + e] * exp2f(ml[2 * c] - Ms[h]);
+      a.out[(((int64_t)ll * a.batch + b) * a.q_heads + h) * D + e] = acc * iLs[h];
+    }
+  }
+
+  const int j = tile * 256 + tid;
+  if (j < nl) {
+    float S = 0.f;
+    const float* lg = a.logits + hbase * a.nmax + j;
+    for (int h = 0; h < a.q_heads; ++h) S += exp2f(lg[(int64_t)h * a.nmax] - Ms[h]) * iLs[h];
+    a.layer_score[((int64_t)l * a.batch + b) * a.nmax + j] = S;
+  }
+}
+
+// Eq. 1 update: s[pos(j)] += (sum over layers, in order) * 1/(L*H).
+__global__ __launch_bounds__(256) void k_score(const ScoreArgs a) {
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= a.nlive[b]) return;
+  float acc = 0.f;
+  for (int l = 0; l < a.layers; ++l) acc += a.layer_score[((int64_t)l * a.batch + b) * a.nmax + j];
+  const int64_t p = (int64_t)b * a.nmax + a.live_pos[(int64_t)b * a.nmax + j];
+  a.s[p] += acc * a.inv_lh;
+}
+
+template <typename T, int D, int G>
+hipError_t launch_attn_t(const AttnArgs& a, int chunk, dim3 grid, hipStream_t s) {
+  switch (chunk) {
+    case 128: k_attn_chunk<T, D, G, 128><<<grid, 256, 0, s>>>(a); break;
+    case 256: k_attn_chunk<T, D, G, 256><<<grid, 256, 0, s>>>(a); break;
+    case 512: k_attn_chunk<T, D, G, 512><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_attn_g(const AttnArgs& a, int group, int chunk, dim3 grid, hipStream_t s) {
+  switch (group) {
+    case 1: return launch_attn_t<T, D, 1>(a, chunk, grid, s);
+    case 2: return launch_attn_t<T, D, 2>(a, chunk, grid, s);
+    case 4: return launch_attn_t<T, D, 4>(a, chunk, grid, s);
+    case 5: return launch_attn_t<T, D, 5>(a, chunk, grid, s);
+    case 8: return launch_attn_t<T, D, 8>(a, chunk, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  k_append<<<dim3(a.layers * a.batch, 2), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnArgs& a, int dtype, int head_dim, int group, int chunk,
+                       int layer_count, int chunks_now, hipStream_t s) {
+  const dim3 grid(chunks_now, a.kv_heads, layer_count * a.batch);
+  if (dtype == TKV_BF16) {
+    if (head_dim == 128) return launch_attn_g<bf16_t, 128>(a, group, chunk, grid, s);
+    if (head_dim == 64) return launch_attn_g<bf16_t, 64>(a, group, chunk, grid, s);
+  } else {
+    if (head_dim == 128) return launch_attn_g<float, 128>(a, group, chunk, grid, s);
+    if (head_dim == 64) return launch_attn_g<float, 64>(a, group, chunk, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_finalize(const FinalizeArgs& a, int head_dim, int layer_count, int tiles_now,
+                           hipStream_t s) {
+  const dim3 grid(tiles_now, a.batch, layer_count);
+  if (head_dim == 128)
+    k_finalize<128><<<grid, 256, 0, s>>>(a);
+  else if (head_dim == 64)
+    k_finalize<64><<<grid, 256, 0, s>>>(a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s) {
+  k_score<<<dim3(tiles_now, a.batch), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace tkvd

@@ -1,0 +1,81 @@
+// The tkv handle: configuration, device buffers, host-side placement state.
+#pragma once
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "tkv_internal.hpp"
+
+enum class TkvState { Empty, Ready, InStep };
+
+struct tkv {
+  // ---- configuration
+  int L = 0, Hq = 0, Hkv = 0, D = 0, B = 0, nmax = 0, dtype = 0, esz = 0, group = 0;
+  int delta = 0, chunk = 256, S = 0;  // S = staging slots (== L when resident)
+  bool resident = true;
+  double hbm = 0, evict = 0, t2 = 0;
+  int prompt = 0, sinks = 0, recent = 0;
+  uint64_t flags = 0;
+  int cap0 = 0, cap1 = 0, cap2 = 0, capS = 0, max_chunks = 0;
+  int64_t row_elems = 0, row_bytes = 0;
+
+  // ---- device buffers (owned)
+  void* pool_k = nullptr;  // [L][B][cap0][Hkv][D]
+  void* pool_v = nullptr;
+  void* stage_k = nullptr;  // [S][B][capS][Hkv][D]
+  void* stage_v = nullptr;
+  uint32_t* live_loc = nullptr;  // [B][nmax]
+  int32_t* live_pos = nullptr;   // [B][nmax]
+  uint8_t* tier = nullptr;       // [B][nmax]
+  uint32_t* loc = nullptr;       // [B][nmax]
+  float* s = nullptr;            // [B][nmax]
+  float* logits = nullptr;       // [L][B][Hq][nmax]
+  float* part_ml = nullptr;      // [L][B][Hq][max_chunks][2]
+  float* part_o = nullptr;       // [L][B][Hq][max_chunks][D]
+  float* layer_score = nullptr;  // [L][B][nmax]
+  std::vector<void*> device_allocs;
+
+  // ---- pinned host arenas (owned)
+  void* arena1_k = nullptr;  // [L][B][cap1][Hkv][D]: T1 rows, dense per (layer, seq)
+  void* arena1_v = nullptr;
+  std::vector<void*> host_allocs;
+
+  // ---- host-side placement state
+  int n = 0;  // positions appended per sequence
+  int64_t step = 0;
+  int layers_done = 0;
+  TkvState state = TkvState::Empty;
+  std::vector<int32_t> nlive;                 // [B] live rows
+  std::vector<std::vector<int32_t>> free0;    // [B] free T0 slots (back = next to use)
+  std::vector<uint8_t> h_tier;                // [B][nmax]
+  std::vector<uint32_t> h_loc;                // [B][nmax]
+  std::vector<std::vector<int32_t>> t1_owner; // [B]: T1 arena index -> position
+
+  // ---- last reassignment's changed rows
+  std::vector<tkv_delta> last_promote, last_demote;  // [B][nmax]
+  std::vector<int32_t> last_counts;                  // [B][2]
+
+  // ---- stats and timing
+  tkv_stats_t st{};
+  std::vector<hipEvent_t> ev_free;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_pending;
+
+  std::string err;
+
+  tkvd::RowSpace rowspace() const {
+    tkvd::RowSpace r{};
+    r.pool_k = pool_k;
+    r.pool_v = pool_v;
+    r.stage_k = stage_k;
+    r.stage_v = stage_v;
+    r.pool_bstride = (int64_t)cap0 * row_elems;
+    r.pool_lstride = r.pool_bstride * B;
+    r.stage_bstride = (int64_t)capS * row_elems;
+    r.stage_lstride = r.stage_bstride * B;
+    r.cap0 = cap0;
+    r.stage_slots = S;
+    return r;
+  }
+};

@@ -1,0 +1,49 @@
+// Small host-side helpers shared by the C ABI files.
+#pragma once
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "handle.hpp"
+
+int tkv_fail(tkv* t, int code, const char* fmt, ...);
+
+#define HIP_TRY(t, call)                                                                       \
+  do {                                                                                         \
+    hipError_t e_ = (call);                                                                    \
+    if (e_ != hipSuccess) {                                                                    \
+      (void)hipGetLastError();                                                                 \
+      return tkv_fail((t), TKV_EHIP, "%s failed: %s", #call, hipGetErrorString(e_));           \
+    }                                                                                          \
+  } while (0)
+
+// floor(ratio * n) in fp64: the tier budgets of Method §1.
+inline int64_t floor_ratio(double r, int64_t n) { return (int64_t)std::floor(r * (double)n); }
+
+// Protected positions of a sequence holding n positions: [0, prompt),
+// [0, sinks) and the last `recent` (Method §1: prompt, sinks, recent window).
+inline bool is_protected(const tkv& t, int64_t i, int64_t n) {
+  return i < t.prompt || i < t.sinks || i >= n - t.recent;
+}
+
+// Placement of a freshly filled cache before any score exists: protected
+// rows plus the lowest positions in T0 up to floor(hbm * n), the rest T1.
+inline std::vector<uint8_t> first_placement(const tkv& t, int n) {
+  std::vector<uint8_t> tier(n, TKV_T1);
+  int64_t np = 0;
+  for (int i = 0; i < n; ++i)
+    if (is_protected(t, i, n)) {
+      tier[i] = TKV_T0;
+      ++np;
+    }
+  const int64_t ncand = n - np;
+  int64_t room = std::min<int64_t>(ncand, std::max<int64_t>(0, floor_ratio(t.hbm, n) - np));
+  for (int i = 0; i < n && room > 0; ++i)
+    if (tier[i] == TKV_T1) {
+      tier[i] = TKV_T0;
+      --room;
+    }
+  return tier;
+}

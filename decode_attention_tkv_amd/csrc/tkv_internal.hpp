@@ -1,0 +1,104 @@
+// Internal declarations of the tkv library: handle state, kernel argument
+// blocks and kernel launchers.  Host code (api.cpp, reassign.cpp) and the
+// HIP kernels (attn.hip, reassign.hip, move.hip) include this.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/tkv.h"
+
+namespace tkvd {
+
+constexpr int kMaxBatch = 64;
+constexpr int kMaxQHeads = 256;
+constexpr uint32_t kNoLoc = 0xFFFFFFFFu;  // loc code of evicted / unused positions
+constexpr uint8_t kUnused = 255;           // tier code of positions not appended yet
+
+// ---- kernel argument blocks (passed by value) ------------------------------
+
+// Where the K/V rows of one layer live.  A live row's location code `loc` is
+// a T0 pool slot when loc < cap0, else index (loc - cap0) of the staging area
+// of slot (layer % stage_slots).  Both areas are [..][batch][cap][kv_heads][head_dim].
+struct RowSpace {
+  const void* pool_k;
+  const void* pool_v;
+  const void* stage_k;
+  const void* stage_v;
+  int64_t pool_lstride, pool_bstride;    // elements per layer / per sequence of the pool
+  int64_t stage_lstride, stage_bstride;  // elements per slot / per sequence of the staging area
+  int32_t cap0;
+  int32_t stage_slots;
+};
+
+struct AttnArgs {
+  RowSpace rows;
+  const uint32_t* live_loc;  // [batch][nmax] loc code of live index j (ascending position)
+  const void* q;             // [layer_count][batch][q_heads][head_dim]
+  float* logits;             // [layers][batch][q_heads][nmax], log2-scaled q.k/sqrt(d)
+  float* part_ml;            // [layers][batch][q_heads][max_chunks][2] chunk (max, sum)
+  float* part_o;             // [layers][batch][q_heads][max_chunks][head_dim]
+  float qscale;              // log2(e) / sqrt(head_dim)
+  int32_t layer_begin, batch, q_heads, kv_heads, nmax, max_chunks;
+  int32_t nlive[kMaxBatch];
+};
+
+struct FinalizeArgs {
+  const float* logits;
+  const float* part_ml;
+  const float* part_o;
+  float* out;     // [layer_count][batch][q_heads][head_dim] fp32
+  float* layer_score;  // [layers][batch][nmax]: sum over heads of alpha, per live index
+  int32_t layer_begin, batch, q_heads, nmax, max_chunks, chunk;
+  int32_t nlive[kMaxBatch];
+};
+
+struct ScoreArgs {
+  const float* layer_score;
+  const int32_t* live_pos;  // [batch][nmax]
+  float* s;                 // [batch][nmax] by position
+  float inv_lh;             // 1 / (layers * q_heads)
+  int32_t layers, batch, nmax;
+  int32_t nlive[kMaxBatch];
+};
+
+struct AppendArgs {
+  RowSpace rows;
+  const void* k;  // [layers][batch][kv_heads][head_dim]
+  const void* v;
+  uint32_t* live_loc;
+  int32_t* live_pos;
+  uint8_t* tier;
+  uint32_t* loc;
+  float* s;
+  int32_t layers, batch, kv_heads, head_dim, elem_bytes, nmax, pos;
+  int32_t slot[kMaxBatch];
+  int32_t nlive[kMaxBatch];
+};
+
+// Place input rows [layers][batch][n_tokens][row] at their location codes
+// (codes [batch][n_tokens]; kNoLoc = skip).
+struct PlaceArgs {
+  RowSpace rows;
+  const void* k;
+  const void* v;
+  const uint32_t* codes;
+  int64_t row_bytes;
+  int32_t batch, n_tokens, elem_bytes;
+};
+
+// ---- launchers (attn.hip) -------------------------------------------------
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, int dtype, int head_dim, int group, int chunk,
+                       int layer_count, int chunks_now, hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs& a, int head_dim, int layer_count, int tiles_now,
+                           hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s);
+
+// ---- launchers (move.hip) -------------------------------------------------
+hipError_t launch_place_rows(const PlaceArgs& a, int layers, hipStream_t s);
+
+}  // namespace tkvd

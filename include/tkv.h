@@ -1,0 +1,170 @@
+/*
+ * tkv.h -- tiered-KV decode attention with cumulative attention scoring,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the semantics-aware KV-cache hierarchy of "Not All Thoughts
+ * Need HBM: Semantics-Aware Memory Hierarchy for LLM Reasoning" (arXiv
+ * 2605.09490; gist.science technical summary and the arXiv abstract):
+ *   - Method §1: every cache position sits in one of four tiers -- T0 (HBM;
+ *     always holds the prompt, the attention sinks and the recent window),
+ *     T1 (host DDR at full precision, brought to the GPU before attention),
+ *     T2 (host, 8-bit), T3 (evicted for good).
+ *   - Method §2, Eq. 1: per decode step, s_i += mean over layers and heads of
+ *     the attention weight alpha_{l,h}[i].
+ *   - Method §3, Proposition 1: T1 rows take part in attention at full
+ *     precision, so outputs depend only on the evicted set, never on the
+ *     T0/T1 split.  Here that holds bit for bit: the reduction order follows
+ *     logical position, not where a row is stored.
+ *   - Method §4: re-placement every Delta (default 64) steps; only rows whose
+ *     tier changed are moved.
+ *
+ * Conventions for every call:
+ *   - Return TKV_OK (0) or a negative tkv_status.  Nothing throws across the
+ *     boundary.  tkv_last_error() gives the message of the last failure on a
+ *     handle (or of the last failed tkv_create when passed NULL).
+ *   - "device" pointers are HIP device memory (e.g. a torch tensor's
+ *     data_ptr()); "host" pointers are ordinary CPU memory.  The caller owns
+ *     every pointer it passes; the library owns everything it allocates.
+ *   - Work is ordered on the caller's `stream` (a hipStream_t; NULL is the
+ *     null stream).  Device buffers passed in must stay valid until that
+ *     stream's work has completed.  Calls that return host data synchronise
+ *     the stream.
+ *   - A handle is used from one host thread at a time.
+ *   - Layouts are dense row-major; element type is the handle's dtype (bf16
+ *     bit patterns or fp32) unless stated.
+ */
+#ifndef TKV_H
+#define TKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tkv tkv_t;
+typedef void* tkv_stream_t; /* a hipStream_t */
+
+typedef enum {
+  TKV_OK = 0,
+  TKV_EINVAL = -1,    /* bad argument: shape, ratio outside [0,1], delta <= 0, NULL pointer */
+  TKV_ECAPACITY = -2, /* more positions than max_tokens, or the T0 pool is full */
+  TKV_ENOMEM = -3,    /* device or pinned-host allocation failed */
+  TKV_ESTATE = -4,    /* call out of order (e.g. reassign between layer groups of a step) */
+  TKV_EHIP = -5       /* a HIP runtime call failed; see tkv_last_error */
+} tkv_status;
+
+typedef enum { TKV_BF16 = 0, TKV_F32 = 1 } tkv_dtype;
+typedef enum { TKV_T0 = 0, TKV_T1 = 1, TKV_T2 = 2, TKV_T3 = 3 } tkv_tier;
+
+/* Model and batch shape.  q_heads must be a multiple of kv_heads (query head
+ * h reads kv head h / (q_heads / kv_heads)); head_dim is 64 or 128; batch is
+ * 1..64; q_heads <= 256. */
+typedef struct {
+  int32_t layers, q_heads, kv_heads, head_dim, batch, max_tokens;
+  int32_t dtype; /* tkv_dtype */
+} tkv_shape;
+
+/* Always-T0 positions of every sequence: [0, prompt), [0, sinks) and the
+ * last `recent` positions (Method §1). */
+typedef struct {
+  int32_t prompt, sinks, recent;
+} tkv_protect;
+
+typedef struct {
+  double t2_ratio;        /* share of positions held 8-bit on the host (T2); 0 = no T2 */
+  int32_t staging_layers; /* S: HBM staging slots for T1/T2 rows.  0 or >= layers: every
+                             layer keeps its staging ("resident": only changed rows move).
+                             2..layers-1: "stream": each step copies a layer's T1/T2 rows
+                             from pinned host memory into slot (layer mod S), one layer
+                             ahead of the attention that reads it. */
+  int32_t chunk;          /* split-K rows per work-group: 0 (default 256), 128, 256 or 512 */
+  uint64_t flags;         /* TKV_FLAG_* */
+} tkv_options;
+
+/* Record HIP events around the attention kernels; tkv_stats reports their time. */
+#define TKV_FLAG_TIME_KERNELS 1ull
+
+/* One changed row of a reassignment (Method §4). */
+typedef struct {
+  uint32_t pos;     /* logical position */
+  uint8_t old_tier; /* tkv_tier */
+  uint8_t new_tier; /* tkv_tier */
+  uint16_t reserved;
+} tkv_delta;
+
+typedef struct {
+  int64_t step;              /* decode steps completed */
+  int64_t n_tokens;          /* positions appended per sequence (incl. evicted) */
+  int64_t tier_count[4];     /* positions per tier, summed over the batch */
+  int64_t hbm_bytes;         /* K/V bytes allocated in HBM (T0 pool + staging) */
+  int64_t host_bytes;        /* pinned host K/V bytes (T1 + T2 arenas) */
+  int64_t full_cache_bytes;  /* K/V bytes an all-HBM cache of max_tokens would take */
+  int64_t promotions, demotions, evictions, reassigns;
+  int64_t h2d_bytes, d2h_bytes; /* K/V rows moved host<->device since create */
+  double attn_kernel_ms;     /* with TKV_FLAG_TIME_KERNELS: summed split-K kernel time */
+  int64_t attn_kernel_launches;
+  double reassign_ms;        /* host wall time inside tkv_reassign */
+} tkv_stats_t;
+
+/* Create a handle and allocate every pool.  delta: reassignment period
+ * (Method §4); hbm_ratio / evict_ratio in [0,1] give the T0 and T3 shares
+ * floor(ratio * N) of the N positions appended so far.  opts may be NULL.
+ * On failure *out is NULL and tkv_last_error(NULL) explains. */
+int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_ratio, double evict_ratio,
+               tkv_protect protect, const tkv_options* opts, tkv_t** out);
+
+/* Synchronise the library's own streams and free everything.  NULL is a no-op. */
+int tkv_destroy(tkv_t* t);
+
+/* Message of the last failure on t (NULL: of the last failed tkv_create). */
+const char* tkv_last_error(const tkv_t* t);
+
+/* Fill an empty cache with n_tokens positions.  k, v: device
+ * [layers][batch][n_tokens][kv_heads][head_dim].  Scores start at 0; the
+ * first placement (before any score exists) is the protected set plus the
+ * lowest positions in T0 up to floor(hbm_ratio * n_tokens), the rest in T1;
+ * nothing is evicted and nothing goes to T2.  Synchronises `stream`. */
+int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tokens, tkv_stream_t stream);
+
+/* Start a decode step: append one position to every sequence.  k, v: device
+ * [layers][batch][kv_heads][head_dim].  The new row enters T0 with score 0.
+ * TKV_ECAPACITY at max_tokens or when the T0 pool is full (reassign first). */
+int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream);
+
+/* Attention of layers [layer_begin, layer_begin + layer_count) of the
+ * current step (Method §3): every non-evicted row of every tier takes part.
+ * q: device [layer_count][batch][q_heads][head_dim] (handle dtype);
+ * out: device fp32 [layer_count][batch][q_heads][head_dim].  Layer groups of
+ * one step must be called in order and cover every layer once; when the last
+ * layer is done the step's Eq. 1 increment is added to the scores. */
+int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
+                    tkv_stream_t stream);
+
+/* Re-place every sequence's rows by score (Method §1, §4): protected rows to
+ * T0; of the other live rows, ranked by score descending then position
+ * ascending, the lowest go to T3 (up to floor(evict_ratio*N) evicted in
+ * total), the highest fill T0 up to floor(hbm_ratio*N), the next lowest
+ * floor(t2_ratio*N) go to T2 and the rest to T1.  Only changed rows move.
+ * Call between steps, normally when the step count is a multiple of delta.
+ * Synchronises `stream` once (to read the change counts). */
+int tkv_reassign(tkv_t* t, tkv_stream_t stream);
+
+/* Counters and sizes; synchronises the library's streams. */
+int tkv_stats(tkv_t* t, tkv_stats_t* out);
+
+/* Test and inspection hooks (synchronise `stream`).  Arrays are host
+ * [batch][max_tokens]; entries at positions >= n_tokens are unspecified. */
+int tkv_read_scores(tkv_t* t, float* scores, tkv_stream_t stream);
+int tkv_write_scores(tkv_t* t, const float* scores, tkv_stream_t stream);
+int tkv_read_tiers(tkv_t* t, uint8_t* tiers, tkv_stream_t stream);
+/* Changed rows of the last tkv_reassign: promote/demote are host
+ * [batch][max_tokens], ascending by position per sequence; counts is host
+ * [batch][2] = {promotions, demotions}. */
+int tkv_read_deltas(tkv_t* t, tkv_delta* promote, tkv_delta* demote, int32_t* counts);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TKV_H */

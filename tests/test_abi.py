@@ -1,0 +1,70 @@
+"""The C-ABI library, on the CPU: it loads, exports every call that
+include/tkv.h declares, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tkv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tkv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def tkv():
+    import decode_attention_tkv_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from decode_attention_tkv_amd import _build
+        _build.build()
+    return m
+
+
+def test_every_declared_symbol_is_exported(tkv):
+    names = _declared()
+    assert "tkv_create" in names and "tkv_decode_attn" in names and "tkv_reassign" in names
+    lib = tkv.lib()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_call(tkv):
+    for n in _declared():
+        assert n in tkv._SIGS, n
+
+
+@pytest.mark.parametrize("field,value", [("layers", 0), ("q_heads", 6), ("head_dim", 96), ("batch", 65),
+                                         ("dtype", 7), ("max_tokens", 0)])
+def test_create_rejects_bad_shape(tkv, field, value):
+    args = dict(layers=2, q_heads=8, kv_heads=4, head_dim=64, batch=1, max_tokens=64, dtype=tkv.TKV_F32,
+                delta=16, hbm_ratio=0.5, evict_ratio=0.1, prompt=4, sinks=4, recent=8)
+    args[field] = value
+    with pytest.raises(tkv.TkvError) as e:
+        tkv.tkv_create(**args)
+    assert e.value.code == tkv.TKV_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(hbm_ratio=1.5), dict(evict_ratio=-0.1), dict(delta=0),
+                                dict(t2_ratio=2.0), dict(chunk=100), dict(staging_layers=1),
+                                dict(prompt=-1), dict(hbm_ratio=float("nan"))])
+def test_create_rejects_bad_policy(tkv, kw):
+    args = dict(layers=2, q_heads=8, kv_heads=4, head_dim=64, batch=1, max_tokens=64, dtype=tkv.TKV_F32,
+                delta=16, hbm_ratio=0.5, evict_ratio=0.1, prompt=4, sinks=4, recent=8)
+    args.update(kw)
+    with pytest.raises(tkv.TkvError) as e:
+        tkv.tkv_create(**args)
+    assert e.value.code == tkv.TKV_EINVAL
+    assert tkv.lib().tkv_last_error(None)
+
+
+def test_null_handle_calls_fail_cleanly(tkv):
+    lib = tkv.lib()
+    assert lib.tkv_destroy(None) == tkv.TKV_OK
+    assert lib.tkv_append(None, None, None, None) == tkv.TKV_EINVAL
+    assert lib.tkv_decode_attn(None, 0, 1, None, None, None) == tkv.TKV_EINVAL
+    assert lib.tkv_reassign(None, None) == tkv.TKV_EINVAL
