@@ -50,8 +50,21 @@ static int host_alloc(tkv* t, void** p, size_t bytes) {
 }
 
 static void release(tkv* t) {
+  if (t->side) (void)hipStreamSynchronize(t->side);
   for (void* p : t->device_allocs) (void)hipFree(p);
   for (void* p : t->host_allocs) (void)hipHostFree(p);
+  if (t->d_ops) (void)hipFree(t->d_ops);
+  if (t->h_ops) (void)hipHostFree(t->h_ops);
+  if (t->h_pack_in) (void)hipHostFree(t->h_pack_in);
+  for (hipEvent_t e : t->ev_h2d) (void)hipEventDestroy(e);
+  for (hipEvent_t e : t->ev_comp) (void)hipEventDestroy(e);
+  if (t->ev_arena) (void)hipEventDestroy(t->ev_arena);
+  if (t->side) (void)hipStreamDestroy(t->side);
+  t->d_ops = t->h_ops = t->h_pack_in = nullptr;
+  t->ev_h2d.clear();
+  t->ev_comp.clear();
+  t->ev_arena = nullptr;
+  t->side = nullptr;
   for (hipEvent_t e : t->ev_free) (void)hipEventDestroy(e);
   for (auto& pr : t->ev_pending) {
     (void)hipEventDestroy(pr.first);
@@ -95,7 +108,6 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   if (o.staging_layers < 0 || o.staging_layers == 1)
     return tkv_fail(nullptr, TKV_EINVAL, "staging_layers must be 0 or >= 2");
   const bool resident = o.staging_layers == 0 || o.staging_layers >= s.layers;
-  if (!resident) return tkv_fail(nullptr, TKV_EINVAL, "stream staging (staging_layers < layers) is not available yet");
   if (o.t2_ratio > 0) return tkv_fail(nullptr, TKV_EINVAL, "the 8-bit host tier is not available yet");
 
   tkv* t = new tkv();
@@ -149,8 +161,27 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   dev((void**)&t->part_ml, L * B * Hq * t->max_chunks * 2 * 4);
   dev((void**)&t->part_o, L * B * Hq * t->max_chunks * t->D * 4);
   dev((void**)&t->layer_score, L * B * nmax * 4);
+  dev((void**)&t->tier_alt, B * nmax);
+  dev((void**)&t->d_promote, B * nmax * sizeof(tkv_delta));
+  dev((void**)&t->d_demote, B * nmax * sizeof(tkv_delta));
+  dev((void**)&t->d_counts, B * 2 * 4);
   if (rc == TKV_OK) rc = host_alloc(t, &t->arena1_k, L * B * t->cap1 * t->row_bytes);
   if (rc == TKV_OK) rc = host_alloc(t, &t->arena1_v, L * B * t->cap1 * t->row_bytes);
+  if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_promote, B * nmax * sizeof(tkv_delta));
+  if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_demote, B * nmax * sizeof(tkv_delta));
+  if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_counts, B * 2 * 4);
+  if (rc == TKV_OK) {
+    hipError_t e = hipStreamCreateWithFlags(&t->side, hipStreamNonBlocking);
+    t->ev_h2d.assign(t->S, nullptr);
+    t->ev_comp.assign(t->S, nullptr);
+    t->comp_recorded.assign(t->S, 0);
+    for (int i = 0; i < t->S && e == hipSuccess; ++i) {
+      e = hipEventCreateWithFlags(&t->ev_h2d[i], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_comp[i], hipEventDisableTiming);
+    }
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_arena, hipEventDisableTiming);
+    if (e != hipSuccess) rc = tkv_fail(t, TKV_EHIP, "creating streams/events: %s", hipGetErrorString(e));
+  }
   if (rc == TKV_OK) {
     hipError_t e = hipSuccess;
     if (e == hipSuccess) e = hipMemset(t->tier, kUnused, B * nmax);
@@ -174,9 +205,7 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   t->h_tier.assign(B * nmax, kUnused);
   t->h_loc.assign(B * nmax, kNoLoc);
   t->t1_owner.resize(B);
-  t->last_promote.assign(B * nmax, tkv_delta{});
-  t->last_demote.assign(B * nmax, tkv_delta{});
-  t->last_counts.assign(B * 2, 0);
+  std::memset(t->h_counts, 0, B * 2 * 4);
   t->st.hbm_bytes = (int64_t)(2 * L * B * t->cap0 + 2 * (size_t)t->S * B * t->capS) * t->row_bytes;
   t->st.host_bytes = (int64_t)(2 * L * B * t->cap1) * t->row_bytes;
   t->st.full_cache_bytes = (int64_t)(2 * L * B * nmax) * t->row_bytes;
@@ -233,6 +262,22 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
   HIP_TRY(t, hipMemcpyAsync(d_codes, codes.data(), codes.size() * 4, hipMemcpyHostToDevice, st));
   PlaceArgs pa{};
   pa.rows = t->rowspace();
+  // T1 rows land in a staging area first: the resident staging itself, or (stream
+  // mode, whose staging holds only S layers) a temporary [L][B][cap1] area.
+  void* tmp_k = nullptr;
+  void* tmp_v = nullptr;
+  size_t src_pitch = (size_t)t->capS * t->row_bytes;
+  if (!t->resident && nt1 > 0) {
+    const size_t bytes = (size_t)t->L * t->B * t->cap1 * t->row_bytes;
+    HIP_TRY(t, hipMallocAsync(&tmp_k, bytes, st));
+    HIP_TRY(t, hipMallocAsync(&tmp_v, bytes, st));
+    pa.rows.stage_k = tmp_k;
+    pa.rows.stage_v = tmp_v;
+    pa.rows.stage_slots = t->L;
+    pa.rows.stage_bstride = (int64_t)t->cap1 * t->row_elems;
+    pa.rows.stage_lstride = pa.rows.stage_bstride * t->B;
+    src_pitch = (size_t)t->cap1 * t->row_bytes;
+  }
   pa.k = k;
   pa.v = v;
   pa.codes = (const uint32_t*)d_codes;
@@ -246,11 +291,13 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
     const size_t width = (size_t)nt1 * t->row_bytes;
     for (int which = 0; which < 2; ++which) {
       HIP_TRY(t, hipMemcpy2DAsync(which ? t->arena1_v : t->arena1_k, (size_t)t->cap1 * t->row_bytes,
-                                  which ? t->stage_v : t->stage_k, (size_t)t->capS * t->row_bytes, width,
+                                  which ? pa.rows.stage_v : pa.rows.stage_k, src_pitch, width,
                                   (size_t)t->L * t->B, hipMemcpyDeviceToHost, st));
     }
     t->st.d2h_bytes += 2 * (int64_t)width * t->L * t->B;
   }
+  if (tmp_k) HIP_TRY(t, hipFreeAsync(tmp_k, st));
+  if (tmp_v) HIP_TRY(t, hipFreeAsync(tmp_v, st));
   // per-position tables and the live list (every prefilled position is live)
   std::vector<int32_t> pos((size_t)t->B * n0);
   for (int b = 0; b < t->B; ++b)
@@ -336,18 +383,8 @@ static int drain_events(tkv* t) {
   return TKV_OK;
 }
 
-extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
-                               tkv_stream_t stream) {
-  if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
-  if (t->state != TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "no step in progress (append first)");
-  if (!q || !out) return tkv_fail(t, TKV_EINVAL, "q/out is NULL");
-  if (layer_begin != t->layers_done)
-    return tkv_fail(t, TKV_ESTATE, "layer groups must come in order: expected layer %d", t->layers_done);
-  if (layer_count < 1 || layer_begin + layer_count > t->L) return tkv_fail(t, TKV_EINVAL, "bad layer range");
-  hipStream_t st = (hipStream_t)stream;
-  int max_live = 0;
-  for (int b = 0; b < t->B; ++b) max_live = std::max(max_live, t->nlive[b]);
-
+// Split-K attention + chunk merge for layers [lb, lb + lc) whose q/out start at q, out.
+static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int max_live, hipStream_t st) {
   AttnArgs a{};
   a.rows = t->rowspace();
   a.live_loc = t->live_loc;
@@ -356,7 +393,7 @@ extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_coun
   a.part_ml = t->part_ml;
   a.part_o = t->part_o;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)t->D));
-  a.layer_begin = layer_begin;
+  a.layer_begin = lb;
   a.batch = t->B;
   a.q_heads = t->Hq;
   a.kv_heads = t->Hkv;
@@ -370,20 +407,19 @@ extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_coun
     int rc = record_event(t, &e0, st);
     if (rc) return rc;
   }
-  if (chunks_now > 0) HIP_TRY(t, launch_attn(a, t->dtype, t->D, t->group, t->chunk, layer_count, chunks_now, st));
+  if (chunks_now > 0) HIP_TRY(t, launch_attn(a, t->dtype, t->D, t->group, t->chunk, lc, chunks_now, st));
   if (timed) {
     int rc = record_event(t, &e1, st);
     if (rc) return rc;
     t->ev_pending.emplace_back(e0, e1);
   }
-
   FinalizeArgs f{};
   f.logits = t->logits;
   f.part_ml = t->part_ml;
   f.part_o = t->part_o;
   f.out = out;
   f.layer_score = t->layer_score;
-  f.layer_begin = layer_begin;
+  f.layer_begin = lb;
   f.batch = t->B;
   f.q_heads = t->Hq;
   f.nmax = t->nmax;
@@ -391,7 +427,68 @@ extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_coun
   f.chunk = t->chunk;
   for (int b = 0; b < t->B; ++b) f.nlive[b] = t->nlive[b];
   const int tiles_now = (max_live + 255) / 256;
-  if (tiles_now > 0) HIP_TRY(t, launch_finalize(f, t->D, layer_count, tiles_now, st));
+  if (tiles_now > 0) HIP_TRY(t, launch_finalize(f, t->D, lc, tiles_now, st));
+  return TKV_OK;
+}
+
+// Stream mode: copy layers' T1 rows from the pinned arena into their staging
+// slot (layer mod S) on the side stream, up to layer `upto`, each after the
+// attention that last read that slot.
+static int issue_prefetch(tkv* t, int upto) {
+  if (t->arena_pending) {
+    HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_arena, 0));
+    t->arena_pending = false;
+  }
+  size_t n1max = 0;
+  for (int b = 0; b < t->B; ++b) n1max = std::max(n1max, t->t1_owner[b].size());
+  for (; t->next_issue <= upto && t->next_issue < t->L; ++t->next_issue) {
+    const int x = t->next_issue, slot = x % t->S;
+    if (t->comp_recorded[slot]) HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_comp[slot], 0));
+    if (n1max > 0) {
+      const size_t width = n1max * t->row_bytes;
+      for (int which = 0; which < 2; ++which) {
+        char* dst = (char*)(which ? t->stage_v : t->stage_k) + (size_t)slot * t->B * t->capS * t->row_bytes;
+        const char* src = (const char*)(which ? t->arena1_v : t->arena1_k) + (size_t)x * t->B * t->cap1 * t->row_bytes;
+        HIP_TRY(t, hipMemcpy2DAsync(dst, (size_t)t->capS * t->row_bytes, src, (size_t)t->cap1 * t->row_bytes, width,
+                                    t->B, hipMemcpyHostToDevice, t->side));
+      }
+      t->st.h2d_bytes += 2 * (int64_t)width * t->B;
+    }
+    HIP_TRY(t, hipEventRecord(t->ev_h2d[slot], t->side));
+  }
+  return TKV_OK;
+}
+
+extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
+                               tkv_stream_t stream) {
+  if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  if (t->state != TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "no step in progress (append first)");
+  if (!q || !out) return tkv_fail(t, TKV_EINVAL, "q/out is NULL");
+  if (layer_begin != t->layers_done)
+    return tkv_fail(t, TKV_ESTATE, "layer groups must come in order: expected layer %d", t->layers_done);
+  if (layer_count < 1 || layer_begin + layer_count > t->L) return tkv_fail(t, TKV_EINVAL, "bad layer range");
+  hipStream_t st = (hipStream_t)stream;
+  int max_live = 0;
+  for (int b = 0; b < t->B; ++b) max_live = std::max(max_live, t->nlive[b]);
+
+  if (t->resident) {
+    int rc = launch_layers(t, layer_begin, layer_count, q, out, max_live, st);
+    if (rc) return rc;
+  } else {
+    if (layer_begin == 0) t->next_issue = 0;
+    const size_t q_layer = (size_t)t->B * t->Hq * t->D * t->esz;
+    const size_t o_layer = (size_t)t->B * t->Hq * t->D;
+    for (int i = 0; i < layer_count; ++i) {
+      const int l = layer_begin + i, slot = l % t->S;
+      int rc = issue_prefetch(t, l + t->S - 1);
+      if (rc) return rc;
+      HIP_TRY(t, hipStreamWaitEvent(st, t->ev_h2d[slot], 0));
+      rc = launch_layers(t, l, 1, (const char*)q + i * q_layer, out + i * o_layer, max_live, st);
+      if (rc) return rc;
+      HIP_TRY(t, hipEventRecord(t->ev_comp[slot], st));
+      t->comp_recorded[slot] = 1;
+    }
+  }
 
   t->layers_done += layer_count;
   if (t->layers_done == t->L) {
@@ -404,6 +501,7 @@ extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_coun
     sa.batch = t->B;
     sa.nmax = t->nmax;
     for (int b = 0; b < t->B; ++b) sa.nlive[b] = t->nlive[b];
+    const int tiles_now = (max_live + 255) / 256;
     if (tiles_now > 0) HIP_TRY(t, launch_score(sa, tiles_now, st));
     t->step += 1;
     t->state = TkvState::Ready;
@@ -413,6 +511,7 @@ extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_coun
 
 extern "C" int tkv_stats(tkv_t* t, tkv_stats_t* out) {
   if (!t || !out) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  HIP_TRY(t, hipStreamSynchronize(t->side));
   int rc = drain_events(t);
   if (rc) return rc;
   t->st.step = t->step;
@@ -451,8 +550,9 @@ extern "C" int tkv_read_tiers(tkv_t* t, uint8_t* tiers, tkv_stream_t stream) {
 
 extern "C" int tkv_read_deltas(tkv_t* t, tkv_delta* promote, tkv_delta* demote, int32_t* counts) {
   if (!t || !promote || !demote || !counts) return tkv_fail(t, TKV_EINVAL, "NULL argument");
-  std::memcpy(promote, t->last_promote.data(), t->last_promote.size() * sizeof(tkv_delta));
-  std::memcpy(demote, t->last_demote.data(), t->last_demote.size() * sizeof(tkv_delta));
-  std::memcpy(counts, t->last_counts.data(), t->last_counts.size() * sizeof(int32_t));
+  const size_t nd = (size_t)t->B * t->nmax;
+  std::memcpy(promote, t->h_promote, nd * sizeof(tkv_delta));
+  std::memcpy(demote, t->h_demote, nd * sizeof(tkv_delta));
+  std::memcpy(counts, t->h_counts, (size_t)t->B * 2 * sizeof(int32_t));
   return TKV_OK;
 }

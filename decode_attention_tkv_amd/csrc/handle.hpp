@@ -35,7 +35,19 @@ struct tkv {
   float* part_ml = nullptr;      // [L][B][Hq][max_chunks][2]
   float* part_o = nullptr;       // [L][B][Hq][max_chunks][D]
   float* layer_score = nullptr;  // [L][B][nmax]
+  uint8_t* tier_alt = nullptr;   // [B][nmax] labels being computed by a reassignment
+  tkv_delta* d_promote = nullptr;  // [B][nmax]
+  tkv_delta* d_demote = nullptr;   // [B][nmax]
+  int32_t* d_counts = nullptr;     // [B][2]
   std::vector<void*> device_allocs;
+
+  // growable device / pinned scratch of the reassignment
+  void* d_ops = nullptr;
+  size_t d_ops_bytes = 0;
+  void* h_ops = nullptr;  // pinned staging of ops + loc updates
+  size_t h_ops_bytes = 0;
+  void* h_pack_in = nullptr;  // pinned: promoted T1 rows packed on the host (stream mode)
+  size_t h_pack_in_bytes = 0;
 
   // ---- pinned host arenas (owned)
   void* arena1_k = nullptr;  // [L][B][cap1][Hkv][D]: T1 rows, dense per (layer, seq)
@@ -53,9 +65,19 @@ struct tkv {
   std::vector<uint32_t> h_loc;                // [B][nmax]
   std::vector<std::vector<int32_t>> t1_owner; // [B]: T1 arena index -> position
 
-  // ---- last reassignment's changed rows
-  std::vector<tkv_delta> last_promote, last_demote;  // [B][nmax]
-  std::vector<int32_t> last_counts;                  // [B][2]
+  // ---- last reassignment's changed rows (pinned host copies)
+  tkv_delta* h_promote = nullptr;  // [B][nmax]
+  tkv_delta* h_demote = nullptr;   // [B][nmax]
+  int32_t* h_counts = nullptr;     // [B][2]
+
+  // ---- streams and events
+  hipStream_t side = nullptr;           // host<->device row traffic of the stream mode
+  std::vector<hipEvent_t> ev_h2d;       // [S] staging slot filled
+  std::vector<hipEvent_t> ev_comp;      // [S] attention done reading the slot
+  std::vector<char> comp_recorded;      // [S]
+  hipEvent_t ev_arena = nullptr;        // host arena writes of the last reassignment done
+  bool arena_pending = false;
+  int next_issue = 0;                   // next layer whose staging copy is to be issued this step
 
   // ---- stats and timing
   tkv_stats_t st{};

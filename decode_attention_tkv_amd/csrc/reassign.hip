@@ -1,0 +1,243 @@
+// Reassignment kernels (Method §1 and §4 of "Not All Thoughts Need HBM",
+// gist.science technical summary): score-ranked tier labels, the lists of
+// changed rows, location-table updates, live-list rebuild and row copies.
+//
+// Ranking: candidates (not protected, not evicted) are ordered by the 64-bit
+// key (bits(s) << 32) | (0xFFFFFFFF - position): s >= 0, so its fp32 bit
+// pattern orders like the value, and a lower position wins a tie.  Keys are
+// unique, so three order statistics (radix select, 8 passes of 8 bits, one
+// work-group per sequence, LDS histograms with integer atomics) give the
+// exact cut points between T3 | T2 | T1 | T0.
+#include "tkv_internal.hpp"
+
+namespace tkvd {
+namespace {
+
+constexpr int kBlock = 1024;
+
+__device__ __forceinline__ uint64_t rank_key(float s, int i) {
+  const uint32_t bits = s == 0.f ? 0u : __float_as_uint(s);
+  return ((uint64_t)bits << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+__device__ __forceinline__ bool protected_pos(int i, int n, int prompt, int sinks, int recent) {
+  return i < prompt || i < sinks || i >= n - recent;
+}
+
+// grid (batch), block 1024
+__global__ __launch_bounds__(kBlock) void k_rank_label(const RankArgs a) {
+  __shared__ uint32_t hist[3][256];
+  __shared__ uint64_t prefix[3];
+  __shared__ int32_t want[3];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const float* s = a.s + (int64_t)b * a.nmax;
+  const uint8_t* old = a.tier_old + (int64_t)b * a.nmax;
+  uint8_t* neu = a.tier_new + (int64_t)b * a.nmax;
+  const int n = a.n, ncand = a.ncand[b];
+  if (tid < 3) {
+    prefix[tid] = 0;
+    want[tid] = a.rank[b][tid];
+  }
+  uint64_t mask = 0;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int x = tid; x < 3 * 256; x += kBlock) (&hist[0][0])[x] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kBlock) {
+      if (old[i] == TKV_T3 || protected_pos(i, n, a.prompt, a.sinks, a.recent)) continue;
+      const uint64_t key = rank_key(s[i], i);
+      const uint32_t digit = (uint32_t)(key >> shift) & 255u;
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        if (want[k] < ncand && (key & mask) == prefix[k]) atomicAdd(&hist[k][digit], 1u);
+    }
+    __syncthreads();
+    if (tid < 3 && want[tid] < ncand) {
+      uint32_t cum = 0;
+      for (int d = 0; d < 256; ++d) {
+        const uint32_t c = hist[tid][d];
+        if ((uint32_t)want[tid] < cum + c) {
+          prefix[tid] |= (uint64_t)d << shift;
+          want[tid] -= (int32_t)cum;
+          break;
+        }
+        cum += c;
+      }
+    }
+    mask |= (uint64_t)255u << shift;
+    __syncthreads();
+  }
+  // cut keys: a rank at or past the candidate count has no key; use one above every key
+  uint64_t cut[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) cut[k] = a.rank[b][k] < ncand ? prefix[k] : ~0ull;
+  for (int i = tid; i < n; i += kBlock) {
+    uint8_t t;
+    if (old[i] == TKV_T3)
+      t = TKV_T3;
+    else if (protected_pos(i, n, a.prompt, a.sinks, a.recent))
+      t = TKV_T0;
+    else {
+      const uint64_t key = rank_key(s[i], i);
+      if (key < cut[0])
+        t = TKV_T3;
+      else if (key < cut[1])
+        t = TKV_T2;
+      else if (key >= cut[2])
+        t = TKV_T0;
+      else
+        t = TKV_T1;
+    }
+    neu[i] = t;
+  }
+}
+
+// Exclusive prefix sum over the block (1024 threads = 16 waves); returns
+// the exclusive offset of this thread, *total = block sum.
+__device__ int block_exclusive_scan(int x, int* total) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < 16; ++i) {
+    if (i < w) base += wsum[i];
+    tot += wsum[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - x;
+}
+
+// Changed rows, ascending by position.  grid (batch), block 1024.
+__global__ __launch_bounds__(kBlock) void k_deltas(const DeltaArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const uint8_t* old = a.tier_old + (int64_t)b * a.nmax;
+  const uint8_t* neu = a.tier_new + (int64_t)b * a.nmax;
+  tkv_delta* pro = a.promote + (int64_t)b * a.nmax;
+  tkv_delta* dem = a.demote + (int64_t)b * a.nmax;
+  int np = 0, nd = 0;
+  for (int i0 = 0; i0 < a.n; i0 += kBlock) {
+    const int i = i0 + tid;
+    uint8_t o = 0, w = 0;
+    if (i < a.n) {
+      o = old[i];
+      w = neu[i];
+    }
+    const int fp = (i < a.n && w < o) ? 1 : 0;
+    const int fd = (i < a.n && w > o) ? 1 : 0;
+    int tp, td;
+    const int op = block_exclusive_scan(fp, &tp);
+    const int od = block_exclusive_scan(fd, &td);
+    tkv_delta e;
+    e.pos = (uint32_t)i;
+    e.old_tier = o;
+    e.new_tier = w;
+    e.reserved = 0;
+    if (fp) pro[np + op] = e;
+    if (fd) dem[nd + od] = e;
+    np += tp;
+    nd += td;
+  }
+  if (tid == 0) {
+    a.counts[2 * b] = np;
+    a.counts[2 * b + 1] = nd;
+  }
+}
+
+// loc[b][pos] = code for a list of updates.  grid (ceil(n/256)), block 256.
+__global__ __launch_bounds__(256) void k_set_loc(const LocUpdate* u, int n, uint32_t* loc, int nmax) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k < n) loc[(int64_t)u[k].b * nmax + u[k].pos] = u[k].code;
+}
+
+// Live list = non-evicted positions in ascending order with their codes.
+// grid (batch), block 1024.
+__global__ __launch_bounds__(kBlock) void k_build_live(const LiveArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const uint8_t* tier = a.tier + (int64_t)b * a.nmax;
+  const uint32_t* loc = a.loc + (int64_t)b * a.nmax;
+  int base = 0;
+  for (int i0 = 0; i0 < a.n; i0 += kBlock) {
+    const int i = i0 + tid;
+    const int f = (i < a.n && tier[i] != TKV_T3) ? 1 : 0;
+    int tot;
+    const int off = block_exclusive_scan(f, &tot);
+    if (f) {
+      a.live_pos[(int64_t)b * a.nmax + base + off] = i;
+      a.live_loc[(int64_t)b * a.nmax + base + off] = loc[i];
+    }
+    base += tot;
+  }
+}
+
+__device__ __forceinline__ char* area_row(const CopyArgs& a, int area, int which, int l, int b, uint32_t idx) {
+  const RowSpace& rs = a.rows;
+  switch (area) {
+    case kAreaPool: {
+      char* base = (char*)(which ? rs.pool_v : rs.pool_k);
+      return base + ((int64_t)l * rs.pool_lstride + (int64_t)b * rs.pool_bstride) * a.elem_bytes +
+             (int64_t)idx * a.row_bytes;
+    }
+    case kAreaStage: {
+      char* base = (char*)(which ? rs.stage_v : rs.stage_k);
+      return base + ((int64_t)(l % rs.stage_slots) * rs.stage_lstride + (int64_t)b * rs.stage_bstride) * a.elem_bytes +
+             (int64_t)idx * a.row_bytes;
+    }
+    case kAreaPackOut: {
+      char* base = (char*)(which ? a.pack_out_v : a.pack_out_k);
+      return base + ((int64_t)l * a.pack_out_rows + idx) * a.row_bytes;
+    }
+    default: {
+      char* base = (char*)(which ? a.pack_in_v : a.pack_in_k);
+      return base + ((int64_t)l * a.pack_in_rows + idx) * a.row_bytes;
+    }
+  }
+}
+
+// One op = one row of one sequence copied in every layer, K and V.
+// grid (n_ops, layers, 2), block 256.
+__global__ __launch_bounds__(256) void k_copy_rows(const CopyArgs a, const RowOp* ops) {
+  const RowOp op = ops[blockIdx.x];
+  const int l = blockIdx.y, which = blockIdx.z;
+  const char* src = area_row(a, op.src_area, which, l, op.b, op.src);
+  char* dst = area_row(a, op.dst_area, which, l, op.b, op.dst);
+  for (int64_t off = (int64_t)threadIdx.x * 16; off < a.row_bytes; off += 256 * 16)
+    *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(src + off);
+}
+
+}  // namespace
+
+hipError_t launch_rank_label(const RankArgs& a, int batch, hipStream_t s) {
+  k_rank_label<<<batch, kBlock, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_deltas(const DeltaArgs& a, int batch, hipStream_t s) {
+  k_deltas<<<batch, kBlock, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_loc(const LocUpdate* u, int n, uint32_t* loc, int nmax, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_set_loc<<<(n + 255) / 256, 256, 0, s>>>(u, n, loc, nmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_live(const LiveArgs& a, int batch, hipStream_t s) {
+  k_build_live<<<batch, kBlock, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const CopyArgs& a, const RowOp* ops, int n_ops, int layers, hipStream_t s) {
+  if (n_ops <= 0) return hipSuccess;
+  k_copy_rows<<<dim3(n_ops, layers, 2), 256, 0, s>>>(a, ops);
+  return hipGetLastError();
+}
+
+}  // namespace tkvd

@@ -90,6 +90,58 @@ struct PlaceArgs {
   int32_t batch, n_tokens, elem_bytes;
 };
 
+// ---- reassignment (reassign.hip) ---------------------------------------------
+struct RankArgs {
+  const float* s;
+  const uint8_t* tier_old;
+  uint8_t* tier_new;
+  int32_t nmax, n, prompt, sinks, recent;
+  int32_t ncand[kMaxBatch];    // candidates (live, unprotected) per sequence
+  int32_t rank[kMaxBatch][3];  // ascending-rank cut points: first non-T3, first non-T2, first T0
+};
+
+struct DeltaArgs {
+  const uint8_t* tier_old;
+  const uint8_t* tier_new;
+  tkv_delta* promote;  // [batch][nmax]
+  tkv_delta* demote;   // [batch][nmax]
+  int32_t* counts;     // [batch][2]
+  int32_t nmax, n;
+};
+
+struct LocUpdate {
+  int32_t b;
+  uint32_t pos;
+  uint32_t code;
+};
+
+struct LiveArgs {
+  const uint8_t* tier;
+  const uint32_t* loc;
+  int32_t* live_pos;
+  uint32_t* live_loc;
+  int32_t nmax, n;
+};
+
+// Row areas of a copy op.  Packs are [layers][rows][row].
+enum : uint8_t { kAreaPool = 0, kAreaStage = 1, kAreaPackOut = 2, kAreaPackIn = 3 };
+
+struct RowOp {
+  uint8_t src_area, dst_area;
+  uint16_t b;
+  uint32_t src, dst;
+};
+
+struct CopyArgs {
+  RowSpace rows;
+  void* pack_out_k;
+  void* pack_out_v;
+  void* pack_in_k;
+  void* pack_in_v;
+  int64_t pack_out_rows, pack_in_rows, row_bytes;
+  int32_t elem_bytes;
+};
+
 // ---- launchers (attn.hip) -------------------------------------------------
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int head_dim, int group, int chunk,
@@ -100,5 +152,12 @@ hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s);
 
 // ---- launchers (move.hip) -------------------------------------------------
 hipError_t launch_place_rows(const PlaceArgs& a, int layers, hipStream_t s);
+
+// ---- launchers (reassign.hip) -----------------------------------------------
+hipError_t launch_rank_label(const RankArgs& a, int batch, hipStream_t s);
+hipError_t launch_deltas(const DeltaArgs& a, int batch, hipStream_t s);
+hipError_t launch_set_loc(const LocUpdate* u, int n, uint32_t* loc, int nmax, hipStream_t s);
+hipError_t launch_build_live(const LiveArgs& a, int batch, hipStream_t s);
+hipError_t launch_copy_rows(const CopyArgs& a, const RowOp* ops, int n_ops, int layers, hipStream_t s);
 
 }  // namespace tkvd
