@@ -1,0 +1,220 @@
+"""Benchmark of the tiered-KV decode step on one MI355X.
+
+One step = append the new token's K/V, split-K attention over every live
+row of every layer, chunk merge, the Eq. 1 score update, and -- every Delta
+steps -- the reassignment (rank, label, changed-row lists, row moves).  The
+workload is the 7B-shaped one: 32 layers, 32 query / 32 kv heads, head_dim
+128, bf16, batch 1, 2200 prefilled positions, 512 decode steps, Delta = 64,
+HBM ratio 0.5, eviction 0.03, protected 200 prompt + 4 sinks + 128 recent,
+T1 staging resident in HBM.  Inputs are seeded synthetic (Gaussian with
+planted heavy hitters) and sit in HBM before the timed region starts.
+
+Prints one JSON line.  Extra fields: the split-K kernel's roofline (live K/V
+bytes per launch / launch time, HIP events on the launch stream), the
+stream-staging leg (T1 rows copied from pinned host memory one layer ahead
+of attention; H2D GB/s against the pinned H2D bandwidth measured here), and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode steps/sec (attn+scoring, all layers) at 7B shape; achieved HBM GB/s %peak"
+
+
+def _dev(a, dtype, torch):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+def load_inputs(w, steps, torch):
+    heavy, u = w.heavy_mask(), w.unit_vector()
+    k0 = _dev(w.kv(0, 0, w.prefill, heavy, u), w.dtype, torch)
+    v0 = _dev(w.kv(1, 0, w.prefill, heavy, u), w.dtype, torch)
+    kn = w.kv(0, w.prefill, steps, heavy, u)
+    vn = w.kv(1, w.prefill, steps, heavy, u)
+    # [steps][L][B][Hkv][d] so that each step's rows are one contiguous block
+    kn = _dev(np.ascontiguousarray(np.moveaxis(kn, 2, 0)), w.dtype, torch)
+    vn = _dev(np.ascontiguousarray(np.moveaxis(vn, 2, 0)), w.dtype, torch)
+    q = _dev(w.q(0, steps, u), w.dtype, torch)
+    return k0, v0, kn, vn, q
+
+
+def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kernels=True):
+    """Prefill, `warmup` untimed steps, then `steps` timed steps.  Returns
+    (seconds, stats before, stats after)."""
+    k0, v0, kn, vn, q = inputs
+    c = tkv.TieredKV.for_workload(w, staging_layers=staging_layers, time_kernels=time_kernels)
+    c.prefill(k0, v0)
+    h = c.h
+    out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    lib = tkv.lib()
+    optr = out.data_ptr()
+    kp = [kn[t].data_ptr() for t in range(warmup + steps)]
+    vp = [vn[t].data_ptr() for t in range(warmup + steps)]
+    qp = [q[t].data_ptr() for t in range(warmup + steps)]
+
+    def step(t):
+        rc = lib.tkv_append(h, kp[t], vp[t], stream)
+        if rc == 0:
+            rc = lib.tkv_decode_attn(h, 0, w.layers, qp[t], optr, stream)
+        if rc == 0 and (t + 1) % w.delta == 0:
+            rc = lib.tkv_reassign(h, stream)
+        if rc != 0:
+            raise tkv.TkvError(rc, lib.tkv_last_error(h).decode())
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    before = c.stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(warmup, warmup + steps):
+        step(t)
+    torch.cuda.synchronize()
+    secs = time.perf_counter() - t0
+    after = c.stats()
+    c.close()
+    return secs, before, after
+
+
+def pinned_h2d_gbs(torch, mb=256, reps=20):
+    src = torch.empty(mb << 20, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(mb << 20, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    return (mb << 20) / float(np.median(times)) / 1e9
+
+
+def cpu_baseline(w, n_steps):
+    """The oracle as it stands, on the host cores: prefill untimed, then
+    n_steps decode steps (with its own reassignment every Delta steps)."""
+    import oracle
+    heavy, u = w.heavy_mask(), w.unit_vector()
+    o = oracle.OracleTKV.for_workload(w)
+    o.prefill(w.values(w.kv(0, 0, w.prefill, heavy, u)), w.values(w.kv(1, 0, w.prefill, heavy, u)))
+    kn = w.values(w.kv(0, w.prefill, n_steps, heavy, u))
+    vn = w.values(w.kv(1, w.prefill, n_steps, heavy, u))
+    q = w.values(w.q(0, n_steps, u))
+    t0 = time.perf_counter()
+    for t in range(n_steps):
+        o.append(kn[:, :, t], vn[:, :, t])
+        o.attend(q[t])
+        if (t + 1) % w.delta == 0:
+            o.reassign()
+    secs = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    return {"value": n_steps / secs, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": "7b workload, prefill %d, decode steps 1..%d incl. %d reassignment(s); fp64 C "
+                      "attention (OpenMP) + numpy scoring/tiering; %.1f s"
+                      % (w.prefill, n_steps, n_steps // w.delta, secs)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=448)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="7b")
+    ap.add_argument("--stream-steps", type=int, default=64, help="timed steps of the stream-staging leg (0: skip)")
+    ap.add_argument("--cpu-steps", type=int, default=64, help="oracle steps of the CPU baseline (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the tiered-KV decode path has no multi-GPU leg "
+              "(sequences would shard one per GPU with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_attention_tkv_amd as tkv
+    import tkvsynth
+
+    base = tkvsynth.CONFIGS[args.workload]
+    total = args.warmup + args.steps
+    # the workload's own decode length, stretched if more steps are asked for
+    w = base if total <= base.steps else base.replace(steps=total)
+    print("[bench] drawing inputs for %s (%d steps)" % (w.name, w.steps), file=sys.stderr, flush=True)
+    inputs = load_inputs(w, w.steps, torch)
+    torch.cuda.synchronize()
+
+    print("[bench] resident staging: %d warmup + %d timed steps" % (args.warmup, args.steps),
+          file=sys.stderr, flush=True)
+    secs, before, after = run_decode(w, inputs, args.warmup, args.steps, torch, tkv)
+    kern_ms = after["attn_kernel_ms"] - before["attn_kernel_ms"]
+    launches = after["attn_kernel_launches"] - before["attn_kernel_launches"]
+    kv_bytes = after["attn_kv_bytes"] - before["attn_kv_bytes"]
+    steps_per_s = args.steps / secs
+    achieved = kv_bytes / (kern_ms / 1e3) / 1e9
+    step_gbs = kv_bytes / secs / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": secs / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s: %d layers, %d q / %d kv heads, head_dim %d, %s, batch %d, cache %d -> %d, "
+                               "delta %d, hbm %.2f, evict %.2f, protect %d prompt + %d sinks + %d recent, "
+                               "resident T1 staging" % (w.name, w.layers, w.q_heads, w.kv_heads, w.head_dim,
+                                                        w.dtype, w.batch, w.prefill, w.prefill + total, w.delta,
+                                                        w.hbm_ratio, w.evict_ratio, w.prompt, w.sinks, w.recent),
+                   "timed_steps": "%d..%d" % (args.warmup + 1, total),
+                   "reassignments_timed": int(after["reassigns"] - before["reassigns"])},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_attn_chunk (split-K attention pass)",
+                     "avg_launch_us": kern_ms / launches * 1e3, "launches": launches,
+                     "kv_bytes_per_launch": kv_bytes / launches},
+        "step_hbm_gbs": step_gbs,
+        "step_hbm_frac": step_gbs / HBM_PEAK_GBS,
+        "reassign_ms_per_call": (after["reassign_ms"] - before["reassign_ms"]) / max(1, after["reassigns"] - before["reassigns"]),
+    }
+
+    if args.stream_steps > 0:
+        print("[bench] stream staging (S=2): %d timed steps" % args.stream_steps, file=sys.stderr, flush=True)
+        pinned = pinned_h2d_gbs(torch)
+        ssecs, sb, sa = run_decode(w, inputs, args.warmup, args.stream_steps, torch, tkv, staging_layers=2)
+        h2d = sa["h2d_bytes"] - sb["h2d_bytes"]
+        result["stream_staging"] = {
+            "staging_layers": 2, "steps": args.stream_steps, "steps_per_s": args.stream_steps / ssecs,
+            "h2d_gbs": h2d / ssecs / 1e9, "pinned_h2d_gbs": pinned,
+            "h2d_frac_of_pinned": (h2d / ssecs / 1e9) / pinned,
+            "h2d_bytes_per_step": h2d / args.stream_steps,
+            "hbm_kv_bytes_allocated": sa["hbm_bytes"], "full_cache_bytes": sa["full_cache_bytes"]}
+
+    if args.cpu_steps > 0:
+        print("[bench] cpu baseline: oracle, %d steps" % args.cpu_steps, file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -65,6 +65,7 @@ class tkv_stats_t(ctypes.Structure):
                 ("demotions", ctypes.c_int64), ("evictions", ctypes.c_int64), ("reassigns", ctypes.c_int64),
                 ("h2d_bytes", ctypes.c_int64), ("d2h_bytes", ctypes.c_int64),
                 ("attn_kernel_ms", ctypes.c_double), ("attn_kernel_launches", ctypes.c_int64),
+                ("attn_kv_bytes", ctypes.c_int64),
                 ("reassign_ms", ctypes.c_double)]
 
 

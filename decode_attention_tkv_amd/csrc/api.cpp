@@ -50,16 +50,29 @@ static int host_alloc(tkv* t, void** p, size_t bytes) {
 }
 
 static void release(tkv* t) {
+  if (t->arena_job.valid()) (void)t->arena_job.get();
   if (t->side) (void)hipStreamSynchronize(t->side);
+  if (t->wb) (void)hipStreamSynchronize(t->wb);
   for (void* p : t->device_allocs) (void)hipFree(p);
   for (void* p : t->host_allocs) (void)hipHostFree(p);
   if (t->d_ops) (void)hipFree(t->d_ops);
   if (t->h_ops) (void)hipHostFree(t->h_ops);
   if (t->h_pack_in) (void)hipHostFree(t->h_pack_in);
+  if (t->h_pack_out) (void)hipHostFree(t->h_pack_out);
+  for (void* p : {t->pack_out_k, t->pack_out_v, t->pack_in_k, t->pack_in_v})
+    if (p) (void)hipFree(p);
+  t->pack_out_k = t->pack_out_v = t->pack_in_k = t->pack_in_v = nullptr;
+  t->h_pack_out = nullptr;
+  if (t->ev_pack) (void)hipEventDestroy(t->ev_pack);
+  t->ev_pack = nullptr;
   for (hipEvent_t e : t->ev_h2d) (void)hipEventDestroy(e);
   for (hipEvent_t e : t->ev_comp) (void)hipEventDestroy(e);
   if (t->ev_arena) (void)hipEventDestroy(t->ev_arena);
   if (t->side) (void)hipStreamDestroy(t->side);
+  if (t->wb) (void)hipStreamDestroy(t->wb);
+  if (t->ev_gathered) (void)hipEventDestroy(t->ev_gathered);
+  t->wb = nullptr;
+  t->ev_gathered = nullptr;
   t->d_ops = t->h_ops = t->h_pack_in = nullptr;
   t->ev_h2d.clear();
   t->ev_comp.clear();
@@ -172,6 +185,8 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_counts, B * 2 * 4);
   if (rc == TKV_OK) {
     hipError_t e = hipStreamCreateWithFlags(&t->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&t->wb, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_gathered, hipEventDisableTiming);
     t->ev_h2d.assign(t->S, nullptr);
     t->ev_comp.assign(t->S, nullptr);
     t->comp_recorded.assign(t->S, 0);
@@ -180,6 +195,7 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
       if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_comp[i], hipEventDisableTiming);
     }
     if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_arena, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_pack, hipEventDisableTiming);
     if (e != hipSuccess) rc = tkv_fail(t, TKV_EHIP, "creating streams/events: %s", hipGetErrorString(e));
   }
   if (rc == TKV_OK) {
@@ -266,7 +282,8 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
   // mode, whose staging holds only S layers) a temporary [L][B][cap1] area.
   void* tmp_k = nullptr;
   void* tmp_v = nullptr;
-  size_t src_pitch = (size_t)t->capS * t->row_bytes;
+  const size_t hb = (size_t)t->D * t->esz;  // bytes of one head's row
+  size_t src_pitch = (size_t)t->capS * hb;
   if (!t->resident && nt1 > 0) {
     const size_t bytes = (size_t)t->L * t->B * t->cap1 * t->row_bytes;
     HIP_TRY(t, hipMallocAsync(&tmp_k, bytes, st));
@@ -274,27 +291,29 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
     pa.rows.stage_k = tmp_k;
     pa.rows.stage_v = tmp_v;
     pa.rows.stage_slots = t->L;
-    pa.rows.stage_bstride = (int64_t)t->cap1 * t->row_elems;
+    pa.rows.stage_hstride = (int64_t)t->cap1 * t->D;
+    pa.rows.stage_bstride = pa.rows.stage_hstride * t->Hkv;
     pa.rows.stage_lstride = pa.rows.stage_bstride * t->B;
-    src_pitch = (size_t)t->cap1 * t->row_bytes;
+    src_pitch = (size_t)t->cap1 * hb;
   }
   pa.k = k;
   pa.v = v;
   pa.codes = (const uint32_t*)d_codes;
-  pa.row_bytes = t->row_bytes;
   pa.batch = t->B;
   pa.n_tokens = n0;
+  pa.kv_heads = t->Hkv;
+  pa.head_bytes = (int32_t)hb;
   pa.elem_bytes = t->esz;
   HIP_TRY(t, launch_place_rows(pa, t->L, st));
   // T1 rows also go to their home in pinned host memory
   if (nt1 > 0) {
-    const size_t width = (size_t)nt1 * t->row_bytes;
+    const size_t width = (size_t)nt1 * hb;
     for (int which = 0; which < 2; ++which) {
-      HIP_TRY(t, hipMemcpy2DAsync(which ? t->arena1_v : t->arena1_k, (size_t)t->cap1 * t->row_bytes,
+      HIP_TRY(t, hipMemcpy2DAsync(which ? t->arena1_v : t->arena1_k, (size_t)t->cap1 * hb,
                                   which ? pa.rows.stage_v : pa.rows.stage_k, src_pitch, width,
-                                  (size_t)t->L * t->B, hipMemcpyDeviceToHost, st));
+                                  (size_t)t->L * t->B * t->Hkv, hipMemcpyDeviceToHost, st));
     }
-    t->st.d2h_bytes += 2 * (int64_t)width * t->L * t->B;
+    t->st.d2h_bytes += 2 * (int64_t)width * t->L * t->B * t->Hkv;
   }
   if (tmp_k) HIP_TRY(t, hipFreeAsync(tmp_k, st));
   if (tmp_v) HIP_TRY(t, hipFreeAsync(tmp_v, st));
@@ -412,6 +431,9 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
     int rc = record_event(t, &e1, st);
     if (rc) return rc;
     t->ev_pending.emplace_back(e0, e1);
+    int64_t rows = 0;
+    for (int b = 0; b < t->B; ++b) rows += t->nlive[b];
+    t->st.attn_kv_bytes += rows * lc * 2 * t->row_bytes;
   }
   FinalizeArgs f{};
   f.logits = t->logits;
@@ -435,6 +457,10 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
 // slot (layer mod S) on the side stream, up to layer `upto`, each after the
 // attention that last read that slot.
 static int issue_prefetch(tkv* t, int upto) {
+  if (t->arena_job.valid()) {
+    const int rc = t->arena_job.get();
+    if (rc) return rc;
+  }
   if (t->arena_pending) {
     HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_arena, 0));
     t->arena_pending = false;
@@ -445,14 +471,15 @@ static int issue_prefetch(tkv* t, int upto) {
     const int x = t->next_issue, slot = x % t->S;
     if (t->comp_recorded[slot]) HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_comp[slot], 0));
     if (n1max > 0) {
-      const size_t width = n1max * t->row_bytes;
+      const size_t hb = (size_t)t->D * t->esz;
+      const size_t width = n1max * hb;
       for (int which = 0; which < 2; ++which) {
         char* dst = (char*)(which ? t->stage_v : t->stage_k) + (size_t)slot * t->B * t->capS * t->row_bytes;
         const char* src = (const char*)(which ? t->arena1_v : t->arena1_k) + (size_t)x * t->B * t->cap1 * t->row_bytes;
-        HIP_TRY(t, hipMemcpy2DAsync(dst, (size_t)t->capS * t->row_bytes, src, (size_t)t->cap1 * t->row_bytes, width,
-                                    t->B, hipMemcpyHostToDevice, t->side));
+        HIP_TRY(t, hipMemcpy2DAsync(dst, (size_t)t->capS * hb, src, (size_t)t->cap1 * hb, width,
+                                    (size_t)t->B * t->Hkv, hipMemcpyHostToDevice, t->side));
       }
-      t->st.h2d_bytes += 2 * (int64_t)width * t->B;
+      t->st.h2d_bytes += 2 * (int64_t)width * t->B * t->Hkv;
     }
     HIP_TRY(t, hipEventRecord(t->ev_h2d[slot], t->side));
   }
@@ -511,7 +538,12 @@ extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_coun
 
 extern "C" int tkv_stats(tkv_t* t, tkv_stats_t* out) {
   if (!t || !out) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (t->arena_job.valid()) {
+    const int rc = t->arena_job.get();
+    if (rc) return rc;
+  }
   HIP_TRY(t, hipStreamSynchronize(t->side));
+  HIP_TRY(t, hipStreamSynchronize(t->wb));
   int rc = drain_events(t);
   if (rc) return rc;
   t->st.step = t->step;

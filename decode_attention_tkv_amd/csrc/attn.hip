@@ -91,13 +91,17 @@ __global__ __launch_bounds__(256) void k_append(const AppendArgs a) {
   const int b = lb % a.batch;
   const int l = lb / a.batch;
   const int which = blockIdx.y;
-  const int64_t row_bytes = (int64_t)a.kv_heads * a.head_dim * a.elem_bytes;
+  const int head_bytes = a.head_dim * a.elem_bytes;
+  const int row_bytes = a.kv_heads * head_bytes;
   const char* src = (const char*)(which ? a.v : a.k) + (int64_t)lb * row_bytes;
   char* dst = (char*)(which ? a.rows.pool_v : a.rows.pool_k) +
               ((int64_t)l * a.rows.pool_lstride + (int64_t)b * a.rows.pool_bstride) * a.elem_bytes +
-              (int64_t)a.slot[b] * row_bytes;
-  for (int64_t off = (int64_t)threadIdx.x * 16; off < row_bytes; off += 256 * 16)
-    *reinterpret_cast<uint4*>(dst + off) = load16(src + off);
+              (int64_t)a.slot[b] * head_bytes;
+  const int64_t hstride = a.rows.pool_hstride * a.elem_bytes;
+  for (int off = threadIdx.x * 16; off < row_bytes; off += 256 * 16) {
+    const int h = off / head_bytes, w = off % head_bytes;
+    *reinterpret_cast<uint4*>(dst + h * hstride + w) = load16(src + off);
+  }
   if (l == 0 && which == 0 && threadIdx.x == 0) {
     const int64_t j = (int64_t)b * a.nmax + a.nlive[b];
     const int64_t p = (int64_t)b * a.nmax + a.pos;
@@ -137,11 +141,11 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   if (j0 >= nl) return;
   const int nrows = min(CHUNK, nl - j0);
 
-  const int64_t rs = (int64_t)a.kv_heads * D;  // elements between consecutive rows
+  constexpr int64_t rs = D;  // elements between consecutive rows of one kv head
   const int64_t poff = (int64_t)l * a.rows.pool_lstride + (int64_t)b * a.rows.pool_bstride +
-                       (int64_t)kvh * D + part * EPL;
+                       (int64_t)kvh * a.rows.pool_hstride + part * EPL;
   const int64_t soff = (int64_t)(l % a.rows.stage_slots) * a.rows.stage_lstride +
-                       (int64_t)b * a.rows.stage_bstride + (int64_t)kvh * D + part * EPL;
+                       (int64_t)b * a.rows.stage_bstride + (int64_t)kvh * a.rows.stage_hstride + part * EPL;
   const T* poolK = (const T*)a.rows.pool_k + poff;
   const T* poolV = (const T*)a.rows.pool_v + poff;
   const T* stageK = (const T*)a.rows.stage_k + soff;
@@ -302,8 +306,10 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
   for (int h = tid; h < a.q_heads; h += 256) {
     const float* ml = a.part_ml + (hbase + h) * a.max_chunks * 2;
     float M = -INFINITY;
+#pragma unroll 8
     for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[2 * c]);
     float L = 0.f;
+#pragma unroll 8
     for (int c = 0; c < nch; ++c) L += ml[2 * c + 1] * exp2f(ml[2 * c] - M);
     Ms[h] = M;
     iLs[h] = 1.f / L;
@@ -316,6 +322,7 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
     const float* po = a.part_o + (hbase + h) * a.max_chunks * D;
     for (int e = tid; e < D; e += 256) {
       float acc = 0.f;
+#pragma unroll 8
       for (int c = 0; c < nch; ++c) acc += po[(int64_t)c * D + e] * exp2f(ml[2 * c] - Ms[h]);
       a.out[(((int64_t)ll * a.batch + b) * a.q_heads + h) * D + e] = acc * iLs[h];
     }
@@ -325,6 +332,7 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
   if (j < nl) {
     float S = 0.f;
     const float* lg = a.logits + hbase * a.nmax + j;
+#pragma unroll 8
     for (int h = 0; h < a.q_heads; ++h) S += exp2f(lg[(int64_t)h * a.nmax] - Ms[h]) * iLs[h];
     a.layer_score[((int64_t)l * a.batch + b) * a.nmax + j] = S;
   }
@@ -336,6 +344,7 @@ __global__ __launch_bounds__(256) void k_score(const ScoreArgs a) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= a.nlive[b]) return;
   float acc = 0.f;
+#pragma unroll 8
   for (int l = 0; l < a.layers; ++l) acc += a.layer_score[((int64_t)l * a.batch + b) * a.nmax + j];
   const int64_t p = (int64_t)b * a.nmax + a.live_pos[(int64_t)b * a.nmax + j];
   a.s[p] += acc * a.inv_lh;

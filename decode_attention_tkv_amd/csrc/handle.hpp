@@ -3,6 +3,8 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <functional>
+#include <future>
 #include <string>
 #include <vector>
 
@@ -22,9 +24,9 @@ struct tkv {
   int64_t row_elems = 0, row_bytes = 0;
 
   // ---- device buffers (owned)
-  void* pool_k = nullptr;  // [L][B][cap0][Hkv][D]
+  void* pool_k = nullptr;  // [L][B][Hkv][cap0][D]
   void* pool_v = nullptr;
-  void* stage_k = nullptr;  // [S][B][capS][Hkv][D]
+  void* stage_k = nullptr;  // [S][B][Hkv][capS][D]
   void* stage_v = nullptr;
   uint32_t* live_loc = nullptr;  // [B][nmax]
   int32_t* live_pos = nullptr;   // [B][nmax]
@@ -48,9 +50,18 @@ struct tkv {
   size_t h_ops_bytes = 0;
   void* h_pack_in = nullptr;  // pinned: promoted T1 rows packed on the host (stream mode)
   size_t h_pack_in_bytes = 0;
+  void* h_pack_out = nullptr;  // pinned: rows entering T1, [2][L][Hkv][E][D]
+  size_t h_pack_out_bytes = 0;
+  void* pack_out_k = nullptr;  // device packs [L][Hkv][rows][D], persistent, grown on demand
+  void* pack_out_v = nullptr;
+  void* pack_in_k = nullptr;
+  void* pack_in_v = nullptr;
+  size_t pack_out_cap = 0, pack_in_cap = 0;  // rows
+  hipEvent_t ev_pack = nullptr;              // entrant rows landed in h_pack_out
+  std::future<int> arena_job;                // host arena maintenance of the last reassignment
 
   // ---- pinned host arenas (owned)
-  void* arena1_k = nullptr;  // [L][B][cap1][Hkv][D]: T1 rows, dense per (layer, seq)
+  void* arena1_k = nullptr;  // [L][B][Hkv][cap1][D]: T1 rows, dense per (layer, seq, head)
   void* arena1_v = nullptr;
   std::vector<void*> host_allocs;
 
@@ -71,7 +82,9 @@ struct tkv {
   int32_t* h_counts = nullptr;     // [B][2]
 
   // ---- streams and events
-  hipStream_t side = nullptr;           // host<->device row traffic of the stream mode
+  hipStream_t side = nullptr;           // host->device row traffic of the stream mode
+  hipStream_t wb = nullptr;             // device->host write-back of rows entering T1
+  hipEvent_t ev_gathered = nullptr;     // rows entering T1 are in the device pack
   std::vector<hipEvent_t> ev_h2d;       // [S] staging slot filled
   std::vector<hipEvent_t> ev_comp;      // [S] attention done reading the slot
   std::vector<char> comp_recorded;      // [S]
@@ -92,9 +105,11 @@ struct tkv {
     r.pool_v = pool_v;
     r.stage_k = stage_k;
     r.stage_v = stage_v;
-    r.pool_bstride = (int64_t)cap0 * row_elems;
+    r.pool_hstride = (int64_t)cap0 * D;
+    r.pool_bstride = r.pool_hstride * Hkv;
     r.pool_lstride = r.pool_bstride * B;
-    r.stage_bstride = (int64_t)capS * row_elems;
+    r.stage_hstride = (int64_t)capS * D;
+    r.stage_bstride = r.stage_hstride * Hkv;
     r.stage_lstride = r.stage_bstride * B;
     r.cap0 = cap0;
     r.stage_slots = S;

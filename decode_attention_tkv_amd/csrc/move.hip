@@ -7,21 +7,19 @@
 namespace tkvd {
 namespace {
 
-__device__ __forceinline__ char* row_addr(const RowSpace& rs, int which, int l, int b, uint32_t code,
-                                          int64_t row_bytes, int elem_bytes) {
+__device__ __forceinline__ char* head_row(const RowSpace& rs, int which, int l, int b, int h, uint32_t code,
+                                          int head_bytes, int elem_bytes) {
   if (code < (uint32_t)rs.cap0) {
     char* base = (char*)(which ? rs.pool_v : rs.pool_k);
-    return base + ((int64_t)l * rs.pool_lstride + (int64_t)b * rs.pool_bstride) * elem_bytes +
-           (int64_t)code * row_bytes;
+    return base + ((int64_t)l * rs.pool_lstride + (int64_t)b * rs.pool_bstride + (int64_t)h * rs.pool_hstride) *
+                      elem_bytes +
+           (int64_t)code * head_bytes;
   }
   char* base = (char*)(which ? rs.stage_v : rs.stage_k);
-  return base + ((int64_t)(l % rs.stage_slots) * rs.stage_lstride + (int64_t)b * rs.stage_bstride) * elem_bytes +
-         (int64_t)(code - rs.cap0) * row_bytes;
-}
-
-__device__ __forceinline__ void copy_row(char* dst, const char* src, int64_t row_bytes) {
-  for (int64_t off = (int64_t)threadIdx.x * 16; off < row_bytes; off += (int64_t)blockDim.x * 16)
-    *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(src + off);
+  return base + ((int64_t)(l % rs.stage_slots) * rs.stage_lstride + (int64_t)b * rs.stage_bstride +
+                 (int64_t)h * rs.stage_hstride) *
+                    elem_bytes +
+         (int64_t)(code - rs.cap0) * head_bytes;
 }
 
 // grid (n_tokens, layers*batch, 2): input row (l, b, p) -> its location code.
@@ -32,8 +30,13 @@ __global__ __launch_bounds__(256) void k_place_rows(const PlaceArgs a) {
   const int which = blockIdx.z;
   const uint32_t code = a.codes[(int64_t)b * a.n_tokens + p];
   if (code == kNoLoc) return;
-  const char* src = (const char*)(which ? a.v : a.k) + (((int64_t)lb * a.n_tokens) + p) * a.row_bytes;
-  copy_row(row_addr(a.rows, which, l, b, code, a.row_bytes, a.elem_bytes), src, a.row_bytes);
+  const int row_bytes = a.kv_heads * a.head_bytes;
+  const char* src = (const char*)(which ? a.v : a.k) + (((int64_t)lb * a.n_tokens) + p) * row_bytes;
+  for (int off = threadIdx.x * 16; off < row_bytes; off += 256 * 16) {
+    const int h = off / a.head_bytes, w = off % a.head_bytes;
+    char* dst = head_row(a.rows, which, l, b, h, code, a.head_bytes, a.elem_bytes);
+    *reinterpret_cast<uint4*>(dst + w) = *reinterpret_cast<const uint4*>(src + off);
+  }
 }
 
 }  // namespace

@@ -12,10 +12,14 @@
 // Rows move in three dependent phases of one copy kernel: (1) rows that
 // leave their home are gathered into pack buffers, (2a) arena compaction in
 // the staging mirror and promotions into T0 slots, (2b) entrants into the
-// staging mirror.  Entrants reach the pinned arena with one 2-D copy per
-// (sequence, K|V).  In stream mode promoted rows come from the host arena.
+// staging mirror.  Entrants leave the GPU as one contiguous copy per K|V into
+// a pinned pack; a host job (never waited for by the GPU) compacts the
+// pinned arena and files the entrants.  In stream mode promoted rows come
+// from the host arena.  Every area is head-major, [..][kv_head][row][d].
 #include <chrono>
 #include <cstring>
+#include <memory>
+#include <thread>
 
 #include "handle.hpp"
 #include "host_util.hpp"
@@ -54,6 +58,29 @@ int grow_pinned(tkv* t, void** p, size_t* cap, size_t need) {
   return TKV_OK;
 }
 
+int grow_packs(tkv* t, int64_t E, int64_t P) {
+  const size_t lrb = (size_t)t->L * t->row_bytes;
+  if ((size_t)E > t->pack_out_cap) {
+    const size_t rows = std::max<size_t>((size_t)E * 2, 64);
+    for (void** p : {&t->pack_out_k, &t->pack_out_v}) {
+      if (*p) HIP_TRY(t, hipFree(*p));
+      *p = nullptr;
+      HIP_TRY(t, hipMalloc(p, rows * lrb));
+    }
+    t->pack_out_cap = rows;
+  }
+  if ((size_t)P > t->pack_in_cap) {
+    const size_t rows = std::max<size_t>((size_t)P * 2, 64);
+    for (void** p : {&t->pack_in_k, &t->pack_in_v}) {
+      if (*p) HIP_TRY(t, hipFree(*p));
+      *p = nullptr;
+      HIP_TRY(t, hipMalloc(p, rows * lrb));
+    }
+    t->pack_in_cap = rows;
+  }
+  return TKV_OK;
+}
+
 }  // namespace
 
 extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
@@ -65,7 +92,11 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   const int B = t->B, L = t->L, n = t->n;
   const size_t nmax = t->nmax;
   // The host arena and the pinned staging buffers may still be read or
-  // written by copies of the previous step / reassignment.
+  // written by the previous reassignment's host job and copies.
+  if (t->arena_job.valid()) {
+    const int rc = t->arena_job.get();
+    if (rc) return rc;
+  }
   HIP_TRY(t, hipStreamSynchronize(t->side));
   HIP_TRY(t, hipEventSynchronize(t->ev_arena));
 
@@ -213,8 +244,10 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
 
   // ---- host arena: promoted rows out first (stream mode), then compaction
   const size_t rb = t->row_bytes;
-  auto arena_row = [&](int which, int l, int b, uint32_t idx) -> char* {
-    return (char*)(which ? t->arena1_v : t->arena1_k) + (((size_t)l * B + b) * t->cap1 + idx) * rb;
+  const size_t hb = (size_t)t->D * t->esz;
+  const int H = t->Hkv;
+  auto arena_row = [&](int which, int l, int b, int h, uint32_t idx) -> char* {
+    return (char*)(which ? t->arena1_v : t->arena1_k) + ((((size_t)l * B + b) * H + h) * t->cap1 + idx) * hb;
   };
   if (!t->resident && P > 0) {
     int rc = grow_pinned(t, &t->h_pack_in, &t->h_pack_in_bytes, 2 * (size_t)L * P * rb);
@@ -223,13 +256,10 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
       for (size_t p = 0; p < plan[b].promo_idx.size(); ++p)
         for (int which = 0; which < 2; ++which)
           for (int l = 0; l < L; ++l)
-            std::memcpy((char*)t->h_pack_in + (((size_t)which * L + l) * P + plan[b].poff + p) * rb,
-                        arena_row(which, l, b, plan[b].promo_idx[p]), rb);
+            for (int h = 0; h < H; ++h)
+              std::memcpy((char*)t->h_pack_in + ((((size_t)which * L + l) * H + h) * P + plan[b].poff + p) * hb,
+                          arena_row(which, l, b, h, plan[b].promo_idx[p]), hb);
   }
-  for (int b = 0; b < B; ++b)
-    for (auto& mv : plan[b].movers)
-      for (int which = 0; which < 2; ++which)
-        for (int l = 0; l < L; ++l) std::memcpy(arena_row(which, l, b, mv.second), arena_row(which, l, b, mv.first), rb);
 
   // ---- row-copy ops
   std::vector<RowOp> ops1, ops2a, ops2b;
@@ -267,19 +297,21 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
 
   CopyArgs ca{};
   ca.rows = t->rowspace();
-  ca.row_bytes = (int64_t)rb;
+  ca.kv_heads = H;
+  ca.head_bytes = (int32_t)hb;
   ca.elem_bytes = t->esz;
   ca.pack_out_rows = E;
   ca.pack_in_rows = P;
-  if (E > 0) {
-    HIP_TRY(t, hipMallocAsync(&ca.pack_out_k, (size_t)L * E * rb, st));
-    HIP_TRY(t, hipMallocAsync(&ca.pack_out_v, (size_t)L * E * rb, st));
+  {
+    int rc = grow_packs(t, E, P);
+    if (rc) return rc;
   }
-  if (P > 0) {
-    HIP_TRY(t, hipMallocAsync(&ca.pack_in_k, (size_t)L * P * rb, st));
-    HIP_TRY(t, hipMallocAsync(&ca.pack_in_v, (size_t)L * P * rb, st));
-  }
+  ca.pack_out_k = t->pack_out_k;
+  ca.pack_out_v = t->pack_out_v;
+  ca.pack_in_k = t->pack_in_k;
+  ca.pack_in_v = t->pack_in_v;
   HIP_TRY(t, launch_copy_rows(ca, d_ops1, (int)ops1.size(), L, st));
+  HIP_TRY(t, hipEventRecord(t->ev_gathered, st));
   if (!t->resident && P > 0) {
     HIP_TRY(t, hipMemcpyAsync(ca.pack_in_k, t->h_pack_in, (size_t)L * P * rb, hipMemcpyHostToDevice, st));
     HIP_TRY(t, hipMemcpyAsync(ca.pack_in_v, (char*)t->h_pack_in + (size_t)L * P * rb, (size_t)L * P * rb,
@@ -297,25 +329,77 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   la.nmax = t->nmax;
   la.n = n;
   HIP_TRY(t, launch_build_live(la, B, st));
-  // entrants to their home in pinned host memory: one 2-D copy per (sequence, K|V)
-  for (int b = 0; b < B; ++b) {
-    const SeqPlan& sp = plan[b];
-    const size_t ne = sp.entrant_pos.size();
-    if (!ne) continue;
-    for (int which = 0; which < 2; ++which) {
-      char* dst = arena_row(which, 0, b, sp.m);
-      const char* src = (const char*)(which ? ca.pack_out_v : ca.pack_out_k) + sp.eoff * rb;
-      HIP_TRY(t, hipMemcpy2DAsync(dst, (size_t)B * t->cap1 * rb, src, (size_t)E * rb, ne * rb, L,
-                                  hipMemcpyDeviceToHost, st));
-    }
+  // entrants leave the GPU as one contiguous copy per K|V into a pinned pack;
+  // a host job then compacts the arena and files the entrants at [m, m + E_b)
+  if (E > 0) {
+    int rc = grow_pinned(t, &t->h_pack_out, &t->h_pack_out_bytes, 2 * (size_t)L * E * rb);
+    if (rc) return rc;
+    // on the write-back stream, so the decode steps that follow do not wait for it
+    HIP_TRY(t, hipStreamWaitEvent(t->wb, t->ev_gathered, 0));
+    HIP_TRY(t, hipMemcpyAsync(t->h_pack_out, t->pack_out_k, (size_t)L * E * rb, hipMemcpyDeviceToHost, t->wb));
+    HIP_TRY(t, hipMemcpyAsync((char*)t->h_pack_out + (size_t)L * E * rb, t->pack_out_v, (size_t)L * E * rb,
+                              hipMemcpyDeviceToHost, t->wb));
+    t->st.d2h_bytes += 2 * (int64_t)L * E * rb;
   }
-  t->st.d2h_bytes += 2 * (int64_t)L * E * rb;
-  if (ca.pack_out_k) HIP_TRY(t, hipFreeAsync(ca.pack_out_k, st));
-  if (ca.pack_out_v) HIP_TRY(t, hipFreeAsync(ca.pack_out_v, st));
-  if (ca.pack_in_k) HIP_TRY(t, hipFreeAsync(ca.pack_in_k, st));
-  if (ca.pack_in_v) HIP_TRY(t, hipFreeAsync(ca.pack_in_v, st));
+  HIP_TRY(t, hipEventRecord(t->ev_pack, t->wb));
   HIP_TRY(t, hipEventRecord(t->ev_arena, st));
   t->arena_pending = true;
+  bool any_host_work = E > 0;
+  for (int b = 0; b < B && !any_host_work; ++b) any_host_work = !plan[b].movers.empty();
+  if (any_host_work) {
+    struct Job {
+      std::vector<SeqPlan> plan;
+      char* ak;
+      char* av;
+      const char* pack;
+      hipEvent_t ev;
+      int L, B, H;
+      size_t cap1, hb;
+      int64_t E;
+    };
+    auto job = std::make_shared<Job>(Job{std::move(plan), (char*)t->arena1_k, (char*)t->arena1_v,
+                                         (const char*)t->h_pack_out, t->ev_pack, L, B, H, (size_t)t->cap1, hb, E});
+    t->arena_job = std::async(std::launch::async, [job]() -> int {
+      const Job& j = *job;
+      auto row = [&](int which, int l, int b, int h, uint32_t idx) -> char* {
+        return (which ? j.av : j.ak) + ((((size_t)l * j.B + b) * j.H + h) * j.cap1 + idx) * j.hb;
+      };
+      // layers split over a few threads; each layer's rows are independent
+      auto work = [&](int l0, int l1) {
+        for (int l = l0; l < l1; ++l)
+          for (int b = 0; b < j.B; ++b)
+            for (auto& mv : j.plan[b].movers)
+              for (int which = 0; which < 2; ++which)
+                for (int h = 0; h < j.H; ++h)
+                  std::memcpy(row(which, l, b, h, mv.second), row(which, l, b, h, mv.first), j.hb);
+      };
+      // pack_out is [K|V][layer][kv head][entrant][head_dim]
+      auto file = [&](int l0, int l1) {
+        for (int l = l0; l < l1; ++l)
+          for (int b = 0; b < j.B; ++b) {
+            const size_t ne = j.plan[b].entrant_pos.size();
+            if (!ne) continue;
+            for (int which = 0; which < 2; ++which)
+              for (int h = 0; h < j.H; ++h)
+                std::memcpy(row(which, l, b, h, j.plan[b].m),
+                            j.pack + ((((size_t)which * j.L + l) * j.H + h) * j.E + j.plan[b].eoff) * j.hb, ne * j.hb);
+          }
+      };
+      const int nth = std::min(4, j.L);
+      auto split = [&](const std::function<void(int, int)>& f) {
+        std::vector<std::thread> th;
+        for (int i = 1; i < nth; ++i) th.emplace_back(f, j.L * i / nth, j.L * (i + 1) / nth);
+        f(0, j.L / nth);
+        for (auto& x : th) x.join();
+      };
+      split(work);
+      if (j.E > 0) {
+        if (hipEventSynchronize(j.ev) != hipSuccess) return TKV_EHIP;
+        split(file);
+      }
+      return TKV_OK;
+    });
+  }
 
   t->st.promotions += n_prom;
   t->st.demotions += n_dem;

@@ -51,16 +51,35 @@ __global__ __launch_bounds__(kBlock) void k_rank_label(const RankArgs a) {
         if (want[k] < ncand && (key & mask) == prefix[k]) atomicAdd(&hist[k][digit], 1u);
     }
     __syncthreads();
-    if (tid < 3 && want[tid] < ncand) {
-      uint32_t cum = 0;
-      for (int d = 0; d < 256; ++d) {
-        const uint32_t c = hist[tid][d];
-        if ((uint32_t)want[tid] < cum + c) {
-          prefix[tid] |= (uint64_t)d << shift;
-          want[tid] -= (int32_t)cum;
-          break;
+    // digit of each cut: wave k scans the 256 bins of select k, 4 bins per lane
+    const int wv = tid >> 6, lane = tid & 63;
+    if (wv < 3) {
+      const int r = want[wv];
+      if (r < ncand) {
+        uint32_t c[4], sum4 = 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          c[d] = hist[wv][4 * lane + d];
+          sum4 += c[d];
         }
-        cum += c;
+        uint32_t incl = sum4;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_up(incl, off);
+          if (lane >= off) incl += y;
+        }
+        uint32_t cum = incl - sum4;
+        if ((uint32_t)r >= cum && (uint32_t)r < incl) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            if ((uint32_t)r < cum + c[d]) {
+              prefix[wv] |= (uint64_t)(4 * lane + d) << shift;
+              want[wv] = r - (int)cum;
+              break;
+            }
+            cum += c[d];
+          }
+        }
       }
     }
     mask |= (uint64_t)255u << shift;
@@ -176,39 +195,45 @@ __global__ __launch_bounds__(kBlock) void k_build_live(const LiveArgs a) {
   }
 }
 
-__device__ __forceinline__ char* area_row(const CopyArgs& a, int area, int which, int l, int b, uint32_t idx) {
+__device__ __forceinline__ char* area_row(const CopyArgs& a, int area, int which, int l, int b, int h, uint32_t idx) {
   const RowSpace& rs = a.rows;
   switch (area) {
     case kAreaPool: {
       char* base = (char*)(which ? rs.pool_v : rs.pool_k);
-      return base + ((int64_t)l * rs.pool_lstride + (int64_t)b * rs.pool_bstride) * a.elem_bytes +
-             (int64_t)idx * a.row_bytes;
+      return base + ((int64_t)l * rs.pool_lstride + (int64_t)b * rs.pool_bstride + (int64_t)h * rs.pool_hstride) *
+                        a.elem_bytes +
+             (int64_t)idx * a.head_bytes;
     }
     case kAreaStage: {
       char* base = (char*)(which ? rs.stage_v : rs.stage_k);
-      return base + ((int64_t)(l % rs.stage_slots) * rs.stage_lstride + (int64_t)b * rs.stage_bstride) * a.elem_bytes +
-             (int64_t)idx * a.row_bytes;
+      return base + ((int64_t)(l % rs.stage_slots) * rs.stage_lstride + (int64_t)b * rs.stage_bstride +
+                     (int64_t)h * rs.stage_hstride) *
+                        a.elem_bytes +
+             (int64_t)idx * a.head_bytes;
     }
     case kAreaPackOut: {
       char* base = (char*)(which ? a.pack_out_v : a.pack_out_k);
-      return base + ((int64_t)l * a.pack_out_rows + idx) * a.row_bytes;
+      return base + (((int64_t)l * a.kv_heads + h) * a.pack_out_rows + idx) * a.head_bytes;
     }
     default: {
       char* base = (char*)(which ? a.pack_in_v : a.pack_in_k);
-      return base + ((int64_t)l * a.pack_in_rows + idx) * a.row_bytes;
+      return base + (((int64_t)l * a.kv_heads + h) * a.pack_in_rows + idx) * a.head_bytes;
     }
   }
 }
 
-// One op = one row of one sequence copied in every layer, K and V.
-// grid (n_ops, layers, 2), block 256.
+// One op = one position of one sequence copied in every layer and kv head,
+// K and V.  grid (n_ops, layers, 2), block 256.
 __global__ __launch_bounds__(256) void k_copy_rows(const CopyArgs a, const RowOp* ops) {
   const RowOp op = ops[blockIdx.x];
   const int l = blockIdx.y, which = blockIdx.z;
-  const char* src = area_row(a, op.src_area, which, l, op.b, op.src);
-  char* dst = area_row(a, op.dst_area, which, l, op.b, op.dst);
-  for (int64_t off = (int64_t)threadIdx.x * 16; off < a.row_bytes; off += 256 * 16)
-    *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(src + off);
+  const int row_bytes = a.kv_heads * a.head_bytes;
+  for (int off = threadIdx.x * 16; off < row_bytes; off += 256 * 16) {
+    const int h = off / a.head_bytes, w = off % a.head_bytes;
+    const char* src = area_row(a, op.src_area, which, l, op.b, h, op.src);
+    char* dst = area_row(a, op.dst_area, which, l, op.b, h, op.dst);
+    *reinterpret_cast<uint4*>(dst + w) = *reinterpret_cast<const uint4*>(src + w);
+  }
 }
 
 }  // namespace

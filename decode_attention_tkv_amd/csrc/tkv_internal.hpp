@@ -20,16 +20,18 @@ constexpr uint8_t kUnused = 255;           // tier code of positions not appende
 
 // ---- kernel argument blocks (passed by value) ------------------------------
 
-// Where the K/V rows of one layer live.  A live row's location code `loc` is
+// Where the K/V rows live.  Every area is head-major:
+// [..][batch][kv_heads][cap][head_dim], so the rows of one kv head are
+// contiguous (head_dim elements apart).  A live row's location code `loc` is
 // a T0 pool slot when loc < cap0, else index (loc - cap0) of the staging area
-// of slot (layer % stage_slots).  Both areas are [..][batch][cap][kv_heads][head_dim].
+// of slot (layer % stage_slots).
 struct RowSpace {
   const void* pool_k;
   const void* pool_v;
   const void* stage_k;
   const void* stage_v;
-  int64_t pool_lstride, pool_bstride;    // elements per layer / per sequence of the pool
-  int64_t stage_lstride, stage_bstride;  // elements per slot / per sequence of the staging area
+  int64_t pool_lstride, pool_bstride, pool_hstride;     // elements per layer / sequence / kv head
+  int64_t stage_lstride, stage_bstride, stage_hstride;  // elements per slot / sequence / kv head
   int32_t cap0;
   int32_t stage_slots;
 };
@@ -86,8 +88,7 @@ struct PlaceArgs {
   const void* k;
   const void* v;
   const uint32_t* codes;
-  int64_t row_bytes;
-  int32_t batch, n_tokens, elem_bytes;
+  int32_t batch, n_tokens, kv_heads, head_bytes, elem_bytes;
 };
 
 // ---- reassignment (reassign.hip) ---------------------------------------------
@@ -123,7 +124,7 @@ struct LiveArgs {
   int32_t nmax, n;
 };
 
-// Row areas of a copy op.  Packs are [layers][rows][row].
+// Row areas of a copy op.  Packs are [layers][kv_heads][rows][head_dim].
 enum : uint8_t { kAreaPool = 0, kAreaStage = 1, kAreaPackOut = 2, kAreaPackIn = 3 };
 
 struct RowOp {
@@ -138,8 +139,8 @@ struct CopyArgs {
   void* pack_out_v;
   void* pack_in_k;
   void* pack_in_v;
-  int64_t pack_out_rows, pack_in_rows, row_bytes;
-  int32_t elem_bytes;
+  int64_t pack_out_rows, pack_in_rows;
+  int32_t kv_heads, head_bytes, elem_bytes;  // head_bytes = head_dim * elem_bytes
 };
 
 // ---- launchers (attn.hip) -------------------------------------------------

@@ -104,6 +104,8 @@ typedef struct {
   int64_t h2d_bytes, d2h_bytes; /* K/V rows moved host<->device since create */
   double attn_kernel_ms;     /* with TKV_FLAG_TIME_KERNELS: summed split-K kernel time */
   int64_t attn_kernel_launches;
+  int64_t attn_kv_bytes;     /* with TKV_FLAG_TIME_KERNELS: K/V bytes of the live rows those
+                                launches had to read (the algorithmic traffic) */
   double reassign_ms;        /* host wall time inside tkv_reassign */
 } tkv_stats_t;
 
