@@ -85,6 +85,8 @@ _SIGS = {
     "tkv_write_scores": [_vp, _vp, _vp],
     "tkv_read_tiers": [_vp, _vp, _vp],
     "tkv_read_deltas": [_vp, _vp, _vp, _vp],
+    "tkv_read_kv": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
+    "tkv_read_t2": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
 }
 
 
@@ -194,6 +196,21 @@ def tkv_read_deltas(h, batch, max_tokens):
     return promote, demote, counts
 
 
+def tkv_read_kv(h, layer, seq, pos, kv_heads, head_dim, np_dtype, stream=None):
+    k = np.empty((kv_heads, head_dim), np_dtype)
+    v = np.empty((kv_heads, head_dim), np_dtype)
+    _check(lib().tkv_read_kv(h, layer, seq, pos, k.ctypes.data, v.ctypes.data, _stream(stream)), h)
+    return k, v
+
+
+def tkv_read_t2(h, layer, seq, pos, kv_heads, head_dim):
+    kc = np.empty((kv_heads, head_dim), np.int8)
+    vc = np.empty((kv_heads, head_dim), np.int8)
+    sc = np.empty(2, np.float32)
+    _check(lib().tkv_read_t2(h, layer, seq, pos, kc.ctypes.data, vc.ctypes.data, sc.ctypes.data), h)
+    return kc, vc, sc
+
+
 # ---- a handle object over the same calls ---------------------------------------
 
 class TieredKV:
@@ -262,3 +279,11 @@ class TieredKV:
 
     def read_deltas(self):
         return tkv_read_deltas(self.h, self.B, self.nmax)
+
+    def read_kv(self, layer, seq, pos, stream=None):
+        """Values attention reads for a live row (bf16 bits as uint16, or fp32)."""
+        return tkv_read_kv(self.h, layer, seq, pos, self.Hkv, self.D,
+                           np.uint16 if self.dtype == "bf16" else np.float32, stream)
+
+    def read_t2(self, layer, seq, pos):
+        return tkv_read_t2(self.h, layer, seq, pos, self.Hkv, self.D)

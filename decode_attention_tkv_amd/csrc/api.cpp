@@ -57,12 +57,12 @@ static void release(tkv* t) {
   for (void* p : t->host_allocs) (void)hipHostFree(p);
   if (t->d_ops) (void)hipFree(t->d_ops);
   if (t->h_ops) (void)hipHostFree(t->h_ops);
-  if (t->h_pack_in) (void)hipHostFree(t->h_pack_in);
-  if (t->h_pack_out) (void)hipHostFree(t->h_pack_out);
-  for (void* p : {t->pack_out_k, t->pack_out_v, t->pack_in_k, t->pack_in_v})
+  for (void* p : {t->h_pack_in, t->h_pack_out, t->h_qout, t->h_qin})
+    if (p) (void)hipHostFree(p);
+  for (void* p : {t->fpack, t->fin, t->qin, t->qout})
     if (p) (void)hipFree(p);
-  t->pack_out_k = t->pack_out_v = t->pack_in_k = t->pack_in_v = nullptr;
-  t->h_pack_out = nullptr;
+  t->fpack = t->fin = t->qin = t->qout = nullptr;
+  t->h_pack_in = t->h_pack_out = t->h_qout = t->h_qin = nullptr;
   if (t->ev_pack) (void)hipEventDestroy(t->ev_pack);
   t->ev_pack = nullptr;
   for (hipEvent_t e : t->ev_h2d) (void)hipEventDestroy(e);
@@ -121,7 +121,6 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   if (o.staging_layers < 0 || o.staging_layers == 1)
     return tkv_fail(nullptr, TKV_EINVAL, "staging_layers must be 0 or >= 2");
   const bool resident = o.staging_layers == 0 || o.staging_layers >= s.layers;
-  if (o.t2_ratio > 0) return tkv_fail(nullptr, TKV_EINVAL, "the 8-bit host tier is not available yet");
 
   tkv* t = new tkv();
   t->L = s.layers;
@@ -180,6 +179,20 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   dev((void**)&t->d_counts, B * 2 * 4);
   if (rc == TKV_OK) rc = host_alloc(t, &t->arena1_k, L * B * t->cap1 * t->row_bytes);
   if (rc == TKV_OK) rc = host_alloc(t, &t->arena1_v, L * B * t->cap1 * t->row_bytes);
+  if (t->cap2 > 0) {
+    const size_t codes = L * B * t->Hkv * (size_t)t->cap2 * t->D;
+    if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->arena2_k, codes);
+    if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->arena2_v, codes);
+    if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->ascale_k, L * B * t->cap2 * 4);
+    if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->ascale_v, L * B * t->cap2 * 4);
+    if (!resident) {
+      const size_t qc = (size_t)t->S * B * t->Hkv * t->cap2 * t->D;
+      dev((void**)&t->qstage_k, qc);
+      dev((void**)&t->qstage_v, qc);
+      dev((void**)&t->qsscale_k, (size_t)t->S * B * t->cap2 * 4);
+      dev((void**)&t->qsscale_v, (size_t)t->S * B * t->cap2 * 4);
+    }
+  }
   if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_promote, B * nmax * sizeof(tkv_delta));
   if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_demote, B * nmax * sizeof(tkv_delta));
   if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_counts, B * 2 * 4);
@@ -221,9 +234,11 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   t->h_tier.assign(B * nmax, kUnused);
   t->h_loc.assign(B * nmax, kNoLoc);
   t->t1_owner.resize(B);
+  t->t2_owner.resize(B);
   std::memset(t->h_counts, 0, B * 2 * 4);
   t->st.hbm_bytes = (int64_t)(2 * L * B * t->cap0 + 2 * (size_t)t->S * B * t->capS) * t->row_bytes;
-  t->st.host_bytes = (int64_t)(2 * L * B * t->cap1) * t->row_bytes;
+  t->st.host_bytes = (int64_t)(2 * L * B * t->cap1) * t->row_bytes +
+                     (int64_t)(2 * L * B * t->cap2) * (t->Hkv * t->D + 4);
   t->st.full_cache_bytes = (int64_t)(2 * L * B * nmax) * t->row_bytes;
   *out = t;
   return TKV_OK;
@@ -465,8 +480,11 @@ static int issue_prefetch(tkv* t, int upto) {
     HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_arena, 0));
     t->arena_pending = false;
   }
-  size_t n1max = 0;
-  for (int b = 0; b < t->B; ++b) n1max = std::max(n1max, t->t1_owner[b].size());
+  size_t n1max = 0, n2max = 0;
+  for (int b = 0; b < t->B; ++b) {
+    n1max = std::max(n1max, t->t1_owner[b].size());
+    n2max = std::max(n2max, t->t2_owner[b].size());
+  }
   for (; t->next_issue <= upto && t->next_issue < t->L; ++t->next_issue) {
     const int x = t->next_issue, slot = x % t->S;
     if (t->comp_recorded[slot]) HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_comp[slot], 0));
@@ -480,6 +498,34 @@ static int issue_prefetch(tkv* t, int upto) {
                                     (size_t)t->B * t->Hkv, hipMemcpyHostToDevice, t->side));
       }
       t->st.h2d_bytes += 2 * (int64_t)width * t->B * t->Hkv;
+    }
+    if (n2max > 0) {
+      // 8-bit rows: codes and scales over PCIe, dequantised into the slot on the GPU
+      const size_t cw = n2max * t->D;
+      const size_t c_layer = (size_t)t->B * t->Hkv * t->cap2 * t->D;
+      const size_t s_layer = (size_t)t->B * t->cap2;
+      DequantStageArgs dq{};
+      dq.rows = t->rowspace();
+      for (int which = 0; which < 2; ++which) {
+        int8_t* qd = (which ? t->qstage_v : t->qstage_k) + (size_t)slot * c_layer;
+        float* sd = (which ? t->qsscale_v : t->qsscale_k) + (size_t)slot * s_layer;
+        HIP_TRY(t, hipMemcpy2DAsync(qd, (size_t)t->cap2 * t->D, (which ? t->arena2_v : t->arena2_k) + (size_t)x * c_layer,
+                                    (size_t)t->cap2 * t->D, cw, (size_t)t->B * t->Hkv, hipMemcpyHostToDevice, t->side));
+        HIP_TRY(t, hipMemcpy2DAsync(sd, (size_t)t->cap2 * 4, (which ? t->ascale_v : t->ascale_k) + (size_t)x * s_layer,
+                                    (size_t)t->cap2 * 4, n2max * 4, (size_t)t->B, hipMemcpyHostToDevice, t->side));
+        (which ? dq.codes_v : dq.codes_k) = qd;
+        (which ? dq.scale_v : dq.scale_k) = sd;
+      }
+      t->st.h2d_bytes += 2 * (int64_t)(cw * t->B * t->Hkv + n2max * 4 * t->B);
+      dq.layer = x;
+      dq.cap1 = t->cap1;
+      dq.cap2 = t->cap2;
+      dq.batch = t->B;
+      dq.kv_heads = t->Hkv;
+      dq.head_dim = t->D;
+      dq.elem_bytes = t->esz;
+      for (int b = 0; b < t->B; ++b) dq.n2[b] = (int32_t)t->t2_owner[b].size();
+      HIP_TRY(t, launch_dequant_stage(dq, (int)n2max, t->side));
     }
     HIP_TRY(t, hipEventRecord(t->ev_h2d[slot], t->side));
   }
@@ -586,5 +632,74 @@ extern "C" int tkv_read_deltas(tkv_t* t, tkv_delta* promote, tkv_delta* demote, 
   std::memcpy(promote, t->h_promote, nd * sizeof(tkv_delta));
   std::memcpy(demote, t->h_demote, nd * sizeof(tkv_delta));
   std::memcpy(counts, t->h_counts, (size_t)t->B * 2 * sizeof(int32_t));
+  return TKV_OK;
+}
+
+extern "C" int tkv_read_kv(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, void* k, void* v,
+                           tkv_stream_t stream) {
+  if (!t || !k || !v) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (layer < 0 || layer >= t->L || seq < 0 || seq >= t->B || pos < 0 || pos >= t->n)
+    return tkv_fail(t, TKV_EINVAL, "layer/seq/pos out of range");
+  if (t->arena_job.valid()) {
+    const int rc = t->arena_job.get();
+    if (rc) return rc;
+  }
+  const size_t at = (size_t)seq * t->nmax + pos;
+  const uint8_t tier = t->h_tier[at];
+  const uint32_t code = t->h_loc[at];
+  if (tier > TKV_T2) return tkv_fail(t, TKV_ESTATE, "position %d is not live", pos);
+  hipStream_t st = (hipStream_t)stream;
+  const size_t hb = (size_t)t->D * t->esz;
+  const RowSpace rs = t->rowspace();
+  if (tier == TKV_T0 || t->resident) {
+    for (int which = 0; which < 2; ++which) {
+      const char* base;
+      size_t hstride;
+      if (code < (uint32_t)t->cap0) {
+        base = (const char*)(which ? t->pool_v : t->pool_k) +
+               ((size_t)layer * rs.pool_lstride + (size_t)seq * rs.pool_bstride) * t->esz + (size_t)code * hb;
+        hstride = (size_t)rs.pool_hstride * t->esz;
+      } else {
+        base = (const char*)(which ? t->stage_v : t->stage_k) +
+               ((size_t)(layer % t->S) * rs.stage_lstride + (size_t)seq * rs.stage_bstride) * t->esz +
+               (size_t)(code - t->cap0) * hb;
+        hstride = (size_t)rs.stage_hstride * t->esz;
+      }
+      HIP_TRY(t, hipMemcpy2DAsync(which ? v : k, hb, base, hstride, hb, t->Hkv, hipMemcpyDeviceToHost, st));
+    }
+    HIP_TRY(t, hipStreamSynchronize(st));
+    return TKV_OK;
+  }
+  if (tier == TKV_T2) return tkv_fail(t, TKV_ESTATE, "T2 rows of stream staging exist only as codes");
+  HIP_TRY(t, hipStreamSynchronize(st));
+  const uint32_t idx = code - t->cap0;
+  for (int which = 0; which < 2; ++which)
+    for (int h = 0; h < t->Hkv; ++h)
+      std::memcpy((char*)(which ? v : k) + h * hb,
+                  (const char*)(which ? t->arena1_v : t->arena1_k) +
+                      ((((size_t)layer * t->B + seq) * t->Hkv + h) * t->cap1 + idx) * hb,
+                  hb);
+  return TKV_OK;
+}
+
+extern "C" int tkv_read_t2(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, int8_t* k_codes, int8_t* v_codes,
+                           float* scales) {
+  if (!t || !k_codes || !v_codes || !scales) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (layer < 0 || layer >= t->L || seq < 0 || seq >= t->B || pos < 0 || pos >= t->n)
+    return tkv_fail(t, TKV_EINVAL, "layer/seq/pos out of range");
+  if (t->arena_job.valid()) {
+    const int rc = t->arena_job.get();
+    if (rc) return rc;
+  }
+  const size_t at = (size_t)seq * t->nmax + pos;
+  if (t->h_tier[at] != TKV_T2) return tkv_fail(t, TKV_ESTATE, "position %d is not in T2", pos);
+  const uint32_t idx = t->h_loc[at] - (uint32_t)(t->cap0 + t->cap1);
+  for (int which = 0; which < 2; ++which) {
+    for (int h = 0; h < t->Hkv; ++h)
+      std::memcpy((which ? v_codes : k_codes) + (size_t)h * t->D,
+                  (which ? t->arena2_v : t->arena2_k) + ((((size_t)layer * t->B + seq) * t->Hkv + h) * t->cap2 + idx) * t->D,
+                  t->D);
+    scales[which] = (which ? t->ascale_v : t->ascale_k)[((size_t)layer * t->B + seq) * t->cap2 + idx];
+  }
   return TKV_OK;
 }

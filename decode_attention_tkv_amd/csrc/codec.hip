@@ -1,0 +1,118 @@
+// The 8-bit host tier's codec on the GPU ("Not All Thoughts Need HBM",
+// gist.science technical summary, Method §1: T2 keeps low-importance rows on
+// the CPU at low precision, 8-bit as the example; results §4 its cost).
+//
+// Format (the pages fix none): symmetric int8, one fp32 scale per (layer,
+// position, K|V) over the position's kv_heads * head_dim values;
+// scale = amax / 127 (1 for an all-zero row), code = clamp(rne(x / scale),
+// -127, 127) with the division in fp32, value = fp32(code * scale) rounded
+// to the cache type (bf16 round-to-nearest-even).  A row that entered the
+// tier keeps these values for good.
+#include "tkv_internal.hpp"
+
+namespace tkvd {
+namespace {
+
+__device__ __forceinline__ float load_val(const void* base, int64_t idx, int elem_bytes) {
+  if (elem_bytes == 2) return __uint_as_float((uint32_t)((const uint16_t*)base)[idx] << 16);
+  return ((const float*)base)[idx];
+}
+
+__device__ __forceinline__ void store_val(void* base, int64_t idx, float v, int elem_bytes) {
+  if (elem_bytes == 2) {
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even (finite values)
+    ((uint16_t*)base)[idx] = (uint16_t)(u >> 16);
+  } else {
+    ((float*)base)[idx] = v;
+  }
+}
+
+__device__ __forceinline__ int64_t stage_elem(const RowSpace& rs, int l, int b, int h, uint32_t idx, int d) {
+  return (int64_t)(l % rs.stage_slots) * rs.stage_lstride + (int64_t)b * rs.stage_bstride +
+         (int64_t)h * rs.stage_hstride + (int64_t)idx * d;
+}
+
+// grid (n_ops, layers, 2), block 256: quantise F rows into a QPack and
+// (optionally) write their dequantised values into the staging area.
+__global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const QuantOp* ops) {
+  __shared__ float red[4];
+  const QuantOp op = ops[blockIdx.x];
+  const int l = blockIdx.y, which = blockIdx.z;
+  const int d = a.head_dim, n = a.kv_heads * d;
+  const void* f = which ? a.f.v : a.f.k;
+  float amax = 0.f;
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int h = e / d, j = e % d;
+    amax = fmaxf(amax, fabsf(load_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.src) * d + j, a.elem_bytes)));
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float scale = amax > 0.f ? amax / 127.f : 1.f;
+  int8_t* codes = a.out.codes + (int64_t)which * (int64_t)gridDim.y * a.kv_heads * a.out.rows * d;
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int h = e / d, j = e % d;
+    const float x = load_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.src) * d + j, a.elem_bytes);
+    const float c = fminf(fmaxf(rintf(x / scale), -127.f), 127.f);
+    codes[(((int64_t)l * a.kv_heads + h) * a.out.rows + op.dst) * d + j] = (int8_t)c;
+    if (op.stage != kNoLoc) {
+      void* st = which ? (void*)a.rows.stage_v : (void*)a.rows.stage_k;
+      store_val(st, stage_elem(a.rows, l, op.b, h, op.stage, d) + j, c * scale, a.elem_bytes);
+    }
+  }
+  if (threadIdx.x == 0) a.out.scales[((int64_t)which * gridDim.y + l) * a.out.rows + op.dst] = scale;
+}
+
+// grid (n_ops, layers, 2), block 256: QPack rows -> cache-type values in F.
+__global__ __launch_bounds__(256) void k_dequant_rows(const DequantArgs a, const DequantOp* ops) {
+  const DequantOp op = ops[blockIdx.x];
+  const int l = blockIdx.y, which = blockIdx.z;
+  const int d = a.head_dim, n = a.kv_heads * d;
+  const int8_t* codes = a.in.codes + (int64_t)which * (int64_t)gridDim.y * a.kv_heads * a.in.rows * d;
+  const float scale = a.in.scales[((int64_t)which * gridDim.y + l) * a.in.rows + op.src];
+  void* f = which ? a.f.v : a.f.k;
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int h = e / d, j = e % d;
+    const float c = (float)codes[(((int64_t)l * a.kv_heads + h) * a.in.rows + op.src) * d + j];
+    store_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.dst) * d + j, c * scale, a.elem_bytes);
+  }
+}
+
+// grid (n2max, batch, 2), block 256: one layer's 8-bit rows -> its staging slot.
+__global__ __launch_bounds__(256) void k_dequant_stage(const DequantStageArgs a) {
+  const int k = blockIdx.x, b = blockIdx.y, which = blockIdx.z;
+  if (k >= a.n2[b]) return;
+  const int d = a.head_dim, n = a.kv_heads * d;
+  const int8_t* codes = which ? a.codes_v : a.codes_k;
+  const float scale = (which ? a.scale_v : a.scale_k)[(int64_t)b * a.cap2 + k];
+  void* st = which ? (void*)a.rows.stage_v : (void*)a.rows.stage_k;
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int h = e / d, j = e % d;
+    const float c = (float)codes[(((int64_t)b * a.kv_heads + h) * a.cap2 + k) * d + j];
+    store_val(st, stage_elem(a.rows, a.layer, b, h, (uint32_t)(a.cap1 + k), d) + j, c * scale, a.elem_bytes);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(const QuantArgs& a, const QuantOp* ops, int n_ops, int layers, hipStream_t s) {
+  if (n_ops <= 0) return hipSuccess;
+  k_quant_rows<<<dim3(n_ops, layers, 2), 256, 0, s>>>(a, ops);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_rows(const DequantArgs& a, const DequantOp* ops, int n_ops, int layers, hipStream_t s) {
+  if (n_ops <= 0) return hipSuccess;
+  k_dequant_rows<<<dim3(n_ops, layers, 2), 256, 0, s>>>(a, ops);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_stage(const DequantStageArgs& a, int n2max, hipStream_t s) {
+  if (n2max <= 0) return hipSuccess;
+  k_dequant_stage<<<dim3(n2max, a.batch, 2), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace tkvd

@@ -50,20 +50,37 @@ struct tkv {
   size_t h_ops_bytes = 0;
   void* h_pack_in = nullptr;  // pinned: promoted T1 rows packed on the host (stream mode)
   size_t h_pack_in_bytes = 0;
-  void* h_pack_out = nullptr;  // pinned: rows entering T1, [2][L][Hkv][E][D]
+  void* h_pack_out = nullptr;  // pinned: rows entering T1, [2][L][Hkv][E1][D]
   size_t h_pack_out_bytes = 0;
-  void* pack_out_k = nullptr;  // device packs [L][Hkv][rows][D], persistent, grown on demand
-  void* pack_out_v = nullptr;
-  void* pack_in_k = nullptr;
-  void* pack_in_v = nullptr;
-  size_t pack_out_cap = 0, pack_in_cap = 0;  // rows
+  void* h_qout = nullptr;      // pinned: rows entering T2, codes [2][L][Hkv][E2][D] + scales [2][L][E2]
+  size_t h_qout_bytes = 0;
+  void* h_qin = nullptr;       // pinned (stream mode): 8-bit rows fetched from the T2 arena
+  size_t h_qin_bytes = 0;
+  // device packs, persistent, grown on demand
+  void* fpack = nullptr;       // F: every moved row's value, K then V, [L][Hkv][rows][D] each
+  size_t fpack_bytes = 0;
+  void* fin = nullptr;         // FI (stream mode): T1 rows fetched from the host, K then V
+  size_t fin_bytes = 0;
+  void* qin = nullptr;         // QIn (stream mode): T2 rows fetched from the host
+  size_t qin_bytes = 0;
+  void* qout = nullptr;        // QOut: rows entering T2
+  size_t qout_bytes = 0;
   hipEvent_t ev_pack = nullptr;              // entrant rows landed in h_pack_out
   std::future<int> arena_job;                // host arena maintenance of the last reassignment
 
   // ---- pinned host arenas (owned)
   void* arena1_k = nullptr;  // [L][B][Hkv][cap1][D]: T1 rows, dense per (layer, seq, head)
   void* arena1_v = nullptr;
+  int8_t* arena2_k = nullptr;  // [L][B][Hkv][cap2][D]: T2 codes, dense per (layer, seq, head)
+  int8_t* arena2_v = nullptr;
+  float* ascale_k = nullptr;   // [L][B][cap2]: T2 scales
+  float* ascale_v = nullptr;
   std::vector<void*> host_allocs;
+  // stream mode: one layer's 8-bit rows on the device before dequantisation
+  int8_t* qstage_k = nullptr;  // [S][B][Hkv][cap2][D]
+  int8_t* qstage_v = nullptr;
+  float* qsscale_k = nullptr;  // [S][B][cap2]
+  float* qsscale_v = nullptr;
 
   // ---- host-side placement state
   int n = 0;  // positions appended per sequence
@@ -75,6 +92,7 @@ struct tkv {
   std::vector<uint8_t> h_tier;                // [B][nmax]
   std::vector<uint32_t> h_loc;                // [B][nmax]
   std::vector<std::vector<int32_t>> t1_owner; // [B]: T1 arena index -> position
+  std::vector<std::vector<int32_t>> t2_owner; // [B]: T2 arena index -> position
 
   // ---- last reassignment's changed rows (pinned host copies)
   tkv_delta* h_promote = nullptr;  // [B][nmax]

@@ -1,21 +1,26 @@
 // tkv_reassign: score-ranked re-placement of every sequence's rows
 // ("Not All Thoughts Need HBM", gist.science technical summary, Method §1
-// four tiers and §4 periodic reassignment with differential movement).
+// four tiers and §4 periodic reassignment where only changed rows move).
 //
-// Device: rank + label (radix select on the GPU's fp32 scores), changed-row
-// lists by prefix-scan compaction.  Host: one synchronisation to read the
-// lists, then a placement plan per sequence:
-//   * the T1 arena of a sequence stays dense: rows leaving T1 leave holes,
-//     the last remaining rows move into the holes, rows entering T1 are
-//     appended (so they land in one contiguous block per layer);
+// Device: rank + label (radix select on the GPU's fp32 scores) and the
+// changed-row lists (prefix-scan compaction).  Host: one synchronisation to
+// read the lists, then a placement plan per sequence:
+//   * the T1 and T2 arenas of a sequence stay dense: rows that leave leave
+//     holes, the last remaining rows move into the holes, rows that enter are
+//     appended (one contiguous block per layer and kv head);
 //   * T0 slots freed by demotions are reused by promotions.
-// Rows move in three dependent phases of one copy kernel: (1) rows that
-// leave their home are gathered into pack buffers, (2a) arena compaction in
-// the staging mirror and promotions into T0 slots, (2b) entrants into the
-// staging mirror.  Entrants leave the GPU as one contiguous copy per K|V into
-// a pinned pack; a host job (never waited for by the GPU) compacts the
-// pinned arena and files the entrants.  In stream mode promoted rows come
-// from the host arena.  Every area is head-major, [..][kv_head][row][d].
+// Data movement:
+//   phase 1   every moved row's value lands in the fetch pack F (from the T0
+//             pool, the resident staging, or -- stream mode -- the pinned
+//             arenas, 8-bit rows dequantised on the GPU);
+//   phase 2a  promotions F -> T0 slots; compaction moves inside the staging;
+//   phase 2b  rows entering T1: F -> staging; rows entering T2: quantised
+//             from F on the GPU (codes + scale out, dequantised values into
+//             the staging).
+// Rows entering T1/T2 reach their pinned home through one write-back copy per
+// pack on a stream of their own; a host job (never waited for by the GPU)
+// compacts the arenas and files them.  Every area is head-major.
+#include <algorithm>
 #include <chrono>
 #include <cstring>
 #include <memory>
@@ -28,12 +33,20 @@ using namespace tkvd;
 
 namespace {
 
+enum SrcKind : uint8_t { kFromPool, kFromT1, kFromT2 };
+
+struct Move {
+  uint32_t pos;
+  SrcKind kind;
+  uint32_t idx;  // pool slot, T1 index or T2 index
+};
+
 struct SeqPlan {
-  std::vector<uint32_t> entrant_pos, entrant_slot;    // T0 -> T1: position, old T0 slot
-  std::vector<uint32_t> promo_pos, promo_idx, promo_slot;  // T1 -> T0: position, old arena index, new slot
-  std::vector<std::pair<uint32_t, uint32_t>> movers;  // arena (src, dst)
-  uint32_t m = 0;                                     // arena rows before the entrants
-  int64_t eoff = 0, poff = 0;                         // offsets in the pack buffers
+  std::vector<Move> ent1, ent2, promo;  // rows entering T1, T2 and T0
+  std::vector<uint32_t> promo_slot;
+  std::vector<std::pair<uint32_t, uint32_t>> mov1, mov2;  // arena (src, dst)
+  uint32_t m1 = 0, m2 = 0;              // arena rows kept before the entrants
+  int64_t e1off = 0, e2off = 0, poff = 0;  // offsets within the F segments
 };
 
 int grow_device(tkv* t, void** p, size_t* cap, size_t need) {
@@ -58,27 +71,24 @@ int grow_pinned(tkv* t, void** p, size_t* cap, size_t need) {
   return TKV_OK;
 }
 
-int grow_packs(tkv* t, int64_t E, int64_t P) {
-  const size_t lrb = (size_t)t->L * t->row_bytes;
-  if ((size_t)E > t->pack_out_cap) {
-    const size_t rows = std::max<size_t>((size_t)E * 2, 64);
-    for (void** p : {&t->pack_out_k, &t->pack_out_v}) {
-      if (*p) HIP_TRY(t, hipFree(*p));
-      *p = nullptr;
-      HIP_TRY(t, hipMalloc(p, rows * lrb));
-    }
-    t->pack_out_cap = rows;
+// Dense-arena compaction: indices marked vacated leave; the kept rows above
+// the new size m move down into the holes below it, in order.
+void compact(std::vector<int32_t>& own, const std::vector<char>& vac, uint32_t* m,
+             std::vector<std::pair<uint32_t, uint32_t>>* moves) {
+  const uint32_t n = (uint32_t)own.size();
+  uint32_t kept = 0;
+  for (uint32_t i = 0; i < n; ++i) kept += vac[i] ? 0 : 1;
+  std::vector<uint32_t> holes, srcs;
+  for (uint32_t i = 0; i < kept; ++i)
+    if (vac[i]) holes.push_back(i);
+  for (uint32_t i = kept; i < n; ++i)
+    if (!vac[i]) srcs.push_back(i);
+  for (size_t k = 0; k < holes.size(); ++k) {
+    moves->emplace_back(srcs[k], holes[k]);
+    own[holes[k]] = own[srcs[k]];
   }
-  if ((size_t)P > t->pack_in_cap) {
-    const size_t rows = std::max<size_t>((size_t)P * 2, 64);
-    for (void** p : {&t->pack_in_k, &t->pack_in_v}) {
-      if (*p) HIP_TRY(t, hipFree(*p));
-      *p = nullptr;
-      HIP_TRY(t, hipMalloc(p, rows * lrb));
-    }
-    t->pack_in_cap = rows;
-  }
-  return TKV_OK;
+  own.resize(kept);
+  *m = kept;
 }
 
 }  // namespace
@@ -89,10 +99,11 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   if (t->n == 0) return TKV_OK;
   const auto wall0 = std::chrono::steady_clock::now();
   hipStream_t st = (hipStream_t)stream;
-  const int B = t->B, L = t->L, n = t->n;
+  const int B = t->B, L = t->L, n = t->n, H = t->Hkv, D = t->D;
   const size_t nmax = t->nmax;
-  // The host arena and the pinned staging buffers may still be read or
-  // written by the previous reassignment's host job and copies.
+  const size_t hb = (size_t)D * t->esz;  // bytes of one head's row
+  // The host arenas and the pinned packs may still be in use by the previous
+  // reassignment's host job and copies.
   if (t->arena_job.valid()) {
     const int rc = t->arena_job.get();
     if (rc) return rc;
@@ -153,173 +164,250 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   // ---- placement plan
   std::vector<SeqPlan> plan(B);
   std::vector<LocUpdate> upd;
-  int64_t E = 0, P = 0, n_evict = 0, n_prom = 0, n_dem = 0;
+  int64_t E1 = 0, E2 = 0, P = 0, n_evict = 0, n_prom = 0, n_dem = 0;
   for (int b = 0; b < B; ++b) {
     SeqPlan& sp = plan[b];
-    auto& own = t->t1_owner[b];
     uint8_t* tr = &t->h_tier[b * nmax];
     uint32_t* lc = &t->h_loc[b * nmax];
-    std::vector<char> vacated(own.size(), 0);
+    auto& own1 = t->t1_owner[b];
+    auto& own2 = t->t2_owner[b];
+    std::vector<char> vac1(own1.size(), 0), vac2(own2.size(), 0);
     std::vector<uint32_t> freed;
-    const tkv_delta* pro = t->h_promote + b * nmax;
-    const tkv_delta* dem = t->h_demote + b * nmax;
-    const int cp = t->h_counts[2 * b], cd = t->h_counts[2 * b + 1];
-    for (int k = 0; k < cd; ++k) {
-      const tkv_delta& d = dem[k];
-      if (d.old_tier == TKV_T0) {
-        freed.push_back(lc[d.pos]);
-        if (d.new_tier == TKV_T1) {
-          sp.entrant_pos.push_back(d.pos);
-          sp.entrant_slot.push_back(lc[d.pos]);
+    const uint32_t c1 = (uint32_t)t->cap0, c2 = (uint32_t)(t->cap0 + t->cap1);
+    auto source = [&](uint32_t pos, uint8_t old) -> Move {
+      if (old == TKV_T0) return {pos, kFromPool, lc[pos]};
+      if (old == TKV_T1) {
+        vac1[lc[pos] - c1] = 1;
+        return {pos, kFromT1, lc[pos] - c1};
+      }
+      vac2[lc[pos] - c2] = 1;
+      return {pos, kFromT2, lc[pos] - c2};
+    };
+    auto take = [&](const tkv_delta* list, int count) {
+      for (int k = 0; k < count; ++k) {
+        const tkv_delta& d = list[k];
+        const Move mv = source(d.pos, d.old_tier);
+        if (d.old_tier == TKV_T0) freed.push_back(mv.idx);
+        switch (d.new_tier) {
+          case TKV_T0: sp.promo.push_back(mv); break;
+          case TKV_T1: sp.ent1.push_back(mv); break;
+          case TKV_T2: sp.ent2.push_back(mv); break;
+          default:
+            lc[d.pos] = kNoLoc;
+            upd.push_back({b, d.pos, kNoLoc});
+            ++n_evict;
         }
-      } else if (d.old_tier == TKV_T1) {
-        vacated[lc[d.pos] - t->cap0] = 1;
-      } else {
-        return tkv_fail(t, TKV_ESTATE, "unexpected demotion from tier %d", d.old_tier);
+        tr[d.pos] = d.new_tier;
       }
-      if (d.new_tier == TKV_T3) {
-        lc[d.pos] = kNoLoc;
-        upd.push_back({b, d.pos, kNoLoc});
-        ++n_evict;
-      } else if (d.new_tier == TKV_T2) {
-        return tkv_fail(t, TKV_ESTATE, "8-bit tier rows are not supported by this build");
-      }
-      tr[d.pos] = d.new_tier;
-    }
-    for (int k = 0; k < cp; ++k) {
-      const tkv_delta& d = pro[k];
-      if (d.old_tier != TKV_T1 || d.new_tier != TKV_T0)
-        return tkv_fail(t, TKV_ESTATE, "unexpected promotion %d -> %d", d.old_tier, d.new_tier);
-      const uint32_t idx = lc[d.pos] - t->cap0;
-      vacated[idx] = 1;
-      sp.promo_pos.push_back(d.pos);
-      sp.promo_idx.push_back(idx);
-      tr[d.pos] = d.new_tier;
-    }
+    };
+    const int cp = t->h_counts[2 * b], cd = t->h_counts[2 * b + 1];
+    take(t->h_demote + b * nmax, cd);
+    take(t->h_promote + b * nmax, cp);
     n_prom += cp;
     n_dem += cd;
-    // T0 slots: freed ones first go back, then promotions take slots
+    auto by_pos = [](const Move& x, const Move& y) { return x.pos < y.pos; };
+    std::sort(sp.ent1.begin(), sp.ent1.end(), by_pos);
+    std::sort(sp.ent2.begin(), sp.ent2.end(), by_pos);
+    // T0 slots: freed ones go back first, then promotions take slots
     for (auto it = freed.rbegin(); it != freed.rend(); ++it) t->free0[b].push_back((int32_t)*it);
-    for (size_t k = 0; k < sp.promo_pos.size(); ++k) {
+    for (const Move& mv : sp.promo) {
       if (t->free0[b].empty()) return tkv_fail(t, TKV_ECAPACITY, "T0 pool full while promoting");
       const uint32_t slot = (uint32_t)t->free0[b].back();
       t->free0[b].pop_back();
       sp.promo_slot.push_back(slot);
-      lc[sp.promo_pos[k]] = slot;
-      upd.push_back({b, sp.promo_pos[k], slot});
+      lc[mv.pos] = slot;
+      upd.push_back({b, mv.pos, slot});
     }
-    // arena compaction: the last kept rows fill the holes below m
-    const uint32_t n1 = (uint32_t)own.size();
-    uint32_t kept = 0;
-    for (uint32_t i = 0; i < n1; ++i) kept += vacated[i] ? 0 : 1;
-    sp.m = kept;
-    std::vector<uint32_t> holes, srcs;
-    for (uint32_t i = 0; i < sp.m; ++i)
-      if (vacated[i]) holes.push_back(i);
-    for (uint32_t i = sp.m; i < n1; ++i)
-      if (!vacated[i]) srcs.push_back(i);
-    if (holes.size() != srcs.size()) return tkv_fail(t, TKV_ESTATE, "arena compaction mismatch");
-    for (size_t k = 0; k < holes.size(); ++k) {
-      sp.movers.emplace_back(srcs[k], holes[k]);
-      own[holes[k]] = own[srcs[k]];
-      lc[own[holes[k]]] = (uint32_t)t->cap0 + holes[k];
-      upd.push_back({b, (uint32_t)own[holes[k]], (uint32_t)t->cap0 + holes[k]});
+    // arenas: compaction, then the entrants at the end
+    compact(own1, vac1, &sp.m1, &sp.mov1);
+    compact(own2, vac2, &sp.m2, &sp.mov2);
+    for (auto& mv : sp.mov1) {
+      lc[own1[mv.second]] = c1 + mv.second;
+      upd.push_back({b, (uint32_t)own1[mv.second], c1 + mv.second});
     }
-    own.resize(sp.m);
-    for (size_t e = 0; e < sp.entrant_pos.size(); ++e) {
-      const uint32_t idx = sp.m + (uint32_t)e;
-      if (idx >= (uint32_t)t->cap1) return tkv_fail(t, TKV_ECAPACITY, "T1 arena full");
-      own.push_back((int32_t)sp.entrant_pos[e]);
-      lc[sp.entrant_pos[e]] = (uint32_t)t->cap0 + idx;
-      upd.push_back({b, sp.entrant_pos[e], (uint32_t)t->cap0 + idx});
+    for (auto& mv : sp.mov2) {
+      lc[own2[mv.second]] = c2 + mv.second;
+      upd.push_back({b, (uint32_t)own2[mv.second], c2 + mv.second});
     }
-    sp.eoff = E;
+    if (sp.m1 + sp.ent1.size() > (size_t)t->cap1) return tkv_fail(t, TKV_ECAPACITY, "T1 arena full");
+    if (sp.m2 + sp.ent2.size() > (size_t)t->cap2) return tkv_fail(t, TKV_ECAPACITY, "T2 arena full");
+    for (size_t e = 0; e < sp.ent1.size(); ++e) {
+      own1.push_back((int32_t)sp.ent1[e].pos);
+      lc[sp.ent1[e].pos] = c1 + sp.m1 + (uint32_t)e;
+      upd.push_back({b, sp.ent1[e].pos, c1 + sp.m1 + (uint32_t)e});
+    }
+    for (size_t e = 0; e < sp.ent2.size(); ++e) {
+      own2.push_back((int32_t)sp.ent2[e].pos);
+      lc[sp.ent2[e].pos] = c2 + sp.m2 + (uint32_t)e;
+      upd.push_back({b, sp.ent2[e].pos, c2 + sp.m2 + (uint32_t)e});
+    }
+    sp.e1off = E1;
+    sp.e2off = E2;
     sp.poff = P;
-    E += (int64_t)sp.entrant_pos.size();
-    P += (int64_t)sp.promo_pos.size();
+    E1 += (int64_t)sp.ent1.size();
+    E2 += (int64_t)sp.ent2.size();
+    P += (int64_t)sp.promo.size();
     int32_t evicted_b = 0;
     for (int p = 0; p < n; ++p) evicted_b += tr[p] == TKV_T3 ? 1 : 0;
     t->nlive[b] = n - evicted_b;
   }
 
-  // ---- host arena: promoted rows out first (stream mode), then compaction
-  const size_t rb = t->row_bytes;
-  const size_t hb = (size_t)t->D * t->esz;
-  const int H = t->Hkv;
-  auto arena_row = [&](int which, int l, int b, int h, uint32_t idx) -> char* {
-    return (char*)(which ? t->arena1_v : t->arena1_k) + ((((size_t)l * B + b) * H + h) * t->cap1 + idx) * hb;
-  };
-  if (!t->resident && P > 0) {
-    int rc = grow_pinned(t, &t->h_pack_in, &t->h_pack_in_bytes, 2 * (size_t)L * P * rb);
+  // ---- F layout: [rows entering T1 | rows entering T2 | promotions]
+  const int64_t F = E1 + E2 + P;
+  const size_t f_bytes = (size_t)L * H * F * hb;  // per K|V
+  {
+    int rc = grow_device(t, &t->fpack, &t->fpack_bytes, 2 * f_bytes);
     if (rc) return rc;
-    for (int b = 0; b < B; ++b)
-      for (size_t p = 0; p < plan[b].promo_idx.size(); ++p)
-        for (int which = 0; which < 2; ++which)
-          for (int l = 0; l < L; ++l)
-            for (int h = 0; h < H; ++h)
-              std::memcpy((char*)t->h_pack_in + ((((size_t)which * L + l) * H + h) * P + plan[b].poff + p) * hb,
-                          arena_row(which, l, b, h, plan[b].promo_idx[p]), hb);
   }
+  FPack fp{t->fpack, (char*)t->fpack + f_bytes, F};
 
-  // ---- row-copy ops
+  // ---- phase 1 sources
   std::vector<RowOp> ops1, ops2a, ops2b;
+  std::vector<DequantOp> dq1;
+  std::vector<QuantOp> q2;
+  // stream mode: rows that live only on the host are packed there first
+  std::vector<std::pair<int, uint32_t>> host_t1, host_t2;  // (sequence, arena index) in pack order
+  auto fetch = [&](int b, const Move& mv, uint32_t frow) {
+    if (mv.kind == kFromPool) {
+      ops1.push_back({kAreaPool, kAreaPackOut, (uint16_t)b, mv.idx, frow});
+    } else if (t->resident) {
+      const uint32_t sidx = mv.kind == kFromT1 ? mv.idx : (uint32_t)t->cap1 + mv.idx;
+      ops1.push_back({kAreaStage, kAreaPackOut, (uint16_t)b, sidx, frow});
+    } else if (mv.kind == kFromT1) {
+      ops1.push_back({kAreaPackIn, kAreaPackOut, (uint16_t)b, (uint32_t)host_t1.size(), frow});
+      host_t1.emplace_back(b, mv.idx);
+    } else {
+      dq1.push_back({(uint16_t)b, (uint32_t)host_t2.size(), frow});
+      host_t2.emplace_back(b, mv.idx);
+    }
+  };
   for (int b = 0; b < B; ++b) {
     const SeqPlan& sp = plan[b];
-    for (size_t e = 0; e < sp.entrant_pos.size(); ++e) {
-      ops1.push_back({kAreaPool, kAreaPackOut, (uint16_t)b, sp.entrant_slot[e], (uint32_t)(sp.eoff + e)});
-      if (t->resident)
-        ops2b.push_back({kAreaPackOut, kAreaStage, (uint16_t)b, (uint32_t)(sp.eoff + e), sp.m + (uint32_t)e});
+    for (size_t e = 0; e < sp.ent1.size(); ++e) fetch(b, sp.ent1[e], (uint32_t)(sp.e1off + e));
+    for (size_t e = 0; e < sp.ent2.size(); ++e) fetch(b, sp.ent2[e], (uint32_t)(E1 + sp.e2off + e));
+    for (size_t p = 0; p < sp.promo.size(); ++p) fetch(b, sp.promo[p], (uint32_t)(E1 + E2 + sp.poff + p));
+    // phase 2a: promotions into T0 slots, compaction inside the resident staging
+    for (size_t p = 0; p < sp.promo.size(); ++p)
+      ops2a.push_back({kAreaPackOut, kAreaPool, (uint16_t)b, (uint32_t)(E1 + E2 + sp.poff + p), sp.promo_slot[p]});
+    if (t->resident) {
+      for (auto& mv : sp.mov1) ops2a.push_back({kAreaStage, kAreaStage, (uint16_t)b, mv.first, mv.second});
+      for (auto& mv : sp.mov2)
+        ops2a.push_back({kAreaStage, kAreaStage, (uint16_t)b, (uint32_t)t->cap1 + mv.first,
+                         (uint32_t)t->cap1 + mv.second});
+      // phase 2b: entrants into the resident staging
+      for (size_t e = 0; e < sp.ent1.size(); ++e)
+        ops2b.push_back({kAreaPackOut, kAreaStage, (uint16_t)b, (uint32_t)(sp.e1off + e), sp.m1 + (uint32_t)e});
     }
-    for (size_t p = 0; p < sp.promo_pos.size(); ++p) {
-      if (t->resident) ops1.push_back({kAreaStage, kAreaPackIn, (uint16_t)b, sp.promo_idx[p], (uint32_t)(sp.poff + p)});
-      ops2a.push_back({kAreaPackIn, kAreaPool, (uint16_t)b, (uint32_t)(sp.poff + p), sp.promo_slot[p]});
-    }
-    if (t->resident)
-      for (auto& mv : sp.movers) ops2a.push_back({kAreaStage, kAreaStage, (uint16_t)b, mv.first, mv.second});
+    for (size_t e = 0; e < sp.ent2.size(); ++e)
+      q2.push_back({(uint16_t)b, (uint32_t)(E1 + sp.e2off + e), (uint32_t)(sp.e2off + e),
+                    t->resident ? (uint32_t)t->cap1 + sp.m2 + (uint32_t)e : kNoLoc});
   }
+
+  // ---- stream mode: host-resident sources packed and sent
+  const int64_t NF1 = (int64_t)host_t1.size(), NF2 = (int64_t)host_t2.size();
+  auto a1row = [&](int which, int l, int b, int h, uint32_t idx) -> char* {
+    return (char*)(which ? t->arena1_v : t->arena1_k) + ((((size_t)l * B + b) * H + h) * t->cap1 + idx) * hb;
+  };
+  const size_t qrow = (size_t)D;  // bytes of one head's int8 row
+  if (NF1 > 0) {
+    const size_t half = (size_t)L * H * NF1 * hb;
+    int rc = grow_pinned(t, &t->h_pack_in, &t->h_pack_in_bytes, 2 * half);
+    if (!rc) rc = grow_device(t, &t->fin, &t->fin_bytes, 2 * half);
+    if (rc) return rc;
+    for (int64_t i = 0; i < NF1; ++i)
+      for (int which = 0; which < 2; ++which)
+        for (int l = 0; l < L; ++l)
+          for (int h = 0; h < H; ++h)
+            std::memcpy((char*)t->h_pack_in + ((((size_t)which * L + l) * H + h) * NF1 + i) * hb,
+                        a1row(which, l, host_t1[i].first, h, host_t1[i].second), hb);
+    HIP_TRY(t, hipMemcpyAsync(t->fin, t->h_pack_in, 2 * half, hipMemcpyHostToDevice, st));
+    t->st.h2d_bytes += 2 * (int64_t)half;
+  }
+  QPack qin{};
+  if (NF2 > 0) {
+    const size_t codes_half = (size_t)L * H * NF2 * qrow, sc_half = (size_t)L * NF2 * 4;
+    const size_t bytes = 2 * codes_half + 2 * sc_half;
+    int rc = grow_pinned(t, &t->h_qin, &t->h_qin_bytes, bytes);
+    if (!rc) rc = grow_device(t, &t->qin, &t->qin_bytes, bytes);
+    if (rc) return rc;
+    char* hc = (char*)t->h_qin;
+    float* hs = (float*)(hc + 2 * codes_half);
+    for (int64_t i = 0; i < NF2; ++i) {
+      const int b = host_t2[i].first;
+      const uint32_t idx = host_t2[i].second;
+      for (int which = 0; which < 2; ++which)
+        for (int l = 0; l < L; ++l) {
+          for (int h = 0; h < H; ++h)
+            std::memcpy(hc + ((((size_t)which * L + l) * H + h) * NF2 + i) * qrow,
+                        (which ? t->arena2_v : t->arena2_k) + ((((size_t)l * B + b) * H + h) * t->cap2 + idx) * qrow,
+                        qrow);
+          hs[((size_t)which * L + l) * NF2 + i] =
+              (which ? t->ascale_v : t->ascale_k)[((size_t)l * B + b) * t->cap2 + idx];
+        }
+    }
+    HIP_TRY(t, hipMemcpyAsync(t->qin, t->h_qin, bytes, hipMemcpyHostToDevice, st));
+    t->st.h2d_bytes += (int64_t)bytes;
+    qin = QPack{(int8_t*)t->qin, (float*)((char*)t->qin + 2 * codes_half), NF2};
+  }
+
+  // ---- ops and location updates to the device
   const size_t nops = ops1.size() + ops2a.size() + ops2b.size();
-  const size_t bytes = nops * sizeof(RowOp) + upd.size() * sizeof(LocUpdate);
+  const size_t bytes = nops * sizeof(RowOp) + dq1.size() * sizeof(DequantOp) + q2.size() * sizeof(QuantOp) +
+                       upd.size() * sizeof(LocUpdate);
+  const RowOp* d_ops1 = nullptr;
+  const RowOp* d_ops2a = nullptr;
+  const RowOp* d_ops2b = nullptr;
+  const DequantOp* d_dq1 = nullptr;
+  const QuantOp* d_q2 = nullptr;
+  const LocUpdate* d_upd = nullptr;
   if (bytes > 0) {
     int rc = grow_pinned(t, &t->h_ops, &t->h_ops_bytes, bytes);
     if (!rc) rc = grow_device(t, &t->d_ops, &t->d_ops_bytes, bytes);
     if (rc) return rc;
     char* h = (char*)t->h_ops;
-    std::memcpy(h, ops1.data(), ops1.size() * sizeof(RowOp));
-    std::memcpy(h + ops1.size() * sizeof(RowOp), ops2a.data(), ops2a.size() * sizeof(RowOp));
-    std::memcpy(h + (ops1.size() + ops2a.size()) * sizeof(RowOp), ops2b.data(), ops2b.size() * sizeof(RowOp));
-    std::memcpy(h + nops * sizeof(RowOp), upd.data(), upd.size() * sizeof(LocUpdate));
+    char* d = (char*)t->d_ops;
+    size_t off = 0;
+    auto put = [&](const void* src, size_t sz) -> const void* {
+      if (sz) std::memcpy(h + off, src, sz);
+      const void* dev_ptr = d + off;
+      off += sz;
+      return dev_ptr;
+    };
+    d_ops1 = (const RowOp*)put(ops1.data(), ops1.size() * sizeof(RowOp));
+    d_ops2a = (const RowOp*)put(ops2a.data(), ops2a.size() * sizeof(RowOp));
+    d_ops2b = (const RowOp*)put(ops2b.data(), ops2b.size() * sizeof(RowOp));
+    d_dq1 = (const DequantOp*)put(dq1.data(), dq1.size() * sizeof(DequantOp));
+    d_q2 = (const QuantOp*)put(q2.data(), q2.size() * sizeof(QuantOp));
+    d_upd = (const LocUpdate*)put(upd.data(), upd.size() * sizeof(LocUpdate));
     HIP_TRY(t, hipMemcpyAsync(t->d_ops, t->h_ops, bytes, hipMemcpyHostToDevice, st));
   }
-  const RowOp* d_ops1 = (const RowOp*)t->d_ops;
-  const RowOp* d_ops2a = d_ops1 + ops1.size();
-  const RowOp* d_ops2b = d_ops2a + ops2a.size();
-  const LocUpdate* d_upd = (const LocUpdate*)(d_ops1 + nops);
 
+  // ---- device phases
   CopyArgs ca{};
   ca.rows = t->rowspace();
   ca.kv_heads = H;
   ca.head_bytes = (int32_t)hb;
   ca.elem_bytes = t->esz;
-  ca.pack_out_rows = E;
-  ca.pack_in_rows = P;
-  {
-    int rc = grow_packs(t, E, P);
-    if (rc) return rc;
-  }
-  ca.pack_out_k = t->pack_out_k;
-  ca.pack_out_v = t->pack_out_v;
-  ca.pack_in_k = t->pack_in_k;
-  ca.pack_in_v = t->pack_in_v;
+  ca.pack_out_k = fp.k;  // F
+  ca.pack_out_v = fp.v;
+  ca.pack_out_rows = F;
+  ca.pack_in_k = t->fin;  // FI
+  ca.pack_in_v = t->fin ? (char*)t->fin + (size_t)L * H * NF1 * hb : nullptr;
+  ca.pack_in_rows = NF1;
   HIP_TRY(t, launch_copy_rows(ca, d_ops1, (int)ops1.size(), L, st));
-  HIP_TRY(t, hipEventRecord(t->ev_gathered, st));
-  if (!t->resident && P > 0) {
-    HIP_TRY(t, hipMemcpyAsync(ca.pack_in_k, t->h_pack_in, (size_t)L * P * rb, hipMemcpyHostToDevice, st));
-    HIP_TRY(t, hipMemcpyAsync(ca.pack_in_v, (char*)t->h_pack_in + (size_t)L * P * rb, (size_t)L * P * rb,
-                              hipMemcpyHostToDevice, st));
-    t->st.h2d_bytes += 2 * (int64_t)L * P * rb;
-  }
+  DequantArgs dqa{qin, fp, H, D, t->esz};
+  HIP_TRY(t, launch_dequant_rows(dqa, d_dq1, (int)dq1.size(), L, st));
   HIP_TRY(t, launch_copy_rows(ca, d_ops2a, (int)ops2a.size(), L, st));
   HIP_TRY(t, launch_copy_rows(ca, d_ops2b, (int)ops2b.size(), L, st));
+  QPack qout{};
+  if (E2 > 0) {
+    const size_t codes_half = (size_t)L * H * E2 * qrow, sc_half = (size_t)L * E2 * 4;
+    int rc = grow_device(t, &t->qout, &t->qout_bytes, 2 * codes_half + 2 * sc_half);
+    if (rc) return rc;
+    qout = QPack{(int8_t*)t->qout, (float*)((char*)t->qout + 2 * codes_half), E2};
+    QuantArgs qa{t->rowspace(), fp, qout, H, D, t->esz};
+    HIP_TRY(t, launch_quant_rows(qa, d_q2, (int)q2.size(), L, st));
+  }
   HIP_TRY(t, launch_set_loc(d_upd, (int)upd.size(), t->loc, t->nmax, st));
   LiveArgs la{};
   la.tier = t->tier;
@@ -329,61 +417,89 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   la.nmax = t->nmax;
   la.n = n;
   HIP_TRY(t, launch_build_live(la, B, st));
-  // entrants leave the GPU as one contiguous copy per K|V into a pinned pack;
-  // a host job then compacts the arena and files the entrants at [m, m + E_b)
-  if (E > 0) {
-    int rc = grow_pinned(t, &t->h_pack_out, &t->h_pack_out_bytes, 2 * (size_t)L * E * rb);
+  HIP_TRY(t, hipEventRecord(t->ev_gathered, st));
+
+  // ---- write-back of the entrants, on its own stream
+  if (E1 > 0 || E2 > 0) HIP_TRY(t, hipStreamWaitEvent(t->wb, t->ev_gathered, 0));
+  if (E1 > 0) {
+    const size_t half = (size_t)L * H * E1 * hb;
+    int rc = grow_pinned(t, &t->h_pack_out, &t->h_pack_out_bytes, 2 * half);
     if (rc) return rc;
-    // on the write-back stream, so the decode steps that follow do not wait for it
-    HIP_TRY(t, hipStreamWaitEvent(t->wb, t->ev_gathered, 0));
-    HIP_TRY(t, hipMemcpyAsync(t->h_pack_out, t->pack_out_k, (size_t)L * E * rb, hipMemcpyDeviceToHost, t->wb));
-    HIP_TRY(t, hipMemcpyAsync((char*)t->h_pack_out + (size_t)L * E * rb, t->pack_out_v, (size_t)L * E * rb,
-                              hipMemcpyDeviceToHost, t->wb));
-    t->st.d2h_bytes += 2 * (int64_t)L * E * rb;
+    for (int which = 0; which < 2; ++which)
+      HIP_TRY(t, hipMemcpy2DAsync((char*)t->h_pack_out + which * half, E1 * hb, which ? fp.v : fp.k, F * hb, E1 * hb,
+                                  (size_t)L * H, hipMemcpyDeviceToHost, t->wb));
+    t->st.d2h_bytes += 2 * (int64_t)half;
+  }
+  if (E2 > 0) {
+    const size_t qbytes = 2 * (size_t)L * H * E2 * qrow + 2 * (size_t)L * E2 * 4;
+    int rc = grow_pinned(t, &t->h_qout, &t->h_qout_bytes, qbytes);
+    if (rc) return rc;
+    HIP_TRY(t, hipMemcpyAsync(t->h_qout, t->qout, qbytes, hipMemcpyDeviceToHost, t->wb));
+    t->st.d2h_bytes += (int64_t)qbytes;
   }
   HIP_TRY(t, hipEventRecord(t->ev_pack, t->wb));
   HIP_TRY(t, hipEventRecord(t->ev_arena, st));
   t->arena_pending = true;
-  bool any_host_work = E > 0;
-  for (int b = 0; b < B && !any_host_work; ++b) any_host_work = !plan[b].movers.empty();
+
+  // ---- host job: compact the arenas, file the entrants
+  bool any_host_work = E1 > 0 || E2 > 0;
+  for (int b = 0; b < B && !any_host_work; ++b) any_host_work = !plan[b].mov1.empty() || !plan[b].mov2.empty();
   if (any_host_work) {
     struct Job {
       std::vector<SeqPlan> plan;
-      char* ak;
-      char* av;
-      const char* pack;
+      char *a1k, *a1v;
+      int8_t *a2k, *a2v;
+      float *s2k, *s2v;
+      const char* pack1;  // [2][L][H][E1][D] cache type
+      const char* pack2;  // codes [2][L][H][E2][D], scales [2][L][E2]
       hipEvent_t ev;
-      int L, B, H;
-      size_t cap1, hb;
-      int64_t E;
+      int L, B, H, D;
+      size_t cap1, cap2, hb;
+      int64_t E1, E2;
     };
-    auto job = std::make_shared<Job>(Job{std::move(plan), (char*)t->arena1_k, (char*)t->arena1_v,
-                                         (const char*)t->h_pack_out, t->ev_pack, L, B, H, (size_t)t->cap1, hb, E});
+    auto job = std::make_shared<Job>(Job{std::move(plan), (char*)t->arena1_k, (char*)t->arena1_v, t->arena2_k,
+                                         t->arena2_v, t->ascale_k, t->ascale_v, (const char*)t->h_pack_out,
+                                         (const char*)t->h_qout, t->ev_pack, L, B, H, D, (size_t)t->cap1,
+                                         (size_t)t->cap2, hb, E1, E2});
     t->arena_job = std::async(std::launch::async, [job]() -> int {
       const Job& j = *job;
-      auto row = [&](int which, int l, int b, int h, uint32_t idx) -> char* {
-        return (which ? j.av : j.ak) + ((((size_t)l * j.B + b) * j.H + h) * j.cap1 + idx) * j.hb;
+      auto r1 = [&](int which, int l, int b, int h, uint32_t idx) -> char* {
+        return (which ? j.a1v : j.a1k) + ((((size_t)l * j.B + b) * j.H + h) * j.cap1 + idx) * j.hb;
       };
-      // layers split over a few threads; each layer's rows are independent
-      auto work = [&](int l0, int l1) {
+      auto r2 = [&](int which, int l, int b, int h, uint32_t idx) -> int8_t* {
+        return (which ? j.a2v : j.a2k) + ((((size_t)l * j.B + b) * j.H + h) * j.cap2 + idx) * j.D;
+      };
+      auto s2 = [&](int which, int l, int b, uint32_t idx) -> float* {
+        return (which ? j.s2v : j.s2k) + ((size_t)l * j.B + b) * j.cap2 + idx;
+      };
+      auto moves = [&](int l0, int l1) {
         for (int l = l0; l < l1; ++l)
           for (int b = 0; b < j.B; ++b)
-            for (auto& mv : j.plan[b].movers)
-              for (int which = 0; which < 2; ++which)
-                for (int h = 0; h < j.H; ++h)
-                  std::memcpy(row(which, l, b, h, mv.second), row(which, l, b, h, mv.first), j.hb);
+            for (int which = 0; which < 2; ++which) {
+              for (auto& mv : j.plan[b].mov1)
+                for (int h = 0; h < j.H; ++h) std::memcpy(r1(which, l, b, h, mv.second), r1(which, l, b, h, mv.first), j.hb);
+              for (auto& mv : j.plan[b].mov2) {
+                for (int h = 0; h < j.H; ++h) std::memcpy(r2(which, l, b, h, mv.second), r2(which, l, b, h, mv.first), j.D);
+                *s2(which, l, b, mv.second) = *s2(which, l, b, mv.first);
+              }
+            }
       };
-      // pack_out is [K|V][layer][kv head][entrant][head_dim]
       auto file = [&](int l0, int l1) {
+        const size_t c2half = (size_t)j.L * j.H * j.E2 * j.D;
+        const float* sc = (const float*)(j.pack2 + 2 * c2half);
         for (int l = l0; l < l1; ++l)
-          for (int b = 0; b < j.B; ++b) {
-            const size_t ne = j.plan[b].entrant_pos.size();
-            if (!ne) continue;
-            for (int which = 0; which < 2; ++which)
-              for (int h = 0; h < j.H; ++h)
-                std::memcpy(row(which, l, b, h, j.plan[b].m),
-                            j.pack + ((((size_t)which * j.L + l) * j.H + h) * j.E + j.plan[b].eoff) * j.hb, ne * j.hb);
-          }
+          for (int b = 0; b < j.B; ++b)
+            for (int which = 0; which < 2; ++which) {
+              const SeqPlan& sp = j.plan[b];
+              const size_t n1 = sp.ent1.size(), n2 = sp.ent2.size();
+              for (int h = 0; h < j.H && n1; ++h)
+                std::memcpy(r1(which, l, b, h, sp.m1),
+                            j.pack1 + ((((size_t)which * j.L + l) * j.H + h) * j.E1 + sp.e1off) * j.hb, n1 * j.hb);
+              for (int h = 0; h < j.H && n2; ++h)
+                std::memcpy(r2(which, l, b, h, sp.m2),
+                            j.pack2 + ((((size_t)which * j.L + l) * j.H + h) * j.E2 + sp.e2off) * j.D, n2 * j.D);
+              if (n2) std::memcpy(s2(which, l, b, sp.m2), sc + ((size_t)which * j.L + l) * j.E2 + sp.e2off, n2 * 4);
+            }
       };
       const int nth = std::min(4, j.L);
       auto split = [&](const std::function<void(int, int)>& f) {
@@ -392,8 +508,8 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
         f(0, j.L / nth);
         for (auto& x : th) x.join();
       };
-      split(work);
-      if (j.E > 0) {
+      split(moves);
+      if (j.E1 > 0 || j.E2 > 0) {
         if (hipEventSynchronize(j.ev) != hipSuccess) return TKV_EHIP;
         split(file);
       }

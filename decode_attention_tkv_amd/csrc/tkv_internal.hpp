@@ -143,6 +143,61 @@ struct CopyArgs {
   int32_t kv_heads, head_bytes, elem_bytes;  // head_bytes = head_dim * elem_bytes
 };
 
+// ---- 8-bit host tier codec (codec.hip) ---------------------------------------
+// Quantised rows: codes [2 (K,V)][layers][kv_heads][rows][head_dim] int8 and
+// one fp32 scale per (K|V, layer, row): scales [2][layers][rows].
+struct QPack {
+  int8_t* codes;
+  float* scales;
+  int64_t rows;  // row stride of this pack
+};
+
+// Fetch pack F: every moved row's value, [layers][kv_heads][rows][head_dim]
+struct FPack {
+  void* k;
+  void* v;
+  int64_t rows;
+};
+
+struct QuantOp {
+  uint16_t b;
+  uint32_t src;    // F row
+  uint32_t dst;    // QPack row
+  uint32_t stage;  // staging index that receives the dequantised values, or kNoLoc
+};
+
+struct QuantArgs {
+  RowSpace rows;
+  FPack f;
+  QPack out;
+  int32_t kv_heads, head_dim, elem_bytes;
+};
+
+struct DequantOp {
+  uint16_t b;
+  uint32_t src;  // QPack row
+  uint32_t dst;  // F row
+};
+
+struct DequantArgs {
+  QPack in;
+  FPack f;
+  int32_t kv_heads, head_dim, elem_bytes;
+};
+
+// Stream staging of the 8-bit rows of one layer: codes [B][Hkv][cap2][d] and
+// scales [B][cap2] (K and V each) already copied to the device; dequantise
+// into staging indices [cap1, cap1 + n2).
+struct DequantStageArgs {
+  RowSpace rows;
+  const int8_t* codes_k;
+  const int8_t* codes_v;
+  const float* scale_k;
+  const float* scale_v;
+  int32_t layer, cap1, cap2, batch, kv_heads, head_dim, elem_bytes;
+  int32_t n2[kMaxBatch];
+};
+
 // ---- launchers (attn.hip) -------------------------------------------------
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int head_dim, int group, int chunk,
@@ -160,5 +215,10 @@ hipError_t launch_deltas(const DeltaArgs& a, int batch, hipStream_t s);
 hipError_t launch_set_loc(const LocUpdate* u, int n, uint32_t* loc, int nmax, hipStream_t s);
 hipError_t launch_build_live(const LiveArgs& a, int batch, hipStream_t s);
 hipError_t launch_copy_rows(const CopyArgs& a, const RowOp* ops, int n_ops, int layers, hipStream_t s);
+
+// ---- launchers (codec.hip) --------------------------------------------------
+hipError_t launch_quant_rows(const QuantArgs& a, const QuantOp* ops, int n_ops, int layers, hipStream_t s);
+hipError_t launch_dequant_rows(const DequantArgs& a, const DequantOp* ops, int n_ops, int layers, hipStream_t s);
+hipError_t launch_dequant_stage(const DequantStageArgs& a, int n2max, hipStream_t s);
 
 }  // namespace tkvd

@@ -165,6 +165,18 @@ int tkv_read_tiers(tkv_t* t, uint8_t* tiers, tkv_stream_t stream);
  * [batch][2] = {promotions, demotions}. */
 int tkv_read_deltas(tkv_t* t, tkv_delta* promote, tkv_delta* demote, int32_t* counts);
 
+/* The values attention reads for one live row: host k, v [kv_heads][head_dim]
+ * (handle dtype).  For a T2 row these are its dequantised values.  TKV_ESTATE
+ * for an evicted or unused position, and for a T2 row in stream staging (its
+ * values then exist only as 8-bit codes; see tkv_read_t2). */
+int tkv_read_kv(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, void* k, void* v, tkv_stream_t stream);
+
+/* The 8-bit host copy of one T2 row: host k_codes, v_codes [kv_heads][head_dim]
+ * int8 and scales[2] = {K scale, V scale} (fp32).  TKV_ESTATE if the row is
+ * not in T2. */
+int tkv_read_t2(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, int8_t* k_codes, int8_t* v_codes,
+                float* scales);
+
 #ifdef __cplusplus
 }
 #endif
