@@ -61,6 +61,11 @@ __device__ __forceinline__ float group_max(float x) {
 }
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <typename T>
 __device__ __forceinline__ void unpack(const uint4& u, float* f);
@@ -130,6 +135,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   __shared__ float zs[G][CHUNK];
   __shared__ float red[NW][G];
   __shared__ float osum[NW][G][D];
+  __shared__ uint32_t codes_s[CHUNK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = lane % LPR, rg = lane / LPR;
@@ -152,6 +158,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   const T* stageV = (const T*)a.rows.stage_v + soff;
   const uint32_t cap0 = (uint32_t)a.rows.cap0;
   const uint32_t* locs = a.live_loc + (int64_t)b * a.nmax + j0;
+  for (int r = tid; r < CHUNK; r += 256) codes_s[r] = r < nrows ? locs[r] : 0u;
+  __syncthreads();
 
   float qv[G][EPL];
 #pragma unroll
@@ -173,9 +181,9 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
       const int r = wave * RPW + (it0 + u) * RPI + rg;
       kd[u] = make_uint4(0, 0, 0, 0);
       if (r < nrows) {
-        const uint32_t code = locs[r];
+        const uint32_t code = codes_s[r];
         const T* p = code < cap0 ? poolK + (int64_t)code * rs : stageK + (int64_t)(code - cap0) * rs;
-        kd[u] = load16(p);
+        kd[u] = load16nt(p);
       }
     }
 #pragma unroll
@@ -244,9 +252,9 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
       const int r = wave * RPW + (it0 + u) * RPI + rg;
       vd[u] = make_uint4(0, 0, 0, 0);
       if (r < nrows) {
-        const uint32_t code = locs[r];
+        const uint32_t code = codes_s[r];
         const T* p = code < cap0 ? poolV + (int64_t)code * rs : stageV + (int64_t)(code - cap0) * rs;
-        vd[u] = load16(p);
+        vd[u] = load16nt(p);
       }
     }
 #pragma unroll
