@@ -24,6 +24,8 @@
 //   k_score       one thread per live row: adds the layers' sums (layer
 //                 order) times 1/(L*H) to s.  No atomics anywhere, so every
 //                 result is bitwise reproducible.
+#include <type_traits>
+
 #include "tkv_internal.hpp"
 
 namespace tkvd {
@@ -62,6 +64,12 @@ __device__ __forceinline__ float group_max(float x) {
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
+  const u32x4 v = {u.x, u.y, u.z, u.w};
+  return __builtin_bit_cast(bf16x8, v);
+}
 __device__ __forceinline__ uint4 load16nt(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(256) void k_append(const AppendArgs a) {
 
 // ---------------------------------------------------------------------------
 // Split-K attention, pass 1.  grid (chunks, kv_heads, layer_count*batch).
-template <typename T, int D, int G, int CHUNK>
+template <typename T, int D, int G, int CHUNK, bool MK>
 __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   constexpr int LPR = D * (int)sizeof(T) / 16;  // lanes per row
   constexpr int EPL = 16 / (int)sizeof(T);      // elements per lane
@@ -161,59 +169,120 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   for (int r = tid; r < CHUNK; r += 256) codes_s[r] = r < nrows ? locs[r] : 0u;
   __syncthreads();
 
-  float qv[G][EPL];
+  float mc[G];
+  if constexpr (MK) {
+    // ---- phase 1 on the matrix cores: Z[16 heads x 16 rows] += Q[16 x 32] K^T[32 x 16],
+    // D/32 steps per tile of 16 rows (v_mfma_f32_16x16x32_bf16).  Lane l feeds
+    // head / row (l % 16) and the 8 elements 8*(l/16) of each 32-wide slice;
+    // it receives Z for heads 4*(l/16)..+3 of row (l % 16).  Heads >= G are 0.
+    constexpr int KC = D / 32;
+    constexpr int TILES = RPW / 16;
+    const int hl = lane & 15, kq = lane >> 4;
+    bf16x8 qa[KC];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const T* qp = (const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + g) * D + part * EPL;
-    unpack<T>(load16(qp), qv[g]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[g][e] *= a.qscale;
-  }
-
-  // ---- phase 1: logits and the chunk max
-  float mx[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) mx[g] = -INFINITY;
-  for (int it0 = 0; it0 < ITERS; it0 += U) {
-    uint4 kd[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = wave * RPW + (it0 + u) * RPI + rg;
-      kd[u] = make_uint4(0, 0, 0, 0);
-      if (r < nrows) {
-        const uint32_t code = codes_s[r];
-        const T* p = code < cap0 ? poolK + (int64_t)code * rs : stageK + (int64_t)(code - cap0) * rs;
-        kd[u] = load16nt(p);
-      }
+    for (int kc = 0; kc < KC; ++kc) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (hl < G)
+        u = load16((const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + hl) * D + 32 * kc + 8 * kq);
+      qa[kc] = as_bf16x8(u);
     }
+    float mx[4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = wave * RPW + (it0 + u) * RPI + rg;
-      float kf[EPL];
-      unpack<T>(kd[u], kf);
+    for (int i = 0; i < 4; ++i) mx[i] = -INFINITY;
+    const T* pK = poolK - part * EPL + 8 * kq;  // this lane's 8-element slice of a row
+    const T* sK = stageK - part * EPL + 8 * kq;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float acc = 0.f;
+    for (int t0 = 0; t0 < TILES; t0 += 2) {
+      uint4 kd[2][KC];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(qv[g][e], kf[e], acc);
-        const float z = group_sum<LPR>(acc);
+      for (int tt = 0; tt < 2; ++tt) {
+        const int r = wave * RPW + (t0 + tt) * 16 + hl;
+        const bool ok = t0 + tt < TILES && r < nrows;
+        const uint32_t code = ok ? codes_s[r] : 0u;
+        const T* p = code < cap0 ? pK + (int64_t)code * rs : sK + (int64_t)(code - cap0) * rs;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) kd[tt][kc] = ok ? load16nt(p + 32 * kc) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        if (t0 + tt >= TILES) break;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kc], as_bf16x8(kd[tt][kc]), acc, 0, 0, 0);
+        const int r = wave * RPW + (t0 + tt) * 16 + hl;
         if (r < nrows) {
-          if (part == 0) zs[g][r] = z;
-          mx[g] = fmaxf(mx[g], z);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int h = 4 * kq + i;
+            const float z = acc[i] * a.qscale;
+            if (h < G) zs[h][r] = z;
+            mx[i] = fmaxf(mx[i], z);
+          }
         }
       }
     }
-  }
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = mx[g];
-    for (int off = LPR; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (lane == 0) red[wave][g] = m;
-  }
-  __syncthreads();
-  float mc[G];
+    for (int i = 0; i < 4; ++i) {
+      const float m = group_max<16>(mx[i]);
+      if (hl == 0 && 4 * kq + i < G) red[wave][4 * kq + i] = m;
+    }
+    __syncthreads();
 #pragma unroll
-  for (int g = 0; g < G; ++g) mc[g] = fmaxf(fmaxf(red[0][g], red[1][g]), fmaxf(red[2][g], red[3][g]));
+    for (int g = 0; g < G; ++g) mc[g] = fmaxf(fmaxf(red[0][g], red[1][g]), fmaxf(red[2][g], red[3][g]));
+  } else {
+    float qv[G][EPL];
+  #pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const T* qp = (const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + g) * D + part * EPL;
+      unpack<T>(load16(qp), qv[g]);
+  #pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[g][e] *= a.qscale;
+    }
+
+    // ---- phase 1: logits and the chunk max
+    float mx[G];
+  #pragma unroll
+    for (int g = 0; g < G; ++g) mx[g] = -INFINITY;
+    for (int it0 = 0; it0 < ITERS; it0 += U) {
+      uint4 kd[U];
+  #pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = wave * RPW + (it0 + u) * RPI + rg;
+        kd[u] = make_uint4(0, 0, 0, 0);
+        if (r < nrows) {
+          const uint32_t code = codes_s[r];
+          const T* p = code < cap0 ? poolK + (int64_t)code * rs : stageK + (int64_t)(code - cap0) * rs;
+          kd[u] = load16nt(p);
+        }
+      }
+  #pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = wave * RPW + (it0 + u) * RPI + rg;
+        float kf[EPL];
+        unpack<T>(kd[u], kf);
+  #pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float acc = 0.f;
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) acc = fmaf(qv[g][e], kf[e], acc);
+          const float z = group_sum<LPR>(acc);
+          if (r < nrows) {
+            if (part == 0) zs[g][r] = z;
+            mx[g] = fmaxf(mx[g], z);
+          }
+        }
+      }
+    }
+  #pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float m = mx[g];
+      for (int off = LPR; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+      if (lane == 0) red[wave][g] = m;
+    }
+    __syncthreads();
+  #pragma unroll
+    for (int g = 0; g < G; ++g) mc[g] = fmaxf(fmaxf(red[0][g], red[1][g]), fmaxf(red[2][g], red[3][g]));
+  }
 
   // ---- logits out; p = 2^(z - m) in place; chunk sums
   float ls[G];
@@ -358,12 +427,14 @@ __global__ __launch_bounds__(256) void k_score(const ScoreArgs a) {
   a.s[p] += acc * a.inv_lh;
 }
 
+// Grouped-query heads (G >= 4) of bf16 caches take the matrix-core logits.
 template <typename T, int D, int G>
 hipError_t launch_attn_t(const AttnArgs& a, int chunk, dim3 grid, hipStream_t s) {
+  constexpr bool MK = std::is_same<T, bf16_t>::value && G >= 4;
   switch (chunk) {
-    case 128: k_attn_chunk<T, D, G, 128><<<grid, 256, 0, s>>>(a); break;
-    case 256: k_attn_chunk<T, D, G, 256><<<grid, 256, 0, s>>>(a); break;
-    case 512: k_attn_chunk<T, D, G, 512><<<grid, 256, 0, s>>>(a); break;
+    case 128: k_attn_chunk<T, D, G, 128, MK><<<grid, 256, 0, s>>>(a); break;
+    case 256: k_attn_chunk<T, D, G, 256, MK><<<grid, 256, 0, s>>>(a); break;
+    case 512: k_attn_chunk<T, D, G, 512, MK><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
