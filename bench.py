@@ -18,6 +18,9 @@ the CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +32,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_tkv_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_chunk_7b_traffic.md")
+COPY_BYTES = 1 << 30  # plain device copy used to scale the HBM byte counters
 METRIC = "decode steps/sec (attn+scoring, all layers) at 7B shape; achieved HBM GB/s %peak"
 
 
@@ -106,6 +112,77 @@ def pinned_h2d_gbs(torch, mb=256, reps=20):
     return (mb << 20) / float(np.median(times)) / 1e9
 
 
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def _pmc_rows(d):
+    """Rows of a rocprofv3 counter_collection.csv under directory d."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    return list(csv.DictReader(open(files[0])))
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of
+    `bench.py --pmc-probe` into the traffic summary under profiles/."""
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _pmc_rows(d) if r.get("Counter_Name") == counter]
+        attn = [float(r["Counter_Value"]) for r in rows if "k_attn_chunk" in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()
+                and "k_" not in r["Kernel_Name"]]
+        if not attn or not copy:
+            raise SystemExit("%s: attention or copy dispatches missing" % counter)
+        copy_kib = max(copy)          # the 1 GiB copy is the largest copy dispatch
+        factor = (COPY_BYTES / 1024.0) / copy_kib
+        out[counter] = {"attn_kib_mean": sum(attn) / len(attn), "dispatches": len(attn),
+                        "copy_kib": copy_kib, "factor": factor,
+                        "bytes_per_launch": sum(attn) / len(attn) * 1024.0 * factor}
+    total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    # live K/V bytes per dispatch of the probe: 8 + 24 steps from the 7b prefill, none evicted yet
+    import tkvsynth
+    w = tkvsynth.CONFIGS["7b"]
+    n_disp = out["FETCH_SIZE"]["dispatches"]
+    kv = sum((w.prefill + 1 + t) * w.kv_bytes_per_token() * w.batch for t in range(n_disp)) / n_disp
+    lines = ["# k_attn_chunk HBM traffic, 7b workload (rocprofv3 counters)", "",
+             "Commands (one MI355X, repo root; each counter in its own run):", "",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o pmc -- python bench.py --pmc-probe",
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o pmc -- python bench.py --pmc-probe",
+             "    python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write", "",
+             "`--pmc-probe` runs 8 warmup + 24 decode steps of the 7b workload, then one plain 1 GiB device",
+             "copy (torch copy_) whose counter reading scales KiB to bytes (factor = 1 GiB / counted).", "",
+             "| Counter | attention dispatches | mean KiB / dispatch | copy KiB (1 GiB copy) | scale | bytes / launch |",
+             "|---|---|---|---|---|---|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        o = out[c]
+        lines.append("| %s | %d | %.0f | %.0f | %.4f | %.4g |" % (c, o["dispatches"], o["attn_kib_mean"], o["copy_kib"],
+                                                                o["factor"], o["bytes_per_launch"]))
+    lines += ["", "Live K/V bytes per dispatch of the probe (algorithmic): %.6g" % kv,
+              "", "traffic_bytes_per_launch: %.6g" % total,
+              "traffic_over_kv_bytes: %.6f" % (total / kv),
+              "kernel_source_sha256_16: %s" % kernel_hash()]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    open(TRAFFIC_FILE, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def measured_traffic(kv_bytes_per_launch):
+    """Counter-derived HBM bytes per split-K launch (the probe's traffic-to-
+    live-K/V ratio applied to this run's launches), if the counters were
+    taken on this kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = dict(l.split(": ", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ": " in l and not l.startswith("|"))
+    if kv.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(kv["traffic_over_kv_bytes"]) * kv_bytes_per_launch
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, n_steps):
     """The oracle as it stands, on the host cores: prefill untimed, then
     n_steps decode steps (with its own reassignment every Delta steps)."""
@@ -138,7 +215,14 @@ def main():
     ap.add_argument("--workload", default="7b")
     ap.add_argument("--stream-steps", type=int, default=64, help="timed steps of the stream-staging leg (0: skip)")
     ap.add_argument("--cpu-steps", type=int, default=64, help="oracle steps of the CPU baseline (0: skip)")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="short run for counter collection: 8 + 24 steps, then one 1 GiB device copy")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from two rocprofv3 --pmc runs of --pmc-probe")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the tiered-KV decode path has no multi-GPU leg "
               "(sequences would shard one per GPU with no exchange); run with --gpus 1", file=sys.stderr)
@@ -149,6 +233,8 @@ def main():
     import decode_attention_tkv_amd as tkv
     import tkvsynth
 
+    if args.pmc_probe:
+        args.warmup, args.steps, args.stream_steps, args.cpu_steps = 8, 24, 0, 0
     base = tkvsynth.CONFIGS[args.workload]
     total = args.warmup + args.steps
     # the workload's own decode length, stretched if more steps are asked for
@@ -160,6 +246,13 @@ def main():
     print("[bench] resident staging: %d warmup + %d timed steps" % (args.warmup, args.steps),
           file=sys.stderr, flush=True)
     secs, before, after = run_decode(w, inputs, args.warmup, args.steps, torch, tkv)
+    if args.pmc_probe:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] pmc probe done", file=sys.stderr, flush=True)
+        return
     kern_ms = after["attn_kernel_ms"] - before["attn_kernel_ms"]
     launches = after["attn_kernel_launches"] - before["attn_kernel_launches"]
     kv_bytes = after["attn_kv_bytes"] - before["attn_kv_bytes"]
@@ -188,7 +281,7 @@ def main():
                    "timed_steps": "%d..%d" % (args.warmup + 1, total),
                    "reassignments_timed": int(after["reassigns"] - before["reassigns"])},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(kv_bytes / launches),
                      "kernel": "k_attn_chunk (split-K attention pass)",
                      "avg_launch_us": kern_ms / launches * 1e3, "launches": launches,
                      "kv_bytes_per_launch": kv_bytes / launches},
