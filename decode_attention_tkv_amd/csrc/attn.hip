@@ -365,22 +365,25 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge chunk partials and sum alpha over heads.  grid (tiles, batch,
-// layer_count), block 256; tile t covers live rows [256t, 256t+256).
+// Merge chunk partials and sum alpha over heads.  grid (tiles + ceil(Hq /
+// (256 / D)), batch, layer_count), block 256.  Blocks x < tiles sum alpha over
+// the layer's heads for live rows [256x, 256x + 256); the other blocks merge
+// the chunk partials of 256 / D heads into M, 1 / sum and the output row.
+// Both kinds merge the chunk (max, sum) pairs in chunk order, so they agree.
 template <int D>
 __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
   __shared__ float Ms[kMaxQHeads];
   __shared__ float iLs[kMaxQHeads];
   const int tid = threadIdx.x;
-  const int tile = blockIdx.x, b = blockIdx.y, ll = blockIdx.z;
+  const int x = blockIdx.x, b = blockIdx.y, ll = blockIdx.z;
   const int l = a.layer_begin + ll;
   const int nl = a.nlive[b];
   const int tiles = (nl + 255) / 256;
-  if (tile >= tiles) return;
+  const int tiles_grid = a.tiles_grid;
   const int nch = (nl + a.chunk - 1) / a.chunk;
   const int64_t hbase = ((int64_t)l * a.batch + b) * a.q_heads;
 
-  for (int h = tid; h < a.q_heads; h += 256) {
+  auto merge_head = [&](int h, float* M_out, float* iL_out) {
     const float* ml = a.part_ml + (hbase + h) * a.max_chunks * 2;
     float M = -INFINITY;
 #pragma unroll 8
@@ -388,29 +391,42 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
     float L = 0.f;
 #pragma unroll 8
     for (int c = 0; c < nch; ++c) L += ml[2 * c + 1] * exp2f(ml[2 * c] - M);
-    Ms[h] = M;
-    iLs[h] = 1.f / L;
-  }
-  __syncthreads();
+    *M_out = M;
+    *iL_out = 1.f / L;
+  };
 
-  // output rows of the heads assigned to this tile
-  for (int h = tile; h < a.q_heads; h += tiles) {
+  if (x >= tiles_grid) {
+    // ---- output rows
+    constexpr int HPB = 256 / D;
+    const int h = (x - tiles_grid) * HPB + tid / D, e = tid % D;
+    if (h >= a.q_heads || nl == 0) return;
+    float M, iL;
+    merge_head(h, &M, &iL);
     const float* ml = a.part_ml + (hbase + h) * a.max_chunks * 2;
     const float* po = a.part_o + (hbase + h) * a.max_chunks * D;
-    for (int e = tid; e < D; e += 256) {
-      float acc = 0.f;
+    float acc = 0.f;
 #pragma unroll 8
-      for (int c = 0; c < nch; ++c) acc += po[(int64_t)c * D + e] * exp2f(ml[2 * c] - Ms[h]);
-      a.out[(((int64_t)ll * a.batch + b) * a.q_heads + h) * D + e] = acc * iLs[h];
-    }
+    for (int c = 0; c < nch; ++c) acc += po[(int64_t)c * D + e] * exp2f(ml[2 * c] - M);
+    a.out[(((int64_t)ll * a.batch + b) * a.q_heads + h) * D + e] = acc * iL;
+    return;
   }
-
-  const int j = tile * 256 + tid;
+  if (x >= tiles) return;
+  // ---- per-layer score of 256 live rows
+  const int j = x * 256 + tid;
+  const float* lg = a.logits + hbase * a.nmax + j;
+  constexpr int KP = 32;  // this row's first logits are in flight during the merge
+  float zr[KP];
+#pragma unroll
+  for (int h = 0; h < KP; ++h) zr[h] = (j < nl && h < a.q_heads) ? lg[(int64_t)h * a.nmax] : 0.f;
+  for (int h = tid; h < a.q_heads; h += 256) merge_head(h, &Ms[h], &iLs[h]);
+  __syncthreads();
   if (j < nl) {
     float S = 0.f;
-    const float* lg = a.logits + hbase * a.nmax + j;
+#pragma unroll
+    for (int h = 0; h < KP; ++h)
+      if (h < a.q_heads) S += exp2f(zr[h] - Ms[h]) * iLs[h];
 #pragma unroll 8
-    for (int h = 0; h < a.q_heads; ++h) S += exp2f(lg[(int64_t)h * a.nmax] - Ms[h]) * iLs[h];
+    for (int h = KP; h < a.q_heads; ++h) S += exp2f(lg[(int64_t)h * a.nmax] - Ms[h]) * iLs[h];
     a.layer_score[((int64_t)l * a.batch + b) * a.nmax + j] = S;
   }
 }
@@ -474,7 +490,8 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, int head_dim, int group, in
 
 hipError_t launch_finalize(const FinalizeArgs& a, int head_dim, int layer_count, int tiles_now,
                            hipStream_t s) {
-  const dim3 grid(tiles_now, a.batch, layer_count);
+  const int hpb = 256 / head_dim;
+  const dim3 grid(a.tiles_grid + (a.q_heads + hpb - 1) / hpb, a.batch, layer_count);
   if (head_dim == 128)
     k_finalize<128><<<grid, 256, 0, s>>>(a);
   else if (head_dim == 64)

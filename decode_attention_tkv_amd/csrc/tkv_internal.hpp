@@ -55,6 +55,7 @@ struct FinalizeArgs {
   float* out;     // [layer_count][batch][q_heads][head_dim] fp32
   float* layer_score;  // [layers][batch][nmax]: sum over heads of alpha, per live index
   int32_t layer_begin, batch, q_heads, nmax, max_chunks, chunk;
+  int32_t tiles_grid;  // score blocks in the grid (tiles of the longest sequence)
   int32_t nlive[kMaxBatch];
 };
 
