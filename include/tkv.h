@@ -131,6 +131,8 @@ int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tokens, tkv_st
 
 /* Start a decode step: append one position to every sequence.  k, v: device
  * [layers][batch][kv_heads][head_dim].  The new row enters T0 with score 0.
+ * The copy out of k, v is enqueued on `stream` by this call, so the caller may
+ * reuse them in stream order right after it returns.
  * TKV_ECAPACITY at max_tokens or when the T0 pool is full (reassign first). */
 int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream);
 
