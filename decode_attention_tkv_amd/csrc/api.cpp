@@ -115,7 +115,8 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   tkv_options o{};
   if (opts) o = *opts;
   if (!ratio_ok(o.t2_ratio)) return tkv_fail(nullptr, TKV_EINVAL, "t2_ratio must be in [0, 1]");
-  if (o.chunk == 0) o.chunk = 256;
+  // grouped-query heads (q_heads >= 4 kv_heads) move more partials per row: larger chunks
+  if (o.chunk == 0) o.chunk = (s.q_heads >= 4 * s.kv_heads) ? 512 : 256;
   if (o.chunk != 128 && o.chunk != 256 && o.chunk != 512)
     return tkv_fail(nullptr, TKV_EINVAL, "chunk must be 128, 256 or 512");
   if (o.staging_layers < 0 || o.staging_layers == 1)

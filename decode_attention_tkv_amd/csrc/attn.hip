@@ -66,6 +66,8 @@ __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cas
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   const u32x4 v = {u.x, u.y, u.z, u.w};
   return __builtin_bit_cast(bf16x8, v);
@@ -144,6 +146,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   __shared__ float red[NW][G];
   __shared__ float osum[NW][G][D];
   __shared__ uint32_t codes_s[CHUNK];
+  // matrix-core p.V: P in fp16, 16 (padded) heads x CHUNK rows
+  __shared__ __attribute__((aligned(16))) _Float16 p16[MK ? 16 : 1][MK ? CHUNK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = lane % LPR, rg = lane / LPR;
@@ -297,10 +301,19 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
         lg[r] = z;
         p = exp2f(z - mc[g]);
       }
-      zs[g][r] = p;
-      ls[g] += p;
+      if constexpr (MK) {
+        // the weights the matrix cores use are fp16; the chunk sum uses the same values
+        const _Float16 h = (_Float16)p;
+        p16[g][r] = h;
+        ls[g] += (float)h;
+      } else {
+        zs[g][r] = p;
+        ls[g] += p;
+      }
     }
   }
+  if constexpr (MK)
+    for (int x = tid; x < (16 - G) * CHUNK; x += 256) p16[G + x / CHUNK][x % CHUNK] = (_Float16)0.f;
   __syncthreads();  // all reads of red[] (maxima) done before it is reused below
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -309,46 +322,103 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   }
 
   // ---- phase 2: o = sum_r p_r * v_r
-  float o[G][EPL];
+  if constexpr (MK) {
+    // Matrix cores, O[16 heads][D] += P[16 x 32 rows] V[32 rows x D], no transpose:
+    // lane (hl, kq) loads 16 B (d = 8hl..8hl+7) of rows 8kq..8kq+7 of a 32-row
+    // sub-tile (every load instruction covers 4 full rows), and MFMA #j takes
+    // element j of those 8 rows, so its output columns are d = 8n + j.
+    // V goes to fp16 exactly (bf16 values are fp16 values in its normal range).
+    constexpr int ST = RPW / 32;
+    const int hl = lane & 15, kq = lane >> 4;
+    const T* pV = poolV - part * EPL + 8 * hl;
+    const T* sV = stageV - part * EPL + 8 * hl;
+    f32x4 acc[8];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
-  for (int it0 = 0; it0 < ITERS; it0 += U) {
-    uint4 vd[U];
+    for (int st = 0; st < ST; ++st) {
+      const int rb = wave * RPW + st * 32 + 8 * kq;
+      uint4 vr[8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = wave * RPW + (it0 + u) * RPI + rg;
-      vd[u] = make_uint4(0, 0, 0, 0);
-      if (r < nrows) {
-        const uint32_t code = codes_s[r];
-        const T* p = code < cap0 ? poolV + (int64_t)code * rs : stageV + (int64_t)(code - cap0) * rs;
-        vd[u] = load16nt(p);
+      for (int i = 0; i < 8; ++i) {
+        const int r = rb + i;
+        const uint32_t code = r < nrows ? codes_s[r] : 0u;
+        const T* p = code < cap0 ? pV + (int64_t)code * rs : sV + (int64_t)(code - cap0) * rs;
+        vr[i] = r < nrows ? load16nt(p) : make_uint4(0, 0, 0, 0);
+      }
+      const half8 pa = *reinterpret_cast<const half8*>(&p16[hl][rb]);
+      uint32_t vh[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[t] << 16), __uint_as_float(w[t] & 0xFFFF0000u));
+          vh[i][t] = __builtin_bit_cast(uint32_t, h);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u32x4 bw;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t a0 = vh[2 * t][j >> 1], a1 = vh[2 * t + 1][j >> 1];
+          bw[t] = (j & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
+        }
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(half8, bw), acc[j], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = wave * RPW + (it0 + u) * RPI + rg;
-      if (r < nrows) {
-        float vf[EPL];
-        unpack<T>(vd[u], vf);
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * kq + i;
+      if (h < G) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float pg = zs[g][r];
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(pg, vf[e], o[g][e]);
+        for (int j = 0; j < 8; ++j) osum[wave][h][8 * hl + j] = acc[j][i];
+      }
+    }
+  } else {
+    // ---- phase 2: o = sum_r p_r * v_r
+    float o[G][EPL];
+  #pragma unroll
+    for (int g = 0; g < G; ++g)
+  #pragma unroll
+      for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
+    for (int it0 = 0; it0 < ITERS; it0 += U) {
+      uint4 vd[U];
+  #pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = wave * RPW + (it0 + u) * RPI + rg;
+        vd[u] = make_uint4(0, 0, 0, 0);
+        if (r < nrows) {
+          const uint32_t code = codes_s[r];
+          const T* p = code < cap0 ? poolV + (int64_t)code * rs : stageV + (int64_t)(code - cap0) * rs;
+          vd[u] = load16nt(p);
+        }
+      }
+  #pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = wave * RPW + (it0 + u) * RPI + rg;
+        if (r < nrows) {
+          float vf[EPL];
+          unpack<T>(vd[u], vf);
+  #pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float pg = zs[g][r];
+  #pragma unroll
+            for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(pg, vf[e], o[g][e]);
+          }
         }
       }
     }
+  #pragma unroll
+    for (int g = 0; g < G; ++g)
+  #pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float x = o[g][e];
+        for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
+        if (rg == 0) osum[wave][g][part * EPL + e] = x;
+      }
   }
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float x = o[g][e];
-      for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
-      if (rg == 0) osum[wave][g][part * EPL + e] = x;
-    }
   __syncthreads();
   const int64_t hbase = ((int64_t)l * a.batch + b) * a.q_heads + kvh * G;
   for (int t = tid; t < G * D; t += 256) {

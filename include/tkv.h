@@ -78,7 +78,8 @@ typedef struct {
                              2..layers-1: "stream": each step copies a layer's T1/T2 rows
                              from pinned host memory into slot (layer mod S), one layer
                              ahead of the attention that reads it. */
-  int32_t chunk;          /* split-K rows per work-group: 0 (default 256), 128, 256 or 512 */
+  int32_t chunk;          /* split-K rows per work-group: 128, 256 or 512; 0 = 512 when
+                             q_heads >= 4 * kv_heads, else 256 */
   uint64_t flags;         /* TKV_FLAG_* */
 } tkv_options;
 
