@@ -204,8 +204,10 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
         const bool ok = t0 + tt < TILES && r < nrows;
         const uint32_t code = ok ? codes_s[r] : 0u;
         const T* p = code < cap0 ? pK + (int64_t)code * rs : sK + (int64_t)(code - cap0) * rs;
+        // 64-byte pieces per row per load: a streaming (non-temporal) hint would let
+        // the row's lines leave the cache before the neighbouring piece is read.
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) kd[tt][kc] = ok ? load16nt(p + 32 * kc) : make_uint4(0, 0, 0, 0);
+        for (int kc = 0; kc < KC; ++kc) kd[tt][kc] = ok ? load16(p + 32 * kc) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
