@@ -287,7 +287,10 @@ def main():
                      "kv_bytes_per_launch": kv_bytes / launches},
         "step_hbm_gbs": step_gbs,
         "step_hbm_frac": step_gbs / HBM_PEAK_GBS,
-        "reassign_ms_per_call": (after["reassign_ms"] - before["reassign_ms"]) / max(1, after["reassigns"] - before["reassigns"]),
+        # Host wall time inside tkv_reassign.  The call waits for the tier counts, so it also
+        # covers draining the decode steps still queued on the stream when it was made.
+        "reassign_wall_ms_per_call": (after["reassign_ms"] - before["reassign_ms"])
+        / max(1, after["reassigns"] - before["reassigns"]),
     }
 
     if args.stream_steps > 0:
