@@ -12,8 +12,10 @@ planted heavy hitters) and sit in HBM before the timed region starts.
 Prints one JSON line.  Extra fields: the split-K kernel's roofline (live K/V
 bytes per launch / launch time, HIP events on the launch stream), the
 stream-staging leg (T1 rows copied from pinned host memory one layer ahead
-of attention; H2D GB/s against the pinned H2D bandwidth measured here), and
-the CPU oracle timed on a bounded sample of the same workload.
+of attention; H2D GB/s against the pinned H2D bandwidth measured here), the
+CPU oracle timed on a bounded sample of the same workload, and the parity of
+the GPU with the oracle over that sample (sampled outputs, final scores,
+every reassignment's labels).
 """
 from __future__ import annotations
 
@@ -183,9 +185,36 @@ def measured_traffic(kv_bytes_per_launch):
         return None
 
 
-def cpu_baseline(w, n_steps):
+def gpu_trace(w, inputs, n_steps, torch, tkv, sample_every=16):
+    """The first n_steps decode steps on a fresh handle, recorded for the
+    oracle to follow: outputs at sampled steps, the fp32 scores each
+    reassignment ranks by, the labels it produced, and the final scores."""
+    k0, v0, kn, vn, q = inputs
+    c = tkv.TieredKV.for_workload(w)
+    c.prefill(k0, v0)
+    out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    tr = {"outs": {}, "ranks": [], "labels": []}
+    for t in range(n_steps):
+        c.append(kn[t], vn[t])
+        c.decode_attn(q[t], out)
+        if t % sample_every == 0 or t == n_steps - 1:
+            tr["outs"][t] = out.cpu().numpy()
+        if (t + 1) % w.delta == 0:
+            n = w.prefill + t + 1
+            tr["ranks"].append(c.read_scores()[:, :n])
+            c.reassign()
+            tr["labels"].append(c.read_tiers()[:, :n])
+    tr["s"] = c.read_scores()
+    c.close()
+    return tr
+
+
+def cpu_baseline(w, n_steps, trace=None):
     """The oracle as it stands, on the host cores: prefill untimed, then
-    n_steps decode steps (with its own reassignment every Delta steps)."""
+    n_steps decode steps with a reassignment every Delta steps.  Given the
+    GPU's trace of the same steps, the oracle ranks on the GPU's fp32 scores
+    (the labelling decision is taken in the kernel's precision) and, after
+    the timed loop, the two runs are compared."""
     import oracle
     heavy, u = w.heavy_mask(), w.unit_vector()
     o = oracle.OracleTKV.for_workload(w)
@@ -193,18 +222,37 @@ def cpu_baseline(w, n_steps):
     kn = w.values(w.kv(0, w.prefill, n_steps, heavy, u))
     vn = w.values(w.kv(1, w.prefill, n_steps, heavy, u))
     q = w.values(w.q(0, n_steps, u))
+    refs, labels = {}, []
     t0 = time.perf_counter()
     for t in range(n_steps):
         o.append(kn[:, :, t], vn[:, :, t])
-        o.attend(q[t])
+        ref = o.attend(q[t])
+        if trace is not None and t in trace["outs"]:
+            refs[t] = ref
         if (t + 1) % w.delta == 0:
-            o.reassign()
+            ranks = trace["ranks"][len(labels)] if trace is not None else None
+            new, _ = o.reassign(rank_scores=ranks)
+            labels.append(new)
     secs = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
-    return {"value": n_steps / secs, "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": "7b workload, prefill %d, decode steps 1..%d incl. %d reassignment(s); fp64 C "
-                      "attention (OpenMP) + numpy scoring/tiering; %.1f s"
-                      % (w.prefill, n_steps, n_steps // w.delta, secs)}
+    res = {"value": n_steps / secs, "unit": "steps/s", "cores": threads, "kind": "oracle",
+           "sample": "%s workload, prefill %d, decode steps 1..%d incl. %d reassignment(s); fp64 C "
+                     "attention (OpenMP) + numpy scoring/tiering; %.1f s"
+                     % (w.name, w.prefill, n_steps, n_steps // w.delta, secs)}
+    if trace is None:
+        return res, None
+    n = o.n
+    out_err = max(float(np.max(np.abs(trace["outs"][t] - refs[t]))) for t in refs)
+    g = trace["s"][:, :n].astype(np.float64)
+    r = o.s[:, :n]
+    m = r > 0
+    s_rel = float(np.max(np.abs(g[m] - r[m]) / r[m])) if m.any() else 0.0
+    same = all(np.array_equal(a, b) for a, b in zip(trace["labels"], labels))
+    tol = 5e-3 if w.dtype == "bf16" else 1e-5
+    parity = {"steps": n_steps, "sampled_steps": len(refs), "out_max_abs": out_err, "out_tol": tol,
+              "score_max_rel": s_rel, "score_tol": 1e-4, "reassignments": len(labels),
+              "labels_bit_exact": same, "ok": bool(out_err <= tol and s_rel <= 1e-4 and same)}
+    return res, parity
 
 
 def main():
@@ -214,7 +262,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="7b")
     ap.add_argument("--stream-steps", type=int, default=64, help="timed steps of the stream-staging leg (0: skip)")
-    ap.add_argument("--cpu-steps", type=int, default=64, help="oracle steps of the CPU baseline (0: skip)")
+    ap.add_argument("--cpu-steps", type=int, default=192,
+                    help="steps of the CPU oracle baseline and of the parity check beside it (0: skip)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short run for counter collection: 8 + 24 steps, then one 1 GiB device copy")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -303,11 +352,18 @@ def main():
             "h2d_gbs": h2d / ssecs / 1e9, "pinned_h2d_gbs": pinned,
             "h2d_frac_of_pinned": (h2d / ssecs / 1e9) / pinned,
             "h2d_bytes_per_step": h2d / args.stream_steps,
+            # max(H2D time at the pinned rate, resident step time) / stream step time: 1.0 means the
+            # layer-ahead copies hide the compute completely (or the compute hides the copies)
+            "overlap_efficiency": max(h2d / args.stream_steps / (pinned * 1e9), secs / args.steps)
+            / (ssecs / args.stream_steps),
             "hbm_kv_bytes_allocated": sa["hbm_bytes"], "full_cache_bytes": sa["full_cache_bytes"]}
 
+    args.cpu_steps = min(args.cpu_steps, w.steps)
     if args.cpu_steps > 0:
+        print("[bench] parity trace: %d GPU steps" % args.cpu_steps, file=sys.stderr, flush=True)
+        trace = gpu_trace(w, inputs, args.cpu_steps, torch, tkv)
         print("[bench] cpu baseline: oracle, %d steps" % args.cpu_steps, file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(w, args.cpu_steps, trace)
 
     print(json.dumps(result), flush=True)
 

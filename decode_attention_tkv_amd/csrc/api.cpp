@@ -155,6 +155,7 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   t->cap2 = o.t2_ratio > 0 ? (int)std::min<int64_t>(nmax, floor_ratio(o.t2_ratio, nmax) + 1) : 0;
   t->capS = t->cap1 + t->cap2;
   t->max_chunks = (int)((nmax + t->chunk - 1) / t->chunk);
+  t->lstride = (int)((nmax + kLogitAlign - 1) / kLogitAlign * kLogitAlign);
 
   const size_t L = t->L, B = t->B, Hq = t->Hq;
   int rc = TKV_OK;
@@ -170,10 +171,10 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   dev((void**)&t->tier, B * nmax);
   dev((void**)&t->loc, B * nmax * 4);
   dev((void**)&t->s, B * nmax * 4);
-  dev((void**)&t->logits, L * B * Hq * nmax * 4);
+  dev((void**)&t->logits, L * B * Hq * t->lstride * 4);
   dev((void**)&t->part_ml, L * B * Hq * t->max_chunks * 2 * 4);
   dev((void**)&t->part_o, L * B * Hq * t->max_chunks * t->D * 4);
-  dev((void**)&t->layer_score, L * B * nmax * 4);
+  dev((void**)&t->layer_score, L * B * t->lstride * 4);
   dev((void**)&t->tier_alt, B * nmax);
   dev((void**)&t->d_promote, B * nmax * sizeof(tkv_delta));
   dev((void**)&t->d_demote, B * nmax * sizeof(tkv_delta));
@@ -434,6 +435,7 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
   a.kv_heads = t->Hkv;
   a.nmax = t->nmax;
   a.max_chunks = t->max_chunks;
+  a.lstride = t->lstride;
   for (int b = 0; b < t->B; ++b) a.nlive[b] = t->nlive[b];
   const int chunks_now = (max_live + t->chunk - 1) / t->chunk;
   const bool timed = (t->flags & TKV_FLAG_TIME_KERNELS) != 0;
@@ -463,6 +465,7 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
   f.nmax = t->nmax;
   f.max_chunks = t->max_chunks;
   f.chunk = t->chunk;
+  f.lstride = t->lstride;
   for (int b = 0; b < t->B; ++b) f.nlive[b] = t->nlive[b];
   const int tiles_now = (max_live + 255) / 256;
   f.tiles_grid = tiles_now;
@@ -575,6 +578,7 @@ extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_coun
     sa.layers = t->L;
     sa.batch = t->B;
     sa.nmax = t->nmax;
+    sa.lstride = t->lstride;
     for (int b = 0; b < t->B; ++b) sa.nlive[b] = t->nlive[b];
     const int tiles_now = (max_live + 255) / 256;
     if (tiles_now > 0) HIP_TRY(t, launch_score(sa, tiles_now, st));

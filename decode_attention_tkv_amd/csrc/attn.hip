@@ -15,9 +15,15 @@
 //                 is loaded once for all G query heads of its kv head.  The
 //                 dot products reduce over the LPR lanes with DPP butterflies
 //                 (quad_perm, row_half_mirror, row_mirror), the chunk max and
-//                 sums with DPP + LDS in a fixed order.  Phase 1 writes the
-//                 log2-scaled logits; phase 2 forms p = 2^(z - m_chunk) once
-//                 per (head, row) in LDS and accumulates p * V.
+//                 sums with DPP + LDS in a fixed order.  Phase 1 keeps the
+//                 log2-scaled logits in LDS; phase 2 forms p = 2^(z - m_chunk)
+//                 once per (head, row) and accumulates p * V.  Grouped-query
+//                 heads (G >= 4) of bf16 caches do both contractions on the
+//                 matrix cores instead.  The block's outputs (logits, chunk
+//                 max/sum, partial o) leave last, as non-temporal stores:
+//                 writes mixed into the read stream cost the HBM far more
+//                 than their size, so the kernel writes only what Eq. 1 and
+//                 the merge need.
 //   k_finalize    one work-group per (256 live rows, sequence, layer): merges
 //                 the chunk partials in chunk order into M, 1/sum and out, and
 //                 sums alpha over the layer's heads for its rows.
@@ -142,7 +148,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   constexpr int U = ITERS < UB ? ITERS : UB;    // loads in flight per lane per batch
   static_assert(RPW % RPI == 0 && ITERS % U == 0, "chunk shape");
 
-  __shared__ float zs[G][CHUNK];
+  __shared__ float zs[G][CHUNK];                       // logits (log2 units), kept to the end
+  __shared__ float ps[MK ? 1 : G][MK ? 1 : CHUNK];     // p = 2^(z - m) of the vector path
   __shared__ float red[NW][G];
   __shared__ float osum[NW][G][D];
   __shared__ uint32_t codes_s[CHUNK];
@@ -290,26 +297,23 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
     for (int g = 0; g < G; ++g) mc[g] = fmaxf(fmaxf(red[0][g], red[1][g]), fmaxf(red[2][g], red[3][g]));
   }
 
-  // ---- logits out; p = 2^(z - m) in place; chunk sums
+  // ---- p = 2^(z - m) and the chunk sums.  The logits go out at the very end:
+  // a global store ahead of a barrier would hold every wave at that barrier
+  // until the store is acknowledged.
   float ls[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     ls[g] = 0.f;
-    float* lg = a.logits + (((int64_t)l * a.batch + b) * a.q_heads + kvh * G + g) * a.nmax + j0;
     for (int r = tid; r < CHUNK; r += 256) {
       float p = 0.f;
-      if (r < nrows) {
-        const float z = zs[g][r];
-        lg[r] = z;
-        p = exp2f(z - mc[g]);
-      }
+      if (r < nrows) p = exp2f(zs[g][r] - mc[g]);
       if constexpr (MK) {
         // the weights the matrix cores use are fp16; the chunk sum uses the same values
         const _Float16 h = (_Float16)p;
         p16[g][r] = h;
         ls[g] += (float)h;
       } else {
-        zs[g][r] = p;
+        ps[g][r] = p;
         ls[g] += p;
       }
     }
@@ -405,7 +409,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
           unpack<T>(vd[u], vf);
   #pragma unroll
           for (int g = 0; g < G; ++g) {
-            const float pg = zs[g][r];
+            const float pg = ps[g][r];
   #pragma unroll
             for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(pg, vf[e], o[g][e]);
           }
@@ -426,13 +430,19 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   for (int t = tid; t < G * D; t += 256) {
     const int g = t / D, e = t % D;
     const float x = ((osum[0][g][e] + osum[1][g][e]) + osum[2][g][e]) + osum[3][g][e];
-    a.part_o[((hbase + g) * a.max_chunks + c) * D + e] = x;
+    __builtin_nontemporal_store(x, a.part_o + ((hbase + g) * a.max_chunks + c) * D + e);
   }
-  if (tid < G) {
-    const float s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-    float* ml = a.part_ml + ((hbase + tid) * a.max_chunks + c) * 2;
-    ml[0] = mc[tid];
-    ml[1] = s;
+  if (tid < 2 * G) {
+    const int g = tid >> 1;
+    const float v = (tid & 1) ? ((red[0][g] + red[1][g]) + red[2][g]) + red[3][g] : mc[g];
+    __builtin_nontemporal_store(v, a.part_ml + ((hbase + g) * a.max_chunks + c) * 2 + (tid & 1));
+  }
+  // logits, padded with zeros to the line that holds the chunk's last row
+  const int nw = min(CHUNK, (nrows + 31) / 32 * 32);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float* lg = a.logits + (hbase + g) * a.lstride + j0;
+    for (int r = tid; r < nw; r += 256) __builtin_nontemporal_store(r < nrows ? zs[g][r] : 0.f, lg + r);
   }
 }
 
@@ -485,21 +495,24 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
   if (x >= tiles) return;
   // ---- per-layer score of 256 live rows
   const int j = x * 256 + tid;
-  const float* lg = a.logits + hbase * a.nmax + j;
+  const float* lg = a.logits + hbase * a.lstride + j;
   constexpr int KP = 32;  // this row's first logits are in flight during the merge
   float zr[KP];
 #pragma unroll
-  for (int h = 0; h < KP; ++h) zr[h] = (j < nl && h < a.q_heads) ? lg[(int64_t)h * a.nmax] : 0.f;
+  for (int h = 0; h < KP; ++h) zr[h] = (j < nl && h < a.q_heads) ? lg[(int64_t)h * a.lstride] : 0.f;
   for (int h = tid; h < a.q_heads; h += 256) merge_head(h, &Ms[h], &iLs[h]);
   __syncthreads();
+  float* ls_row = a.layer_score + ((int64_t)l * a.batch + b) * a.lstride;
   if (j < nl) {
     float S = 0.f;
 #pragma unroll
     for (int h = 0; h < KP; ++h)
       if (h < a.q_heads) S += exp2f(zr[h] - Ms[h]) * iLs[h];
 #pragma unroll 8
-    for (int h = KP; h < a.q_heads; ++h) S += exp2f(lg[(int64_t)h * a.nmax] - Ms[h]) * iLs[h];
-    a.layer_score[((int64_t)l * a.batch + b) * a.nmax + j] = S;
+    for (int h = KP; h < a.q_heads; ++h) S += exp2f(lg[(int64_t)h * a.lstride] - Ms[h]) * iLs[h];
+    ls_row[j] = S;
+  } else if (j < (nl + 31) / 32 * 32) {
+    ls_row[j] = 0.f;  // the rest of the last line
   }
 }
 
@@ -510,7 +523,7 @@ __global__ __launch_bounds__(256) void k_score(const ScoreArgs a) {
   if (j >= a.nlive[b]) return;
   float acc = 0.f;
 #pragma unroll 8
-  for (int l = 0; l < a.layers; ++l) acc += a.layer_score[((int64_t)l * a.batch + b) * a.nmax + j];
+  for (int l = 0; l < a.layers; ++l) acc += a.layer_score[((int64_t)l * a.batch + b) * a.lstride + j];
   const int64_t p = (int64_t)b * a.nmax + a.live_pos[(int64_t)b * a.nmax + j];
   a.s[p] += acc * a.inv_lh;
 }

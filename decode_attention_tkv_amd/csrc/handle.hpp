@@ -21,6 +21,7 @@ struct tkv {
   int prompt = 0, sinks = 0, recent = 0;
   uint64_t flags = 0;
   int cap0 = 0, cap1 = 0, cap2 = 0, capS = 0, max_chunks = 0;
+  int lstride = 0;  // logits row stride: nmax rounded up to whole lines
   int64_t row_elems = 0, row_bytes = 0;
 
   // ---- device buffers (owned)
@@ -33,10 +34,10 @@ struct tkv {
   uint8_t* tier = nullptr;       // [B][nmax]
   uint32_t* loc = nullptr;       // [B][nmax]
   float* s = nullptr;            // [B][nmax]
-  float* logits = nullptr;       // [L][B][Hq][nmax]
+  float* logits = nullptr;       // [L][B][Hq][lstride]
   float* part_ml = nullptr;      // [L][B][Hq][max_chunks][2]
   float* part_o = nullptr;       // [L][B][Hq][max_chunks][D]
-  float* layer_score = nullptr;  // [L][B][nmax]
+  float* layer_score = nullptr;  // [L][B][lstride]
   uint8_t* tier_alt = nullptr;   // [B][nmax] labels being computed by a reassignment
   tkv_delta* d_promote = nullptr;  // [B][nmax]
   tkv_delta* d_demote = nullptr;   // [B][nmax]

@@ -36,15 +36,19 @@ struct RowSpace {
   int32_t stage_slots;
 };
 
+// Logits and per-layer score rows are padded to kLogitAlign floats, so every
+// chunk's stores start on a line boundary.
+constexpr int kLogitAlign = 64;
+
 struct AttnArgs {
   RowSpace rows;
   const uint32_t* live_loc;  // [batch][nmax] loc code of live index j (ascending position)
   const void* q;             // [layer_count][batch][q_heads][head_dim]
-  float* logits;             // [layers][batch][q_heads][nmax], log2-scaled q.k/sqrt(d)
+  float* logits;             // [layers][batch][q_heads][lstride], log2-scaled q.k/sqrt(d)
   float* part_ml;            // [layers][batch][q_heads][max_chunks][2] chunk (max, sum)
   float* part_o;             // [layers][batch][q_heads][max_chunks][head_dim]
   float qscale;              // log2(e) / sqrt(head_dim)
-  int32_t layer_begin, batch, q_heads, kv_heads, nmax, max_chunks;
+  int32_t layer_begin, batch, q_heads, kv_heads, nmax, max_chunks, lstride;
   int32_t nlive[kMaxBatch];
 };
 
@@ -53,18 +57,18 @@ struct FinalizeArgs {
   const float* part_ml;
   const float* part_o;
   float* out;     // [layer_count][batch][q_heads][head_dim] fp32
-  float* layer_score;  // [layers][batch][nmax]: sum over heads of alpha, per live index
-  int32_t layer_begin, batch, q_heads, nmax, max_chunks, chunk;
+  float* layer_score;  // [layers][batch][lstride]: sum over heads of alpha, per live index
+  int32_t layer_begin, batch, q_heads, nmax, max_chunks, chunk, lstride;
   int32_t tiles_grid;  // score blocks in the grid (tiles of the longest sequence)
   int32_t nlive[kMaxBatch];
 };
 
 struct ScoreArgs {
-  const float* layer_score;
-  const int32_t* live_pos;  // [batch][nmax]
-  float* s;                 // [batch][nmax] by position
-  float inv_lh;             // 1 / (layers * q_heads)
-  int32_t layers, batch, nmax;
+  const float* layer_score;  // [layers][batch][lstride]
+  const int32_t* live_pos;   // [batch][nmax]
+  float* s;                  // [batch][nmax] by position
+  float inv_lh;              // 1 / (layers * q_heads)
+  int32_t layers, batch, nmax, lstride;
   int32_t nlive[kMaxBatch];
 };
 
