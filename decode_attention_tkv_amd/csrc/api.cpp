@@ -379,7 +379,9 @@ extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t s
     a.slot[b] = t->free0[b].back();
     a.nlive[b] = t->nlive[b];
   }
-  HIP_TRY(t, launch_append(a, (hipStream_t)stream));
+  HIP_TRY(t, launch_append(a, t->score_pending ? &t->pending_score : nullptr, t->pending_tiles,
+                           (hipStream_t)stream));
+  t->score_pending = false;
   for (int b = 0; b < t->B; ++b) {
     t->free0[b].pop_back();
     const size_t off = (size_t)b * t->nmax + t->n;
@@ -580,8 +582,10 @@ extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_coun
     sa.nmax = t->nmax;
     sa.lstride = t->lstride;
     for (int b = 0; b < t->B; ++b) sa.nlive[b] = t->nlive[b];
-    const int tiles_now = (max_live + 255) / 256;
-    if (tiles_now > 0) HIP_TRY(t, launch_score(sa, tiles_now, st));
+    // applied by the next append's launch (or by tkv_flush_score)
+    t->pending_score = sa;
+    t->pending_tiles = (max_live + 255) / 256;
+    t->score_pending = t->pending_tiles > 0;
     t->step += 1;
     t->state = TkvState::Ready;
   }
@@ -610,8 +614,16 @@ extern "C" int tkv_stats(tkv_t* t, tkv_stats_t* out) {
   return TKV_OK;
 }
 
+int tkv_flush_score(tkv* t, hipStream_t stream) {
+  if (!t->score_pending) return TKV_OK;
+  HIP_TRY(t, launch_score(t->pending_score, t->pending_tiles, stream));
+  t->score_pending = false;
+  return TKV_OK;
+}
+
 extern "C" int tkv_read_scores(tkv_t* t, float* scores, tkv_stream_t stream) {
   if (!t || !scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (int rc = tkv_flush_score(t, (hipStream_t)stream)) return rc;
   HIP_TRY(t, hipMemcpyAsync(scores, t->s, (size_t)t->B * t->nmax * 4, hipMemcpyDeviceToHost, (hipStream_t)stream));
   HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
   return TKV_OK;
@@ -620,6 +632,7 @@ extern "C" int tkv_read_scores(tkv_t* t, float* scores, tkv_stream_t stream) {
 extern "C" int tkv_write_scores(tkv_t* t, const float* scores, tkv_stream_t stream) {
   if (!t || !scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "step in progress");
+  if (int rc = tkv_flush_score(t, (hipStream_t)stream)) return rc;
   HIP_TRY(t, hipMemcpyAsync(t->s, scores, (size_t)t->B * t->nmax * 4, hipMemcpyHostToDevice, (hipStream_t)stream));
   HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
   return TKV_OK;

@@ -28,8 +28,10 @@
 //                 the chunk partials in chunk order into M, 1/sum and out, and
 //                 sums alpha over the layer's heads for its rows.
 //   k_score       one thread per live row: adds the layers' sums (layer
-//                 order) times 1/(L*H) to s.  No atomics anywhere, so every
-//                 result is bitwise reproducible.
+//                 order) times 1/(L*H) to s.  The same code normally runs in
+//                 the next step's append launch, saving a launch per step.
+//                 No atomics anywhere, so every result is bitwise
+//                 reproducible.
 #include <type_traits>
 
 #include "tkv_internal.hpp"
@@ -104,14 +106,35 @@ __device__ __forceinline__ void unpack<float>(const uint4& u, float* f) {
   f[3] = __uint_as_float(u.w);
 }
 
+// Eq. 1 update for live rows [256 tile, 256 tile + 256) of sequence b:
+// s[pos(j)] += (sum over layers, in order) * 1/(L*H).
+__device__ __forceinline__ void score_rows(const ScoreArgs& a, int tile, int b) {
+  const int j = tile * 256 + threadIdx.x;
+  if (j >= a.nlive[b]) return;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int l = 0; l < a.layers; ++l) acc += a.layer_score[((int64_t)l * a.batch + b) * a.lstride + j];
+  const int64_t p = (int64_t)b * a.nmax + a.live_pos[(int64_t)b * a.nmax + j];
+  a.s[p] += acc * a.inv_lh;
+}
+
 // ---------------------------------------------------------------------------
 // Append: copy the new token's K/V rows of every (layer, sequence) into its
-// T0 slot and extend the live list.  grid (layers*batch, 2), block 256.
-__global__ __launch_bounds__(256) void k_append(const AppendArgs a) {
-  const int lb = blockIdx.x;
+// T0 slot and extend the live list.  Blocks [0, 2*layers*batch) copy (one per
+// (layer, sequence, K|V)); the fold_tiles*batch blocks after them apply the
+// previous step's Eq. 1 update, which reads only positions and live indices
+// below the ones the append writes.  Block 256.
+__global__ __launch_bounds__(256) void k_append(const AppendArgs a, const ScoreArgs f, int fold_tiles) {
+  const int nappend = 2 * a.layers * a.batch;
+  if ((int)blockIdx.x >= nappend) {
+    const int y = blockIdx.x - nappend;
+    score_rows(f, y % fold_tiles, y / fold_tiles);
+    return;
+  }
+  const int lb = blockIdx.x >> 1;
   const int b = lb % a.batch;
   const int l = lb / a.batch;
-  const int which = blockIdx.y;
+  const int which = blockIdx.x & 1;
   const int head_bytes = a.head_dim * a.elem_bytes;
   const int row_bytes = a.kv_heads * head_bytes;
   const char* src = (const char*)(which ? a.v : a.k) + (int64_t)lb * row_bytes;
@@ -516,17 +539,8 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
   }
 }
 
-// Eq. 1 update: s[pos(j)] += (sum over layers, in order) * 1/(L*H).
-__global__ __launch_bounds__(256) void k_score(const ScoreArgs a) {
-  const int b = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= a.nlive[b]) return;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int l = 0; l < a.layers; ++l) acc += a.layer_score[((int64_t)l * a.batch + b) * a.lstride + j];
-  const int64_t p = (int64_t)b * a.nmax + a.live_pos[(int64_t)b * a.nmax + j];
-  a.s[p] += acc * a.inv_lh;
-}
+// Eq. 1 update on its own: grid (tiles, batch).
+__global__ __launch_bounds__(256) void k_score(const ScoreArgs a) { score_rows(a, blockIdx.x, blockIdx.y); }
 
 // Grouped-query heads (G >= 4) of bf16 caches take the matrix-core logits.
 template <typename T, int D, int G>
@@ -555,8 +569,10 @@ hipError_t launch_attn_g(const AttnArgs& a, int group, int chunk, dim3 grid, hip
 
 }  // namespace
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
-  k_append<<<dim3(a.layers * a.batch, 2), 256, 0, s>>>(a);
+hipError_t launch_append(const AppendArgs& a, const ScoreArgs* fold, int fold_tiles, hipStream_t s) {
+  ScoreArgs f{};
+  if (fold) f = *fold; else fold_tiles = 0;
+  k_append<<<dim3(2 * a.layers * a.batch + fold_tiles * a.batch), 256, 0, s>>>(a, f, fold_tiles);
   return hipGetLastError();
 }
 

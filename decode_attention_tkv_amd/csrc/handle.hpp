@@ -88,6 +88,11 @@ struct tkv {
   int64_t step = 0;
   int layers_done = 0;
   TkvState state = TkvState::Empty;
+  // The last completed step's Eq. 1 update of s, not yet applied: it runs
+  // in the next append's launch, or before anything else reads or writes s.
+  bool score_pending = false;
+  tkvd::ScoreArgs pending_score{};
+  int pending_tiles = 0;
   std::vector<int32_t> nlive;                 // [B] live rows
   std::vector<std::vector<int32_t>> free0;    // [B] free T0 slots (back = next to use)
   std::vector<uint8_t> h_tier;                // [B][nmax]

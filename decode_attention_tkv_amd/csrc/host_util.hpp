@@ -10,6 +10,9 @@
 
 int tkv_fail(tkv* t, int code, const char* fmt, ...);
 
+// Apply a pending Eq. 1 update of s on `stream` (no-op when none is pending).
+int tkv_flush_score(tkv* t, hipStream_t stream);
+
 #define HIP_TRY(t, call)                                                                       \
   do {                                                                                         \
     hipError_t e_ = (call);                                                                    \

@@ -99,6 +99,7 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   if (t->n == 0) return TKV_OK;
   const auto wall0 = std::chrono::steady_clock::now();
   hipStream_t st = (hipStream_t)stream;
+  if (int rc = tkv_flush_score(t, st)) return rc;  // ranking reads s
   const int B = t->B, L = t->L, n = t->n, H = t->Hkv, D = t->D;
   const size_t nmax = t->nmax;
   const size_t hb = (size_t)D * t->esz;  // bytes of one head's row

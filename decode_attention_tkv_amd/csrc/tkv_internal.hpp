@@ -204,7 +204,9 @@ struct DequantStageArgs {
 };
 
 // ---- launchers (attn.hip) -------------------------------------------------
-hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+// fold != nullptr: the same launch also applies a pending Eq. 1 update
+// (fold_tiles tiles of 256 live rows per sequence); the two touch disjoint data.
+hipError_t launch_append(const AppendArgs& a, const ScoreArgs* fold, int fold_tiles, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int head_dim, int group, int chunk,
                        int layer_count, int chunks_now, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, int head_dim, int layer_count, int tiles_now,

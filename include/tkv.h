@@ -141,8 +141,11 @@ int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream);
  * current step (Method §3): every non-evicted row of every tier takes part.
  * q: device [layer_count][batch][q_heads][head_dim] (handle dtype);
  * out: device fp32 [layer_count][batch][q_heads][head_dim].  Layer groups of
- * one step must be called in order and cover every layer once; when the last
- * layer is done the step's Eq. 1 increment is added to the scores. */
+ * one step must be called in order and cover every layer once.  The step's
+ * Eq. 1 increment of the scores (Method §2) is applied in stream order before
+ * anything that reads or writes them: it runs inside the next tkv_append's
+ * launch, or first thing in tkv_reassign, tkv_read_scores or tkv_write_scores
+ * on the stream given to that call. */
 int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
                     tkv_stream_t stream);
 
