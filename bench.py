@@ -264,6 +264,8 @@ def main():
     ap.add_argument("--stream-steps", type=int, default=64, help="timed steps of the stream-staging leg (0: skip)")
     ap.add_argument("--cpu-steps", type=int, default=192,
                     help="steps of the CPU oracle baseline and of the parity check beside it (0: skip)")
+    ap.add_argument("--baseline-steps", type=int, default=None,
+                    help="timed steps of each baseline policy on the same engine (default: --steps; 0: skip)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short run for counter collection: 8 + 24 steps, then one 1 GiB device copy")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -283,7 +285,7 @@ def main():
     import tkvsynth
 
     if args.pmc_probe:
-        args.warmup, args.steps, args.stream_steps, args.cpu_steps = 8, 24, 0, 0
+        args.warmup, args.steps, args.stream_steps, args.cpu_steps, args.baseline_steps = 8, 24, 0, 0, 0
     base = tkvsynth.CONFIGS[args.workload]
     total = args.warmup + args.steps
     # the workload's own decode length, stretched if more steps are asked for
@@ -357,6 +359,32 @@ def main():
             "overlap_efficiency": max(h2d / args.stream_steps / (pinned * 1e9), secs / args.steps)
             / (ssecs / args.stream_steps),
             "hbm_kv_bytes_allocated": sa["hbm_bytes"], "full_cache_bytes": sa["full_cache_bytes"]}
+
+    if args.baseline_steps is None:
+        args.baseline_steps = args.steps
+    if args.baseline_steps > 0:
+        # the same engine under other policies, same inputs and step window
+        result["baselines"] = {}
+        policies = (("full cache (all rows in T0)", dict(hbm_ratio=1.0, evict_ratio=0.0)),
+                    ("eviction only, heavy hitters (no T1)", dict(no_t1=True)),
+                    ("sinks + recent window", dict(hbm_ratio=0.0, no_t1=True, prompt=0)))
+        result["baselines"]["tiered (this line)"] = {
+            "steps_per_s": steps_per_s, "live_rows_per_seq_at_end":
+                (after["tier_count"][0] + after["tier_count"][1] + after["tier_count"][2]) / w.batch,
+            "hbm_ratio": w.hbm_ratio, "evict_ratio": w.evict_ratio, "no_t1": False,
+            "kernel_gbs": achieved, "host_bytes": after["host_bytes"]}
+        for name, kw in policies:
+            print("[bench] baseline %s: %d timed steps" % (name, args.baseline_steps), file=sys.stderr, flush=True)
+            wb = w.replace(**kw)
+            bsecs, bb, ba = run_decode(wb, inputs, args.warmup, args.baseline_steps, torch, tkv)
+            live = (ba["tier_count"][0] + ba["tier_count"][1] + ba["tier_count"][2]) / w.batch
+            kb = ba["attn_kv_bytes"] - bb["attn_kv_bytes"]
+            km = ba["attn_kernel_ms"] - bb["attn_kernel_ms"]
+            result["baselines"][name] = {
+                "steps_per_s": args.baseline_steps / bsecs, "live_rows_per_seq_at_end": live,
+                "hbm_ratio": wb.hbm_ratio, "evict_ratio": wb.evict_ratio, "no_t1": wb.no_t1,
+                "kernel_gbs": kb / (km / 1e3) / 1e9 if km > 0 else None,
+                "host_bytes": ba["host_bytes"]}
 
     args.cpu_steps = min(args.cpu_steps, w.steps)
     if args.cpu_steps > 0:

@@ -151,7 +151,7 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   const int64_t pmax = std::min<int64_t>(nmax, (int64_t)std::max(protect.prompt, protect.sinks) + protect.recent);
   const int64_t h_at_max = floor_ratio(hbm_ratio, nmax);
   t->cap0 = (int)std::min<int64_t>(nmax, std::max(pmax, h_at_max) + delta + 1);
-  t->cap1 = (int)std::max<int64_t>(1, std::min<int64_t>(nmax, nmax - h_at_max + 1));
+  t->cap1 = (o.flags & TKV_FLAG_NO_T1) ? 1 : (int)std::max<int64_t>(1, std::min<int64_t>(nmax, nmax - h_at_max + 1));
   t->cap2 = o.t2_ratio > 0 ? (int)std::min<int64_t>(nmax, floor_ratio(o.t2_ratio, nmax) + 1) : 0;
   t->capS = t->cap1 + t->cap2;
   t->max_chunks = (int)((nmax + t->chunk - 1) / t->chunk);
@@ -266,7 +266,8 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
   // first placement: every score is 0, so candidates rank by position
   std::vector<uint8_t> first = first_placement(*t, n0);
   const int nt0 = (int)std::count(first.begin(), first.end(), (uint8_t)TKV_T0);
-  const int nt1 = n0 - nt0;
+  const int nt1 = (int)std::count(first.begin(), first.end(), (uint8_t)TKV_T1);
+  const int nt3 = n0 - nt0 - nt1;  // evicted at once (eviction-only baseline)
   if (nt0 > t->cap0 || nt1 > t->cap1)
     return tkv_fail(t, TKV_ECAPACITY, "first placement does not fit (T0 %d/%d, T1 %d/%d)", nt0, t->cap0, nt1, t->cap1);
 
@@ -279,16 +280,19 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
       if (first[p] == TKV_T0) {
         code = (uint32_t)t->free0[b].back();
         t->free0[b].pop_back();
-      } else {
+      } else if (first[p] == TKV_T1) {
         code = (uint32_t)(t->cap0 + own.size());
         own.push_back(p);
+      } else {
+        code = kNoLoc;
       }
       codes[(size_t)b * n0 + p] = code;
       t->h_tier[(size_t)b * t->nmax + p] = first[p];
       t->h_loc[(size_t)b * t->nmax + p] = code;
     }
-    t->nlive[b] = n0;
+    t->nlive[b] = n0 - nt3;
   }
+  t->st.evictions += (int64_t)nt3 * t->B;
 
   void* d_codes = nullptr;
   HIP_TRY(t, hipMallocAsync(&d_codes, codes.size() * 4, st));
@@ -334,16 +338,27 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
   }
   if (tmp_k) HIP_TRY(t, hipFreeAsync(tmp_k, st));
   if (tmp_v) HIP_TRY(t, hipFreeAsync(tmp_v, st));
-  // per-position tables and the live list (every prefilled position is live)
-  std::vector<int32_t> pos((size_t)t->B * n0);
-  for (int b = 0; b < t->B; ++b)
-    for (int p = 0; p < n0; ++p) pos[(size_t)b * n0 + p] = p;
+  // per-position tables and the live list (the non-evicted positions, ascending)
+  const int nl = n0 - nt3;
+  std::vector<int32_t> pos((size_t)t->B * nl);
+  std::vector<uint32_t> lloc((size_t)t->B * nl);
+  for (int b = 0; b < t->B; ++b) {
+    int j = 0;
+    for (int p = 0; p < n0; ++p)
+      if (first[p] != TKV_T3) {
+        pos[(size_t)b * nl + j] = p;
+        lloc[(size_t)b * nl + j] = codes[(size_t)b * n0 + p];
+        ++j;
+      }
+  }
   for (int b = 0; b < t->B; ++b) {
     const size_t off = (size_t)b * t->nmax;
     HIP_TRY(t, hipMemcpyAsync(t->tier + off, &t->h_tier[off], n0, hipMemcpyHostToDevice, st));
     HIP_TRY(t, hipMemcpyAsync(t->loc + off, &t->h_loc[off], (size_t)n0 * 4, hipMemcpyHostToDevice, st));
-    HIP_TRY(t, hipMemcpyAsync(t->live_loc + off, &t->h_loc[off], (size_t)n0 * 4, hipMemcpyHostToDevice, st));
-    HIP_TRY(t, hipMemcpyAsync(t->live_pos + off, &pos[(size_t)b * n0], (size_t)n0 * 4, hipMemcpyHostToDevice, st));
+    if (nl > 0) {
+      HIP_TRY(t, hipMemcpyAsync(t->live_loc + off, &lloc[(size_t)b * nl], (size_t)nl * 4, hipMemcpyHostToDevice, st));
+      HIP_TRY(t, hipMemcpyAsync(t->live_pos + off, &pos[(size_t)b * nl], (size_t)nl * 4, hipMemcpyHostToDevice, st));
+    }
   }
   HIP_TRY(t, hipFreeAsync(d_codes, st));
   HIP_TRY(t, hipStreamSynchronize(st));

@@ -48,5 +48,28 @@ inline std::vector<uint8_t> first_placement(const tkv& t, int n) {
       tier[i] = TKV_T0;
       --room;
     }
+  if (t.flags & TKV_FLAG_NO_T1)
+    for (auto& x : tier)
+      if (x == TKV_T1) x = TKV_T3;
   return tier;
+}
+
+// Candidates newly evicted (n3), kept in T0 (n0c) and put in T2 (n2) at one
+// reassignment (Method §1 budgets as floor(ratio * n)).
+struct CutCounts {
+  int64_t n3, n0c, n2;
+};
+inline CutCounts cut_counts(const tkv& t, int64_t n, int64_t np, int64_t nev) {
+  const int64_t ncand = n - np - nev;
+  CutCounts c{};
+  if (t.flags & TKV_FLAG_NO_T1) {
+    c.n0c = std::min<int64_t>(ncand, std::max<int64_t>(0, floor_ratio(t.hbm, n) - np));
+    c.n2 = std::min<int64_t>(ncand - c.n0c, floor_ratio(t.t2, n));
+    c.n3 = ncand - c.n0c - c.n2;
+    return c;
+  }
+  c.n3 = std::min<int64_t>(ncand, std::max<int64_t>(0, floor_ratio(t.evict, n) - nev));
+  c.n0c = std::min<int64_t>(ncand - c.n3, std::max<int64_t>(0, floor_ratio(t.hbm, n) - np));
+  c.n2 = std::min<int64_t>(ncand - c.n3 - c.n0c, floor_ratio(t.t2, n));
+  return c;
 }

@@ -132,9 +132,8 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
         ++np;
     }
     const int64_t ncand = n - np - nev;
-    const int64_t n3 = std::min<int64_t>(ncand, std::max<int64_t>(0, floor_ratio(t->evict, n) - nev));
-    const int64_t n0c = std::min<int64_t>(ncand - n3, std::max<int64_t>(0, floor_ratio(t->hbm, n) - np));
-    const int64_t n2 = std::min<int64_t>(ncand - n3 - n0c, floor_ratio(t->t2, n));
+    const CutCounts cc = cut_counts(*t, n, np, nev);
+    const int64_t n3 = cc.n3, n0c = cc.n0c, n2 = cc.n2;
     ra.ncand[b] = (int32_t)ncand;
     ra.rank[b][0] = (int32_t)n3;
     ra.rank[b][1] = (int32_t)(n3 + n2);

@@ -85,6 +85,17 @@ typedef struct {
 
 /* Record HIP events around the attention kernels; tkv_stats reports their time. */
 #define TKV_FLAG_TIME_KERNELS 1ull
+/* Eviction-only baseline on the same engine (the heavy-hitter eviction policies
+ * the gist.science summary compares against, Results): no T1.  Each
+ * reassignment keeps the protected rows plus the floor(hbm_ratio*N) - |P|
+ * best-ranked candidates in T0, puts the next floor(t2_ratio*N) in T2 and
+ * evicts every other candidate; evict_ratio plays no part.  The first
+ * placement evicts the rows the tiered policy would put in T1.  With
+ * hbm_ratio 0 and prompt 0 this is the sinks-plus-recent-window policy: only
+ * the attention sinks and the recent window are ever live.  (Without the flag,
+ * hbm_ratio 0, evict_ratio 1 and prompt 0 reach the same set at every
+ * reassignment, keeping the other rows in T1 until the first one.) */
+#define TKV_FLAG_NO_T1 2ull
 
 /* One changed row of a reassignment (Method §4). */
 typedef struct {

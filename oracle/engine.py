@@ -94,10 +94,11 @@ class OracleTKV:
     """Plain model of the tiered cache of a batch of sequences."""
 
     def __init__(self, layers, q_heads, kv_heads, head_dim, batch, max_tokens, delta,
-                 hbm_ratio, evict_ratio, t2_ratio, prompt, sinks, recent, bf16):
+                 hbm_ratio, evict_ratio, t2_ratio, prompt, sinks, recent, bf16, no_t1=False):
         self.L, self.Hq, self.Hkv, self.d, self.B = layers, q_heads, kv_heads, head_dim, batch
         self.nmax, self.delta = max_tokens, delta
         self.hbm, self.evict, self.t2 = hbm_ratio, evict_ratio, t2_ratio
+        self.no_t1 = no_t1
         self.prompt, self.sinks, self.recent = prompt, sinks, recent
         self.bf16 = bf16
         self.K = np.zeros((layers, batch, max_tokens, kv_heads, head_dim), np.float32)
@@ -111,7 +112,7 @@ class OracleTKV:
     def for_workload(cls, w, max_tokens=None):
         return cls(w.layers, w.q_heads, w.kv_heads, w.head_dim, w.batch,
                    max_tokens or w.n_final, w.delta, w.hbm_ratio, w.evict_ratio, w.t2_ratio,
-                   w.prompt, w.sinks, w.recent, w.dtype == "bf16")
+                   w.prompt, w.sinks, w.recent, w.dtype == "bf16", w.no_t1)
 
     # -- cache contents ------------------------------------------------------
     def prefill(self, K, V):
@@ -121,7 +122,7 @@ class OracleTKV:
         self.K[:, :, :n0] = K
         self.V[:, :, :n0] = V
         self.n = n0
-        first = tiering.initial_placement(n0, self.prompt, self.sinks, self.recent, self.hbm)
+        first = tiering.initial_placement(n0, self.prompt, self.sinks, self.recent, self.hbm, self.no_t1)
         self.tier[:, :n0] = first[None, :]
 
     def append(self, k, v):
@@ -165,7 +166,7 @@ class OracleTKV:
         for b in range(self.B):
             old = self.tier[b, :n].copy()
             new = tiering.reassign(old, scores[b], n, self.prompt, self.sinks, self.recent,
-                                   self.hbm, self.evict, self.t2)
+                                   self.hbm, self.evict, self.t2, self.no_t1)
             if adopt is not None:
                 new = np.asarray(adopt[b][:n], np.uint8)
             deltas.append(tiering.delta_lists(old, new))

@@ -15,7 +15,12 @@ notes):
     precedence T3, then T0, then T2, then T1;
   * rank order is score descending, then position ascending (unique keys);
   * the first placement (before any score exists) protects P, fills T0 with
-    the lowest-index candidates, evicts nothing and uses no T2.
+    the lowest-index candidates, evicts nothing and uses no T2;
+  * the eviction-only baseline (no T1, heavy hitters kept in T0, in the
+    manner of the H2O-style policies the summary compares against) takes the
+    same ranking and evicts every candidate that would have gone to T1: T0
+    first, then T2, and the rest to T3 (the eviction ratio then plays no
+    part).  Its first placement evicts what the tiered one puts in T1.
 """
 from __future__ import annotations
 
@@ -33,13 +38,20 @@ def protected_mask(n: int, prompt: int, sinks: int, recent: int) -> np.ndarray:
 
 
 def tier_counts(n: int, n_protected: int, n_candidates: int, n_evicted: int,
-                hbm_ratio: float, evict_ratio: float, t2_ratio: float):
+                hbm_ratio: float, evict_ratio: float, t2_ratio: float, no_t1: bool = False):
     """How many candidates go to T3, T0 and T2 at one reassignment.
 
     n3  = min(|C|, max(0, floor(e N) - |T3|))        newly evicted
     n0c = min(|C| - n3, max(0, floor(h N) - |P|))    candidates kept in T0
     n2  = min(|C| - n3 - n0c, floor(t2 N))           candidates put in T2
+
+    Without T1 (eviction-only baseline): n0c = min(|C|, max(0, floor(h N) -
+    |P|)), n2 = min(|C| - n0c, floor(t2 N)) and n3 = |C| - n0c - n2.
     """
+    if no_t1:
+        n0c = min(n_candidates, max(0, math.floor(hbm_ratio * n) - n_protected))
+        n2 = min(n_candidates - n0c, math.floor(t2_ratio * n))
+        return n_candidates - n0c - n2, n0c, n2
     n3 = min(n_candidates, max(0, math.floor(evict_ratio * n) - n_evicted))
     n0c = min(n_candidates - n3, max(0, math.floor(hbm_ratio * n) - n_protected))
     n2 = min(n_candidates - n3 - n0c, math.floor(t2_ratio * n))
@@ -52,7 +64,8 @@ def rank_best_first(candidates, scores) -> list:
 
 
 def reassign(old_tiers: np.ndarray, scores: np.ndarray, n: int, prompt: int, sinks: int,
-             recent: int, hbm_ratio: float, evict_ratio: float, t2_ratio: float) -> np.ndarray:
+             recent: int, hbm_ratio: float, evict_ratio: float, t2_ratio: float,
+             no_t1: bool = False) -> np.ndarray:
     """New tier of each of the n positions from the scores (Method §1, §4)."""
     old = np.asarray(old_tiers)[:n]
     new = np.empty(n, np.uint8)
@@ -60,7 +73,7 @@ def reassign(old_tiers: np.ndarray, scores: np.ndarray, n: int, prompt: int, sin
     evicted = old == T3
     cand = np.nonzero(~prot & ~evicted)[0]
     n3, n0c, n2 = tier_counts(n, int(prot.sum()), len(cand), int(evicted.sum()),
-                              hbm_ratio, evict_ratio, t2_ratio)
+                              hbm_ratio, evict_ratio, t2_ratio, no_t1)
     ranked = rank_best_first(cand, scores)          # best first
     c = len(ranked)
     new[evicted] = T3
@@ -77,12 +90,17 @@ def reassign(old_tiers: np.ndarray, scores: np.ndarray, n: int, prompt: int, sin
     return new
 
 
-def initial_placement(n: int, prompt: int, sinks: int, recent: int, hbm_ratio: float) -> np.ndarray:
+def initial_placement(n: int, prompt: int, sinks: int, recent: int, hbm_ratio: float,
+                      no_t1: bool = False) -> np.ndarray:
     """Tiers of a freshly filled cache: every score is 0, so the rank order is
-    position order; no eviction and no T2 before the first real ranking."""
+    position order; no eviction and no T2 before the first real ranking.
+    Without T1, the rows that would go to T1 are evicted instead."""
     none_yet = np.full(n, T1, np.uint8)
     zero = np.zeros(n)
-    return reassign(none_yet, zero, n, prompt, sinks, recent, hbm_ratio, 0.0, 0.0)
+    first = reassign(none_yet, zero, n, prompt, sinks, recent, hbm_ratio, 0.0, 0.0)
+    if no_t1:
+        first[first == T1] = T3
+    return first
 
 
 def delta_lists(old_tiers: np.ndarray, new_tiers: np.ndarray):

@@ -106,6 +106,7 @@ class Workload:
     sinks: int
     recent: int
     seed: int = 0
+    no_t1: bool = False   # eviction-only baseline: rows that would go to T1 are evicted
     heavy_frac: float = 0.05
     k_amp: float = 3.0
     q_amp: float = 2.0
