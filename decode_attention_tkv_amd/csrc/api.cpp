@@ -153,7 +153,7 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   t->cap0 = (int)std::min<int64_t>(nmax, std::max(pmax, h_at_max) + delta + 1);
   t->cap1 = (o.flags & TKV_FLAG_NO_T1) ? 1 : (int)std::max<int64_t>(1, std::min<int64_t>(nmax, nmax - h_at_max + 1));
   t->cap2 = o.t2_ratio > 0 ? (int)std::min<int64_t>(nmax, floor_ratio(o.t2_ratio, nmax) + 1) : 0;
-  t->capS = t->cap1 + t->cap2;
+  t->capS = resident ? t->cap1 + t->cap2 : t->cap1;
   t->max_chunks = (int)((nmax + t->chunk - 1) / t->chunk);
   t->lstride = (int)((nmax + kLogitAlign - 1) / kLogitAlign * kLogitAlign);
 
@@ -238,7 +238,8 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   t->t1_owner.resize(B);
   t->t2_owner.resize(B);
   std::memset(t->h_counts, 0, B * 2 * 4);
-  t->st.hbm_bytes = (int64_t)(2 * L * B * t->cap0 + 2 * (size_t)t->S * B * t->capS) * t->row_bytes;
+  t->st.hbm_bytes = (int64_t)(2 * L * B * t->cap0 + 2 * (size_t)t->S * B * t->capS) * t->row_bytes +
+                    (resident ? 0 : (int64_t)(2 * (size_t)t->S * B * t->cap2) * (t->Hkv * t->D + 4));
   t->st.host_bytes = (int64_t)(2 * L * B * t->cap1) * t->row_bytes +
                      (int64_t)(2 * L * B * t->cap2) * (t->Hkv * t->D + 4);
   t->st.full_cache_bytes = (int64_t)(2 * L * B * nmax) * t->row_bytes;
@@ -522,12 +523,11 @@ static int issue_prefetch(tkv* t, int upto) {
       t->st.h2d_bytes += 2 * (int64_t)width * t->B * t->Hkv;
     }
     if (n2max > 0) {
-      // 8-bit rows: codes and scales over PCIe, dequantised into the slot on the GPU
+      // 8-bit rows: codes and scales over PCIe into the slot's T2 area, which the
+      // attention pass reads directly
       const size_t cw = n2max * t->D;
       const size_t c_layer = (size_t)t->B * t->Hkv * t->cap2 * t->D;
       const size_t s_layer = (size_t)t->B * t->cap2;
-      DequantStageArgs dq{};
-      dq.rows = t->rowspace();
       for (int which = 0; which < 2; ++which) {
         int8_t* qd = (which ? t->qstage_v : t->qstage_k) + (size_t)slot * c_layer;
         float* sd = (which ? t->qsscale_v : t->qsscale_k) + (size_t)slot * s_layer;
@@ -535,19 +535,8 @@ static int issue_prefetch(tkv* t, int upto) {
                                     (size_t)t->cap2 * t->D, cw, (size_t)t->B * t->Hkv, hipMemcpyHostToDevice, t->side));
         HIP_TRY(t, hipMemcpy2DAsync(sd, (size_t)t->cap2 * 4, (which ? t->ascale_v : t->ascale_k) + (size_t)x * s_layer,
                                     (size_t)t->cap2 * 4, n2max * 4, (size_t)t->B, hipMemcpyHostToDevice, t->side));
-        (which ? dq.codes_v : dq.codes_k) = qd;
-        (which ? dq.scale_v : dq.scale_k) = sd;
       }
       t->st.h2d_bytes += 2 * (int64_t)(cw * t->B * t->Hkv + n2max * 4 * t->B);
-      dq.layer = x;
-      dq.cap1 = t->cap1;
-      dq.cap2 = t->cap2;
-      dq.batch = t->B;
-      dq.kv_heads = t->Hkv;
-      dq.head_dim = t->D;
-      dq.elem_bytes = t->esz;
-      for (int b = 0; b < t->B; ++b) dq.n2[b] = (int32_t)t->t2_owner[b].size();
-      HIP_TRY(t, launch_dequant_stage(dq, (int)n2max, t->side));
     }
     HIP_TRY(t, hipEventRecord(t->ev_h2d[slot], t->side));
   }

@@ -106,6 +106,44 @@ __device__ __forceinline__ void unpack<float>(const uint4& u, float* f) {
   f[3] = __uint_as_float(u.w);
 }
 
+// One 16-byte piece (EPL elements of the cache type) of a T2 row, from its
+// 8-bit codes: value = fp32(code * scale), rounded to the cache type (bf16
+// round-to-nearest-even) -- the same values the codec defines for the tier.
+template <typename T>
+__device__ __forceinline__ uint4 deq_piece(const int8_t* codes, float scale);
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even (finite values)
+  return u >> 16;
+}
+
+// signed byte `byte` of w as a float
+__device__ __forceinline__ float code_at(uint32_t w, int byte) {
+  return (float)((int32_t)(w << (24 - 8 * byte)) >> 24);
+}
+
+template <>
+__device__ __forceinline__ uint4 deq_piece<bf16_t>(const int8_t* codes, float scale) {
+  const uint2 c = *reinterpret_cast<const uint2*>(codes);
+  const uint32_t w[2] = {c.x, c.y};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i >> 1];
+    const int k = 2 * (i & 1);
+    o[i] = bf16_bits(code_at(x, k) * scale) | (bf16_bits(code_at(x, k + 1) * scale) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <>
+__device__ __forceinline__ uint4 deq_piece<float>(const int8_t* codes, float scale) {
+  const uint32_t x = *reinterpret_cast<const uint32_t*>(codes);
+  return make_uint4(__float_as_uint(code_at(x, 0) * scale), __float_as_uint(code_at(x, 1) * scale),
+                    __float_as_uint(code_at(x, 2) * scale), __float_as_uint(code_at(x, 3) * scale));
+}
+
 // Eq. 1 update for live rows [256 tile, 256 tile + 256) of sequence b:
 // s[pos(j)] += (sum over layers, in order) * 1/(L*H).
 __device__ __forceinline__ void score_rows(const ScoreArgs& a, int tile, int b) {
@@ -159,7 +197,7 @@ __global__ __launch_bounds__(256) void k_append(const AppendArgs a, const ScoreA
 
 // ---------------------------------------------------------------------------
 // Split-K attention, pass 1.  grid (chunks, kv_heads, layer_count*batch).
-template <typename T, int D, int G, int CHUNK, bool MK>
+template <typename T, int D, int G, int CHUNK, bool MK, bool QT>
 __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   constexpr int LPR = D * (int)sizeof(T) / 16;  // lanes per row
   constexpr int EPL = 16 / (int)sizeof(T);      // elements per lane
@@ -199,6 +237,18 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   const T* stageK = (const T*)a.rows.stage_k + soff;
   const T* stageV = (const T*)a.rows.stage_v + soff;
   const uint32_t cap0 = (uint32_t)a.rows.cap0;
+  // T2 rows (codes >= qbase): row 0 of this (slot, sequence, kv head) in the 8-bit area
+  const uint32_t qbase = cap0 + (uint32_t)a.rows.cap1;
+  const int8_t* qK = nullptr;
+  const int8_t* qV = nullptr;
+  const float* qsK = nullptr;
+  const float* qsV = nullptr;
+  if constexpr (QT) {
+    qK = a.rows.q_k + q_codes_at(a.rows, l, b, kvh, 0, D);
+    qV = a.rows.q_v + q_codes_at(a.rows, l, b, kvh, 0, D);
+    qsK = a.rows.qs_k + q_scale_at(a.rows, l, b, 0);
+    qsV = a.rows.qs_v + q_scale_at(a.rows, l, b, 0);
+  }
   const uint32_t* locs = a.live_loc + (int64_t)b * a.nmax + j0;
   for (int r = tid; r < CHUNK; r += 256) codes_s[r] = r < nrows ? locs[r] : 0u;
   __syncthreads();
@@ -233,11 +283,19 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
         const int r = wave * RPW + (t0 + tt) * 16 + hl;
         const bool ok = t0 + tt < TILES && r < nrows;
         const uint32_t code = ok ? codes_s[r] : 0u;
-        const T* p = code < cap0 ? pK + (int64_t)code * rs : sK + (int64_t)(code - cap0) * rs;
-        // 64-byte pieces per row per load: a streaming (non-temporal) hint would let
-        // the row's lines leave the cache before the neighbouring piece is read.
+        if (QT && ok && code >= qbase) {
+          const uint32_t qi = code - qbase;
+          const float sc = qsK[qi];
+          const int8_t* qp = qK + (int64_t)qi * D + 8 * kq;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) kd[tt][kc] = ok ? load16(p + 32 * kc) : make_uint4(0, 0, 0, 0);
+          for (int kc = 0; kc < KC; ++kc) kd[tt][kc] = deq_piece<T>(qp + 32 * kc, sc);
+        } else {
+          const T* p = code < cap0 ? pK + (int64_t)code * rs : sK + (int64_t)(code - cap0) * rs;
+          // 64-byte pieces per row per load: a streaming (non-temporal) hint would let
+          // the row's lines leave the cache before the neighbouring piece is read.
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) kd[tt][kc] = ok ? load16(p + 32 * kc) : make_uint4(0, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -287,8 +345,13 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
         kd[u] = make_uint4(0, 0, 0, 0);
         if (r < nrows) {
           const uint32_t code = codes_s[r];
-          const T* p = code < cap0 ? poolK + (int64_t)code * rs : stageK + (int64_t)(code - cap0) * rs;
-          kd[u] = load16nt(p);
+          if (QT && code >= qbase) {
+            const uint32_t qi = code - qbase;
+            kd[u] = deq_piece<T>(qK + (int64_t)qi * D + part * EPL, qsK[qi]);
+          } else {
+            const T* p = code < cap0 ? poolK + (int64_t)code * rs : stageK + (int64_t)(code - cap0) * rs;
+            kd[u] = load16nt(p);
+          }
         }
       }
   #pragma unroll
@@ -372,8 +435,13 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
       for (int i = 0; i < 8; ++i) {
         const int r = rb + i;
         const uint32_t code = r < nrows ? codes_s[r] : 0u;
-        const T* p = code < cap0 ? pV + (int64_t)code * rs : sV + (int64_t)(code - cap0) * rs;
-        vr[i] = r < nrows ? load16nt(p) : make_uint4(0, 0, 0, 0);
+        if (QT && r < nrows && code >= qbase) {
+          const uint32_t qi = code - qbase;
+          vr[i] = deq_piece<T>(qV + (int64_t)qi * D + 8 * hl, qsV[qi]);
+        } else {
+          const T* p = code < cap0 ? pV + (int64_t)code * rs : sV + (int64_t)(code - cap0) * rs;
+          vr[i] = r < nrows ? load16nt(p) : make_uint4(0, 0, 0, 0);
+        }
       }
       const half8 pa = *reinterpret_cast<const half8*>(&p16[hl][rb]);
       uint32_t vh[8][4];
@@ -420,8 +488,13 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
         vd[u] = make_uint4(0, 0, 0, 0);
         if (r < nrows) {
           const uint32_t code = codes_s[r];
-          const T* p = code < cap0 ? poolV + (int64_t)code * rs : stageV + (int64_t)(code - cap0) * rs;
-          vd[u] = load16nt(p);
+          if (QT && code >= qbase) {
+            const uint32_t qi = code - qbase;
+            vd[u] = deq_piece<T>(qV + (int64_t)qi * D + part * EPL, qsV[qi]);
+          } else {
+            const T* p = code < cap0 ? poolV + (int64_t)code * rs : stageV + (int64_t)(code - cap0) * rs;
+            vd[u] = load16nt(p);
+          }
         }
       }
   #pragma unroll
@@ -543,28 +616,35 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
 __global__ __launch_bounds__(256) void k_score(const ScoreArgs a) { score_rows(a, blockIdx.x, blockIdx.y); }
 
 // Grouped-query heads (G >= 4) of bf16 caches take the matrix-core logits.
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool QT>
 hipError_t launch_attn_t(const AttnArgs& a, int chunk, dim3 grid, hipStream_t s) {
   constexpr bool MK = std::is_same<T, bf16_t>::value && G >= 4;
   switch (chunk) {
-    case 128: k_attn_chunk<T, D, G, 128, MK><<<grid, 256, 0, s>>>(a); break;
-    case 256: k_attn_chunk<T, D, G, 256, MK><<<grid, 256, 0, s>>>(a); break;
-    case 512: k_attn_chunk<T, D, G, 512, MK><<<grid, 256, 0, s>>>(a); break;
+    case 128: k_attn_chunk<T, D, G, 128, MK, QT><<<grid, 256, 0, s>>>(a); break;
+    case 256: k_attn_chunk<T, D, G, 256, MK, QT><<<grid, 256, 0, s>>>(a); break;
+    case 512: k_attn_chunk<T, D, G, 512, MK, QT><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool QT>
 hipError_t launch_attn_g(const AttnArgs& a, int group, int chunk, dim3 grid, hipStream_t s) {
   switch (group) {
-    case 1: return launch_attn_t<T, D, 1>(a, chunk, grid, s);
-    case 2: return launch_attn_t<T, D, 2>(a, chunk, grid, s);
-    case 4: return launch_attn_t<T, D, 4>(a, chunk, grid, s);
-    case 5: return launch_attn_t<T, D, 5>(a, chunk, grid, s);
-    case 8: return launch_attn_t<T, D, 8>(a, chunk, grid, s);
+    case 1: return launch_attn_t<T, D, 1, QT>(a, chunk, grid, s);
+    case 2: return launch_attn_t<T, D, 2, QT>(a, chunk, grid, s);
+    case 4: return launch_attn_t<T, D, 4, QT>(a, chunk, grid, s);
+    case 5: return launch_attn_t<T, D, 5, QT>(a, chunk, grid, s);
+    case 8: return launch_attn_t<T, D, 8, QT>(a, chunk, grid, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Stream staging with an 8-bit tier takes the variant that reads T2 rows as codes.
+template <typename T, int D>
+hipError_t launch_attn_q(const AttnArgs& a, int group, int chunk, dim3 grid, hipStream_t s) {
+  if (a.rows.q_k != nullptr) return launch_attn_g<T, D, true>(a, group, chunk, grid, s);
+  return launch_attn_g<T, D, false>(a, group, chunk, grid, s);
 }
 
 }  // namespace
@@ -580,11 +660,11 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, int head_dim, int group, in
                        int layer_count, int chunks_now, hipStream_t s) {
   const dim3 grid(chunks_now, a.kv_heads, layer_count * a.batch);
   if (dtype == TKV_BF16) {
-    if (head_dim == 128) return launch_attn_g<bf16_t, 128>(a, group, chunk, grid, s);
-    if (head_dim == 64) return launch_attn_g<bf16_t, 64>(a, group, chunk, grid, s);
+    if (head_dim == 128) return launch_attn_q<bf16_t, 128>(a, group, chunk, grid, s);
+    if (head_dim == 64) return launch_attn_q<bf16_t, 64>(a, group, chunk, grid, s);
   } else {
-    if (head_dim == 128) return launch_attn_g<float, 128>(a, group, chunk, grid, s);
-    if (head_dim == 64) return launch_attn_g<float, 64>(a, group, chunk, grid, s);
+    if (head_dim == 128) return launch_attn_q<float, 128>(a, group, chunk, grid, s);
+    if (head_dim == 64) return launch_attn_q<float, 64>(a, group, chunk, grid, s);
   }
   return hipErrorInvalidValue;
 }

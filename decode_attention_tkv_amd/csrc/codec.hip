@@ -80,21 +80,6 @@ __global__ __launch_bounds__(256) void k_dequant_rows(const DequantArgs a, const
   }
 }
 
-// grid (n2max, batch, 2), block 256: one layer's 8-bit rows -> its staging slot.
-__global__ __launch_bounds__(256) void k_dequant_stage(const DequantStageArgs a) {
-  const int k = blockIdx.x, b = blockIdx.y, which = blockIdx.z;
-  if (k >= a.n2[b]) return;
-  const int d = a.head_dim, n = a.kv_heads * d;
-  const int8_t* codes = which ? a.codes_v : a.codes_k;
-  const float scale = (which ? a.scale_v : a.scale_k)[(int64_t)b * a.cap2 + k];
-  void* st = which ? (void*)a.rows.stage_v : (void*)a.rows.stage_k;
-  for (int e = threadIdx.x; e < n; e += 256) {
-    const int h = e / d, j = e % d;
-    const float c = (float)codes[(((int64_t)b * a.kv_heads + h) * a.cap2 + k) * d + j];
-    store_val(st, stage_elem(a.rows, a.layer, b, h, (uint32_t)(a.cap1 + k), d) + j, c * scale, a.elem_bytes);
-  }
-}
-
 }  // namespace
 
 hipError_t launch_quant_rows(const QuantArgs& a, const QuantOp* ops, int n_ops, int layers, hipStream_t s) {
@@ -106,12 +91,6 @@ hipError_t launch_quant_rows(const QuantArgs& a, const QuantOp* ops, int n_ops, 
 hipError_t launch_dequant_rows(const DequantArgs& a, const DequantOp* ops, int n_ops, int layers, hipStream_t s) {
   if (n_ops <= 0) return hipSuccess;
   k_dequant_rows<<<dim3(n_ops, layers, 2), 256, 0, s>>>(a, ops);
-  return hipGetLastError();
-}
-
-hipError_t launch_dequant_stage(const DequantStageArgs& a, int n2max, hipStream_t s) {
-  if (n2max <= 0) return hipSuccess;
-  k_dequant_stage<<<dim3(n2max, a.batch, 2), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -20,14 +20,14 @@ struct tkv {
   double hbm = 0, evict = 0, t2 = 0;
   int prompt = 0, sinks = 0, recent = 0;
   uint64_t flags = 0;
-  int cap0 = 0, cap1 = 0, cap2 = 0, capS = 0, max_chunks = 0;
+  int cap0 = 0, cap1 = 0, cap2 = 0, capS = 0, max_chunks = 0;  // capS: staging rows per slot
   int lstride = 0;  // logits row stride: nmax rounded up to whole lines
   int64_t row_elems = 0, row_bytes = 0;
 
   // ---- device buffers (owned)
   void* pool_k = nullptr;  // [L][B][Hkv][cap0][D]
   void* pool_v = nullptr;
-  void* stage_k = nullptr;  // [S][B][Hkv][capS][D]
+  void* stage_k = nullptr;  // [S][B][Hkv][capS][D]: T1 rows, then (resident) T2 values
   void* stage_v = nullptr;
   uint32_t* live_loc = nullptr;  // [B][nmax]
   int32_t* live_pos = nullptr;   // [B][nmax]
@@ -77,7 +77,8 @@ struct tkv {
   float* ascale_k = nullptr;   // [L][B][cap2]: T2 scales
   float* ascale_v = nullptr;
   std::vector<void*> host_allocs;
-  // stream mode: one layer's 8-bit rows on the device before dequantisation
+  // stream staging: one layer's 8-bit rows per slot, as they crossed PCIe; the
+  // attention pass reads the codes directly
   int8_t* qstage_k = nullptr;  // [S][B][Hkv][cap2][D]
   int8_t* qstage_v = nullptr;
   float* qsscale_k = nullptr;  // [S][B][cap2]
@@ -135,7 +136,18 @@ struct tkv {
     r.stage_hstride = (int64_t)capS * D;
     r.stage_bstride = r.stage_hstride * Hkv;
     r.stage_lstride = r.stage_bstride * B;
+    r.q_k = qstage_k;
+    r.q_v = qstage_v;
+    r.qs_k = qsscale_k;
+    r.qs_v = qsscale_v;
+    r.q_hstride = (int64_t)cap2 * D;
+    r.q_bstride = r.q_hstride * Hkv;
+    r.q_lstride = r.q_bstride * B;
+    r.qs_bstride = cap2;
+    r.qs_lstride = (int64_t)cap2 * B;
     r.cap0 = cap0;
+    r.cap1 = cap1;
+    r.cap2 = cap2;
     r.stage_slots = S;
     return r;
   }

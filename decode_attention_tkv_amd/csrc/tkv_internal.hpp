@@ -24,17 +24,36 @@ constexpr uint8_t kUnused = 255;           // tier code of positions not appende
 // [..][batch][kv_heads][cap][head_dim], so the rows of one kv head are
 // contiguous (head_dim elements apart).  A live row's location code `loc` is
 // a T0 pool slot when loc < cap0, else index (loc - cap0) of the staging area
-// of slot (layer % stage_slots).
+// of slot (layer % stage_slots): T1 rows first, then (resident staging) the
+// T2 rows' dequantised values from index cap1.  Stream staging instead
+// carries a layer's T2 rows as the 8-bit codes and scales that crossed PCIe
+// (q_k != nullptr): codes >= cap0 + cap1 are rows of that area, and the
+// attention pass dequantises them as it reads them.
 struct RowSpace {
   const void* pool_k;
   const void* pool_v;
   const void* stage_k;
   const void* stage_v;
+  int8_t* q_k;  // stream staging: T2 codes [stage_slots][batch][kv_heads][cap2][head_dim]; else null
+  int8_t* q_v;
+  float* qs_k;  // T2 scales [stage_slots][batch][cap2]
+  float* qs_v;
   int64_t pool_lstride, pool_bstride, pool_hstride;     // elements per layer / sequence / kv head
   int64_t stage_lstride, stage_bstride, stage_hstride;  // elements per slot / sequence / kv head
-  int32_t cap0;
+  int64_t q_lstride, q_bstride, q_hstride;              // T2 codes per slot / sequence / kv head
+  int64_t qs_lstride, qs_bstride;                       // T2 scales per slot / sequence
+  int32_t cap0, cap1, cap2;
   int32_t stage_slots;
 };
+
+// T2 area offsets: codes of row idx (kv head h) of layer l's slot, and its scale.
+__host__ __device__ inline int64_t q_codes_at(const RowSpace& r, int l, int b, int h, uint32_t idx, int d) {
+  return (int64_t)(l % r.stage_slots) * r.q_lstride + (int64_t)b * r.q_bstride + (int64_t)h * r.q_hstride +
+         (int64_t)idx * d;
+}
+__host__ __device__ inline int64_t q_scale_at(const RowSpace& r, int l, int b, uint32_t idx) {
+  return (int64_t)(l % r.stage_slots) * r.qs_lstride + (int64_t)b * r.qs_bstride + idx;
+}
 
 // Logits and per-layer score rows are padded to kLogitAlign floats, so every
 // chunk's stores start on a line boundary.
@@ -168,7 +187,7 @@ struct QuantOp {
   uint16_t b;
   uint32_t src;    // F row
   uint32_t dst;    // QPack row
-  uint32_t stage;  // staging index that receives the dequantised values, or kNoLoc
+  uint32_t stage;  // resident staging index that receives the dequantised values, or kNoLoc
 };
 
 struct QuantArgs {
@@ -188,19 +207,6 @@ struct DequantArgs {
   QPack in;
   FPack f;
   int32_t kv_heads, head_dim, elem_bytes;
-};
-
-// Stream staging of the 8-bit rows of one layer: codes [B][Hkv][cap2][d] and
-// scales [B][cap2] (K and V each) already copied to the device; dequantise
-// into staging indices [cap1, cap1 + n2).
-struct DequantStageArgs {
-  RowSpace rows;
-  const int8_t* codes_k;
-  const int8_t* codes_v;
-  const float* scale_k;
-  const float* scale_v;
-  int32_t layer, cap1, cap2, batch, kv_heads, head_dim, elem_bytes;
-  int32_t n2[kMaxBatch];
 };
 
 // ---- launchers (attn.hip) -------------------------------------------------
@@ -226,6 +232,5 @@ hipError_t launch_copy_rows(const CopyArgs& a, const RowOp* ops, int n_ops, int 
 // ---- launchers (codec.hip) --------------------------------------------------
 hipError_t launch_quant_rows(const QuantArgs& a, const QuantOp* ops, int n_ops, int layers, hipStream_t s);
 hipError_t launch_dequant_rows(const DequantArgs& a, const DequantOp* ops, int n_ops, int layers, hipStream_t s);
-hipError_t launch_dequant_stage(const DequantStageArgs& a, int n2max, hipStream_t s);
 
 }  // namespace tkvd
