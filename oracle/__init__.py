@@ -4,7 +4,8 @@ A plain, slow fp64 CPU model of the tiered-KV decode step of "Not All
 Thoughts Need HBM: Semantics-Aware Memory Hierarchy for LLM Reasoning"
 (arXiv 2605.09490): attention over the non-evicted rows, the cumulative
 score of Eq. 1, score-ranked re-placement into T0..T3 every Delta steps, the
-changed-row lists, and the 8-bit codec of T2.
+changed-row lists, the 8-bit codec of T2, and the scores of a scored
+prefill (causal attention weights of the prompt added up as Eq. 1 does).
 
 It shares no code with the GPU library (decode_attention_tkv_amd) and never
 imports it.  Only tests/, the smoke check in __graft_entry__.py and the
@@ -17,6 +18,7 @@ independence from the T0/T1 split, exhaustive ranking properties on tiny
 cases, hand-derived tier counts (tests/golden/), and the codec's error bound.
 """
 from .engine import OracleTKV, attend, build, eq1_increment
+from .prefill import prefill_scores
 from .tiering import T0, T1, T2, T3
 
-__all__ = ["OracleTKV", "attend", "build", "eq1_increment", "T0", "T1", "T2", "T3"]
+__all__ = ["OracleTKV", "attend", "build", "eq1_increment", "prefill_scores", "T0", "T1", "T2", "T3"]

@@ -23,7 +23,7 @@ import subprocess
 
 import numpy as np
 
-from . import codec, tiering
+from . import codec, prefill as _prefill, tiering
 from .tiering import T0, T1, T2, T3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -124,6 +124,15 @@ class OracleTKV:
         self.n = n0
         first = tiering.initial_placement(n0, self.prompt, self.sinks, self.recent, self.hbm, self.no_t1)
         self.tier[:, :n0] = first[None, :]
+
+    def prefill_scored(self, K, V, Q):
+        """Scored prefill: the rows as prefill() places them, the prompt's
+        causal attention weights added to the scores (prefill.py), then one
+        re-placement by those scores with the full tier rules.  Returns what
+        reassign() returns."""
+        self.prefill(K, V)
+        self.s[:, : self.n] = _prefill.prefill_scores(K, Q, self.n)
+        return self.reassign()
 
     def append(self, k, v):
         """k, v: float32 values [L][B][Hkv][d] of the new token (position n)."""
