@@ -78,6 +78,7 @@ _SIGS = {
     "tkv_destroy": [_vp],
     "tkv_last_error": [_vp],
     "tkv_prefill": [_vp, _vp, _vp, _i32, _vp],
+    "tkv_prefill_scored": [_vp, _vp, _vp, _vp, _i32, _vp],
     "tkv_append": [_vp, _vp, _vp, _vp],
     "tkv_decode_attn": [_vp, _i32, _i32, _vp, _vp, _vp],
     "tkv_reassign": [_vp, _vp],
@@ -150,6 +151,10 @@ def tkv_destroy(h):
 
 def tkv_prefill(h, k_ptr, v_ptr, n_tokens, stream=None):
     _check(lib().tkv_prefill(h, k_ptr, v_ptr, n_tokens, _stream(stream)), h)
+
+
+def tkv_prefill_scored(h, k_ptr, v_ptr, q_ptr, n_tokens, stream=None):
+    _check(lib().tkv_prefill_scored(h, k_ptr, v_ptr, q_ptr, n_tokens, _stream(stream)), h)
 
 
 def tkv_append(h, k_ptr, v_ptr, stream=None):
@@ -252,6 +257,12 @@ class TieredKV:
         n = k.shape[2]
         shape = (self.L, self.B, n, self.Hkv, self.D)
         tkv_prefill(self.h, _dev_ptr(k, shape, self.tdtype, "k"), _dev_ptr(v, shape, self.tdtype, "v"), n, stream)
+
+    def prefill_scored(self, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, stream=None):
+        n = k.shape[2]
+        shape = (self.L, self.B, n, self.Hkv, self.D)
+        tkv_prefill_scored(self.h, _dev_ptr(k, shape, self.tdtype, "k"), _dev_ptr(v, shape, self.tdtype, "v"),
+                           _dev_ptr(q, (self.L, self.B, n, self.Hq, self.D), self.tdtype, "q"), n, stream)
 
     def append(self, k: torch.Tensor, v: torch.Tensor, stream=None):
         shape = (self.L, self.B, self.Hkv, self.D)

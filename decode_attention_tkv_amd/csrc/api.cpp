@@ -368,6 +368,36 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
   return TKV_OK;
 }
 
+extern "C" int tkv_prefill_scored(tkv_t* t, const void* k, const void* v, const void* q, int32_t n_tokens,
+                                  tkv_stream_t stream) {
+  if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  if (!q) return tkv_fail(t, TKV_EINVAL, "q is NULL");
+  if (int rc = tkv_prefill(t, k, v, n_tokens, stream)) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t per = (size_t)t->L * t->B * t->Hq * n_tokens * 4;
+  PrefillScoreArgs a{};
+  HIP_TRY(t, hipMallocAsync((void**)&a.row_max, per, st));
+  HIP_TRY(t, hipMallocAsync((void**)&a.row_inv, per, st));
+  HIP_TRY(t, hipMallocAsync((void**)&a.colsum, per, st));
+  a.k = k;
+  a.q = q;
+  a.s = t->s;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)t->D));
+  a.inv_lh = (float)(1.0 / ((double)t->L * t->Hq));
+  a.layers = t->L;
+  a.batch = t->B;
+  a.q_heads = t->Hq;
+  a.kv_heads = t->Hkv;
+  a.n = n_tokens;
+  a.nmax = t->nmax;
+  const hipError_t e = launch_prefill_scores(a, t->dtype, t->D, st);
+  HIP_TRY(t, hipFreeAsync(a.row_max, st));
+  HIP_TRY(t, hipFreeAsync(a.row_inv, st));
+  HIP_TRY(t, hipFreeAsync(a.colsum, st));
+  HIP_TRY(t, e);
+  return tkv_reassign(t, stream);
+}
+
 extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "previous step has layers left");

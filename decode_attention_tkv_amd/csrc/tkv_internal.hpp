@@ -209,6 +209,24 @@ struct DequantArgs {
   int32_t kv_heads, head_dim, elem_bytes;
 };
 
+// Scored prefill: inputs k [layers][batch][n][kv_heads][d], q [layers][batch][n][q_heads][d]
+// (cache type); scratch row_max, row_inv, colsum [layers][batch][q_heads][n] fp32; the
+// scores s[b][j] (row stride nmax) are set for j < n.
+struct PrefillScoreArgs {
+  const void* k;
+  const void* q;
+  float* row_max;
+  float* row_inv;
+  float* colsum;
+  float* s;
+  float qscale;  // log2(e) / sqrt(head_dim)
+  float inv_lh;  // 1 / (layers * q_heads)
+  int32_t layers, batch, q_heads, kv_heads, n, nmax;
+};
+
+// ---- launchers (prefill.hip) ------------------------------------------------
+hipError_t launch_prefill_scores(const PrefillScoreArgs& a, int dtype, int head_dim, hipStream_t s);
+
 // ---- launchers (attn.hip) -------------------------------------------------
 // fold != nullptr: the same launch also applies a pending Eq. 1 update
 // (fold_tiles tiles of 256 live rows per sequence); the two touch disjoint data.

@@ -141,6 +141,20 @@ const char* tkv_last_error(const tkv_t* t);
  * nothing is evicted and nothing goes to T2.  Synchronises `stream`. */
 int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tokens, tkv_stream_t stream);
 
+/* Scored prefill (the step before the decode path): fill an empty cache as
+ * tkv_prefill does, then give the prompt the scores its own causal attention
+ * earns -- every position t attends to positions 0..t with its query and adds
+ * its weights, averaged over layers and query heads, to the scores (Eq. 1 of
+ * Method §2, applied to the prompt as to decode steps) -- and re-place every
+ * row by those scores with the full tier rules, as tkv_reassign does
+ * (counted as one reassignment).  q: device [layers][batch][n_tokens]
+ * [q_heads][head_dim] (handle dtype); k, v as for tkv_prefill.  Scratch of
+ * 12 * layers * batch * q_heads * n_tokens bytes is taken from the stream's
+ * allocator and returned before the call ends.  Errors as tkv_prefill, plus
+ * those of tkv_reassign.  Synchronises `stream`. */
+int tkv_prefill_scored(tkv_t* t, const void* k, const void* v, const void* q, int32_t n_tokens,
+                       tkv_stream_t stream);
+
 /* Start a decode step: append one position to every sequence.  k, v: device
  * [layers][batch][kv_heads][head_dim].  The new row enters T0 with score 0.
  * The copy out of k, v is enqueued on `stream` by this call, so the caller may
