@@ -11,10 +11,12 @@
 //                       sequence): sum over queries t >= j of 2^(z - m_t) / l_t;
 //   k_prefill_sum       one thread per (position, sequence): the scores,
 //                       layers then heads in a fixed order, times 1/(L*H).
-// fp32 caches take these per-thread passes; bf16 caches take the matrix-core
-// passes below.  Both passes compute every z = q_t . k_j the same way (the
-// same fma chain, or the same MFMA tile), so every weight is at most 1 and
-// the weights of a query sum to 1 up to rounding.
+// fp32 caches take these per-thread passes.  bf16 caches take the
+// matrix-core passes below: the row maxima, then the row sums against them
+// (two cheap MFMA passes instead of one online pass with two exponentials
+// per weight), then the column sums.  Every pass computes each z = q_t . k_j
+// the same way (the same fma chain, or the same MFMA tile), so every weight
+// is at most 1 and the weights of a query sum to 1 up to rounding.
 #include <type_traits>
 
 #include "tkv_internal.hpp"
@@ -160,108 +162,212 @@ __device__ __forceinline__ f32x4 tile_z(const bf16x8* qa, const bf16x8* kb) {
   return acc;
 }
 
-// grid (ceil(n / 64), q_heads, layers * batch), block 256: wave w owns query
-// rows 16w.. of the block's 64 and walks the keys 0..(its last row).
+// Operand tiles of 32 rows (of one head, row stride `stride` elements) are
+// staged in LDS once per block and shared by its 4 waves: rows padded by 16
+// bytes so that the 16-byte reads of 16 rows at one offset hit distinct banks.
 template <int D>
-__global__ __launch_bounds__(256) void k_prefill_rowstats_mk(const PrefillScoreArgs a) {
-  constexpr int KC = D / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, sgrp = lane >> 4;
-  const int h = blockIdx.y, lb = blockIdx.z;
-  const int kvh = h / (a.q_heads / a.kv_heads);
-  const int t0 = blockIdx.x * 64 + 16 * wave;
-  if (t0 >= a.n) return;  // no barriers in this kernel
-  const uint16_t* Q = (const uint16_t*)a.q + ((int64_t)lb * a.n * a.q_heads + h) * D;
-  const uint16_t* K = (const uint16_t*)a.k + ((int64_t)lb * a.n * a.kv_heads + kvh) * D;
-  bf16x8 qa[KC];
+struct Tile {
+  static constexpr int RB = 2 * D + 16;  // padded row bytes
+  static constexpr int PR = D / 8;       // 16-byte pieces per row
+  static constexpr int RPP = 256 / PR;   // rows per block-wide pass
+  static constexpr int NP = 32 / RPP;    // passes per 32-row tile
+};
+
+template <int D>
+__device__ __forceinline__ void tile_fetch(const uint16_t* base, int64_t stride, int row0, int n, uint4* reg) {
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    const int t = t0 + r;
-    qa[kc] = t < a.n ? ld8(Q + (int64_t)t * a.q_heads * D + 32 * kc + 8 * sgrp) : bf16x8{};
-  }
-  float m[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
-  }
-  const int jend = min(a.n, t0 + 16);
-  for (int j0 = 0; j0 < jend; j0 += 16) {
-    const int j = j0 + r;
-    bf16x8 kb[KC];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      kb[kc] = j < a.n ? ld8(K + (int64_t)j * a.kv_heads * D + 32 * kc + 8 * sgrp) : bf16x8{};
-    const f32x4 acc = tile_z<D>(qa, kb);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * sgrp + i;
-      if (t < a.n && j <= t) {
-        const float z = acc[i] * a.qscale;
-        const float mn = fmaxf(m[i], z);
-        l[i] = l[i] * exp2f(m[i] - mn) + exp2f(z - mn);
-        m[i] = mn;
-      }
-    }
-  }
-  const int64_t so = ((int64_t)lb * a.q_heads + h) * a.n;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float M = row16_max(m[i]);
-    const float part = m[i] == -INFINITY ? 0.f : l[i] * exp2f(m[i] - M);
-    const float L = row16_sum(part);
-    const int t = t0 + 4 * sgrp + i;
-    if (r == 0 && t < a.n) {
-      a.row_max[so + t] = M;
-      a.row_inv[so + t] = 1.f / L;
-    }
+  for (int p = 0; p < Tile<D>::NP; ++p) {
+    const int row = p * Tile<D>::RPP + (int)threadIdx.x / Tile<D>::PR, piece = (int)threadIdx.x % Tile<D>::PR;
+    const int gr = row0 + row;
+    reg[p] = gr < n ? *reinterpret_cast<const uint4*>(base + (int64_t)gr * stride + 8 * piece) : make_uint4(0, 0, 0, 0);
   }
 }
 
-// grid (ceil(n / 64), q_heads, layers * batch), block 256: wave w owns keys
-// 16w.. of the block's 64 and walks the queries from its first key to n.
 template <int D>
-__global__ __launch_bounds__(256) void k_prefill_colsum_mk(const PrefillScoreArgs a) {
+__device__ __forceinline__ void tile_store(char* lds, const uint4* reg) {
+#pragma unroll
+  for (int p = 0; p < Tile<D>::NP; ++p) {
+    const int row = p * Tile<D>::RPP + (int)threadIdx.x / Tile<D>::PR, piece = (int)threadIdx.x % Tile<D>::PR;
+    *reinterpret_cast<uint4*>(lds + row * Tile<D>::RB + 16 * piece) = reg[p];
+  }
+}
+
+// MFMA operand (8 elements 32kc + 8s..) of row `row` of an LDS tile
+template <int D>
+__device__ __forceinline__ bf16x8 tile_op(const char* lds, int row, int kc, int sgrp) {
+  const uint4 u = *reinterpret_cast<const uint4*>(lds + row * Tile<D>::RB + 2 * (32 * kc + 8 * sgrp));
+  const u32x4 v = {u.x, u.y, u.z, u.w};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// grid (ceil(n / 128), q_heads, layers * batch), block 256: the block owns
+// query rows [128x, 128x + 128), wave w the 32 rows 32w.. (two 16-row tiles,
+// operands in registers); key tiles of 32 rows come through LDS.
+// PH 0: the rows' maxima (no exponentials); PH 1: their sums of 2^(z - max).
+template <int D, int PH>
+__global__ __launch_bounds__(256) void k_prefill_rowstats_mk(const PrefillScoreArgs a) {
   constexpr int KC = D / 32;
+  __shared__ __attribute__((aligned(16))) char kt_s[2][32 * Tile<D>::RB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, sgrp = lane >> 4;
   const int h = blockIdx.y, lb = blockIdx.z;
   const int kvh = h / (a.q_heads / a.kv_heads);
-  const int j0 = blockIdx.x * 64 + 16 * wave;
-  if (j0 >= a.n) return;  // no barriers in this kernel
+  const int T0 = blockIdx.x * 128, tw = T0 + 32 * wave;
   const uint16_t* Q = (const uint16_t*)a.q + ((int64_t)lb * a.n * a.q_heads + h) * D;
   const uint16_t* K = (const uint16_t*)a.k + ((int64_t)lb * a.n * a.kv_heads + kvh) * D;
-  const int j = j0 + r;
-  bf16x8 kb[KC];
+  bf16x8 qa[2][KC];
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
-    kb[kc] = j < a.n ? ld8(K + (int64_t)j * a.kv_heads * D + 32 * kc + 8 * sgrp) : bf16x8{};
-  const int64_t so = ((int64_t)lb * a.q_heads + h) * a.n;
-  float c = 0.f;
-  for (int t0 = j0; t0 < a.n; t0 += 16) {
-    bf16x8 qa[KC];
+  for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      const int t = t0 + r;
-      qa[kc] = t < a.n ? ld8(Q + (int64_t)t * a.q_heads * D + 32 * kc + 8 * sgrp) : bf16x8{};
+      const int t = tw + 16 * qt + r;
+      qa[qt][kc] = t < a.n ? ld8(Q + (int64_t)t * a.q_heads * D + 32 * kc + 8 * sgrp) : bf16x8{};
     }
-    float mt[4], it[4];
+  const int64_t so = ((int64_t)lb * a.q_heads + h) * a.n;
+  float m[2][4], l[2][4];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * sgrp + i;
-      mt[i] = t < a.n ? a.row_max[so + t] : 0.f;
-      it[i] = t < a.n ? a.row_inv[so + t] : 0.f;
+      const int t = tw + 16 * qt + 4 * sgrp + i;
+      m[qt][i] = (PH == 1 && t < a.n) ? a.row_max[so + t] : -INFINITY;
+      l[qt][i] = 0.f;
     }
-    const f32x4 acc = tile_z<D>(qa, kb);
+  const int jend = min(a.n, T0 + 128);  // keys the block's rows can see
+  const int iters = (jend + 31) / 32;
+  uint4 reg[Tile<D>::NP];
+  tile_fetch<D>(K, (int64_t)a.kv_heads * D, 0, a.n, reg);
+  tile_store<D>(kt_s[0], reg);
+  __syncthreads();
+  for (int it = 0; it < iters; ++it) {
+    const bool more = it + 1 < iters;
+    if (more) tile_fetch<D>(K, (int64_t)a.kv_heads * D, 32 * (it + 1), a.n, reg);
+    const char* ks = kt_s[it & 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * sgrp + i;
-      if (t < a.n && t >= j) c += exp2f(acc[i] * a.qscale - mt[i]) * it[i];
+    for (int kt = 0; kt < 2; ++kt) {
+      bf16x8 kb[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) kb[kc] = tile_op<D>(ks, 16 * kt + r, kc, sgrp);
+      const int j = 32 * it + 16 * kt + r;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const f32x4 acc = tile_z<D>(qa[qt], kb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tw + 16 * qt + 4 * sgrp + i;
+          if (t < a.n && j <= t) {
+            const float z = acc[i] * a.qscale;
+            if constexpr (PH == 0)
+              m[qt][i] = fmaxf(m[qt][i], z);
+            else
+              l[qt][i] += exp2f(z - m[qt][i]);
+          }
+        }
+      }
     }
+    if (more) tile_store<D>(kt_s[(it + 1) & 1], reg);
+    __syncthreads();
   }
-  c += __shfl_xor(c, 16);
-  c += __shfl_xor(c, 32);
-  if (sgrp == 0 && j < a.n) a.colsum[so + j] = c;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = tw + 16 * qt + 4 * sgrp + i;
+      if constexpr (PH == 0) {
+        const float M = row16_max(m[qt][i]);
+        if (r == 0 && t < a.n) a.row_max[so + t] = M;
+      } else {
+        const float L = row16_sum(l[qt][i]);
+        if (r == 0 && t < a.n) a.row_inv[so + t] = 1.f / L;
+      }
+    }
+}
+
+// grid (ceil(n / 128), q_heads, layers * batch), block 256: the block owns
+// keys [128x, 128x + 128), wave w the 32 keys 32w.. (operands in registers);
+// query tiles of 32 rows and their row statistics come through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void k_prefill_colsum_mk(const PrefillScoreArgs a) {
+  constexpr int KC = D / 32;
+  __shared__ __attribute__((aligned(16))) char qt_s[2][32 * Tile<D>::RB];
+  __shared__ float ms[2][32], is[2][32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, sgrp = lane >> 4;
+  const int h = blockIdx.y, lb = blockIdx.z;
+  const int kvh = h / (a.q_heads / a.kv_heads);
+  const int J0 = blockIdx.x * 128, jw = J0 + 32 * wave;
+  const uint16_t* Q = (const uint16_t*)a.q + ((int64_t)lb * a.n * a.q_heads + h) * D;
+  const uint16_t* K = (const uint16_t*)a.k + ((int64_t)lb * a.n * a.kv_heads + kvh) * D;
+  const int64_t so = ((int64_t)lb * a.q_heads + h) * a.n;
+  bf16x8 kb[2][KC];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int j = jw + 16 * kt + r;
+      kb[kt][kc] = j < a.n ? ld8(K + (int64_t)j * a.kv_heads * D + 32 * kc + 8 * sgrp) : bf16x8{};
+    }
+  float c[2] = {0.f, 0.f};
+  const int iters = (a.n - J0 + 31) / 32;  // query tiles from the block's first key on
+  uint4 reg[Tile<D>::NP];
+  float sreg = 0.f;
+  auto stat_fetch = [&](int t0) {
+    const int t = t0 + (int)(threadIdx.x & 31);
+    if (threadIdx.x < 64) sreg = t < a.n ? (threadIdx.x < 32 ? a.row_max[so + t] : a.row_inv[so + t]) : 0.f;
+  };
+  auto stat_store = [&](int buf) {
+    if (threadIdx.x < 32) ms[buf][threadIdx.x] = sreg;
+    else if (threadIdx.x < 64) is[buf][threadIdx.x - 32] = sreg;
+  };
+  tile_fetch<D>(Q, (int64_t)a.q_heads * D, J0, a.n, reg);
+  stat_fetch(J0);
+  tile_store<D>(qt_s[0], reg);
+  stat_store(0);
+  __syncthreads();
+  for (int it = 0; it < iters; ++it) {
+    const bool more = it + 1 < iters;
+    const int t0 = J0 + 32 * it;
+    if (more) {
+      tile_fetch<D>(Q, (int64_t)a.q_heads * D, t0 + 32, a.n, reg);
+      stat_fetch(t0 + 32);
+    }
+    const int p = it & 1;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      bf16x8 qa[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qa[kc] = tile_op<D>(qt_s[p], 16 * qt + r, kc, sgrp);
+      float mt[4], iv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mt[i] = ms[p][16 * qt + 4 * sgrp + i];
+        iv[i] = is[p][16 * qt + 4 * sgrp + i];
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const f32x4 acc = tile_z<D>(qa, kb[kt]);
+        const int j = jw + 16 * kt + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 16 * qt + 4 * sgrp + i;
+          if (t < a.n && t >= j) c[kt] += exp2f(acc[i] * a.qscale - mt[i]) * iv[i];
+        }
+      }
+    }
+    if (more) {
+      tile_store<D>(qt_s[(it + 1) & 1], reg);
+      stat_store((it + 1) & 1);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    float x = c[kt];
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    const int j = jw + 16 * kt + r;
+    if (sgrp == 0 && j < a.n) a.colsum[so + j] = x;
+  }
 }
 
 __global__ __launch_bounds__(256) void k_prefill_sum(const PrefillScoreArgs a) {
@@ -281,8 +387,11 @@ template <typename T, int D>
 hipError_t launch_t(const PrefillScoreArgs& a, hipStream_t s) {
   hipError_t e;
   if constexpr (std::is_same<T, uint16_t>::value) {
-    const dim3 grid((a.n + 63) / 64, a.q_heads, a.layers * a.batch);
-    k_prefill_rowstats_mk<D><<<grid, 256, 0, s>>>(a);
+    const dim3 grid((a.n + 127) / 128, a.q_heads, a.layers * a.batch);
+    k_prefill_rowstats_mk<D, 0><<<grid, 256, 0, s>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_prefill_rowstats_mk<D, 1><<<grid, 256, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_prefill_colsum_mk<D><<<grid, 256, 0, s>>>(a);
