@@ -420,8 +420,11 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
     // sub-tile (every load instruction covers 4 full rows), and MFMA #j takes
     // element j of those 8 rows, so its output columns are d = 8n + j.
     // V goes to fp16 exactly (bf16 values are fp16 values in its normal range).
+    // With head_dim 64 only lanes hl < 8 carry columns; the others load zeros
+    // and their output columns are dropped.
     constexpr int ST = RPW / 32;
     const int hl = lane & 15, kq = lane >> 4;
+    const bool col_ok = 8 * hl < D;
     const T* pV = poolV - part * EPL + 8 * hl;
     const T* sV = stageV - part * EPL + 8 * hl;
     f32x4 acc[8];
@@ -434,13 +437,14 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = rb + i;
-        const uint32_t code = r < nrows ? codes_s[r] : 0u;
-        if (QT && r < nrows && code >= qbase) {
+        const bool ok = col_ok && r < nrows;
+        const uint32_t code = ok ? codes_s[r] : 0u;
+        if (QT && ok && code >= qbase) {
           const uint32_t qi = code - qbase;
           vr[i] = deq_piece<T>(qV + (int64_t)qi * D + 8 * hl, qsV[qi]);
         } else {
           const T* p = code < cap0 ? pV + (int64_t)code * rs : sV + (int64_t)(code - cap0) * rs;
-          vr[i] = r < nrows ? load16nt(p) : make_uint4(0, 0, 0, 0);
+          vr[i] = ok ? load16nt(p) : make_uint4(0, 0, 0, 0);
         }
       }
       const half8 pa = *reinterpret_cast<const half8*>(&p16[hl][rb]);
@@ -468,7 +472,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * kq + i;
-      if (h < G) {
+      if (h < G && col_ok) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) osum[wave][h][8 * hl + j] = acc[j][i];
       }
