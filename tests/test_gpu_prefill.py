@@ -85,3 +85,14 @@ def test_scored_prefill_gqa_t2_stream():
                                            recent=64)
     st, _ = run_scored(w, w.steps, check_every=8, staging_layers=2)
     assert st["tier_count"][2] > 0
+
+
+PCASES = [(dt, d, g) for dt in ("bf16", "f32") for d in (64, 128) for g in (1, 5, 8)]
+
+
+@pytest.mark.parametrize("dtype,head_dim,group", PCASES, ids=["%s-d%d-g%d" % c for c in PCASES])
+def test_scored_prefill_each_path(dtype, head_dim, group):
+    # 229 positions: ragged against the 16-, 32- and 128-row tiles of the scoring passes
+    w = tkvsynth.CONFIGS["tiny"].replace(dtype=dtype, head_dim=head_dim, kv_heads=2, q_heads=2 * group, layers=2,
+                                         batch=2, prefill=229, steps=9, delta=8, prompt=8, recent=16)
+    run_scored(w, w.steps)
