@@ -266,6 +266,8 @@ def main():
                     help="steps of the CPU oracle baseline and of the parity check beside it (0: skip)")
     ap.add_argument("--baseline-steps", type=int, default=None,
                     help="timed steps of each baseline policy on the same engine (default: --steps; 0: skip)")
+    ap.add_argument("--prefill-reps", type=int, default=3,
+                    help="timed runs of the plain and the scored prefill of the workload's cache (0: skip)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short run for counter collection: 8 + 24 steps, then one 1 GiB device copy")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -286,6 +288,7 @@ def main():
 
     if args.pmc_probe:
         args.warmup, args.steps, args.stream_steps, args.cpu_steps, args.baseline_steps = 8, 24, 0, 0, 0
+        args.prefill_reps = 0
     base = tkvsynth.CONFIGS[args.workload]
     total = args.warmup + args.steps
     # the workload's own decode length, stretched if more steps are asked for
@@ -385,6 +388,34 @@ def main():
                 "hbm_ratio": wb.hbm_ratio, "evict_ratio": wb.evict_ratio, "no_t1": wb.no_t1,
                 "kernel_gbs": kb / (km / 1e3) / 1e9 if km > 0 else None,
                 "host_bytes": ba["host_bytes"]}
+
+    q_bytes = w.prefill * w.layers * w.batch * w.q_heads * w.head_dim * w.elem_bytes
+    if args.prefill_reps > 0 and q_bytes > (8 << 30):
+        result["prefill"] = {"skipped": "the prompt's queries would take %.0f GB of host memory" % (q_bytes / 1e9)}
+    elif args.prefill_reps > 0:
+        # the step before the decode path: fill the cache, with and without the prompt's scores
+        print("[bench] prefill: plain and scored, %d runs each" % args.prefill_reps, file=sys.stderr, flush=True)
+        qp = _dev(np.ascontiguousarray(np.moveaxis(w.q(w.steps, w.prefill, w.unit_vector()), 0, 2)), w.dtype, torch)
+        times = {}
+        for scored in (False, True):
+            ts = []
+            for _ in range(args.prefill_reps + 1):  # the first run warms up
+                c = tkv.TieredKV.for_workload(w)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                if scored:
+                    c.prefill_scored(inputs[0], inputs[1], qp)
+                else:
+                    c.prefill(inputs[0], inputs[1])
+                torch.cuda.synchronize()
+                ts.append(time.perf_counter() - t0)
+                c.close()
+            times[scored] = float(np.median(ts[1:])) * 1e3
+        del qp
+        result["prefill"] = {"positions": w.prefill, "plain_ms": times[False], "scored_ms": times[True],
+                             "scoring_and_replacement_ms": times[True] - times[False],
+                             "note": "plain: first placement + T1 rows to pinned host memory; scored adds the "
+                                     "prompt's causal attention scores and one full re-placement"}
 
     args.cpu_steps = min(args.cpu_steps, w.steps)
     if args.cpu_steps > 0:
