@@ -45,3 +45,65 @@ def dequantize_row(codes: np.ndarray, scale, bf16: bool) -> np.ndarray:
 def roundtrip(row: np.ndarray, bf16: bool) -> np.ndarray:
     codes, scale = quantize_row(row)
     return dequantize_row(codes, scale, bf16).reshape(np.shape(row))
+
+
+# ---- FP8 variant (the "FP8 etc." the ARKV summary names for low-precision
+# tiers): OCP FP8 E4M3, the "FN" encoding -- 1 sign bit, 4 exponent bits with
+# bias 7, 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9;
+# no infinities; exponent 15 with mantissa 7 is NaN, so the largest finite
+# magnitude is 2^8 * 1.75 = 448.  Reading used here, as for int8: one fp32
+# scale per (layer, token, K or V) row, scale = amax / 448 (1 for an all-zero
+# row); code = nearest E4M3 value of clamp(x / scale, -448, 448), ties to the
+# even code, the division in fp32; value = fp32(decode(code) * scale) rounded
+# to the cache type.
+def _e4m3_magnitudes() -> np.ndarray:
+    vals = np.empty(127, np.float64)          # codes 0x00 .. 0x7E
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        vals[c] = m * 2.0 ** -9 if e == 0 else 2.0 ** (e - 7) * (1.0 + m / 8.0)
+    return vals
+
+
+E4M3_MAGNITUDES = _e4m3_magnitudes()
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """fp32 values -> E4M3 codes (uint8): nearest magnitude, ties to the even
+    code, saturating at 448; the sign bit follows the sign of x (also -0)."""
+    x = np.asarray(x, np.float32).ravel()
+    a = np.minimum(np.abs(x.astype(np.float64)), E4M3_MAX)
+    dist = np.abs(a[:, None] - E4M3_MAGNITUDES[None, :])
+    idx = np.argmin(dist, axis=1)                       # the lower code of a tie
+    nxt = np.minimum(idx + 1, len(E4M3_MAGNITUDES) - 1)
+    tie = (nxt != idx) & (dist[np.arange(len(a)), nxt] == dist[np.arange(len(a)), idx])
+    idx = np.where(tie & (idx % 2 == 1), nxt, idx)     # ties go to the even code
+    sign = np.signbit(x).astype(np.uint8) << 7
+    return (sign | idx.astype(np.uint8)).astype(np.uint8)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """E4M3 codes (uint8) -> values (float32); the NaN codes give NaN."""
+    c = np.asarray(codes, np.uint8).ravel()
+    mag = c & 0x7F
+    v = np.where(mag == 0x7F, np.nan, E4M3_MAGNITUDES[np.minimum(mag, 126)])
+    return np.where(c & 0x80, -v, v).astype(np.float32)
+
+
+def quantize_row_fp8(row: np.ndarray):
+    """row: float32 values of one (layer, token, K|V) row -> (E4M3 codes, fp32 scale)."""
+    x = np.asarray(row, np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    scale = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+    y = np.clip(x / scale, np.float32(-E4M3_MAX), np.float32(E4M3_MAX)).astype(np.float32)
+    return e4m3_encode(y).reshape(np.shape(row)), scale
+
+
+def dequantize_row_fp8(codes: np.ndarray, scale, bf16: bool) -> np.ndarray:
+    v = (e4m3_decode(codes) * np.float32(scale)).astype(np.float32).reshape(np.shape(codes))
+    return _round_f32_to_bf16(v) if bf16 else v
+
+
+def roundtrip_fp8(row: np.ndarray, bf16: bool) -> np.ndarray:
+    codes, scale = quantize_row_fp8(row)
+    return dequantize_row_fp8(codes, scale, bf16).reshape(np.shape(row))
