@@ -107,10 +107,19 @@ __device__ __forceinline__ void unpack<float>(const uint4& u, float* f) {
 }
 
 // One 16-byte piece (EPL elements of the cache type) of a T2 row, from its
-// 8-bit codes: value = fp32(code * scale), rounded to the cache type (bf16
-// round-to-nearest-even) -- the same values the codec defines for the tier.
+// 8-bit codes (int8, or FP8 E4M3 when fp8): value = fp32(code value * scale),
+// rounded to the cache type (bf16 round-to-nearest-even) -- the same values
+// the codec defines for the tier.
 template <typename T>
-__device__ __forceinline__ uint4 deq_piece(const int8_t* codes, float scale);
+__device__ __forceinline__ uint4 deq_piece(const int8_t* codes, float scale, int fp8);
+
+// the four E4M3 bytes of w as floats (exact)
+__device__ __forceinline__ void e4m3x4(uint32_t w, float* f) {
+  f[0] = __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+  f[1] = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+  f[2] = __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+  f[3] = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+}
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   uint32_t u = __float_as_uint(x);
@@ -124,24 +133,37 @@ __device__ __forceinline__ float code_at(uint32_t w, int byte) {
 }
 
 template <>
-__device__ __forceinline__ uint4 deq_piece<bf16_t>(const int8_t* codes, float scale) {
+__device__ __forceinline__ uint4 deq_piece<bf16_t>(const int8_t* codes, float scale, int fp8) {
   const uint2 c = *reinterpret_cast<const uint2*>(codes);
-  const uint32_t w[2] = {c.x, c.y};
+  float v[8];
+  if (fp8) {
+    e4m3x4(c.x, v);
+    e4m3x4(c.y, v + 4);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = code_at(c.x, k);
+      v[4 + k] = code_at(c.y, k);
+    }
+  }
   uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = w[i >> 1];
-    const int k = 2 * (i & 1);
-    o[i] = bf16_bits(code_at(x, k) * scale) | (bf16_bits(code_at(x, k + 1) * scale) << 16);
-  }
+  for (int i = 0; i < 4; ++i) o[i] = bf16_bits(v[2 * i] * scale) | (bf16_bits(v[2 * i + 1] * scale) << 16);
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 template <>
-__device__ __forceinline__ uint4 deq_piece<float>(const int8_t* codes, float scale) {
+__device__ __forceinline__ uint4 deq_piece<float>(const int8_t* codes, float scale, int fp8) {
   const uint32_t x = *reinterpret_cast<const uint32_t*>(codes);
-  return make_uint4(__float_as_uint(code_at(x, 0) * scale), __float_as_uint(code_at(x, 1) * scale),
-                    __float_as_uint(code_at(x, 2) * scale), __float_as_uint(code_at(x, 3) * scale));
+  float v[4];
+  if (fp8) {
+    e4m3x4(x, v);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = code_at(x, k);
+  }
+  return make_uint4(__float_as_uint(v[0] * scale), __float_as_uint(v[1] * scale), __float_as_uint(v[2] * scale),
+                    __float_as_uint(v[3] * scale));
 }
 
 // Eq. 1 update for live rows [256 tile, 256 tile + 256) of sequence b:
@@ -288,7 +310,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
           const float sc = qsK[qi];
           const int8_t* qp = qK + (int64_t)qi * D + 8 * kq;
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) kd[tt][kc] = deq_piece<T>(qp + 32 * kc, sc);
+          for (int kc = 0; kc < KC; ++kc) kd[tt][kc] = deq_piece<T>(qp + 32 * kc, sc, a.rows.q_fp8);
         } else {
           const T* p = code < cap0 ? pK + (int64_t)code * rs : sK + (int64_t)(code - cap0) * rs;
           // 64-byte pieces per row per load: a streaming (non-temporal) hint would let
@@ -347,7 +369,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
           const uint32_t code = codes_s[r];
           if (QT && code >= qbase) {
             const uint32_t qi = code - qbase;
-            kd[u] = deq_piece<T>(qK + (int64_t)qi * D + part * EPL, qsK[qi]);
+            kd[u] = deq_piece<T>(qK + (int64_t)qi * D + part * EPL, qsK[qi], a.rows.q_fp8);
           } else {
             const T* p = code < cap0 ? poolK + (int64_t)code * rs : stageK + (int64_t)(code - cap0) * rs;
             kd[u] = load16nt(p);
@@ -441,7 +463,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
         const uint32_t code = ok ? codes_s[r] : 0u;
         if (QT && ok && code >= qbase) {
           const uint32_t qi = code - qbase;
-          vr[i] = deq_piece<T>(qV + (int64_t)qi * D + 8 * hl, qsV[qi]);
+          vr[i] = deq_piece<T>(qV + (int64_t)qi * D + 8 * hl, qsV[qi], a.rows.q_fp8);
         } else {
           const T* p = code < cap0 ? pV + (int64_t)code * rs : sV + (int64_t)(code - cap0) * rs;
           vr[i] = ok ? load16nt(p) : make_uint4(0, 0, 0, 0);
@@ -494,7 +516,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
           const uint32_t code = codes_s[r];
           if (QT && code >= qbase) {
             const uint32_t qi = code - qbase;
-            vd[u] = deq_piece<T>(qV + (int64_t)qi * D + part * EPL, qsV[qi]);
+            vd[u] = deq_piece<T>(qV + (int64_t)qi * D + part * EPL, qsV[qi], a.rows.q_fp8);
           } else {
             const T* p = code < cap0 ? poolV + (int64_t)code * rs : stageV + (int64_t)(code - cap0) * rs;
             vd[u] = load16nt(p);

@@ -2,16 +2,29 @@
 // gist.science technical summary, Method §1: T2 keeps low-importance rows on
 // the CPU at low precision, 8-bit as the example; results §4 its cost).
 //
-// Format (the pages fix none): symmetric int8, one fp32 scale per (layer,
-// position, K|V) over the position's kv_heads * head_dim values;
-// scale = amax / 127 (1 for an all-zero row), code = clamp(rne(x / scale),
-// -127, 127) with the division in fp32, value = fp32(code * scale) rounded
-// to the cache type (bf16 round-to-nearest-even).  A row that entered the
-// tier keeps these values for good.
+// Format (the pages fix none): one fp32 scale per (layer, position, K|V)
+// over the position's kv_heads * head_dim values.  int8: scale = amax / 127
+// (1 for an all-zero row), code = clamp(rne(x / scale), -127, 127).  FP8
+// (OCP E4M3): scale = amax / 448, code = the hardware's round-to-nearest-even
+// E4M3 of clamp(x / scale, -448, 448).  Both: the division in fp32, value =
+// fp32(code value * scale) rounded to the cache type (bf16
+// round-to-nearest-even).  A row that entered the tier keeps these values
+// for good.
 #include "tkv_internal.hpp"
 
 namespace tkvd {
 namespace {
+
+// E4M3 byte of y (|y| <= 448 already), and back (exact)
+__device__ __forceinline__ uint32_t e4m3_of(float y) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xFFu;
+}
+__device__ __forceinline__ float e4m3_val(uint32_t byte) { return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0); }
+
+// code (int8 or E4M3 byte) as the value it stands for
+__device__ __forceinline__ float code_val(int8_t c, int fp8) {
+  return fp8 ? e4m3_val((uint32_t)(uint8_t)c) : (float)c;
+}
 
 __device__ __forceinline__ float load_val(const void* base, int64_t idx, int elem_bytes) {
   if (elem_bytes == 2) return __uint_as_float((uint32_t)((const uint16_t*)base)[idx] << 16);
@@ -50,13 +63,23 @@ __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const Qua
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float scale = amax > 0.f ? amax / 127.f : 1.f;
+  const float qmax = a.fp8 ? 448.f : 127.f;
+  const float scale = amax > 0.f ? amax / qmax : 1.f;
   int8_t* codes = a.out.codes + (int64_t)which * (int64_t)gridDim.y * a.kv_heads * a.out.rows * d;
   for (int e = threadIdx.x; e < n; e += 256) {
     const int h = e / d, j = e % d;
     const float x = load_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.src) * d + j, a.elem_bytes);
-    const float c = fminf(fmaxf(rintf(x / scale), -127.f), 127.f);
-    codes[(((int64_t)l * a.kv_heads + h) * a.out.rows + op.dst) * d + j] = (int8_t)c;
+    float c;
+    int8_t code;
+    if (a.fp8) {
+      const uint32_t byte = e4m3_of(fminf(fmaxf(x / scale, -448.f), 448.f));
+      code = (int8_t)(uint8_t)byte;
+      c = e4m3_val(byte);
+    } else {
+      c = fminf(fmaxf(rintf(x / scale), -127.f), 127.f);
+      code = (int8_t)c;
+    }
+    codes[(((int64_t)l * a.kv_heads + h) * a.out.rows + op.dst) * d + j] = code;
     if (op.stage != kNoLoc) {
       void* st = which ? (void*)a.rows.stage_v : (void*)a.rows.stage_k;
       store_val(st, stage_elem(a.rows, l, op.b, h, op.stage, d) + j, c * scale, a.elem_bytes);
@@ -75,7 +98,7 @@ __global__ __launch_bounds__(256) void k_dequant_rows(const DequantArgs a, const
   void* f = which ? a.f.v : a.f.k;
   for (int e = threadIdx.x; e < n; e += 256) {
     const int h = e / d, j = e % d;
-    const float c = (float)codes[(((int64_t)l * a.kv_heads + h) * a.in.rows + op.src) * d + j];
+    const float c = code_val(codes[(((int64_t)l * a.kv_heads + h) * a.in.rows + op.src) * d + j], a.fp8);
     store_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.dst) * d + j, c * scale, a.elem_bytes);
   }
 }

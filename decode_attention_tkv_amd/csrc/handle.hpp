@@ -149,6 +149,7 @@ struct tkv {
     r.cap1 = cap1;
     r.cap2 = cap2;
     r.stage_slots = S;
+    r.q_fp8 = (flags & TKV_FLAG_T2_FP8) ? 1 : 0;
     return r;
   }
 };

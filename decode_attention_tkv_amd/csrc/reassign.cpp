@@ -395,7 +395,7 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   ca.pack_in_v = t->fin ? (char*)t->fin + (size_t)L * H * NF1 * hb : nullptr;
   ca.pack_in_rows = NF1;
   HIP_TRY(t, launch_copy_rows(ca, d_ops1, (int)ops1.size(), L, st));
-  DequantArgs dqa{qin, fp, H, D, t->esz};
+  DequantArgs dqa{qin, fp, H, D, t->esz, (t->flags & TKV_FLAG_T2_FP8) ? 1 : 0};
   HIP_TRY(t, launch_dequant_rows(dqa, d_dq1, (int)dq1.size(), L, st));
   HIP_TRY(t, launch_copy_rows(ca, d_ops2a, (int)ops2a.size(), L, st));
   HIP_TRY(t, launch_copy_rows(ca, d_ops2b, (int)ops2b.size(), L, st));
@@ -405,7 +405,7 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
     int rc = grow_device(t, &t->qout, &t->qout_bytes, 2 * codes_half + 2 * sc_half);
     if (rc) return rc;
     qout = QPack{(int8_t*)t->qout, (float*)((char*)t->qout + 2 * codes_half), E2};
-    QuantArgs qa{t->rowspace(), fp, qout, H, D, t->esz};
+    QuantArgs qa{t->rowspace(), fp, qout, H, D, t->esz, (t->flags & TKV_FLAG_T2_FP8) ? 1 : 0};
     HIP_TRY(t, launch_quant_rows(qa, d_q2, (int)q2.size(), L, st));
   }
   HIP_TRY(t, launch_set_loc(d_upd, (int)upd.size(), t->loc, t->nmax, st));

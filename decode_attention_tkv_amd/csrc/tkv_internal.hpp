@@ -44,6 +44,7 @@ struct RowSpace {
   int64_t qs_lstride, qs_bstride;                       // T2 scales per slot / sequence
   int32_t cap0, cap1, cap2;
   int32_t stage_slots;
+  int32_t q_fp8;  // T2 codes are FP8 E4M3 (else int8)
 };
 
 // T2 area offsets: codes of row idx (kv head h) of layer l's slot, and its scale.
@@ -195,6 +196,7 @@ struct QuantArgs {
   FPack f;
   QPack out;
   int32_t kv_heads, head_dim, elem_bytes;
+  int32_t fp8;  // FP8 E4M3 codes (else int8)
 };
 
 struct DequantOp {
@@ -207,6 +209,7 @@ struct DequantArgs {
   QPack in;
   FPack f;
   int32_t kv_heads, head_dim, elem_bytes;
+  int32_t fp8;
 };
 
 // Scored prefill: inputs k [layers][batch][n][kv_heads][d], q [layers][batch][n][q_heads][d]

@@ -96,6 +96,13 @@ typedef struct {
  * hbm_ratio 0, evict_ratio 1 and prompt 0 reach the same set at every
  * reassignment, keeping the other rows in T1 until the first one.) */
 #define TKV_FLAG_NO_T1 2ull
+/* T2 rows as FP8 instead of int8 (the "FP8 etc." low-precision formats the
+ * ARKV summary names): OCP E4M3 ("FN": bias 7, largest finite 448), one fp32
+ * scale per (layer, position, K|V) row, scale = amax / 448 (1 for a zero
+ * row), code = nearest E4M3 of clamp(x / scale, -448, 448) with ties to even,
+ * value = fp32(decode(code) * scale) rounded to the cache type.  Codes and
+ * scales have the int8 format's sizes; tkv_read_t2 returns the E4M3 bytes. */
+#define TKV_FLAG_T2_FP8 4ull
 
 /* One changed row of a reassignment (Method §4). */
 typedef struct {

@@ -1,7 +1,8 @@
 """GPU 8-bit host tier (T2) against the oracle, through the C ABI.
 
 "Not All Thoughts Need HBM" (gist.science summary), Method §1: T2 holds
-low-importance rows on the host at 8 bits; §4: only changed rows move.
+low-importance rows on the host at 8 bits; §4: only changed rows move.  Both
+8-bit formats: int8 and FP8 (OCP E4M3).
 
 Checks:
   * every row entering T2 gets int8 codes and scales identical to the
@@ -54,17 +55,21 @@ def _run_t2(w, inp, staging_layers=0, check_codec=True):
                     if new != 2:
                         continue
                     entered += 1
+                    quant = codec.quantize_row_fp8 if w.t2_fp8 else codec.quantize_row
+                    deq = codec.dequantize_row_fp8 if w.t2_fp8 else codec.dequantize_row
                     for l in range(w.layers):
                         kc, vc, sc = c.read_t2(l, b, pos)
-                        rk, sk = codec.quantize_row(before_k[l, b, pos])
-                        rv, sv = codec.quantize_row(before_v[l, b, pos])
-                        assert np.array_equal(kc.ravel(), rk.ravel()) and np.array_equal(vc.ravel(), rv.ravel())
+                        rk, sk = quant(before_k[l, b, pos])
+                        rv, sv = quant(before_v[l, b, pos])
+                        # codes compared as bytes: int8 two's complement, or the E4M3 bit patterns
+                        assert np.array_equal(kc.view(np.uint8).ravel(), np.asarray(rk).view(np.uint8).ravel())
+                        assert np.array_equal(vc.view(np.uint8).ravel(), np.asarray(rv).view(np.uint8).ravel())
                         assert sc[0] == sk and sc[1] == sv
                         if staging_layers == 0:
                             gk, gv = c.read_kv(l, b, pos)
                             gk, gv = w.values(gk), w.values(gv)
-                            assert np.array_equal(gk, codec.dequantize_row(rk, sk, bf16).reshape(gk.shape))
-                            assert np.array_equal(gv, codec.dequantize_row(rv, sv, bf16).reshape(gv.shape))
+                            assert np.array_equal(gk, deq(rk, sk, bf16).reshape(gk.shape))
+                            assert np.array_equal(gv, deq(rv, sv, bf16).reshape(gv.shape))
     s = c.read_scores()
     st = c.stats()
     c.close()
@@ -99,4 +104,22 @@ def test_t2_stream_equals_resident():
 
 def test_t2_fp32_cache():
     w = tkvsynth.CONFIGS["tiny"].replace(t2_ratio=0.15, steps=64)
+    _run_t2(w, Inputs(w))
+
+
+def test_t2_fp8_resident_parity_and_codec():
+    w = _w32(t2_fp8=True)
+    _run_t2(w, Inputs(w))
+
+
+def test_t2_fp8_stream_equals_resident():
+    w = _w32(layers=5, t2_fp8=True)
+    inp = Inputs(w)
+    a, _, _ = _run_t2(w, inp, staging_layers=0, check_codec=False)
+    b, st, _ = _run_t2(w, inp, staging_layers=2, check_codec=True)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_t2_fp8_fp32_cache():
+    w = tkvsynth.CONFIGS["tiny"].replace(t2_ratio=0.15, steps=64, t2_fp8=True)
     _run_t2(w, Inputs(w))
