@@ -94,12 +94,14 @@ class OracleTKV:
     """Plain model of the tiered cache of a batch of sequences."""
 
     def __init__(self, layers, q_heads, kv_heads, head_dim, batch, max_tokens, delta,
-                 hbm_ratio, evict_ratio, t2_ratio, prompt, sinks, recent, bf16, no_t1=False, t2_fp8=False):
+                 hbm_ratio, evict_ratio, t2_ratio, prompt, sinks, recent, bf16, no_t1=False, t2_fp8=False,
+                 shared_hbm=False):
         self.L, self.Hq, self.Hkv, self.d, self.B = layers, q_heads, kv_heads, head_dim, batch
         self.nmax, self.delta = max_tokens, delta
         self.hbm, self.evict, self.t2 = hbm_ratio, evict_ratio, t2_ratio
         self.no_t1 = no_t1
         self.t2_fp8 = t2_fp8
+        self.shared_hbm = shared_hbm
         self.prompt, self.sinks, self.recent = prompt, sinks, recent
         self.bf16 = bf16
         self.K = np.zeros((layers, batch, max_tokens, kv_heads, head_dim), np.float32)
@@ -113,7 +115,7 @@ class OracleTKV:
     def for_workload(cls, w, max_tokens=None):
         return cls(w.layers, w.q_heads, w.kv_heads, w.head_dim, w.batch,
                    max_tokens or w.n_final, w.delta, w.hbm_ratio, w.evict_ratio, w.t2_ratio,
-                   w.prompt, w.sinks, w.recent, w.dtype == "bf16", w.no_t1, w.t2_fp8)
+                   w.prompt, w.sinks, w.recent, w.dtype == "bf16", w.no_t1, w.t2_fp8, w.shared_hbm)
 
     # -- cache contents ------------------------------------------------------
     def prefill(self, K, V):
@@ -173,10 +175,17 @@ class OracleTKV:
         scores = self.s[:, :n] if rank_scores is None else np.asarray(rank_scores, np.float64)
         new_all = np.empty((self.B, n), np.uint8)
         deltas = []
+        shared = None
+        if self.shared_hbm:
+            shared = tiering.reassign_shared(self.tier[:, :n].copy(), scores, n, self.prompt, self.sinks,
+                                             self.recent, self.hbm, self.evict, self.t2)
         for b in range(self.B):
             old = self.tier[b, :n].copy()
-            new = tiering.reassign(old, scores[b], n, self.prompt, self.sinks, self.recent,
-                                   self.hbm, self.evict, self.t2, self.no_t1)
+            if shared is not None:
+                new = shared[b]
+            else:
+                new = tiering.reassign(old, scores[b], n, self.prompt, self.sinks, self.recent,
+                                       self.hbm, self.evict, self.t2, self.no_t1)
             if adopt is not None:
                 new = np.asarray(adopt[b][:n], np.uint8)
             deltas.append(tiering.delta_lists(old, new))

@@ -112,3 +112,50 @@ def delta_lists(old_tiers: np.ndarray, new_tiers: np.ndarray):
     promote = [(int(i), int(old[i]), int(new[i])) for i in np.nonzero(new < old)[0]]
     demote = [(int(i), int(old[i]), int(new[i])) for i in np.nonzero(new > old)[0]]
     return promote, demote
+
+
+def reassign_shared(old_tiers: np.ndarray, scores: np.ndarray, n: int, prompt: int, sinks: int, recent: int,
+                    hbm_ratio: float, evict_ratio: float, t2_ratio: float) -> np.ndarray:
+    """Budget variant: one HBM (T0) budget shared by the sequences of a batch
+    (the batch projection of the summary's Results; Method §1 rules
+    otherwise).  Per sequence, exactly as reassign(): the protected rows stay
+    in T0, the n3 lowest-ranked candidates are evicted and T2 takes the next
+    lowest.  T0 beyond the protected rows holds the best n0c_total of the
+    batch's remaining candidates, ranked jointly by (score descending,
+    sequence ascending, position ascending), with
+        n0c_total = min(sum of remaining, max(0, B floor(h N) - sum |P|)).
+    old_tiers, scores: [B][>= n]."""
+    B = len(old_tiers)
+    prot = protected_mask(n, prompt, sinks, recent)
+    ranked, n3s = [], []
+    for b in range(B):
+        old = np.asarray(old_tiers[b])[:n]
+        evicted = old == T3
+        cand = np.nonzero(~prot & ~evicted)[0]
+        n3, _, _ = tier_counts(n, int(prot.sum()), len(cand), int(evicted.sum()), hbm_ratio, evict_ratio, t2_ratio)
+        ranked.append(rank_best_first(cand, scores[b]))
+        n3s.append(n3)
+    remaining = [(b, i) for b in range(B) for i in ranked[b][: len(ranked[b]) - n3s[b]]]
+    budget = B * math.floor(hbm_ratio * n) - B * int(prot.sum())
+    n0c_total = min(len(remaining), max(0, budget))
+    joint = sorted(remaining, key=lambda bi: (-float(scores[bi[0]][bi[1]]), bi[0], bi[1]))
+    in_t0 = set(joint[:n0c_total])
+    new = np.empty((B, n), np.uint8)
+    for b in range(B):
+        old = np.asarray(old_tiers[b])[:n]
+        new[b][old == T3] = T3
+        new[b][prot & (old != T3)] = T0
+        rb = ranked[b]
+        c, n3 = len(rb), n3s[b]
+        n0c = sum(1 for i in rb if (b, i) in in_t0)
+        n2 = min(c - n3 - n0c, math.floor(t2_ratio * n))
+        for r, i in enumerate(rb):
+            if (b, i) in in_t0:
+                new[b][i] = T0
+            elif r >= c - n3:
+                new[b][i] = T3
+            elif r >= c - n3 - n2:
+                new[b][i] = T2
+            else:
+                new[b][i] = T1
+    return new
