@@ -25,6 +25,7 @@ TKV_T0, TKV_T1, TKV_T2, TKV_T3 = 0, 1, 2, 3
 TKV_FLAG_TIME_KERNELS = 1
 TKV_FLAG_NO_T1 = 2
 TKV_FLAG_T2_FP8 = 4
+TKV_FLAG_SHARED_HBM = 8
 
 _NAMES = {TKV_EINVAL: "EINVAL", TKV_ECAPACITY: "ECAPACITY", TKV_ENOMEM: "ENOMEM",
           TKV_ESTATE: "ESTATE", TKV_EHIP: "EHIP"}
@@ -225,7 +226,7 @@ class TieredKV:
 
     def __init__(self, layers, q_heads, kv_heads, head_dim, batch, max_tokens, dtype="bf16", delta=64,
                  hbm_ratio=0.5, evict_ratio=0.03, prompt=0, sinks=4, recent=128, t2_ratio=0.0,
-                 staging_layers=0, chunk=0, time_kernels=False, no_t1=False, t2_fp8=False):
+                 staging_layers=0, chunk=0, time_kernels=False, no_t1=False, t2_fp8=False, shared_hbm=False):
         self.L, self.Hq, self.Hkv, self.D, self.B, self.nmax = layers, q_heads, kv_heads, head_dim, batch, max_tokens
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -233,14 +234,15 @@ class TieredKV:
                             TKV_BF16 if dtype == "bf16" else TKV_F32, delta, hbm_ratio, evict_ratio,
                             prompt, sinks, recent, t2_ratio, staging_layers, chunk,
                             (TKV_FLAG_TIME_KERNELS if time_kernels else 0) | (TKV_FLAG_NO_T1 if no_t1 else 0)
-                            | (TKV_FLAG_T2_FP8 if t2_fp8 else 0))
+                            | (TKV_FLAG_T2_FP8 if t2_fp8 else 0) | (TKV_FLAG_SHARED_HBM if shared_hbm else 0))
 
     @classmethod
     def for_workload(cls, w, **kw):
         args = dict(layers=w.layers, q_heads=w.q_heads, kv_heads=w.kv_heads, head_dim=w.head_dim,
                     batch=w.batch, max_tokens=w.n_final, dtype=w.dtype, delta=w.delta,
                     hbm_ratio=w.hbm_ratio, evict_ratio=w.evict_ratio, prompt=w.prompt, sinks=w.sinks,
-                    recent=w.recent, t2_ratio=w.t2_ratio, no_t1=w.no_t1, t2_fp8=w.t2_fp8)
+                    recent=w.recent, t2_ratio=w.t2_ratio, no_t1=w.no_t1, t2_fp8=w.t2_fp8,
+                    shared_hbm=w.shared_hbm)
         args.update(kw)
         return cls(**args)
 

@@ -121,6 +121,8 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
     return tkv_fail(nullptr, TKV_EINVAL, "chunk must be 128, 256 or 512");
   if (o.staging_layers < 0 || o.staging_layers == 1)
     return tkv_fail(nullptr, TKV_EINVAL, "staging_layers must be 0 or >= 2");
+  if ((o.flags & TKV_FLAG_NO_T1) && (o.flags & TKV_FLAG_SHARED_HBM))
+    return tkv_fail(nullptr, TKV_EINVAL, "TKV_FLAG_NO_T1 and TKV_FLAG_SHARED_HBM do not combine");
   const bool resident = o.staging_layers == 0 || o.staging_layers >= s.layers;
 
   tkv* t = new tkv();
@@ -150,7 +152,9 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   const int64_t nmax = s.max_tokens;
   const int64_t pmax = std::min<int64_t>(nmax, (int64_t)std::max(protect.prompt, protect.sinks) + protect.recent);
   const int64_t h_at_max = floor_ratio(hbm_ratio, nmax);
+  t->shared_hbm = (o.flags & TKV_FLAG_SHARED_HBM) != 0;
   t->cap0 = (int)std::min<int64_t>(nmax, std::max(pmax, h_at_max) + delta + 1);
+  if (t->shared_hbm) t->cap0 *= s.batch;  // slots of the whole batch in one space
   t->cap1 = (o.flags & TKV_FLAG_NO_T1) ? 1 : (int)std::max<int64_t>(1, std::min<int64_t>(nmax, nmax - h_at_max + 1));
   t->cap2 = o.t2_ratio > 0 ? (int)std::min<int64_t>(nmax, floor_ratio(o.t2_ratio, nmax) + 1) : 0;
   t->capS = resident ? t->cap1 + t->cap2 : t->cap1;
@@ -162,8 +166,9 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   auto dev = [&](void** p, size_t bytes) {
     if (rc == TKV_OK) rc = device_alloc(t, p, bytes);
   };
-  dev(&t->pool_k, L * B * t->cap0 * t->row_bytes);
-  dev(&t->pool_v, L * B * t->cap0 * t->row_bytes);
+  const size_t pool_rows = (size_t)L * t->cap0 * (t->shared_hbm ? 1 : B);
+  dev(&t->pool_k, pool_rows * t->row_bytes);
+  dev(&t->pool_v, pool_rows * t->row_bytes);
   dev(&t->stage_k, (size_t)t->S * B * t->capS * t->row_bytes);
   dev(&t->stage_v, (size_t)t->S * B * t->capS * t->row_bytes);
   dev((void**)&t->live_loc, B * nmax * 4);
@@ -228,7 +233,7 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
     return rc;
   }
   t->nlive.assign(B, 0);
-  t->free0.resize(B);
+  t->free0.resize(t->shared_hbm ? 1 : B);
   for (auto& f : t->free0) {
     f.resize(t->cap0);
     for (int i = 0; i < t->cap0; ++i) f[i] = t->cap0 - 1 - i;  // back() = lowest free slot
@@ -238,7 +243,8 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   t->t1_owner.resize(B);
   t->t2_owner.resize(B);
   std::memset(t->h_counts, 0, B * 2 * 4);
-  t->st.hbm_bytes = (int64_t)(2 * L * B * t->cap0 + 2 * (size_t)t->S * B * t->capS) * t->row_bytes +
+  t->st.hbm_bytes = (int64_t)(2 * (size_t)L * t->cap0 * (t->shared_hbm ? 1 : B) + 2 * (size_t)t->S * B * t->capS) *
+                        t->row_bytes +
                     (resident ? 0 : (int64_t)(2 * (size_t)t->S * B * t->cap2) * (t->Hkv * t->D + 4));
   t->st.host_bytes = (int64_t)(2 * L * B * t->cap1) * t->row_bytes +
                      (int64_t)(2 * L * B * t->cap2) * (t->Hkv * t->D + 4);
@@ -269,7 +275,7 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
   const int nt0 = (int)std::count(first.begin(), first.end(), (uint8_t)TKV_T0);
   const int nt1 = (int)std::count(first.begin(), first.end(), (uint8_t)TKV_T1);
   const int nt3 = n0 - nt0 - nt1;  // evicted at once (eviction-only baseline)
-  if (nt0 > t->cap0 || nt1 > t->cap1)
+  if (nt0 * (t->shared_hbm ? t->B : 1) > t->cap0 || nt1 > t->cap1)
     return tkv_fail(t, TKV_ECAPACITY, "first placement does not fit (T0 %d/%d, T1 %d/%d)", nt0, t->cap0, nt1, t->cap1);
 
   std::vector<uint32_t> codes((size_t)t->B * n0);
@@ -279,8 +285,8 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
     for (int p = 0; p < n0; ++p) {
       uint32_t code;
       if (first[p] == TKV_T0) {
-        code = (uint32_t)t->free0[b].back();
-        t->free0[b].pop_back();
+        code = (uint32_t)t->free_list(b).back();
+        t->free_list(b).pop_back();
       } else if (first[p] == TKV_T1) {
         code = (uint32_t)(t->cap0 + own.size());
         own.push_back(p);
@@ -403,8 +409,12 @@ extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t s
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "previous step has layers left");
   if (!k || !v) return tkv_fail(t, TKV_EINVAL, "k/v is NULL");
   if (t->n >= t->nmax) return tkv_fail(t, TKV_ECAPACITY, "max_tokens (%d) reached", t->nmax);
-  for (int b = 0; b < t->B; ++b)
-    if (t->free0[b].empty()) return tkv_fail(t, TKV_ECAPACITY, "T0 pool full (sequence %d): reassign first", b);
+  if (t->shared_hbm) {
+    if ((int)t->free0[0].size() < t->B) return tkv_fail(t, TKV_ECAPACITY, "shared T0 pool full: reassign first");
+  } else {
+    for (int b = 0; b < t->B; ++b)
+      if (t->free0[b].empty()) return tkv_fail(t, TKV_ECAPACITY, "T0 pool full (sequence %d): reassign first", b);
+  }
   AppendArgs a{};
   a.rows = t->rowspace();
   a.k = k;
@@ -422,14 +432,14 @@ extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t s
   a.nmax = t->nmax;
   a.pos = t->n;
   for (int b = 0; b < t->B; ++b) {
-    a.slot[b] = t->free0[b].back();
+    a.slot[b] = t->free_list(b)[t->free_list(b).size() - 1 - (t->shared_hbm ? b : 0)];
     a.nlive[b] = t->nlive[b];
   }
   HIP_TRY(t, launch_append(a, t->score_pending ? &t->pending_score : nullptr, t->pending_tiles,
                            (hipStream_t)stream));
   t->score_pending = false;
   for (int b = 0; b < t->B; ++b) {
-    t->free0[b].pop_back();
+    t->free_list(b).pop_back();  // shared: the B slots taken above, from the back
     const size_t off = (size_t)b * t->nmax + t->n;
     t->h_tier[off] = TKV_T0;
     t->h_loc[off] = (uint32_t)a.slot[b];

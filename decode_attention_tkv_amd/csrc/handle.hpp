@@ -25,7 +25,7 @@ struct tkv {
   int64_t row_elems = 0, row_bytes = 0;
 
   // ---- device buffers (owned)
-  void* pool_k = nullptr;  // [L][B][Hkv][cap0][D]
+  void* pool_k = nullptr;  // [L][B][Hkv][cap0][D], or [L][Hkv][cap0][D] when the batch shares it
   void* pool_v = nullptr;
   void* stage_k = nullptr;  // [S][B][Hkv][capS][D]: T1 rows, then (resident) T2 values
   void* stage_v = nullptr;
@@ -95,7 +95,9 @@ struct tkv {
   tkvd::ScoreArgs pending_score{};
   int pending_tiles = 0;
   std::vector<int32_t> nlive;                 // [B] live rows
-  std::vector<std::vector<int32_t>> free0;    // [B] free T0 slots (back = next to use)
+  std::vector<std::vector<int32_t>> free0;    // [B] free T0 slots (back = next to use); [1] when shared
+  bool shared_hbm = false;                    // one T0 slot space and budget for the batch
+  std::vector<int32_t>& free_list(int b) { return free0[shared_hbm ? 0 : b]; }
   std::vector<uint8_t> h_tier;                // [B][nmax]
   std::vector<uint32_t> h_loc;                // [B][nmax]
   std::vector<std::vector<int32_t>> t1_owner; // [B]: T1 arena index -> position
@@ -131,8 +133,8 @@ struct tkv {
     r.stage_k = stage_k;
     r.stage_v = stage_v;
     r.pool_hstride = (int64_t)cap0 * D;
-    r.pool_bstride = r.pool_hstride * Hkv;
-    r.pool_lstride = r.pool_bstride * B;
+    r.pool_bstride = shared_hbm ? 0 : r.pool_hstride * Hkv;
+    r.pool_lstride = r.pool_hstride * Hkv * (shared_hbm ? 1 : B);
     r.stage_hstride = (int64_t)capS * D;
     r.stage_bstride = r.stage_hstride * Hkv;
     r.stage_lstride = r.stage_bstride * B;

@@ -93,6 +93,62 @@ void compact(std::vector<int32_t>& own, const std::vector<char>& vac, uint32_t* 
 
 }  // namespace
 
+// Batch-shared HBM budget: how many candidates of each sequence the joint
+// ranking puts in T0.  Per sequence the n3 lowest-ranked candidates are set
+// aside (eviction keeps its own budget); the rest of the batch is ranked by
+// (fp32 score descending, sequence ascending, position ascending) -- the
+// kernel's keys, extended by the sequence -- and the best
+// min(remaining, B * floor(hN) - sum |P|) go to T0.  T2 then takes its own
+// budget from what each sequence has left.
+static int shared_t0_counts(tkv* t, hipStream_t st, const std::vector<int64_t>& ncand, const std::vector<int64_t>& nprot,
+                     std::vector<CutCounts>* cuts) {
+  const int B = t->B, n = t->n;
+  const size_t nmax = t->nmax;
+  std::vector<float> s((size_t)B * nmax);
+  HIP_TRY(t, hipMemcpyAsync(s.data(), t->s, s.size() * 4, hipMemcpyDeviceToHost, st));
+  HIP_TRY(t, hipStreamSynchronize(st));
+  struct Key {
+    uint32_t bits;  // fp32 score bits: scores are >= 0, so the bits order as the values
+    int32_t b, pos;
+  };
+  auto better = [](const Key& x, const Key& y) {
+    if (x.bits != y.bits) return x.bits > y.bits;
+    if (x.b != y.b) return x.b < y.b;
+    return x.pos < y.pos;
+  };
+  std::vector<Key> remaining;
+  int64_t budget = 0;
+  for (int b = 0; b < B; ++b) {
+    std::vector<Key> cand;
+    cand.reserve(ncand[b]);
+    for (int p = 0; p < n; ++p) {
+      const uint8_t x = t->h_tier[(size_t)b * nmax + p];
+      if (x == TKV_T3 || is_protected(*t, p, n)) continue;
+      uint32_t bits;
+      std::memcpy(&bits, &s[(size_t)b * nmax + p], 4);
+      cand.push_back({bits, b, p});
+    }
+    std::sort(cand.begin(), cand.end(), better);
+    cand.resize(cand.size() - (size_t)(*cuts)[b].n3);  // the lowest n3 are evicted
+    remaining.insert(remaining.end(), cand.begin(), cand.end());
+    budget += floor_ratio(t->hbm, n) - nprot[b];
+  }
+  const int64_t take = std::min<int64_t>((int64_t)remaining.size(), std::max<int64_t>(0, budget));
+  std::vector<int64_t> n0c(B, 0);
+  if (take > 0) {
+    std::nth_element(remaining.begin(), remaining.begin() + (take - 1), remaining.end(), better);
+    const Key last = remaining[take - 1];
+    for (const Key& k : remaining)
+      if (!better(last, k)) n0c[k.b] += 1;  // k is at least as good as the last one taken
+  }
+  for (int b = 0; b < B; ++b) {
+    CutCounts& c = (*cuts)[b];
+    c.n0c = n0c[b];
+    c.n2 = std::min<int64_t>(ncand[b] - c.n3 - c.n0c, floor_ratio(t->t2, n));
+  }
+  return TKV_OK;
+}
+
 extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "reassign between the layer groups of a step");
@@ -122,6 +178,8 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   ra.prompt = t->prompt;
   ra.sinks = t->sinks;
   ra.recent = t->recent;
+  std::vector<CutCounts> cuts(B);
+  std::vector<int64_t> ncands(B), nprots(B);
   for (int b = 0; b < B; ++b) {
     int64_t np = 0, nev = 0;
     const uint8_t* tr = &t->h_tier[b * nmax];
@@ -131,9 +189,16 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
       else if (is_protected(*t, p, n))
         ++np;
     }
-    const int64_t ncand = n - np - nev;
-    const CutCounts cc = cut_counts(*t, n, np, nev);
-    const int64_t n3 = cc.n3, n0c = cc.n0c, n2 = cc.n2;
+    ncands[b] = n - np - nev;
+    nprots[b] = np;
+    cuts[b] = cut_counts(*t, n, np, nev);
+  }
+  if (t->shared_hbm) {
+    int rc = shared_t0_counts(t, st, ncands, nprots, &cuts);
+    if (rc) return rc;
+  }
+  for (int b = 0; b < B; ++b) {
+    const int64_t ncand = ncands[b], n3 = cuts[b].n3, n0c = cuts[b].n0c, n2 = cuts[b].n2;
     ra.ncand[b] = (int32_t)ncand;
     ra.rank[b][0] = (int32_t)n3;
     ra.rank[b][1] = (int32_t)(n3 + n2);
@@ -165,15 +230,20 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   std::vector<SeqPlan> plan(B);
   std::vector<LocUpdate> upd;
   int64_t E1 = 0, E2 = 0, P = 0, n_evict = 0, n_prom = 0, n_dem = 0;
+  const uint32_t c1 = (uint32_t)t->cap0, c2 = (uint32_t)(t->cap0 + t->cap1);
+  std::vector<std::vector<char>> vac1s(B), vac2s(B);
+  // pass 1: who leaves which place; every freed T0 slot goes back to its free
+  // list before any promotion takes one (the lists are shared by the batch
+  // when the HBM budget is)
   for (int b = 0; b < B; ++b) {
     SeqPlan& sp = plan[b];
     uint8_t* tr = &t->h_tier[b * nmax];
     uint32_t* lc = &t->h_loc[b * nmax];
-    auto& own1 = t->t1_owner[b];
-    auto& own2 = t->t2_owner[b];
-    std::vector<char> vac1(own1.size(), 0), vac2(own2.size(), 0);
+    auto& vac1 = vac1s[b];
+    auto& vac2 = vac2s[b];
+    vac1.assign(t->t1_owner[b].size(), 0);
+    vac2.assign(t->t2_owner[b].size(), 0);
     std::vector<uint32_t> freed;
-    const uint32_t c1 = (uint32_t)t->cap0, c2 = (uint32_t)(t->cap0 + t->cap1);
     auto source = [&](uint32_t pos, uint8_t old) -> Move {
       if (old == TKV_T0) return {pos, kFromPool, lc[pos]};
       if (old == TKV_T1) {
@@ -208,19 +278,26 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
     auto by_pos = [](const Move& x, const Move& y) { return x.pos < y.pos; };
     std::sort(sp.ent1.begin(), sp.ent1.end(), by_pos);
     std::sort(sp.ent2.begin(), sp.ent2.end(), by_pos);
-    // T0 slots: freed ones go back first, then promotions take slots
-    for (auto it = freed.rbegin(); it != freed.rend(); ++it) t->free0[b].push_back((int32_t)*it);
+    for (auto it = freed.rbegin(); it != freed.rend(); ++it) t->free_list(b).push_back((int32_t)*it);
+  }
+  // pass 2: promotions take T0 slots; arenas compact and take their entrants
+  for (int b = 0; b < B; ++b) {
+    SeqPlan& sp = plan[b];
+    uint8_t* tr = &t->h_tier[b * nmax];
+    uint32_t* lc = &t->h_loc[b * nmax];
+    auto& own1 = t->t1_owner[b];
+    auto& own2 = t->t2_owner[b];
     for (const Move& mv : sp.promo) {
-      if (t->free0[b].empty()) return tkv_fail(t, TKV_ECAPACITY, "T0 pool full while promoting");
-      const uint32_t slot = (uint32_t)t->free0[b].back();
-      t->free0[b].pop_back();
+      if (t->free_list(b).empty()) return tkv_fail(t, TKV_ECAPACITY, "T0 pool full while promoting");
+      const uint32_t slot = (uint32_t)t->free_list(b).back();
+      t->free_list(b).pop_back();
       sp.promo_slot.push_back(slot);
       lc[mv.pos] = slot;
       upd.push_back({b, mv.pos, slot});
     }
     // arenas: compaction, then the entrants at the end
-    compact(own1, vac1, &sp.m1, &sp.mov1);
-    compact(own2, vac2, &sp.m2, &sp.mov2);
+    compact(own1, vac1s[b], &sp.m1, &sp.mov1);
+    compact(own2, vac2s[b], &sp.m2, &sp.mov2);
     for (auto& mv : sp.mov1) {
       lc[own1[mv.second]] = c1 + mv.second;
       upd.push_back({b, (uint32_t)own1[mv.second], c1 + mv.second});

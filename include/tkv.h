@@ -103,6 +103,15 @@ typedef struct {
  * value = fp32(decode(code) * scale) rounded to the cache type.  Codes and
  * scales have the int8 format's sizes; tkv_read_t2 returns the E4M3 bytes. */
 #define TKV_FLAG_T2_FP8 4ull
+/* Budget variant: one HBM budget for the whole batch (the batch projection of
+ * the summary's Results).  The T0 pool is one slot space shared by the
+ * sequences; at each reassignment the protected rows stay in T0, eviction and
+ * T2 follow each sequence's own budgets as usual, and the remaining
+ * batch * floor(hbm_ratio*N) - sum |P| T0 slots go to the best candidates of
+ * the whole batch, ranked jointly by score (ties: lower sequence, then lower
+ * position).  The first placement is per sequence (no scores yet).  Not
+ * combinable with TKV_FLAG_NO_T1 (TKV_EINVAL). */
+#define TKV_FLAG_SHARED_HBM 8ull
 
 /* One changed row of a reassignment (Method §4). */
 typedef struct {
