@@ -371,6 +371,8 @@ def main():
         policies = (("full cache (all rows in T0)", dict(hbm_ratio=1.0, evict_ratio=0.0)),
                     ("eviction only, heavy hitters (no T1)", dict(no_t1=True)),
                     ("sinks + recent window", dict(hbm_ratio=0.0, no_t1=True, prompt=0)))
+        if w.batch > 1:
+            policies += (("one HBM budget for the batch", dict(shared_hbm=True)),)
         result["baselines"]["tiered (this line)"] = {
             "steps_per_s": steps_per_s, "live_rows_per_seq_at_end":
                 (after["tier_count"][0] + after["tier_count"][1] + after["tier_count"][2]) / w.batch,
@@ -385,6 +387,7 @@ def main():
             km = ba["attn_kernel_ms"] - bb["attn_kernel_ms"]
             result["baselines"][name] = {
                 "steps_per_s": args.baseline_steps / bsecs, "live_rows_per_seq_at_end": live,
+                "t0_rows_at_end": ba["tier_count"][0],
                 "hbm_ratio": wb.hbm_ratio, "evict_ratio": wb.evict_ratio, "no_t1": wb.no_t1,
                 "kernel_gbs": kb / (km / 1e3) / 1e9 if km > 0 else None,
                 "host_bytes": ba["host_bytes"]}
