@@ -376,6 +376,7 @@ def main():
         result["baselines"]["tiered (this line)"] = {
             "steps_per_s": steps_per_s, "live_rows_per_seq_at_end":
                 (after["tier_count"][0] + after["tier_count"][1] + after["tier_count"][2]) / w.batch,
+            "t0_rows_at_end": after["tier_count"][0],
             "hbm_ratio": w.hbm_ratio, "evict_ratio": w.evict_ratio, "no_t1": False,
             "kernel_gbs": achieved, "host_bytes": after["host_bytes"]}
         for name, kw in policies:
