@@ -107,3 +107,25 @@ def dequantize_row_fp8(codes: np.ndarray, scale, bf16: bool) -> np.ndarray:
 def roundtrip_fp8(row: np.ndarray, bf16: bool) -> np.ndarray:
     codes, scale = quantize_row_fp8(row)
     return dequantize_row_fp8(codes, scale, bf16).reshape(np.shape(row))
+
+
+# ---- per-head scales: the same formats with one fp32 scale per kv head of
+# the row (Hkv scales instead of one), each from that head's own amax, so a
+# head of small values keeps its precision next to a head of large ones.
+def quantize_row_heads(row: np.ndarray, fp8: bool):
+    """row: float32 [kv_heads][head_dim] -> (codes [kv_heads][head_dim], scales [kv_heads])."""
+    x = np.asarray(row, np.float32)
+    quant = quantize_row_fp8 if fp8 else quantize_row
+    pairs = [quant(x[h]) for h in range(x.shape[0])]
+    codes = np.stack([p[0] for p in pairs])
+    return codes, np.array([p[1] for p in pairs], np.float32)
+
+
+def dequantize_row_heads(codes: np.ndarray, scales: np.ndarray, fp8: bool, bf16: bool) -> np.ndarray:
+    deq = dequantize_row_fp8 if fp8 else dequantize_row
+    return np.stack([deq(codes[h], scales[h], bf16).reshape(-1) for h in range(codes.shape[0])])
+
+
+def roundtrip_heads(row: np.ndarray, fp8: bool, bf16: bool) -> np.ndarray:
+    codes, scales = quantize_row_heads(row, fp8)
+    return dequantize_row_heads(codes, scales, fp8, bf16).reshape(np.shape(row))

@@ -95,13 +95,14 @@ class OracleTKV:
 
     def __init__(self, layers, q_heads, kv_heads, head_dim, batch, max_tokens, delta,
                  hbm_ratio, evict_ratio, t2_ratio, prompt, sinks, recent, bf16, no_t1=False, t2_fp8=False,
-                 shared_hbm=False):
+                 shared_hbm=False, t2_head_scales=False):
         self.L, self.Hq, self.Hkv, self.d, self.B = layers, q_heads, kv_heads, head_dim, batch
         self.nmax, self.delta = max_tokens, delta
         self.hbm, self.evict, self.t2 = hbm_ratio, evict_ratio, t2_ratio
         self.no_t1 = no_t1
         self.t2_fp8 = t2_fp8
         self.shared_hbm = shared_hbm
+        self.t2_head_scales = t2_head_scales
         self.prompt, self.sinks, self.recent = prompt, sinks, recent
         self.bf16 = bf16
         self.K = np.zeros((layers, batch, max_tokens, kv_heads, head_dim), np.float32)
@@ -115,7 +116,8 @@ class OracleTKV:
     def for_workload(cls, w, max_tokens=None):
         return cls(w.layers, w.q_heads, w.kv_heads, w.head_dim, w.batch,
                    max_tokens or w.n_final, w.delta, w.hbm_ratio, w.evict_ratio, w.t2_ratio,
-                   w.prompt, w.sinks, w.recent, w.dtype == "bf16", w.no_t1, w.t2_fp8, w.shared_hbm)
+                   w.prompt, w.sinks, w.recent, w.dtype == "bf16", w.no_t1, w.t2_fp8, w.shared_hbm,
+                   w.t2_head_scales)
 
     # -- cache contents ------------------------------------------------------
     def prefill(self, K, V):
@@ -194,7 +196,11 @@ class OracleTKV:
             for i in entering:
                 for l in range(self.L):
                     for X in (self.K, self.V):
-                        X[l, b, i] = (codec.roundtrip_fp8 if self.t2_fp8 else codec.roundtrip)(X[l, b, i], self.bf16)
+                        if self.t2_head_scales:
+                            X[l, b, i] = codec.roundtrip_heads(X[l, b, i], self.t2_fp8, self.bf16)
+                        else:
+                            X[l, b, i] = (codec.roundtrip_fp8 if self.t2_fp8 else codec.roundtrip)(X[l, b, i],
+                                                                                                   self.bf16)
             self.tier[b, :n] = new
             new_all[b] = new
         return new_all, deltas

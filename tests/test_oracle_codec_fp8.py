@@ -57,3 +57,19 @@ def test_fp8_beats_int8_on_relative_error_of_small_values():
     small = slice(1, None)
     assert np.max(np.abs(f8[small] - row[small]) / row[small]) < 0.07
     assert np.max(np.abs(i8[small] - row[small]) / row[small]) > 0.5
+
+
+def test_head_scales_are_the_row_codec_per_head():
+    rng = np.random.default_rng(3)
+    row = rng.standard_normal((4, 64)).astype(np.float32)
+    row[2] *= 0.01                              # a head of small values
+    for fp8 in (False, True):
+        codes, scales = codec.quantize_row_heads(row, fp8)
+        quant = codec.quantize_row_fp8 if fp8 else codec.quantize_row
+        for h in range(4):
+            c, s = quant(row[h])
+            assert np.array_equal(codes[h], c) and scales[h] == s
+        # the small head keeps its precision, which one row scale would not give it
+        per_head = codec.roundtrip_heads(row, fp8, bf16=False)
+        per_row = (codec.roundtrip_fp8 if fp8 else codec.roundtrip)(row, bf16=False)
+        assert np.max(np.abs(per_head[2] - row[2])) < np.max(np.abs(per_row[2] - row[2]))

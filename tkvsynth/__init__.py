@@ -109,6 +109,7 @@ class Workload:
     no_t1: bool = False   # eviction-only baseline: rows that would go to T1 are evicted
     t2_fp8: bool = False  # T2 rows held as FP8 E4M3 codes instead of int8
     shared_hbm: bool = False  # one T0 budget for the whole batch, ranked jointly
+    t2_head_scales: bool = False  # one T2 scale per kv head instead of one per row
     heavy_frac: float = 0.05
     k_amp: float = 3.0
     q_amp: float = 2.0
