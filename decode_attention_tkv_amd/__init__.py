@@ -26,6 +26,7 @@ TKV_FLAG_TIME_KERNELS = 1
 TKV_FLAG_NO_T1 = 2
 TKV_FLAG_T2_FP8 = 4
 TKV_FLAG_SHARED_HBM = 8
+TKV_FLAG_T2_HEAD_SCALES = 16
 
 _NAMES = {TKV_EINVAL: "EINVAL", TKV_ECAPACITY: "ECAPACITY", TKV_ENOMEM: "ENOMEM",
           TKV_ESTATE: "ESTATE", TKV_EHIP: "EHIP"}
@@ -211,10 +212,12 @@ def tkv_read_kv(h, layer, seq, pos, kv_heads, head_dim, np_dtype, stream=None):
     return k, v
 
 
-def tkv_read_t2(h, layer, seq, pos, kv_heads, head_dim):
+def tkv_read_t2(h, layer, seq, pos, kv_heads, head_dim, n_scales=1):
+    """n_scales: scales per row (kv_heads with per-head scales, else 1); returns
+    codes [kv_heads][head_dim] for K and V and the scales [2 * n_scales]."""
     kc = np.empty((kv_heads, head_dim), np.int8)
     vc = np.empty((kv_heads, head_dim), np.int8)
-    sc = np.empty(2, np.float32)
+    sc = np.empty(2 * n_scales, np.float32)
     _check(lib().tkv_read_t2(h, layer, seq, pos, kc.ctypes.data, vc.ctypes.data, sc.ctypes.data), h)
     return kc, vc, sc
 
@@ -226,7 +229,8 @@ class TieredKV:
 
     def __init__(self, layers, q_heads, kv_heads, head_dim, batch, max_tokens, dtype="bf16", delta=64,
                  hbm_ratio=0.5, evict_ratio=0.03, prompt=0, sinks=4, recent=128, t2_ratio=0.0,
-                 staging_layers=0, chunk=0, time_kernels=False, no_t1=False, t2_fp8=False, shared_hbm=False):
+                 staging_layers=0, chunk=0, time_kernels=False, no_t1=False, t2_fp8=False, shared_hbm=False,
+                 t2_head_scales=False):
         self.L, self.Hq, self.Hkv, self.D, self.B, self.nmax = layers, q_heads, kv_heads, head_dim, batch, max_tokens
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -234,7 +238,9 @@ class TieredKV:
                             TKV_BF16 if dtype == "bf16" else TKV_F32, delta, hbm_ratio, evict_ratio,
                             prompt, sinks, recent, t2_ratio, staging_layers, chunk,
                             (TKV_FLAG_TIME_KERNELS if time_kernels else 0) | (TKV_FLAG_NO_T1 if no_t1 else 0)
-                            | (TKV_FLAG_T2_FP8 if t2_fp8 else 0) | (TKV_FLAG_SHARED_HBM if shared_hbm else 0))
+                            | (TKV_FLAG_T2_FP8 if t2_fp8 else 0) | (TKV_FLAG_SHARED_HBM if shared_hbm else 0)
+                            | (TKV_FLAG_T2_HEAD_SCALES if t2_head_scales else 0))
+        self.n_scales = kv_heads if t2_head_scales else 1
 
     @classmethod
     def for_workload(cls, w, **kw):
@@ -242,7 +248,7 @@ class TieredKV:
                     batch=w.batch, max_tokens=w.n_final, dtype=w.dtype, delta=w.delta,
                     hbm_ratio=w.hbm_ratio, evict_ratio=w.evict_ratio, prompt=w.prompt, sinks=w.sinks,
                     recent=w.recent, t2_ratio=w.t2_ratio, no_t1=w.no_t1, t2_fp8=w.t2_fp8,
-                    shared_hbm=w.shared_hbm)
+                    shared_hbm=w.shared_hbm, t2_head_scales=w.t2_head_scales)
         args.update(kw)
         return cls(**args)
 
@@ -302,4 +308,4 @@ class TieredKV:
                            np.uint16 if self.dtype == "bf16" else np.float32, stream)
 
     def read_t2(self, layer, seq, pos):
-        return tkv_read_t2(self.h, layer, seq, pos, self.Hkv, self.D)
+        return tkv_read_t2(self.h, layer, seq, pos, self.Hkv, self.D, self.n_scales)

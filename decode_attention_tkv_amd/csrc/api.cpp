@@ -158,6 +158,7 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   t->cap1 = (o.flags & TKV_FLAG_NO_T1) ? 1 : (int)std::max<int64_t>(1, std::min<int64_t>(nmax, nmax - h_at_max + 1));
   t->cap2 = o.t2_ratio > 0 ? (int)std::min<int64_t>(nmax, floor_ratio(o.t2_ratio, nmax) + 1) : 0;
   t->capS = resident ? t->cap1 + t->cap2 : t->cap1;
+  t->sh = (o.flags & TKV_FLAG_T2_HEAD_SCALES) ? s.kv_heads : 1;
   t->max_chunks = (int)((nmax + t->chunk - 1) / t->chunk);
   t->lstride = (int)((nmax + kLogitAlign - 1) / kLogitAlign * kLogitAlign);
 
@@ -190,14 +191,14 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
     const size_t codes = L * B * t->Hkv * (size_t)t->cap2 * t->D;
     if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->arena2_k, codes);
     if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->arena2_v, codes);
-    if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->ascale_k, L * B * t->cap2 * 4);
-    if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->ascale_v, L * B * t->cap2 * 4);
+    if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->ascale_k, L * B * t->cap2 * t->sh * 4);
+    if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->ascale_v, L * B * t->cap2 * t->sh * 4);
     if (!resident) {
       const size_t qc = (size_t)t->S * B * t->Hkv * t->cap2 * t->D;
       dev((void**)&t->qstage_k, qc);
       dev((void**)&t->qstage_v, qc);
-      dev((void**)&t->qsscale_k, (size_t)t->S * B * t->cap2 * 4);
-      dev((void**)&t->qsscale_v, (size_t)t->S * B * t->cap2 * 4);
+      dev((void**)&t->qsscale_k, (size_t)t->S * B * t->cap2 * t->sh * 4);
+      dev((void**)&t->qsscale_v, (size_t)t->S * B * t->cap2 * t->sh * 4);
     }
   }
   if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_promote, B * nmax * sizeof(tkv_delta));
@@ -245,9 +246,9 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   std::memset(t->h_counts, 0, B * 2 * 4);
   t->st.hbm_bytes = (int64_t)(2 * (size_t)L * t->cap0 * (t->shared_hbm ? 1 : B) + 2 * (size_t)t->S * B * t->capS) *
                         t->row_bytes +
-                    (resident ? 0 : (int64_t)(2 * (size_t)t->S * B * t->cap2) * (t->Hkv * t->D + 4));
+                    (resident ? 0 : (int64_t)(2 * (size_t)t->S * B * t->cap2) * (t->Hkv * t->D + 4 * t->sh));
   t->st.host_bytes = (int64_t)(2 * L * B * t->cap1) * t->row_bytes +
-                     (int64_t)(2 * L * B * t->cap2) * (t->Hkv * t->D + 4);
+                     (int64_t)(2 * L * B * t->cap2) * (t->Hkv * t->D + 4 * t->sh);
   t->st.full_cache_bytes = (int64_t)(2 * L * B * nmax) * t->row_bytes;
   *out = t;
   return TKV_OK;
@@ -567,16 +568,17 @@ static int issue_prefetch(tkv* t, int upto) {
       // attention pass reads directly
       const size_t cw = n2max * t->D;
       const size_t c_layer = (size_t)t->B * t->Hkv * t->cap2 * t->D;
-      const size_t s_layer = (size_t)t->B * t->cap2;
+      const size_t s_layer = (size_t)t->B * t->cap2 * t->sh;
       for (int which = 0; which < 2; ++which) {
         int8_t* qd = (which ? t->qstage_v : t->qstage_k) + (size_t)slot * c_layer;
         float* sd = (which ? t->qsscale_v : t->qsscale_k) + (size_t)slot * s_layer;
         HIP_TRY(t, hipMemcpy2DAsync(qd, (size_t)t->cap2 * t->D, (which ? t->arena2_v : t->arena2_k) + (size_t)x * c_layer,
                                     (size_t)t->cap2 * t->D, cw, (size_t)t->B * t->Hkv, hipMemcpyHostToDevice, t->side));
-        HIP_TRY(t, hipMemcpy2DAsync(sd, (size_t)t->cap2 * 4, (which ? t->ascale_v : t->ascale_k) + (size_t)x * s_layer,
-                                    (size_t)t->cap2 * 4, n2max * 4, (size_t)t->B, hipMemcpyHostToDevice, t->side));
+        HIP_TRY(t, hipMemcpy2DAsync(sd, (size_t)t->cap2 * t->sh * 4,
+                                    (which ? t->ascale_v : t->ascale_k) + (size_t)x * s_layer, (size_t)t->cap2 * t->sh * 4,
+                                    n2max * t->sh * 4, (size_t)t->B, hipMemcpyHostToDevice, t->side));
       }
-      t->st.h2d_bytes += 2 * (int64_t)(cw * t->B * t->Hkv + n2max * 4 * t->B);
+      t->st.h2d_bytes += 2 * (int64_t)(cw * t->B * t->Hkv + n2max * t->sh * 4 * t->B);
     }
     HIP_TRY(t, hipEventRecord(t->ev_h2d[slot], t->side));
   }
@@ -762,7 +764,9 @@ extern "C" int tkv_read_t2(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, in
       std::memcpy((which ? v_codes : k_codes) + (size_t)h * t->D,
                   (which ? t->arena2_v : t->arena2_k) + ((((size_t)layer * t->B + seq) * t->Hkv + h) * t->cap2 + idx) * t->D,
                   t->D);
-    scales[which] = (which ? t->ascale_v : t->ascale_k)[((size_t)layer * t->B + seq) * t->cap2 + idx];
+    for (int k = 0; k < t->sh; ++k)
+      scales[which * t->sh + k] =
+          (which ? t->ascale_v : t->ascale_k)[(((size_t)layer * t->B + seq) * t->cap2 + idx) * t->sh + k];
   }
   return TKV_OK;
 }

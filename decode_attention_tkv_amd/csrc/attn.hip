@@ -268,8 +268,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
   if constexpr (QT) {
     qK = a.rows.q_k + q_codes_at(a.rows, l, b, kvh, 0, D);
     qV = a.rows.q_v + q_codes_at(a.rows, l, b, kvh, 0, D);
-    qsK = a.rows.qs_k + q_scale_at(a.rows, l, b, 0);
-    qsV = a.rows.qs_v + q_scale_at(a.rows, l, b, 0);
+    qsK = a.rows.qs_k + q_scale_at(a.rows, l, b, 0) + (a.rows.q_sh > 1 ? kvh : 0);  // row qi: [qi * q_sh]
+    qsV = a.rows.qs_v + q_scale_at(a.rows, l, b, 0) + (a.rows.q_sh > 1 ? kvh : 0);
   }
   const uint32_t* locs = a.live_loc + (int64_t)b * a.nmax + j0;
   for (int r = tid; r < CHUNK; r += 256) codes_s[r] = r < nrows ? locs[r] : 0u;
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
         const uint32_t code = ok ? codes_s[r] : 0u;
         if (QT && ok && code >= qbase) {
           const uint32_t qi = code - qbase;
-          const float sc = qsK[qi];
+          const float sc = qsK[(int64_t)qi * a.rows.q_sh];
           const int8_t* qp = qK + (int64_t)qi * D + 8 * kq;
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) kd[tt][kc] = deq_piece<T>(qp + 32 * kc, sc, a.rows.q_fp8);
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
           const uint32_t code = codes_s[r];
           if (QT && code >= qbase) {
             const uint32_t qi = code - qbase;
-            kd[u] = deq_piece<T>(qK + (int64_t)qi * D + part * EPL, qsK[qi], a.rows.q_fp8);
+            kd[u] = deq_piece<T>(qK + (int64_t)qi * D + part * EPL, qsK[(int64_t)qi * a.rows.q_sh], a.rows.q_fp8);
           } else {
             const T* p = code < cap0 ? poolK + (int64_t)code * rs : stageK + (int64_t)(code - cap0) * rs;
             kd[u] = load16nt(p);
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
         const uint32_t code = ok ? codes_s[r] : 0u;
         if (QT && ok && code >= qbase) {
           const uint32_t qi = code - qbase;
-          vr[i] = deq_piece<T>(qV + (int64_t)qi * D + 8 * hl, qsV[qi], a.rows.q_fp8);
+          vr[i] = deq_piece<T>(qV + (int64_t)qi * D + 8 * hl, qsV[(int64_t)qi * a.rows.q_sh], a.rows.q_fp8);
         } else {
           const T* p = code < cap0 ? pV + (int64_t)code * rs : sV + (int64_t)(code - cap0) * rs;
           vr[i] = ok ? load16nt(p) : make_uint4(0, 0, 0, 0);
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
           const uint32_t code = codes_s[r];
           if (QT && code >= qbase) {
             const uint32_t qi = code - qbase;
-            vd[u] = deq_piece<T>(qV + (int64_t)qi * D + part * EPL, qsV[qi], a.rows.q_fp8);
+            vd[u] = deq_piece<T>(qV + (int64_t)qi * D + part * EPL, qsV[(int64_t)qi * a.rows.q_sh], a.rows.q_fp8);
           } else {
             const T* p = code < cap0 ? poolV + (int64_t)code * rs : stageV + (int64_t)(code - cap0) * rs;
             vd[u] = load16nt(p);

@@ -50,6 +50,7 @@ __device__ __forceinline__ int64_t stage_elem(const RowSpace& rs, int l, int b, 
 // (optionally) write their dequantised values into the staging area.
 __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const QuantOp* ops) {
   __shared__ float red[4];
+  __shared__ uint32_t hmax[kMaxQHeads];  // per-head amax bits (non-negative floats order as their bits)
   const QuantOp op = ops[blockIdx.x];
   const int l = blockIdx.y, which = blockIdx.z;
   const int d = a.head_dim, n = a.kv_heads * d;
@@ -64,11 +65,27 @@ __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const Qua
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float qmax = a.fp8 ? 448.f : 127.f;
-  const float scale = amax > 0.f ? amax / qmax : 1.f;
+  const float row_scale = amax > 0.f ? amax / qmax : 1.f;
+  if (a.sh > 1) {  // one scale per kv head, from that head's own amax
+    for (int h = threadIdx.x; h < a.kv_heads; h += 256) hmax[h] = 0u;
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += 256) {
+      const int h = e / d, j = e % d;
+      const float x = load_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.src) * d + j, a.elem_bytes);
+      atomicMax(&hmax[h], __float_as_uint(fabsf(x)));
+    }
+    __syncthreads();
+  }
+  auto head_scale = [&](int h) {
+    if (a.sh == 1) return row_scale;
+    const float m = __uint_as_float(hmax[h]);
+    return m > 0.f ? m / qmax : 1.f;
+  };
   int8_t* codes = a.out.codes + (int64_t)which * (int64_t)gridDim.y * a.kv_heads * a.out.rows * d;
   for (int e = threadIdx.x; e < n; e += 256) {
     const int h = e / d, j = e % d;
     const float x = load_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.src) * d + j, a.elem_bytes);
+    const float scale = head_scale(h);
     float c;
     int8_t code;
     if (a.fp8) {
@@ -85,7 +102,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const Qua
       store_val(st, stage_elem(a.rows, l, op.b, h, op.stage, d) + j, c * scale, a.elem_bytes);
     }
   }
-  if (threadIdx.x == 0) a.out.scales[((int64_t)which * gridDim.y + l) * a.out.rows + op.dst] = scale;
+  for (int k = threadIdx.x; k < a.sh; k += 256)
+    a.out.scales[(((int64_t)which * gridDim.y + l) * a.out.rows + op.dst) * a.sh + k] = head_scale(k);
 }
 
 // grid (n_ops, layers, 2), block 256: QPack rows -> cache-type values in F.
@@ -94,10 +112,11 @@ __global__ __launch_bounds__(256) void k_dequant_rows(const DequantArgs a, const
   const int l = blockIdx.y, which = blockIdx.z;
   const int d = a.head_dim, n = a.kv_heads * d;
   const int8_t* codes = a.in.codes + (int64_t)which * (int64_t)gridDim.y * a.kv_heads * a.in.rows * d;
-  const float scale = a.in.scales[((int64_t)which * gridDim.y + l) * a.in.rows + op.src];
+  const float* scales = a.in.scales + (((int64_t)which * gridDim.y + l) * a.in.rows + op.src) * a.sh;
   void* f = which ? a.f.v : a.f.k;
   for (int e = threadIdx.x; e < n; e += 256) {
     const int h = e / d, j = e % d;
+    const float scale = scales[a.sh > 1 ? h : 0];
     const float c = code_val(codes[(((int64_t)l * a.kv_heads + h) * a.in.rows + op.src) * d + j], a.fp8);
     store_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.dst) * d + j, c * scale, a.elem_bytes);
   }

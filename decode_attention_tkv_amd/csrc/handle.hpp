@@ -21,6 +21,7 @@ struct tkv {
   int prompt = 0, sinks = 0, recent = 0;
   uint64_t flags = 0;
   int cap0 = 0, cap1 = 0, cap2 = 0, capS = 0, max_chunks = 0;  // capS: staging rows per slot
+  int sh = 1;  // T2 scales per row: Hkv with per-head scales, else 1
   int lstride = 0;  // logits row stride: nmax rounded up to whole lines
   int64_t row_elems = 0, row_bytes = 0;
 
@@ -81,7 +82,7 @@ struct tkv {
   // attention pass reads the codes directly
   int8_t* qstage_k = nullptr;  // [S][B][Hkv][cap2][D]
   int8_t* qstage_v = nullptr;
-  float* qsscale_k = nullptr;  // [S][B][cap2]
+  float* qsscale_k = nullptr;  // [S][B][cap2][sh]
   float* qsscale_v = nullptr;
 
   // ---- host-side placement state
@@ -145,13 +146,14 @@ struct tkv {
     r.q_hstride = (int64_t)cap2 * D;
     r.q_bstride = r.q_hstride * Hkv;
     r.q_lstride = r.q_bstride * B;
-    r.qs_bstride = cap2;
-    r.qs_lstride = (int64_t)cap2 * B;
+    r.qs_bstride = (int64_t)cap2 * sh;
+    r.qs_lstride = (int64_t)cap2 * sh * B;
     r.cap0 = cap0;
     r.cap1 = cap1;
     r.cap2 = cap2;
     r.stage_slots = S;
     r.q_fp8 = (flags & TKV_FLAG_T2_FP8) ? 1 : 0;
+    r.q_sh = sh;
     return r;
   }
 };

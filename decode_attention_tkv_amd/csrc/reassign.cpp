@@ -402,7 +402,7 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   }
   QPack qin{};
   if (NF2 > 0) {
-    const size_t codes_half = (size_t)L * H * NF2 * qrow, sc_half = (size_t)L * NF2 * 4;
+    const size_t codes_half = (size_t)L * H * NF2 * qrow, sc_half = (size_t)L * NF2 * t->sh * 4;
     const size_t bytes = 2 * codes_half + 2 * sc_half;
     int rc = grow_pinned(t, &t->h_qin, &t->h_qin_bytes, bytes);
     if (!rc) rc = grow_device(t, &t->qin, &t->qin_bytes, bytes);
@@ -418,8 +418,9 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
             std::memcpy(hc + ((((size_t)which * L + l) * H + h) * NF2 + i) * qrow,
                         (which ? t->arena2_v : t->arena2_k) + ((((size_t)l * B + b) * H + h) * t->cap2 + idx) * qrow,
                         qrow);
-          hs[((size_t)which * L + l) * NF2 + i] =
-              (which ? t->ascale_v : t->ascale_k)[((size_t)l * B + b) * t->cap2 + idx];
+          for (int k = 0; k < t->sh; ++k)
+            hs[(((size_t)which * L + l) * NF2 + i) * t->sh + k] =
+                (which ? t->ascale_v : t->ascale_k)[(((size_t)l * B + b) * t->cap2 + idx) * t->sh + k];
         }
     }
     HIP_TRY(t, hipMemcpyAsync(t->qin, t->h_qin, bytes, hipMemcpyHostToDevice, st));
@@ -472,17 +473,17 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   ca.pack_in_v = t->fin ? (char*)t->fin + (size_t)L * H * NF1 * hb : nullptr;
   ca.pack_in_rows = NF1;
   HIP_TRY(t, launch_copy_rows(ca, d_ops1, (int)ops1.size(), L, st));
-  DequantArgs dqa{qin, fp, H, D, t->esz, (t->flags & TKV_FLAG_T2_FP8) ? 1 : 0};
+  DequantArgs dqa{qin, fp, H, D, t->esz, (t->flags & TKV_FLAG_T2_FP8) ? 1 : 0, t->sh};
   HIP_TRY(t, launch_dequant_rows(dqa, d_dq1, (int)dq1.size(), L, st));
   HIP_TRY(t, launch_copy_rows(ca, d_ops2a, (int)ops2a.size(), L, st));
   HIP_TRY(t, launch_copy_rows(ca, d_ops2b, (int)ops2b.size(), L, st));
   QPack qout{};
   if (E2 > 0) {
-    const size_t codes_half = (size_t)L * H * E2 * qrow, sc_half = (size_t)L * E2 * 4;
+    const size_t codes_half = (size_t)L * H * E2 * qrow, sc_half = (size_t)L * E2 * t->sh * 4;
     int rc = grow_device(t, &t->qout, &t->qout_bytes, 2 * codes_half + 2 * sc_half);
     if (rc) return rc;
     qout = QPack{(int8_t*)t->qout, (float*)((char*)t->qout + 2 * codes_half), E2};
-    QuantArgs qa{t->rowspace(), fp, qout, H, D, t->esz, (t->flags & TKV_FLAG_T2_FP8) ? 1 : 0};
+    QuantArgs qa{t->rowspace(), fp, qout, H, D, t->esz, (t->flags & TKV_FLAG_T2_FP8) ? 1 : 0, t->sh};
     HIP_TRY(t, launch_quant_rows(qa, d_q2, (int)q2.size(), L, st));
   }
   HIP_TRY(t, launch_set_loc(d_upd, (int)upd.size(), t->loc, t->nmax, st));
@@ -508,7 +509,7 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
     t->st.d2h_bytes += 2 * (int64_t)half;
   }
   if (E2 > 0) {
-    const size_t qbytes = 2 * (size_t)L * H * E2 * qrow + 2 * (size_t)L * E2 * 4;
+    const size_t qbytes = 2 * (size_t)L * H * E2 * qrow + 2 * (size_t)L * E2 * t->sh * 4;
     int rc = grow_pinned(t, &t->h_qout, &t->h_qout_bytes, qbytes);
     if (rc) return rc;
     HIP_TRY(t, hipMemcpyAsync(t->h_qout, t->qout, qbytes, hipMemcpyDeviceToHost, t->wb));
@@ -528,15 +529,15 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
       int8_t *a2k, *a2v;
       float *s2k, *s2v;
       const char* pack1;  // [2][L][H][E1][D] cache type
-      const char* pack2;  // codes [2][L][H][E2][D], scales [2][L][E2]
+      const char* pack2;  // codes [2][L][H][E2][D], scales [2][L][E2][SH]
       hipEvent_t ev;
-      int L, B, H, D;
+      int L, B, H, D, SH;
       size_t cap1, cap2, hb;
       int64_t E1, E2;
     };
     auto job = std::make_shared<Job>(Job{std::move(plan), (char*)t->arena1_k, (char*)t->arena1_v, t->arena2_k,
                                          t->arena2_v, t->ascale_k, t->ascale_v, (const char*)t->h_pack_out,
-                                         (const char*)t->h_qout, t->ev_pack, L, B, H, D, (size_t)t->cap1,
+                                         (const char*)t->h_qout, t->ev_pack, L, B, H, D, t->sh, (size_t)t->cap1,
                                          (size_t)t->cap2, hb, E1, E2});
     t->arena_job = std::async(std::launch::async, [job]() -> int {
       const Job& j = *job;
@@ -547,7 +548,7 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
         return (which ? j.a2v : j.a2k) + ((((size_t)l * j.B + b) * j.H + h) * j.cap2 + idx) * j.D;
       };
       auto s2 = [&](int which, int l, int b, uint32_t idx) -> float* {
-        return (which ? j.s2v : j.s2k) + ((size_t)l * j.B + b) * j.cap2 + idx;
+        return (which ? j.s2v : j.s2k) + (((size_t)l * j.B + b) * j.cap2 + idx) * j.SH;
       };
       auto moves = [&](int l0, int l1) {
         for (int l = l0; l < l1; ++l)
@@ -557,7 +558,7 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
                 for (int h = 0; h < j.H; ++h) std::memcpy(r1(which, l, b, h, mv.second), r1(which, l, b, h, mv.first), j.hb);
               for (auto& mv : j.plan[b].mov2) {
                 for (int h = 0; h < j.H; ++h) std::memcpy(r2(which, l, b, h, mv.second), r2(which, l, b, h, mv.first), j.D);
-                *s2(which, l, b, mv.second) = *s2(which, l, b, mv.first);
+                std::memcpy(s2(which, l, b, mv.second), s2(which, l, b, mv.first), j.SH * 4);
               }
             }
       };
@@ -575,7 +576,9 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
               for (int h = 0; h < j.H && n2; ++h)
                 std::memcpy(r2(which, l, b, h, sp.m2),
                             j.pack2 + ((((size_t)which * j.L + l) * j.H + h) * j.E2 + sp.e2off) * j.D, n2 * j.D);
-              if (n2) std::memcpy(s2(which, l, b, sp.m2), sc + ((size_t)which * j.L + l) * j.E2 + sp.e2off, n2 * 4);
+              if (n2)
+                std::memcpy(s2(which, l, b, sp.m2), sc + (((size_t)which * j.L + l) * j.E2 + sp.e2off) * j.SH,
+                            n2 * j.SH * 4);
             }
       };
       const int nth = std::min(4, j.L);

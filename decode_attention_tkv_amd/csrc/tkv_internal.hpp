@@ -36,7 +36,7 @@ struct RowSpace {
   const void* stage_v;
   int8_t* q_k;  // stream staging: T2 codes [stage_slots][batch][kv_heads][cap2][head_dim]; else null
   int8_t* q_v;
-  float* qs_k;  // T2 scales [stage_slots][batch][cap2]
+  float* qs_k;  // T2 scales [stage_slots][batch][cap2][q_sh]
   float* qs_v;
   int64_t pool_lstride, pool_bstride, pool_hstride;     // elements per layer / sequence / kv head
   int64_t stage_lstride, stage_bstride, stage_hstride;  // elements per slot / sequence / kv head
@@ -45,6 +45,7 @@ struct RowSpace {
   int32_t cap0, cap1, cap2;
   int32_t stage_slots;
   int32_t q_fp8;  // T2 codes are FP8 E4M3 (else int8)
+  int32_t q_sh;   // T2 scales per row: kv_heads (one per head) or 1
 };
 
 // T2 area offsets: codes of row idx (kv head h) of layer l's slot, and its scale.
@@ -53,7 +54,7 @@ __host__ __device__ inline int64_t q_codes_at(const RowSpace& r, int l, int b, i
          (int64_t)idx * d;
 }
 __host__ __device__ inline int64_t q_scale_at(const RowSpace& r, int l, int b, uint32_t idx) {
-  return (int64_t)(l % r.stage_slots) * r.qs_lstride + (int64_t)b * r.qs_bstride + idx;
+  return (int64_t)(l % r.stage_slots) * r.qs_lstride + (int64_t)b * r.qs_bstride + (int64_t)idx * r.q_sh;
 }
 
 // Logits and per-layer score rows are padded to kLogitAlign floats, so every
@@ -172,9 +173,9 @@ struct CopyArgs {
 // Quantised rows: codes [2 (K,V)][layers][kv_heads][rows][head_dim] int8 and
 // one fp32 scale per (K|V, layer, row): scales [2][layers][rows].
 struct QPack {
-  int8_t* codes;
-  float* scales;
-  int64_t rows;  // row stride of this pack
+  int8_t* codes;   // [2][layers][kv_heads][rows][head_dim]
+  float* scales;   // [2][layers][rows][sh]
+  int64_t rows;    // row stride of this pack
 };
 
 // Fetch pack F: every moved row's value, [layers][kv_heads][rows][head_dim]
@@ -197,6 +198,7 @@ struct QuantArgs {
   QPack out;
   int32_t kv_heads, head_dim, elem_bytes;
   int32_t fp8;  // FP8 E4M3 codes (else int8)
+  int32_t sh;   // scales per row: kv_heads or 1
 };
 
 struct DequantOp {
@@ -210,6 +212,7 @@ struct DequantArgs {
   FPack f;
   int32_t kv_heads, head_dim, elem_bytes;
   int32_t fp8;
+  int32_t sh;
 };
 
 // Scored prefill: inputs k [layers][batch][n][kv_heads][d], q [layers][batch][n][q_heads][d]

@@ -112,6 +112,11 @@ typedef struct {
  * position).  The first placement is per sequence (no scores yet).  Not
  * combinable with TKV_FLAG_NO_T1 (TKV_EINVAL). */
 #define TKV_FLAG_SHARED_HBM 8ull
+/* T2 with one fp32 scale per kv head of a row (each from that head's own
+ * amax) instead of one per row: heads of small values keep their precision
+ * next to heads of large ones.  Combines with TKV_FLAG_T2_FP8.  tkv_read_t2
+ * then returns kv_heads scales for K followed by kv_heads for V. */
+#define TKV_FLAG_T2_HEAD_SCALES 16ull
 
 /* One changed row of a reassignment (Method §4). */
 typedef struct {
@@ -219,8 +224,9 @@ int tkv_read_deltas(tkv_t* t, tkv_delta* promote, tkv_delta* demote, int32_t* co
 int tkv_read_kv(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, void* k, void* v, tkv_stream_t stream);
 
 /* The 8-bit host copy of one T2 row: host k_codes, v_codes [kv_heads][head_dim]
- * int8 and scales[2] = {K scale, V scale} (fp32).  TKV_ESTATE if the row is
- * not in T2. */
+ * (int8, or E4M3 bytes with TKV_FLAG_T2_FP8) and the fp32 scales: {K, V}, or
+ * with TKV_FLAG_T2_HEAD_SCALES the kv_heads K scales then the kv_heads V
+ * scales.  TKV_ESTATE if the row is not in T2. */
 int tkv_read_t2(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, int8_t* k_codes, int8_t* v_codes,
                 float* scales);
 

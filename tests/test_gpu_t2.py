@@ -55,8 +55,16 @@ def _run_t2(w, inp, staging_layers=0, check_codec=True):
                     if new != 2:
                         continue
                     entered += 1
-                    quant = codec.quantize_row_fp8 if w.t2_fp8 else codec.quantize_row
-                    deq = codec.dequantize_row_fp8 if w.t2_fp8 else codec.dequantize_row
+                    if w.t2_head_scales:
+                        def quant(x):
+                            return codec.quantize_row_heads(x, w.t2_fp8)
+
+                        def deq(cd, sc_, bf):
+                            return codec.dequantize_row_heads(cd, sc_, w.t2_fp8, bf)
+                    else:
+                        quant = codec.quantize_row_fp8 if w.t2_fp8 else codec.quantize_row
+                        deq = codec.dequantize_row_fp8 if w.t2_fp8 else codec.dequantize_row
+                    ns = w.kv_heads if w.t2_head_scales else 1
                     for l in range(w.layers):
                         kc, vc, sc = c.read_t2(l, b, pos)
                         rk, sk = quant(before_k[l, b, pos])
@@ -64,7 +72,7 @@ def _run_t2(w, inp, staging_layers=0, check_codec=True):
                         # codes compared as bytes: int8 two's complement, or the E4M3 bit patterns
                         assert np.array_equal(kc.view(np.uint8).ravel(), np.asarray(rk).view(np.uint8).ravel())
                         assert np.array_equal(vc.view(np.uint8).ravel(), np.asarray(rv).view(np.uint8).ravel())
-                        assert sc[0] == sk and sc[1] == sv
+                        assert np.array_equal(sc[:ns], np.ravel(sk)) and np.array_equal(sc[ns:], np.ravel(sv))
                         if staging_layers == 0:
                             gk, gv = c.read_kv(l, b, pos)
                             gk, gv = w.values(gk), w.values(gv)
@@ -122,4 +130,18 @@ def test_t2_fp8_stream_equals_resident():
 
 def test_t2_fp8_fp32_cache():
     w = tkvsynth.CONFIGS["tiny"].replace(t2_ratio=0.15, steps=64, t2_fp8=True)
+    _run_t2(w, Inputs(w))
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
+def test_t2_head_scales_resident_and_stream(fp8):
+    w = _w32(layers=4, t2_fp8=fp8, t2_head_scales=True)
+    inp = Inputs(w)
+    a, _, _ = _run_t2(w, inp, staging_layers=0, check_codec=True)
+    b, _, _ = _run_t2(w, inp, staging_layers=2, check_codec=True)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_t2_head_scales_fp32_cache():
+    w = tkvsynth.CONFIGS["tiny"].replace(t2_ratio=0.15, steps=64, t2_head_scales=True)
     _run_t2(w, Inputs(w))
