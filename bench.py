@@ -75,9 +75,8 @@ def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kern
     qp = [q[t].data_ptr() for t in range(warmup + steps)]
 
     def step(t):
-        rc = lib.tkv_append(h, kp[t], vp[t], stream)
-        if rc == 0:
-            rc = lib.tkv_decode_attn(h, 0, w.layers, qp[t], optr, stream)
+        # append + attention of every layer (+ the pending Eq. 1 update) in one call
+        rc = lib.tkv_decode_step(h, kp[t], vp[t], qp[t], optr, stream)
         if rc == 0 and (t + 1) % w.delta == 0:
             rc = lib.tkv_reassign(h, stream)
         if rc != 0:

@@ -84,6 +84,7 @@ _SIGS = {
     "tkv_prefill_scored": [_vp, _vp, _vp, _vp, _i32, _vp],
     "tkv_append": [_vp, _vp, _vp, _vp],
     "tkv_decode_attn": [_vp, _i32, _i32, _vp, _vp, _vp],
+    "tkv_decode_step": [_vp, _vp, _vp, _vp, _vp, _vp],
     "tkv_reassign": [_vp, _vp],
     "tkv_stats": [_vp, ctypes.POINTER(tkv_stats_t)],
     "tkv_read_scores": [_vp, _vp, _vp],
@@ -132,6 +133,8 @@ def _dev_ptr(x: torch.Tensor, shape, dtype, name):
         raise TypeError("%s has dtype %s, expected %s" % (name, x.dtype, dtype))
     if not x.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+    if x.data_ptr() % 16:
+        raise ValueError("%s must start on a 16-byte boundary" % name)
     return x.data_ptr()
 
 
@@ -166,6 +169,10 @@ def tkv_append(h, k_ptr, v_ptr, stream=None):
 
 def tkv_decode_attn(h, layer_begin, layer_count, q_ptr, out_ptr, stream=None):
     _check(lib().tkv_decode_attn(h, layer_begin, layer_count, q_ptr, out_ptr, _stream(stream)), h)
+
+
+def tkv_decode_step(h, k_ptr, v_ptr, q_ptr, out_ptr, stream=None):
+    _check(lib().tkv_decode_step(h, k_ptr, v_ptr, q_ptr, out_ptr, _stream(stream)), h)
 
 
 def tkv_reassign(h, stream=None):
@@ -283,6 +290,13 @@ class TieredKV:
         tkv_decode_attn(self.h, layer_begin, lc,
                         _dev_ptr(q, (lc, self.B, self.Hq, self.D), self.tdtype, "q"),
                         _dev_ptr(out, (lc, self.B, self.Hq, self.D), torch.float32, "out"), stream)
+
+    def decode_step(self, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, out: torch.Tensor, stream=None):
+        """append(k, v) then decode_attn(q, out) over every layer, as one call."""
+        shape = (self.L, self.B, self.Hkv, self.D)
+        tkv_decode_step(self.h, _dev_ptr(k, shape, self.tdtype, "k"), _dev_ptr(v, shape, self.tdtype, "v"),
+                        _dev_ptr(q, (self.L, self.B, self.Hq, self.D), self.tdtype, "q"),
+                        _dev_ptr(out, (self.L, self.B, self.Hq, self.D), torch.float32, "out"), stream)
 
     def reassign(self, stream=None):
         tkv_reassign(self.h, stream)

@@ -266,6 +266,7 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
   if (t->state != TkvState::Empty || t->n != 0) return tkv_fail(t, TKV_ESTATE, "prefill needs an empty cache");
   if (!k || !v) return tkv_fail(t, TKV_EINVAL, "k/v is NULL");
+  if (misaligned(k) || misaligned(v)) return tkv_fail(t, TKV_EINVAL, "k/v not 16-byte aligned");
   if (n_tokens < 1) return tkv_fail(t, TKV_EINVAL, "n_tokens must be >= 1");
   if (n_tokens > t->nmax) return tkv_fail(t, TKV_ECAPACITY, "n_tokens %d > max_tokens %d", n_tokens, t->nmax);
   hipStream_t st = (hipStream_t)stream;
@@ -379,6 +380,7 @@ extern "C" int tkv_prefill_scored(tkv_t* t, const void* k, const void* v, const 
                                   tkv_stream_t stream) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
   if (!q) return tkv_fail(t, TKV_EINVAL, "q is NULL");
+  if (misaligned(q)) return tkv_fail(t, TKV_EINVAL, "q not 16-byte aligned");
   if (int rc = tkv_prefill(t, k, v, n_tokens, stream)) return rc;
   hipStream_t st = (hipStream_t)stream;
   const size_t per = (size_t)t->L * t->B * t->Hq * n_tokens * 4;
@@ -405,10 +407,12 @@ extern "C" int tkv_prefill_scored(tkv_t* t, const void* k, const void* v, const 
   return tkv_reassign(t, stream);
 }
 
-extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream) {
+// Checks of an append; TKV_OK when a step may start.
+static int append_check(tkv* t, const void* k, const void* v) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "previous step has layers left");
   if (!k || !v) return tkv_fail(t, TKV_EINVAL, "k/v is NULL");
+  if (misaligned(k) || misaligned(v)) return tkv_fail(t, TKV_EINVAL, "k/v not 16-byte aligned");
   if (t->n >= t->nmax) return tkv_fail(t, TKV_ECAPACITY, "max_tokens (%d) reached", t->nmax);
   if (t->shared_hbm) {
     if ((int)t->free0[0].size() < t->B) return tkv_fail(t, TKV_ECAPACITY, "shared T0 pool full: reassign first");
@@ -416,6 +420,33 @@ extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t s
     for (int b = 0; b < t->B; ++b)
       if (t->free0[b].empty()) return tkv_fail(t, TKV_ECAPACITY, "T0 pool full (sequence %d): reassign first", b);
   }
+  return TKV_OK;
+}
+
+// T0 slot of each sequence's new row (shared pool: the last B free slots).
+static void append_slots(tkv* t, int32_t* slot) {
+  for (int b = 0; b < t->B; ++b)
+    slot[b] = t->free_list(b)[t->free_list(b).size() - 1 - (t->shared_hbm ? b : 0)];
+}
+
+// Host side of an append whose launch has been enqueued.
+static void append_commit(tkv* t, const int32_t* slot) {
+  t->score_pending = false;
+  for (int b = 0; b < t->B; ++b) {
+    t->free_list(b).pop_back();  // shared: the B slots taken, from the back
+    const size_t off = (size_t)b * t->nmax + t->n;
+    t->h_tier[off] = TKV_T0;
+    t->h_loc[off] = (uint32_t)slot[b];
+    t->nlive[b] += 1;
+  }
+  t->n += 1;
+  t->layers_done = 0;
+  t->state = TkvState::InStep;
+}
+
+extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream) {
+  int rc = append_check(t, k, v);
+  if (rc) return rc;
   AppendArgs a{};
   a.rows = t->rowspace();
   a.k = k;
@@ -432,35 +463,25 @@ extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t s
   a.elem_bytes = t->esz;
   a.nmax = t->nmax;
   a.pos = t->n;
-  for (int b = 0; b < t->B; ++b) {
-    a.slot[b] = t->free_list(b)[t->free_list(b).size() - 1 - (t->shared_hbm ? b : 0)];
-    a.nlive[b] = t->nlive[b];
-  }
+  append_slots(t, a.slot);
+  for (int b = 0; b < t->B; ++b) a.nlive[b] = t->nlive[b];
   HIP_TRY(t, launch_append(a, t->score_pending ? &t->pending_score : nullptr, t->pending_tiles,
                            (hipStream_t)stream));
-  t->score_pending = false;
-  for (int b = 0; b < t->B; ++b) {
-    t->free_list(b).pop_back();  // shared: the B slots taken above, from the back
-    const size_t off = (size_t)b * t->nmax + t->n;
-    t->h_tier[off] = TKV_T0;
-    t->h_loc[off] = (uint32_t)a.slot[b];
-    t->nlive[b] += 1;
-  }
-  t->n += 1;
-  t->layers_done = 0;
-  t->state = TkvState::InStep;
+  append_commit(t, a.slot);
   return TKV_OK;
 }
 
-static int record_event(tkv* t, hipEvent_t* e, hipStream_t st) {
+// A timing event from the pool.  The launch binds it to its kernel's own start
+// or end; no host reads device memory through it, so it carries no
+// system-scope fence (which would write back the caches at every launch).
+static int take_event(tkv* t, hipEvent_t* e) {
   if (t->ev_free.empty()) {
     hipEvent_t x;
-    HIP_TRY(t, hipEventCreate(&x));
+    HIP_TRY(t, hipEventCreateWithFlags(&x, hipEventDisableSystemFence));
     t->ev_free.push_back(x);
   }
   *e = t->ev_free.back();
   t->ev_free.pop_back();
-  HIP_TRY(t, hipEventRecord(*e, st));
   return TKV_OK;
 }
 
@@ -479,7 +500,9 @@ static int drain_events(tkv* t) {
 }
 
 // Split-K attention + chunk merge for layers [lb, lb + lc) whose q/out start at q, out.
-static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int max_live, hipStream_t st) {
+// step: the fused append + Eq. 1 update of a whole-step launch, or nullptr.
+static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int max_live, hipStream_t st,
+                         const StepArgs* step = nullptr) {
   AttnArgs a{};
   a.rows = t->rowspace();
   a.live_loc = t->live_loc;
@@ -497,16 +520,17 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
   a.lstride = t->lstride;
   for (int b = 0; b < t->B; ++b) a.nlive[b] = t->nlive[b];
   const int chunks_now = (max_live + t->chunk - 1) / t->chunk;
-  const bool timed = (t->flags & TKV_FLAG_TIME_KERNELS) != 0;
+  const bool timed = (t->flags & TKV_FLAG_TIME_KERNELS) != 0 && chunks_now > 0;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (timed) {
-    int rc = record_event(t, &e0, st);
+    int rc = take_event(t, &e0);
+    if (!rc) rc = take_event(t, &e1);
     if (rc) return rc;
   }
-  if (chunks_now > 0) HIP_TRY(t, launch_attn(a, t->dtype, t->D, t->group, t->chunk, lc, chunks_now, st));
+  StepArgs none{};
+  if (chunks_now > 0)
+    HIP_TRY(t, launch_attn(a, step ? *step : none, t->dtype, t->D, t->group, t->chunk, lc, chunks_now, e0, e1, st));
   if (timed) {
-    int rc = record_event(t, &e1, st);
-    if (rc) return rc;
     t->ev_pending.emplace_back(e0, e1);
     int64_t rows = 0;
     for (int b = 0; b < t->B; ++b) rows += t->nlive[b];
@@ -585,11 +609,32 @@ static int issue_prefetch(tkv* t, int upto) {
   return TKV_OK;
 }
 
+// Close a step whose every layer is enqueued: its Eq. 1 update becomes pending.
+static void end_step(tkv* t, int max_live) {
+  ScoreArgs sa{};
+  sa.layer_score = t->layer_score;
+  sa.live_pos = t->live_pos;
+  sa.s = t->s;
+  sa.inv_lh = (float)(1.0 / ((double)t->L * t->Hq));
+  sa.layers = t->L;
+  sa.batch = t->B;
+  sa.nmax = t->nmax;
+  sa.lstride = t->lstride;
+  for (int b = 0; b < t->B; ++b) sa.nlive[b] = t->nlive[b];
+  // applied by the next append's launch (or by tkv_flush_score)
+  t->pending_score = sa;
+  t->pending_tiles = (max_live + 255) / 256;
+  t->score_pending = t->pending_tiles > 0;
+  t->step += 1;
+  t->state = TkvState::Ready;
+}
+
 extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
                                tkv_stream_t stream) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
   if (t->state != TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "no step in progress (append first)");
   if (!q || !out) return tkv_fail(t, TKV_EINVAL, "q/out is NULL");
+  if (misaligned(q) || misaligned(out)) return tkv_fail(t, TKV_EINVAL, "q/out not 16-byte aligned");
   if (layer_begin != t->layers_done)
     return tkv_fail(t, TKV_ESTATE, "layer groups must come in order: expected layer %d", t->layers_done);
   if (layer_count < 1 || layer_begin + layer_count > t->L) return tkv_fail(t, TKV_EINVAL, "bad layer range");
@@ -617,24 +662,39 @@ extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_coun
   }
 
   t->layers_done += layer_count;
-  if (t->layers_done == t->L) {
-    ScoreArgs sa{};
-    sa.layer_score = t->layer_score;
-    sa.live_pos = t->live_pos;
-    sa.s = t->s;
-    sa.inv_lh = (float)(1.0 / ((double)t->L * t->Hq));
-    sa.layers = t->L;
-    sa.batch = t->B;
-    sa.nmax = t->nmax;
-    sa.lstride = t->lstride;
-    for (int b = 0; b < t->B; ++b) sa.nlive[b] = t->nlive[b];
-    // applied by the next append's launch (or by tkv_flush_score)
-    t->pending_score = sa;
-    t->pending_tiles = (max_live + 255) / 256;
-    t->score_pending = t->pending_tiles > 0;
-    t->step += 1;
-    t->state = TkvState::Ready;
+  if (t->layers_done == t->L) end_step(t, max_live);
+  return TKV_OK;
+}
+
+extern "C" int tkv_decode_step(tkv_t* t, const void* k, const void* v, const void* q, float* out,
+                               tkv_stream_t stream) {
+  int rc = append_check(t, k, v);
+  if (rc) return rc;
+  if (!q || !out) return tkv_fail(t, TKV_EINVAL, "q/out is NULL");
+  if (misaligned(q) || misaligned(out)) return tkv_fail(t, TKV_EINVAL, "q/out not 16-byte aligned");
+  if (!t->resident) {
+    rc = tkv_append(t, k, v, stream);
+    return rc ? rc : tkv_decode_attn(t, 0, t->L, q, out, stream);
   }
+  StepArgs n{};
+  n.k = k;
+  n.v = v;
+  n.live_loc = t->live_loc;
+  n.live_pos = t->live_pos;
+  n.tier = t->tier;
+  n.loc = t->loc;
+  n.s = t->s;
+  n.pos = t->n;
+  n.fold = t->score_pending ? 1 : 0;
+  n.f = t->pending_score;
+  append_slots(t, n.slot);
+  append_commit(t, n.slot);
+  int max_live = 0;
+  for (int b = 0; b < t->B; ++b) max_live = std::max(max_live, t->nlive[b]);
+  rc = launch_layers(t, 0, t->L, q, out, max_live, (hipStream_t)stream, &n);
+  if (rc) return rc;
+  t->layers_done = t->L;
+  end_step(t, max_live);
   return TKV_OK;
 }
 

@@ -32,6 +32,8 @@
 //                 the next step's append launch, saving a launch per step.
 //                 No atomics anywhere, so every result is bitwise
 //                 reproducible.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "tkv_internal.hpp"
@@ -219,8 +221,15 @@ __global__ __launch_bounds__(256) void k_append(const AppendArgs a, const ScoreA
 
 // ---------------------------------------------------------------------------
 // Split-K attention, pass 1.  grid (chunks, kv_heads, layer_count*batch).
+// With n.k set (a whole-step launch over resident staging) the new token's
+// row, live index nlive - 1, is read from n.k / n.v through the location
+// code kNewRow; the block holding it stores it into its T0 slot after its
+// own reads, and the (chunk, kv head 0, layer 0) blocks apply n.f to the
+// live-row tiles starting in their chunk.  Nothing else in the launch reads
+// what these writes touch: the slot was free, and the fold only reads
+// positions and live indices below the new row's.
 template <typename T, int D, int G, int CHUNK, bool MK, bool QT>
-__global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
+__global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   constexpr int LPR = D * (int)sizeof(T) / 16;  // lanes per row
   constexpr int EPL = 16 / (int)sizeof(T);      // elements per lane
   constexpr int RPI = 64 / LPR;                 // rows per wave load
@@ -271,8 +280,13 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
     qsK = a.rows.qs_k + q_scale_at(a.rows, l, b, 0) + (a.rows.q_sh > 1 ? kvh : 0);  // row qi: [qi * q_sh]
     qsV = a.rows.qs_v + q_scale_at(a.rows, l, b, 0) + (a.rows.q_sh > 1 ? kvh : 0);
   }
+  // the appended row of a step launch: read from the caller's k / v
+  const int jn = n.k ? nl - 1 : -1;
+  const int64_t noff = (((int64_t)l * a.batch + b) * a.kv_heads + kvh) * D + part * EPL;
+  const T* newK = n.k ? (const T*)n.k + noff : poolK;
+  const T* newV = n.k ? (const T*)n.v + noff : poolV;
   const uint32_t* locs = a.live_loc + (int64_t)b * a.nmax + j0;
-  for (int r = tid; r < CHUNK; r += 256) codes_s[r] = r < nrows ? locs[r] : 0u;
+  for (int r = tid; r < CHUNK; r += 256) codes_s[r] = r < nrows ? (j0 + r == jn ? kNewRow : locs[r]) : 0u;
   __syncthreads();
 
   float mc[G];
@@ -297,6 +311,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
     for (int i = 0; i < 4; ++i) mx[i] = -INFINITY;
     const T* pK = poolK - part * EPL + 8 * kq;  // this lane's 8-element slice of a row
     const T* sK = stageK - part * EPL + 8 * kq;
+    const T* nK = newK - part * EPL + 8 * kq;
 #pragma unroll
     for (int t0 = 0; t0 < TILES; t0 += 2) {
       uint4 kd[2][KC];
@@ -312,7 +327,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) kd[tt][kc] = deq_piece<T>(qp + 32 * kc, sc, a.rows.q_fp8);
         } else {
-          const T* p = code < cap0 ? pK + (int64_t)code * rs : sK + (int64_t)(code - cap0) * rs;
+          const T* p = code < cap0 ? pK + (int64_t)code * rs
+                       : code == kNewRow ? nK : sK + (int64_t)(code - cap0) * rs;
           // 64-byte pieces per row per load: a streaming (non-temporal) hint would let
           // the row's lines leave the cache before the neighbouring piece is read.
 #pragma unroll
@@ -371,7 +387,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
             const uint32_t qi = code - qbase;
             kd[u] = deq_piece<T>(qK + (int64_t)qi * D + part * EPL, qsK[(int64_t)qi * a.rows.q_sh], a.rows.q_fp8);
           } else {
-            const T* p = code < cap0 ? poolK + (int64_t)code * rs : stageK + (int64_t)(code - cap0) * rs;
+            const T* p = code < cap0 ? poolK + (int64_t)code * rs
+                         : code == kNewRow ? newK : stageK + (int64_t)(code - cap0) * rs;
             kd[u] = load16nt(p);
           }
         }
@@ -449,6 +466,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
     const bool col_ok = 8 * hl < D;
     const T* pV = poolV - part * EPL + 8 * hl;
     const T* sV = stageV - part * EPL + 8 * hl;
+    const T* nV = newV - part * EPL + 8 * hl;
     f32x4 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -465,7 +483,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
           const uint32_t qi = code - qbase;
           vr[i] = deq_piece<T>(qV + (int64_t)qi * D + 8 * hl, qsV[(int64_t)qi * a.rows.q_sh], a.rows.q_fp8);
         } else {
-          const T* p = code < cap0 ? pV + (int64_t)code * rs : sV + (int64_t)(code - cap0) * rs;
+          const T* p = code < cap0 ? pV + (int64_t)code * rs
+                       : code == kNewRow ? nV : sV + (int64_t)(code - cap0) * rs;
           vr[i] = ok ? load16nt(p) : make_uint4(0, 0, 0, 0);
         }
       }
@@ -518,7 +537,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
             const uint32_t qi = code - qbase;
             vd[u] = deq_piece<T>(qV + (int64_t)qi * D + part * EPL, qsV[(int64_t)qi * a.rows.q_sh], a.rows.q_fp8);
           } else {
-            const T* p = code < cap0 ? poolV + (int64_t)code * rs : stageV + (int64_t)(code - cap0) * rs;
+            const T* p = code < cap0 ? poolV + (int64_t)code * rs
+                         : code == kNewRow ? newV : stageV + (int64_t)(code - cap0) * rs;
             vd[u] = load16nt(p);
           }
         }
@@ -566,6 +586,29 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a) {
     float* lg = a.logits + (hbase + g) * a.lstride + j0;
     for (int r = tid; r < nw; r += 256) __builtin_nontemporal_store(r < nrows ? zs[g][r] : 0.f, lg + r);
   }
+  if (jn >= j0 && jn < j0 + nrows) {
+    // the appended row's K and V of this kv head into T0 slot n.slot[b]
+    constexpr int PPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per head row
+    if (tid < 2 * PPR) {
+      const int which = tid / PPR, piece = tid % PPR;
+      const int64_t src = (((int64_t)l * a.batch + b) * a.kv_heads + kvh) * D + piece * EPL;
+      const int64_t dst = (int64_t)l * a.rows.pool_lstride + (int64_t)b * a.rows.pool_bstride +
+                          (int64_t)kvh * a.rows.pool_hstride + (int64_t)n.slot[b] * D + piece * EPL;
+      const uint4 x = load16((const T*)(which ? n.v : n.k) + src);
+      *reinterpret_cast<uint4*>((T*)(which ? a.rows.pool_v : a.rows.pool_k) + dst) = x;
+    }
+    if (kvh == 0 && l == 0 && tid == 0) {
+      const int64_t j = (int64_t)b * a.nmax + jn;
+      const int64_t p = (int64_t)b * a.nmax + n.pos;
+      n.live_loc[j] = (uint32_t)n.slot[b];
+      n.live_pos[j] = n.pos;
+      n.tier[p] = 0;
+      n.loc[p] = (uint32_t)n.slot[b];
+      n.s[p] = 0.f;
+    }
+  }
+  if (n.fold && kvh == 0 && l == 0)
+    for (int y = (j0 + 255) / 256; y * 256 < j0 + CHUNK; ++y) score_rows(n.f, y, b);
 }
 
 // ---------------------------------------------------------------------------
@@ -642,35 +685,51 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
 __global__ __launch_bounds__(256) void k_score(const ScoreArgs a) { score_rows(a, blockIdx.x, blockIdx.y); }
 
 // Grouped-query heads (G >= 4) of bf16 caches take the matrix-core logits.
+// Launched through hipExtLaunchKernel so that timing events (when given) take
+// the dispatch's own start and end instead of packets of their own.
+struct AttnLaunch {
+  dim3 grid;
+  hipEvent_t e0, e1;
+  hipStream_t s;
+};
+
 template <typename T, int D, int G, bool QT>
-hipError_t launch_attn_t(const AttnArgs& a, int chunk, dim3 grid, hipStream_t s) {
+hipError_t launch_attn_t(const AttnArgs& a, const StepArgs& n, int chunk, const AttnLaunch& L) {
   constexpr bool MK = std::is_same<T, bf16_t>::value && G >= 4;
+  const void* fn = nullptr;
   switch (chunk) {
-    case 128: k_attn_chunk<T, D, G, 128, MK, QT><<<grid, 256, 0, s>>>(a); break;
-    case 256: k_attn_chunk<T, D, G, 256, MK, QT><<<grid, 256, 0, s>>>(a); break;
-    case 512: k_attn_chunk<T, D, G, 512, MK, QT><<<grid, 256, 0, s>>>(a); break;
+    case 128: fn = (const void*)&k_attn_chunk<T, D, G, 128, MK, QT>; break;
+    case 256: fn = (const void*)&k_attn_chunk<T, D, G, 256, MK, QT>; break;
+    case 512: fn = (const void*)&k_attn_chunk<T, D, G, 512, MK, QT>; break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  AttnArgs ac = a;
+  StepArgs nc = n;
+  void* args[] = {&ac, &nc};
+  return hipExtLaunchKernel(fn, L.grid, dim3(256), args, 0, L.s, L.e0, L.e1, 0);
 }
 
 template <typename T, int D, bool QT>
-hipError_t launch_attn_g(const AttnArgs& a, int group, int chunk, dim3 grid, hipStream_t s) {
+hipError_t launch_attn_g(const AttnArgs& a, const StepArgs& n, int group, int chunk, const AttnLaunch& L) {
   switch (group) {
-    case 1: return launch_attn_t<T, D, 1, QT>(a, chunk, grid, s);
-    case 2: return launch_attn_t<T, D, 2, QT>(a, chunk, grid, s);
-    case 4: return launch_attn_t<T, D, 4, QT>(a, chunk, grid, s);
-    case 5: return launch_attn_t<T, D, 5, QT>(a, chunk, grid, s);
-    case 8: return launch_attn_t<T, D, 8, QT>(a, chunk, grid, s);
+    case 1: return launch_attn_t<T, D, 1, QT>(a, n, chunk, L);
+    case 2: return launch_attn_t<T, D, 2, QT>(a, n, chunk, L);
+    case 4: return launch_attn_t<T, D, 4, QT>(a, n, chunk, L);
+    case 5: return launch_attn_t<T, D, 5, QT>(a, n, chunk, L);
+    case 8: return launch_attn_t<T, D, 8, QT>(a, n, chunk, L);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Stream staging with an 8-bit tier takes the variant that reads T2 rows as codes.
+// A step launch (n.k set) never comes with 8-bit staging: kNewRow is above every T2 code.
 template <typename T, int D>
-hipError_t launch_attn_q(const AttnArgs& a, int group, int chunk, dim3 grid, hipStream_t s) {
-  if (a.rows.q_k != nullptr) return launch_attn_g<T, D, true>(a, group, chunk, grid, s);
-  return launch_attn_g<T, D, false>(a, group, chunk, grid, s);
+hipError_t launch_attn_q(const AttnArgs& a, const StepArgs& n, int group, int chunk, const AttnLaunch& L) {
+  if (a.rows.q_k != nullptr) {
+    if (n.k) return hipErrorInvalidValue;
+    return launch_attn_g<T, D, true>(a, n, group, chunk, L);
+  }
+  return launch_attn_g<T, D, false>(a, n, group, chunk, L);
 }
 
 }  // namespace
@@ -682,15 +741,15 @@ hipError_t launch_append(const AppendArgs& a, const ScoreArgs* fold, int fold_ti
   return hipGetLastError();
 }
 
-hipError_t launch_attn(const AttnArgs& a, int dtype, int head_dim, int group, int chunk,
-                       int layer_count, int chunks_now, hipStream_t s) {
-  const dim3 grid(chunks_now, a.kv_heads, layer_count * a.batch);
+hipError_t launch_attn(const AttnArgs& a, const StepArgs& n, int dtype, int head_dim, int group, int chunk,
+                       int layer_count, int chunks_now, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
+  const AttnLaunch L{dim3(chunks_now, a.kv_heads, layer_count * a.batch), e0, e1, s};
   if (dtype == TKV_BF16) {
-    if (head_dim == 128) return launch_attn_q<bf16_t, 128>(a, group, chunk, grid, s);
-    if (head_dim == 64) return launch_attn_q<bf16_t, 64>(a, group, chunk, grid, s);
+    if (head_dim == 128) return launch_attn_q<bf16_t, 128>(a, n, group, chunk, L);
+    if (head_dim == 64) return launch_attn_q<bf16_t, 64>(a, n, group, chunk, L);
   } else {
-    if (head_dim == 128) return launch_attn_q<float, 128>(a, group, chunk, grid, s);
-    if (head_dim == 64) return launch_attn_q<float, 64>(a, group, chunk, grid, s);
+    if (head_dim == 128) return launch_attn_q<float, 128>(a, n, group, chunk, L);
+    if (head_dim == 64) return launch_attn_q<float, 64>(a, n, group, chunk, L);
   }
   return hipErrorInvalidValue;
 }

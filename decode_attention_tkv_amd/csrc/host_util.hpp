@@ -22,6 +22,9 @@ int tkv_flush_score(tkv* t, hipStream_t stream);
     }                                                                                          \
   } while (0)
 
+// Device buffers handed over are read in 16-byte pieces.
+inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
 // floor(ratio * n) in fp64: the tier budgets of Method §1.
 inline int64_t floor_ratio(double r, int64_t n) { return (int64_t)std::floor(r * (double)n); }
 

@@ -107,6 +107,29 @@ struct AppendArgs {
   int32_t nlive[kMaxBatch];
 };
 
+// The append and the pending Eq. 1 update, carried out by the attention launch
+// of a whole step (resident staging only).  The new token's row is live index
+// nlive - 1 of every sequence; the attention blocks read it from k / v and
+// the block whose chunk holds it also writes it to T0 slot slot[b].  With
+// fold set, blocks (chunk, kv head 0, layer 0) apply `f` to the 256-row tiles
+// that start in their chunk.  k == nullptr: neither (a plain attention launch).
+struct StepArgs {
+  const void* k;  // [layers][batch][kv_heads][head_dim]
+  const void* v;
+  uint32_t* live_loc;
+  int32_t* live_pos;
+  uint8_t* tier;
+  uint32_t* loc;
+  float* s;
+  int32_t pos;
+  int32_t fold;
+  ScoreArgs f;
+  int32_t slot[kMaxBatch];
+};
+
+// Location code that stands for the row being appended in a step launch.
+constexpr uint32_t kNewRow = 0xFFFFFFFEu;
+
 // Place input rows [layers][batch][n_tokens][row] at their location codes
 // (codes [batch][n_tokens]; kNoLoc = skip).
 struct PlaceArgs {
@@ -237,8 +260,10 @@ hipError_t launch_prefill_scores(const PrefillScoreArgs& a, int dtype, int head_
 // fold != nullptr: the same launch also applies a pending Eq. 1 update
 // (fold_tiles tiles of 256 live rows per sequence); the two touch disjoint data.
 hipError_t launch_append(const AppendArgs& a, const ScoreArgs* fold, int fold_tiles, hipStream_t s);
-hipError_t launch_attn(const AttnArgs& a, int dtype, int head_dim, int group, int chunk,
-                       int layer_count, int chunks_now, hipStream_t s);
+// step: the fused append and Eq. 1 update of a whole-step launch, or k == nullptr.
+// e0, e1 (may be null): events that take the kernel's own start and end times.
+hipError_t launch_attn(const AttnArgs& a, const StepArgs& step, int dtype, int head_dim, int group, int chunk,
+                       int layer_count, int chunks_now, hipEvent_t e0, hipEvent_t e1, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, int head_dim, int layer_count, int tiles_now,
                            hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s);

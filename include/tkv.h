@@ -47,7 +47,8 @@ typedef void* tkv_stream_t; /* a hipStream_t */
 
 typedef enum {
   TKV_OK = 0,
-  TKV_EINVAL = -1,    /* bad argument: shape, ratio outside [0,1], delta <= 0, NULL pointer */
+  TKV_EINVAL = -1,    /* bad argument: shape, ratio outside [0,1], delta <= 0, NULL pointer,
+                         a device buffer (k, v, q, out) not 16-byte aligned */
   TKV_ECAPACITY = -2, /* more positions than max_tokens, or the T0 pool is full */
   TKV_ENOMEM = -3,    /* device or pinned-host allocation failed */
   TKV_ESTATE = -4,    /* call out of order (e.g. reassign between layer groups of a step) */
@@ -194,6 +195,16 @@ int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream);
  * on the stream given to that call. */
 int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
                     tkv_stream_t stream);
+
+/* One whole decode step: tkv_append(k, v) followed by tkv_decode_attn over
+ * every layer, with identical results (bit for bit) and the same errors and
+ * state rules (no step may be open).  k, v as for tkv_append; q, out as for
+ * tkv_decode_attn with layer_count = layers.  With resident staging the
+ * append and the pending Eq. 1 update run inside the attention launch (the
+ * new row is read straight from k, v), so the step takes two launches
+ * instead of three; with stream staging it is exactly the two calls.  k, v,
+ * q are read by work enqueued on `stream` by this call. */
+int tkv_decode_step(tkv_t* t, const void* k, const void* v, const void* q, float* out, tkv_stream_t stream);
 
 /* Re-place every sequence's rows by score (Method §1, §4): protected rows to
  * T0; of the other live rows, ranked by score descending then position
