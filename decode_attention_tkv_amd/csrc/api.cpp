@@ -182,9 +182,13 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   dev((void**)&t->part_o, L * B * Hq * t->max_chunks * t->D * 4);
   dev((void**)&t->layer_score, L * B * t->lstride * 4);
   dev((void**)&t->tier_alt, B * nmax);
-  dev((void**)&t->d_promote, B * nmax * sizeof(tkv_delta));
-  dev((void**)&t->d_demote, B * nmax * sizeof(tkv_delta));
-  dev((void**)&t->d_counts, B * 2 * 4);
+  const size_t counts_bytes = (B * 2 * 4 + 15) / 16 * 16;
+  t->delta_block_bytes = counts_bytes + 2 * B * nmax * sizeof(tkv_delta);
+  dev((void**)&t->d_counts, t->delta_block_bytes);
+  if (t->d_counts) {
+    t->d_promote = (tkv_delta*)((char*)t->d_counts + counts_bytes);
+    t->d_demote = t->d_promote + B * nmax;
+  }
   if (rc == TKV_OK) rc = host_alloc(t, &t->arena1_k, L * B * t->cap1 * t->row_bytes);
   if (rc == TKV_OK) rc = host_alloc(t, &t->arena1_v, L * B * t->cap1 * t->row_bytes);
   if (t->cap2 > 0) {
@@ -201,9 +205,11 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
       dev((void**)&t->qsscale_v, (size_t)t->S * B * t->cap2 * t->sh * 4);
     }
   }
-  if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_promote, B * nmax * sizeof(tkv_delta));
-  if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_demote, B * nmax * sizeof(tkv_delta));
-  if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_counts, B * 2 * 4);
+  if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_counts, t->delta_block_bytes);
+  if (rc == TKV_OK) {
+    t->h_promote = (tkv_delta*)((char*)t->h_counts + counts_bytes);
+    t->h_demote = t->h_promote + B * nmax;
+  }
   if (rc == TKV_OK) {
     hipError_t e = hipStreamCreateWithFlags(&t->side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&t->wb, hipStreamNonBlocking);

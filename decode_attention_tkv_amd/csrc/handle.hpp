@@ -1,16 +1,66 @@
 // The tkv handle: configuration, device buffers, host-side placement state.
 #pragma once
 
+#include <condition_variable>
 #include <cstdarg>
 #include <cstdio>
+#include <deque>
 #include <functional>
 #include <future>
+#include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "tkv_internal.hpp"
 
 enum class TkvState { Empty, Ready, InStep };
+
+// One host thread per handle that runs the reassignments' arena jobs in
+// submission order; started on first use, joined on destruction after the
+// queue has drained.
+class HostWorker {
+ public:
+  ~HostWorker() {
+    {
+      std::lock_guard<std::mutex> g(m_);
+      stop_ = true;
+    }
+    cv_.notify_one();
+    if (th_.joinable()) th_.join();
+  }
+  std::future<int> submit(std::function<int()> f) {
+    std::packaged_task<int()> task(std::move(f));
+    std::future<int> fut = task.get_future();
+    {
+      std::lock_guard<std::mutex> g(m_);
+      if (!th_.joinable()) th_ = std::thread([this] { run(); });
+      q_.push_back(std::move(task));
+    }
+    cv_.notify_one();
+    return fut;
+  }
+
+ private:
+  void run() {
+    for (;;) {
+      std::packaged_task<int()> task;
+      {
+        std::unique_lock<std::mutex> lk(m_);
+        cv_.wait(lk, [&] { return stop_ || !q_.empty(); });
+        if (q_.empty()) return;
+        task = std::move(q_.front());
+        q_.pop_front();
+      }
+      task();
+    }
+  }
+  std::thread th_;
+  std::mutex m_;
+  std::condition_variable cv_;
+  std::deque<std::packaged_task<int()>> q_;
+  bool stop_ = false;
+};
 
 struct tkv {
   // ---- configuration
@@ -40,9 +90,12 @@ struct tkv {
   float* part_o = nullptr;       // [L][B][Hq][max_chunks][D]
   float* layer_score = nullptr;  // [L][B][lstride]
   uint8_t* tier_alt = nullptr;   // [B][nmax] labels being computed by a reassignment
-  tkv_delta* d_promote = nullptr;  // [B][nmax]
-  tkv_delta* d_demote = nullptr;   // [B][nmax]
-  int32_t* d_counts = nullptr;     // [B][2]
+  // changed rows of a reassignment, one block: counts [B][2] (padded to 16 B),
+  // then promote [B][nmax], then demote [B][nmax]; mirrored in pinned host memory
+  int32_t* d_counts = nullptr;
+  tkv_delta* d_promote = nullptr;
+  tkv_delta* d_demote = nullptr;
+  size_t delta_block_bytes = 0;
   std::vector<void*> device_allocs;
 
   // growable device / pinned scratch of the reassignment
@@ -69,6 +122,7 @@ struct tkv {
   size_t qout_bytes = 0;
   hipEvent_t ev_pack = nullptr;              // entrant rows landed in h_pack_out
   std::future<int> arena_job;                // host arena maintenance of the last reassignment
+  HostWorker worker;                         // runs those jobs
 
   // ---- pinned host arenas (owned)
   void* arena1_k = nullptr;  // [L][B][Hkv][cap1][D]: T1 rows, dense per (layer, seq, head)
@@ -104,10 +158,10 @@ struct tkv {
   std::vector<std::vector<int32_t>> t1_owner; // [B]: T1 arena index -> position
   std::vector<std::vector<int32_t>> t2_owner; // [B]: T2 arena index -> position
 
-  // ---- last reassignment's changed rows (pinned host copies)
+  // ---- last reassignment's changed rows (pinned host copy of the device block)
+  int32_t* h_counts = nullptr;     // [B][2]
   tkv_delta* h_promote = nullptr;  // [B][nmax]
   tkv_delta* h_demote = nullptr;   // [B][nmax]
-  int32_t* h_counts = nullptr;     // [B][2]
 
   // ---- streams and events
   hipStream_t side = nullptr;           // host->device row traffic of the stream mode

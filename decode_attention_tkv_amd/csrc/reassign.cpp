@@ -33,6 +33,10 @@ using namespace tkvd;
 
 namespace {
 
+// Largest changed-row block read back whole (one copy, one wait); a few tens
+// of microseconds over PCIe, about one synchronisation round trip.
+constexpr size_t kOneCopyDeltaBytes = 1u << 20;
+
 enum SrcKind : uint8_t { kFromPool, kFromT1, kFromT2 };
 
 struct Move {
@@ -214,16 +218,23 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   da.nmax = t->nmax;
   da.n = n;
   HIP_TRY(t, launch_deltas(da, B, st));
-  HIP_TRY(t, hipMemcpyAsync(t->h_counts, t->d_counts, (size_t)B * 2 * 4, hipMemcpyDeviceToHost, st));
-  HIP_TRY(t, hipStreamSynchronize(st));
-  for (int b = 0; b < B; ++b) {
-    const size_t np = t->h_counts[2 * b], nd = t->h_counts[2 * b + 1];
-    if (np) HIP_TRY(t, hipMemcpyAsync(t->h_promote + b * nmax, t->d_promote + b * nmax, np * sizeof(tkv_delta),
-                                      hipMemcpyDeviceToHost, st));
-    if (nd) HIP_TRY(t, hipMemcpyAsync(t->h_demote + b * nmax, t->d_demote + b * nmax, nd * sizeof(tkv_delta),
-                                      hipMemcpyDeviceToHost, st));
+  // Counts and lists in one copy and one wait while the block is small;
+  // otherwise the counts first, then only the filled part of each list.
+  if (t->delta_block_bytes <= kOneCopyDeltaBytes) {
+    HIP_TRY(t, hipMemcpyAsync(t->h_counts, t->d_counts, t->delta_block_bytes, hipMemcpyDeviceToHost, st));
+    HIP_TRY(t, hipStreamSynchronize(st));
+  } else {
+    HIP_TRY(t, hipMemcpyAsync(t->h_counts, t->d_counts, (size_t)B * 2 * 4, hipMemcpyDeviceToHost, st));
+    HIP_TRY(t, hipStreamSynchronize(st));
+    for (int b = 0; b < B; ++b) {
+      const size_t np = t->h_counts[2 * b], nd = t->h_counts[2 * b + 1];
+      if (np) HIP_TRY(t, hipMemcpyAsync(t->h_promote + b * nmax, t->d_promote + b * nmax, np * sizeof(tkv_delta),
+                                        hipMemcpyDeviceToHost, st));
+      if (nd) HIP_TRY(t, hipMemcpyAsync(t->h_demote + b * nmax, t->d_demote + b * nmax, nd * sizeof(tkv_delta),
+                                        hipMemcpyDeviceToHost, st));
+    }
+    HIP_TRY(t, hipStreamSynchronize(st));
   }
-  HIP_TRY(t, hipStreamSynchronize(st));
   std::swap(t->tier, t->tier_alt);  // device labels are now the new ones
 
   // ---- placement plan
@@ -539,7 +550,7 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
                                          t->arena2_v, t->ascale_k, t->ascale_v, (const char*)t->h_pack_out,
                                          (const char*)t->h_qout, t->ev_pack, L, B, H, D, t->sh, (size_t)t->cap1,
                                          (size_t)t->cap2, hb, E1, E2});
-    t->arena_job = std::async(std::launch::async, [job]() -> int {
+    t->arena_job = t->worker.submit([job]() -> int {
       const Job& j = *job;
       auto r1 = [&](int which, int l, int b, int h, uint32_t idx) -> char* {
         return (which ? j.a1v : j.a1k) + ((((size_t)l * j.B + b) * j.H + h) * j.cap1 + idx) * j.hb;
