@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_tkv_amd", "csrc", "attn.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_chunk_7b_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_chunk_7b_traffic.txt")
 COPY_BYTES = 1 << 30  # plain device copy used to scale the HBM byte counters
 METRIC = "decode steps/sec (attn+scoring, all layers) at 7B shape; achieved HBM GB/s %peak"
 
@@ -59,9 +59,11 @@ def load_inputs(w, steps, torch):
     return k0, v0, kn, vn, q
 
 
-def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kernels=True):
+def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kernels=True, sync_reassign=False):
     """Prefill, `warmup` untimed steps, then `steps` timed steps.  Returns
-    (seconds, stats before, stats after)."""
+    (seconds, stats before, stats after).  sync_reassign: drain the stream
+    before and after every reassignment of the timed steps and put the
+    per-call wall times (ms) under after["reassign_synced_ms"]."""
     k0, v0, kn, vn, q = inputs
     c = tkv.TieredKV.for_workload(w, staging_layers=staging_layers, time_kernels=time_kernels)
     c.prefill(k0, v0)
@@ -74,11 +76,23 @@ def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kern
     vp = [vn[t].data_ptr() for t in range(warmup + steps)]
     qp = [q[t].data_ptr() for t in range(warmup + steps)]
 
+    synced = []
+
     def step(t):
         # append + attention of every layer (+ the pending Eq. 1 update) in one call
         rc = lib.tkv_decode_step(h, kp[t], vp[t], qp[t], optr, stream)
         if rc == 0 and (t + 1) % w.delta == 0:
-            rc = lib.tkv_reassign(h, stream)
+            if sync_reassign and t >= warmup:
+                # the caller's stream only: the write-back of rows entering T1 runs on the
+                # library's own stream, beside the next steps
+                cur = torch.cuda.current_stream()
+                cur.synchronize()
+                r0 = time.perf_counter()
+                rc = lib.tkv_reassign(h, stream)
+                cur.synchronize()
+                synced.append((time.perf_counter() - r0) * 1e3)
+            else:
+                rc = lib.tkv_reassign(h, stream)
         if rc != 0:
             raise tkv.TkvError(rc, lib.tkv_last_error(h).decode())
 
@@ -93,6 +107,7 @@ def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kern
     torch.cuda.synchronize()
     secs = time.perf_counter() - t0
     after = c.stats()
+    after["reassign_synced_ms"] = synced
     c.close()
     return secs, before, after
 
@@ -267,6 +282,8 @@ def main():
                     help="timed steps of each baseline policy on the same engine (default: --steps; 0: skip)")
     ap.add_argument("--prefill-reps", type=int, default=3,
                     help="timed runs of the plain and the scored prefill of the workload's cache (0: skip)")
+    ap.add_argument("--no-drained-leg", dest="drained_leg", action="store_false",
+                    help="skip the run that times each reassignment with the stream drained around it")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short run for counter collection: 8 + 24 steps, then one 1 GiB device copy")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -345,6 +362,13 @@ def main():
         "reassign_wall_ms_per_call": (after["reassign_ms"] - before["reassign_ms"])
         / max(1, after["reassigns"] - before["reassigns"]),
     }
+    # The cost of one reassignment on its own: the same run with the stream drained before and
+    # after each reassignment call, so the call's wall time is its host work plus its GPU work.
+    if args.drained_leg and result["config"]["reassignments_timed"] > 0:
+        print("[bench] reassignment cost, stream drained around each call", file=sys.stderr, flush=True)
+        _, _, rs = run_decode(w, inputs, args.warmup, args.steps, torch, tkv, time_kernels=False,
+                              sync_reassign=True)
+        result["reassign_ms_per_call_drained"] = float(np.median(rs["reassign_synced_ms"]))
 
     if args.stream_steps > 0:
         print("[bench] stream staging (S=2): %d timed steps" % args.stream_steps, file=sys.stderr, flush=True)
