@@ -128,3 +128,37 @@ def test_decode_step_state_and_arguments():
     c.decode_step(kd, vd, qd, out)                        # fine again
     assert c.stats()["step"] == 2
     c.close()
+
+
+def test_decode_step_capacity():
+    """The append's capacity errors, through the single call: the T0 pool runs
+    full without reassignments, then max_tokens is reached."""
+    import decode_attention_tkv_amd as tkv
+    w = tkvsynth.CONFIGS["tiny"].replace(prefill=100, steps=60, hbm_ratio=0.3, delta=4, prompt=8, recent=8)
+    inp = Inputs(w)
+    c = tkv.TieredKV.for_workload(w)
+    c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
+    out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    full_at = None
+    for t in range(w.steps):
+        k, v = inp.step_kv(t)
+        try:
+            c.decode_step(to_device(k, w.dtype), to_device(v, w.dtype), to_device(inp.q[t], w.dtype), out)
+        except tkv.TkvError as e:
+            assert e.code == tkv.TKV_ECAPACITY
+            full_at = t
+            break
+    assert full_at is not None
+    assert c.stats()["step"] == full_at                 # the failed call changed nothing
+    c.reassign()
+    for t in range(full_at, w.steps):
+        k, v = inp.step_kv(t)
+        c.decode_step(to_device(k, w.dtype), to_device(v, w.dtype), to_device(inp.q[t], w.dtype), out)
+        if (t + 1) % w.delta == 0:
+            c.reassign()
+    assert c.stats()["n_tokens"] == w.n_final
+    with pytest.raises(tkv.TkvError) as e:
+        c.decode_step(to_device(k, w.dtype), to_device(v, w.dtype), to_device(inp.q[0], w.dtype), out)
+    assert e.value.code == tkv.TKV_ECAPACITY            # max_tokens
+    assert np.isfinite(out.cpu().numpy()).all()
+    c.close()
