@@ -12,11 +12,12 @@
 //   k_prefill_sum       one thread per (position, sequence): the scores,
 //                       layers then heads in a fixed order, times 1/(L*H).
 // fp32 caches take these per-thread passes.  bf16 caches take the
-// matrix-core passes below: the row maxima, then the row sums against them
-// (two cheap MFMA passes instead of one online pass with two exponentials
-// per weight), then the column sums.  Every pass computes each z = q_t . k_j
-// the same way (the same fma chain, or the same MFMA tile), so every weight
-// is at most 1 and the weights of a query sum to 1 up to rounding.
+// matrix-core passes below: the row statistics in one online pass (one
+// exponential per weight: 2^-|z - m| serves both the rescale of a running
+// sum and a new term), then the column sums.  Every pass computes each
+// z = q_t . k_j the same way (the same fma chain, or the same MFMA tile), so
+// every weight is at most 1 and the weights of a query sum to 1 up to
+// rounding.
 #include <type_traits>
 
 #include "tkv_internal.hpp"
@@ -121,6 +122,11 @@ __global__ __launch_bounds__(256) void k_prefill_colsum(const PrefillScoreArgs a
 }
 
 // ---- matrix-core passes (bf16 caches) ----------------------------------------
+// 2^x by the hardware instruction alone: results below 2^-126 flush to zero
+// instead of taking the denormal-scaling sequence (five more VALU operations
+// per weight); such weights are below fp32's resolution of any sum they join.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Tiles of 16 query rows x 16 keys, z = q k^T by v_mfma_f32_16x16x32_bf16 over
 // head_dim/32 slices.  Lane (r, s) = (lane % 16, lane / 16) feeds query / key
 // row r with the 8 elements 8s.. of each 32-wide slice and receives z of
@@ -202,9 +208,10 @@ __device__ __forceinline__ bf16x8 tile_op(const char* lds, int row, int kc, int 
 
 // grid (ceil(n / 128), q_heads, layers * batch), block 256: the block owns
 // query rows [128x, 128x + 128), wave w the 32 rows 32w.. (two 16-row tiles,
-// operands in registers); key tiles of 32 rows come through LDS.
-// PH 0: the rows' maxima (no exponentials); PH 1: their sums of 2^(z - max).
-template <int D, int PH>
+// operands in registers); key tiles of 32 rows come through LDS.  Each lane
+// keeps a running (max, sum of 2^(z - max)) per row over its own keys (key
+// index = lane mod 16); the 16 partial pairs of a row merge at the end.
+template <int D>
 __global__ __launch_bounds__(256) void k_prefill_rowstats_mk(const PrefillScoreArgs a) {
   constexpr int KC = D / 32;
   __shared__ __attribute__((aligned(16))) char kt_s[2][32 * Tile<D>::RB];
@@ -229,8 +236,7 @@ __global__ __launch_bounds__(256) void k_prefill_rowstats_mk(const PrefillScoreA
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = tw + 16 * qt + 4 * sgrp + i;
-      m[qt][i] = (PH == 1 && t < a.n) ? a.row_max[so + t] : -INFINITY;
+      m[qt][i] = -INFINITY;
       l[qt][i] = 0.f;
     }
   const int jend = min(a.n, T0 + 128);  // keys the block's rows can see
@@ -243,28 +249,44 @@ __global__ __launch_bounds__(256) void k_prefill_rowstats_mk(const PrefillScoreA
     const bool more = it + 1 < iters;
     if (more) tile_fetch<D>(K, (int64_t)a.kv_heads * D, 32 * (it + 1), a.n, reg);
     const char* ks = kt_s[it & 1];
+    // Branch-free tile body; MASKED drops (by selection) keys after a row's
+    // query and rows past the prompt.
+    auto body = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      bf16x8 kb[KC];
+      for (int kt = 0; kt < 2; ++kt) {
+        bf16x8 kb[KC];
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) kb[kc] = tile_op<D>(ks, 16 * kt + r, kc, sgrp);
-      const int j = 32 * it + 16 * kt + r;
+        for (int kc = 0; kc < KC; ++kc) kb[kc] = tile_op<D>(ks, 16 * kt + r, kc, sgrp);
+        const int j = 32 * it + 16 * kt + r;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const f32x4 acc = tile_z<D>(qa[qt], kb);
+        for (int qt = 0; qt < 2; ++qt) {
+          const f32x4 acc = tile_z<D>(qa[qt], kb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = tw + 16 * qt + 4 * sgrp + i;
-          if (t < a.n && j <= t) {
+          for (int i = 0; i < 4; ++i) {
             const float z = acc[i] * a.qscale;
-            if constexpr (PH == 0)
-              m[qt][i] = fmaxf(m[qt][i], z);
-            else
-              l[qt][i] += exp2f(z - m[qt][i]);
+            const float e = exp2_hw(-fabsf(z - m[qt][i]));  // 0 for the first key (m = -inf)
+            const bool up = z > m[qt][i];
+            const float nl = up ? fmaf(l[qt][i], e, 1.f) : l[qt][i] + e;
+            const float nm = up ? z : m[qt][i];
+            if constexpr (MASKED) {
+              const int t = tw + 16 * qt + 4 * sgrp + i;
+              const bool ok = t < a.n && j <= t;
+              l[qt][i] = ok ? nl : l[qt][i];
+              m[qt][i] = ok ? nm : m[qt][i];
+            } else {
+              l[qt][i] = nl;
+              m[qt][i] = nm;
+            }
           }
         }
       }
-    }
+    };
+    // keys 32it..32it+31 all precede this wave's rows, which all exist: no masks
+    if (32 * it + 31 <= tw && tw + 31 < a.n)
+      body(std::false_type{});
+    else
+      body(std::true_type{});
     if (more) tile_store<D>(kt_s[(it + 1) & 1], reg);
     __syncthreads();
   }
@@ -273,12 +295,12 @@ __global__ __launch_bounds__(256) void k_prefill_rowstats_mk(const PrefillScoreA
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = tw + 16 * qt + 4 * sgrp + i;
-      if constexpr (PH == 0) {
-        const float M = row16_max(m[qt][i]);
-        if (r == 0 && t < a.n) a.row_max[so + t] = M;
-      } else {
-        const float L = row16_sum(l[qt][i]);
-        if (r == 0 && t < a.n) a.row_inv[so + t] = 1.f / L;
+      const float M = row16_max(m[qt][i]);
+      // a lane that saw no key of this row holds (-inf, 0)
+      const float L = row16_sum(m[qt][i] == -INFINITY ? 0.f : l[qt][i] * exp2_hw(m[qt][i] - M));
+      if (r == 0 && t < a.n) {
+        a.row_max[so + t] = M;
+        a.row_inv[so + t] = 1.f / L;
       }
     }
 }
@@ -332,28 +354,43 @@ __global__ __launch_bounds__(256) void k_prefill_colsum_mk(const PrefillScoreArg
       stat_fetch(t0 + 32);
     }
     const int p = it & 1;
+    // Branch-free tile body; MASKED drops (by selection) queries before a key
+    // and rows past the prompt.
+    auto body = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      bf16x8 qa[KC];
+      for (int qt = 0; qt < 2; ++qt) {
+        bf16x8 qa[KC];
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) qa[kc] = tile_op<D>(qt_s[p], 16 * qt + r, kc, sgrp);
-      float mt[4], iv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        mt[i] = ms[p][16 * qt + 4 * sgrp + i];
-        iv[i] = is[p][16 * qt + 4 * sgrp + i];
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const f32x4 acc = tile_z<D>(qa, kb[kt]);
-        const int j = jw + 16 * kt + r;
+        for (int kc = 0; kc < KC; ++kc) qa[kc] = tile_op<D>(qt_s[p], 16 * qt + r, kc, sgrp);
+        float mt[4], iv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 16 * qt + 4 * sgrp + i;
-          if (t < a.n && t >= j) c[kt] += exp2f(acc[i] * a.qscale - mt[i]) * iv[i];
+          mt[i] = ms[p][16 * qt + 4 * sgrp + i];
+          iv[i] = is[p][16 * qt + 4 * sgrp + i];
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const f32x4 acc = tile_z<D>(qa, kb[kt]);
+          const int j = jw + 16 * kt + r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float w = exp2_hw(acc[i] * a.qscale - mt[i]) * iv[i];
+            if constexpr (MASKED) {
+              const int t = t0 + 16 * qt + 4 * sgrp + i;
+              c[kt] += (t < a.n && t >= j) ? w : 0.f;
+            } else {
+              c[kt] += w;
+            }
+          }
         }
       }
-    }
+    };
+    // queries t0..t0+31 all follow this wave's keys and all exist: no masks
+    if (t0 >= jw + 31 && t0 + 31 < a.n)
+      body(std::false_type{});
+    else
+      body(std::true_type{});
     if (more) {
       tile_store<D>(qt_s[(it + 1) & 1], reg);
       stat_store((it + 1) & 1);
@@ -388,10 +425,7 @@ hipError_t launch_t(const PrefillScoreArgs& a, hipStream_t s) {
   hipError_t e;
   if constexpr (std::is_same<T, uint16_t>::value) {
     const dim3 grid((a.n + 127) / 128, a.q_heads, a.layers * a.batch);
-    k_prefill_rowstats_mk<D, 0><<<grid, 256, 0, s>>>(a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    k_prefill_rowstats_mk<D, 1><<<grid, 256, 0, s>>>(a);
+    k_prefill_rowstats_mk<D><<<grid, 256, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_prefill_colsum_mk<D><<<grid, 256, 0, s>>>(a);
