@@ -54,6 +54,11 @@ CASES = {
     "tiny_f32": (tkvsynth.CONFIGS["tiny"].replace(steps=40), {}),
     # stream staging with 8-bit rows: the step is the two separate calls
     "tiny_stream_t2": (tkvsynth.CONFIGS["tiny"].replace(steps=40, t2_ratio=0.1), {"staging_layers": 2}),
+    # the largest batch: 64 sequences, one new row and one fold tile each
+    "batch64": (tkvsynth.CONFIGS["tiny"].replace(batch=64, prefill=90, steps=17, delta=8, prompt=8, recent=8), {}),
+    # the most query heads: 256 on 32 kv heads (G = 8), bf16 head_dim 64
+    "heads256": (tkvsynth.CONFIGS["tiny"].replace(dtype="bf16", head_dim=64, kv_heads=32, q_heads=256, layers=1,
+                                                  prefill=300, steps=17, delta=8, prompt=8, recent=16), {}),
 }
 
 
