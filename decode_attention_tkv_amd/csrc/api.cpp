@@ -18,10 +18,13 @@ int tkv_fail(tkv* t, int code, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  if (t)
-    t->err = buf;
-  else
-    g_create_err = buf;
+  try {
+    if (t)
+      t->err = buf;
+    else
+      g_create_err = buf;
+  } catch (...) {  // no room even for the message: the code still tells
+  }
   return code;
 }
 
@@ -89,7 +92,7 @@ static void release(tkv* t) {
 
 extern "C" const char* tkv_last_error(const tkv_t* t) { return t ? t->err.c_str() : g_create_err.c_str(); }
 
-extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_ratio, double evict_ratio,
+static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, double evict_ratio,
                           tkv_protect protect, const tkv_options* opts, tkv_t** out) {
   if (!out) return tkv_fail(nullptr, TKV_EINVAL, "out is NULL");
   *out = nullptr;
@@ -126,6 +129,16 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   const bool resident = o.staging_layers == 0 || o.staging_layers >= s.layers;
 
   tkv* t = new tkv();
+  // frees the half-built handle on every early return and on an exception
+  struct Owner {
+    tkv* t;
+    ~Owner() {
+      if (t) {
+        release(t);
+        delete t;
+      }
+    }
+  } owner{t};
   t->L = s.layers;
   t->Hq = s.q_heads;
   t->Hkv = s.kv_heads;
@@ -235,9 +248,7 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   }
   if (rc != TKV_OK) {
     g_create_err = t->err;
-    release(t);
-    delete t;
-    return rc;
+    return rc;  // the owner frees the handle
   }
   t->nlive.assign(B, 0);
   t->free0.resize(t->shared_hbm ? 1 : B);
@@ -256,19 +267,27 @@ extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_rati
   t->st.host_bytes = (int64_t)(2 * L * B * t->cap1) * t->row_bytes +
                      (int64_t)(2 * L * B * t->cap2) * (t->Hkv * t->D + 4 * t->sh);
   t->st.full_cache_bytes = (int64_t)(2 * L * B * nmax) * t->row_bytes;
+  owner.t = nullptr;
   *out = t;
   return TKV_OK;
 }
+extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_ratio, double evict_ratio,
+                          tkv_protect protect, const tkv_options* opts, tkv_t** out) {
+  return guarded(nullptr, [&] { return create_impl(shape, delta, hbm_ratio, evict_ratio, protect, opts, out); });
+}
 
-extern "C" int tkv_destroy(tkv_t* t) {
+static int destroy_impl(tkv_t* t) {
   if (!t) return TKV_OK;
   (void)hipDeviceSynchronize();
   release(t);
   delete t;
   return TKV_OK;
 }
+extern "C" int tkv_destroy(tkv_t* t) {
+  return guarded(nullptr, [&] { return destroy_impl(t); });
+}
 
-extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tokens, tkv_stream_t stream) {
+static int prefill_impl(tkv_t* t, const void* k, const void* v, int32_t n_tokens, tkv_stream_t stream) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
   if (t->state != TkvState::Empty || t->n != 0) return tkv_fail(t, TKV_ESTATE, "prefill needs an empty cache");
   if (!k || !v) return tkv_fail(t, TKV_EINVAL, "k/v is NULL");
@@ -381,8 +400,11 @@ extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tok
   t->state = TkvState::Ready;
   return TKV_OK;
 }
+extern "C" int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tokens, tkv_stream_t stream) {
+  return guarded(t, [&] { return prefill_impl(t, k, v, n_tokens, stream); });
+}
 
-extern "C" int tkv_prefill_scored(tkv_t* t, const void* k, const void* v, const void* q, int32_t n_tokens,
+static int prefill_scored_impl(tkv_t* t, const void* k, const void* v, const void* q, int32_t n_tokens,
                                   tkv_stream_t stream) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
   if (!q) return tkv_fail(t, TKV_EINVAL, "q is NULL");
@@ -411,6 +433,10 @@ extern "C" int tkv_prefill_scored(tkv_t* t, const void* k, const void* v, const 
   HIP_TRY(t, hipFreeAsync(a.colsum, st));
   HIP_TRY(t, e);
   return tkv_reassign(t, stream);
+}
+extern "C" int tkv_prefill_scored(tkv_t* t, const void* k, const void* v, const void* q, int32_t n_tokens,
+                                  tkv_stream_t stream) {
+  return guarded(t, [&] { return prefill_scored_impl(t, k, v, q, n_tokens, stream); });
 }
 
 // Checks of an append; TKV_OK when a step may start.
@@ -450,7 +476,7 @@ static void append_commit(tkv* t, const int32_t* slot) {
   t->state = TkvState::InStep;
 }
 
-extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream) {
+static int append_impl(tkv_t* t, const void* k, const void* v, tkv_stream_t stream) {
   int rc = append_check(t, k, v);
   if (rc) return rc;
   AppendArgs a{};
@@ -475,6 +501,9 @@ extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t s
                            (hipStream_t)stream));
   append_commit(t, a.slot);
   return TKV_OK;
+}
+extern "C" int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream) {
+  return guarded(t, [&] { return append_impl(t, k, v, stream); });
 }
 
 // A timing event from the pool.  The launch binds it to its kernel's own start
@@ -568,7 +597,7 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
 static int issue_prefetch(tkv* t, int upto) {
   if (t->arena_job.valid()) {
     const int rc = t->arena_job.get();
-    if (rc) return rc;
+    if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
   }
   if (t->arena_pending) {
     HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_arena, 0));
@@ -635,7 +664,7 @@ static void end_step(tkv* t, int max_live) {
   t->state = TkvState::Ready;
 }
 
-extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
+static int decode_attn_impl(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
                                tkv_stream_t stream) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
   if (t->state != TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "no step in progress (append first)");
@@ -671,8 +700,12 @@ extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_coun
   if (t->layers_done == t->L) end_step(t, max_live);
   return TKV_OK;
 }
+extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
+                               tkv_stream_t stream) {
+  return guarded(t, [&] { return decode_attn_impl(t, layer_begin, layer_count, q, out, stream); });
+}
 
-extern "C" int tkv_decode_step(tkv_t* t, const void* k, const void* v, const void* q, float* out,
+static int decode_step_impl(tkv_t* t, const void* k, const void* v, const void* q, float* out,
                                tkv_stream_t stream) {
   int rc = append_check(t, k, v);
   if (rc) return rc;
@@ -703,12 +736,16 @@ extern "C" int tkv_decode_step(tkv_t* t, const void* k, const void* v, const voi
   end_step(t, max_live);
   return TKV_OK;
 }
+extern "C" int tkv_decode_step(tkv_t* t, const void* k, const void* v, const void* q, float* out,
+                               tkv_stream_t stream) {
+  return guarded(t, [&] { return decode_step_impl(t, k, v, q, out, stream); });
+}
 
-extern "C" int tkv_stats(tkv_t* t, tkv_stats_t* out) {
+static int stats_impl(tkv_t* t, tkv_stats_t* out) {
   if (!t || !out) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (t->arena_job.valid()) {
     const int rc = t->arena_job.get();
-    if (rc) return rc;
+    if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
   }
   HIP_TRY(t, hipStreamSynchronize(t->side));
   HIP_TRY(t, hipStreamSynchronize(t->wb));
@@ -725,6 +762,9 @@ extern "C" int tkv_stats(tkv_t* t, tkv_stats_t* out) {
   *out = t->st;
   return TKV_OK;
 }
+extern "C" int tkv_stats(tkv_t* t, tkv_stats_t* out) {
+  return guarded(t, [&] { return stats_impl(t, out); });
+}
 
 int tkv_flush_score(tkv* t, hipStream_t stream) {
   if (!t->score_pending) return TKV_OK;
@@ -733,15 +773,18 @@ int tkv_flush_score(tkv* t, hipStream_t stream) {
   return TKV_OK;
 }
 
-extern "C" int tkv_read_scores(tkv_t* t, float* scores, tkv_stream_t stream) {
+static int read_scores_impl(tkv_t* t, float* scores, tkv_stream_t stream) {
   if (!t || !scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (int rc = tkv_flush_score(t, (hipStream_t)stream)) return rc;
   HIP_TRY(t, hipMemcpyAsync(scores, t->s, (size_t)t->B * t->nmax * 4, hipMemcpyDeviceToHost, (hipStream_t)stream));
   HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
   return TKV_OK;
 }
+extern "C" int tkv_read_scores(tkv_t* t, float* scores, tkv_stream_t stream) {
+  return guarded(t, [&] { return read_scores_impl(t, scores, stream); });
+}
 
-extern "C" int tkv_write_scores(tkv_t* t, const float* scores, tkv_stream_t stream) {
+static int write_scores_impl(tkv_t* t, const float* scores, tkv_stream_t stream) {
   if (!t || !scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "step in progress");
   if (int rc = tkv_flush_score(t, (hipStream_t)stream)) return rc;
@@ -749,15 +792,21 @@ extern "C" int tkv_write_scores(tkv_t* t, const float* scores, tkv_stream_t stre
   HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
   return TKV_OK;
 }
+extern "C" int tkv_write_scores(tkv_t* t, const float* scores, tkv_stream_t stream) {
+  return guarded(t, [&] { return write_scores_impl(t, scores, stream); });
+}
 
-extern "C" int tkv_read_tiers(tkv_t* t, uint8_t* tiers, tkv_stream_t stream) {
+static int read_tiers_impl(tkv_t* t, uint8_t* tiers, tkv_stream_t stream) {
   if (!t || !tiers) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   HIP_TRY(t, hipMemcpyAsync(tiers, t->tier, (size_t)t->B * t->nmax, hipMemcpyDeviceToHost, (hipStream_t)stream));
   HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
   return TKV_OK;
 }
+extern "C" int tkv_read_tiers(tkv_t* t, uint8_t* tiers, tkv_stream_t stream) {
+  return guarded(t, [&] { return read_tiers_impl(t, tiers, stream); });
+}
 
-extern "C" int tkv_read_deltas(tkv_t* t, tkv_delta* promote, tkv_delta* demote, int32_t* counts) {
+static int read_deltas_impl(tkv_t* t, tkv_delta* promote, tkv_delta* demote, int32_t* counts) {
   if (!t || !promote || !demote || !counts) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   const size_t nd = (size_t)t->B * t->nmax;
   std::memcpy(promote, t->h_promote, nd * sizeof(tkv_delta));
@@ -765,15 +814,18 @@ extern "C" int tkv_read_deltas(tkv_t* t, tkv_delta* promote, tkv_delta* demote, 
   std::memcpy(counts, t->h_counts, (size_t)t->B * 2 * sizeof(int32_t));
   return TKV_OK;
 }
+extern "C" int tkv_read_deltas(tkv_t* t, tkv_delta* promote, tkv_delta* demote, int32_t* counts) {
+  return guarded(t, [&] { return read_deltas_impl(t, promote, demote, counts); });
+}
 
-extern "C" int tkv_read_kv(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, void* k, void* v,
+static int read_kv_impl(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, void* k, void* v,
                            tkv_stream_t stream) {
   if (!t || !k || !v) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (layer < 0 || layer >= t->L || seq < 0 || seq >= t->B || pos < 0 || pos >= t->n)
     return tkv_fail(t, TKV_EINVAL, "layer/seq/pos out of range");
   if (t->arena_job.valid()) {
     const int rc = t->arena_job.get();
-    if (rc) return rc;
+    if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
   }
   const size_t at = (size_t)seq * t->nmax + pos;
   const uint8_t tier = t->h_tier[at];
@@ -812,15 +864,19 @@ extern "C" int tkv_read_kv(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, vo
                   hb);
   return TKV_OK;
 }
+extern "C" int tkv_read_kv(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, void* k, void* v,
+                           tkv_stream_t stream) {
+  return guarded(t, [&] { return read_kv_impl(t, layer, seq, pos, k, v, stream); });
+}
 
-extern "C" int tkv_read_t2(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, int8_t* k_codes, int8_t* v_codes,
+static int read_t2_impl(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, int8_t* k_codes, int8_t* v_codes,
                            float* scales) {
   if (!t || !k_codes || !v_codes || !scales) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (layer < 0 || layer >= t->L || seq < 0 || seq >= t->B || pos < 0 || pos >= t->n)
     return tkv_fail(t, TKV_EINVAL, "layer/seq/pos out of range");
   if (t->arena_job.valid()) {
     const int rc = t->arena_job.get();
-    if (rc) return rc;
+    if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
   }
   const size_t at = (size_t)seq * t->nmax + pos;
   if (t->h_tier[at] != TKV_T2) return tkv_fail(t, TKV_ESTATE, "position %d is not in T2", pos);
@@ -835,4 +891,8 @@ extern "C" int tkv_read_t2(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, in
           (which ? t->ascale_v : t->ascale_k)[(((size_t)layer * t->B + seq) * t->cap2 + idx) * t->sh + k];
   }
   return TKV_OK;
+}
+extern "C" int tkv_read_t2(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, int8_t* k_codes, int8_t* v_codes,
+                           float* scales) {
+  return guarded(t, [&] { return read_t2_impl(t, layer, seq, pos, k_codes, v_codes, scales); });
 }

@@ -4,11 +4,28 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <exception>
+#include <new>
 #include <vector>
 
 #include "handle.hpp"
 
 int tkv_fail(tkv* t, int code, const char* fmt, ...);
+
+// Runs the body of a C ABI call: no C++ exception leaves the library; a host
+// allocation failure becomes TKV_ENOMEM, anything else TKV_EHIP.
+template <typename F>
+int guarded(tkv* t, F&& f) noexcept {
+  try {
+    return f();
+  } catch (const std::bad_alloc&) {
+    return tkv_fail(t, TKV_ENOMEM, "host memory allocation failed");
+  } catch (const std::exception& e) {
+    return tkv_fail(t, TKV_EHIP, "internal error: %s", e.what());
+  } catch (...) {
+    return tkv_fail(t, TKV_EHIP, "internal error");
+  }
+}
 
 // Apply a pending Eq. 1 update of s on `stream` (no-op when none is pending).
 int tkv_flush_score(tkv* t, hipStream_t stream);

@@ -153,7 +153,7 @@ static int shared_t0_counts(tkv* t, hipStream_t st, const std::vector<int64_t>& 
   return TKV_OK;
 }
 
-extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
+static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "reassign between the layer groups of a step");
   if (t->n == 0) return TKV_OK;
@@ -167,7 +167,7 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   // reassignment's host job and copies.
   if (t->arena_job.valid()) {
     const int rc = t->arena_job.get();
-    if (rc) return rc;
+    if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
   }
   HIP_TRY(t, hipStreamSynchronize(t->side));
   HIP_TRY(t, hipEventSynchronize(t->ev_arena));
@@ -551,6 +551,7 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
                                          (const char*)t->h_qout, t->ev_pack, L, B, H, D, t->sh, (size_t)t->cap1,
                                          (size_t)t->cap2, hb, E1, E2});
     t->arena_job = t->worker.submit([job]() -> int {
+     try {
       const Job& j = *job;
       auto r1 = [&](int which, int l, int b, int h, uint32_t idx) -> char* {
         return (which ? j.a1v : j.a1k) + ((((size_t)l * j.B + b) * j.H + h) * j.cap1 + idx) * j.hb;
@@ -605,6 +606,11 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
         split(file);
       }
       return TKV_OK;
+     } catch (const std::bad_alloc&) {  // the job reports, never throws
+      return TKV_ENOMEM;
+     } catch (...) {
+      return TKV_EHIP;
+     }
     });
   }
 
@@ -615,4 +621,7 @@ extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
   t->st.reassign_ms +=
       std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - wall0).count();
   return TKV_OK;
+}
+extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
+  return guarded(t, [&] { return reassign_impl(t, stream); });
 }
