@@ -585,9 +585,7 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
   f.chunk = t->chunk;
   f.lstride = t->lstride;
   for (int b = 0; b < t->B; ++b) f.nlive[b] = t->nlive[b];
-  const int tiles_now = (max_live + 255) / 256;
-  f.tiles_grid = tiles_now;
-  if (tiles_now > 0) HIP_TRY(t, launch_finalize(f, t->D, lc, tiles_now, st));
+  if (max_live > 0) HIP_TRY(t, launch_finalize(f, t->D, lc, max_live, st));
   return TKV_OK;
 }
 

@@ -613,19 +613,23 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
 
 // ---------------------------------------------------------------------------
 // Merge chunk partials and sum alpha over heads.  grid (tiles + ceil(Hq /
-// (256 / D)), batch, layer_count), block 256.  Blocks x < tiles sum alpha over
-// the layer's heads for live rows [256x, 256x + 256); the other blocks merge
-// the chunk partials of 256 / D heads into M, 1 / sum and the output row.
-// Both kinds merge the chunk (max, sum) pairs in chunk order, so they agree.
-template <int D>
+// HPB), batch, layer_count), block 256.  Blocks x < tiles sum alpha over the
+// layer's heads for RPT * 256 live rows, RPT consecutive rows per thread (one
+// 16-byte load per head when RPT = 4); the other blocks merge the chunk
+// partials of HPB = 256 / (D / RPT) heads into M, 1 / sum and the output
+// rows, RPT elements per thread.  Both kinds merge the chunk (max, sum) pairs in
+// chunk order, so they agree, and every sum runs in head order (rows) or chunk
+// order (outputs) whatever RPT is.
+template <int D, int RPT>
 __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
   __shared__ float Ms[kMaxQHeads];
   __shared__ float iLs[kMaxQHeads];
+  constexpr int TILE = 256 * RPT;
   const int tid = threadIdx.x;
   const int x = blockIdx.x, b = blockIdx.y, ll = blockIdx.z;
   const int l = a.layer_begin + ll;
   const int nl = a.nlive[b];
-  const int tiles = (nl + 255) / 256;
+  const int tiles = (nl + TILE - 1) / TILE;
   const int tiles_grid = a.tiles_grid;
   const int nch = (nl + a.chunk - 1) / a.chunk;
   const int64_t hbase = ((int64_t)l * a.batch + b) * a.q_heads;
@@ -643,41 +647,63 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
   };
 
   if (x >= tiles_grid) {
-    // ---- output rows
-    constexpr int HPB = 256 / D;
-    const int h = (x - tiles_grid) * HPB + tid / D, e = tid % D;
+    // ---- output rows: D / RPT threads per head
+    typedef float outv __attribute__((ext_vector_type(RPT)));
+    constexpr int TPH = D / RPT;
+    constexpr int HPB = 256 / TPH;
+    const int h = (x - tiles_grid) * HPB + tid / TPH, ev = tid % TPH;
     if (h >= a.q_heads || nl == 0) return;
     float M, iL;
     merge_head(h, &M, &iL);
     const float* ml = a.part_ml + (hbase + h) * a.max_chunks * 2;
-    const float* po = a.part_o + (hbase + h) * a.max_chunks * D;
-    float acc = 0.f;
+    const outv* po = reinterpret_cast<const outv*>(a.part_o + (hbase + h) * a.max_chunks * D) + ev;
+    outv acc = {};
 #pragma unroll 8
-    for (int c = 0; c < nch; ++c) acc += po[(int64_t)c * D + e] * exp2f(ml[2 * c] - M);
-    a.out[(((int64_t)ll * a.batch + b) * a.q_heads + h) * D + e] = acc * iL;
+    for (int c = 0; c < nch; ++c) {
+      const outv v = po[(int64_t)c * (D / RPT)];
+      const float w = exp2f(ml[2 * c] - M);
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) acc[k] += v[k] * w;
+    }
+    outv o;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) o[k] = acc[k] * iL;
+    reinterpret_cast<outv*>(a.out + (((int64_t)ll * a.batch + b) * a.q_heads + h) * D)[ev] = o;
     return;
   }
   if (x >= tiles) return;
-  // ---- per-layer score of 256 live rows
-  const int j = x * 256 + tid;
-  const float* lg = a.logits + hbase * a.lstride + j;
-  constexpr int KP = 32;  // this row's first logits are in flight during the merge
-  float zr[KP];
+  // ---- per-layer score of RPT consecutive live rows per thread
+  typedef float rowv __attribute__((ext_vector_type(RPT)));
+  const int j0 = x * TILE + RPT * tid;
+  const float* lg = a.logits + hbase * a.lstride + j0;
+  constexpr int KP = 32 / RPT;  // this thread's first KP heads' logits are in flight during the merge
+  rowv zr[KP];
 #pragma unroll
-  for (int h = 0; h < KP; ++h) zr[h] = (j < nl && h < a.q_heads) ? lg[(int64_t)h * a.lstride] : 0.f;
+  for (int h = 0; h < KP; ++h)
+    zr[h] = (j0 < nl && h < a.q_heads) ? *reinterpret_cast<const rowv*>(lg + (int64_t)h * a.lstride) : rowv{};
   for (int h = tid; h < a.q_heads; h += 256) merge_head(h, &Ms[h], &iLs[h]);
   __syncthreads();
   float* ls_row = a.layer_score + ((int64_t)l * a.batch + b) * a.lstride;
-  if (j < nl) {
-    float S = 0.f;
+  if (j0 < (nl + 31) / 32 * 32) {  // the rows past nl on the last line get 0
+    float S[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) S[k] = 0.f;
 #pragma unroll
     for (int h = 0; h < KP; ++h)
-      if (h < a.q_heads) S += exp2f(zr[h] - Ms[h]) * iLs[h];
-#pragma unroll 8
-    for (int h = KP; h < a.q_heads; ++h) S += exp2f(lg[(int64_t)h * a.lstride] - Ms[h]) * iLs[h];
-    ls_row[j] = S;
-  } else if (j < (nl + 31) / 32 * 32) {
-    ls_row[j] = 0.f;  // the rest of the last line
+      if (h < a.q_heads) {
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) S[k] += exp2f(zr[h][k] - Ms[h]) * iLs[h];
+      }
+#pragma unroll 4
+    for (int h = KP; h < a.q_heads; ++h) {
+      const rowv z = *reinterpret_cast<const rowv*>(lg + (int64_t)h * a.lstride);
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) S[k] += exp2f(z[k] - Ms[h]) * iLs[h];
+    }
+    rowv o;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) o[k] = j0 + k < nl ? S[k] : 0.f;
+    *reinterpret_cast<rowv*>(ls_row + j0) = o;
   }
 }
 
@@ -754,14 +780,25 @@ hipError_t launch_attn(const AttnArgs& a, const StepArgs& n, int dtype, int head
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_finalize(const FinalizeArgs& a, int head_dim, int layer_count, int tiles_now,
+hipError_t launch_finalize(const FinalizeArgs& a, int head_dim, int layer_count, int max_live,
                            hipStream_t s) {
-  const int hpb = 256 / head_dim;
-  const dim3 grid(a.tiles_grid + (a.q_heads + hpb - 1) / hpb, a.batch, layer_count);
-  if (head_dim == 128)
-    k_finalize<128><<<grid, 256, 0, s>>>(a);
+  // four rows (or output elements) per thread once that still gives 512 or
+  // more score blocks (long or batched caches); one per thread otherwise,
+  // where the pass is a single round of short, latency-bound blocks
+  const int wide_tiles = (max_live + 1023) / 1024;
+  const bool wide = (int64_t)wide_tiles * a.batch * layer_count >= 512;
+  FinalizeArgs f = a;
+  f.tiles_grid = wide ? wide_tiles : (max_live + 255) / 256;
+  const int hpb = 256 / (head_dim / (wide ? 4 : 1));
+  const dim3 grid(f.tiles_grid + (a.q_heads + hpb - 1) / hpb, a.batch, layer_count);
+  if (head_dim == 128 && wide)
+    k_finalize<128, 4><<<grid, 256, 0, s>>>(f);
+  else if (head_dim == 128)
+    k_finalize<128, 1><<<grid, 256, 0, s>>>(f);
+  else if (head_dim == 64 && wide)
+    k_finalize<64, 4><<<grid, 256, 0, s>>>(f);
   else if (head_dim == 64)
-    k_finalize<64><<<grid, 256, 0, s>>>(a);
+    k_finalize<64, 1><<<grid, 256, 0, s>>>(f);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

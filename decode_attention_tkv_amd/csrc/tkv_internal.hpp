@@ -80,7 +80,7 @@ struct FinalizeArgs {
   float* out;     // [layer_count][batch][q_heads][head_dim] fp32
   float* layer_score;  // [layers][batch][lstride]: sum over heads of alpha, per live index
   int32_t layer_begin, batch, q_heads, nmax, max_chunks, chunk, lstride;
-  int32_t tiles_grid;  // score blocks in the grid (tiles of the longest sequence)
+  int32_t tiles_grid;  // score blocks in the grid (tiles of the longest sequence; set by the launcher)
   int32_t nlive[kMaxBatch];
 };
 
@@ -264,7 +264,8 @@ hipError_t launch_append(const AppendArgs& a, const ScoreArgs* fold, int fold_ti
 // e0, e1 (may be null): events that take the kernel's own start and end times.
 hipError_t launch_attn(const AttnArgs& a, const StepArgs& step, int dtype, int head_dim, int group, int chunk,
                        int layer_count, int chunks_now, hipEvent_t e0, hipEvent_t e1, hipStream_t s);
-hipError_t launch_finalize(const FinalizeArgs& a, int head_dim, int layer_count, int tiles_now,
+// max_live: live rows of the longest sequence; the launcher sets tiles_grid.
+hipError_t launch_finalize(const FinalizeArgs& a, int head_dim, int layer_count, int max_live,
                            hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s);
 
