@@ -236,7 +236,10 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
   constexpr int NW = 4;
   constexpr int RPW = CHUNK / NW;               // rows per wave
   constexpr int ITERS = RPW / RPI;
-  constexpr int UB = (G <= 2) ? 8 : 4;
+  // loads in flight per lane per batch: 16 for one query head per kv head
+  // (1.2% faster than 8 at the 7B shape, though it leaves 5 waves per SIMD
+  // instead of 8), fewer as the G query heads' accumulators take registers
+  constexpr int UB = (G == 1) ? 16 : (G == 2) ? 8 : 4;
   constexpr int U = ITERS < UB ? ITERS : UB;    // loads in flight per lane per batch
   static_assert(RPW % RPI == 0 && ITERS % U == 0, "chunk shape");
 
