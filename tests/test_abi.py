@@ -68,3 +68,6 @@ def test_null_handle_calls_fail_cleanly(tkv):
     assert lib.tkv_append(None, None, None, None) == tkv.TKV_EINVAL
     assert lib.tkv_decode_attn(None, 0, 1, None, None, None) == tkv.TKV_EINVAL
     assert lib.tkv_reassign(None, None) == tkv.TKV_EINVAL
+    assert lib.tkv_decode_step(None, None, None, None, None, None) == tkv.TKV_EINVAL
+    assert lib.tkv_prefill_scored(None, None, None, None, 1, None) == tkv.TKV_EINVAL
+    assert lib.tkv_stats(None, None) == tkv.TKV_EINVAL
