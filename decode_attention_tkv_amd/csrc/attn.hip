@@ -637,12 +637,37 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
   const int nch = (nl + a.chunk - 1) / a.chunk;
   const int64_t hbase = ((int64_t)l * a.batch + b) * a.q_heads;
 
+  // M = max of the chunk maxima, L = sum over chunks, in chunk order, of
+  // sum_c * 2^(max_c - M).  Up to MC chunks the pairs arrive in one batch of
+  // loads and stay in registers; longer lists take two passes over memory.
+  // Both forms add the same terms in the same order.
+  constexpr int MC = 16;
+  auto load_pairs = [&](int h, float2 (&v)[MC]) {
+    const float2* ml = reinterpret_cast<const float2*>(a.part_ml + (hbase + h) * a.max_chunks * 2);
+#pragma unroll
+    for (int c = 0; c < MC; ++c) v[c] = c < nch ? ml[c] : make_float2(-INFINITY, 0.f);
+  };
+  auto merge_pairs = [&](const float2 (&v)[MC], float* M_out, float* iL_out) {
+    float M = -INFINITY, L = 0.f;
+#pragma unroll
+    for (int c = 0; c < MC; ++c) M = fmaxf(M, v[c].x);
+#pragma unroll
+    for (int c = 0; c < MC; ++c)
+      if (c < nch) L += v[c].y * exp2f(v[c].x - M);
+    *M_out = M;
+    *iL_out = 1.f / L;
+  };
   auto merge_head = [&](int h, float* M_out, float* iL_out) {
+    if (nch <= MC) {
+      float2 v[MC];
+      load_pairs(h, v);
+      merge_pairs(v, M_out, iL_out);
+      return;
+    }
     const float* ml = a.part_ml + (hbase + h) * a.max_chunks * 2;
-    float M = -INFINITY;
+    float M = -INFINITY, L = 0.f;
 #pragma unroll 8
     for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[2 * c]);
-    float L = 0.f;
 #pragma unroll 8
     for (int c = 0; c < nch; ++c) L += ml[2 * c + 1] * exp2f(ml[2 * c] - M);
     *M_out = M;
@@ -656,11 +681,33 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
     constexpr int HPB = 256 / TPH;
     const int h = (x - tiles_grid) * HPB + tid / TPH, ev = tid % TPH;
     if (h >= a.q_heads || nl == 0) return;
-    float M, iL;
-    merge_head(h, &M, &iL);
     const float* ml = a.part_ml + (hbase + h) * a.max_chunks * 2;
     const outv* po = reinterpret_cast<const outv*>(a.part_o + (hbase + h) * a.max_chunks * D) + ev;
     outv acc = {};
+    if (nch <= MC) {
+      // the partials' loads go out with the pairs', before M is known
+      float2 v[MC];
+      outv pv[MC];
+      load_pairs(h, v);
+#pragma unroll
+      for (int c = 0; c < MC; ++c) pv[c] = c < nch ? po[(int64_t)c * (D / RPT)] : outv{};
+      float M, iL;
+      merge_pairs(v, &M, &iL);
+#pragma unroll
+      for (int c = 0; c < MC; ++c)
+        if (c < nch) {
+          const float w = exp2f(v[c].x - M);
+#pragma unroll
+          for (int k = 0; k < RPT; ++k) acc[k] += pv[c][k] * w;
+        }
+      outv o;
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) o[k] = acc[k] * iL;
+      reinterpret_cast<outv*>(a.out + (((int64_t)ll * a.batch + b) * a.q_heads + h) * D)[ev] = o;
+      return;
+    }
+    float M, iL;
+    merge_head(h, &M, &iL);
 #pragma unroll 8
     for (int c = 0; c < nch; ++c) {
       const outv v = po[(int64_t)c * (D / RPT)];
