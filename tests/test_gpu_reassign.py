@@ -46,7 +46,8 @@ def run_parity(w, inp, steps, check_every=1, **kw):
     """Drive GPU and oracle together; at every reassignment the oracle ranks by
     the GPU's fp32 scores, its labels must equal the GPU's, then both go on."""
     c = _new(w, **kw)
-    c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
+    if w.prefill:  # a workload with no prefill starts from an empty cache
+        c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
     o = make_oracle(w, inp)
     out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     outs = []
@@ -88,6 +89,31 @@ def test_tiny_full_run_parity():
     # floor(.3*544)=163 in T0, floor(.03*544)=16 evicted (Method §1 budgets)
     assert counts[0] == 163 and counts[3] == 16 and counts[2] == 0
     assert st["evictions"] == 16 and st["reassigns"] == nr
+
+
+@pytest.mark.parametrize("name", ["tiny", "14b"])
+def test_empty_cache_start(name):
+    """No prefill: the cache grows from nothing by decode steps alone, with
+    reassignments (T1 and eviction) once the protected window is outgrown."""
+    if name == "tiny":
+        w = tkvsynth.CONFIGS["tiny"].replace(prefill=0, prompt=0, sinks=2, recent=8, steps=64)
+    else:  # bf16 grouped-query heads (matrix-core path), two sequences
+        w = tkvsynth.CONFIGS["14b"].replace(layers=2, batch=2, prefill=0, prompt=0, sinks=4, recent=16,
+                                            delta=32, steps=96)
+    inp = Inputs(w)
+    outs, s, tiers, st, o, nr = run_parity(w, inp, w.steps)
+    assert nr == w.steps // w.delta
+    # step 0 has one live row: its weight is exactly 1, so every query head
+    # returns its kv head's v row unchanged
+    v0 = w.values(inp.vn[:, :, 0])  # [L][B][Hkv][d]
+    g = w.q_heads // w.kv_heads
+    assert np.array_equal(outs[0].astype(np.float64), np.repeat(v0, g, axis=2))
+    n = o.n
+    for b in range(w.batch):
+        counts = [int((tiers[b, :n] == t).sum()) for t in range(4)]
+        assert counts[0] == int(w.hbm_ratio * n) and counts[3] == int(w.evict_ratio * n) and counts[1] > 0
+        # each step's weights sum to 1 over the live rows; evicted scores stay frozen
+        assert abs(float(np.sum(s[b, :n], dtype=np.float64)) - w.steps) <= 1e-4 * w.steps
 
 
 def test_tiny_stream_staging_matches_resident():
