@@ -190,10 +190,19 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   dev((void**)&t->tier, B * nmax);
   dev((void**)&t->loc, B * nmax * 4);
   dev((void**)&t->s, B * nmax * 4);
-  dev((void**)&t->logits, L * B * Hq * t->lstride * 4);
+  t->defer = resident && s.dtype == TKV_BF16 && group >= 4;  // the matrix-core path over resident staging
+  if (t->defer) {
+    dev(&t->qbuf[0], L * B * Hq * t->D * t->esz);
+    dev(&t->qbuf[1], L * B * Hq * t->D * t->esz);
+    dev((void**)&t->mlbuf[0], L * B * Hq * 2 * 4);
+    dev((void**)&t->mlbuf[1], L * B * Hq * 2 * 4);
+    dev((void**)&t->spart, L * t->Hkv * B * t->lstride * 4);
+  } else {
+    dev((void**)&t->logits, L * B * Hq * t->lstride * 4);
+    dev((void**)&t->layer_score, L * B * t->lstride * 4);
+  }
   dev((void**)&t->part_ml, L * B * Hq * t->max_chunks * 2 * 4);
   dev((void**)&t->part_o, L * B * Hq * t->max_chunks * t->D * 4);
-  dev((void**)&t->layer_score, L * B * t->lstride * 4);
   dev((void**)&t->tier_alt, B * nmax);
   const size_t counts_bytes = (B * 2 * 4 + 15) / 16 * 16;
   t->delta_block_bytes = counts_bytes + 2 * B * nmax * sizeof(tkv_delta);
@@ -251,6 +260,7 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
     return rc;  // the owner frees the handle
   }
   t->nlive.assign(B, 0);
+  t->prev_nlive.assign(B, 0);
   t->free0.resize(t->shared_hbm ? 1 : B);
   for (auto& f : t->free0) {
     f.resize(t->cap0);
@@ -534,11 +544,39 @@ static int drain_events(tkv* t) {
   return TKV_OK;
 }
 
+// Deferred Eq. 1: the fold of the pending step's per-group sums into s.
+static ScoreArgs defer_fold_args(const tkv* t) {
+  ScoreArgs sa{};
+  sa.layer_score = t->spart;  // rows [layer][kv head], summed in that order
+  sa.live_pos = t->live_pos;
+  sa.s = t->s;
+  sa.inv_lh = (float)(1.0 / ((double)t->L * t->Hq));
+  sa.layers = t->L * t->Hkv;
+  sa.batch = t->B;
+  sa.nmax = t->nmax;
+  sa.lstride = t->lstride;
+  for (int b = 0; b < t->B; ++b) sa.nlive[b] = t->prev_nlive[b];
+  return sa;
+}
+
+static int prev_tiles(const tkv* t) {
+  int m = 0;
+  for (int b = 0; b < t->B; ++b) m = std::max(m, t->prev_nlive[b]);
+  return (m + 255) / 256;
+}
+
 // Split-K attention + chunk merge for layers [lb, lb + lc) whose q/out start at q, out.
 // step: the fused append + Eq. 1 update of a whole-step launch, or nullptr.
 static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int max_live, hipStream_t st,
                          const StepArgs* step = nullptr) {
   AttnArgs a{};
+  if (t->defer) {
+    a.prev_mode = t->prev_pending ? 1 : 0;
+    a.qprev = t->qbuf[t->qcur];
+    a.qsave = t->qbuf[t->qcur ^ 1];
+    a.mlprev = t->mlbuf[t->qcur];
+    a.spart = t->spart;
+  }
   a.rows = t->rowspace();
   a.live_loc = t->live_loc;
   a.q = q;
@@ -585,7 +623,52 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
   f.chunk = t->chunk;
   f.lstride = t->lstride;
   for (int b = 0; b < t->B; ++b) f.nlive[b] = t->nlive[b];
-  if (max_live > 0) HIP_TRY(t, launch_finalize(f, t->D, lc, max_live, st));
+  // deferred Eq. 1: keep (M, 1/L) for the next step; the step's last layer
+  // group also folds the pending step's sums, complete once every layer ran
+  ScoreArgs fold{};
+  int fold_tiles = 0;
+  if (t->defer) {
+    f.mlprev = t->mlbuf[t->qcur ^ 1];
+    if (t->prev_pending && lb + lc == t->L) {
+      fold = defer_fold_args(t);
+      fold_tiles = prev_tiles(t);
+    }
+  }
+  if (max_live > 0)
+    HIP_TRY(t, launch_finalize(f, fold_tiles ? &fold : nullptr, fold_tiles, t->D, lc, max_live, st));
+  return TKV_OK;
+}
+
+// Deferred Eq. 1 of the pending step on its own: a score-only pass over its
+// rows' K in every layer, then the fold.
+static int flush_deferred(tkv* t, hipStream_t st) {
+  AttnArgs a{};
+  a.rows = t->rowspace();
+  a.live_loc = t->live_loc;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)t->D));
+  a.layer_begin = 0;
+  a.batch = t->B;
+  a.q_heads = t->Hq;
+  a.kv_heads = t->Hkv;
+  a.nmax = t->nmax;
+  a.max_chunks = t->max_chunks;
+  a.lstride = t->lstride;
+  a.prev_mode = 2;
+  a.qprev = t->qbuf[t->qcur];
+  a.mlprev = t->mlbuf[t->qcur];
+  a.spart = t->spart;
+  int m = 0;
+  for (int b = 0; b < t->B; ++b) {
+    a.nlive[b] = t->prev_nlive[b];  // that step's rows (the live list only grew since)
+    m = std::max(m, a.nlive[b]);
+  }
+  const int chunks = (m + t->chunk - 1) / t->chunk;
+  StepArgs none{};
+  if (chunks > 0) {
+    HIP_TRY(t, launch_attn(a, none, t->dtype, t->D, t->group, t->chunk, t->L, chunks, nullptr, nullptr, st));
+    HIP_TRY(t, launch_score(defer_fold_args(t), prev_tiles(t), st));
+  }
+  t->prev_pending = false;
   return TKV_OK;
 }
 
@@ -654,10 +737,17 @@ static void end_step(tkv* t, int max_live) {
   sa.nmax = t->nmax;
   sa.lstride = t->lstride;
   for (int b = 0; b < t->B; ++b) sa.nlive[b] = t->nlive[b];
-  // applied by the next append's launch (or by tkv_flush_score)
-  t->pending_score = sa;
-  t->pending_tiles = (max_live + 255) / 256;
-  t->score_pending = t->pending_tiles > 0;
+  if (t->defer) {
+    // computed and folded by the next step's launches (or by tkv_flush_score)
+    t->prev_pending = max_live > 0;
+    t->prev_nlive = t->nlive;
+    t->qcur ^= 1;
+  } else {
+    // applied by the next append's launch (or by tkv_flush_score)
+    t->pending_score = sa;
+    t->pending_tiles = (max_live + 255) / 256;
+    t->score_pending = t->pending_tiles > 0;
+  }
   t->step += 1;
   t->state = TkvState::Ready;
 }
@@ -765,6 +855,7 @@ extern "C" int tkv_stats(tkv_t* t, tkv_stats_t* out) {
 }
 
 int tkv_flush_score(tkv* t, hipStream_t stream) {
+  if (t->defer) return t->prev_pending ? flush_deferred(t, stream) : TKV_OK;
   if (!t->score_pending) return TKV_OK;
   HIP_TRY(t, launch_score(t->pending_score, t->pending_tiles, stream));
   t->score_pending = false;

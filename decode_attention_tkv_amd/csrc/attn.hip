@@ -228,7 +228,14 @@ __global__ __launch_bounds__(256) void k_append(const AppendArgs a, const ScoreA
 // live-row tiles starting in their chunk.  Nothing else in the launch reads
 // what these writes touch: the slot was free, and the fold only reads
 // positions and live indices below the new row's.
-template <typename T, int D, int G, int CHUNK, bool MK, bool QT>
+//
+// DEF (matrix-core path, resident staging): Eq. 1 for the previous step runs
+// here instead of from stored logits.  Its queries fill the padded rows
+// G..2G-1 of the logits tile, so each K tile gives both steps' logits in the
+// same MFMAs; with that step's (M, 1/L) each row's weights are summed over
+// the group's heads and one value per row and kv head leaves the block, in
+// place of G logits.  Chunk-0 blocks keep this step's queries for the next.
+template <typename T, int D, int G, int CHUNK, bool MK, bool QT, bool DEF>
 __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   constexpr int LPR = D * (int)sizeof(T) / 16;  // lanes per row
   constexpr int EPL = 16 / (int)sizeof(T);      // elements per lane
@@ -293,6 +300,10 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
   __syncthreads();
 
   float mc[G];
+  // deferred Eq. 1: rows of the previous step (its new row came after it)
+  const int prev = DEF ? a.prev_mode : 0;
+  const int nprev = prev == 1 ? nl - 1 : nl;
+  (void)nprev;
   if constexpr (MK) {
     // ---- phase 1 on the matrix cores: Z[16 heads x 16 rows] += Q[16 x 32] K^T[32 x 16],
     // D/32 steps per tile of 16 rows (v_mfma_f32_16x16x32_bf16).  Lane l feeds
@@ -302,13 +313,29 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
     constexpr int TILES = RPW / 16;
     const int hl = lane & 15, kq = lane >> 4;
     bf16x8 qa[KC];
+    const int64_t qrow = ((int64_t)l * a.batch + b) * a.q_heads + kvh * G;  // head 0 of the group, layer l
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (hl < G)
+      if (hl < G && prev != 2)
         u = load16((const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + hl) * D + 32 * kc + 8 * kq);
+      else if (DEF && prev != 0 && hl >= G && hl < 2 * G)
+        u = load16((const T*)a.qprev + (qrow + hl - G) * D + 32 * kc + 8 * kq);
+      if (DEF && prev != 2 && c == 0 && hl < G)
+        *reinterpret_cast<uint4*>((T*)a.qsave + (qrow + hl) * D + 32 * kc + 8 * kq) = u;
       qa[kc] = as_bf16x8(u);
     }
+    // the previous step's (M, 1/L) of the heads this lane receives in rows G..2G-1
+    bool vp[4];
+    float pM[4], piL[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hp = 4 * kq + i - G;
+      vp[i] = DEF && prev != 0 && hp >= 0 && hp < G;
+      pM[i] = vp[i] ? a.mlprev[(qrow + hp) * 2] : 0.f;
+      piL[i] = vp[i] ? a.mlprev[(qrow + hp) * 2 + 1] : 0.f;
+    }
+    float* sp = DEF ? a.spart + (((int64_t)l * a.kv_heads + kvh) * a.batch + b) * a.lstride + j0 : nullptr;
     float mx[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) mx[i] = -INFINITY;
@@ -345,7 +372,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kc], as_bf16x8(kd[tt][kc]), acc, 0, 0, 0);
         const int r = wave * RPW + (t0 + tt) * 16 + hl;
-        if (r < nrows) {
+        if (prev != 2 && r < nrows) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int h = 4 * kq + i;
@@ -354,8 +381,20 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
             mx[i] = fmaxf(mx[i], z);
           }
         }
+        if (DEF && prev != 0) {
+          // sum of the previous step's weights of row r over the group's heads:
+          // this lane's heads, then the four lanes that hold row r, in a fixed order
+          float e = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (vp[i]) e += exp2f(acc[i] * a.qscale - pM[i]) * piL[i];
+          e += __shfl_xor(e, 16);
+          e += __shfl_xor(e, 32);
+          if (kq == 0 && j0 + r < nprev) __builtin_nontemporal_store(e, sp + r);
+        }
       }
     }
+    if (prev == 2) return;  // score only: the whole block leaves here
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float m = group_max<16>(mx[i]);
@@ -583,7 +622,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
     __builtin_nontemporal_store(v, a.part_ml + ((hbase + g) * a.max_chunks + c) * 2 + (tid & 1));
   }
   // logits, padded with zeros to the line that holds the chunk's last row
-  const int nw = min(CHUNK, (nrows + 31) / 32 * 32);
+  // (none when Eq. 1 is deferred)
+  const int nw = DEF ? 0 : min(CHUNK, (nrows + 31) / 32 * 32);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float* lg = a.logits + (hbase + g) * a.lstride + j0;
@@ -623,8 +663,13 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
 // rows, RPT elements per thread.  Both kinds merge the chunk (max, sum) pairs in
 // chunk order, so they agree, and every sum runs in head order (rows) or chunk
 // order (outputs) whatever RPT is.
+//
+// Deferred Eq. 1 (a.mlprev set): there are no score blocks (tiles_grid = 0);
+// the output blocks also keep every head's (M, 1/L) for the next step, and
+// blocks past the heads' fold the previous step's per-group sums into the
+// scores (layer-0 slice only, a.fold_tiles tiles per sequence).
 template <int D, int RPT>
-__global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
+__global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a, const ScoreArgs fold) {
   __shared__ float Ms[kMaxQHeads];
   __shared__ float iLs[kMaxQHeads];
   constexpr int TILE = 256 * RPT;
@@ -679,6 +724,11 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
     typedef float outv __attribute__((ext_vector_type(RPT)));
     constexpr int TPH = D / RPT;
     constexpr int HPB = 256 / TPH;
+    const int hblocks = (a.q_heads + HPB - 1) / HPB;
+    if (x >= tiles_grid + hblocks) {
+      if (ll == 0) score_rows(fold, x - tiles_grid - hblocks, b);
+      return;
+    }
     const int h = (x - tiles_grid) * HPB + tid / TPH, ev = tid % TPH;
     if (h >= a.q_heads || nl == 0) return;
     const float* ml = a.part_ml + (hbase + h) * a.max_chunks * 2;
@@ -693,6 +743,10 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
       for (int c = 0; c < MC; ++c) pv[c] = c < nch ? po[(int64_t)c * (D / RPT)] : outv{};
       float M, iL;
       merge_pairs(v, &M, &iL);
+      if (a.mlprev && ev == 0) {
+        a.mlprev[(hbase + h) * 2] = M;
+        a.mlprev[(hbase + h) * 2 + 1] = iL;
+      }
 #pragma unroll
       for (int c = 0; c < MC; ++c)
         if (c < nch) {
@@ -708,6 +762,10 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a) {
     }
     float M, iL;
     merge_head(h, &M, &iL);
+    if (a.mlprev && ev == 0) {
+      a.mlprev[(hbase + h) * 2] = M;
+      a.mlprev[(hbase + h) * 2 + 1] = iL;
+    }
 #pragma unroll 8
     for (int c = 0; c < nch; ++c) {
       const outv v = po[(int64_t)c * (D / RPT)];
@@ -769,16 +827,30 @@ struct AttnLaunch {
   hipStream_t s;
 };
 
+template <typename T, int D, int G, bool QT, bool DEF>
+const void* attn_fn(int chunk) {
+  constexpr bool MK = std::is_same<T, bf16_t>::value && G >= 4;
+  switch (chunk) {
+    case 128: return (const void*)&k_attn_chunk<T, D, G, 128, MK, QT, DEF>;
+    case 256: return (const void*)&k_attn_chunk<T, D, G, 256, MK, QT, DEF>;
+    case 512: return (const void*)&k_attn_chunk<T, D, G, 512, MK, QT, DEF>;
+    default: return nullptr;
+  }
+}
+
+// a.spart set: deferred Eq. 1, which only the matrix-core path without 8-bit
+// staging has (the launcher checks this before it sets a.spart)
 template <typename T, int D, int G, bool QT>
 hipError_t launch_attn_t(const AttnArgs& a, const StepArgs& n, int chunk, const AttnLaunch& L) {
   constexpr bool MK = std::is_same<T, bf16_t>::value && G >= 4;
   const void* fn = nullptr;
-  switch (chunk) {
-    case 128: fn = (const void*)&k_attn_chunk<T, D, G, 128, MK, QT>; break;
-    case 256: fn = (const void*)&k_attn_chunk<T, D, G, 256, MK, QT>; break;
-    case 512: fn = (const void*)&k_attn_chunk<T, D, G, 512, MK, QT>; break;
-    default: return hipErrorInvalidValue;
+  if constexpr (MK && !QT) {
+    fn = a.spart ? attn_fn<T, D, G, QT, true>(chunk) : attn_fn<T, D, G, QT, false>(chunk);
+  } else {
+    if (a.spart) return hipErrorInvalidValue;
+    fn = attn_fn<T, D, G, QT, false>(chunk);
   }
+  if (!fn) return hipErrorInvalidValue;
   AttnArgs ac = a;
   StepArgs nc = n;
   void* args[] = {&ac, &nc};
@@ -830,25 +902,28 @@ hipError_t launch_attn(const AttnArgs& a, const StepArgs& n, int dtype, int head
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_finalize(const FinalizeArgs& a, int head_dim, int layer_count, int max_live,
-                           hipStream_t s) {
+hipError_t launch_finalize(const FinalizeArgs& a, const ScoreArgs* fold, int fold_tiles, int head_dim,
+                           int layer_count, int max_live, hipStream_t s) {
   // four rows (or output elements) per thread once that still gives 512 or
   // more score blocks (long or batched caches); one per thread otherwise,
   // where the pass is a single round of short, latency-bound blocks
   const int wide_tiles = (max_live + 1023) / 1024;
   const bool wide = (int64_t)wide_tiles * a.batch * layer_count >= 512;
   FinalizeArgs f = a;
-  f.tiles_grid = wide ? wide_tiles : (max_live + 255) / 256;
+  ScoreArgs fa{};
+  if (fold) fa = *fold; else fold_tiles = 0;
+  f.tiles_grid = a.mlprev ? 0 : wide ? wide_tiles : (max_live + 255) / 256;
+  f.fold_tiles = fold_tiles;
   const int hpb = 256 / (head_dim / (wide ? 4 : 1));
-  const dim3 grid(f.tiles_grid + (a.q_heads + hpb - 1) / hpb, a.batch, layer_count);
+  const dim3 grid(f.tiles_grid + (a.q_heads + hpb - 1) / hpb + fold_tiles, a.batch, layer_count);
   if (head_dim == 128 && wide)
-    k_finalize<128, 4><<<grid, 256, 0, s>>>(f);
+    k_finalize<128, 4><<<grid, 256, 0, s>>>(f, fa);
   else if (head_dim == 128)
-    k_finalize<128, 1><<<grid, 256, 0, s>>>(f);
+    k_finalize<128, 1><<<grid, 256, 0, s>>>(f, fa);
   else if (head_dim == 64 && wide)
-    k_finalize<64, 4><<<grid, 256, 0, s>>>(f);
+    k_finalize<64, 4><<<grid, 256, 0, s>>>(f, fa);
   else if (head_dim == 64)
-    k_finalize<64, 1><<<grid, 256, 0, s>>>(f);
+    k_finalize<64, 1><<<grid, 256, 0, s>>>(f, fa);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -149,6 +149,19 @@ struct tkv {
   bool score_pending = false;
   tkvd::ScoreArgs pending_score{};
   int pending_tiles = 0;
+  // Deferred Eq. 1 (bf16 grouped-query heads on the matrix cores, resident
+  // staging): a step's weights are recomputed, from its queries and its
+  // heads' (M, 1/L), by the next step's attention launch, which streams the
+  // same K rows anyway, and folded into s by that step's merge pass; a
+  // score-only pass over K does it when s is needed first.  No logits are
+  // stored.
+  bool defer = false;
+  bool prev_pending = false;        // the last step's weights are not in s yet
+  std::vector<int32_t> prev_nlive;  // [B] live rows of that step
+  int qcur = 0;                        // qbuf[qcur], mlbuf[qcur]: that step's queries and (M, 1/L)
+  void* qbuf[2] = {nullptr, nullptr};  // [L][B][Hq][D] each
+  float* mlbuf[2] = {nullptr, nullptr};  // [L][B][Hq][2] each
+  float* spart = nullptr;              // [L][Hkv][B][lstride]
   std::vector<int32_t> nlive;                 // [B] live rows
   std::vector<std::vector<int32_t>> free0;    // [B] free T0 slots (back = next to use); [1] when shared
   bool shared_hbm = false;                    // one T0 slot space and budget for the batch

@@ -70,6 +70,15 @@ struct AttnArgs {
   float* part_o;             // [layers][batch][q_heads][max_chunks][head_dim]
   float qscale;              // log2(e) / sqrt(head_dim)
   int32_t layer_begin, batch, q_heads, kv_heads, nmax, max_chunks, lstride;
+  // Deferred Eq. 1 (matrix-core path, resident staging): the previous step's
+  // weights are recomputed from its queries while this launch streams K.
+  //   prev_mode 0: none; 1: this step's launch, previous step's rows are live
+  //   indices < nlive - 1; 2: score only (flush), rows < nlive, no attention.
+  int32_t prev_mode;
+  const void* qprev;   // [layers][batch][q_heads][head_dim]: the previous step's q
+  void* qsave;         // [layers][batch][q_heads][head_dim]: this step's q, kept for the next
+  const float* mlprev; // [layers][batch][q_heads][2]: the previous step's (M, 1/L), log2 units
+  float* spart;        // [layers][kv_heads][batch][lstride]: sum over the group's heads of alpha
   int32_t nlive[kMaxBatch];
 };
 
@@ -81,6 +90,8 @@ struct FinalizeArgs {
   float* layer_score;  // [layers][batch][lstride]: sum over heads of alpha, per live index
   int32_t layer_begin, batch, q_heads, nmax, max_chunks, chunk, lstride;
   int32_t tiles_grid;  // score blocks in the grid (tiles of the longest sequence; set by the launcher)
+  float* mlprev;       // deferred Eq. 1: (M, 1/L) of every head kept for the next step, or null
+  int32_t fold_tiles;  // deferred Eq. 1: tiles of the fold of `fold` run by layer-0 blocks (0: none)
   int32_t nlive[kMaxBatch];
 };
 
@@ -265,8 +276,9 @@ hipError_t launch_append(const AppendArgs& a, const ScoreArgs* fold, int fold_ti
 hipError_t launch_attn(const AttnArgs& a, const StepArgs& step, int dtype, int head_dim, int group, int chunk,
                        int layer_count, int chunks_now, hipEvent_t e0, hipEvent_t e1, hipStream_t s);
 // max_live: live rows of the longest sequence; the launcher sets tiles_grid.
-hipError_t launch_finalize(const FinalizeArgs& a, int head_dim, int layer_count, int max_live,
-                           hipStream_t s);
+// fold (or null): the deferred Eq. 1 sums to add to the scores, fold_tiles tiles per sequence
+hipError_t launch_finalize(const FinalizeArgs& a, const ScoreArgs* fold, int fold_tiles, int head_dim,
+                           int layer_count, int max_live, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s);
 
 // ---- launchers (move.hip) -------------------------------------------------

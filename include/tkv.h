@@ -192,7 +192,13 @@ int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream);
  * Eq. 1 increment of the scores (Method §2) is applied in stream order before
  * anything that reads or writes them: it runs inside the next tkv_append's
  * launch, or first thing in tkv_reassign, tkv_read_scores or tkv_write_scores
- * on the stream given to that call. */
+ * on the stream given to that call.  bf16 caches with 4 or more query heads
+ * per kv head and resident staging (staging_layers 0 or layers) defer it
+ * further: the next step's attention launch recomputes the step's weights
+ * from its queries while it streams the same K rows, and the next step's last
+ * layer group adds them; a score read or write, or tkv_reassign, first runs a
+ * score-only pass over K (half a step's reads) when a step is still pending.
+ * The scores are the same either way (tested bit for bit). */
 int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
                     tkv_stream_t stream);
 

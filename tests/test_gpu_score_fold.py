@@ -1,7 +1,10 @@
 """The Eq. 1 update of a step is applied in stream order before the scores
 are next read or written ("Not All Thoughts Need HBM", gist.science summary,
 Method §2): whether it runs inside the next append's launch or is flushed by
-a score read, a score write or a reassignment, the scores are the same bits."""
+a score read, a score write or a reassignment, the scores are the same bits.
+For bf16 grouped-query heads over resident staging the next step's attention
+launch recomputes the step's weights (no logits are stored); a flush then
+runs a score-only pass over K, with the same bits again."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +15,7 @@ from harness import Inputs, to_device
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, inp, read_every_step, write_at=None):
+def _run(w, inp, read_every_step, write_at=None, groups=None, read_mid_step=False):
     import decode_attention_tkv_amd as tkv
     c = tkv.TieredKV.for_workload(w)
     c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
@@ -21,7 +24,16 @@ def _run(w, inp, read_every_step, write_at=None):
     for t in range(w.steps):
         k, v = inp.step_kv(t)
         c.append(to_device(k, w.dtype), to_device(v, w.dtype))
-        c.decode_attn(to_device(inp.q[t], w.dtype), out)
+        q = to_device(inp.q[t], w.dtype)
+        if groups is None:
+            c.decode_attn(q, out)
+        else:
+            lb = 0
+            for g in groups:
+                c.decode_attn(q[lb:lb + g].contiguous(), out[lb:lb + g], layer_begin=lb, layer_count=g)
+                lb += g
+                if read_mid_step and lb < w.layers:
+                    c.read_scores()
         if read_every_step:
             c.read_scores()
         if write_at == t:
@@ -37,8 +49,18 @@ def _run(w, inp, read_every_step, write_at=None):
     return s, tiers
 
 
-def test_fold_placement_does_not_change_scores():
-    w = tkvsynth.CONFIGS["7b"].replace(layers=4, prefill=300, steps=40, delta=16, prompt=20, recent=16)
+SHAPES = {
+    # one query head per kv head: the update is summed from stored logits
+    "7b": dict(layers=4, prefill=300, steps=40, delta=16, prompt=20, recent=16),
+    # bf16 grouped-query heads: the next step's launch recomputes the weights
+    # (or a score-only pass over K does, when the scores are read first)
+    "14b": dict(layers=4, batch=2, prefill=300, steps=40, delta=16, prompt=20, recent=16),
+}
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_fold_placement_does_not_change_scores(name):
+    w = tkvsynth.CONFIGS[name].replace(**SHAPES[name])
     inp = Inputs(w)
     a, ta = _run(w, inp, read_every_step=False)
     b, tb = _run(w, inp, read_every_step=True)
@@ -51,3 +73,16 @@ def test_write_scores_replaces_pending_update():
     w = tkvsynth.CONFIGS["tiny"].replace(prefill=64, steps=20, delta=8)
     inp = Inputs(w)
     _run(w, inp, read_every_step=False, write_at=9)
+
+
+def test_scores_read_between_layer_groups():
+    """Layer groups of one step with the scores read between them: the read
+    applies the last step's update on its own, and the rest of the step then
+    adds nothing twice."""
+    w = tkvsynth.CONFIGS["14b"].replace(**SHAPES["14b"])
+    inp = Inputs(w)
+    a, ta = _run(w, inp, read_every_step=False)
+    b, tb = _run(w, inp, read_every_step=False, groups=[1, 2, 1], read_mid_step=True)
+    n = w.n_final
+    assert np.array_equal(a[:, :n], b[:, :n])
+    assert np.array_equal(ta[:, :n], tb[:, :n])
