@@ -559,10 +559,11 @@ static ScoreArgs defer_fold_args(const tkv* t) {
   return sa;
 }
 
+// tiles of 64 rows of the deferred fold
 static int prev_tiles(const tkv* t) {
   int m = 0;
   for (int b = 0; b < t->B; ++b) m = std::max(m, t->prev_nlive[b]);
-  return (m + 255) / 256;
+  return (m + 63) / 64;
 }
 
 // Split-K attention + chunk merge for layers [lb, lb + lc) whose q/out start at q, out.
@@ -666,7 +667,7 @@ static int flush_deferred(tkv* t, hipStream_t st) {
   StepArgs none{};
   if (chunks > 0) {
     HIP_TRY(t, launch_attn(a, none, t->dtype, t->D, t->group, t->chunk, t->L, chunks, nullptr, nullptr, st));
-    HIP_TRY(t, launch_score(defer_fold_args(t), prev_tiles(t), st));
+    HIP_TRY(t, launch_fold64(defer_fold_args(t), prev_tiles(t), st));
   }
   t->prev_pending = false;
   return TKV_OK;

@@ -180,6 +180,33 @@ __device__ __forceinline__ void score_rows(const ScoreArgs& a, int tile, int b) 
   a.s[p] += acc * a.inv_lh;
 }
 
+// Deferred Eq. 1 fold for live rows [64 tile, 64 tile + 64) of sequence b:
+// s[pos(j)] += (sum over the f.layers rows [layer][kv head] of f.layer_score)
+// * 1/(L*H).  Wave k of the block adds every fourth row of that list from
+// row k, in order, for 64 consecutive live rows (256 contiguous bytes per
+// load); the four partials are added in order.  The sums are long (layers x
+// kv heads), so one thread per row would wait on one long load chain.
+// Every thread of the block calls it.
+__device__ __forceinline__ void fold_rows64(const ScoreArgs& f, int tile, int b, float (*red)[64]) {
+  const int r = threadIdx.x & 63, k = threadIdx.x >> 6;
+  const int j = tile * 64 + r;
+  const bool live = j < f.nlive[b];
+  float acc = 0.f;
+  if (live) {
+    const float* p = f.layer_score + (int64_t)b * f.lstride + j;
+    const int64_t step = (int64_t)f.batch * f.lstride;
+#pragma unroll 16
+    for (int l = k; l < f.layers; l += 4) acc += p[l * step];
+  }
+  red[k][r] = acc;
+  __syncthreads();
+  if (k == 0 && live) {
+    const float t = ((red[0][r] + red[1][r]) + red[2][r]) + red[3][r];
+    const int64_t pos = (int64_t)b * f.nmax + f.live_pos[(int64_t)b * f.nmax + j];
+    f.s[pos] += t * f.inv_lh;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Append: copy the new token's K/V rows of every (layer, sequence) into its
 // T0 slot and extend the live list.  Blocks [0, 2*layers*batch) copy (one per
@@ -666,12 +693,14 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
 //
 // Deferred Eq. 1 (a.mlprev set): there are no score blocks (tiles_grid = 0);
 // the output blocks also keep every head's (M, 1/L) for the next step, and
-// blocks past the heads' fold the previous step's per-group sums into the
-// scores (layer-0 slice only, a.fold_tiles tiles per sequence).
+// blocks past the heads fold the previous step's per-group sums into the
+// scores (a.fold_tiles tiles of 64 rows per sequence, dealt over the layer
+// slices of the grid).
 template <int D, int RPT>
 __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a, const ScoreArgs fold) {
   __shared__ float Ms[kMaxQHeads];
   __shared__ float iLs[kMaxQHeads];
+  __shared__ float fold_red[4][64];
   constexpr int TILE = 256 * RPT;
   const int tid = threadIdx.x;
   const int x = blockIdx.x, b = blockIdx.y, ll = blockIdx.z;
@@ -726,7 +755,10 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a, const Sc
     constexpr int HPB = 256 / TPH;
     const int hblocks = (a.q_heads + HPB - 1) / HPB;
     if (x >= tiles_grid + hblocks) {
-      if (ll == 0) score_rows(fold, x - tiles_grid - hblocks, b);
+      // fold tiles are dealt over the layer slices: ceil(fold_tiles / slices) per slice
+      const int per = (a.fold_tiles + gridDim.z - 1) / gridDim.z;
+      const int ft = ll * per + (x - tiles_grid - hblocks);
+      if (ft < a.fold_tiles) fold_rows64(fold, ft, b, fold_red);
       return;
     }
     const int h = (x - tiles_grid) * HPB + tid / TPH, ev = tid % TPH;
@@ -817,6 +849,12 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a, const Sc
 
 // Eq. 1 update on its own: grid (tiles, batch).
 __global__ __launch_bounds__(256) void k_score(const ScoreArgs a) { score_rows(a, blockIdx.x, blockIdx.y); }
+
+// Deferred Eq. 1 fold on its own: grid (tiles of 64 rows, batch).
+__global__ __launch_bounds__(256) void k_fold64(const ScoreArgs a) {
+  __shared__ float red[4][64];
+  fold_rows64(a, blockIdx.x, blockIdx.y, red);
+}
 
 // Grouped-query heads (G >= 4) of bf16 caches take the matrix-core logits.
 // Launched through hipExtLaunchKernel so that timing events (when given) take
@@ -915,7 +953,8 @@ hipError_t launch_finalize(const FinalizeArgs& a, const ScoreArgs* fold, int fol
   f.tiles_grid = a.mlprev ? 0 : wide ? wide_tiles : (max_live + 255) / 256;
   f.fold_tiles = fold_tiles;
   const int hpb = 256 / (head_dim / (wide ? 4 : 1));
-  const dim3 grid(f.tiles_grid + (a.q_heads + hpb - 1) / hpb + fold_tiles, a.batch, layer_count);
+  const int fold_x = (fold_tiles + layer_count - 1) / layer_count;
+  const dim3 grid(f.tiles_grid + (a.q_heads + hpb - 1) / hpb + fold_x, a.batch, layer_count);
   if (head_dim == 128 && wide)
     k_finalize<128, 4><<<grid, 256, 0, s>>>(f, fa);
   else if (head_dim == 128)
@@ -931,6 +970,11 @@ hipError_t launch_finalize(const FinalizeArgs& a, const ScoreArgs* fold, int fol
 
 hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s) {
   k_score<<<dim3(tiles_now, a.batch), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold64(const ScoreArgs& a, int tiles64, hipStream_t s) {
+  k_fold64<<<dim3(tiles64, a.batch), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -276,10 +276,12 @@ hipError_t launch_append(const AppendArgs& a, const ScoreArgs* fold, int fold_ti
 hipError_t launch_attn(const AttnArgs& a, const StepArgs& step, int dtype, int head_dim, int group, int chunk,
                        int layer_count, int chunks_now, hipEvent_t e0, hipEvent_t e1, hipStream_t s);
 // max_live: live rows of the longest sequence; the launcher sets tiles_grid.
-// fold (or null): the deferred Eq. 1 sums to add to the scores, fold_tiles tiles per sequence
+// fold (or null): the deferred Eq. 1 sums to add to the scores, fold_tiles tiles of 64 rows per sequence
 hipError_t launch_finalize(const FinalizeArgs& a, const ScoreArgs* fold, int fold_tiles, int head_dim,
                            int layer_count, int max_live, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s);
+// deferred Eq. 1 fold (a.layers rows [layer][kv head]), tiles of 64 live rows
+hipError_t launch_fold64(const ScoreArgs& a, int tiles64, hipStream_t s);
 
 // ---- launchers (move.hip) -------------------------------------------------
 hipError_t launch_place_rows(const PlaceArgs& a, int layers, hipStream_t s);
