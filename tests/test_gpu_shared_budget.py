@@ -45,6 +45,18 @@ def test_shared_budget_gqa_t2_stream():
     run_parity(w, Inputs(w), w.steps, check_every=8, staging_layers=2)
 
 
+def test_shared_budget_gqa_t2_resident():
+    # bf16 grouped-query heads over resident staging: Eq. 1 is deferred to the
+    # next step's launch, so each reassignment first runs the score-only pass
+    # whose scores the joint ranking then reads
+    w = tkvsynth.CONFIGS["32b_t2"].replace(layers=3, batch=3, prefill=600, steps=65, delta=32, prompt=40,
+                                           recent=64, shared_hbm=True)
+    outs, s, tiers, st, o, nr = run_parity(w, Inputs(w), w.steps, check_every=8)
+    assert nr == 2
+    shares = _t0_shares(tiers, w, o.n)
+    assert max(shares) > min(shares)
+
+
 def test_shared_budget_fp32_tiny_batch():
     w = tkvsynth.CONFIGS["tiny"].replace(batch=3, steps=48, prompt=8, recent=16, shared_hbm=True)
     run_parity(w, Inputs(w), w.steps)
