@@ -168,9 +168,11 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   t->shared_hbm = (o.flags & TKV_FLAG_SHARED_HBM) != 0;
   t->cap0 = (int)std::min<int64_t>(nmax, std::max(pmax, h_at_max) + delta + 1);
   if (t->shared_hbm) t->cap0 *= s.batch;  // slots of the whole batch in one space
+  t->positional = resident && !t->shared_hbm;
+  if (t->positional) t->cap0 = (int)nmax;  // one slot per position
   t->cap1 = (o.flags & TKV_FLAG_NO_T1) ? 1 : (int)std::max<int64_t>(1, std::min<int64_t>(nmax, nmax - h_at_max + 1));
   t->cap2 = o.t2_ratio > 0 ? (int)std::min<int64_t>(nmax, floor_ratio(o.t2_ratio, nmax) + 1) : 0;
-  t->capS = resident ? t->cap1 + t->cap2 : t->cap1;
+  t->capS = t->positional ? 1 : resident ? t->cap1 + t->cap2 : t->cap1;  // positional: nothing lives there
   t->sh = (o.flags & TKV_FLAG_T2_HEAD_SCALES) ? s.kv_heads : 1;
   t->max_chunks = (int)((nmax + t->chunk - 1) / t->chunk);
   t->lstride = (int)((nmax + kLogitAlign - 1) / kLogitAlign * kLogitAlign);
@@ -262,10 +264,12 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   t->nlive.assign(B, 0);
   t->prev_nlive.assign(B, 0);
   t->free0.resize(t->shared_hbm ? 1 : B);
-  for (auto& f : t->free0) {
-    f.resize(t->cap0);
-    for (int i = 0; i < t->cap0; ++i) f[i] = t->cap0 - 1 - i;  // back() = lowest free slot
-  }
+  if (!t->positional)
+    for (auto& f : t->free0) {
+      f.resize(t->cap0);
+      for (int i = 0; i < t->cap0; ++i) f[i] = t->cap0 - 1 - i;  // back() = lowest free slot
+    }
+  if (t->positional) t->h_aidx.assign((size_t)B * nmax, kNoLoc);
   t->h_tier.assign(B * nmax, kUnused);
   t->h_loc.assign(B * nmax, kNoLoc);
   t->t1_owner.resize(B);
@@ -316,19 +320,29 @@ static int prefill_impl(tkv_t* t, const void* k, const void* v, int32_t n_tokens
     return tkv_fail(t, TKV_ECAPACITY, "first placement does not fit (T0 %d/%d, T1 %d/%d)", nt0, t->cap0, nt1, t->cap1);
 
   std::vector<uint32_t> codes((size_t)t->B * n0);
+  // positional staging: every live row at its position, and the T1 rows also
+  // through a temporary [L][B][cap1] area on the way to their pinned home
+  std::vector<uint32_t> codes1(t->positional ? (size_t)t->B * n0 : 0, kNoLoc);
   for (int b = 0; b < t->B; ++b) {
     auto& own = t->t1_owner[b];
     own.clear();
     for (int p = 0; p < n0; ++p) {
       uint32_t code;
-      if (first[p] == TKV_T0) {
+      if (first[p] == TKV_T3) {
+        code = kNoLoc;
+      } else if (t->positional) {
+        code = (uint32_t)p;
+        if (first[p] == TKV_T1) {
+          codes1[(size_t)b * n0 + p] = (uint32_t)(t->cap0 + own.size());
+          t->h_aidx[(size_t)b * t->nmax + p] = (uint32_t)own.size();
+          own.push_back(p);
+        }
+      } else if (first[p] == TKV_T0) {
         code = (uint32_t)t->free_list(b).back();
         t->free_list(b).pop_back();
-      } else if (first[p] == TKV_T1) {
+      } else {
         code = (uint32_t)(t->cap0 + own.size());
         own.push_back(p);
-      } else {
-        code = kNoLoc;
       }
       codes[(size_t)b * n0 + p] = code;
       t->h_tier[(size_t)b * t->nmax + p] = first[p];
@@ -339,8 +353,11 @@ static int prefill_impl(tkv_t* t, const void* k, const void* v, int32_t n_tokens
   t->st.evictions += (int64_t)nt3 * t->B;
 
   void* d_codes = nullptr;
-  HIP_TRY(t, hipMallocAsync(&d_codes, codes.size() * 4, st));
+  HIP_TRY(t, hipMallocAsync(&d_codes, codes.size() * 4 * (t->positional ? 2 : 1), st));
   HIP_TRY(t, hipMemcpyAsync(d_codes, codes.data(), codes.size() * 4, hipMemcpyHostToDevice, st));
+  if (t->positional)
+    HIP_TRY(t, hipMemcpyAsync((uint32_t*)d_codes + codes.size(), codes1.data(), codes1.size() * 4,
+                              hipMemcpyHostToDevice, st));
   PlaceArgs pa{};
   pa.rows = t->rowspace();
   // T1 rows land in a staging area first: the resident staging itself, or (stream
@@ -349,7 +366,7 @@ static int prefill_impl(tkv_t* t, const void* k, const void* v, int32_t n_tokens
   void* tmp_v = nullptr;
   const size_t hb = (size_t)t->D * t->esz;  // bytes of one head's row
   size_t src_pitch = (size_t)t->capS * hb;
-  if (!t->resident && nt1 > 0) {
+  if ((!t->resident || t->positional) && nt1 > 0) {
     const size_t bytes = (size_t)t->L * t->B * t->cap1 * t->row_bytes;
     HIP_TRY(t, hipMallocAsync(&tmp_k, bytes, st));
     HIP_TRY(t, hipMallocAsync(&tmp_v, bytes, st));
@@ -369,7 +386,16 @@ static int prefill_impl(tkv_t* t, const void* k, const void* v, int32_t n_tokens
   pa.kv_heads = t->Hkv;
   pa.head_bytes = (int32_t)hb;
   pa.elem_bytes = t->esz;
-  HIP_TRY(t, launch_place_rows(pa, t->L, st));
+  if (t->positional) {
+    // every live row at its position in the pool, then the T1 rows again into the temporary area
+    PlaceArgs pp = pa;
+    pp.rows = t->rowspace();
+    HIP_TRY(t, launch_place_rows(pp, t->L, st));
+    pa.codes = (const uint32_t*)d_codes + codes.size();
+    if (nt1 > 0) HIP_TRY(t, launch_place_rows(pa, t->L, st));
+  } else {
+    HIP_TRY(t, launch_place_rows(pa, t->L, st));
+  }
   // T1 rows also go to their home in pinned host memory
   if (nt1 > 0) {
     const size_t width = (size_t)nt1 * hb;
@@ -456,7 +482,9 @@ static int append_check(tkv* t, const void* k, const void* v) {
   if (!k || !v) return tkv_fail(t, TKV_EINVAL, "k/v is NULL");
   if (misaligned(k) || misaligned(v)) return tkv_fail(t, TKV_EINVAL, "k/v not 16-byte aligned");
   if (t->n >= t->nmax) return tkv_fail(t, TKV_ECAPACITY, "max_tokens (%d) reached", t->nmax);
-  if (t->shared_hbm) {
+  if (t->positional) {
+    // every position has its slot
+  } else if (t->shared_hbm) {
     if ((int)t->free0[0].size() < t->B) return tkv_fail(t, TKV_ECAPACITY, "shared T0 pool full: reassign first");
   } else {
     for (int b = 0; b < t->B; ++b)
@@ -465,8 +493,13 @@ static int append_check(tkv* t, const void* k, const void* v) {
   return TKV_OK;
 }
 
-// T0 slot of each sequence's new row (shared pool: the last B free slots).
+// T0 slot of each sequence's new row (shared pool: the last B free slots;
+// positional staging: its position).
 static void append_slots(tkv* t, int32_t* slot) {
+  if (t->positional) {
+    for (int b = 0; b < t->B; ++b) slot[b] = t->n;
+    return;
+  }
   for (int b = 0; b < t->B; ++b)
     slot[b] = t->free_list(b)[t->free_list(b).size() - 1 - (t->shared_hbm ? b : 0)];
 }
@@ -475,7 +508,7 @@ static void append_slots(tkv* t, int32_t* slot) {
 static void append_commit(tkv* t, const int32_t* slot) {
   t->score_pending = false;
   for (int b = 0; b < t->B; ++b) {
-    t->free_list(b).pop_back();  // shared: the B slots taken, from the back
+    if (!t->positional) t->free_list(b).pop_back();  // shared: the B slots taken, from the back
     const size_t off = (size_t)b * t->nmax + t->n;
     t->h_tier[off] = TKV_T0;
     t->h_loc[off] = (uint32_t)slot[b];
@@ -970,7 +1003,7 @@ static int read_t2_impl(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, int8_
   }
   const size_t at = (size_t)seq * t->nmax + pos;
   if (t->h_tier[at] != TKV_T2) return tkv_fail(t, TKV_ESTATE, "position %d is not in T2", pos);
-  const uint32_t idx = t->h_loc[at] - (uint32_t)(t->cap0 + t->cap1);
+  const uint32_t idx = t->positional ? t->h_aidx[at] : t->h_loc[at] - (uint32_t)(t->cap0 + t->cap1);
   for (int which = 0; which < 2; ++which) {
     for (int h = 0; h < t->Hkv; ++h)
       std::memcpy((which ? v_codes : k_codes) + (size_t)h * t->D,

@@ -98,8 +98,16 @@ __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const Qua
     }
     codes[(((int64_t)l * a.kv_heads + h) * a.out.rows + op.dst) * d + j] = code;
     if (op.stage != kNoLoc) {
-      void* st = which ? (void*)a.rows.stage_v : (void*)a.rows.stage_k;
-      store_val(st, stage_elem(a.rows, l, op.b, h, op.stage, d) + j, c * scale, a.elem_bytes);
+      if (op.stage < (uint32_t)a.rows.cap0) {
+        void* pl = which ? (void*)a.rows.pool_v : (void*)a.rows.pool_k;
+        const int64_t at = (int64_t)l * a.rows.pool_lstride + (int64_t)op.b * a.rows.pool_bstride +
+                           (int64_t)h * a.rows.pool_hstride + (int64_t)op.stage * d;
+        store_val(pl, at + j, c * scale, a.elem_bytes);
+      } else {
+        void* st = which ? (void*)a.rows.stage_v : (void*)a.rows.stage_k;
+        store_val(st, stage_elem(a.rows, l, op.b, h, op.stage - (uint32_t)a.rows.cap0, d) + j, c * scale,
+                  a.elem_bytes);
+      }
     }
   }
   for (int k = threadIdx.x; k < a.sh; k += 256)

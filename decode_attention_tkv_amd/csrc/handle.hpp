@@ -165,6 +165,12 @@ struct tkv {
   std::vector<int32_t> nlive;                 // [B] live rows
   std::vector<std::vector<int32_t>> free0;    // [B] free T0 slots (back = next to use); [1] when shared
   bool shared_hbm = false;                    // one T0 slot space and budget for the batch
+  // Positional resident staging: every live row, whatever its tier, sits in
+  // the pool at its own position (location code = position), so the pass
+  // reads each region in order and a reassignment moves no row inside HBM.
+  // T1/T2 rows keep their pinned homes; h_aidx holds their arena index.
+  bool positional = false;
+  std::vector<uint32_t> h_aidx;               // [B][nmax] (positional only)
   std::vector<int32_t>& free_list(int b) { return free0[shared_hbm ? 0 : b]; }
   std::vector<uint8_t> h_tier;                // [B][nmax]
   std::vector<uint32_t> h_loc;                // [B][nmax]

@@ -255,7 +255,15 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
     vac1.assign(t->t1_owner[b].size(), 0);
     vac2.assign(t->t2_owner[b].size(), 0);
     std::vector<uint32_t> freed;
+    uint32_t* ai = t->positional ? &t->h_aidx[b * nmax] : nullptr;
     auto source = [&](uint32_t pos, uint8_t old) -> Move {
+      if (t->positional) {
+        // the row's values are at its own slot whatever its tier; a T1/T2
+        // row's departure leaves a hole in its arena
+        if (old == TKV_T1) vac1[ai[pos]] = 1;
+        if (old == TKV_T2) vac2[ai[pos]] = 1;
+        return {pos, kFromPool, pos};
+      }
       if (old == TKV_T0) return {pos, kFromPool, lc[pos]};
       if (old == TKV_T1) {
         vac1[lc[pos] - c1] = 1;
@@ -268,7 +276,7 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
       for (int k = 0; k < count; ++k) {
         const tkv_delta& d = list[k];
         const Move mv = source(d.pos, d.old_tier);
-        if (d.old_tier == TKV_T0) freed.push_back(mv.idx);
+        if (d.old_tier == TKV_T0 && !t->positional) freed.push_back(mv.idx);
         switch (d.new_tier) {
           case TKV_T0: sp.promo.push_back(mv); break;
           case TKV_T1: sp.ent1.push_back(mv); break;
@@ -298,6 +306,7 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
     uint32_t* lc = &t->h_loc[b * nmax];
     auto& own1 = t->t1_owner[b];
     auto& own2 = t->t2_owner[b];
+    if (t->positional) sp.promo.clear();  // promoted rows stay where they are
     for (const Move& mv : sp.promo) {
       if (t->free_list(b).empty()) return tkv_fail(t, TKV_ECAPACITY, "T0 pool full while promoting");
       const uint32_t slot = (uint32_t)t->free_list(b).back();
@@ -309,11 +318,20 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
     // arenas: compaction, then the entrants at the end
     compact(own1, vac1s[b], &sp.m1, &sp.mov1);
     compact(own2, vac2s[b], &sp.m2, &sp.mov2);
+    uint32_t* ai = t->positional ? &t->h_aidx[b * nmax] : nullptr;
     for (auto& mv : sp.mov1) {
+      if (ai) {
+        ai[own1[mv.second]] = mv.second;
+        continue;
+      }
       lc[own1[mv.second]] = c1 + mv.second;
       upd.push_back({b, (uint32_t)own1[mv.second], c1 + mv.second});
     }
     for (auto& mv : sp.mov2) {
+      if (ai) {
+        ai[own2[mv.second]] = mv.second;
+        continue;
+      }
       lc[own2[mv.second]] = c2 + mv.second;
       upd.push_back({b, (uint32_t)own2[mv.second], c2 + mv.second});
     }
@@ -321,11 +339,19 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
     if (sp.m2 + sp.ent2.size() > (size_t)t->cap2) return tkv_fail(t, TKV_ECAPACITY, "T2 arena full");
     for (size_t e = 0; e < sp.ent1.size(); ++e) {
       own1.push_back((int32_t)sp.ent1[e].pos);
+      if (ai) {
+        ai[sp.ent1[e].pos] = sp.m1 + (uint32_t)e;
+        continue;
+      }
       lc[sp.ent1[e].pos] = c1 + sp.m1 + (uint32_t)e;
       upd.push_back({b, sp.ent1[e].pos, c1 + sp.m1 + (uint32_t)e});
     }
     for (size_t e = 0; e < sp.ent2.size(); ++e) {
       own2.push_back((int32_t)sp.ent2[e].pos);
+      if (ai) {
+        ai[sp.ent2[e].pos] = sp.m2 + (uint32_t)e;
+        continue;
+      }
       lc[sp.ent2[e].pos] = c2 + sp.m2 + (uint32_t)e;
       upd.push_back({b, sp.ent2[e].pos, c2 + sp.m2 + (uint32_t)e});
     }
@@ -377,7 +403,7 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
     // phase 2a: promotions into T0 slots, compaction inside the resident staging
     for (size_t p = 0; p < sp.promo.size(); ++p)
       ops2a.push_back({kAreaPackOut, kAreaPool, (uint16_t)b, (uint32_t)(E1 + E2 + sp.poff + p), sp.promo_slot[p]});
-    if (t->resident) {
+    if (t->resident && !t->positional) {
       for (auto& mv : sp.mov1) ops2a.push_back({kAreaStage, kAreaStage, (uint16_t)b, mv.first, mv.second});
       for (auto& mv : sp.mov2)
         ops2a.push_back({kAreaStage, kAreaStage, (uint16_t)b, (uint32_t)t->cap1 + mv.first,
@@ -386,9 +412,12 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
       for (size_t e = 0; e < sp.ent1.size(); ++e)
         ops2b.push_back({kAreaPackOut, kAreaStage, (uint16_t)b, (uint32_t)(sp.e1off + e), sp.m1 + (uint32_t)e});
     }
+    // the dequantised values go to the row's location: its own slot
+    // (positional), its new staging place (resident), or nowhere (stream)
     for (size_t e = 0; e < sp.ent2.size(); ++e)
       q2.push_back({(uint16_t)b, (uint32_t)(E1 + sp.e2off + e), (uint32_t)(sp.e2off + e),
-                    t->resident ? (uint32_t)t->cap1 + sp.m2 + (uint32_t)e : kNoLoc});
+                    t->positional ? sp.ent2[e].pos
+                    : t->resident ? c2 + sp.m2 + (uint32_t)e : kNoLoc});
   }
 
   // ---- stream mode: host-resident sources packed and sent

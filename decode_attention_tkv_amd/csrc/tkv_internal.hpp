@@ -223,7 +223,8 @@ struct QuantOp {
   uint16_t b;
   uint32_t src;    // F row
   uint32_t dst;    // QPack row
-  uint32_t stage;  // resident staging index that receives the dequantised values, or kNoLoc
+  uint32_t stage;  // location code that receives the dequantised values (pool slot, or cap0 +
+                   // staging index), or kNoLoc
 };
 
 struct QuantArgs {

@@ -74,8 +74,10 @@ typedef struct {
 
 typedef struct {
   double t2_ratio;        /* share of positions held 8-bit on the host (T2); 0 = no T2 */
-  int32_t staging_layers; /* S: HBM staging slots for T1/T2 rows.  0 or >= layers: every
-                             layer keeps its staging ("resident": only changed rows move).
+  int32_t staging_layers; /* S: HBM staging slots for T1/T2 rows.  0 or >= layers:
+                             "resident": every live row stays in HBM, at its own position
+                             (with TKV_FLAG_SHARED_HBM: T0 slots plus a staging mirror of
+                             T1/T2), and only changed rows cross to or from the host.
                              2..layers-1: "stream": each step copies a layer's T1/T2 rows
                              from pinned host memory into slot (layer mod S), one layer
                              ahead of the attention that reads it. */
@@ -181,7 +183,8 @@ int tkv_prefill_scored(tkv_t* t, const void* k, const void* v, const void* q, in
  * [layers][batch][kv_heads][head_dim].  The new row enters T0 with score 0.
  * The copy out of k, v is enqueued on `stream` by this call, so the caller may
  * reuse them in stream order right after it returns.
- * TKV_ECAPACITY at max_tokens or when the T0 pool is full (reassign first). */
+ * TKV_ECAPACITY at max_tokens, or (stream staging, or a batch-shared budget)
+ * when the T0 pool is full (reassign first). */
 int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream);
 
 /* Attention of layers [layer_begin, layer_begin + layer_count) of the

@@ -136,12 +136,14 @@ def test_decode_step_state_and_arguments():
 
 
 def test_decode_step_capacity():
-    """The append's capacity errors, through the single call: the T0 pool runs
-    full without reassignments, then max_tokens is reached."""
+    """The append's capacity errors, through the single call: the T0 pool
+    (stream staging) runs full without reassignments, then max_tokens is
+    reached."""
     import decode_attention_tkv_amd as tkv
-    w = tkvsynth.CONFIGS["tiny"].replace(prefill=100, steps=60, hbm_ratio=0.3, delta=4, prompt=8, recent=8)
+    w = tkvsynth.CONFIGS["tiny"].replace(layers=3, prefill=100, steps=60, hbm_ratio=0.3, delta=4, prompt=8,
+                                         recent=8)
     inp = Inputs(w)
-    c = tkv.TieredKV.for_workload(w)
+    c = tkv.TieredKV.for_workload(w, staging_layers=2)
     c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
     out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     full_at = None

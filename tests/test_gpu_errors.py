@@ -74,12 +74,12 @@ def test_max_tokens_reached():
 
 
 def test_t0_pool_full_until_reassigned():
-    """Without reassignment the T0 pool fills up (appended rows are T0); a
-    reassignment frees it and the run goes on."""
+    """Stream staging: without reassignment the T0 pool fills up (appended
+    rows are T0); a reassignment frees it and the run goes on."""
     import decode_attention_tkv_amd as tkv
-    w = _tiny(prefill=100, steps=60, hbm_ratio=0.3, delta=4, prompt=8, recent=8)
+    w = _tiny(layers=3, prefill=100, steps=60, hbm_ratio=0.3, delta=4, prompt=8, recent=8)
     inp = Inputs(w)
-    c = _cache(w)
+    c = _cache(w, staging_layers=2)
     c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
     out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     full_at = None
@@ -98,6 +98,22 @@ def test_t0_pool_full_until_reassigned():
     c.append(to_device(k, w.dtype), to_device(v, w.dtype))
     c.decode_attn(to_device(inp.q[full_at], w.dtype), out)
     assert np.isfinite(out.cpu().numpy()).all()
+    c.close()
+
+
+def test_resident_pool_holds_every_position():
+    """Resident staging keeps every row at its own position, so appends never
+    wait for a reassignment to free T0 slots."""
+    w = _tiny(prefill=100, steps=60, hbm_ratio=0.3, delta=4, prompt=8, recent=8)
+    inp = Inputs(w)
+    c = _cache(w)
+    c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
+    out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    for t in range(w.steps):
+        k, v = inp.step_kv(t)
+        c.append(to_device(k, w.dtype), to_device(v, w.dtype))
+        c.decode_attn(to_device(inp.q[t], w.dtype), out)
+    assert c.stats()["n_tokens"] == w.n_final
     c.close()
 
 
