@@ -30,6 +30,12 @@
 //   k_score       one thread per live row: adds the layers' sums (layer
 //                 order) times 1/(L*H) to s.  The same code normally runs in
 //                 the next step's append launch, saving a launch per step.
+//   Deferred Eq. 1 (bf16 grouped-query heads over resident staging): no
+//                 logits are stored; the next step's k_attn_chunk recomputes
+//                 the step's weights in the padded rows of its logits tile and
+//                 writes their sum over each group's heads, and its
+//                 k_finalize folds those sums into s (k_fold64 when a
+//                 score-only pass flushes a step).
 //                 No atomics anywhere, so every result is bitwise
 //                 reproducible.
 #include <hip/hip_ext.h>
@@ -327,11 +333,11 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
   __syncthreads();
 
   float mc[G];
-  // deferred Eq. 1: rows of the previous step (its new row came after it)
-  const int prev = DEF ? a.prev_mode : 0;
-  const int nprev = prev == 1 ? nl - 1 : nl;
-  (void)nprev;
   if constexpr (MK) {
+    // deferred Eq. 1 (DEF): prev_mode 1, the previous step's rows are the live
+    // indices below the new row's; 2, score only over every live row
+    const int prev = DEF ? a.prev_mode : 0;
+    const int nprev = prev == 1 ? nl - 1 : nl;
     // ---- phase 1 on the matrix cores: Z[16 heads x 16 rows] += Q[16 x 32] K^T[32 x 16],
     // D/32 steps per tile of 16 rows (v_mfma_f32_16x16x32_bf16).  Lane l feeds
     // head / row (l % 16) and the 8 elements 8*(l/16) of each 32-wide slice;

@@ -17,6 +17,11 @@
 //   phase 2b  rows entering T1: F -> staging; rows entering T2: quantised
 //             from F on the GPU (codes + scale out, dequantised values into
 //             the staging).
+// Positional resident staging (every live row at its own position in the
+// pool) moves no row inside HBM: phase 1 gathers only the rows entering T1
+// or T2, for their write-back, and T2 entrants get their dequantised values
+// in their own slots; phases 2a and 2b are empty.  T1/T2 rows keep a
+// host-side arena index per position.
 // Rows entering T1/T2 reach their pinned home through one write-back copy per
 // pack on a stream of their own; a host job (never waited for by the GPU)
 // compacts the arenas and files them.  Every area is head-major.
