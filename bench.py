@@ -59,13 +59,16 @@ def load_inputs(w, steps, torch):
     return k0, v0, kn, vn, q
 
 
+CHUNK = 0  # split-K rows per work-group (0: the library's default for the shape)
+
+
 def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kernels=True, sync_reassign=False):
     """Prefill, `warmup` untimed steps, then `steps` timed steps.  Returns
     (seconds, stats before, stats after).  sync_reassign: drain the stream
     before and after every reassignment of the timed steps and put the
     per-call wall times (ms) under after["reassign_synced_ms"]."""
     k0, v0, kn, vn, q = inputs
-    c = tkv.TieredKV.for_workload(w, staging_layers=staging_layers, time_kernels=time_kernels)
+    c = tkv.TieredKV.for_workload(w, staging_layers=staging_layers, time_kernels=time_kernels, chunk=CHUNK)
     c.prefill(k0, v0)
     h = c.h
     out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
@@ -275,6 +278,7 @@ def main():
     ap.add_argument("--steps", type=int, default=448)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="7b")
+    ap.add_argument("--chunk", type=int, default=0, help="split-K rows per work-group: 128, 256 or 512 (0: default)")
     ap.add_argument("--stream-steps", type=int, default=64, help="timed steps of the stream-staging leg (0: skip)")
     ap.add_argument("--cpu-steps", type=int, default=192,
                     help="steps of the CPU oracle baseline and of the parity check beside it (0: skip)")
@@ -289,6 +293,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc runs of --pmc-probe")
     args = ap.parse_args()
+    global CHUNK
+    CHUNK = args.chunk
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
