@@ -366,7 +366,20 @@ static int prefill_impl(tkv_t* t, const void* k, const void* v, int32_t n_tokens
   void* tmp_v = nullptr;
   const size_t hb = (size_t)t->D * t->esz;  // bytes of one head's row
   size_t src_pitch = (size_t)t->capS * hb;
-  if ((!t->resident || t->positional) && nt1 > 0) {
+  // positional staging: when the T1 rows are one run of positions (the first
+  // placement ranks candidates by position, so they normally are) their
+  // pinned home fills straight from the pool
+  int t1_first = -1;
+  if (t->positional && nt1 > 0) {
+    int lo = n0, hi = -1;
+    for (int p = 0; p < n0; ++p)
+      if (first[p] == TKV_T1) {
+        lo = std::min(lo, p);
+        hi = std::max(hi, p);
+      }
+    if (hi - lo + 1 == nt1) t1_first = lo;
+  }
+  if ((!t->resident || (t->positional && t1_first < 0)) && nt1 > 0) {
     const size_t bytes = (size_t)t->L * t->B * t->cap1 * t->row_bytes;
     HIP_TRY(t, hipMallocAsync(&tmp_k, bytes, st));
     HIP_TRY(t, hipMallocAsync(&tmp_v, bytes, st));
@@ -386,13 +399,22 @@ static int prefill_impl(tkv_t* t, const void* k, const void* v, int32_t n_tokens
   pa.kv_heads = t->Hkv;
   pa.head_bytes = (int32_t)hb;
   pa.elem_bytes = t->esz;
+  const void* arena_src_k = pa.rows.stage_k;
+  const void* arena_src_v = pa.rows.stage_v;
   if (t->positional) {
-    // every live row at its position in the pool, then the T1 rows again into the temporary area
+    // every live row at its position in the pool; the T1 rows also into the
+    // temporary area unless they are one run of positions in the pool
     PlaceArgs pp = pa;
     pp.rows = t->rowspace();
     HIP_TRY(t, launch_place_rows(pp, t->L, st));
-    pa.codes = (const uint32_t*)d_codes + codes.size();
-    if (nt1 > 0) HIP_TRY(t, launch_place_rows(pa, t->L, st));
+    if (nt1 > 0 && t1_first >= 0) {
+      arena_src_k = (const char*)t->pool_k + (size_t)t1_first * hb;
+      arena_src_v = (const char*)t->pool_v + (size_t)t1_first * hb;
+      src_pitch = (size_t)t->cap0 * hb;
+    } else if (nt1 > 0) {
+      pa.codes = (const uint32_t*)d_codes + codes.size();
+      HIP_TRY(t, launch_place_rows(pa, t->L, st));
+    }
   } else {
     HIP_TRY(t, launch_place_rows(pa, t->L, st));
   }
@@ -401,7 +423,7 @@ static int prefill_impl(tkv_t* t, const void* k, const void* v, int32_t n_tokens
     const size_t width = (size_t)nt1 * hb;
     for (int which = 0; which < 2; ++which) {
       HIP_TRY(t, hipMemcpy2DAsync(which ? t->arena1_v : t->arena1_k, (size_t)t->cap1 * hb,
-                                  which ? pa.rows.stage_v : pa.rows.stage_k, src_pitch, width,
+                                  which ? arena_src_v : arena_src_k, src_pitch, width,
                                   (size_t)t->L * t->B * t->Hkv, hipMemcpyDeviceToHost, st));
     }
     t->st.d2h_bytes += 2 * (int64_t)width * t->L * t->B * t->Hkv;
