@@ -188,3 +188,43 @@ def test_7b_shape_with_reassignment():
     two reassignments."""
     w = tkvsynth.CONFIGS["7b"].replace(layers=8, steps=129)
     run_parity(w, Inputs(w), w.steps, check_every=16)
+
+
+@pytest.mark.parametrize("name", ["tiny", "32b_t2"])
+def test_rows_keep_their_values_through_reassignments(name):
+    """Resident staging keeps every live row at its own position: after each
+    reassignment every live row reads back bit for bit as the oracle holds it
+    (its appended values, or its dequantised values once it has entered T2)."""
+    if name == "tiny":
+        w = tkvsynth.CONFIGS["tiny"].replace(steps=48, delta=16)
+    else:  # bf16 grouped-query heads with an 8-bit tier
+        w = tkvsynth.CONFIGS["32b_t2"].replace(layers=2, batch=2, prefill=300, steps=64, delta=32, prompt=40,
+                                               recent=32)
+    inp = Inputs(w)
+    c = _new(w)
+    c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
+    o = make_oracle(w, inp)
+    out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    checked = 0
+    for t in range(w.steps):
+        k, v = inp.step_kv(t)
+        c.decode_step(to_device(k, w.dtype), to_device(v, w.dtype), to_device(inp.q[t], w.dtype), out)
+        o.append(w.values(k), w.values(v))
+        o.attend(w.values(inp.q[t]))
+        if (t + 1) % w.delta:
+            continue
+        g_s = c.read_scores()[:, : o.n]
+        c.reassign()
+        tiers, _ = o.reassign(rank_scores=g_s)
+        assert np.array_equal(c.read_tiers()[:, : o.n], tiers)
+        for b in range(w.batch):
+            for pos in range(o.n):
+                if tiers[b, pos] > 2:
+                    continue
+                for l in range(w.layers):
+                    gk, gv = c.read_kv(l, b, pos)
+                    assert np.array_equal(w.values(gk), o.K[l, b, pos])
+                    assert np.array_equal(w.values(gv), o.V[l, b, pos])
+                    checked += 1
+    c.close()
+    assert checked > 0
