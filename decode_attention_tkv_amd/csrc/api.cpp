@@ -55,6 +55,7 @@ static int host_alloc(tkv* t, void** p, size_t bytes) {
 static void release(tkv* t) {
   if (t->arena_job.valid()) (void)t->arena_job.get();
   if (t->side) (void)hipStreamSynchronize(t->side);
+  if (t->side_v) (void)hipStreamSynchronize(t->side_v);
   if (t->wb) (void)hipStreamSynchronize(t->wb);
   for (void* p : t->device_allocs) (void)hipFree(p);
   for (void* p : t->host_allocs) (void)hipHostFree(p);
@@ -69,18 +70,22 @@ static void release(tkv* t) {
   if (t->ev_pack) (void)hipEventDestroy(t->ev_pack);
   t->ev_pack = nullptr;
   for (hipEvent_t e : t->ev_h2d) (void)hipEventDestroy(e);
+  for (hipEvent_t e : t->ev_h2d_v) (void)hipEventDestroy(e);
   for (hipEvent_t e : t->ev_comp) (void)hipEventDestroy(e);
   if (t->ev_arena) (void)hipEventDestroy(t->ev_arena);
   if (t->side) (void)hipStreamDestroy(t->side);
+  if (t->side_v) (void)hipStreamDestroy(t->side_v);
   if (t->wb) (void)hipStreamDestroy(t->wb);
   if (t->ev_gathered) (void)hipEventDestroy(t->ev_gathered);
   t->wb = nullptr;
   t->ev_gathered = nullptr;
   t->d_ops = t->h_ops = t->h_pack_in = nullptr;
   t->ev_h2d.clear();
+  t->ev_h2d_v.clear();
   t->ev_comp.clear();
   t->ev_arena = nullptr;
   t->side = nullptr;
+  t->side_v = nullptr;
   for (hipEvent_t e : t->ev_free) (void)hipEventDestroy(e);
   for (auto& pr : t->ev_pending) {
     (void)hipEventDestroy(pr.first);
@@ -236,13 +241,16 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   }
   if (rc == TKV_OK) {
     hipError_t e = hipStreamCreateWithFlags(&t->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&t->side_v, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&t->wb, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_gathered, hipEventDisableTiming);
     t->ev_h2d.assign(t->S, nullptr);
+    t->ev_h2d_v.assign(t->S, nullptr);
     t->ev_comp.assign(t->S, nullptr);
     t->comp_recorded.assign(t->S, 0);
     for (int i = 0; i < t->S && e == hipSuccess; ++i) {
       e = hipEventCreateWithFlags(&t->ev_h2d[i], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_h2d_v[i], hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_comp[i], hipEventDisableTiming);
     }
     if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_arena, hipEventDisableTiming);
@@ -729,7 +737,8 @@ static int flush_deferred(tkv* t, hipStream_t st) {
 }
 
 // Stream mode: copy layers' T1 rows from the pinned arena into their staging
-// slot (layer mod S) on the side stream, up to layer `upto`, each after the
+// slot (layer mod S) on the side streams (K rows and 8-bit rows on one, V rows
+// on the other), up to layer `upto`, each after the
 // attention that last read that slot.
 static int issue_prefetch(tkv* t, int upto) {
   if (t->arena_job.valid()) {
@@ -738,6 +747,7 @@ static int issue_prefetch(tkv* t, int upto) {
   }
   if (t->arena_pending) {
     HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_arena, 0));
+    HIP_TRY(t, hipStreamWaitEvent(t->side_v, t->ev_arena, 0));
     t->arena_pending = false;
   }
   size_t n1max = 0, n2max = 0;
@@ -747,7 +757,10 @@ static int issue_prefetch(tkv* t, int upto) {
   }
   for (; t->next_issue <= upto && t->next_issue < t->L; ++t->next_issue) {
     const int x = t->next_issue, slot = x % t->S;
-    if (t->comp_recorded[slot]) HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_comp[slot], 0));
+    if (t->comp_recorded[slot]) {
+      HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_comp[slot], 0));
+      HIP_TRY(t, hipStreamWaitEvent(t->side_v, t->ev_comp[slot], 0));
+    }
     if (n1max > 0) {
       const size_t hb = (size_t)t->D * t->esz;
       const size_t width = n1max * hb;
@@ -755,7 +768,7 @@ static int issue_prefetch(tkv* t, int upto) {
         char* dst = (char*)(which ? t->stage_v : t->stage_k) + (size_t)slot * t->B * t->capS * t->row_bytes;
         const char* src = (const char*)(which ? t->arena1_v : t->arena1_k) + (size_t)x * t->B * t->cap1 * t->row_bytes;
         HIP_TRY(t, hipMemcpy2DAsync(dst, (size_t)t->capS * hb, src, (size_t)t->cap1 * hb, width,
-                                    (size_t)t->B * t->Hkv, hipMemcpyHostToDevice, t->side));
+                                    (size_t)t->B * t->Hkv, hipMemcpyHostToDevice, which ? t->side_v : t->side));
       }
       t->st.h2d_bytes += 2 * (int64_t)width * t->B * t->Hkv;
     }
@@ -777,6 +790,7 @@ static int issue_prefetch(tkv* t, int upto) {
       t->st.h2d_bytes += 2 * (int64_t)(cw * t->B * t->Hkv + n2max * t->sh * 4 * t->B);
     }
     HIP_TRY(t, hipEventRecord(t->ev_h2d[slot], t->side));
+    HIP_TRY(t, hipEventRecord(t->ev_h2d_v[slot], t->side_v));
   }
   return TKV_OK;
 }
@@ -833,6 +847,7 @@ static int decode_attn_impl(tkv_t* t, int32_t layer_begin, int32_t layer_count, 
       int rc = issue_prefetch(t, l + t->S - 1);
       if (rc) return rc;
       HIP_TRY(t, hipStreamWaitEvent(st, t->ev_h2d[slot], 0));
+      HIP_TRY(t, hipStreamWaitEvent(st, t->ev_h2d_v[slot], 0));
       rc = launch_layers(t, l, 1, (const char*)q + i * q_layer, out + i * o_layer, max_live, st);
       if (rc) return rc;
       HIP_TRY(t, hipEventRecord(t->ev_comp[slot], st));
@@ -892,6 +907,7 @@ static int stats_impl(tkv_t* t, tkv_stats_t* out) {
     if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
   }
   HIP_TRY(t, hipStreamSynchronize(t->side));
+  HIP_TRY(t, hipStreamSynchronize(t->side_v));
   HIP_TRY(t, hipStreamSynchronize(t->wb));
   int rc = drain_events(t);
   if (rc) return rc;

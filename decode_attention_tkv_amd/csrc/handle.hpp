@@ -183,10 +183,12 @@ struct tkv {
   tkv_delta* h_demote = nullptr;   // [B][nmax]
 
   // ---- streams and events
-  hipStream_t side = nullptr;           // host->device row traffic of the stream mode
+  hipStream_t side = nullptr;           // host->device row traffic of the stream mode (K rows, 8-bit rows)
+  hipStream_t side_v = nullptr;         // the same for V rows: two copy queues overlap their gaps
   hipStream_t wb = nullptr;             // device->host write-back of rows entering T1
   hipEvent_t ev_gathered = nullptr;     // rows entering T1 are in the device pack
-  std::vector<hipEvent_t> ev_h2d;       // [S] staging slot filled
+  std::vector<hipEvent_t> ev_h2d;       // [S] staging slot filled (side)
+  std::vector<hipEvent_t> ev_h2d_v;     // [S] its V rows filled (side_v)
   std::vector<hipEvent_t> ev_comp;      // [S] attention done reading the slot
   std::vector<char> comp_recorded;      // [S]
   hipEvent_t ev_arena = nullptr;        // host arena writes of the last reassignment done
