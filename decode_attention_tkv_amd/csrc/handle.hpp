@@ -184,7 +184,7 @@ struct tkv {
 
   // ---- streams and events
   hipStream_t side = nullptr;           // host->device row traffic of the stream mode (K rows, 8-bit rows)
-  hipStream_t side_v = nullptr;         // the same for V rows: two copy queues overlap their gaps
+  hipStream_t side_v = nullptr;         // the same for V rows: two copy queues overlap their gaps (stream staging only)
   hipStream_t wb = nullptr;             // device->host write-back of rows entering T1
   hipEvent_t ev_gathered = nullptr;     // rows entering T1 are in the device pack
   std::vector<hipEvent_t> ev_h2d;       // [S] staging slot filled (side)

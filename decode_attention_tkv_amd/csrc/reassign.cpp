@@ -175,7 +175,7 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
     if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
   }
   HIP_TRY(t, hipStreamSynchronize(t->side));
-  HIP_TRY(t, hipStreamSynchronize(t->side_v));
+  if (t->side_v) HIP_TRY(t, hipStreamSynchronize(t->side_v));
   HIP_TRY(t, hipEventSynchronize(t->ev_arena));
 
   // ---- cut points from the host mirror of the tiers
