@@ -18,10 +18,10 @@ pytestmark = pytest.mark.gpu
 TOL = {"bf16": 5e-3, "f32": 1e-5}
 
 
-def _run(w, inputs, steps, hbm=None, chunk=0, groups=None, check=None):
+def _run(w, inputs, steps, hbm=None, chunk=0, groups=None, check=None, staging_layers=0):
     import decode_attention_tkv_amd as tkv
     kw = {} if hbm is None else {"hbm_ratio": hbm}
-    c = tkv.TieredKV.for_workload(w, chunk=chunk, **kw)
+    c = tkv.TieredKV.for_workload(w, chunk=chunk, staging_layers=staging_layers, **kw)
     c.prefill(to_device(inputs.k0, w.dtype), to_device(inputs.v0, w.dtype))
     outs = []
     out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
@@ -95,6 +95,18 @@ def test_chunk_sizes_and_layer_groups(chunk):
     assert all(np.array_equal(x, y) for x, y in zip(a[0], b[0]))
     assert np.array_equal(a[1], b[1])
     _compare(w, a, _oracle(w, inp, 3), 3)
+
+
+def test_layer_groups_stream_staging():
+    # stream staging prefetches each layer's T1 rows one layer ahead, across
+    # the caller's layer groups; outputs equal the resident single call's bit
+    # for bit (the reduction follows logical position, whatever the staging)
+    w = tkvsynth.CONFIGS["14b"].replace(layers=6, batch=2, prefill=1000, steps=3, hbm_ratio=0.5)
+    inp = Inputs(w)
+    a = _run(w, inp, 3)
+    b = _run(w, inp, 3, groups=[1, 2, 3], staging_layers=2)
+    assert all(np.array_equal(x, y) for x, y in zip(a[0], b[0]))
+    _compare(w, b, _oracle(w, inp, 3), 3)
 
 
 @pytest.mark.parametrize("name", ["7b", "14b", "32b", "70b"])
