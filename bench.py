@@ -60,16 +60,26 @@ def load_inputs(w, steps, torch):
 
 
 CHUNK = 0  # split-K rows per work-group (0: the library's default for the shape)
+EXTRA_FLAGS = 0  # TKV_FLAG_* added to every handle (e.g. the vector pass for grouped-query heads)
 
 
-def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kernels=True, sync_reassign=False):
+def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kernels=True, sync_reassign=False,
+               samples=(), scored_prefill=None):
     """Prefill, `warmup` untimed steps, then `steps` timed steps.  Returns
     (seconds, stats before, stats after).  sync_reassign: drain the stream
     before and after every reassignment of the timed steps and put the
-    per-call wall times (ms) under after["reassign_synced_ms"]."""
+    per-call wall times (ms) under after["reassign_synced_ms"].  samples:
+    0-based steps whose outputs are copied to the host (a synchronisation
+    each; for untimed runs), under after["samples"]; the last step's output
+    is always under after["last_out"].  scored_prefill: the prompt's queries
+    [L][B][n][Hq][d] to prefill with scores instead of the plain placement."""
     k0, v0, kn, vn, q = inputs
-    c = tkv.TieredKV.for_workload(w, staging_layers=staging_layers, time_kernels=time_kernels, chunk=CHUNK)
-    c.prefill(k0, v0)
+    c = tkv.TieredKV.for_workload(w, staging_layers=staging_layers, time_kernels=time_kernels, chunk=CHUNK,
+                                  extra_flags=EXTRA_FLAGS)
+    if scored_prefill is not None:
+        c.prefill_scored(k0, v0, scored_prefill)
+    else:
+        c.prefill(k0, v0)
     h = c.h
     out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
@@ -80,10 +90,13 @@ def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kern
     qp = [q[t].data_ptr() for t in range(warmup + steps)]
 
     synced = []
+    sampled = {}
 
     def step(t):
         # append + attention of every layer (+ the pending Eq. 1 update) in one call
         rc = lib.tkv_decode_step(h, kp[t], vp[t], qp[t], optr, stream)
+        if rc == 0 and t in samples:
+            sampled[t] = out.cpu().numpy()
         if rc == 0 and (t + 1) % w.delta == 0:
             if sync_reassign and t >= warmup:
                 # the caller's stream only: the write-back of rows entering T1 runs on the
@@ -111,6 +124,8 @@ def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kern
     secs = time.perf_counter() - t0
     after = c.stats()
     after["reassign_synced_ms"] = synced
+    after["samples"] = sampled
+    after["last_out"] = out.cpu().numpy()
     c.close()
     return secs, before, after
 
@@ -272,6 +287,49 @@ def cpu_baseline(w, n_steps, trace=None):
     return res, parity
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_steps_per_s(w, n_steps):
+    """The oracle alone over the first n_steps decode steps (prefill untimed)."""
+    import oracle
+    heavy, u = w.heavy_mask(), w.unit_vector()
+    o = oracle.OracleTKV.for_workload(w)
+    o.prefill(w.values(w.kv(0, 0, w.prefill, heavy, u)), w.values(w.kv(1, 0, w.prefill, heavy, u)))
+    kn = w.values(w.kv(0, w.prefill, n_steps, heavy, u))
+    vn = w.values(w.kv(1, w.prefill, n_steps, heavy, u))
+    q = w.values(w.q(0, n_steps, u))
+    t0 = time.perf_counter()
+    for t in range(n_steps):
+        o.append(kn[:, :, t], vn[:, :, t])
+        o.attend(q[t])
+        if (t + 1) % w.delta == 0:
+            o.reassign()
+    return n_steps / (time.perf_counter() - t0)
+
+
+def single_thread_oracle(name, n_steps, timeout=120):
+    """oracle_steps_per_s in a child process limited to one OpenMP thread (the
+    child touches no GPU)."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-only", name, str(n_steps)],
+                           env=env, capture_output=True, text=True, timeout=timeout)
+        if r.returncode != 0:
+            return {"error": (r.stderr or "")[-300:]}
+        return json.loads(r.stdout.strip().splitlines()[-1])
+    except Exception as e:  # reported, never fatal to the bench line
+        return {"error": str(e)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -279,6 +337,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="7b")
     ap.add_argument("--chunk", type=int, default=0, help="split-K rows per work-group: 128, 256 or 512 (0: default)")
+    ap.add_argument("--vector-pass", action="store_true",
+                    help="grouped-query bf16 heads on the vector units instead of the matrix cores")
     ap.add_argument("--stream-steps", type=int, default=64, help="timed steps of the stream-staging leg (0: skip)")
     ap.add_argument("--cpu-steps", type=int, default=192,
                     help="steps of the CPU oracle baseline and of the parity check beside it (0: skip)")
@@ -292,9 +352,24 @@ def main():
                     help="short run for counter collection: 8 + 24 steps, then one 1 GiB device copy")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc runs of --pmc-probe")
+    ap.add_argument("--no-full-run", dest="full_run", action="store_false",
+                    help="skip the legs over the workload's whole decode (every reassignment)")
+    ap.add_argument("--single-thread-steps", type=int, default=12,
+                    help="decode steps of the one-thread oracle runs (tiny: its whole decode; 0: skip)")
+    ap.add_argument("--oracle-only", nargs=2, metavar=("WORKLOAD", "STEPS"),
+                    help="(internal) time the oracle alone on the host and print one JSON line")
     args = ap.parse_args()
-    global CHUNK
+    if args.oracle_only:
+        import tkvsynth
+        name, n = args.oracle_only[0], int(args.oracle_only[1])
+        w = tkvsynth.CONFIGS[name]
+        n = min(n, w.steps)
+        print(json.dumps({"workload": name, "steps": n, "steps_per_s": oracle_steps_per_s(w, n),
+                          "threads": int(os.environ.get("OMP_NUM_THREADS", "0") or 0)}))
+        return
+    global CHUNK, EXTRA_FLAGS
     CHUNK = args.chunk
+    EXTRA_FLAGS = 32 if args.vector_pass else 0  # TKV_FLAG_VECTOR_PASS
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
@@ -364,9 +439,11 @@ def main():
         "step_hbm_gbs": step_gbs,
         "step_hbm_frac": step_gbs / HBM_PEAK_GBS,
         # Host wall time inside tkv_reassign.  The call waits for the tier counts, so it also
-        # covers draining the decode steps still queued on the stream when it was made.
-        "reassign_wall_ms_per_call": (after["reassign_ms"] - before["reassign_ms"])
-        / max(1, after["reassigns"] - before["reassigns"]),
+        # covers draining the decode steps still queued on the stream when it was made.  None
+        # when the timed window holds no reassignment.
+        "reassign_wall_ms_per_call": ((after["reassign_ms"] - before["reassign_ms"])
+                                      / (after["reassigns"] - before["reassigns"])
+                                      if after["reassigns"] > before["reassigns"] else None),
     }
     # The cost of one reassignment on its own: the same run with the stream drained before and
     # after each reassignment call, so the call's wall time is its host work plus its GPU work.
@@ -376,21 +453,90 @@ def main():
                               sync_reassign=True)
         result["reassign_ms_per_call_drained"] = float(np.median(rs["reassign_synced_ms"]))
 
+    # The workload's whole decode (every reassignment of it), whatever --steps is: once timed as
+    # the headline is, once with the stream drained around each reassignment (its cost on its own)
+    # and with outputs sampled for the stream-staging comparison below.
+    full_samples = {}
+    wf = base if base.steps >= w.steps else w
+    # the stream-staging windows (below): the first reassignment (after step delta) mid-window, and
+    # the steady state from the step after it; their last steps are compared with this run's
+    ns = args.stream_steps
+    first_warm, steady_warm = max(0, w.delta - ns // 2), w.delta + 1
+    stream_last = (first_warm + ns - 1, steady_warm + ns - 1) if ns > 0 else ()
+    if args.full_run:
+        print("[bench] full run: %d steps, every reassignment" % wf.steps, file=sys.stderr, flush=True)
+        finputs = inputs if wf is w else load_inputs(wf, wf.steps, torch)
+        fsecs, fb, fa = run_decode(wf, finputs, 0, wf.steps, torch, tkv)
+        fk_ms = fa["attn_kernel_ms"] - fb["attn_kernel_ms"]
+        fkv = fa["attn_kv_bytes"] - fb["attn_kv_bytes"]
+        nre = fa["reassigns"] - fb["reassigns"]
+        result["full_run"] = {
+            "steps": wf.steps, "timed_steps": "1..%d" % wf.steps, "reassignments": int(nre),
+            "steps_per_s": wf.steps / fsecs, "ms_per_step": fsecs / wf.steps * 1e3,
+            "kernel_frac": fkv / (fk_ms / 1e3) / 1e9 / HBM_PEAK_GBS if fk_ms > 0 else None,
+            "step_hbm_frac": fkv / fsecs / 1e9 / HBM_PEAK_GBS,
+            "reassign_ms_per_call_in_stream": (fa["reassign_ms"] - fb["reassign_ms"]) / nre if nre else None}
+        _, _, fr = run_decode(wf, finputs, 0, wf.steps, torch, tkv, time_kernels=False, sync_reassign=True,
+                              samples={t for t in stream_last if t < wf.steps})
+        full_samples = fr["samples"]
+        result["full_run"]["reassign_ms_per_call_drained"] = (float(np.median(fr["reassign_synced_ms"]))
+                                                              if fr["reassign_synced_ms"] else None)
+        result["full_run"]["reassign_ms_drained_each"] = [round(x, 3) for x in fr["reassign_synced_ms"]]
+        if "reassign_ms_per_call_drained" not in result and fr["reassign_synced_ms"]:
+            result["reassign_ms_per_call_drained"] = result["full_run"]["reassign_ms_per_call_drained"]
+        if finputs is not inputs:
+            del finputs
+
     if args.stream_steps > 0:
-        print("[bench] stream staging (S=2): %d timed steps" % args.stream_steps, file=sys.stderr, flush=True)
+        # Stream staging: each step copies every layer's T1 rows from pinned host memory into
+        # one of S = 2 HBM slots, one layer ahead of the attention that reads them.  Three
+        # windows of --stream-steps steps: the first reassignment after a plain prefill (whose
+        # positional first placement leaves most rows to re-tier), the steady state (the next
+        # window, ending after the next reassignment), and the first reassignment after a
+        # scored prefill (rows placed by the prompt's own scores from the start).
         pinned = pinned_h2d_gbs(torch)
-        ssecs, sb, sa = run_decode(w, inputs, args.warmup, args.stream_steps, torch, tkv, staging_layers=2)
-        h2d = sa["h2d_bytes"] - sb["h2d_bytes"]
-        result["stream_staging"] = {
-            "staging_layers": 2, "steps": args.stream_steps, "steps_per_s": args.stream_steps / ssecs,
-            "h2d_gbs": h2d / ssecs / 1e9, "pinned_h2d_gbs": pinned,
-            "h2d_frac_of_pinned": (h2d / ssecs / 1e9) / pinned,
-            "h2d_bytes_per_step": h2d / args.stream_steps,
-            # max(H2D time at the pinned rate, resident step time) / stream step time: 1.0 means the
-            # layer-ahead copies hide the compute completely (or the compute hides the copies)
-            "overlap_efficiency": max(h2d / args.stream_steps / (pinned * 1e9), secs / args.steps)
-            / (ssecs / args.stream_steps),
-            "hbm_kv_bytes_allocated": sa["hbm_bytes"], "full_cache_bytes": sa["full_cache_bytes"]}
+        ws = base if base.steps >= steady_warm + ns else base.replace(steps=steady_warm + ns)
+        sinputs = inputs if ws.steps <= w.steps else load_inputs(ws, ws.steps, torch)
+
+        def window(warm, scored=None, label=""):
+            print("[bench] stream staging (S=2) %s: steps %d..%d" % (label, warm + 1, warm + ns),
+                  file=sys.stderr, flush=True)
+            ssecs, sb, sa = run_decode(ws, sinputs, warm, ns, torch, tkv, staging_layers=2,
+                                       scored_prefill=scored)
+            h2d = sa["h2d_bytes"] - sb["h2d_bytes"]
+            return sa, {"timed_steps": "%d..%d" % (warm + 1, warm + ns),
+                        "reassignments": int(sa["reassigns"] - sb["reassigns"]),
+                        "steps_per_s": ns / ssecs, "h2d_gbs": h2d / ssecs / 1e9,
+                        "h2d_frac_of_pinned": (h2d / ssecs / 1e9) / pinned, "h2d_bytes_per_step": h2d / ns,
+                        # max(H2D time at the pinned rate, resident step time) / stream step time: 1.0
+                        # means the layer-ahead copies hide the compute completely (or the reverse)
+                        "overlap_efficiency": max(h2d / ns / (pinned * 1e9), secs / args.steps) / (ssecs / ns)}
+
+        sa1, first = window(first_warm, label="first reassignment")
+        sa2, steady = window(steady_warm, label="steady state")
+        scored = None
+        qb = ws.prefill * ws.layers * ws.batch * ws.q_heads * ws.head_dim * ws.elem_bytes
+        if qb <= (8 << 30):
+            qp = _dev(np.ascontiguousarray(np.moveaxis(ws.q(ws.steps, ws.prefill, ws.unit_vector()), 0, 2)),
+                      ws.dtype, torch)
+            _, scored = window(first_warm, scored=qp, label="first reassignment, scored prefill")
+            del qp
+        # Proposition 1 on the wire: stream staging must give the resident run's outputs bit for bit
+        cmp = {}
+        for t, o in ((first_warm + ns - 1, sa1["last_out"]), (steady_warm + ns - 1, sa2["last_out"])):
+            if t in full_samples:
+                cmp[str(t + 1)] = bool(np.array_equal(o, full_samples[t]))
+        result["stream_staging"] = dict(steady, **{
+            "staging_layers": 2, "steps": ns, "pinned_h2d_gbs": pinned,
+            "window": "steady state: steps %s, after the first reassignment and holding the next"
+                      % steady["timed_steps"],
+            "first_reassignment_window": first, "scored_prefill_window": scored,
+            "outputs_bitwise_equal_resident": cmp,
+            "hbm_kv_bytes_allocated": sa2["hbm_bytes"], "full_cache_bytes": sa2["full_cache_bytes"]})
+        if cmp and not all(cmp.values()):
+            raise SystemExit("stream staging outputs differ from the resident run: %s" % cmp)
+        if sinputs is not inputs:
+            del sinputs
 
     if args.baseline_steps is None:
         args.baseline_steps = args.steps
@@ -456,6 +602,16 @@ def main():
         trace = gpu_trace(w, inputs, args.cpu_steps, torch, tkv)
         print("[bench] cpu baseline: oracle, %d steps" % args.cpu_steps, file=sys.stderr, flush=True)
         result["cpu_baseline"], result["parity"] = cpu_baseline(w, args.cpu_steps, trace)
+        result["cpu_baseline"]["cpu_model"] = cpu_model()
+        if args.single_thread_steps > 0:
+            print("[bench] one-thread oracle: tiny and %s" % w.name, file=sys.stderr, flush=True)
+            import tkvsynth as _ts
+            result["cpu_baseline"]["single_thread"] = {
+                "tiny": single_thread_oracle("tiny", _ts.CONFIGS["tiny"].steps),
+                w.name: single_thread_oracle(w.name, args.single_thread_steps)}
+        if not result["parity"]["ok"]:
+            print(json.dumps(result), flush=True)
+            raise SystemExit("parity with the oracle failed: %s" % result["parity"])
 
     print(json.dumps(result), flush=True)
 

@@ -27,6 +27,9 @@ TKV_FLAG_NO_T1 = 2
 TKV_FLAG_T2_FP8 = 4
 TKV_FLAG_SHARED_HBM = 8
 TKV_FLAG_T2_HEAD_SCALES = 16
+TKV_FLAG_VECTOR_PASS = 32
+TKV_FLAG_TEST_DELAY_COPIES = 256
+TKV_FLAG_TEST_SHUFFLE_SLOTS = 512
 
 _NAMES = {TKV_EINVAL: "EINVAL", TKV_ECAPACITY: "ECAPACITY", TKV_ENOMEM: "ENOMEM",
           TKV_ESTATE: "ESTATE", TKV_EHIP: "EHIP"}
@@ -50,7 +53,7 @@ class tkv_protect(ctypes.Structure):
 
 class tkv_options(ctypes.Structure):
     _fields_ = [("t2_ratio", ctypes.c_double), ("staging_layers", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("flags", ctypes.c_uint64)]
+                ("chunk", ctypes.c_int32), ("flags", ctypes.c_uint64), ("mem_cap_bytes", ctypes.c_int64)]
 
 
 class tkv_delta(ctypes.Structure):
@@ -70,7 +73,7 @@ class tkv_stats_t(ctypes.Structure):
                 ("h2d_bytes", ctypes.c_int64), ("d2h_bytes", ctypes.c_int64),
                 ("attn_kernel_ms", ctypes.c_double), ("attn_kernel_launches", ctypes.c_int64),
                 ("attn_kv_bytes", ctypes.c_int64),
-                ("reassign_ms", ctypes.c_double)]
+                ("reassign_ms", ctypes.c_double), ("mem_bytes", ctypes.c_int64)]
 
 
 _lib = None
@@ -141,9 +144,10 @@ def _dev_ptr(x: torch.Tensor, shape, dtype, name):
 # ---- functions named as the C ABI --------------------------------------------
 
 def tkv_create(layers, q_heads, kv_heads, head_dim, batch, max_tokens, dtype, delta, hbm_ratio,
-               evict_ratio, prompt, sinks, recent, t2_ratio=0.0, staging_layers=0, chunk=0, flags=0):
+               evict_ratio, prompt, sinks, recent, t2_ratio=0.0, staging_layers=0, chunk=0, flags=0,
+               mem_cap_bytes=0):
     shape = tkv_shape(layers, q_heads, kv_heads, head_dim, batch, max_tokens, dtype)
-    opts = tkv_options(t2_ratio, staging_layers, chunk, flags)
+    opts = tkv_options(t2_ratio, staging_layers, chunk, flags, mem_cap_bytes)
     h = _vp()
     rc = lib().tkv_create(ctypes.byref(shape), delta, hbm_ratio, evict_ratio,
                           tkv_protect(prompt, sinks, recent), ctypes.byref(opts), ctypes.byref(h))
@@ -237,7 +241,7 @@ class TieredKV:
     def __init__(self, layers, q_heads, kv_heads, head_dim, batch, max_tokens, dtype="bf16", delta=64,
                  hbm_ratio=0.5, evict_ratio=0.03, prompt=0, sinks=4, recent=128, t2_ratio=0.0,
                  staging_layers=0, chunk=0, time_kernels=False, no_t1=False, t2_fp8=False, shared_hbm=False,
-                 t2_head_scales=False):
+                 t2_head_scales=False, extra_flags=0, mem_cap_bytes=0):
         self.L, self.Hq, self.Hkv, self.D, self.B, self.nmax = layers, q_heads, kv_heads, head_dim, batch, max_tokens
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -246,7 +250,7 @@ class TieredKV:
                             prompt, sinks, recent, t2_ratio, staging_layers, chunk,
                             (TKV_FLAG_TIME_KERNELS if time_kernels else 0) | (TKV_FLAG_NO_T1 if no_t1 else 0)
                             | (TKV_FLAG_T2_FP8 if t2_fp8 else 0) | (TKV_FLAG_SHARED_HBM if shared_hbm else 0)
-                            | (TKV_FLAG_T2_HEAD_SCALES if t2_head_scales else 0))
+                            | (TKV_FLAG_T2_HEAD_SCALES if t2_head_scales else 0) | extra_flags, mem_cap_bytes)
         self.n_scales = kv_heads if t2_head_scales else 1
 
     @classmethod

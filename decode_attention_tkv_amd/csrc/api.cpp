@@ -30,6 +30,11 @@ int tkv_fail(tkv* t, int code, const char* fmt, ...) {
 
 static int device_alloc(tkv* t, void** p, size_t bytes) {
   if (bytes == 0) bytes = 256;
+  if (!within_cap(*t, bytes)) {
+    *p = nullptr;
+    return tkv_fail(t, TKV_ENOMEM, "memory cap (%lld bytes) reached: %zu more device bytes asked",
+                    (long long)t->mem_cap, bytes);
+  }
   hipError_t e = hipMalloc(p, bytes);
   if (e != hipSuccess) {
     *p = nullptr;
@@ -37,11 +42,17 @@ static int device_alloc(tkv* t, void** p, size_t bytes) {
     return tkv_fail(t, TKV_ENOMEM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
   }
   t->device_allocs.push_back(*p);
+  t->mem_held += (int64_t)bytes;
   return TKV_OK;
 }
 
 static int host_alloc(tkv* t, void** p, size_t bytes) {
   if (bytes == 0) bytes = 256;
+  if (!within_cap(*t, bytes)) {
+    *p = nullptr;
+    return tkv_fail(t, TKV_ENOMEM, "memory cap (%lld bytes) reached: %zu more pinned bytes asked",
+                    (long long)t->mem_cap, bytes);
+  }
   hipError_t e = hipHostMalloc(p, bytes, hipHostMallocDefault);
   if (e != hipSuccess) {
     *p = nullptr;
@@ -49,11 +60,11 @@ static int host_alloc(tkv* t, void** p, size_t bytes) {
     return tkv_fail(t, TKV_ENOMEM, "hipHostMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
   }
   t->host_allocs.push_back(*p);
+  t->mem_held += (int64_t)bytes;
   return TKV_OK;
 }
 
 static void release(tkv* t) {
-  if (t->arena_job.valid()) (void)t->arena_job.get();
   if (t->side) (void)hipStreamSynchronize(t->side);
   if (t->side_v) (void)hipStreamSynchronize(t->side_v);
   if (t->wb) (void)hipStreamSynchronize(t->wb);
@@ -61,14 +72,8 @@ static void release(tkv* t) {
   for (void* p : t->host_allocs) (void)hipHostFree(p);
   if (t->d_ops) (void)hipFree(t->d_ops);
   if (t->h_ops) (void)hipHostFree(t->h_ops);
-  for (void* p : {t->h_pack_in, t->h_pack_out, t->h_qout, t->h_qin})
-    if (p) (void)hipHostFree(p);
-  for (void* p : {t->fpack, t->fin, t->qin, t->qout})
-    if (p) (void)hipFree(p);
-  t->fpack = t->fin = t->qin = t->qout = nullptr;
-  t->h_pack_in = t->h_pack_out = t->h_qout = t->h_qin = nullptr;
-  if (t->ev_pack) (void)hipEventDestroy(t->ev_pack);
-  t->ev_pack = nullptr;
+  if (t->fpack) (void)hipFree(t->fpack);
+  t->fpack = nullptr;
   for (hipEvent_t e : t->ev_h2d) (void)hipEventDestroy(e);
   for (hipEvent_t e : t->ev_h2d_v) (void)hipEventDestroy(e);
   for (hipEvent_t e : t->ev_comp) (void)hipEventDestroy(e);
@@ -79,7 +84,7 @@ static void release(tkv* t) {
   if (t->ev_gathered) (void)hipEventDestroy(t->ev_gathered);
   t->wb = nullptr;
   t->ev_gathered = nullptr;
-  t->d_ops = t->h_ops = t->h_pack_in = nullptr;
+  t->d_ops = t->h_ops = nullptr;
   t->ev_h2d.clear();
   t->ev_h2d_v.clear();
   t->ev_comp.clear();
@@ -93,6 +98,20 @@ static void release(tkv* t) {
   }
   t->device_allocs.clear();
   t->host_allocs.clear();
+}
+
+// Before the host reads the pinned arenas: the last reassignment's kernels,
+// which write them, are done.
+static int arena_settled(tkv* t) {
+  HIP_TRY(t, hipEventSynchronize(t->ev_arena));
+  return TKV_OK;
+}
+
+// A handle whose last reassignment failed part way is unusable.
+static int usable(tkv* t) {
+  if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  if (t->failed) return tkv_fail(t, TKV_ESTATE, "handle unusable: an earlier reassignment failed part way");
+  return TKV_OK;
 }
 
 extern "C" const char* tkv_last_error(const tkv_t* t) { return t ? t->err.c_str() : g_create_err.c_str(); }
@@ -127,10 +146,15 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   if (o.chunk == 0) o.chunk = (s.q_heads >= 4 * s.kv_heads) ? 512 : 256;
   if (o.chunk != 128 && o.chunk != 256 && o.chunk != 512)
     return tkv_fail(nullptr, TKV_EINVAL, "chunk must be 128, 256 or 512");
+  if (o.mem_cap_bytes < 0) return tkv_fail(nullptr, TKV_EINVAL, "mem_cap_bytes must be >= 0");
   if (o.staging_layers < 0 || o.staging_layers == 1)
     return tkv_fail(nullptr, TKV_EINVAL, "staging_layers must be 0 or >= 2");
   if ((o.flags & TKV_FLAG_NO_T1) && (o.flags & TKV_FLAG_SHARED_HBM))
     return tkv_fail(nullptr, TKV_EINVAL, "TKV_FLAG_NO_T1 and TKV_FLAG_SHARED_HBM do not combine");
+  if ((o.flags & TKV_FLAG_VECTOR_PASS) && o.t2_ratio > 0 && o.staging_layers != 0 && o.staging_layers < s.layers)
+    return tkv_fail(nullptr, TKV_EINVAL, "TKV_FLAG_VECTOR_PASS does not combine with an 8-bit tier in stream staging");
+  if ((o.flags & TKV_FLAG_SHARED_HBM) && s.max_tokens >= (1 << 26))
+    return tkv_fail(nullptr, TKV_EINVAL, "TKV_FLAG_SHARED_HBM needs max_tokens < 2^26 (joint ranking keys)");
   const bool resident = o.staging_layers == 0 || o.staging_layers >= s.layers;
 
   tkv* t = new tkv();
@@ -164,6 +188,7 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   t->sinks = protect.sinks;
   t->recent = protect.recent;
   t->flags = o.flags;
+  t->mem_cap = o.mem_cap_bytes;
   t->row_elems = (int64_t)s.kv_heads * s.head_dim;
   t->row_bytes = t->row_elems * t->esz;
 
@@ -197,7 +222,9 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   dev((void**)&t->tier, B * nmax);
   dev((void**)&t->loc, B * nmax * 4);
   dev((void**)&t->s, B * nmax * 4);
-  t->defer = resident && s.dtype == TKV_BF16 && group >= 4;  // the matrix-core path over resident staging
+  t->vector_pass = (o.flags & TKV_FLAG_VECTOR_PASS) != 0 && s.dtype == TKV_BF16 && group >= 4;
+  // the matrix-core path over resident staging
+  t->defer = resident && s.dtype == TKV_BF16 && group >= 4 && !t->vector_pass;
   if (t->defer) {
     dev(&t->qbuf[0], L * B * Hq * t->D * t->esz);
     dev(&t->qbuf[1], L * B * Hq * t->D * t->esz);
@@ -211,6 +238,10 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   dev((void**)&t->part_ml, L * B * Hq * t->max_chunks * 2 * 4);
   dev((void**)&t->part_o, L * B * Hq * t->max_chunks * t->D * 4);
   dev((void**)&t->tier_alt, B * nmax);
+  if (t->shared_hbm) {
+    dev((void**)&t->d_cuts, B * 3 * sizeof(uint64_t));
+    dev((void**)&t->d_n0c, B * sizeof(int32_t));
+  }
   const size_t counts_bytes = (B * 2 * 4 + 15) / 16 * 16;
   t->delta_block_bytes = counts_bytes + 2 * B * nmax * sizeof(tkv_delta);
   dev((void**)&t->d_counts, t->delta_block_bytes);
@@ -234,6 +265,18 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
       dev((void**)&t->qsscale_v, (size_t)t->S * B * t->cap2 * t->sh * 4);
     }
   }
+  // the kernels of a stream-staging reassignment address the arenas directly
+  auto map = [&](void* host, void** dev) {
+    if (rc != TKV_OK || !host) return;
+    const hipError_t e = hipHostGetDevicePointer(dev, host, 0);
+    if (e != hipSuccess) rc = tkv_fail(t, TKV_EHIP, "hipHostGetDevicePointer: %s", hipGetErrorString(e));
+  };
+  map(t->arena1_k, &t->d_arena1_k);
+  map(t->arena1_v, &t->d_arena1_v);
+  map(t->arena2_k, (void**)&t->d_arena2_k);
+  map(t->arena2_v, (void**)&t->d_arena2_v);
+  map(t->ascale_k, (void**)&t->d_ascale_k);
+  map(t->ascale_v, (void**)&t->d_ascale_v);
   if (rc == TKV_OK) rc = host_alloc(t, (void**)&t->h_counts, t->delta_block_bytes);
   if (rc == TKV_OK) {
     t->h_promote = (tkv_delta*)((char*)t->h_counts + counts_bytes);
@@ -256,7 +299,6 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
       if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_comp[i], hipEventDisableTiming);
     }
     if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_arena, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ev_pack, hipEventDisableTiming);
     if (e != hipSuccess) rc = tkv_fail(t, TKV_EHIP, "creating streams/events: %s", hipGetErrorString(e));
   }
   if (rc == TKV_OK) {
@@ -275,9 +317,21 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   t->prev_nlive.assign(B, 0);
   t->free0.resize(t->shared_hbm ? 1 : B);
   if (!t->positional)
-    for (auto& f : t->free0) {
+    for (size_t q = 0; q < t->free0.size(); ++q) {
+      auto& f = t->free0[q];
       f.resize(t->cap0);
       for (int i = 0; i < t->cap0; ++i) f[i] = t->cap0 - 1 - i;  // back() = lowest free slot
+      if (t->flags & TKV_FLAG_TEST_SHUFFLE_SLOTS) {
+        // seeded Fisher-Yates over the slots (splitmix64 words)
+        uint64_t x = 0x5EEDull + q;
+        for (int i = t->cap0 - 1; i > 0; --i) {
+          uint64_t z = (x += 0x9E3779B97F4A7C15ull);
+          z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+          z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+          z ^= z >> 31;
+          std::swap(f[i], f[(size_t)(z % (uint64_t)(i + 1))]);
+        }
+      }
     }
   if (t->positional) t->h_aidx.assign((size_t)B * nmax, kNoLoc);
   t->h_tier.assign(B * nmax, kUnused);
@@ -312,7 +366,7 @@ extern "C" int tkv_destroy(tkv_t* t) {
 }
 
 static int prefill_impl(tkv_t* t, const void* k, const void* v, int32_t n_tokens, tkv_stream_t stream) {
-  if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  if (int rc = usable(t)) return rc;
   if (t->state != TkvState::Empty || t->n != 0) return tkv_fail(t, TKV_ESTATE, "prefill needs an empty cache");
   if (!k || !v) return tkv_fail(t, TKV_EINVAL, "k/v is NULL");
   if (misaligned(k) || misaligned(v)) return tkv_fail(t, TKV_EINVAL, "k/v not 16-byte aligned");
@@ -509,7 +563,7 @@ extern "C" int tkv_prefill_scored(tkv_t* t, const void* k, const void* v, const 
 
 // Checks of an append; TKV_OK when a step may start.
 static int append_check(tkv* t, const void* k, const void* v) {
-  if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  if (int rc = usable(t)) return rc;
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "previous step has layers left");
   if (!k || !v) return tkv_fail(t, TKV_EINVAL, "k/v is NULL");
   if (misaligned(k) || misaligned(v)) return tkv_fail(t, TKV_EINVAL, "k/v not 16-byte aligned");
@@ -668,7 +722,8 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
   }
   StepArgs none{};
   if (chunks_now > 0)
-    HIP_TRY(t, launch_attn(a, step ? *step : none, t->dtype, t->D, t->group, t->chunk, lc, chunks_now, e0, e1, st));
+    HIP_TRY(t, launch_attn(a, step ? *step : none, t->dtype, t->D, t->group, t->chunk, t->vector_pass, lc, chunks_now, e0, e1,
+                           st));
   if (timed) {
     t->ev_pending.emplace_back(e0, e1);
     int64_t rows = 0;
@@ -731,7 +786,7 @@ static int flush_deferred(tkv* t, hipStream_t st) {
   const int chunks = (m + t->chunk - 1) / t->chunk;
   StepArgs none{};
   if (chunks > 0) {
-    HIP_TRY(t, launch_attn(a, none, t->dtype, t->D, t->group, t->chunk, t->L, chunks, nullptr, nullptr, st));
+    HIP_TRY(t, launch_attn(a, none, t->dtype, t->D, t->group, t->chunk, false, t->L, chunks, nullptr, nullptr, st));
     HIP_TRY(t, launch_fold64(defer_fold_args(t), prev_tiles(t), st));
   }
   t->prev_pending = false;
@@ -743,10 +798,6 @@ static int flush_deferred(tkv* t, hipStream_t st) {
 // on the other), up to layer `upto`, each after the
 // attention that last read that slot.
 static int issue_prefetch(tkv* t, int upto) {
-  if (t->arena_job.valid()) {
-    const int rc = t->arena_job.get();
-    if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
-  }
   if (t->arena_pending) {
     HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_arena, 0));
     HIP_TRY(t, hipStreamWaitEvent(t->side_v, t->ev_arena, 0));
@@ -762,6 +813,10 @@ static int issue_prefetch(tkv* t, int upto) {
     if (t->comp_recorded[slot]) {
       HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_comp[slot], 0));
       HIP_TRY(t, hipStreamWaitEvent(t->side_v, t->ev_comp[slot], 0));
+    }
+    if (t->flags & TKV_FLAG_TEST_DELAY_COPIES) {
+      HIP_TRY(t, launch_delay(kTestDelayIters, t->side));
+      HIP_TRY(t, launch_delay(kTestDelayIters, t->side_v));
     }
     if (n1max > 0) {
       const size_t hb = (size_t)t->D * t->esz;
@@ -826,7 +881,7 @@ static void end_step(tkv* t, int max_live) {
 
 static int decode_attn_impl(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
                                tkv_stream_t stream) {
-  if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  if (int rc = usable(t)) return rc;
   if (t->state != TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "no step in progress (append first)");
   if (!q || !out) return tkv_fail(t, TKV_EINVAL, "q/out is NULL");
   if (misaligned(q) || misaligned(out)) return tkv_fail(t, TKV_EINVAL, "q/out not 16-byte aligned");
@@ -904,10 +959,7 @@ extern "C" int tkv_decode_step(tkv_t* t, const void* k, const void* v, const voi
 
 static int stats_impl(tkv_t* t, tkv_stats_t* out) {
   if (!t || !out) return tkv_fail(t, TKV_EINVAL, "NULL argument");
-  if (t->arena_job.valid()) {
-    const int rc = t->arena_job.get();
-    if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
-  }
+  if (int rc = arena_settled(t)) return rc;
   HIP_TRY(t, hipStreamSynchronize(t->side));
   if (t->side_v) HIP_TRY(t, hipStreamSynchronize(t->side_v));
   HIP_TRY(t, hipStreamSynchronize(t->wb));
@@ -915,6 +967,7 @@ static int stats_impl(tkv_t* t, tkv_stats_t* out) {
   if (rc) return rc;
   t->st.step = t->step;
   t->st.n_tokens = t->n;
+  t->st.mem_bytes = t->mem_held;
   for (int i = 0; i < 4; ++i) t->st.tier_count[i] = 0;
   for (int b = 0; b < t->B; ++b)
     for (int p = 0; p < t->n; ++p) {
@@ -937,7 +990,8 @@ int tkv_flush_score(tkv* t, hipStream_t stream) {
 }
 
 static int read_scores_impl(tkv_t* t, float* scores, tkv_stream_t stream) {
-  if (!t || !scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (int rc = usable(t)) return rc;
+  if (!scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (int rc = tkv_flush_score(t, (hipStream_t)stream)) return rc;
   HIP_TRY(t, hipMemcpyAsync(scores, t->s, (size_t)t->B * t->nmax * 4, hipMemcpyDeviceToHost, (hipStream_t)stream));
   HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
@@ -948,7 +1002,8 @@ extern "C" int tkv_read_scores(tkv_t* t, float* scores, tkv_stream_t stream) {
 }
 
 static int write_scores_impl(tkv_t* t, const float* scores, tkv_stream_t stream) {
-  if (!t || !scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (int rc = usable(t)) return rc;
+  if (!scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "step in progress");
   if (int rc = tkv_flush_score(t, (hipStream_t)stream)) return rc;
   HIP_TRY(t, hipMemcpyAsync(t->s, scores, (size_t)t->B * t->nmax * 4, hipMemcpyHostToDevice, (hipStream_t)stream));
@@ -960,7 +1015,8 @@ extern "C" int tkv_write_scores(tkv_t* t, const float* scores, tkv_stream_t stre
 }
 
 static int read_tiers_impl(tkv_t* t, uint8_t* tiers, tkv_stream_t stream) {
-  if (!t || !tiers) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (int rc = usable(t)) return rc;
+  if (!tiers) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   HIP_TRY(t, hipMemcpyAsync(tiers, t->tier, (size_t)t->B * t->nmax, hipMemcpyDeviceToHost, (hipStream_t)stream));
   HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
   return TKV_OK;
@@ -970,7 +1026,8 @@ extern "C" int tkv_read_tiers(tkv_t* t, uint8_t* tiers, tkv_stream_t stream) {
 }
 
 static int read_deltas_impl(tkv_t* t, tkv_delta* promote, tkv_delta* demote, int32_t* counts) {
-  if (!t || !promote || !demote || !counts) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (int rc = usable(t)) return rc;
+  if (!promote || !demote || !counts) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   const size_t nd = (size_t)t->B * t->nmax;
   std::memcpy(promote, t->h_promote, nd * sizeof(tkv_delta));
   std::memcpy(demote, t->h_demote, nd * sizeof(tkv_delta));
@@ -983,13 +1040,11 @@ extern "C" int tkv_read_deltas(tkv_t* t, tkv_delta* promote, tkv_delta* demote, 
 
 static int read_kv_impl(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, void* k, void* v,
                            tkv_stream_t stream) {
-  if (!t || !k || !v) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (int rc = usable(t)) return rc;
+  if (!k || !v) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (layer < 0 || layer >= t->L || seq < 0 || seq >= t->B || pos < 0 || pos >= t->n)
     return tkv_fail(t, TKV_EINVAL, "layer/seq/pos out of range");
-  if (t->arena_job.valid()) {
-    const int rc = t->arena_job.get();
-    if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
-  }
+  if (int rc = arena_settled(t)) return rc;
   const size_t at = (size_t)seq * t->nmax + pos;
   const uint8_t tier = t->h_tier[at];
   const uint32_t code = t->h_loc[at];
@@ -1034,13 +1089,11 @@ extern "C" int tkv_read_kv(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, vo
 
 static int read_t2_impl(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, int8_t* k_codes, int8_t* v_codes,
                            float* scales) {
-  if (!t || !k_codes || !v_codes || !scales) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (int rc = usable(t)) return rc;
+  if (!k_codes || !v_codes || !scales) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (layer < 0 || layer >= t->L || seq < 0 || seq >= t->B || pos < 0 || pos >= t->n)
     return tkv_fail(t, TKV_EINVAL, "layer/seq/pos out of range");
-  if (t->arena_job.valid()) {
-    const int rc = t->arena_job.get();
-    if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
-  }
+  if (int rc = arena_settled(t)) return rc;
   const size_t at = (size_t)seq * t->nmax + pos;
   if (t->h_tier[at] != TKV_T2) return tkv_fail(t, TKV_ESTATE, "position %d is not in T2", pos);
   const uint32_t idx = t->positional ? t->h_aidx[at] : t->h_loc[at] - (uint32_t)(t->cap0 + t->cap1);

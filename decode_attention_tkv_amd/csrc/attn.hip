@@ -82,8 +82,6 @@ __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cas
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   const u32x4 v = {u.x, u.y, u.z, u.w};
   return __builtin_bit_cast(bf16x8, v);
@@ -283,13 +281,18 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
   constexpr int U = ITERS < UB ? ITERS : UB;    // loads in flight per lane per batch
   static_assert(RPW % RPI == 0 && ITERS % U == 0, "chunk shape");
 
-  __shared__ float zs[G][CHUNK];                       // logits (log2 units), kept to the end
+  // logits (log2 units), kept to the end unless Eq. 1 is deferred; then the
+  // per-wave partial outputs reuse their space once p is formed (one more
+  // work-group per CU at G = 8)
+  constexpr bool OSUM_IN_ZS = DEF && NW * D <= CHUNK;
+  __shared__ float zs_store[G * CHUNK + (OSUM_IN_ZS ? 0 : NW * G * D)];
+  float (*zs)[CHUNK] = reinterpret_cast<float (*)[CHUNK]>(zs_store);
+  float (*osum)[G][D] = reinterpret_cast<float (*)[G][D]>(zs_store + (OSUM_IN_ZS ? 0 : G * CHUNK));
   __shared__ float ps[MK ? 1 : G][MK ? 1 : CHUNK];     // p = 2^(z - m) of the vector path
   __shared__ float red[NW][G];
-  __shared__ float osum[NW][G][D];
   __shared__ uint32_t codes_s[CHUNK];
-  // matrix-core p.V: P in fp16, 16 (padded) heads x CHUNK rows
-  __shared__ __attribute__((aligned(16))) _Float16 p16[MK ? 16 : 1][MK ? CHUNK : 1];
+  // matrix-core p.V: P as three bf16 terms (hi, mid, lo), G heads x CHUNK rows
+  __shared__ __attribute__((aligned(16))) bf16_t pt[MK ? 3 : 1][MK ? G : 1][MK ? CHUNK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = lane % LPR, rg = lane / LPR;
@@ -508,19 +511,26 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
       float p = 0.f;
       if (r < nrows) p = exp2f(zs[g][r] - mc[g]);
       if constexpr (MK) {
-        // the weights the matrix cores use are fp16; the chunk sum uses the same values
-        const _Float16 h = (_Float16)p;
-        p16[g][r] = h;
-        ls[g] += (float)h;
+        // p = hi + mid + lo, each a bf16 value (each term takes the next 8 of
+        // p's 24 significant bits; the remainders are exact in fp32), so the
+        // bf16 matrix cores weigh V by p itself, as the vector path does
+        const uint32_t hi = bf16_bits(p);
+        const float r1 = p - __uint_as_float(hi << 16);
+        const uint32_t mid = bf16_bits(r1);
+        const uint32_t lo = bf16_bits(r1 - __uint_as_float(mid << 16));
+        pt[0][g][r] = (bf16_t)hi;
+        pt[1][g][r] = (bf16_t)mid;
+        pt[2][g][r] = (bf16_t)lo;
+        ls[g] += p;
       } else {
         ps[g][r] = p;
         ls[g] += p;
       }
     }
   }
-  if constexpr (MK)
-    for (int x = tid; x < (16 - G) * CHUNK; x += 256) p16[G + x / CHUNK][x % CHUNK] = (_Float16)0.f;
-  __syncthreads();  // all reads of red[] (maxima) done before it is reused below
+  // all reads of red[] (maxima) and of zs (when osum reuses it) are done
+  // before either is written again below
+  __syncthreads();
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const float s = group_sum<64>(ls[g]);
@@ -533,9 +543,11 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
     // lane (hl, kq) loads 16 B (d = 8hl..8hl+7) of rows 8kq..8kq+7 of a 32-row
     // sub-tile (every load instruction covers 4 full rows), and MFMA #j takes
     // element j of those 8 rows, so its output columns are d = 8n + j.
-    // V goes to fp16 exactly (bf16 values are fp16 values in its normal range).
-    // With head_dim 64 only lanes hl < 8 carry columns; the others load zeros
-    // and their output columns are dropped.
+    // v_mfma_f32_16x16x32_bf16 takes V's bf16 values as they are (any range)
+    // and P as its three bf16 terms, one MFMA each: the products are exact in
+    // fp32 and the sum is accumulated in fp32.  Heads G..15 of the tile are
+    // zero.  With head_dim 64 only lanes hl < 8 carry columns; the others
+    // load zeros and their output columns are dropped.
     constexpr int ST = RPW / 32;
     const int hl = lane & 15, kq = lane >> 4;
     const bool col_ok = 8 * hl < D;
@@ -563,16 +575,17 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
           vr[i] = ok ? load16nt(p) : make_uint4(0, 0, 0, 0);
         }
       }
-      const half8 pa = *reinterpret_cast<const half8*>(&p16[hl][rb]);
+      bf16x8 pa[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        pa[k] = hl < G ? *reinterpret_cast<const bf16x8*>(&pt[k][hl < G ? hl : 0][rb]) : as_bf16x8(make_uint4(0, 0, 0, 0));
       uint32_t vh[8][4];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[t] << 16), __uint_as_float(w[t] & 0xFFFF0000u));
-          vh[i][t] = __builtin_bit_cast(uint32_t, h);
-        }
+        vh[i][0] = vr[i].x;
+        vh[i][1] = vr[i].y;
+        vh[i][2] = vr[i].z;
+        vh[i][3] = vr[i].w;
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -582,7 +595,9 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
           const uint32_t a0 = vh[2 * t][j >> 1], a1 = vh[2 * t + 1][j >> 1];
           bw[t] = (j & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
         }
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(half8, bw), acc[j], 0, 0, 0);
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, bw);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[k], vb, acc[j], 0, 0, 0);
       }
     }
 #pragma unroll
@@ -871,9 +886,8 @@ struct AttnLaunch {
   hipStream_t s;
 };
 
-template <typename T, int D, int G, bool QT, bool DEF>
+template <typename T, int D, int G, bool QT, bool DEF, bool MK>
 const void* attn_fn(int chunk) {
-  constexpr bool MK = std::is_same<T, bf16_t>::value && G >= 4;
   switch (chunk) {
     case 128: return (const void*)&k_attn_chunk<T, D, G, 128, MK, QT, DEF>;
     case 256: return (const void*)&k_attn_chunk<T, D, G, 256, MK, QT, DEF>;
@@ -883,16 +897,23 @@ const void* attn_fn(int chunk) {
 }
 
 // a.spart set: deferred Eq. 1, which only the matrix-core path without 8-bit
-// staging has (the launcher checks this before it sets a.spart)
+// staging has (the launcher checks this before it sets a.spart).  vec: bf16
+// grouped-query heads on the vector path instead of the matrix cores (not
+// with 8-bit staging).
 template <typename T, int D, int G, bool QT>
-hipError_t launch_attn_t(const AttnArgs& a, const StepArgs& n, int chunk, const AttnLaunch& L) {
+hipError_t launch_attn_t(const AttnArgs& a, const StepArgs& n, int chunk, bool vec, const AttnLaunch& L) {
   constexpr bool MK = std::is_same<T, bf16_t>::value && G >= 4;
   const void* fn = nullptr;
   if constexpr (MK && !QT) {
-    fn = a.spart ? attn_fn<T, D, G, QT, true>(chunk) : attn_fn<T, D, G, QT, false>(chunk);
+    if (vec) {
+      if (a.spart) return hipErrorInvalidValue;
+      fn = attn_fn<T, D, G, QT, false, false>(chunk);
+    } else {
+      fn = a.spart ? attn_fn<T, D, G, QT, true, true>(chunk) : attn_fn<T, D, G, QT, false, true>(chunk);
+    }
   } else {
-    if (a.spart) return hipErrorInvalidValue;
-    fn = attn_fn<T, D, G, QT, false>(chunk);
+    if (a.spart || (vec && MK)) return hipErrorInvalidValue;
+    fn = attn_fn<T, D, G, QT, false, MK>(chunk);
   }
   if (!fn) return hipErrorInvalidValue;
   AttnArgs ac = a;
@@ -902,13 +923,13 @@ hipError_t launch_attn_t(const AttnArgs& a, const StepArgs& n, int chunk, const 
 }
 
 template <typename T, int D, bool QT>
-hipError_t launch_attn_g(const AttnArgs& a, const StepArgs& n, int group, int chunk, const AttnLaunch& L) {
+hipError_t launch_attn_g(const AttnArgs& a, const StepArgs& n, int group, int chunk, bool vec, const AttnLaunch& L) {
   switch (group) {
-    case 1: return launch_attn_t<T, D, 1, QT>(a, n, chunk, L);
-    case 2: return launch_attn_t<T, D, 2, QT>(a, n, chunk, L);
-    case 4: return launch_attn_t<T, D, 4, QT>(a, n, chunk, L);
-    case 5: return launch_attn_t<T, D, 5, QT>(a, n, chunk, L);
-    case 8: return launch_attn_t<T, D, 8, QT>(a, n, chunk, L);
+    case 1: return launch_attn_t<T, D, 1, QT>(a, n, chunk, vec, L);
+    case 2: return launch_attn_t<T, D, 2, QT>(a, n, chunk, vec, L);
+    case 4: return launch_attn_t<T, D, 4, QT>(a, n, chunk, vec, L);
+    case 5: return launch_attn_t<T, D, 5, QT>(a, n, chunk, vec, L);
+    case 8: return launch_attn_t<T, D, 8, QT>(a, n, chunk, vec, L);
     default: return hipErrorInvalidValue;
   }
 }
@@ -916,12 +937,12 @@ hipError_t launch_attn_g(const AttnArgs& a, const StepArgs& n, int group, int ch
 // Stream staging with an 8-bit tier takes the variant that reads T2 rows as codes.
 // A step launch (n.k set) never comes with 8-bit staging: kNewRow is above every T2 code.
 template <typename T, int D>
-hipError_t launch_attn_q(const AttnArgs& a, const StepArgs& n, int group, int chunk, const AttnLaunch& L) {
+hipError_t launch_attn_q(const AttnArgs& a, const StepArgs& n, int group, int chunk, bool vec, const AttnLaunch& L) {
   if (a.rows.q_k != nullptr) {
     if (n.k) return hipErrorInvalidValue;
-    return launch_attn_g<T, D, true>(a, n, group, chunk, L);
+    return launch_attn_g<T, D, true>(a, n, group, chunk, vec, L);
   }
-  return launch_attn_g<T, D, false>(a, n, group, chunk, L);
+  return launch_attn_g<T, D, false>(a, n, group, chunk, vec, L);
 }
 
 }  // namespace
@@ -934,14 +955,15 @@ hipError_t launch_append(const AppendArgs& a, const ScoreArgs* fold, int fold_ti
 }
 
 hipError_t launch_attn(const AttnArgs& a, const StepArgs& n, int dtype, int head_dim, int group, int chunk,
-                       int layer_count, int chunks_now, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
+                       bool vector_pass, int layer_count, int chunks_now, hipEvent_t e0, hipEvent_t e1,
+                       hipStream_t s) {
   const AttnLaunch L{dim3(chunks_now, a.kv_heads, layer_count * a.batch), e0, e1, s};
   if (dtype == TKV_BF16) {
-    if (head_dim == 128) return launch_attn_q<bf16_t, 128>(a, n, group, chunk, L);
-    if (head_dim == 64) return launch_attn_q<bf16_t, 64>(a, n, group, chunk, L);
+    if (head_dim == 128) return launch_attn_q<bf16_t, 128>(a, n, group, chunk, vector_pass, L);
+    if (head_dim == 64) return launch_attn_q<bf16_t, 64>(a, n, group, chunk, vector_pass, L);
   } else {
-    if (head_dim == 128) return launch_attn_q<float, 128>(a, n, group, chunk, L);
-    if (head_dim == 64) return launch_attn_q<float, 64>(a, n, group, chunk, L);
+    if (head_dim == 128) return launch_attn_q<float, 128>(a, n, group, chunk, vector_pass, L);
+    if (head_dim == 64) return launch_attn_q<float, 64>(a, n, group, chunk, vector_pass, L);
   }
   return hipErrorInvalidValue;
 }

@@ -46,8 +46,10 @@ __device__ __forceinline__ int64_t stage_elem(const RowSpace& rs, int l, int b, 
          (int64_t)h * rs.stage_hstride + (int64_t)idx * d;
 }
 
-// grid (n_ops, layers, 2), block 256: quantise F rows into a QPack and
-// (optionally) write their dequantised values into the staging area.
+// grid (n_ops, layers, 2), block 256: quantise F rows straight into the
+// pinned T2 arena (over PCIe) at index op.dst of sequence op.b, and
+// (optionally) write their dequantised values into the pool or the staging
+// area.
 __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const QuantOp* ops) {
   __shared__ float red[4];
   __shared__ uint32_t hmax[kMaxQHeads];  // per-head amax bits (non-negative floats order as their bits)
@@ -81,7 +83,10 @@ __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const Qua
     const float m = __uint_as_float(hmax[h]);
     return m > 0.f ? m / qmax : 1.f;
   };
-  int8_t* codes = a.out.codes + (int64_t)which * (int64_t)gridDim.y * a.kv_heads * a.out.rows * d;
+  auto code_at = [&](int h) -> int8_t* {  // first code of head h of this op's row
+    return (which ? a.arena.a2_v : a.arena.a2_k) +
+           ((((int64_t)l * a.arena.batch + op.b) * a.kv_heads + h) * a.arena.cap2 + op.dst) * d;
+  };
   for (int e = threadIdx.x; e < n; e += 256) {
     const int h = e / d, j = e % d;
     const float x = load_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.src) * d + j, a.elem_bytes);
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const Qua
       c = fminf(fmaxf(rintf(x / scale), -127.f), 127.f);
       code = (int8_t)c;
     }
-    codes[(((int64_t)l * a.kv_heads + h) * a.out.rows + op.dst) * d + j] = code;
+    code_at(h)[j] = code;
     if (op.stage != kNoLoc) {
       if (op.stage < (uint32_t)a.rows.cap0) {
         void* pl = which ? (void*)a.rows.pool_v : (void*)a.rows.pool_k;
@@ -110,23 +115,49 @@ __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const Qua
       }
     }
   }
-  for (int k = threadIdx.x; k < a.sh; k += 256)
-    a.out.scales[(((int64_t)which * gridDim.y + l) * a.out.rows + op.dst) * a.sh + k] = head_scale(k);
+  float* sc = (which ? a.arena.s2_v : a.arena.s2_k) + (((int64_t)l * a.arena.batch + op.b) * a.arena.cap2 + op.dst) * a.sh;
+  for (int k = threadIdx.x; k < a.sh; k += 256) sc[k] = head_scale(k);
 }
 
-// grid (n_ops, layers, 2), block 256: QPack rows -> cache-type values in F.
+// grid (n_ops, layers, 2), block 256: T2 arena rows (codes and scales, read
+// over PCIe) -> cache-type values in F.
 __global__ __launch_bounds__(256) void k_dequant_rows(const DequantArgs a, const DequantOp* ops) {
   const DequantOp op = ops[blockIdx.x];
   const int l = blockIdx.y, which = blockIdx.z;
   const int d = a.head_dim, n = a.kv_heads * d;
-  const int8_t* codes = a.in.codes + (int64_t)which * (int64_t)gridDim.y * a.kv_heads * a.in.rows * d;
-  const float* scales = a.in.scales + (((int64_t)which * gridDim.y + l) * a.in.rows + op.src) * a.sh;
+  const int8_t* codes = (which ? a.arena.a2_v : a.arena.a2_k) +
+                        (((int64_t)l * a.arena.batch + op.b) * a.kv_heads * a.arena.cap2 + op.src) * d;
+  const float* scales = (which ? a.arena.s2_v : a.arena.s2_k) +
+                        (((int64_t)l * a.arena.batch + op.b) * a.arena.cap2 + op.src) * a.sh;
   void* f = which ? a.f.v : a.f.k;
   for (int e = threadIdx.x; e < n; e += 256) {
     const int h = e / d, j = e % d;
     const float scale = scales[a.sh > 1 ? h : 0];
-    const float c = code_val(codes[(((int64_t)l * a.kv_heads + h) * a.in.rows + op.src) * d + j], a.fp8);
+    const float c = code_val(codes[(int64_t)h * a.arena.cap2 * d + j], a.fp8);
     store_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.dst) * d + j, c * scale, a.elem_bytes);
+  }
+}
+
+// T2 arena row op.src -> op.dst of sequence op.b (codes of every kv head,
+// then the scales), within the pinned arena: work items (op, layer, K|V) in
+// a grid-stride loop.  No op's source is another op's destination.
+__global__ __launch_bounds__(256) void k_arena2_moves(const ArenaSpace a, const RowOp* ops, int n_ops, int layers,
+                                                      int d) {
+  const int64_t items = (int64_t)n_ops * layers * 2;
+  const int pieces = d / 16;  // 16-byte pieces per head row of codes
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int which = (int)(it & 1);
+    const int64_t r = it >> 1;
+    const int l = (int)(r % layers);
+    const RowOp op = ops[r / layers];
+    int8_t* base = (which ? a.a2_v : a.a2_k) + ((int64_t)l * a.batch + op.b) * a.kv_heads * a.cap2 * d;
+    for (int x = threadIdx.x; x < a.kv_heads * pieces; x += 256) {
+      const int h = x / pieces, w = (x % pieces) * 16;
+      *reinterpret_cast<uint4*>(base + ((int64_t)h * a.cap2 + op.dst) * d + w) =
+          *reinterpret_cast<const uint4*>(base + ((int64_t)h * a.cap2 + op.src) * d + w);
+    }
+    float* sc = (which ? a.s2_v : a.s2_k) + ((int64_t)l * a.batch + op.b) * a.cap2 * a.sh;
+    for (int k = threadIdx.x; k < a.sh; k += 256) sc[(int64_t)op.dst * a.sh + k] = sc[(int64_t)op.src * a.sh + k];
   }
 }
 
@@ -141,6 +172,15 @@ hipError_t launch_quant_rows(const QuantArgs& a, const QuantOp* ops, int n_ops, 
 hipError_t launch_dequant_rows(const DequantArgs& a, const DequantOp* ops, int n_ops, int layers, hipStream_t s) {
   if (n_ops <= 0) return hipSuccess;
   k_dequant_rows<<<dim3(n_ops, layers, 2), 256, 0, s>>>(a, ops);
+  return hipGetLastError();
+}
+
+hipError_t launch_arena2_moves(const ArenaSpace& a, const RowOp* ops, int n_ops, int layers, int head_dim,
+                               int max_blocks, hipStream_t s) {
+  if (n_ops <= 0) return hipSuccess;
+  if (head_dim % 16 || max_blocks < 1) return hipErrorInvalidValue;
+  const int64_t items = (int64_t)n_ops * layers * 2;
+  k_arena2_moves<<<(unsigned)(items < max_blocks ? items : max_blocks), 256, 0, s>>>(a, ops, n_ops, layers, head_dim);
   return hipGetLastError();
 }
 

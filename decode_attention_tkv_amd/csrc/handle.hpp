@@ -1,75 +1,26 @@
 // The tkv handle: configuration, device buffers, host-side placement state.
 #pragma once
 
-#include <condition_variable>
 #include <cstdarg>
 #include <cstdio>
-#include <deque>
-#include <functional>
-#include <future>
-#include <mutex>
 #include <string>
-#include <thread>
 #include <vector>
 
 #include "tkv_internal.hpp"
 
 enum class TkvState { Empty, Ready, InStep };
 
-// One host thread per handle that runs the reassignments' arena jobs in
-// submission order; started on first use, joined on destruction after the
-// queue has drained.
-class HostWorker {
- public:
-  ~HostWorker() {
-    {
-      std::lock_guard<std::mutex> g(m_);
-      stop_ = true;
-    }
-    cv_.notify_one();
-    if (th_.joinable()) th_.join();
-  }
-  std::future<int> submit(std::function<int()> f) {
-    std::packaged_task<int()> task(std::move(f));
-    std::future<int> fut = task.get_future();
-    {
-      std::lock_guard<std::mutex> g(m_);
-      if (!th_.joinable()) th_ = std::thread([this] { run(); });
-      q_.push_back(std::move(task));
-    }
-    cv_.notify_one();
-    return fut;
-  }
-
- private:
-  void run() {
-    for (;;) {
-      std::packaged_task<int()> task;
-      {
-        std::unique_lock<std::mutex> lk(m_);
-        cv_.wait(lk, [&] { return stop_ || !q_.empty(); });
-        if (q_.empty()) return;
-        task = std::move(q_.front());
-        q_.pop_front();
-      }
-      task();
-    }
-  }
-  std::thread th_;
-  std::mutex m_;
-  std::condition_variable cv_;
-  std::deque<std::packaged_task<int()>> q_;
-  bool stop_ = false;
-};
-
 struct tkv {
   // ---- configuration
   int L = 0, Hq = 0, Hkv = 0, D = 0, B = 0, nmax = 0, dtype = 0, esz = 0, group = 0;
   int delta = 0, chunk = 256, S = 0;  // S = staging slots (== L when resident)
   bool resident = true;
+  bool vector_pass = false;  // bf16 grouped-query heads on the vector units (TKV_FLAG_VECTOR_PASS)
   double hbm = 0, evict = 0, t2 = 0;
   int prompt = 0, sinks = 0, recent = 0;
   uint64_t flags = 0;
+  int64_t mem_cap = 0;   // most device + pinned bytes the handle may hold (0: no cap)
+  int64_t mem_held = 0;  // device + pinned bytes held now
   int cap0 = 0, cap1 = 0, cap2 = 0, capS = 0, max_chunks = 0;  // capS: staging rows per slot
   int sh = 1;  // T2 scales per row: Hkv with per-head scales, else 1
   int lstride = 0;  // logits row stride: nmax rounded up to whole lines
@@ -90,6 +41,8 @@ struct tkv {
   float* part_o = nullptr;       // [L][B][Hq][max_chunks][D]
   float* layer_score = nullptr;  // [L][B][lstride]
   uint8_t* tier_alt = nullptr;   // [B][nmax] labels being computed by a reassignment
+  uint64_t* d_cuts = nullptr;    // batch-shared budget: [B][3] cut keys of the select-only pass
+  int32_t* d_n0c = nullptr;      // batch-shared budget: [B] T0 share from the joint select
   // changed rows of a reassignment, one block: counts [B][2] (padded to 16 B),
   // then promote [B][nmax], then demote [B][nmax]; mirrored in pinned host memory
   int32_t* d_counts = nullptr;
@@ -103,26 +56,9 @@ struct tkv {
   size_t d_ops_bytes = 0;
   void* h_ops = nullptr;  // pinned staging of ops + loc updates
   size_t h_ops_bytes = 0;
-  void* h_pack_in = nullptr;  // pinned: promoted T1 rows packed on the host (stream mode)
-  size_t h_pack_in_bytes = 0;
-  void* h_pack_out = nullptr;  // pinned: rows entering T1, [2][L][Hkv][E1][D]
-  size_t h_pack_out_bytes = 0;
-  void* h_qout = nullptr;      // pinned: rows entering T2, codes [2][L][Hkv][E2][D] + scales [2][L][E2]
-  size_t h_qout_bytes = 0;
-  void* h_qin = nullptr;       // pinned (stream mode): 8-bit rows fetched from the T2 arena
-  size_t h_qin_bytes = 0;
-  // device packs, persistent, grown on demand
+  // device pack, persistent, grown on demand
   void* fpack = nullptr;       // F: every moved row's value, K then V, [L][Hkv][rows][D] each
   size_t fpack_bytes = 0;
-  void* fin = nullptr;         // FI (stream mode): T1 rows fetched from the host, K then V
-  size_t fin_bytes = 0;
-  void* qin = nullptr;         // QIn (stream mode): T2 rows fetched from the host
-  size_t qin_bytes = 0;
-  void* qout = nullptr;        // QOut: rows entering T2
-  size_t qout_bytes = 0;
-  hipEvent_t ev_pack = nullptr;              // entrant rows landed in h_pack_out
-  std::future<int> arena_job;                // host arena maintenance of the last reassignment
-  HostWorker worker;                         // runs those jobs
 
   // ---- pinned host arenas (owned)
   void* arena1_k = nullptr;  // [L][B][Hkv][cap1][D]: T1 rows, dense per (layer, seq, head)
@@ -132,6 +68,13 @@ struct tkv {
   float* ascale_k = nullptr;   // [L][B][cap2]: T2 scales
   float* ascale_v = nullptr;
   std::vector<void*> host_allocs;
+  // the same arenas as the GPU addresses them (hipHostGetDevicePointer)
+  void* d_arena1_k = nullptr;
+  void* d_arena1_v = nullptr;
+  int8_t* d_arena2_k = nullptr;
+  int8_t* d_arena2_v = nullptr;
+  float* d_ascale_k = nullptr;
+  float* d_ascale_v = nullptr;
   // stream staging: one layer's 8-bit rows per slot, as they crossed PCIe; the
   // attention pass reads the codes directly
   int8_t* qstage_k = nullptr;  // [S][B][Hkv][cap2][D]
@@ -144,6 +87,10 @@ struct tkv {
   int64_t step = 0;
   int layers_done = 0;
   TkvState state = TkvState::Empty;
+  // A reassignment failed after the device labels changed: host and device
+  // placement state disagree, so every call but tkv_destroy, tkv_last_error
+  // and tkv_stats returns TKV_ESTATE.
+  bool failed = false;
   // The last completed step's Eq. 1 update of s, not yet applied: it runs
   // in the next append's launch, or before anything else reads or writes s.
   bool score_pending = false;
@@ -185,13 +132,13 @@ struct tkv {
   // ---- streams and events
   hipStream_t side = nullptr;           // host->device row traffic of the stream mode (K rows, 8-bit rows)
   hipStream_t side_v = nullptr;         // the same for V rows: two copy queues overlap their gaps (stream staging only)
-  hipStream_t wb = nullptr;             // device->host write-back of rows entering T1
-  hipEvent_t ev_gathered = nullptr;     // rows entering T1 are in the device pack
+  hipStream_t wb = nullptr;             // resident staging: the T1 arena's reassignment kernels
+  hipEvent_t ev_gathered = nullptr;     // resident staging: rows entering T1 are in F
   std::vector<hipEvent_t> ev_h2d;       // [S] staging slot filled (side)
   std::vector<hipEvent_t> ev_h2d_v;     // [S] its V rows filled (side_v)
   std::vector<hipEvent_t> ev_comp;      // [S] attention done reading the slot
   std::vector<char> comp_recorded;      // [S]
-  hipEvent_t ev_arena = nullptr;        // host arena writes of the last reassignment done
+  hipEvent_t ev_arena = nullptr;        // the last reassignment's arena kernels are done
   bool arena_pending = false;
   int next_issue = 0;                   // next layer whose staging copy is to be issued this step
 
@@ -201,6 +148,22 @@ struct tkv {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_pending;
 
   std::string err;
+
+  tkvd::ArenaSpace arenaspace() const {
+    tkvd::ArenaSpace a{};
+    a.a1_k = d_arena1_k;
+    a.a1_v = d_arena1_v;
+    a.a2_k = d_arena2_k;
+    a.a2_v = d_arena2_v;
+    a.s2_k = d_ascale_k;
+    a.s2_v = d_ascale_v;
+    a.batch = B;
+    a.kv_heads = Hkv;
+    a.cap1 = cap1;
+    a.cap2 = cap2;
+    a.sh = sh;
+    return a;
+  }
 
   tkvd::RowSpace rowspace() const {
     tkvd::RowSpace r{};

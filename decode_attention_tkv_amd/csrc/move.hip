@@ -39,7 +39,18 @@ __global__ __launch_bounds__(256) void k_place_rows(const PlaceArgs a) {
   }
 }
 
+// One wave sleeping a fixed number of times (each s_sleep 127 is 127 * 64
+// clock cycles), then leaving: a delay on a stream that always ends.
+__global__ __launch_bounds__(64) void k_delay(int iters) {
+  for (int i = 0; i < iters; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
 }  // namespace
+
+hipError_t launch_delay(int iters, hipStream_t s) {
+  k_delay<<<1, 64, 0, s>>>(iters);
+  return hipGetLastError();
+}
 
 hipError_t launch_place_rows(const PlaceArgs& a, int layers, hipStream_t s) {
   if (a.n_tokens <= 0) return hipSuccess;

@@ -11,8 +11,9 @@
 //   * T0 slots freed by demotions are reused by promotions.
 // Data movement:
 //   phase 1   every moved row's value lands in the fetch pack F (from the T0
-//             pool, the resident staging, or -- stream mode -- the pinned
-//             arenas, 8-bit rows dequantised on the GPU);
+//             pool, the resident staging, or -- stream staging -- the pinned
+//             arenas, read by the kernels over PCIe; 8-bit rows dequantised
+//             on the way);
 //   phase 2a  promotions F -> T0 slots; compaction moves inside the staging;
 //   phase 2b  rows entering T1: F -> staging; rows entering T2: quantised
 //             from F on the GPU (codes + scale out, dequantised values into
@@ -22,14 +23,22 @@
 // or T2, for their write-back, and T2 entrants get their dequantised values
 // in their own slots; phases 2a and 2b are empty.  T1/T2 rows keep a
 // host-side arena index per position.
-// Rows entering T1/T2 reach their pinned home through one write-back copy per
-// pack on a stream of their own; a host job (never waited for by the GPU)
-// compacts the arenas and files them.  Every area is head-major.
+// Where the arenas change:
+//   * stream staging: the kernels compact the pinned arenas and write the
+//     entrants (codes and scales for T2) straight into them, on the caller's
+//     stream, before the next step's copies read them (an event gates the
+//     copy streams).  No host thread touches a row.
+//   * resident staging: rows entering T1/T2 reach their pinned home through
+//     one write-back copy per pack on a stream of their own, and a host job
+//     (never waited for by the GPU, which reads only HBM in this mode)
+//     compacts the arenas and files them.
+// Every allocation a reassignment may need is made before the device labels
+// change; a failure after that point marks the handle failed (every later
+// call but tkv_destroy, tkv_last_error and tkv_stats returns TKV_ESTATE).
+// Every area is head-major.
 #include <algorithm>
 #include <chrono>
 #include <cstring>
-#include <memory>
-#include <thread>
 
 #include "handle.hpp"
 #include "host_util.hpp"
@@ -42,124 +51,68 @@ namespace {
 // of microseconds over PCIe, about one synchronisation round trip.
 constexpr size_t kOneCopyDeltaBytes = 1u << 20;
 
-enum SrcKind : uint8_t { kFromPool, kFromT1, kFromT2 };
-
-struct Move {
-  uint32_t pos;
-  SrcKind kind;
-  uint32_t idx;  // pool slot, T1 index or T2 index
-};
-
-struct SeqPlan {
-  std::vector<Move> ent1, ent2, promo;  // rows entering T1, T2 and T0
-  std::vector<uint32_t> promo_slot;
-  std::vector<std::pair<uint32_t, uint32_t>> mov1, mov2;  // arena (src, dst)
-  uint32_t m1 = 0, m2 = 0;              // arena rows kept before the entrants
-  int64_t e1off = 0, e2off = 0, poff = 0;  // offsets within the F segments
-};
-
-int grow_device(tkv* t, void** p, size_t* cap, size_t need) {
+// Grow a reassignment buffer to hold `need` bytes (twice that, when the
+// handle's memory cap allows, so that it rarely grows again).  Failure
+// (TKV_ENOMEM) leaves the buffer empty.
+int grow_buffer(tkv* t, void** p, size_t* cap, size_t need, bool pinned) {
   if (need <= *cap) return TKV_OK;
-  if (*p) HIP_TRY(t, hipFree(*p));
-  *p = nullptr;
-  *cap = 0;
-  const size_t bytes = std::max(need, (size_t)4096) * 2;
-  HIP_TRY(t, hipMalloc(p, bytes));
-  *cap = bytes;
-  return TKV_OK;
-}
-
-int grow_pinned(tkv* t, void** p, size_t* cap, size_t need) {
-  if (need <= *cap) return TKV_OK;
-  if (*p) HIP_TRY(t, hipHostFree(*p));
-  *p = nullptr;
-  *cap = 0;
-  const size_t bytes = std::max(need, (size_t)4096) * 2;
-  HIP_TRY(t, hipHostMalloc(p, bytes, hipHostMallocDefault));
-  *cap = bytes;
-  return TKV_OK;
-}
-
-// Dense-arena compaction: indices marked vacated leave; the kept rows above
-// the new size m move down into the holes below it, in order.
-void compact(std::vector<int32_t>& own, const std::vector<char>& vac, uint32_t* m,
-             std::vector<std::pair<uint32_t, uint32_t>>* moves) {
-  const uint32_t n = (uint32_t)own.size();
-  uint32_t kept = 0;
-  for (uint32_t i = 0; i < n; ++i) kept += vac[i] ? 0 : 1;
-  std::vector<uint32_t> holes, srcs;
-  for (uint32_t i = 0; i < kept; ++i)
-    if (vac[i]) holes.push_back(i);
-  for (uint32_t i = kept; i < n; ++i)
-    if (!vac[i]) srcs.push_back(i);
-  for (size_t k = 0; k < holes.size(); ++k) {
-    moves->emplace_back(srcs[k], holes[k]);
-    own[holes[k]] = own[srcs[k]];
+  if (*p) {
+    if (pinned)
+      HIP_TRY(t, hipHostFree(*p));
+    else
+      HIP_TRY(t, hipFree(*p));
   }
-  own.resize(kept);
-  *m = kept;
+  t->mem_held -= (int64_t)*cap;
+  *p = nullptr;
+  *cap = 0;
+  size_t bytes = std::max(need, (size_t)4096) * 2;
+  if (!within_cap(*t, bytes)) bytes = need;
+  if (!within_cap(*t, bytes))
+    return tkv_fail(t, TKV_ENOMEM, "memory cap (%lld bytes) reached: a reassignment needs %zu more bytes",
+                    (long long)t->mem_cap, need);
+  const hipError_t e = pinned ? hipHostMalloc(p, bytes, hipHostMallocDefault) : hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    return tkv_fail(t, TKV_ENOMEM, "%s(%zu bytes) failed: %s", pinned ? "hipHostMalloc" : "hipMalloc", bytes,
+                    hipGetErrorString(e));
+  }
+  *cap = bytes;
+  t->mem_held += (int64_t)bytes;
+  return TKV_OK;
 }
+int grow_device(tkv* t, void** p, size_t* cap, size_t need) { return grow_buffer(t, p, cap, need, false); }
+int grow_pinned(tkv* t, void** p, size_t* cap, size_t need) { return grow_buffer(t, p, cap, need, true); }
 
 }  // namespace
 
-// Batch-shared HBM budget: how many candidates of each sequence the joint
-// ranking puts in T0.  Per sequence the n3 lowest-ranked candidates are set
-// aside (eviction keeps its own budget); the rest of the batch is ranked by
-// (fp32 score descending, sequence ascending, position ascending) -- the
-// kernel's keys, extended by the sequence -- and the best
-// min(remaining, B * floor(hN) - sum |P|) go to T0.  T2 then takes its own
-// budget from what each sequence has left.
-static int shared_t0_counts(tkv* t, hipStream_t st, const std::vector<int64_t>& ncand, const std::vector<int64_t>& nprot,
-                     std::vector<CutCounts>* cuts) {
-  const int B = t->B, n = t->n;
-  const size_t nmax = t->nmax;
-  std::vector<float> s((size_t)B * nmax);
-  HIP_TRY(t, hipMemcpyAsync(s.data(), t->s, s.size() * 4, hipMemcpyDeviceToHost, st));
-  HIP_TRY(t, hipStreamSynchronize(st));
-  struct Key {
-    uint32_t bits;  // fp32 score bits: scores are >= 0, so the bits order as the values
-    int32_t b, pos;
-  };
-  auto better = [](const Key& x, const Key& y) {
-    if (x.bits != y.bits) return x.bits > y.bits;
-    if (x.b != y.b) return x.b < y.b;
-    return x.pos < y.pos;
-  };
-  std::vector<Key> remaining;
-  int64_t budget = 0;
-  for (int b = 0; b < B; ++b) {
-    std::vector<Key> cand;
-    cand.reserve(ncand[b]);
-    for (int p = 0; p < n; ++p) {
-      const uint8_t x = t->h_tier[(size_t)b * nmax + p];
-      if (x == TKV_T3 || is_protected(*t, p, n)) continue;
-      uint32_t bits;
-      std::memcpy(&bits, &s[(size_t)b * nmax + p], 4);
-      cand.push_back({bits, b, p});
+// Counts of a reassignment's changed rows, known from the lists alone (before
+// any host state changes): rows entering T1, T2 and T0, evictions.
+struct DeltaTotals {
+  int64_t e1 = 0, e2 = 0, p = 0, evict = 0, all = 0;
+};
+static DeltaTotals delta_totals(const tkv* t) {
+  DeltaTotals d{};
+  for (int b = 0; b < t->B; ++b)
+    for (int which = 0; which < 2; ++which) {
+      const tkv_delta* list = (which ? t->h_demote : t->h_promote) + (size_t)b * t->nmax;
+      const int cnt = t->h_counts[2 * b + which];
+      d.all += cnt;
+      for (int k = 0; k < cnt; ++k) {
+        switch (list[k].new_tier) {
+          case TKV_T0: d.p += 1; break;
+          case TKV_T1: d.e1 += 1; break;
+          case TKV_T2: d.e2 += 1; break;
+          default: d.evict += 1;
+        }
+      }
     }
-    std::sort(cand.begin(), cand.end(), better);
-    cand.resize(cand.size() - (size_t)(*cuts)[b].n3);  // the lowest n3 are evicted
-    remaining.insert(remaining.end(), cand.begin(), cand.end());
-    budget += floor_ratio(t->hbm, n) - nprot[b];
-  }
-  const int64_t take = std::min<int64_t>((int64_t)remaining.size(), std::max<int64_t>(0, budget));
-  std::vector<int64_t> n0c(B, 0);
-  if (take > 0) {
-    std::nth_element(remaining.begin(), remaining.begin() + (take - 1), remaining.end(), better);
-    const Key last = remaining[take - 1];
-    for (const Key& k : remaining)
-      if (!better(last, k)) n0c[k.b] += 1;  // k is at least as good as the last one taken
-  }
-  for (int b = 0; b < B; ++b) {
-    CutCounts& c = (*cuts)[b];
-    c.n0c = n0c[b];
-    c.n2 = std::min<int64_t>(ncand[b] - c.n3 - c.n0c, floor_ratio(t->t2, n));
-  }
-  return TKV_OK;
+  return d;
 }
 
 static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  if (t->failed) return tkv_fail(t, TKV_ESTATE, "handle unusable: an earlier reassignment failed part way");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "reassign between the layer groups of a step");
   if (t->n == 0) return TKV_OK;
   const auto wall0 = std::chrono::steady_clock::now();
@@ -168,12 +121,8 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
   const int B = t->B, L = t->L, n = t->n, H = t->Hkv, D = t->D;
   const size_t nmax = t->nmax;
   const size_t hb = (size_t)D * t->esz;  // bytes of one head's row
-  // The host arenas and the pinned packs may still be in use by the previous
-  // reassignment's host job and copies.
-  if (t->arena_job.valid()) {
-    const int rc = t->arena_job.get();
-    if (rc) return tkv_fail(t, rc, "host arena work of the last reassignment failed");
-  }
+  const bool stream_mode = !t->resident;
+  // The ops buffers may still be read by the last reassignment's kernels.
   HIP_TRY(t, hipStreamSynchronize(t->side));
   if (t->side_v) HIP_TRY(t, hipStreamSynchronize(t->side_v));
   HIP_TRY(t, hipEventSynchronize(t->ev_arena));
@@ -203,16 +152,42 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
     nprots[b] = np;
     cuts[b] = cut_counts(*t, n, np, nev);
   }
-  if (t->shared_hbm) {
-    int rc = shared_t0_counts(t, st, ncands, nprots, &cuts);
-    if (rc) return rc;
-  }
   for (int b = 0; b < B; ++b) {
     const int64_t ncand = ncands[b], n3 = cuts[b].n3, n0c = cuts[b].n0c, n2 = cuts[b].n2;
     ra.ncand[b] = (int32_t)ncand;
     ra.rank[b][0] = (int32_t)n3;
     ra.rank[b][1] = (int32_t)(n3 + n2);
     ra.rank[b][2] = (int32_t)(ncand - n0c);
+  }
+  if (t->shared_hbm) {
+    // Batch-shared budget, all on the GPU: each sequence's eviction cut
+    // (select-only pass), the joint select of the batch's best remaining
+    // candidates, then the labels with each sequence's share of T0.
+    int64_t remaining = 0, budget = 0;
+    for (int b = 0; b < B; ++b) {
+      remaining += ncands[b] - cuts[b].n3;
+      budget += floor_ratio(t->hbm, n) - nprots[b];
+      ra.rank[b][1] = ra.rank[b][2] = ra.ncand[b];  // no other cut in the select-only pass
+    }
+    ra.cuts_out = t->d_cuts;
+    HIP_TRY(t, launch_rank_label(ra, B, st));
+    JointArgs ja{};
+    ja.s = t->s;
+    ja.tier_old = t->tier;
+    ja.cuts = t->d_cuts;
+    ja.n0c = t->d_n0c;
+    ja.nmax = t->nmax;
+    ja.n = n;
+    ja.prompt = t->prompt;
+    ja.sinks = t->sinks;
+    ja.recent = t->recent;
+    ja.batch = B;
+    ja.remaining = remaining;
+    ja.take = std::min<int64_t>(remaining, std::max<int64_t>(0, budget));
+    HIP_TRY(t, launch_joint_select(ja, st));
+    ra.cuts_out = nullptr;
+    ra.n0c = t->d_n0c;
+    ra.t2cap = (int32_t)std::min<int64_t>(floor_ratio(t->t2, n), INT32_MAX);
   }
   HIP_TRY(t, launch_rank_label(ra, B, st));
   DeltaArgs da{};
@@ -241,152 +216,57 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
     }
     HIP_TRY(t, hipStreamSynchronize(st));
   }
-  std::swap(t->tier, t->tier_alt);  // device labels are now the new ones
 
-  // ---- placement plan
-  std::vector<SeqPlan> plan(B);
-  std::vector<LocUpdate> upd;
-  int64_t E1 = 0, E2 = 0, P = 0, n_evict = 0, n_prom = 0, n_dem = 0;
-  const uint32_t c1 = (uint32_t)t->cap0, c2 = (uint32_t)(t->cap0 + t->cap1);
-  std::vector<std::vector<char>> vac1s(B), vac2s(B);
-  // pass 1: who leaves which place; every freed T0 slot goes back to its free
-  // list before any promotion takes one (the lists are shared by the batch
-  // when the HBM budget is)
-  for (int b = 0; b < B; ++b) {
-    SeqPlan& sp = plan[b];
-    uint8_t* tr = &t->h_tier[b * nmax];
-    uint32_t* lc = &t->h_loc[b * nmax];
-    auto& vac1 = vac1s[b];
-    auto& vac2 = vac2s[b];
-    vac1.assign(t->t1_owner[b].size(), 0);
-    vac2.assign(t->t2_owner[b].size(), 0);
-    std::vector<uint32_t> freed;
-    uint32_t* ai = t->positional ? &t->h_aidx[b * nmax] : nullptr;
-    auto source = [&](uint32_t pos, uint8_t old) -> Move {
-      if (t->positional) {
-        // the row's values are at its own slot whatever its tier; a T1/T2
-        // row's departure leaves a hole in its arena
-        if (old == TKV_T1) vac1[ai[pos]] = 1;
-        if (old == TKV_T2) vac2[ai[pos]] = 1;
-        return {pos, kFromPool, pos};
-      }
-      if (old == TKV_T0) return {pos, kFromPool, lc[pos]};
-      if (old == TKV_T1) {
-        vac1[lc[pos] - c1] = 1;
-        return {pos, kFromT1, lc[pos] - c1};
-      }
-      vac2[lc[pos] - c2] = 1;
-      return {pos, kFromT2, lc[pos] - c2};
-    };
-    auto take = [&](const tkv_delta* list, int count) {
-      for (int k = 0; k < count; ++k) {
-        const tkv_delta& d = list[k];
-        const Move mv = source(d.pos, d.old_tier);
-        if (d.old_tier == TKV_T0 && !t->positional) freed.push_back(mv.idx);
-        switch (d.new_tier) {
-          case TKV_T0: sp.promo.push_back(mv); break;
-          case TKV_T1: sp.ent1.push_back(mv); break;
-          case TKV_T2: sp.ent2.push_back(mv); break;
-          default:
-            lc[d.pos] = kNoLoc;
-            upd.push_back({b, d.pos, kNoLoc});
-            ++n_evict;
-        }
-        tr[d.pos] = d.new_tier;
-      }
-    };
-    const int cp = t->h_counts[2 * b], cd = t->h_counts[2 * b + 1];
-    take(t->h_demote + b * nmax, cd);
-    take(t->h_promote + b * nmax, cp);
-    n_prom += cp;
-    n_dem += cd;
-    auto by_pos = [](const Move& x, const Move& y) { return x.pos < y.pos; };
-    std::sort(sp.ent1.begin(), sp.ent1.end(), by_pos);
-    std::sort(sp.ent2.begin(), sp.ent2.end(), by_pos);
-    for (auto it = freed.rbegin(); it != freed.rend(); ++it) t->free_list(b).push_back((int32_t)*it);
+  // ---- every buffer this reassignment can need, before any state changes:
+  // F holds every moved row once; the ops block is bounded by a few ops per
+  // changed row; the resident write-back packs hold the entrants.
+  const DeltaTotals tot = delta_totals(t);
+  {
+    const int64_t Fmax = tot.e1 + tot.e2 + (t->positional ? 0 : tot.p);
+    int rc = grow_device(t, &t->fpack, &t->fpack_bytes, 2 * (size_t)L * H * Fmax * hb);
+    const size_t ops_max = (size_t)tot.all * (4 * sizeof(RowOp) + sizeof(DequantOp) + sizeof(QuantOp) +
+                                              3 * sizeof(LocUpdate) + sizeof(RowOp));
+    if (!rc && ops_max) rc = grow_pinned(t, &t->h_ops, &t->h_ops_bytes, ops_max);
+    if (!rc && ops_max) rc = grow_device(t, &t->d_ops, &t->d_ops_bytes, ops_max);
+    if (rc) return rc;  // nothing has changed: the handle stays as it was
   }
-  // pass 2: promotions take T0 slots; arenas compact and take their entrants
-  for (int b = 0; b < B; ++b) {
-    SeqPlan& sp = plan[b];
-    uint8_t* tr = &t->h_tier[b * nmax];
-    uint32_t* lc = &t->h_loc[b * nmax];
-    auto& own1 = t->t1_owner[b];
-    auto& own2 = t->t2_owner[b];
-    if (t->positional) sp.promo.clear();  // promoted rows stay where they are
-    for (const Move& mv : sp.promo) {
-      if (t->free_list(b).empty()) return tkv_fail(t, TKV_ECAPACITY, "T0 pool full while promoting");
-      const uint32_t slot = (uint32_t)t->free_list(b).back();
-      t->free_list(b).pop_back();
-      sp.promo_slot.push_back(slot);
-      lc[mv.pos] = slot;
-      upd.push_back({b, mv.pos, slot});
+  std::swap(t->tier, t->tier_alt);  // device labels are now the new ones
+  // from here on a failure leaves device and host state apart
+  struct Poison {
+    tkv* t;
+    bool done = false;
+    ~Poison() {
+      if (!done) t->failed = true;
     }
-    // arenas: compaction, then the entrants at the end
-    compact(own1, vac1s[b], &sp.m1, &sp.mov1);
-    compact(own2, vac2s[b], &sp.m2, &sp.mov2);
-    uint32_t* ai = t->positional ? &t->h_aidx[b * nmax] : nullptr;
-    for (auto& mv : sp.mov1) {
-      if (ai) {
-        ai[own1[mv.second]] = mv.second;
-        continue;
-      }
-      lc[own1[mv.second]] = c1 + mv.second;
-      upd.push_back({b, (uint32_t)own1[mv.second], c1 + mv.second});
-    }
-    for (auto& mv : sp.mov2) {
-      if (ai) {
-        ai[own2[mv.second]] = mv.second;
-        continue;
-      }
-      lc[own2[mv.second]] = c2 + mv.second;
-      upd.push_back({b, (uint32_t)own2[mv.second], c2 + mv.second});
-    }
-    if (sp.m1 + sp.ent1.size() > (size_t)t->cap1) return tkv_fail(t, TKV_ECAPACITY, "T1 arena full");
-    if (sp.m2 + sp.ent2.size() > (size_t)t->cap2) return tkv_fail(t, TKV_ECAPACITY, "T2 arena full");
-    for (size_t e = 0; e < sp.ent1.size(); ++e) {
-      own1.push_back((int32_t)sp.ent1[e].pos);
-      if (ai) {
-        ai[sp.ent1[e].pos] = sp.m1 + (uint32_t)e;
-        continue;
-      }
-      lc[sp.ent1[e].pos] = c1 + sp.m1 + (uint32_t)e;
-      upd.push_back({b, sp.ent1[e].pos, c1 + sp.m1 + (uint32_t)e});
-    }
-    for (size_t e = 0; e < sp.ent2.size(); ++e) {
-      own2.push_back((int32_t)sp.ent2[e].pos);
-      if (ai) {
-        ai[sp.ent2[e].pos] = sp.m2 + (uint32_t)e;
-        continue;
-      }
-      lc[sp.ent2[e].pos] = c2 + sp.m2 + (uint32_t)e;
-      upd.push_back({b, sp.ent2[e].pos, c2 + sp.m2 + (uint32_t)e});
-    }
-    sp.e1off = E1;
-    sp.e2off = E2;
-    sp.poff = P;
-    E1 += (int64_t)sp.ent1.size();
-    E2 += (int64_t)sp.ent2.size();
-    P += (int64_t)sp.promo.size();
-    int32_t evicted_b = 0;
-    for (int p = 0; p < n; ++p) evicted_b += tr[p] == TKV_T3 ? 1 : 0;
-    t->nlive[b] = n - evicted_b;
+  } poison{t};
+
+  // ---- placement plan (host mirror of tiers, locations, free slots, arenas)
+  PlanConfig pc{B, t->nmax, n, t->cap0, t->cap1, t->cap2, t->positional, t->shared_hbm};
+  PlanState ps{&t->h_tier, &t->h_loc, &t->h_aidx, &t->free0, &t->t1_owner, &t->t2_owner, &t->nlive};
+  PlanResult pr;
+  {
+    std::string why;
+    const int rc = make_plan(pc, ps, t->h_counts, t->h_promote, t->h_demote, &pr, &why);
+    if (rc) return tkv_fail(t, rc, "%s", why.c_str());
   }
+  const std::vector<SeqPlan>& plan = pr.seq;
+  const std::vector<LocUpdate>& upd = pr.upd;
+  const int64_t E1 = pr.e1, E2 = pr.e2, P = pr.p;
+  const uint32_t c2 = (uint32_t)(t->cap0 + t->cap1);
 
   // ---- F layout: [rows entering T1 | rows entering T2 | promotions]
   const int64_t F = E1 + E2 + P;
   const size_t f_bytes = (size_t)L * H * F * hb;  // per K|V
-  {
-    int rc = grow_device(t, &t->fpack, &t->fpack_bytes, 2 * f_bytes);
-    if (rc) return rc;
-  }
   FPack fp{t->fpack, (char*)t->fpack + f_bytes, F};
 
-  // ---- phase 1 sources
-  std::vector<RowOp> ops1, ops2a, ops2b;
+  // ---- ops
+  // ops1: phase 1 fetch into F; ops2a: promotions (+ resident staging
+  // compaction); ops2b: resident staging entrants; am1/am2: arena compaction
+  // (T1, T2); ae1: T1 entrants into the arena; q2: T2 entrants quantised into
+  // the arena
+  std::vector<RowOp> ops1, ops2a, ops2b, am1, am2, ae1;
   std::vector<DequantOp> dq1;
   std::vector<QuantOp> q2;
-  // stream mode: rows that live only on the host are packed there first
-  std::vector<std::pair<int, uint32_t>> host_t1, host_t2;  // (sequence, arena index) in pack order
   auto fetch = [&](int b, const Move& mv, uint32_t frow) {
     if (mv.kind == kFromPool) {
       ops1.push_back({kAreaPool, kAreaPackOut, (uint16_t)b, mv.idx, frow});
@@ -394,11 +274,9 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
       const uint32_t sidx = mv.kind == kFromT1 ? mv.idx : (uint32_t)t->cap1 + mv.idx;
       ops1.push_back({kAreaStage, kAreaPackOut, (uint16_t)b, sidx, frow});
     } else if (mv.kind == kFromT1) {
-      ops1.push_back({kAreaPackIn, kAreaPackOut, (uint16_t)b, (uint32_t)host_t1.size(), frow});
-      host_t1.emplace_back(b, mv.idx);
+      ops1.push_back({kAreaArena1, kAreaPackOut, (uint16_t)b, mv.idx, frow});  // over PCIe
     } else {
-      dq1.push_back({(uint16_t)b, (uint32_t)host_t2.size(), frow});
-      host_t2.emplace_back(b, mv.idx);
+      dq1.push_back({(uint16_t)b, mv.idx, frow});  // 8-bit row over PCIe, dequantised
     }
   };
   for (int b = 0; b < B; ++b) {
@@ -418,76 +296,32 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
       for (size_t e = 0; e < sp.ent1.size(); ++e)
         ops2b.push_back({kAreaPackOut, kAreaStage, (uint16_t)b, (uint32_t)(sp.e1off + e), sp.m1 + (uint32_t)e});
     }
-    // the dequantised values go to the row's location: its own slot
-    // (positional), its new staging place (resident), or nowhere (stream)
+    // the pinned arenas: compaction, then the entrants at the end
+    for (auto& mv : sp.mov1) am1.push_back({kAreaArena1, kAreaArena1, (uint16_t)b, mv.first, mv.second});
+    for (auto& mv : sp.mov2) am2.push_back({0, 0, (uint16_t)b, mv.first, mv.second});
+    for (size_t e = 0; e < sp.ent1.size(); ++e)
+      ae1.push_back({kAreaPackOut, kAreaArena1, (uint16_t)b, (uint32_t)(sp.e1off + e), sp.m1 + (uint32_t)e});
+    // T2 entrants: codes and scales into the arena (index m2 + e); the
+    // dequantised values go to the row's location: its own slot (positional),
+    // its new staging place (resident), or nowhere (stream)
     for (size_t e = 0; e < sp.ent2.size(); ++e)
-      q2.push_back({(uint16_t)b, (uint32_t)(E1 + sp.e2off + e), (uint32_t)(sp.e2off + e),
+      q2.push_back({(uint16_t)b, (uint32_t)(E1 + sp.e2off + e), sp.m2 + (uint32_t)e,
                     t->positional ? sp.ent2[e].pos
                     : t->resident ? c2 + sp.m2 + (uint32_t)e : kNoLoc});
   }
 
-  // ---- stream mode: host-resident sources packed and sent
-  const int64_t NF1 = (int64_t)host_t1.size(), NF2 = (int64_t)host_t2.size();
-  auto a1row = [&](int which, int l, int b, int h, uint32_t idx) -> char* {
-    return (char*)(which ? t->arena1_v : t->arena1_k) + ((((size_t)l * B + b) * H + h) * t->cap1 + idx) * hb;
-  };
-  const size_t qrow = (size_t)D;  // bytes of one head's int8 row
-  if (NF1 > 0) {
-    const size_t half = (size_t)L * H * NF1 * hb;
-    int rc = grow_pinned(t, &t->h_pack_in, &t->h_pack_in_bytes, 2 * half);
-    if (!rc) rc = grow_device(t, &t->fin, &t->fin_bytes, 2 * half);
-    if (rc) return rc;
-    for (int64_t i = 0; i < NF1; ++i)
-      for (int which = 0; which < 2; ++which)
-        for (int l = 0; l < L; ++l)
-          for (int h = 0; h < H; ++h)
-            std::memcpy((char*)t->h_pack_in + ((((size_t)which * L + l) * H + h) * NF1 + i) * hb,
-                        a1row(which, l, host_t1[i].first, h, host_t1[i].second), hb);
-    HIP_TRY(t, hipMemcpyAsync(t->fin, t->h_pack_in, 2 * half, hipMemcpyHostToDevice, st));
-    t->st.h2d_bytes += 2 * (int64_t)half;
-  }
-  QPack qin{};
-  if (NF2 > 0) {
-    const size_t codes_half = (size_t)L * H * NF2 * qrow, sc_half = (size_t)L * NF2 * t->sh * 4;
-    const size_t bytes = 2 * codes_half + 2 * sc_half;
-    int rc = grow_pinned(t, &t->h_qin, &t->h_qin_bytes, bytes);
-    if (!rc) rc = grow_device(t, &t->qin, &t->qin_bytes, bytes);
-    if (rc) return rc;
-    char* hc = (char*)t->h_qin;
-    float* hs = (float*)(hc + 2 * codes_half);
-    for (int64_t i = 0; i < NF2; ++i) {
-      const int b = host_t2[i].first;
-      const uint32_t idx = host_t2[i].second;
-      for (int which = 0; which < 2; ++which)
-        for (int l = 0; l < L; ++l) {
-          for (int h = 0; h < H; ++h)
-            std::memcpy(hc + ((((size_t)which * L + l) * H + h) * NF2 + i) * qrow,
-                        (which ? t->arena2_v : t->arena2_k) + ((((size_t)l * B + b) * H + h) * t->cap2 + idx) * qrow,
-                        qrow);
-          for (int k = 0; k < t->sh; ++k)
-            hs[(((size_t)which * L + l) * NF2 + i) * t->sh + k] =
-                (which ? t->ascale_v : t->ascale_k)[(((size_t)l * B + b) * t->cap2 + idx) * t->sh + k];
-        }
-    }
-    HIP_TRY(t, hipMemcpyAsync(t->qin, t->h_qin, bytes, hipMemcpyHostToDevice, st));
-    t->st.h2d_bytes += (int64_t)bytes;
-    qin = QPack{(int8_t*)t->qin, (float*)((char*)t->qin + 2 * codes_half), NF2};
-  }
-
-  // ---- ops and location updates to the device
-  const size_t nops = ops1.size() + ops2a.size() + ops2b.size();
-  const size_t bytes = nops * sizeof(RowOp) + dq1.size() * sizeof(DequantOp) + q2.size() * sizeof(QuantOp) +
-                       upd.size() * sizeof(LocUpdate);
-  const RowOp* d_ops1 = nullptr;
-  const RowOp* d_ops2a = nullptr;
-  const RowOp* d_ops2b = nullptr;
+  // ---- ops and location updates to the device (buffers grown above)
+  const size_t bytes = (ops1.size() + ops2a.size() + ops2b.size() + am1.size() + am2.size() + ae1.size()) *
+                           sizeof(RowOp) +
+                       dq1.size() * sizeof(DequantOp) + q2.size() * sizeof(QuantOp) + upd.size() * sizeof(LocUpdate);
+  if (bytes > t->h_ops_bytes || bytes > t->d_ops_bytes)
+    return tkv_fail(t, TKV_EHIP, "internal error: reassignment ops (%zu bytes) exceed their buffer", bytes);
+  const RowOp *d_ops1 = nullptr, *d_ops2a = nullptr, *d_ops2b = nullptr, *d_am1 = nullptr, *d_am2 = nullptr,
+              *d_ae1 = nullptr;
   const DequantOp* d_dq1 = nullptr;
   const QuantOp* d_q2 = nullptr;
   const LocUpdate* d_upd = nullptr;
   if (bytes > 0) {
-    int rc = grow_pinned(t, &t->h_ops, &t->h_ops_bytes, bytes);
-    if (!rc) rc = grow_device(t, &t->d_ops, &t->d_ops_bytes, bytes);
-    if (rc) return rc;
     char* h = (char*)t->h_ops;
     char* d = (char*)t->d_ops;
     size_t off = 0;
@@ -500,36 +334,41 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
     d_ops1 = (const RowOp*)put(ops1.data(), ops1.size() * sizeof(RowOp));
     d_ops2a = (const RowOp*)put(ops2a.data(), ops2a.size() * sizeof(RowOp));
     d_ops2b = (const RowOp*)put(ops2b.data(), ops2b.size() * sizeof(RowOp));
+    d_am1 = (const RowOp*)put(am1.data(), am1.size() * sizeof(RowOp));
+    d_am2 = (const RowOp*)put(am2.data(), am2.size() * sizeof(RowOp));
+    d_ae1 = (const RowOp*)put(ae1.data(), ae1.size() * sizeof(RowOp));
     d_dq1 = (const DequantOp*)put(dq1.data(), dq1.size() * sizeof(DequantOp));
     d_q2 = (const QuantOp*)put(q2.data(), q2.size() * sizeof(QuantOp));
     d_upd = (const LocUpdate*)put(upd.data(), upd.size() * sizeof(LocUpdate));
     HIP_TRY(t, hipMemcpyAsync(t->d_ops, t->h_ops, bytes, hipMemcpyHostToDevice, st));
   }
 
-  // ---- device phases
+  // ---- device phases.  The caller's stream first waits for the last
+  // reassignment's arena work (it read F, which phase 1 overwrites).
+  if (t->arena_pending) HIP_TRY(t, hipStreamWaitEvent(st, t->ev_arena, 0));
+  const ArenaSpace arena = t->arenaspace();
   CopyArgs ca{};
   ca.rows = t->rowspace();
+  ca.arena = arena;
   ca.kv_heads = H;
   ca.head_bytes = (int32_t)hb;
   ca.elem_bytes = t->esz;
   ca.pack_out_k = fp.k;  // F
   ca.pack_out_v = fp.v;
   ca.pack_out_rows = F;
-  ca.pack_in_k = t->fin;  // FI
-  ca.pack_in_v = t->fin ? (char*)t->fin + (size_t)L * H * NF1 * hb : nullptr;
-  ca.pack_in_rows = NF1;
-  HIP_TRY(t, launch_copy_rows(ca, d_ops1, (int)ops1.size(), L, st));
-  DequantArgs dqa{qin, fp, H, D, t->esz, (t->flags & TKV_FLAG_T2_FP8) ? 1 : 0, t->sh};
+  const int fp8 = (t->flags & TKV_FLAG_T2_FP8) ? 1 : 0;
+  HIP_TRY(t, launch_copy_rows(ca, d_ops1, (int)ops1.size(), L, 0, st));
+  DequantArgs dqa{arena, fp, H, D, t->esz, fp8, t->sh};
   HIP_TRY(t, launch_dequant_rows(dqa, d_dq1, (int)dq1.size(), L, st));
-  HIP_TRY(t, launch_copy_rows(ca, d_ops2a, (int)ops2a.size(), L, st));
-  HIP_TRY(t, launch_copy_rows(ca, d_ops2b, (int)ops2b.size(), L, st));
-  QPack qout{};
+  HIP_TRY(t, launch_copy_rows(ca, d_ops2a, (int)ops2a.size(), L, 0, st));
+  HIP_TRY(t, launch_copy_rows(ca, d_ops2b, (int)ops2b.size(), L, 0, st));
+  // The T2 arena on this stream: compaction (every fetch from it is done; a
+  // move's source, a kept row past the new size, is no op's destination),
+  // then the entrants past the kept rows, whose dequantised values the next
+  // step reads.
+  HIP_TRY(t, launch_arena2_moves(arena, d_am2, (int)am2.size(), L, D, kArenaBlocks, st));
   if (E2 > 0) {
-    const size_t codes_half = (size_t)L * H * E2 * qrow, sc_half = (size_t)L * E2 * t->sh * 4;
-    int rc = grow_device(t, &t->qout, &t->qout_bytes, 2 * codes_half + 2 * sc_half);
-    if (rc) return rc;
-    qout = QPack{(int8_t*)t->qout, (float*)((char*)t->qout + 2 * codes_half), E2};
-    QuantArgs qa{t->rowspace(), fp, qout, H, D, t->esz, (t->flags & TKV_FLAG_T2_FP8) ? 1 : 0, t->sh};
+    QuantArgs qa{t->rowspace(), fp, arena, H, D, t->esz, fp8, t->sh};
     HIP_TRY(t, launch_quant_rows(qa, d_q2, (int)q2.size(), L, st));
   }
   HIP_TRY(t, launch_set_loc(d_upd, (int)upd.size(), t->loc, t->nmax, st));
@@ -541,117 +380,33 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
   la.nmax = t->nmax;
   la.n = n;
   HIP_TRY(t, launch_build_live(la, B, st));
-  HIP_TRY(t, hipEventRecord(t->ev_gathered, st));
-
-  // ---- write-back of the entrants, on its own stream
-  if (E1 > 0 || E2 > 0) HIP_TRY(t, hipStreamWaitEvent(t->wb, t->ev_gathered, 0));
-  if (E1 > 0) {
-    const size_t half = (size_t)L * H * E1 * hb;
-    int rc = grow_pinned(t, &t->h_pack_out, &t->h_pack_out_bytes, 2 * half);
-    if (rc) return rc;
-    for (int which = 0; which < 2; ++which)
-      HIP_TRY(t, hipMemcpy2DAsync((char*)t->h_pack_out + which * half, E1 * hb, which ? fp.v : fp.k, F * hb, E1 * hb,
-                                  (size_t)L * H, hipMemcpyDeviceToHost, t->wb));
-    t->st.d2h_bytes += 2 * (int64_t)half;
+  // The T1 arena the same way.  Stream staging: on this stream, before the
+  // next step's copies read it.  Resident staging (no kernel reads the
+  // arena): on the write-back stream, beside the next steps, from a few
+  // work-groups that loop over the rows.
+  hipStream_t as = st;
+  if (!stream_mode) {
+    HIP_TRY(t, hipEventRecord(t->ev_gathered, st));
+    HIP_TRY(t, hipStreamWaitEvent(t->wb, t->ev_gathered, 0));
+    as = t->wb;
   }
-  if (E2 > 0) {
-    const size_t qbytes = 2 * (size_t)L * H * E2 * qrow + 2 * (size_t)L * E2 * t->sh * 4;
-    int rc = grow_pinned(t, &t->h_qout, &t->h_qout_bytes, qbytes);
-    if (rc) return rc;
-    HIP_TRY(t, hipMemcpyAsync(t->h_qout, t->qout, qbytes, hipMemcpyDeviceToHost, t->wb));
-    t->st.d2h_bytes += (int64_t)qbytes;
-  }
-  HIP_TRY(t, hipEventRecord(t->ev_pack, t->wb));
-  HIP_TRY(t, hipEventRecord(t->ev_arena, st));
+  HIP_TRY(t, launch_copy_rows(ca, d_am1, (int)am1.size(), L, kArenaBlocks, as));
+  HIP_TRY(t, launch_copy_rows(ca, d_ae1, (int)ae1.size(), L, kArenaBlocks, as));
+  HIP_TRY(t, hipEventRecord(t->ev_arena, as));
   t->arena_pending = true;
-
-  // ---- host job: compact the arenas, file the entrants
-  bool any_host_work = E1 > 0 || E2 > 0;
-  for (int b = 0; b < B && !any_host_work; ++b) any_host_work = !plan[b].mov1.empty() || !plan[b].mov2.empty();
-  if (any_host_work) {
-    struct Job {
-      std::vector<SeqPlan> plan;
-      char *a1k, *a1v;
-      int8_t *a2k, *a2v;
-      float *s2k, *s2v;
-      const char* pack1;  // [2][L][H][E1][D] cache type
-      const char* pack2;  // codes [2][L][H][E2][D], scales [2][L][E2][SH]
-      hipEvent_t ev;
-      int L, B, H, D, SH;
-      size_t cap1, cap2, hb;
-      int64_t E1, E2;
-    };
-    auto job = std::make_shared<Job>(Job{std::move(plan), (char*)t->arena1_k, (char*)t->arena1_v, t->arena2_k,
-                                         t->arena2_v, t->ascale_k, t->ascale_v, (const char*)t->h_pack_out,
-                                         (const char*)t->h_qout, t->ev_pack, L, B, H, D, t->sh, (size_t)t->cap1,
-                                         (size_t)t->cap2, hb, E1, E2});
-    t->arena_job = t->worker.submit([job]() -> int {
-     try {
-      const Job& j = *job;
-      auto r1 = [&](int which, int l, int b, int h, uint32_t idx) -> char* {
-        return (which ? j.a1v : j.a1k) + ((((size_t)l * j.B + b) * j.H + h) * j.cap1 + idx) * j.hb;
-      };
-      auto r2 = [&](int which, int l, int b, int h, uint32_t idx) -> int8_t* {
-        return (which ? j.a2v : j.a2k) + ((((size_t)l * j.B + b) * j.H + h) * j.cap2 + idx) * j.D;
-      };
-      auto s2 = [&](int which, int l, int b, uint32_t idx) -> float* {
-        return (which ? j.s2v : j.s2k) + (((size_t)l * j.B + b) * j.cap2 + idx) * j.SH;
-      };
-      auto moves = [&](int l0, int l1) {
-        for (int l = l0; l < l1; ++l)
-          for (int b = 0; b < j.B; ++b)
-            for (int which = 0; which < 2; ++which) {
-              for (auto& mv : j.plan[b].mov1)
-                for (int h = 0; h < j.H; ++h) std::memcpy(r1(which, l, b, h, mv.second), r1(which, l, b, h, mv.first), j.hb);
-              for (auto& mv : j.plan[b].mov2) {
-                for (int h = 0; h < j.H; ++h) std::memcpy(r2(which, l, b, h, mv.second), r2(which, l, b, h, mv.first), j.D);
-                std::memcpy(s2(which, l, b, mv.second), s2(which, l, b, mv.first), j.SH * 4);
-              }
-            }
-      };
-      auto file = [&](int l0, int l1) {
-        const size_t c2half = (size_t)j.L * j.H * j.E2 * j.D;
-        const float* sc = (const float*)(j.pack2 + 2 * c2half);
-        for (int l = l0; l < l1; ++l)
-          for (int b = 0; b < j.B; ++b)
-            for (int which = 0; which < 2; ++which) {
-              const SeqPlan& sp = j.plan[b];
-              const size_t n1 = sp.ent1.size(), n2 = sp.ent2.size();
-              for (int h = 0; h < j.H && n1; ++h)
-                std::memcpy(r1(which, l, b, h, sp.m1),
-                            j.pack1 + ((((size_t)which * j.L + l) * j.H + h) * j.E1 + sp.e1off) * j.hb, n1 * j.hb);
-              for (int h = 0; h < j.H && n2; ++h)
-                std::memcpy(r2(which, l, b, h, sp.m2),
-                            j.pack2 + ((((size_t)which * j.L + l) * j.H + h) * j.E2 + sp.e2off) * j.D, n2 * j.D);
-              if (n2)
-                std::memcpy(s2(which, l, b, sp.m2), sc + (((size_t)which * j.L + l) * j.E2 + sp.e2off) * j.SH,
-                            n2 * j.SH * 4);
-            }
-      };
-      const int nth = std::min(4, j.L);
-      auto split = [&](const std::function<void(int, int)>& f) {
-        std::vector<std::thread> th;
-        for (int i = 1; i < nth; ++i) th.emplace_back(f, j.L * i / nth, j.L * (i + 1) / nth);
-        f(0, j.L / nth);
-        for (auto& x : th) x.join();
-      };
-      split(moves);
-      if (j.E1 > 0 || j.E2 > 0) {
-        if (hipEventSynchronize(j.ev) != hipSuccess) return TKV_EHIP;
-        split(file);
-      }
-      return TKV_OK;
-     } catch (const std::bad_alloc&) {  // the job reports, never throws
-      return TKV_ENOMEM;
-     } catch (...) {
-      return TKV_EHIP;
-     }
-    });
+  {
+    const size_t qrow = (size_t)D;  // bytes of one head's 8-bit row
+    int64_t h2d = 0;
+    for (const RowOp& o : ops1) h2d += o.src_area == kAreaArena1 ? 2 * (int64_t)L * H * hb : 0;
+    h2d += (int64_t)dq1.size() * 2 * L * (H * qrow + t->sh * 4);
+    t->st.h2d_bytes += h2d;
+    t->st.d2h_bytes += 2 * (int64_t)L * H * (E1 * hb + E2 * qrow) + 2 * (int64_t)L * E2 * t->sh * 4;
   }
 
-  t->st.promotions += n_prom;
-  t->st.demotions += n_dem;
-  t->st.evictions += n_evict;
+  poison.done = true;
+  t->st.promotions += pr.promotions;
+  t->st.demotions += pr.demotions;
+  t->st.evictions += pr.evictions;
   t->st.reassigns += 1;
   t->st.reassign_ms +=
       std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - wall0).count();

@@ -10,13 +10,12 @@
 #include <vector>
 
 #include "../../include/tkv.h"
+#include "plan.hpp"
 
 namespace tkvd {
 
 constexpr int kMaxBatch = 64;
 constexpr int kMaxQHeads = 256;
-constexpr uint32_t kNoLoc = 0xFFFFFFFFu;  // loc code of evicted / unused positions
-constexpr uint8_t kUnused = 255;           // tier code of positions not appended yet
 
 // ---- kernel argument blocks (passed by value) ------------------------------
 
@@ -159,6 +158,27 @@ struct RankArgs {
   int32_t nmax, n, prompt, sinks, recent;
   int32_t ncand[kMaxBatch];    // candidates (live, unprotected) per sequence
   int32_t rank[kMaxBatch][3];  // ascending-rank cut points: first non-T3, first non-T2, first T0
+  // cuts_out set: only find the cut keys and store them ([batch][3]); no labels
+  uint64_t* cuts_out;
+  // batch-shared HBM budget: the T0 count of each sequence comes from the
+  // joint select on the device; then rank[b][1] = n3 + min(ncand - n3 - n0c,
+  // t2cap) and rank[b][2] = ncand - n0c, with n3 = rank[b][0]
+  const int32_t* n0c;
+  int32_t t2cap;
+};
+
+// Batch-shared HBM budget: one select over the remaining candidates of every
+// sequence (per-sequence key at or above cut3[b], the sequence's lowest
+// kept key), ordered by the joint key (bits(s) << 32) | ((63 - b) << 26) |
+// (2^26 - 1 - position): best score first, then lower sequence, then lower
+// position.  The `take` best go to T0; n0c[b] counts those of sequence b.
+struct JointArgs {
+  const float* s;
+  const uint8_t* tier_old;
+  const uint64_t* cuts;  // [batch][3] from the select-only rank pass; [b][0] = cut3
+  int32_t* n0c;          // [batch] out
+  int32_t nmax, n, prompt, sinks, recent, batch;
+  int64_t remaining, take;
 };
 
 struct DeltaArgs {
@@ -170,12 +190,6 @@ struct DeltaArgs {
   int32_t nmax, n;
 };
 
-struct LocUpdate {
-  int32_t b;
-  uint32_t pos;
-  uint32_t code;
-};
-
 struct LiveArgs {
   const uint8_t* tier;
   const uint32_t* loc;
@@ -184,8 +198,22 @@ struct LiveArgs {
   int32_t nmax, n;
 };
 
+// The pinned host arenas (the home of T1 and T2 rows) as kernels address
+// them.  With stream staging a reassignment reads rows leaving an arena and
+// writes rows entering it straight over PCIe, in stream order, so no host
+// thread copies rows and no host pack is needed.
+struct ArenaSpace {
+  void* a1_k;   // T1 rows [layers][batch][kv_heads][cap1][head_dim], cache type
+  void* a1_v;
+  int8_t* a2_k; // T2 codes [layers][batch][kv_heads][cap2][head_dim]
+  int8_t* a2_v;
+  float* s2_k;  // T2 scales [layers][batch][cap2][sh]
+  float* s2_v;
+  int32_t batch, kv_heads, cap1, cap2, sh;
+};
+
 // Row areas of a copy op.  Packs are [layers][kv_heads][rows][head_dim].
-enum : uint8_t { kAreaPool = 0, kAreaStage = 1, kAreaPackOut = 2, kAreaPackIn = 3 };
+enum : uint8_t { kAreaPool = 0, kAreaStage = 1, kAreaPackOut = 2, kAreaArena1 = 3 };
 
 struct RowOp {
   uint8_t src_area, dst_area;
@@ -195,23 +223,14 @@ struct RowOp {
 
 struct CopyArgs {
   RowSpace rows;
+  ArenaSpace arena;
   void* pack_out_k;
   void* pack_out_v;
-  void* pack_in_k;
-  void* pack_in_v;
-  int64_t pack_out_rows, pack_in_rows;
+  int64_t pack_out_rows;
   int32_t kv_heads, head_bytes, elem_bytes;  // head_bytes = head_dim * elem_bytes
 };
 
 // ---- 8-bit host tier codec (codec.hip) ---------------------------------------
-// Quantised rows: codes [2 (K,V)][layers][kv_heads][rows][head_dim] int8 and
-// one fp32 scale per (K|V, layer, row): scales [2][layers][rows].
-struct QPack {
-  int8_t* codes;   // [2][layers][kv_heads][rows][head_dim]
-  float* scales;   // [2][layers][rows][sh]
-  int64_t rows;    // row stride of this pack
-};
-
 // Fetch pack F: every moved row's value, [layers][kv_heads][rows][head_dim]
 struct FPack {
   void* k;
@@ -222,28 +241,31 @@ struct FPack {
 struct QuantOp {
   uint16_t b;
   uint32_t src;    // F row
-  uint32_t dst;    // QPack row
+  uint32_t dst;    // T2 arena index
   uint32_t stage;  // location code that receives the dequantised values (pool slot, or cap0 +
                    // staging index), or kNoLoc
 };
 
+// Rows entering T2: F row src quantised into T2 arena index dst of sequence b
+// (codes [layers][batch][kv_heads][cap2][head_dim], scales [layers][batch][cap2][sh]).
 struct QuantArgs {
   RowSpace rows;
   FPack f;
-  QPack out;
+  ArenaSpace arena;
   int32_t kv_heads, head_dim, elem_bytes;
   int32_t fp8;  // FP8 E4M3 codes (else int8)
   int32_t sh;   // scales per row: kv_heads or 1
 };
 
+// T2 arena row src of sequence b -> cache-type values in F row dst.
 struct DequantOp {
   uint16_t b;
-  uint32_t src;  // QPack row
-  uint32_t dst;  // F row
+  uint32_t src;
+  uint32_t dst;
 };
 
 struct DequantArgs {
-  QPack in;
+  ArenaSpace arena;
   FPack f;
   int32_t kv_heads, head_dim, elem_bytes;
   int32_t fp8;
@@ -274,8 +296,10 @@ hipError_t launch_prefill_scores(const PrefillScoreArgs& a, int dtype, int head_
 hipError_t launch_append(const AppendArgs& a, const ScoreArgs* fold, int fold_tiles, hipStream_t s);
 // step: the fused append and Eq. 1 update of a whole-step launch, or k == nullptr.
 // e0, e1 (may be null): events that take the kernel's own start and end times.
+// vector_pass: bf16 grouped-query heads on the vector units instead of the matrix cores.
 hipError_t launch_attn(const AttnArgs& a, const StepArgs& step, int dtype, int head_dim, int group, int chunk,
-                       int layer_count, int chunks_now, hipEvent_t e0, hipEvent_t e1, hipStream_t s);
+                       bool vector_pass, int layer_count, int chunks_now, hipEvent_t e0, hipEvent_t e1,
+                       hipStream_t s);
 // max_live: live rows of the longest sequence; the launcher sets tiles_grid.
 // fold (or null): the deferred Eq. 1 sums to add to the scores, fold_tiles tiles of 64 rows per sequence
 hipError_t launch_finalize(const FinalizeArgs& a, const ScoreArgs* fold, int fold_tiles, int head_dim,
@@ -286,16 +310,29 @@ hipError_t launch_fold64(const ScoreArgs& a, int tiles64, hipStream_t s);
 
 // ---- launchers (move.hip) -------------------------------------------------
 hipError_t launch_place_rows(const PlaceArgs& a, int layers, hipStream_t s);
+// A bounded delay on a stream (test hook): one wave sleeps `iters` times, then exits.
+constexpr int kTestDelayIters = 200;  // about half a millisecond
+hipError_t launch_delay(int iters, hipStream_t s);
 
 // ---- launchers (reassign.hip) -----------------------------------------------
 hipError_t launch_rank_label(const RankArgs& a, int batch, hipStream_t s);
+hipError_t launch_joint_select(const JointArgs& a, hipStream_t s);
 hipError_t launch_deltas(const DeltaArgs& a, int batch, hipStream_t s);
 hipError_t launch_set_loc(const LocUpdate* u, int n, uint32_t* loc, int nmax, hipStream_t s);
 hipError_t launch_build_live(const LiveArgs& a, int batch, hipStream_t s);
-hipError_t launch_copy_rows(const CopyArgs& a, const RowOp* ops, int n_ops, int layers, hipStream_t s);
+// max_blocks: at most this many work-groups, each looping over (op, layer, K|V)
+// items (0: one per item).  Copies over PCIe into the pinned arenas use a few:
+// their rate is PCIe's, and the fewer work-groups they hold, the more the
+// attention running beside them keeps.
+constexpr int kArenaBlocks = 32;
+hipError_t launch_copy_rows(const CopyArgs& a, const RowOp* ops, int n_ops, int layers, int max_blocks,
+                            hipStream_t s);
 
 // ---- launchers (codec.hip) --------------------------------------------------
 hipError_t launch_quant_rows(const QuantArgs& a, const QuantOp* ops, int n_ops, int layers, hipStream_t s);
 hipError_t launch_dequant_rows(const DequantArgs& a, const DequantOp* ops, int n_ops, int layers, hipStream_t s);
+// T2 arena rows moved within the arena (codes and scales; ops' src/dst are arena indices)
+hipError_t launch_arena2_moves(const ArenaSpace& a, const RowOp* ops, int n_ops, int layers, int head_dim,
+                               int max_blocks, hipStream_t s);
 
 }  // namespace tkvd

@@ -84,6 +84,10 @@ typedef struct {
   int32_t chunk;          /* split-K rows per work-group: 128, 256 or 512; 0 = 512 when
                              q_heads >= 4 * kv_heads, else 256 */
   uint64_t flags;         /* TKV_FLAG_* */
+  int64_t mem_cap_bytes;  /* most device + pinned host bytes the handle may hold (pools,
+                             arenas, scratch, the buffers a reassignment grows); an
+                             allocation past it fails with TKV_ENOMEM as a failed hipMalloc
+                             would.  0 = no cap. */
 } tkv_options;
 
 /* Record HIP events around the attention kernels; tkv_stats reports their time. */
@@ -120,6 +124,22 @@ typedef struct {
  * next to heads of large ones.  Combines with TKV_FLAG_T2_FP8.  tkv_read_t2
  * then returns kv_heads scales for K followed by kv_heads for V. */
 #define TKV_FLAG_T2_HEAD_SCALES 16ull
+/* bf16 caches with 4 or more query heads per kv head: run the split-K pass on
+ * the vector units (as for fewer heads per kv head) instead of the matrix
+ * cores; the logits are then stored and Eq. 1 is never deferred.  Outputs
+ * agree with the matrix-core pass to rounding.  Not with an 8-bit tier in
+ * stream staging (TKV_EINVAL).  No effect on other shapes. */
+#define TKV_FLAG_VECTOR_PASS 32ull
+/* Test hooks, off in normal use.  TKV_FLAG_TEST_DELAY_COPIES: stream staging
+ * enqueues a bounded delay kernel (a fixed number of sleep iterations, then
+ * it exits) on each copy stream before every layer's staging copy, so the
+ * copies land late against the attention that waits for them; results must
+ * not change.  TKV_FLAG_TEST_SHUFFLE_SLOTS: free T0 pool slots (stream
+ * staging, and the batch-shared budget) are handed out in a seeded
+ * pseudo-random order instead of lowest first, so rows sit in scattered
+ * slots; results must not change (Method §3, Proposition 1). */
+#define TKV_FLAG_TEST_DELAY_COPIES 256ull
+#define TKV_FLAG_TEST_SHUFFLE_SLOTS 512ull
 
 /* One changed row of a reassignment (Method §4). */
 typedef struct {
@@ -143,6 +163,8 @@ typedef struct {
   int64_t attn_kv_bytes;     /* with TKV_FLAG_TIME_KERNELS: K/V bytes of the live rows those
                                 launches had to read (the algorithmic traffic) */
   double reassign_ms;        /* host wall time inside tkv_reassign */
+  int64_t mem_bytes;         /* device + pinned host bytes the handle holds now (what
+                                tkv_options.mem_cap_bytes caps) */
 } tkv_stats_t;
 
 /* Create a handle and allocate every pool.  delta: reassignment period

@@ -1,0 +1,45 @@
+"""bf16 runs past the score horizon, against the oracle.
+
+Eq. 1 ("Not All Thoughts Need HBM", gist.science summary, Method §2) adds
+every step's weights to the cumulative scores, so rounding builds up with
+the step count.  These runs go 320 decode steps (five reassignments at
+Delta = 64, Method §4) and compare the GPU's fp32 scores with the oracle's
+fp64 scores (relative 1e-4) after 256 steps and at the end, with outputs
+within 5e-3 on the way and every reassignment's labels and changed-row
+lists bit-exact.
+
+  * 7B heads (32 query / 32 kv heads, head_dim 128): the vector pass, which
+    stores the logits and sums each layer's weights in its merge pass.
+  * 14B heads (40 query / 8 kv heads): the matrix-core pass with Eq. 1
+    deferred to the next step's launch (the previous step's queries ride in
+    the padded rows of the logits tile).
+  * The same grouped-query heads with stream staging (stored logits).
+"""
+import pytest
+
+import tkvsynth
+from harness import Inputs
+from test_gpu_reassign import run_parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.timeout(600)
+def test_7b_heads_320_steps():
+    w = tkvsynth.CONFIGS["7b"].replace(layers=4, prefill=2200, steps=320)
+    out = run_parity(w, Inputs(w), w.steps, check_every=8, score_at=(256,))
+    assert out[5] == 5
+
+
+@pytest.mark.timeout(600)
+def test_14b_heads_deferred_eq1_320_steps():
+    w = tkvsynth.CONFIGS["14b"].replace(layers=4, batch=2, prefill=1800, steps=320)
+    out = run_parity(w, Inputs(w), w.steps, check_every=8, score_at=(256,))
+    assert out[5] == 5
+
+
+@pytest.mark.timeout(600)
+def test_14b_heads_stream_320_steps():
+    w = tkvsynth.CONFIGS["14b"].replace(layers=4, batch=2, prefill=1800, steps=320)
+    out = run_parity(w, Inputs(w), w.steps, check_every=8, score_at=(256,), staging_layers=2)
+    assert out[5] == 5 and out[3]["h2d_bytes"] > 0

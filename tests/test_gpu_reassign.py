@@ -42,9 +42,11 @@ def _check_deltas(c, o_deltas, n):
         assert gd == od, "demote list differs (seq %d)" % b
 
 
-def run_parity(w, inp, steps, check_every=1, **kw):
+def run_parity(w, inp, steps, check_every=1, score_at=(), **kw):
     """Drive GPU and oracle together; at every reassignment the oracle ranks by
-    the GPU's fp32 scores, its labels must equal the GPU's, then both go on."""
+    the GPU's fp32 scores, its labels must equal the GPU's, then both go on.
+    score_at: step counts after which the scores are also compared
+    (relative 1e-4), besides the end of the run."""
     c = _new(w, **kw)
     if w.prefill:  # a workload with no prefill starts from an empty cache
         c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
@@ -63,6 +65,9 @@ def run_parity(w, inp, steps, check_every=1, **kw):
         outs.append(got.copy())
         if t % check_every == 0 or t == steps - 1:
             worst = max(worst, float(np.max(np.abs(got - ref))))
+        if t + 1 in score_at:
+            rel = max_rel(c.read_scores()[:, : o.n], o.s[:, : o.n])
+            assert rel <= 1e-4, "scores max-rel %.3g after %d steps" % (rel, t + 1)
         if (t + 1) % w.delta == 0:
             g_s = c.read_scores()[:, : o.n]
             c.reassign()
@@ -145,9 +150,23 @@ def test_prop1_hbm_grid_bitwise(evict):
     # the splits really differ
     t0 = [int((runs[h][2][:, : ref[4].n] == 0).sum()) for h in (0.3, 0.5, 0.7)]
     assert t0[0] < t0[1] <= t0[2]
-    # stream staging gives the same bits
-    s = run_parity(base.replace(hbm_ratio=0.5), inp, base.steps, check_every=7, staging_layers=2)
-    assert all(np.array_equal(x, y) for x, y in zip(ref[0], s[0]))
+    # Stream staging, where a row's HBM place does follow its tier (T0 pool
+    # slot or the layer's staging slot, refilled from pinned memory each
+    # step): outputs, scores and evicted sets bit for bit the same at every
+    # ratio, and outputs and evicted sets the same as resident staging's (its
+    # scores add Eq. 1's terms in another order, so agree to rounding only),
+    # with the splits again different.
+    t0s, sref = [], None
+    for h in (0.3, 0.5, 0.7):
+        s = run_parity(base.replace(hbm_ratio=h), inp, base.steps, check_every=7, staging_layers=2)
+        assert all(np.array_equal(x, y) for x, y in zip(ref[0], s[0])), "stream outputs differ at hbm %s" % h
+        assert np.array_equal(ref[2] == 3, s[2] == 3)
+        if sref is None:
+            sref = s
+        assert np.array_equal(sref[1], s[1]) and np.array_equal(sref[2] == 3, s[2] == 3)
+        assert s[3]["h2d_bytes"] > 0
+        t0s.append(int((s[2][:, : ref[4].n] == 0).sum()))
+    assert t0s[0] < t0s[1] <= t0s[2]
 
 
 def test_labels_from_written_scores_with_ties():
