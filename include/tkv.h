@@ -50,8 +50,9 @@ typedef enum {
   TKV_EINVAL = -1,    /* bad argument: shape, ratio outside [0,1], delta <= 0, NULL pointer,
                          a device buffer (k, v, q, out) not 16-byte aligned */
   TKV_ECAPACITY = -2, /* more positions than max_tokens, or the T0 pool is full */
-  TKV_ENOMEM = -3,    /* device or pinned-host allocation failed */
-  TKV_ESTATE = -4,    /* call out of order (e.g. reassign between layer groups of a step) */
+  TKV_ENOMEM = -3,    /* device or pinned-host allocation failed, or past mem_cap_bytes */
+  TKV_ESTATE = -4,    /* call out of order (e.g. reassign between layer groups of a step), or the
+                         handle is marked failed after a reassignment failed part way */
   TKV_EHIP = -5       /* a HIP runtime call failed; see tkv_last_error */
 } tkv_status;
 
@@ -167,10 +168,12 @@ typedef struct {
                                 tkv_options.mem_cap_bytes caps) */
 } tkv_stats_t;
 
-/* Create a handle and allocate every pool.  delta: reassignment period
- * (Method §4); hbm_ratio / evict_ratio in [0,1] give the T0 and T3 shares
- * floor(ratio * N) of the N positions appended so far.  opts may be NULL.
- * On failure *out is NULL and tkv_last_error(NULL) explains. */
+/* Create a handle and allocate every pool (on the current device, with
+ * synchronous allocations: no stream is involved, and the handle's own
+ * streams are created here).  delta: reassignment period (Method §4);
+ * hbm_ratio / evict_ratio in [0,1] give the T0 and T3 shares floor(ratio * N)
+ * of the N positions appended so far (Method §1).  opts may be NULL.  On
+ * failure *out is NULL and tkv_last_error(NULL) explains. */
 int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_ratio, double evict_ratio,
                tkv_protect protect, const tkv_options* opts, tkv_t** out);
 
@@ -180,11 +183,15 @@ int tkv_destroy(tkv_t* t);
 /* Message of the last failure on t (NULL: of the last failed tkv_create). */
 const char* tkv_last_error(const tkv_t* t);
 
-/* Fill an empty cache with n_tokens positions.  k, v: device
- * [layers][batch][n_tokens][kv_heads][head_dim].  Scores start at 0; the
- * first placement (before any score exists) is the protected set plus the
- * lowest positions in T0 up to floor(hbm_ratio * n_tokens), the rest in T1;
- * nothing is evicted and nothing goes to T2.  Synchronises `stream`. */
+/* Fill an empty cache with n_tokens positions (the prompt and the reasoning
+ * chain so far: every token adds a K/V row, problem statement of the
+ * summary).  k, v: device [layers][batch][n_tokens][kv_heads][head_dim].
+ * Scores start at 0.  The pages place rows by score and have none yet
+ * (Method §1, §4); the reading taken: the protected set plus the lowest
+ * positions in T0 up to floor(hbm_ratio * n_tokens), the rest in T1, nothing
+ * evicted and nothing in T2.  T1 rows are copied to their pinned home.
+ * Allocates temporaries from the stream's allocator.  Synchronises
+ * `stream`. */
 int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tokens, tkv_stream_t stream);
 
 /* Scored prefill (the step before the decode path): fill an empty cache as
@@ -201,8 +208,10 @@ int tkv_prefill(tkv_t* t, const void* k, const void* v, int32_t n_tokens, tkv_st
 int tkv_prefill_scored(tkv_t* t, const void* k, const void* v, const void* q, int32_t n_tokens,
                        tkv_stream_t stream);
 
-/* Start a decode step: append one position to every sequence.  k, v: device
- * [layers][batch][kv_heads][head_dim].  The new row enters T0 with score 0.
+/* Start a decode step: append one position to every sequence (each decoded
+ * token adds a K/V row, problem statement of the summary; the recent window
+ * is always in T0, Method §1).  k, v: device [layers][batch][kv_heads]
+ * [head_dim].  The new row enters T0 with score 0.
  * The copy out of k, v is enqueued on `stream` by this call, so the caller may
  * reuse them in stream order right after it returns.
  * TKV_ECAPACITY at max_tokens, or (stream staging, or a batch-shared budget)
@@ -241,12 +250,19 @@ int tkv_decode_step(tkv_t* t, const void* k, const void* v, const void* q, float
  * T0; of the other live rows, ranked by score descending then position
  * ascending, the lowest go to T3 (up to floor(evict_ratio*N) evicted in
  * total), the highest fill T0 up to floor(hbm_ratio*N), the next lowest
- * floor(t2_ratio*N) go to T2 and the rest to T1.  Only changed rows move.
- * Call between steps, normally when the step count is a multiple of delta.
- * Synchronises `stream` once (to read the change counts). */
+ * floor(t2_ratio*N) go to T2 and the rest to T1.  Only changed rows move:
+ * the kernels read rows leaving the pinned arenas and write rows entering
+ * them over PCIe.  Call between steps, normally when the step count is a
+ * multiple of delta.  Synchronises `stream` once (to read the change
+ * counts); may grow its scratch with hipMalloc / hipHostMalloc.  Errors
+ * before the new labels take effect (TKV_ENOMEM, TKV_ECAPACITY) leave the
+ * handle as it was; a failure after that marks it failed: every later call
+ * but tkv_destroy, tkv_last_error and tkv_stats returns TKV_ESTATE. */
 int tkv_reassign(tkv_t* t, tkv_stream_t stream);
 
-/* Counters and sizes; synchronises the library's streams. */
+/* Counters and sizes (the HBM the tiers save and the traffic they cost: the
+ * summary's Results, system overhead and HBM savings); synchronises the
+ * library's streams.  Never fails on a handle marked failed. */
 int tkv_stats(tkv_t* t, tkv_stats_t* out);
 
 /* Test and inspection hooks (synchronise `stream`).  Arrays are host
