@@ -89,6 +89,7 @@ _SIGS = {
     "tkv_decode_attn": [_vp, _i32, _i32, _vp, _vp, _vp],
     "tkv_decode_step": [_vp, _vp, _vp, _vp, _vp, _vp],
     "tkv_reassign": [_vp, _vp],
+    "tkv_reassign_static": [_vp, _vp],
     "tkv_stats": [_vp, ctypes.POINTER(tkv_stats_t)],
     "tkv_read_scores": [_vp, _vp, _vp],
     "tkv_write_scores": [_vp, _vp, _vp],
@@ -181,6 +182,10 @@ def tkv_decode_step(h, k_ptr, v_ptr, q_ptr, out_ptr, stream=None):
 
 def tkv_reassign(h, stream=None):
     _check(lib().tkv_reassign(h, _stream(stream)), h)
+
+
+def tkv_reassign_static(h, stream=None):
+    _check(lib().tkv_reassign_static(h, _stream(stream)), h)
 
 
 def tkv_stats(h) -> dict:

@@ -189,6 +189,10 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   t->recent = protect.recent;
   t->flags = o.flags;
   t->mem_cap = o.mem_cap_bytes;
+  {
+    const hipError_t e = hipGetDevice(&t->device);
+    if (e != hipSuccess) return tkv_fail(nullptr, TKV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  }
   t->row_elems = (int64_t)s.kv_heads * s.head_dim;
   t->row_bytes = t->row_elems * t->esz;
 
@@ -304,6 +308,7 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   if (rc == TKV_OK) {
     hipError_t e = hipSuccess;
     if (e == hipSuccess) e = hipMemset(t->tier, kUnused, B * nmax);
+    if (e == hipSuccess) e = hipMemset(t->tier_alt, kUnused, B * nmax);  // the two swap at each reassignment
     if (e == hipSuccess) e = hipMemset(t->loc, 0xFF, B * nmax * 4);
     if (e == hipSuccess) e = hipMemset(t->s, 0, B * nmax * 4);
     if (e == hipSuccess) e = hipDeviceSynchronize();

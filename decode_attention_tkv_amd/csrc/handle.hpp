@@ -19,6 +19,7 @@ struct tkv {
   double hbm = 0, evict = 0, t2 = 0;
   int prompt = 0, sinks = 0, recent = 0;
   uint64_t flags = 0;
+  int device = 0;        // the GPU current when the handle was created
   int64_t mem_cap = 0;   // most device + pinned bytes the handle may hold (0: no cap)
   int64_t mem_held = 0;  // device + pinned bytes held now
   int cap0 = 0, cap1 = 0, cap2 = 0, capS = 0, max_chunks = 0;  // capS: staging rows per slot

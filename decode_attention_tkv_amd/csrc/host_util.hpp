@@ -47,6 +47,10 @@ inline bool within_cap(const tkv& t, size_t bytes) {
 // Device buffers handed over are read in 16-byte pieces.
 inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
+// The static device scratch of the handle's GPU (static_scratch.hip): its
+// address there and its size.
+int static_scratch(tkv* t, void** base, size_t* cap);
+
 // The tier rules of plan.hpp with a handle's policy.
 inline bool is_protected(const tkv& t, int64_t i, int64_t n) {
   return tkvd::protected_at(i, n, t.prompt, t.sinks, t.recent);

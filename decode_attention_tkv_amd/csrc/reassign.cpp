@@ -110,7 +110,11 @@ static DeltaTotals delta_totals(const tkv* t) {
   return d;
 }
 
-static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
+// use_static: the fetch pack F and the ops block live in the library's static
+// device scratch (no allocation); a reassignment that needs more returns
+// TKV_ECAPACITY before any state changes, and the call returns only once no
+// kernel reads the scratch any more.
+static int reassign_impl(tkv_t* t, tkv_stream_t stream, bool use_static) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
   if (t->failed) return tkv_fail(t, TKV_ESTATE, "handle unusable: an earlier reassignment failed part way");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "reassign between the layer groups of a step");
@@ -221,14 +225,40 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
   // F holds every moved row once; the ops block is bounded by a few ops per
   // changed row; the resident write-back packs hold the entrants.
   const DeltaTotals tot = delta_totals(t);
+  void* fbase = nullptr;    // F
+  char* d_opsbuf = nullptr;  // ops block, device
+  char* h_opsbuf = nullptr;  // its host staging
+  size_t ops_cap = 0;
+  std::vector<char> h_pageable;  // host staging of the static variant (no pinned allocation)
   {
     const int64_t Fmax = tot.e1 + tot.e2 + (t->positional ? 0 : tot.p);
-    int rc = grow_device(t, &t->fpack, &t->fpack_bytes, 2 * (size_t)L * H * Fmax * hb);
+    const size_t f_need = 2 * (size_t)L * H * Fmax * hb;
     const size_t ops_max = (size_t)tot.all * (4 * sizeof(RowOp) + sizeof(DequantOp) + sizeof(QuantOp) +
                                               3 * sizeof(LocUpdate) + sizeof(RowOp));
-    if (!rc && ops_max) rc = grow_pinned(t, &t->h_ops, &t->h_ops_bytes, ops_max);
-    if (!rc && ops_max) rc = grow_device(t, &t->d_ops, &t->d_ops_bytes, ops_max);
-    if (rc) return rc;  // nothing has changed: the handle stays as it was
+    if (use_static) {
+      void* base = nullptr;
+      size_t cap = 0;
+      if (int rc = static_scratch(t, &base, &cap)) return rc;
+      const size_t f_al = (f_need + 255) / 256 * 256;
+      if (f_al + ops_max > cap)
+        return tkv_fail(t, TKV_ECAPACITY,
+                        "reassignment needs %zu bytes of scratch; the static scratch holds %zu (use tkv_reassign)",
+                        f_al + ops_max, cap);
+      fbase = base;
+      d_opsbuf = (char*)base + f_al;
+      ops_cap = ops_max;
+      h_pageable.resize(ops_max);
+      h_opsbuf = h_pageable.data();
+    } else {
+      int rc = grow_device(t, &t->fpack, &t->fpack_bytes, f_need);
+      if (!rc && ops_max) rc = grow_pinned(t, &t->h_ops, &t->h_ops_bytes, ops_max);
+      if (!rc && ops_max) rc = grow_device(t, &t->d_ops, &t->d_ops_bytes, ops_max);
+      if (rc) return rc;  // nothing has changed: the handle stays as it was
+      fbase = t->fpack;
+      d_opsbuf = (char*)t->d_ops;
+      h_opsbuf = (char*)t->h_ops;
+      ops_cap = std::min(t->h_ops_bytes, t->d_ops_bytes);
+    }
   }
   std::swap(t->tier, t->tier_alt);  // device labels are now the new ones
   // from here on a failure leaves device and host state apart
@@ -257,7 +287,7 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
   // ---- F layout: [rows entering T1 | rows entering T2 | promotions]
   const int64_t F = E1 + E2 + P;
   const size_t f_bytes = (size_t)L * H * F * hb;  // per K|V
-  FPack fp{t->fpack, (char*)t->fpack + f_bytes, F};
+  FPack fp{fbase, (char*)fbase + f_bytes, F};
 
   // ---- ops
   // ops1: phase 1 fetch into F; ops2a: promotions (+ resident staging
@@ -314,7 +344,7 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
   const size_t bytes = (ops1.size() + ops2a.size() + ops2b.size() + am1.size() + am2.size() + ae1.size()) *
                            sizeof(RowOp) +
                        dq1.size() * sizeof(DequantOp) + q2.size() * sizeof(QuantOp) + upd.size() * sizeof(LocUpdate);
-  if (bytes > t->h_ops_bytes || bytes > t->d_ops_bytes)
+  if (bytes > ops_cap)
     return tkv_fail(t, TKV_EHIP, "internal error: reassignment ops (%zu bytes) exceed their buffer", bytes);
   const RowOp *d_ops1 = nullptr, *d_ops2a = nullptr, *d_ops2b = nullptr, *d_am1 = nullptr, *d_am2 = nullptr,
               *d_ae1 = nullptr;
@@ -322,8 +352,8 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
   const QuantOp* d_q2 = nullptr;
   const LocUpdate* d_upd = nullptr;
   if (bytes > 0) {
-    char* h = (char*)t->h_ops;
-    char* d = (char*)t->d_ops;
+    char* h = h_opsbuf;
+    char* d = d_opsbuf;
     size_t off = 0;
     auto put = [&](const void* src, size_t sz) -> const void* {
       if (sz) std::memcpy(h + off, src, sz);
@@ -340,7 +370,7 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
     d_dq1 = (const DequantOp*)put(dq1.data(), dq1.size() * sizeof(DequantOp));
     d_q2 = (const QuantOp*)put(q2.data(), q2.size() * sizeof(QuantOp));
     d_upd = (const LocUpdate*)put(upd.data(), upd.size() * sizeof(LocUpdate));
-    HIP_TRY(t, hipMemcpyAsync(t->d_ops, t->h_ops, bytes, hipMemcpyHostToDevice, st));
+    HIP_TRY(t, hipMemcpyAsync(d_opsbuf, h_opsbuf, bytes, hipMemcpyHostToDevice, st));
   }
 
   // ---- device phases.  The caller's stream first waits for the last
@@ -403,6 +433,7 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
     t->st.d2h_bytes += 2 * (int64_t)L * H * (E1 * hb + E2 * qrow) + 2 * (int64_t)L * E2 * t->sh * 4;
   }
 
+  if (use_static) HIP_TRY(t, hipEventSynchronize(t->ev_arena));  // nothing reads the scratch after return
   poison.done = true;
   t->st.promotions += pr.promotions;
   t->st.demotions += pr.demotions;
@@ -413,5 +444,9 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream) {
   return TKV_OK;
 }
 extern "C" int tkv_reassign(tkv_t* t, tkv_stream_t stream) {
-  return guarded(t, [&] { return reassign_impl(t, stream); });
+  return guarded(t, [&] { return reassign_impl(t, stream, false); });
+}
+
+extern "C" int tkv_reassign_static(tkv_t* t, tkv_stream_t stream) {
+  return guarded(t, [&] { return reassign_impl(t, stream, true); });
 }

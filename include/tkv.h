@@ -49,7 +49,8 @@ typedef enum {
   TKV_OK = 0,
   TKV_EINVAL = -1,    /* bad argument: shape, ratio outside [0,1], delta <= 0, NULL pointer,
                          a device buffer (k, v, q, out) not 16-byte aligned */
-  TKV_ECAPACITY = -2, /* more positions than max_tokens, or the T0 pool is full */
+  TKV_ECAPACITY = -2, /* more positions than max_tokens, the T0 pool is full, or a reassignment
+                         needs more than the static scratch (tkv_reassign_static) */
   TKV_ENOMEM = -3,    /* device or pinned-host allocation failed, or past mem_cap_bytes */
   TKV_ESTATE = -4,    /* call out of order (e.g. reassign between layer groups of a step), or the
                          handle is marked failed after a reassignment failed part way */
@@ -259,6 +260,20 @@ int tkv_decode_step(tkv_t* t, const void* k, const void* v, const void* q, float
  * handle as it was; a failure after that marks it failed: every later call
  * but tkv_destroy, tkv_last_error and tkv_stats returns TKV_ESTATE. */
 int tkv_reassign(tkv_t* t, tkv_stream_t stream);
+
+/* For callers that cannot allocate memory -- code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc: tkv_reassign with the
+ * reassignment's scratch (the pack of moved rows and the row-copy plan) in
+ * the library's static device array, 64 MiB per GPU, instead of buffers that
+ * tkv_reassign grows with hipMalloc / hipHostMalloc.  Same results as
+ * tkv_reassign, bit for bit.  A reassignment needing more than the array
+ * holds -- 2 * layers * kv_heads * head_dim * element bytes per moved row
+ * (rows entering T1 or T2; promotions too outside positional staging) plus
+ * about 100 bytes per changed row -- returns TKV_ECAPACITY and changes
+ * nothing.  The array is shared by every handle on that GPU and keeps the
+ * last call's contents: calls that overlap on one GPU (other host threads)
+ * race.  The call returns only once no kernel reads the array any more. */
+int tkv_reassign_static(tkv_t* t, tkv_stream_t stream);
 
 /* Counters and sizes (the HBM the tiers save and the traffic they cost: the
  * summary's Results, system overhead and HBM savings); synchronises the
