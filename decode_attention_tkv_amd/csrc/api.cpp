@@ -343,6 +343,8 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   t->h_loc.assign(B * nmax, kNoLoc);
   t->t1_owner.resize(B);
   t->t2_owner.resize(B);
+  t->t1_free.resize(B);
+  t->t2_free.resize(B);
   std::memset(t->h_counts, 0, B * 2 * 4);
   t->st.hbm_bytes = (int64_t)(2 * (size_t)L * t->cap0 * (t->shared_hbm ? 1 : B) + 2 * (size_t)t->S * B * t->capS) *
                         t->row_bytes +

@@ -56,11 +56,18 @@ __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const Qua
   const QuantOp op = ops[blockIdx.x];
   const int l = blockIdx.y, which = blockIdx.z;
   const int d = a.head_dim, n = a.kv_heads * d;
-  const void* f = which ? a.f.v : a.f.k;
+  // the row's values: F row op.src, or (from_pool) pool slot op.src of sequence op.b
+  const void* f = a.from_pool ? (which ? a.rows.pool_v : a.rows.pool_k) : (which ? a.f.v : a.f.k);
+  auto at = [&](int h, int j) -> int64_t {
+    if (a.from_pool)
+      return (int64_t)l * a.rows.pool_lstride + (int64_t)op.b * a.rows.pool_bstride + (int64_t)h * a.rows.pool_hstride +
+             (int64_t)op.src * d + j;
+    return (((int64_t)l * a.kv_heads + h) * a.f.rows + op.src) * d + j;
+  };
   float amax = 0.f;
   for (int e = threadIdx.x; e < n; e += 256) {
     const int h = e / d, j = e % d;
-    amax = fmaxf(amax, fabsf(load_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.src) * d + j, a.elem_bytes)));
+    amax = fmaxf(amax, fabsf(load_val(f, at(h, j), a.elem_bytes)));
   }
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const Qua
     __syncthreads();
     for (int e = threadIdx.x; e < n; e += 256) {
       const int h = e / d, j = e % d;
-      const float x = load_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.src) * d + j, a.elem_bytes);
+      const float x = load_val(f, at(h, j), a.elem_bytes);
       atomicMax(&hmax[h], __float_as_uint(fabsf(x)));
     }
     __syncthreads();
@@ -89,7 +96,10 @@ __global__ __launch_bounds__(256) void k_quant_rows(const QuantArgs a, const Qua
   };
   for (int e = threadIdx.x; e < n; e += 256) {
     const int h = e / d, j = e % d;
-    const float x = load_val(f, (((int64_t)l * a.kv_heads + h) * a.f.rows + op.src) * d + j, a.elem_bytes);
+    // from_pool with op.stage == op.src rewrites this very element below:
+    // every thread reads its elements before it writes them, and the amax
+    // passes above finished at a barrier
+    const float x = load_val(f, at(h, j), a.elem_bytes);
     const float scale = head_scale(h);
     float c;
     int8_t code;

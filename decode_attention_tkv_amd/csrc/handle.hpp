@@ -122,8 +122,10 @@ struct tkv {
   std::vector<int32_t>& free_list(int b) { return free0[shared_hbm ? 0 : b]; }
   std::vector<uint8_t> h_tier;                // [B][nmax]
   std::vector<uint32_t> h_loc;                // [B][nmax]
-  std::vector<std::vector<int32_t>> t1_owner; // [B]: T1 arena index -> position
-  std::vector<std::vector<int32_t>> t2_owner; // [B]: T2 arena index -> position
+  std::vector<std::vector<int32_t>> t1_owner; // [B]: T1 arena index -> position (-1: free, positional only)
+  std::vector<std::vector<int32_t>> t2_owner; // [B]: T2 arena index -> position (-1: free, positional only)
+  std::vector<std::vector<int32_t>> t1_free;  // [B]: freed T1 arena indices (positional only)
+  std::vector<std::vector<int32_t>> t2_free;  // [B]: freed T2 arena indices (positional only)
 
   // ---- last reassignment's changed rows (pinned host copy of the device block)
   int32_t* h_counts = nullptr;     // [B][2]

@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <functional>
 
 namespace tkvd {
 
@@ -147,23 +148,60 @@ int make_plan(const PlanConfig& cfg, PlanState& st, const int32_t* counts, const
       lc[mv.pos] = slot;
       r.upd.push_back({b, mv.pos, slot});
     }
-    // arenas: compaction, then the entrants at the end
+    uint32_t* ai = cfg.positional ? &(*st.aidx)[b * nmax] : nullptr;
+    if (cfg.positional) {
+      // arenas nothing reads on the decode path: vacated indices are freed
+      // and the entrants take the lowest free ones, then new ones
+      auto place = [&](std::vector<int32_t>& own, std::vector<int32_t>& fr, const std::vector<char>& vac,
+                       const std::vector<Move>& ent, std::vector<uint32_t>& dst, int cap) -> bool {
+        for (size_t i = 0; i < vac.size(); ++i)
+          if (vac[i]) {
+            own[i] = -1;
+            fr.push_back((int32_t)i);
+          }
+        std::sort(fr.begin(), fr.end(), std::greater<int32_t>());
+        for (const Move& mv : ent) {
+          uint32_t idx;
+          if (!fr.empty()) {
+            idx = (uint32_t)fr.back();
+            fr.pop_back();
+            own[idx] = (int32_t)mv.pos;
+          } else {
+            if (own.size() >= (size_t)cap) return false;
+            idx = (uint32_t)own.size();
+            own.push_back((int32_t)mv.pos);
+          }
+          dst.push_back(idx);
+          ai[mv.pos] = idx;
+        }
+        return true;
+      };
+      if (!place(own1, (*st.free1)[b], vac1s[b], sp.ent1, sp.dst1, cfg.cap1)) {
+        *err = "T1 arena full";
+        return TKV_ECAPACITY;
+      }
+      if (!place(own2, (*st.free2)[b], vac2s[b], sp.ent2, sp.dst2, cfg.cap2)) {
+        *err = "T2 arena full";
+        return TKV_ECAPACITY;
+      }
+      sp.e1off = r.e1;
+      sp.e2off = r.e2;
+      sp.poff = r.p;
+      r.e1 += (int64_t)sp.ent1.size();
+      r.e2 += (int64_t)sp.ent2.size();
+      int32_t evicted_b = 0;
+      for (int p = 0; p < n; ++p) evicted_b += tr[p] == TKV_T3 ? 1 : 0;
+      (*st.nlive)[b] = n - evicted_b;
+      continue;
+    }
+    // dense arenas: compaction, then the entrants at the end
     compact(own1, vac1s[b], &sp.m1, &sp.mov1);
     compact(own2, vac2s[b], &sp.m2, &sp.mov2);
-    uint32_t* ai = cfg.positional ? &(*st.aidx)[b * nmax] : nullptr;
     for (auto& mv : sp.mov1) {
-      if (ai) {
-        ai[own1[mv.second]] = mv.second;
-        continue;
-      }
       lc[own1[mv.second]] = c1 + mv.second;
       r.upd.push_back({b, (uint32_t)own1[mv.second], c1 + mv.second});
     }
     for (auto& mv : sp.mov2) {
-      if (ai) {
-        ai[own2[mv.second]] = mv.second;
-        continue;
-      }
       lc[own2[mv.second]] = c2 + mv.second;
       r.upd.push_back({b, (uint32_t)own2[mv.second], c2 + mv.second});
     }
@@ -177,19 +215,13 @@ int make_plan(const PlanConfig& cfg, PlanState& st, const int32_t* counts, const
     }
     for (size_t e = 0; e < sp.ent1.size(); ++e) {
       own1.push_back((int32_t)sp.ent1[e].pos);
-      if (ai) {
-        ai[sp.ent1[e].pos] = sp.m1 + (uint32_t)e;
-        continue;
-      }
+      sp.dst1.push_back(sp.m1 + (uint32_t)e);
       lc[sp.ent1[e].pos] = c1 + sp.m1 + (uint32_t)e;
       r.upd.push_back({b, sp.ent1[e].pos, c1 + sp.m1 + (uint32_t)e});
     }
     for (size_t e = 0; e < sp.ent2.size(); ++e) {
       own2.push_back((int32_t)sp.ent2[e].pos);
-      if (ai) {
-        ai[sp.ent2[e].pos] = sp.m2 + (uint32_t)e;
-        continue;
-      }
+      sp.dst2.push_back(sp.m2 + (uint32_t)e);
       lc[sp.ent2[e].pos] = c2 + sp.m2 + (uint32_t)e;
       r.upd.push_back({b, sp.ent2[e].pos, c2 + sp.m2 + (uint32_t)e});
     }

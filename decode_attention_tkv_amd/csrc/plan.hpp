@@ -59,8 +59,9 @@ struct Move {
 struct SeqPlan {
   std::vector<Move> ent1, ent2, promo;  // rows entering T1, T2 and T0
   std::vector<uint32_t> promo_slot;
-  std::vector<std::pair<uint32_t, uint32_t>> mov1, mov2;  // arena (src, dst)
-  uint32_t m1 = 0, m2 = 0;              // arena rows kept before the entrants
+  std::vector<uint32_t> dst1, dst2;     // arena index of each entrant
+  std::vector<std::pair<uint32_t, uint32_t>> mov1, mov2;  // arena compaction (src, dst)
+  uint32_t m1 = 0, m2 = 0;              // dense arenas: rows kept before the entrants
   int64_t e1off = 0, e2off = 0, poff = 0;  // offsets within the F segments
 };
 
@@ -77,13 +78,19 @@ struct PlanConfig {
 };
 
 // The host mirror of the placement, updated in place by make_plan.
+// Arenas: dense (index < size holds a row) except under positional staging,
+// where nothing reads them on the decode path and rows entering take freed
+// indices (own = -1 there; free1/free2 list them, back() = lowest) instead
+// of the arena being compacted.
 struct PlanState {
   std::vector<uint8_t>* tier;                  // [batch][nmax]
   std::vector<uint32_t>* loc;                  // [batch][nmax] location codes
   std::vector<uint32_t>* aidx;                 // [batch][nmax] arena index (positional only)
   std::vector<std::vector<int32_t>>* free0;    // free T0 slots, back() next ([1] when shared)
-  std::vector<std::vector<int32_t>>* own1;     // [batch] T1 arena index -> position
-  std::vector<std::vector<int32_t>>* own2;     // [batch] T2 arena index -> position
+  std::vector<std::vector<int32_t>>* own1;     // [batch] T1 arena index -> position (-1: free)
+  std::vector<std::vector<int32_t>>* own2;     // [batch] T2 arena index -> position (-1: free)
+  std::vector<std::vector<int32_t>>* free1;    // [batch] freed T1 arena indices (positional only)
+  std::vector<std::vector<int32_t>>* free2;    // [batch] freed T2 arena indices (positional only)
   std::vector<int32_t>* nlive;                 // [batch] live rows
 };
 
@@ -97,8 +104,9 @@ struct PlanResult {
 // {promote, demote}; lists [batch][nmax], ascending by position): every
 // freed T0 slot returns to its free list before any promotion takes one;
 // promotions take T0 slots (none under positional staging, where rows stay
-// put); arenas compact and take their entrants at the end, in position
-// order; the location updates follow.  TKV_OK, or TKV_ECAPACITY (with *err)
+// put); dense arenas compact and take their entrants at the end, in
+// position order (positional staging: entrants take the lowest freed
+// indices, then new ones); the location updates follow.  TKV_OK, or TKV_ECAPACITY (with *err)
 // when the T0 pool or an arena overflows -- the state is then partly
 // updated.
 int make_plan(const PlanConfig& cfg, PlanState& st, const int32_t* counts, const tkv_delta* promote,

@@ -231,7 +231,8 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream, bool use_static) {
   size_t ops_cap = 0;
   std::vector<char> h_pageable;  // host staging of the static variant (no pinned allocation)
   {
-    const int64_t Fmax = tot.e1 + tot.e2 + (t->positional ? 0 : tot.p);
+    // positional staging: every moved row is read where it sits, F is not needed
+    const int64_t Fmax = t->positional ? 0 : tot.e1 + tot.e2 + tot.p;
     const size_t f_need = 2 * (size_t)L * H * Fmax * hb;
     const size_t ops_max = (size_t)tot.all * (4 * sizeof(RowOp) + sizeof(DequantOp) + sizeof(QuantOp) +
                                               3 * sizeof(LocUpdate) + sizeof(RowOp));
@@ -272,7 +273,8 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream, bool use_static) {
 
   // ---- placement plan (host mirror of tiers, locations, free slots, arenas)
   PlanConfig pc{B, t->nmax, n, t->cap0, t->cap1, t->cap2, t->positional, t->shared_hbm};
-  PlanState ps{&t->h_tier, &t->h_loc, &t->h_aidx, &t->free0, &t->t1_owner, &t->t2_owner, &t->nlive};
+  PlanState ps{&t->h_tier,  &t->h_loc,    &t->h_aidx,  &t->free0, &t->t1_owner,
+               &t->t2_owner, &t->t1_free, &t->t2_free, &t->nlive};
   PlanResult pr;
   {
     std::string why;
@@ -311,6 +313,14 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream, bool use_static) {
   };
   for (int b = 0; b < B; ++b) {
     const SeqPlan& sp = plan[b];
+    if (t->positional) {
+      // rows stay at their positions: entrants go to their arenas from there
+      for (size_t e = 0; e < sp.ent1.size(); ++e)
+        ae1.push_back({kAreaPool, kAreaArena1, (uint16_t)b, sp.ent1[e].pos, sp.dst1[e]});
+      for (size_t e = 0; e < sp.ent2.size(); ++e)
+        q2.push_back({(uint16_t)b, sp.ent2[e].pos, sp.dst2[e], sp.ent2[e].pos});
+      continue;
+    }
     for (size_t e = 0; e < sp.ent1.size(); ++e) fetch(b, sp.ent1[e], (uint32_t)(sp.e1off + e));
     for (size_t e = 0; e < sp.ent2.size(); ++e) fetch(b, sp.ent2[e], (uint32_t)(E1 + sp.e2off + e));
     for (size_t p = 0; p < sp.promo.size(); ++p) fetch(b, sp.promo[p], (uint32_t)(E1 + E2 + sp.poff + p));
@@ -330,14 +340,12 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream, bool use_static) {
     for (auto& mv : sp.mov1) am1.push_back({kAreaArena1, kAreaArena1, (uint16_t)b, mv.first, mv.second});
     for (auto& mv : sp.mov2) am2.push_back({0, 0, (uint16_t)b, mv.first, mv.second});
     for (size_t e = 0; e < sp.ent1.size(); ++e)
-      ae1.push_back({kAreaPackOut, kAreaArena1, (uint16_t)b, (uint32_t)(sp.e1off + e), sp.m1 + (uint32_t)e});
-    // T2 entrants: codes and scales into the arena (index m2 + e); the
-    // dequantised values go to the row's location: its own slot (positional),
-    // its new staging place (resident), or nowhere (stream)
+      ae1.push_back({kAreaPackOut, kAreaArena1, (uint16_t)b, (uint32_t)(sp.e1off + e), sp.dst1[e]});
+    // T2 entrants: codes and scales into the arena; the dequantised values go
+    // to the row's new staging place (resident) or nowhere (stream)
     for (size_t e = 0; e < sp.ent2.size(); ++e)
-      q2.push_back({(uint16_t)b, (uint32_t)(E1 + sp.e2off + e), sp.m2 + (uint32_t)e,
-                    t->positional ? sp.ent2[e].pos
-                    : t->resident ? c2 + sp.m2 + (uint32_t)e : kNoLoc});
+      q2.push_back({(uint16_t)b, (uint32_t)(E1 + sp.e2off + e), sp.dst2[e],
+                    t->resident ? c2 + sp.dst2[e] : kNoLoc});
   }
 
   // ---- ops and location updates to the device (buffers grown above)
@@ -398,7 +406,7 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream, bool use_static) {
   // step reads.
   HIP_TRY(t, launch_arena2_moves(arena, d_am2, (int)am2.size(), L, D, kArenaBlocks, st));
   if (E2 > 0) {
-    QuantArgs qa{t->rowspace(), fp, arena, H, D, t->esz, fp8, t->sh};
+    QuantArgs qa{t->rowspace(), fp, arena, H, D, t->esz, fp8, t->sh, t->positional ? 1 : 0};
     HIP_TRY(t, launch_quant_rows(qa, d_q2, (int)q2.size(), L, st));
   }
   HIP_TRY(t, launch_set_loc(d_upd, (int)upd.size(), t->loc, t->nmax, st));
@@ -420,8 +428,9 @@ static int reassign_impl(tkv_t* t, tkv_stream_t stream, bool use_static) {
     HIP_TRY(t, hipStreamWaitEvent(t->wb, t->ev_gathered, 0));
     as = t->wb;
   }
-  HIP_TRY(t, launch_copy_rows(ca, d_am1, (int)am1.size(), L, kArenaBlocks, as));
-  HIP_TRY(t, launch_copy_rows(ca, d_ae1, (int)ae1.size(), L, kArenaBlocks, as));
+  const int wblocks = stream_mode ? kArenaBlocks : kWritebackBlocks;
+  HIP_TRY(t, launch_copy_rows(ca, d_am1, (int)am1.size(), L, wblocks, as));
+  HIP_TRY(t, launch_copy_rows(ca, d_ae1, (int)ae1.size(), L, wblocks, as));
   HIP_TRY(t, hipEventRecord(t->ev_arena, as));
   t->arena_pending = true;
   {

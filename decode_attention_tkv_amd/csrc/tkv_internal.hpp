@@ -246,8 +246,9 @@ struct QuantOp {
                    // staging index), or kNoLoc
 };
 
-// Rows entering T2: F row src quantised into T2 arena index dst of sequence b
-// (codes [layers][batch][kv_heads][cap2][head_dim], scales [layers][batch][cap2][sh]).
+// Rows entering T2: F row src (from_pool: pool slot src of sequence b)
+// quantised into T2 arena index dst of sequence b (codes [layers][batch]
+// [kv_heads][cap2][head_dim], scales [layers][batch][cap2][sh]).
 struct QuantArgs {
   RowSpace rows;
   FPack f;
@@ -255,6 +256,7 @@ struct QuantArgs {
   int32_t kv_heads, head_dim, elem_bytes;
   int32_t fp8;  // FP8 E4M3 codes (else int8)
   int32_t sh;   // scales per row: kv_heads or 1
+  int32_t from_pool;
 };
 
 // T2 arena row src of sequence b -> cache-type values in F row dst.
@@ -324,7 +326,8 @@ hipError_t launch_build_live(const LiveArgs& a, int batch, hipStream_t s);
 // items (0: one per item).  Copies over PCIe into the pinned arenas use a few:
 // their rate is PCIe's, and the fewer work-groups they hold, the more the
 // attention running beside them keeps.
-constexpr int kArenaBlocks = 32;
+constexpr int kArenaBlocks = 32;     // on the caller's stream (stream staging)
+constexpr int kWritebackBlocks = 8;  // beside the decode steps (resident staging)
 hipError_t launch_copy_rows(const CopyArgs& a, const RowOp* ops, int n_ops, int layers, int max_blocks,
                             hipStream_t s);
 

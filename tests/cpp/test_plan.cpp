@@ -93,7 +93,7 @@ static void check_plan(std::mt19937& rng, bool positional, bool shared) {
   const int cap0 = positional ? nmax : (shared ? B * nmax : nmax);
   std::vector<uint8_t> tier((size_t)B * nmax, kUnused);
   std::vector<uint32_t> loc((size_t)B * nmax, kNoLoc), aidx((size_t)B * nmax, kNoLoc);
-  std::vector<std::vector<int32_t>> free0(shared ? 1 : B), own1(B), own2(B);
+  std::vector<std::vector<int32_t>> free0(shared ? 1 : B), own1(B), own2(B), free1(B), free2(B);
   std::vector<int32_t> nlive(B);
   // a consistent starting placement with random tiers
   std::vector<std::vector<int32_t>> used(shared ? 1 : B);
@@ -151,9 +151,10 @@ static void check_plan(std::mt19937& rng, bool positional, bool shared) {
     counts[2 * b] = np;
     counts[2 * b + 1] = nd;
   }
-  const std::vector<uint32_t> loc_before = loc;
+  const std::vector<uint32_t> loc_before = loc, aidx_before = aidx;
+  const std::vector<uint8_t> tier_before = tier;
   PlanConfig cfg{B, nmax, n, cap0, cap1, cap2, positional, shared};
-  PlanState st{&tier, &loc, &aidx, &free0, &own1, &own2, &nlive};
+  PlanState st{&tier, &loc, &aidx, &free0, &own1, &own2, &free1, &free2, &nlive};
   PlanResult r;
   std::string err;
   const int rc = make_plan(cfg, st, counts.data(), pro.data(), dem.data(), &r, &err);
@@ -164,12 +165,35 @@ static void check_plan(std::mt19937& rng, bool positional, bool shared) {
   for (int b = 0; b < B; ++b) {
     const SeqPlan& sp = r.seq[b];
     for (size_t k = 0; k < sp.promo.size(); ++k) pool[{shared ? 0 : b, sp.promo_slot[k]}] = (int32_t)sp.promo[k].pos;
-    for (auto& mv : sp.mov1) ar1[b][mv.second] = ar1[b][mv.first];
-    for (auto& mv : sp.mov2) ar2[b][mv.second] = ar2[b][mv.first];
-    ar1[b].resize(sp.m1);
-    ar2[b].resize(sp.m2);
-    for (auto& mv : sp.ent1) ar1[b].push_back((int32_t)mv.pos);
-    for (auto& mv : sp.ent2) ar2[b].push_back((int32_t)mv.pos);
+    CHECK(sp.dst1.size() == sp.ent1.size() && sp.dst2.size() == sp.ent2.size(), "entrant destinations");
+    if (positional) {
+      // rows leaving an arena free their index; entrants land at their destinations
+      for (int p = 0; p < n; ++p) {
+        const size_t at = (size_t)b * nmax + p;
+        if (tier_before[at] == TKV_T1 && neu[at] != TKV_T1) ar1[b][aidx_before[at]] = -1;
+        if (tier_before[at] == TKV_T2 && neu[at] != TKV_T2) ar2[b][aidx_before[at]] = -1;
+      }
+      CHECK(sp.mov1.empty() && sp.mov2.empty(), "positional arenas are not compacted");
+    } else {
+      for (auto& mv : sp.mov1) ar1[b][mv.second] = ar1[b][mv.first];
+      for (auto& mv : sp.mov2) ar2[b][mv.second] = ar2[b][mv.first];
+      ar1[b].resize(sp.m1);
+      ar2[b].resize(sp.m2);
+    }
+    for (size_t e = 0; e < sp.ent1.size(); ++e) {
+      const uint32_t d = sp.dst1[e];
+      CHECK(d < (uint32_t)cap1, "T1 destination past the arena");
+      if (d >= ar1[b].size()) ar1[b].resize(d + 1, -1);
+      CHECK(ar1[b][d] == -1, "T1 entrant onto a live row (seq %d index %u)", b, d);
+      ar1[b][d] = (int32_t)sp.ent1[e].pos;
+    }
+    for (size_t e = 0; e < sp.ent2.size(); ++e) {
+      const uint32_t d = sp.dst2[e];
+      CHECK(d < (uint32_t)cap2, "T2 destination past the arena");
+      if (d >= ar2[b].size()) ar2[b].resize(d + 1, -1);
+      CHECK(ar2[b][d] == -1, "T2 entrant onto a live row (seq %d index %u)", b, d);
+      ar2[b][d] = (int32_t)sp.ent2[e].pos;
+    }
     CHECK(sp.e1off == e1 && sp.e2off == e2 && sp.poff == p0, "F offsets");
     e1 += sp.ent1.size();
     e2 += sp.ent2.size();
@@ -183,6 +207,27 @@ static void check_plan(std::mt19937& rng, bool positional, bool shared) {
   for (int b = 0; b < B; ++b) {
     int live = 0;
     CHECK(ar1[b] == own1[b] && ar2[b] == own2[b], "simulated arenas equal the owners (seq %d)", b);
+    if (positional) {  // every live T1/T2 row owns exactly one index; the rest are free, each listed once
+      for (int w = 0; w < 2; ++w) {
+        const auto& own = w ? own2[b] : own1[b];
+        const auto& fr = w ? free2[b] : free1[b];
+        std::set<int32_t> fs(fr.begin(), fr.end());
+        CHECK(fs.size() == fr.size(), "free index twice");
+        int holes = 0, rows = 0;
+        for (size_t i = 0; i < own.size(); ++i) {
+          if (own[i] < 0) {
+            ++holes;
+            CHECK(fs.count((int32_t)i) == 1, "free index not listed");
+          } else {
+            ++rows;
+            CHECK(neu[(size_t)b * nmax + own[i]] == (w ? TKV_T2 : TKV_T1), "arena row of another tier");
+          }
+        }
+        int in_tier = 0;
+        for (int p = 0; p < n; ++p) in_tier += neu[(size_t)b * nmax + p] == (w ? TKV_T2 : TKV_T1);
+        CHECK(holes == (int)fr.size() && rows == in_tier, "arena rows %d vs tier %d", rows, in_tier);
+      }
+    }
     for (int p = 0; p < n; ++p) {
       const size_t at = (size_t)b * nmax + p;
       CHECK(tier[at] == neu[at], "tier mirror");
