@@ -35,6 +35,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_tkv_amd", "csrc", "attn.hip")
+def attention_kernel(w, args):
+    """Which pass of the split-K kernel a workload's decode steps take: bf16
+    caches with four or more query heads per kv head use the matrix cores
+    unless the vector pass is asked for; every other shape the vector units."""
+    if w.dtype == "bf16" and w.q_heads >= 4 * w.kv_heads and not args.vector_pass:
+        return "k_attn_chunk (split-K attention, matrix-core pass)"
+    return "k_attn_chunk (split-K attention, vector pass)"
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_chunk_7b_traffic.txt")
 COPY_BYTES = 1 << 30  # plain device copy used to scale the HBM byte counters
 METRIC = "decode steps/sec (attn+scoring, all layers) at 7B shape; achieved HBM GB/s %peak"
@@ -433,7 +442,7 @@ def main():
                    "reassignments_timed": int(after["reassigns"] - before["reassigns"])},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(kv_bytes / launches),
-                     "kernel": "k_attn_chunk (split-K attention pass)",
+                     "kernel": attention_kernel(w, args),
                      "avg_launch_us": kern_ms / launches * 1e3, "launches": launches,
                      "kv_bytes_per_launch": kv_bytes / launches},
         "step_hbm_gbs": step_gbs,

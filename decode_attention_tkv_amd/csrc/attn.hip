@@ -79,6 +79,15 @@ __device__ __forceinline__ float group_max(float x) {
 }
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// A result the merge pass or Eq. 1 reads later, written through to memory
+// (a relaxed store at system scope: global_store sc0 sc1) rather than held
+// dirty in L2.  Measured on MI355X against non-temporal stores over the same
+// steps: split-K launch 201.1 vs 206.1 us at 7B (-2.4%), 7177 vs 7258 us at
+// 70B, 572 vs 575 us at 14B.
+__device__ __forceinline__ void store_through(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
             if (vp[i]) e += exp2f(acc[i] * a.qscale - pM[i]) * piL[i];
           e += __shfl_xor(e, 16);
           e += __shfl_xor(e, 32);
-          if (kq == 0 && j0 + r < nprev) __builtin_nontemporal_store(e, sp + r);
+          if (kq == 0 && j0 + r < nprev) store_through(sp + r, e);
         }
       }
     }
@@ -662,12 +671,12 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
   for (int t = tid; t < G * D; t += 256) {
     const int g = t / D, e = t % D;
     const float x = ((osum[0][g][e] + osum[1][g][e]) + osum[2][g][e]) + osum[3][g][e];
-    __builtin_nontemporal_store(x, a.part_o + ((hbase + g) * a.max_chunks + c) * D + e);
+    store_through(a.part_o + ((hbase + g) * a.max_chunks + c) * D + e, x);
   }
   if (tid < 2 * G) {
     const int g = tid >> 1;
     const float v = (tid & 1) ? ((red[0][g] + red[1][g]) + red[2][g]) + red[3][g] : mc[g];
-    __builtin_nontemporal_store(v, a.part_ml + ((hbase + g) * a.max_chunks + c) * 2 + (tid & 1));
+    store_through(a.part_ml + ((hbase + g) * a.max_chunks + c) * 2 + (tid & 1), v);
   }
   // logits, padded with zeros to the line that holds the chunk's last row
   // (none when Eq. 1 is deferred)
@@ -675,7 +684,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float* lg = a.logits + (hbase + g) * a.lstride + j0;
-    for (int r = tid; r < nw; r += 256) __builtin_nontemporal_store(r < nrows ? zs[g][r] : 0.f, lg + r);
+    for (int r = tid; r < nw; r += 256) store_through(lg + r, r < nrows ? zs[g][r] : 0.f);
   }
   if (jn >= j0 && jn < j0 + nrows) {
     // the appended row's K and V of this kv head into T0 slot n.slot[b]
