@@ -20,7 +20,7 @@
 //                 once per (head, row) and accumulates p * V.  Grouped-query
 //                 heads (G >= 4) of bf16 caches do both contractions on the
 //                 matrix cores instead.  The block's outputs (logits, chunk
-//                 max/sum, partial o) leave last, as non-temporal stores:
+//                 max/sum, partial o) leave last, written through to memory:
 //                 writes mixed into the read stream cost the HBM far more
 //                 than their size, so the kernel writes only what Eq. 1 and
 //                 the merge need.

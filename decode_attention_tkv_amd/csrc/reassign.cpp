@@ -28,10 +28,12 @@
 //     entrants (codes and scales for T2) straight into them, on the caller's
 //     stream, before the next step's copies read them (an event gates the
 //     copy streams).  No host thread touches a row.
-//   * resident staging: rows entering T1/T2 reach their pinned home through
-//     one write-back copy per pack on a stream of their own, and a host job
-//     (never waited for by the GPU, which reads only HBM in this mode)
-//     compacts the arenas and files them.
+//   * resident staging: nothing reads the arenas on the decode path, so
+//     rows leaving them free their index and entrants take the lowest free
+//     ones (no compaction); the rows entering T1 are copied from their own
+//     HBM slots into the mapped arena by a few work-groups on the write-back
+//     stream, beside the next decode steps, and T2 entrants' codes and
+//     scales are written there by the quantiser.
 // Every allocation a reassignment may need is made before the device labels
 // change; a failure after that point marks the handle failed (every later
 // call but tkv_destroy, tkv_last_error and tkv_stats returns TKV_ESTATE).
