@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+STAGING_LAYERS = 4  # HBM slots of the stream-staging leg (two layers per copy)
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_tkv_amd", "csrc", "attn.hip")
 def attention_kernel(w, args):
     """Which pass of the split-K kernel a workload's decode steps take: bf16
@@ -349,6 +350,8 @@ def main():
     ap.add_argument("--vector-pass", action="store_true",
                     help="grouped-query bf16 heads on the vector units instead of the matrix cores")
     ap.add_argument("--stream-steps", type=int, default=64, help="timed steps of the stream-staging leg (0: skip)")
+    ap.add_argument("--staging-layers", type=int, default=STAGING_LAYERS,
+                    help="HBM staging slots S of the stream-staging leg (2 .. layers - 1)")
     ap.add_argument("--cpu-steps", type=int, default=192,
                     help="steps of the CPU oracle baseline and of the parity check beside it (0: skip)")
     ap.add_argument("--baseline-steps", type=int, default=None,
@@ -498,7 +501,7 @@ def main():
 
     if args.stream_steps > 0:
         # Stream staging: each step copies every layer's T1 rows from pinned host memory into
-        # one of S = 2 HBM slots, one layer ahead of the attention that reads them.  Three
+        # one of S HBM slots, ahead of the attention that reads them.  Three
         # windows of --stream-steps steps: the first reassignment after a plain prefill (whose
         # positional first placement leaves most rows to re-tier), the steady state (the next
         # window, ending after the next reassignment), and the first reassignment after a
@@ -508,9 +511,9 @@ def main():
         sinputs = inputs if ws.steps <= w.steps else load_inputs(ws, ws.steps, torch)
 
         def window(warm, scored=None, label=""):
-            print("[bench] stream staging (S=2) %s: steps %d..%d" % (label, warm + 1, warm + ns),
+            print("[bench] stream staging (S=%d) %s: steps %d..%d" % (args.staging_layers, label, warm + 1, warm + ns),
                   file=sys.stderr, flush=True)
-            ssecs, sb, sa = run_decode(ws, sinputs, warm, ns, torch, tkv, staging_layers=2,
+            ssecs, sb, sa = run_decode(ws, sinputs, warm, ns, torch, tkv, staging_layers=args.staging_layers,
                                        scored_prefill=scored)
             h2d = sa["h2d_bytes"] - sb["h2d_bytes"]
             return sa, {"timed_steps": "%d..%d" % (warm + 1, warm + ns),
@@ -536,7 +539,7 @@ def main():
             if t in full_samples:
                 cmp[str(t + 1)] = bool(np.array_equal(o, full_samples[t]))
         result["stream_staging"] = dict(steady, **{
-            "staging_layers": 2, "steps": ns, "pinned_h2d_gbs": pinned,
+            "staging_layers": args.staging_layers, "steps": ns, "pinned_h2d_gbs": pinned,
             "window": "steady state: steps %s, after the first reassignment and holding the next"
                       % steady["timed_steps"],
             "first_reassignment_window": first, "scored_prefill_window": scored,

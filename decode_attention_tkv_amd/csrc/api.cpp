@@ -802,8 +802,14 @@ static int flush_deferred(tkv* t, hipStream_t st) {
 
 // Stream mode: copy layers' T1 rows from the pinned arena into their staging
 // slot (layer mod S) on the side streams (K rows and 8-bit rows on one, V rows
-// on the other), up to layer `upto`, each after the
-// attention that last read that slot.
+// on the other), up to layer `upto`, each after the attention that last read
+// that slot.  With an even S >= 4 the layers go in groups of S / 2: layers
+// x .. x + S/2 - 1 (x a multiple of S / 2) take slots x mod S onwards, which
+// are adjacent, as their rows are in the arena, so one copy per area moves
+// the group at one pitch (S / 2 times the rows, the same fixed costs).  The
+// two halves of the slots alternate.  A group is issued once all its layers
+// are within `upto`, so no slot is still waiting for the attention that last
+// read it to be enqueued.
 static int issue_prefetch(tkv* t, int upto) {
   if (t->arena_pending) {
     HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_arena, 0));
@@ -815,12 +821,16 @@ static int issue_prefetch(tkv* t, int upto) {
     n1max = std::max(n1max, t->t1_owner[b].size());
     n2max = std::max(n2max, t->t2_owner[b].size());
   }
-  for (; t->next_issue <= upto && t->next_issue < t->L; ++t->next_issue) {
-    const int x = t->next_issue, slot = x % t->S;
-    if (t->comp_recorded[slot]) {
-      HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_comp[slot], 0));
-      HIP_TRY(t, hipStreamWaitEvent(t->side_v, t->ev_comp[slot], 0));
-    }
+  const int per_copy = (t->S >= 4 && t->S % 2 == 0) ? t->S / 2 : 1;
+  while (t->next_issue <= upto && t->next_issue < t->L) {
+    const int x = t->next_issue, slot = x % t->S;  // x is a multiple of per_copy
+    const int nx = std::min(per_copy, t->L - x);  // layers in this copy; slots slot .. slot + nx - 1
+    if (x + nx - 1 > upto) break;
+    for (int k = 0; k < nx; ++k)
+      if (t->comp_recorded[slot + k]) {
+        HIP_TRY(t, hipStreamWaitEvent(t->side, t->ev_comp[slot + k], 0));
+        HIP_TRY(t, hipStreamWaitEvent(t->side_v, t->ev_comp[slot + k], 0));
+      }
     if (t->flags & TKV_FLAG_TEST_DELAY_COPIES) {
       HIP_TRY(t, launch_delay(kTestDelayIters, t->side));
       HIP_TRY(t, launch_delay(kTestDelayIters, t->side_v));
@@ -832,9 +842,9 @@ static int issue_prefetch(tkv* t, int upto) {
         char* dst = (char*)(which ? t->stage_v : t->stage_k) + (size_t)slot * t->B * t->capS * t->row_bytes;
         const char* src = (const char*)(which ? t->arena1_v : t->arena1_k) + (size_t)x * t->B * t->cap1 * t->row_bytes;
         HIP_TRY(t, hipMemcpy2DAsync(dst, (size_t)t->capS * hb, src, (size_t)t->cap1 * hb, width,
-                                    (size_t)t->B * t->Hkv, hipMemcpyHostToDevice, which ? t->side_v : t->side));
+                                    (size_t)nx * t->B * t->Hkv, hipMemcpyHostToDevice, which ? t->side_v : t->side));
       }
-      t->st.h2d_bytes += 2 * (int64_t)width * t->B * t->Hkv;
+      t->st.h2d_bytes += 2 * (int64_t)width * nx * t->B * t->Hkv;
     }
     if (n2max > 0) {
       // 8-bit rows: codes and scales over PCIe into the slot's T2 area, which the
@@ -846,15 +856,19 @@ static int issue_prefetch(tkv* t, int upto) {
         int8_t* qd = (which ? t->qstage_v : t->qstage_k) + (size_t)slot * c_layer;
         float* sd = (which ? t->qsscale_v : t->qsscale_k) + (size_t)slot * s_layer;
         HIP_TRY(t, hipMemcpy2DAsync(qd, (size_t)t->cap2 * t->D, (which ? t->arena2_v : t->arena2_k) + (size_t)x * c_layer,
-                                    (size_t)t->cap2 * t->D, cw, (size_t)t->B * t->Hkv, hipMemcpyHostToDevice, t->side));
+                                    (size_t)t->cap2 * t->D, cw, (size_t)nx * t->B * t->Hkv, hipMemcpyHostToDevice,
+                                    t->side));
         HIP_TRY(t, hipMemcpy2DAsync(sd, (size_t)t->cap2 * t->sh * 4,
                                     (which ? t->ascale_v : t->ascale_k) + (size_t)x * s_layer, (size_t)t->cap2 * t->sh * 4,
-                                    n2max * t->sh * 4, (size_t)t->B, hipMemcpyHostToDevice, t->side));
+                                    n2max * t->sh * 4, (size_t)nx * t->B, hipMemcpyHostToDevice, t->side));
       }
-      t->st.h2d_bytes += 2 * (int64_t)(cw * t->B * t->Hkv + n2max * t->sh * 4 * t->B);
+      t->st.h2d_bytes += 2 * (int64_t)nx * (cw * t->B * t->Hkv + n2max * t->sh * 4 * t->B);
     }
-    HIP_TRY(t, hipEventRecord(t->ev_h2d[slot], t->side));
-    HIP_TRY(t, hipEventRecord(t->ev_h2d_v[slot], t->side_v));
+    for (int k = 0; k < nx; ++k) {
+      HIP_TRY(t, hipEventRecord(t->ev_h2d[slot + k], t->side));
+      HIP_TRY(t, hipEventRecord(t->ev_h2d_v[slot + k], t->side_v));
+    }
+    t->next_issue += nx;
   }
   return TKV_OK;
 }

@@ -97,14 +97,18 @@ def test_chunk_sizes_and_layer_groups(chunk):
     _compare(w, a, _oracle(w, inp, 3), 3)
 
 
-def test_layer_groups_stream_staging():
-    # stream staging prefetches each layer's T1 rows one layer ahead, across
-    # the caller's layer groups; outputs equal the resident single call's bit
-    # for bit (the reduction follows logical position, whatever the staging)
-    w = tkvsynth.CONFIGS["14b"].replace(layers=6, batch=2, prefill=1000, steps=3, hbm_ratio=0.5)
+@pytest.mark.parametrize("slots,groups", [(2, [1, 2, 3]), (4, [1, 2, 3]), (4, [3, 1, 3]), (6, [2, 5])],
+                         ids=["S2", "S4", "S4_odd_groups", "S6_odd_layers"])
+def test_layer_groups_stream_staging(slots, groups):
+    # stream staging prefetches each layer's T1 rows ahead of its attention,
+    # across the caller's layer groups (with an even S >= 4, two layers per
+    # copy, issued once both slots are free); outputs equal the resident
+    # single call's bit for bit (the reduction follows logical position,
+    # whatever the staging)
+    w = tkvsynth.CONFIGS["14b"].replace(layers=sum(groups), batch=2, prefill=1000, steps=3, hbm_ratio=0.5)
     inp = Inputs(w)
     a = _run(w, inp, 3)
-    b = _run(w, inp, 3, groups=[1, 2, 3], staging_layers=2)
+    b = _run(w, inp, 3, groups=groups, staging_layers=slots)
     assert all(np.array_equal(x, y) for x, y in zip(a[0], b[0]))
     _compare(w, b, _oracle(w, inp, 3), 3)
 

@@ -64,13 +64,18 @@ def _gqa_t2():
                                               recent=32)
 
 
-@pytest.mark.parametrize("which", ["tiny_f32", "gqa_bf16_t2"])
-def test_delayed_copies_bitwise(which):
+@pytest.mark.parametrize("which,slots", [("tiny_f32", 2), ("gqa_bf16_t2", 2), ("tiny_f32", 4), ("gqa_bf16_t2", 4)],
+                         ids=["tiny_f32", "gqa_bf16_t2", "tiny_f32_S4_pairs", "gqa_bf16_t2_S4_pairs"])
+def test_delayed_copies_bitwise(which, slots):
+    """S = 4 copies two layers at a time (tiny: 5 layers, so the last goes
+    alone; the grouped-query case then has 6 layers, so that S < layers)."""
     w = _tiny5() if which == "tiny_f32" else _gqa_t2()
+    if slots >= w.layers:
+        w = w.replace(layers=slots + 2)
     inp = Inputs(w)
     tkv = _tkv()
-    base = run_parity(w, inp, w.steps, check_every=8, staging_layers=2)
-    slow = run_parity(w, inp, w.steps, check_every=8, staging_layers=2,
+    base = run_parity(w, inp, w.steps, check_every=8, staging_layers=slots)
+    slow = run_parity(w, inp, w.steps, check_every=8, staging_layers=slots,
                       extra_flags=tkv.TKV_FLAG_TEST_DELAY_COPIES)
     _same_runs(base, slow)
     res = run_parity(w, inp, w.steps, check_every=8)
