@@ -81,8 +81,9 @@ typedef struct {
                              (with TKV_FLAG_SHARED_HBM: T0 slots plus a staging mirror of
                              T1/T2), and only changed rows cross to or from the host.
                              2..layers-1: "stream": each step copies a layer's T1/T2 rows
-                             from pinned host memory into slot (layer mod S), one layer
-                             ahead of the attention that reads it. */
+                             from pinned host memory into slot (layer mod S), ahead of the
+                             attention that reads it (S - 1 layers ahead at most; with an
+                             even S >= 4, S/2 consecutive layers per copy). */
   int32_t chunk;          /* split-K rows per work-group: 128, 256 or 512; 0 = 512 when
                              q_heads >= 4 * kv_heads, else 256 */
   uint64_t flags;         /* TKV_FLAG_* */
