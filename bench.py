@@ -265,9 +265,11 @@ def cpu_baseline(w, n_steps, trace=None):
     vn = w.values(w.kv(1, w.prefill, n_steps, heavy, u))
     q = w.values(w.q(0, n_steps, u))
     refs, labels = {}, []
+    live_rows = 0  # live rows attended, summed over steps and sequences
     t0 = time.perf_counter()
     for t in range(n_steps):
         o.append(kn[:, :, t], vn[:, :, t])
+        live_rows += int(np.count_nonzero(o.tier[:, : o.n] < 3))
         ref = o.attend(q[t])
         if trace is not None and t in trace["outs"]:
             refs[t] = ref
@@ -278,6 +280,8 @@ def cpu_baseline(w, n_steps, trace=None):
     secs = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
     res = {"value": n_steps / secs, "unit": "steps/s", "cores": threads, "kind": "oracle",
+           # the live K/V bytes those steps attend (the GPU roofline's algorithmic bytes) per second
+           "kv_gbs": live_rows * w.kv_bytes_per_token() / secs / 1e9,
            "sample": "%s workload, prefill %d, decode steps 1..%d incl. %d reassignment(s); fp64 C "
                      "attention (OpenMP) + numpy scoring/tiering; %.1f s"
                      % (w.name, w.prefill, n_steps, n_steps // w.delta, secs)}
