@@ -300,6 +300,10 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
   __shared__ float ps[MK ? 1 : G][MK ? 1 : CHUNK];     // p = 2^(z - m) of the vector path
   __shared__ float red[NW][G];
   __shared__ uint32_t codes_s[CHUNK];
+  // deferred Eq. 1: the previous step's weight sums of the chunk's rows, held
+  // here until the block's last barrier is behind it (a global store ahead of
+  // a barrier holds the wave there until the store is acknowledged)
+  __shared__ float es[DEF ? CHUNK : 1];
   // matrix-core p.V: P as three bf16 terms (hi, mid, lo), G heads x CHUNK rows
   __shared__ __attribute__((aligned(16))) bf16_t pt[MK ? 3 : 1][MK ? G : 1][MK ? CHUNK : 1];
 
@@ -435,11 +439,15 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
             if (vp[i]) e += exp2f(acc[i] * a.qscale - pM[i]) * piL[i];
           e += __shfl_xor(e, 16);
           e += __shfl_xor(e, 32);
-          if (kq == 0 && j0 + r < nprev) store_through(sp + r, e);
+          if (kq == 0) es[r] = e;
         }
       }
     }
-    if (prev == 2) return;  // score only: the whole block leaves here
+    if (prev == 2) {  // score only: the sums leave, and so does the whole block
+      __syncthreads();
+      for (int r = tid; r < nrows && j0 + r < nprev; r += 256) store_through(sp + r, es[r]);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float m = group_max<16>(mx[i]);
@@ -677,6 +685,14 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
     const int g = tid >> 1;
     const float v = (tid & 1) ? ((red[0][g] + red[1][g]) + red[2][g]) + red[3][g] : mc[g];
     store_through(a.part_ml + ((hbase + g) * a.max_chunks + c) * 2 + (tid & 1), v);
+  }
+  if constexpr (MK && DEF) {
+    if (a.prev_mode != 0) {
+      // the previous step's rows: live indices below the new row's (all of them in a score-only pass)
+      const int nprev = a.prev_mode == 1 ? nl - 1 : nl;
+      float* sp = a.spart + (((int64_t)l * a.kv_heads + kvh) * a.batch + b) * a.lstride + j0;
+      for (int r = tid; r < nrows && j0 + r < nprev; r += 256) store_through(sp + r, es[r]);
+    }
   }
   // logits, padded with zeros to the line that holds the chunk's last row
   // (none when Eq. 1 is deferred)
