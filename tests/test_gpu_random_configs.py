@@ -1,0 +1,60 @@
+"""Seeded random configurations through the whole path, against the oracle.
+
+Each case draws a small workload -- dtype, head_dim, kv heads and group,
+layers, batch, prefill (0 to a few hundred positions, so also an empty
+cache), decode steps and Delta, the HBM, eviction and 8-bit ratios
+("Not All Thoughts Need HBM", gist.science summary, Method §1: the tier
+budgets; HBM + eviction may exceed 1), the protected prompt, sinks and
+recent window, the 8-bit codec variants, eviction-only, the batch-shared
+budget, resident or stream staging with a random number of slots, and the
+chunk size -- and runs it step by step with a reassignment every Delta steps
+(Method §4), as the fixed tests do: outputs within the dtype's tolerance,
+scores within relative 1e-4 (Method §2, Eq. 1), and every reassignment's
+labels and changed-row lists bit-exact against the oracle's rules applied to
+the GPU's fp32 scores.  The draws cover combinations no fixed test names.
+"""
+import numpy as np
+import pytest
+
+import tkvsynth
+from harness import Inputs
+from test_gpu_reassign import run_parity
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 64
+
+
+def _draw(i):
+    r = np.random.default_rng(1000 + i)
+    dtype = "bf16" if r.random() < 0.6 else "f32"
+    group = int(r.choice([1, 2, 4, 5, 8]))
+    kv_heads = int(r.choice([1, 2, 4]))
+    layers = int(r.integers(1, 5))
+    batch = int(r.integers(1, 4))
+    prefill = int(r.choice([0, int(r.integers(40, 420))]))
+    delta = int(r.choice([8, 16, 32]))
+    steps = int(r.integers(2, 4)) * delta + int(r.integers(0, delta))
+    no_t1 = bool(r.random() < 0.15)
+    shared = bool(not no_t1 and batch > 1 and r.random() < 0.25)
+    t2 = float(r.choice([0.0, 0.0, 0.1, 0.25]))
+    w = tkvsynth.CONFIGS["tiny"].replace(
+        name="random%d" % i, dtype=dtype, head_dim=int(r.choice([64, 128])), kv_heads=kv_heads,
+        q_heads=kv_heads * group, layers=layers, batch=batch, prefill=prefill, steps=steps, delta=delta,
+        hbm_ratio=float(np.round(r.uniform(0.0, 1.0), 2)), evict_ratio=float(np.round(r.uniform(0.0, 0.6), 2)),
+        t2_ratio=t2, prompt=int(r.integers(0, min(prefill, 48) + 1)), sinks=int(r.integers(0, 6)),
+        recent=int(r.integers(0, 40)), seed=int(r.integers(0, 1 << 20)), no_t1=no_t1, shared_hbm=shared,
+        t2_fp8=bool(t2 > 0 and r.random() < 0.5), t2_head_scales=bool(t2 > 0 and r.random() < 0.5))
+    staging = int(r.integers(2, layers)) if layers >= 3 and r.random() < 0.4 else 0
+    chunk = int(r.choice([0, 128, 256, 512]))
+    return w, staging, chunk
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_config(i):
+    w, staging, chunk = _draw(i)
+    print("[random %d] %s staging %d chunk %d" % (i, w, staging, chunk), flush=True)
+    outs, s, tiers, st, o, n_reassign = run_parity(w, Inputs(w), w.steps, check_every=3, staging_layers=staging,
+                                                   chunk=chunk)
+    assert n_reassign == w.steps // w.delta
+    assert st["reassigns"] == n_reassign
