@@ -7,7 +7,9 @@ cache), decode steps and Delta, the HBM, eviction and 8-bit ratios
 budgets; HBM + eviction may exceed 1), the protected prompt, sinks and
 recent window, the 8-bit codec variants, eviction-only, the batch-shared
 budget, resident or stream staging with a random number of slots, and the
-chunk size -- and runs it step by step with a reassignment every Delta steps
+chunk size, and the calls of a step (append and attention, the single-call
+step, or the attention in layer groups) -- and runs it step by step with a
+reassignment every Delta steps
 (Method §4), as the fixed tests do: outputs within the dtype's tolerance,
 scores within relative 1e-4 (Method §2, Eq. 1), and every reassignment's
 labels and changed-row lists bit-exact against the oracle's rules applied to
@@ -47,14 +49,20 @@ def _draw(i):
         t2_fp8=bool(t2 > 0 and r.random() < 0.5), t2_head_scales=bool(t2 > 0 and r.random() < 0.5))
     staging = int(r.integers(2, layers)) if layers >= 3 and r.random() < 0.4 else 0
     chunk = int(r.choice([0, 128, 256, 512]))
-    return w, staging, chunk
+    # the calls of a step: append + attention, the single-call step, or layer groups
+    calls = str(r.choice(["two", "one", "groups"])) if layers > 1 else str(r.choice(["two", "one"]))
+    groups = None
+    if calls == "groups":
+        cut = sorted(r.choice(np.arange(1, layers), size=int(r.integers(1, layers)), replace=False).tolist())
+        groups = [b - a for a, b in zip([0] + cut, cut + [layers])]
+    return w, staging, chunk, calls, groups
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_config(i):
-    w, staging, chunk = _draw(i)
-    print("[random %d] %s staging %d chunk %d" % (i, w, staging, chunk), flush=True)
+    w, staging, chunk, calls, groups = _draw(i)
+    print("[random %d] %s staging %d chunk %d calls %s %s" % (i, w, staging, chunk, calls, groups), flush=True)
     outs, s, tiers, st, o, n_reassign = run_parity(w, Inputs(w), w.steps, check_every=3, staging_layers=staging,
-                                                   chunk=chunk)
+                                                   chunk=chunk, calls=calls, groups=groups)
     assert n_reassign == w.steps // w.delta
     assert st["reassigns"] == n_reassign

@@ -42,11 +42,14 @@ def _check_deltas(c, o_deltas, n):
         assert gd == od, "demote list differs (seq %d)" % b
 
 
-def run_parity(w, inp, steps, check_every=1, score_at=(), **kw):
+def run_parity(w, inp, steps, check_every=1, score_at=(), calls="two", groups=None, **kw):
     """Drive GPU and oracle together; at every reassignment the oracle ranks by
     the GPU's fp32 scores, its labels must equal the GPU's, then both go on.
     score_at: step counts after which the scores are also compared
-    (relative 1e-4), besides the end of the run."""
+    (relative 1e-4), besides the end of the run.  calls: "two" (tkv_append,
+    then tkv_decode_attn over every layer), "one" (tkv_decode_step) or
+    "groups" (tkv_append, then tkv_decode_attn over the layer groups of
+    sizes `groups`, in order)."""
     c = _new(w, **kw)
     if w.prefill:  # a workload with no prefill starts from an empty cache
         c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
@@ -57,9 +60,19 @@ def run_parity(w, inp, steps, check_every=1, score_at=(), **kw):
     n_reassign = 0
     for t in range(steps):
         k, v = inp.step_kv(t)
-        c.append(to_device(k, w.dtype), to_device(v, w.dtype))
+        dq = to_device(inp.q[t], w.dtype)
+        if calls == "one":
+            c.decode_step(to_device(k, w.dtype), to_device(v, w.dtype), dq, out)
+        else:
+            c.append(to_device(k, w.dtype), to_device(v, w.dtype))
+            if calls == "groups":
+                lb = 0
+                for g in groups:
+                    c.decode_attn(dq[lb:lb + g], out[lb:lb + g], layer_begin=lb, layer_count=g)
+                    lb += g
+            else:
+                c.decode_attn(dq, out)
         o.append(w.values(k), w.values(v))
-        c.decode_attn(to_device(inp.q[t], w.dtype), out)
         ref = o.attend(w.values(inp.q[t]))
         got = out.cpu().numpy()
         outs.append(got.copy())
