@@ -8,8 +8,9 @@ budgets; HBM + eviction may exceed 1), the protected prompt, sinks and
 recent window, the 8-bit codec variants, eviction-only, the batch-shared
 budget, resident or stream staging with a random number of slots, and the
 chunk size, and the calls of a step (append and attention, the single-call
-step, or the attention in layer groups) -- and runs it step by step with a
-reassignment every Delta steps
+step, or the attention in layer groups), and whether the reassignments go
+through tkv_reassign or tkv_reassign_static -- and runs it step by step with
+a reassignment every Delta steps
 (Method §4), as the fixed tests do: outputs within the dtype's tolerance,
 scores within relative 1e-4 (Method §2, Eq. 1), and every reassignment's
 labels and changed-row lists bit-exact against the oracle's rules applied to
@@ -55,14 +56,16 @@ def _draw(i):
     if calls == "groups":
         cut = sorted(r.choice(np.arange(1, layers), size=int(r.integers(1, layers)), replace=False).tolist())
         groups = [b - a for a, b in zip([0] + cut, cut + [layers])]
-    return w, staging, chunk, calls, groups
+    static = bool(r.random() < 0.5)  # reassign through the entry point that allocates nothing
+    return w, staging, chunk, calls, groups, static
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_config(i):
-    w, staging, chunk, calls, groups = _draw(i)
-    print("[random %d] %s staging %d chunk %d calls %s %s" % (i, w, staging, chunk, calls, groups), flush=True)
+    w, staging, chunk, calls, groups, static = _draw(i)
+    print("[random %d] %s staging %d chunk %d calls %s %s static %s" % (i, w, staging, chunk, calls, groups, static),
+          flush=True)
     outs, s, tiers, st, o, n_reassign = run_parity(w, Inputs(w), w.steps, check_every=3, staging_layers=staging,
-                                                   chunk=chunk, calls=calls, groups=groups)
+                                                   chunk=chunk, calls=calls, groups=groups, static=static)
     assert n_reassign == w.steps // w.delta
     assert st["reassigns"] == n_reassign

@@ -42,14 +42,16 @@ def _check_deltas(c, o_deltas, n):
         assert gd == od, "demote list differs (seq %d)" % b
 
 
-def run_parity(w, inp, steps, check_every=1, score_at=(), calls="two", groups=None, **kw):
+def run_parity(w, inp, steps, check_every=1, score_at=(), calls="two", groups=None, static=False, **kw):
     """Drive GPU and oracle together; at every reassignment the oracle ranks by
     the GPU's fp32 scores, its labels must equal the GPU's, then both go on.
     score_at: step counts after which the scores are also compared
     (relative 1e-4), besides the end of the run.  calls: "two" (tkv_append,
     then tkv_decode_attn over every layer), "one" (tkv_decode_step) or
     "groups" (tkv_append, then tkv_decode_attn over the layer groups of
-    sizes `groups`, in order)."""
+    sizes `groups`, in order).  static: reassign with tkv_reassign_static
+    (the scratch in the library's static device array) instead of
+    tkv_reassign."""
     c = _new(w, **kw)
     if w.prefill:  # a workload with no prefill starts from an empty cache
         c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
@@ -83,7 +85,11 @@ def run_parity(w, inp, steps, check_every=1, score_at=(), calls="two", groups=No
             assert rel <= 1e-4, "scores max-rel %.3g after %d steps" % (rel, t + 1)
         if (t + 1) % w.delta == 0:
             g_s = c.read_scores()[:, : o.n]
-            c.reassign()
+            if static:
+                import decode_attention_tkv_amd as tkv
+                tkv.tkv_reassign_static(c.h)
+            else:
+                c.reassign()
             tiers, deltas = o.reassign(rank_scores=g_s)
             assert np.array_equal(c.read_tiers()[:, : o.n], tiers), "labels differ at step %d" % (t + 1)
             _check_deltas(c, deltas, o.n)
