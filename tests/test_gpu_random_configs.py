@@ -69,3 +69,32 @@ def test_random_config(i):
                                                    chunk=chunk, calls=calls, groups=groups, static=static)
     assert n_reassign == w.steps // w.delta
     assert st["reassigns"] == n_reassign
+
+
+def _draw_long(i):
+    """A long cache on few layers and heads: up to 9000 prefilled positions,
+    more than 16 chunks of 128 or 256 rows, so a head's chunk list runs past the 16 pairs
+    the merge pass keeps in registers and it takes its two-pass form."""
+    r = np.random.default_rng(5000 + i)
+    chunk = int(r.choice([128, 256]))
+    dtype = "bf16" if r.random() < 0.6 else "f32"
+    kv_heads = int(r.choice([1, 2]))
+    group = int(r.choice([1, 2, 4, 5, 8]))
+    prefill = int(r.integers(17 * chunk, 9001))  # more than 16 chunks
+    delta = 16
+    w = tkvsynth.CONFIGS["tiny"].replace(
+        name="long%d" % i, dtype=dtype, head_dim=int(r.choice([64, 128])), kv_heads=kv_heads,
+        q_heads=kv_heads * group, layers=int(r.integers(1, 3)), batch=int(r.integers(1, 3)), prefill=prefill,
+        steps=delta + int(r.integers(1, delta)), delta=delta, hbm_ratio=float(np.round(r.uniform(0.1, 0.9), 2)),
+        evict_ratio=float(np.round(r.uniform(0.0, 0.3), 2)), t2_ratio=float(r.choice([0.0, 0.1])),
+        prompt=int(r.integers(0, 200)), sinks=4, recent=int(r.integers(16, 129)), seed=int(r.integers(0, 1 << 20)))
+    return w, chunk
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_long_cache(i):
+    w, chunk = _draw_long(i)
+    assert (w.prefill + w.steps + chunk - 1) // chunk > 16
+    print("[long %d] %s chunk %d" % (i, w, chunk), flush=True)
+    outs, s, tiers, st, o, n_reassign = run_parity(w, Inputs(w), w.steps, check_every=4, chunk=chunk)
+    assert n_reassign == 1
