@@ -98,3 +98,16 @@ def test_random_long_cache(i):
     print("[long %d] %s chunk %d" % (i, w, chunk), flush=True)
     outs, s, tiers, st, o, n_reassign = run_parity(w, Inputs(w), w.steps, check_every=4, chunk=chunk)
     assert n_reassign == 1
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_scored_prefill(i):
+    """The same draws (a prompt of at least 40 positions) started with the
+    scored prefill: the prompt's causal attention gives the first scores and
+    one full re-placement, against the oracle's, then the decode steps."""
+    from test_gpu_prefill import run_scored
+    w, staging, chunk, _, _, _ = _draw(100 + i)
+    if w.prefill < 40:
+        w = w.replace(prefill=40 + 7 * i, prompt=min(w.prompt, 20))
+    print("[scored %d] %s staging %d chunk %d" % (i, w, staging, chunk), flush=True)
+    run_scored(w, w.steps, check_every=3, staging_layers=staging, chunk=chunk)
