@@ -230,10 +230,12 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   // the matrix-core path over resident staging
   t->defer = resident && s.dtype == TKV_BF16 && group >= 4 && !t->vector_pass;
   if (t->defer) {
-    dev(&t->qbuf[0], L * B * Hq * t->D * t->esz);
-    dev(&t->qbuf[1], L * B * Hq * t->D * t->esz);
-    dev((void**)&t->mlbuf[0], L * B * Hq * 2 * 4);
-    dev((void**)&t->mlbuf[1], L * B * Hq * 2 * 4);
+    t->pair = 3 * group <= 16;  // two steps' queries beside this step's in the 16-row tile
+    for (int i = 0; i < 3; ++i) {
+      dev(&t->qbuf[i], L * B * Hq * t->D * t->esz);
+      dev((void**)&t->mlbuf[i], L * B * Hq * 2 * 4);
+    }
+    dev((void**)&t->s_view, B * nmax * 4);
     dev((void**)&t->spart, L * t->Hkv * B * t->lstride * 4);
   } else {
     dev((void**)&t->logits, L * B * Hq * t->lstride * 4);
@@ -692,16 +694,29 @@ static int prev_tiles(const tkv* t) {
   return (m + 63) / 64;
 }
 
+// Deferred Eq. 1: how many pending steps the running step's launches form
+// (and its merge pass folds): both once two are pending, or the one pending
+// step when two do not fit the logits tile.  Fixed for the whole step: pend
+// changes only when a step ends or a reassignment commits.
+static int defer_now(const tkv* t) {
+  if (!t->defer) return 0;
+  return t->pend == 2 ? 2 : (t->pend == 1 && !t->pair) ? 1 : 0;
+}
+
 // Split-K attention + chunk merge for layers [lb, lb + lc) whose q/out start at q, out.
 // step: the fused append + Eq. 1 update of a whole-step launch, or nullptr.
 static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int max_live, hipStream_t st,
                          const StepArgs* step = nullptr) {
   AttnArgs a{};
+  const int now = defer_now(t);
   if (t->defer) {
-    a.prev_mode = t->prev_pending ? 1 : 0;
+    a.prev_mode = now ? 1 : 0;
+    a.prev_steps = now;
     a.qprev = t->qbuf[t->qcur];
-    a.qsave = t->qbuf[t->qcur ^ 1];
+    a.qprev2 = t->qbuf[(t->qcur + 2) % 3];
+    a.qsave = t->qbuf[(t->qcur + 1) % 3];
     a.mlprev = t->mlbuf[t->qcur];
+    a.mlprev2 = t->mlbuf[(t->qcur + 2) % 3];
     a.spart = t->spart;
   }
   a.rows = t->rowspace();
@@ -756,8 +771,8 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
   ScoreArgs fold{};
   int fold_tiles = 0;
   if (t->defer) {
-    f.mlprev = t->mlbuf[t->qcur ^ 1];
-    if (t->prev_pending && lb + lc == t->L) {
+    f.mlprev = t->mlbuf[(t->qcur + 1) % 3];
+    if (now && lb + lc == t->L) {
       fold = defer_fold_args(t);
       fold_tiles = prev_tiles(t);
     }
@@ -767,9 +782,12 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
   return TKV_OK;
 }
 
-// Deferred Eq. 1 of the pending step on its own: a score-only pass over its
-// rows' K in every layer, then the fold.
-static int flush_deferred(tkv* t, hipStream_t st) {
+// Deferred Eq. 1 of the pending steps on their own: a score-only pass over
+// their rows' K in every layer, then the fold, into s (commit: nothing is
+// pending afterwards) or into a copy of s that a score read returns (the
+// steps stay pending and are later formed and folded exactly as without the
+// read).
+static int flush_deferred(tkv* t, hipStream_t st, bool commit) {
   AttnArgs a{};
   a.rows = t->rowspace();
   a.live_loc = t->live_loc;
@@ -782,21 +800,29 @@ static int flush_deferred(tkv* t, hipStream_t st) {
   a.max_chunks = t->max_chunks;
   a.lstride = t->lstride;
   a.prev_mode = 2;
+  a.prev_steps = t->pend;
   a.qprev = t->qbuf[t->qcur];
+  a.qprev2 = t->qbuf[(t->qcur + 2) % 3];
   a.mlprev = t->mlbuf[t->qcur];
+  a.mlprev2 = t->mlbuf[(t->qcur + 2) % 3];
   a.spart = t->spart;
   int m = 0;
   for (int b = 0; b < t->B; ++b) {
-    a.nlive[b] = t->prev_nlive[b];  // that step's rows (the live list only grew since)
+    a.nlive[b] = t->prev_nlive[b];  // the last pending step's rows (the live list only grew since)
     m = std::max(m, a.nlive[b]);
   }
   const int chunks = (m + t->chunk - 1) / t->chunk;
   StepArgs none{};
+  ScoreArgs fold = defer_fold_args(t);
+  if (!commit) {
+    HIP_TRY(t, hipMemcpyAsync(t->s_view, t->s, (size_t)t->B * t->nmax * 4, hipMemcpyDeviceToDevice, st));
+    fold.s = t->s_view;
+  }
   if (chunks > 0) {
     HIP_TRY(t, launch_attn(a, none, t->dtype, t->D, t->group, t->chunk, false, t->L, chunks, nullptr, nullptr, st));
-    HIP_TRY(t, launch_fold64(defer_fold_args(t), prev_tiles(t), st));
+    HIP_TRY(t, launch_fold64(fold, prev_tiles(t), st));
   }
-  t->prev_pending = false;
+  if (commit) t->pend = 0;
   return TKV_OK;
 }
 
@@ -887,9 +913,9 @@ static void end_step(tkv* t, int max_live) {
   for (int b = 0; b < t->B; ++b) sa.nlive[b] = t->nlive[b];
   if (t->defer) {
     // computed and folded by the next step's launches (or by tkv_flush_score)
-    t->prev_pending = max_live > 0;
+    t->pend = t->pend - defer_now(t) + (max_live > 0 ? 1 : 0);
     t->prev_nlive = t->nlive;
-    t->qcur ^= 1;
+    t->qcur = (t->qcur + 1) % 3;
   } else {
     // applied by the next append's launch (or by tkv_flush_score)
     t->pending_score = sa;
@@ -1003,7 +1029,7 @@ extern "C" int tkv_stats(tkv_t* t, tkv_stats_t* out) {
 }
 
 int tkv_flush_score(tkv* t, hipStream_t stream) {
-  if (t->defer) return t->prev_pending ? flush_deferred(t, stream) : TKV_OK;
+  if (t->defer) return t->pend ? flush_deferred(t, stream, true) : TKV_OK;
   if (!t->score_pending) return TKV_OK;
   HIP_TRY(t, launch_score(t->pending_score, t->pending_tiles, stream));
   t->score_pending = false;
@@ -1013,8 +1039,16 @@ int tkv_flush_score(tkv* t, hipStream_t stream) {
 static int read_scores_impl(tkv_t* t, float* scores, tkv_stream_t stream) {
   if (int rc = usable(t)) return rc;
   if (!scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
-  if (int rc = tkv_flush_score(t, (hipStream_t)stream)) return rc;
-  HIP_TRY(t, hipMemcpyAsync(scores, t->s, (size_t)t->B * t->nmax * 4, hipMemcpyDeviceToHost, (hipStream_t)stream));
+  const float* src = t->s;
+  if (t->defer && t->pend) {
+    // the pending steps into a copy of s: they stay pending, so a read never
+    // changes which steps a later launch sums together
+    if (int rc = flush_deferred(t, (hipStream_t)stream, false)) return rc;
+    src = t->s_view;
+  } else if (int rc = tkv_flush_score(t, (hipStream_t)stream)) {
+    return rc;
+  }
+  HIP_TRY(t, hipMemcpyAsync(scores, src, (size_t)t->B * t->nmax * 4, hipMemcpyDeviceToHost, (hipStream_t)stream));
   HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
   return TKV_OK;
 }
@@ -1026,7 +1060,12 @@ static int write_scores_impl(tkv_t* t, const float* scores, tkv_stream_t stream)
   if (int rc = usable(t)) return rc;
   if (!scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "step in progress");
-  if (int rc = tkv_flush_score(t, (hipStream_t)stream)) return rc;
+  // the written scores replace s with every pending update: those are dropped
+  if (t->defer) {
+    t->pend = 0;
+  } else {
+    t->score_pending = false;
+  }
   HIP_TRY(t, hipMemcpyAsync(t->s, scores, (size_t)t->B * t->nmax * 4, hipMemcpyHostToDevice, (hipStream_t)stream));
   HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
   return TKV_OK;

@@ -269,14 +269,23 @@ __global__ __launch_bounds__(256) void k_append(const AppendArgs a, const ScoreA
 // what these writes touch: the slot was free, and the fold only reads
 // positions and live indices below the new row's.
 //
-// DEF (matrix-core path, resident staging): Eq. 1 for the previous step runs
-// here instead of from stored logits.  Its queries fill the padded rows
-// G..2G-1 of the logits tile, so each K tile gives both steps' logits in the
-// same MFMAs; with that step's (M, 1/L) each row's weights are summed over
-// the group's heads and one value per row and kv head leaves the block, in
-// place of G logits.  Chunk-0 blocks keep this step's queries for the next.
+// DEF (matrix-core path, resident staging): Eq. 1 for pending steps runs
+// here instead of from stored logits.  Their queries fill the padded rows of
+// the logits tile (G..2G-1 the last pending step, 2G..3G-1 the one before it
+// when 3G <= 16), so each K tile gives every step's logits in the same MFMAs;
+// with each pending step's (M, 1/L) a row's weights are summed over the
+// group's heads (and both steps) and one value per row and kv head leaves the
+// block, in place of G logits per step.  The host asks for two steps every
+// other launch when they fit, and for none in between.  Chunk-0 blocks keep
+// this step's queries for later.
+//
+// At least four waves per SIMD: without that bound the compiler puts the
+// matrix-core accumulators in AGPRs and, at G = 5 with two pending steps,
+// needs 132 registers, one wave fewer; with it, the same code fits in VGPRs
+// alone (no spills).  The vector path's allocation is unchanged.
 template <typename T, int D, int G, int CHUNK, bool MK, bool QT, bool DEF>
-__global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const StepArgs n) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   constexpr int LPR = D * (int)sizeof(T) / 16;  // lanes per row
   constexpr int EPL = 16 / (int)sizeof(T);      // elements per lane
   constexpr int RPI = 64 / LPR;                 // rows per wave load
@@ -350,10 +359,13 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
 
   float mc[G];
   if constexpr (MK) {
-    // deferred Eq. 1 (DEF): prev_mode 1, the previous step's rows are the live
-    // indices below the new row's; 2, score only over every live row
+    // deferred Eq. 1 (DEF): prev_mode 1, the last pending step's rows are the
+    // live indices below the new row's; 2, score only over every live row.
+    // With two pending steps the earlier one had one row fewer (each step
+    // appends one row per sequence and nothing leaves between reassignments).
     const int prev = DEF ? a.prev_mode : 0;
     const int nprev = prev == 1 ? nl - 1 : nl;
+    const bool two = DEF && prev != 0 && a.prev_steps == 2;
     // ---- phase 1 on the matrix cores: Z[16 heads x 16 rows] += Q[16 x 32] K^T[32 x 16],
     // D/32 steps per tile of 16 rows (v_mfma_f32_16x16x32_bf16).  Lane l feeds
     // head / row (l % 16) and the 8 elements 8*(l/16) of each 32-wide slice;
@@ -363,26 +375,34 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
     const int hl = lane & 15, kq = lane >> 4;
     bf16x8 qa[KC];
     const int64_t qrow = ((int64_t)l * a.batch + b) * a.q_heads + kvh * G;  // head 0 of the group, layer l
+    // this lane's query row of the tile: this step's head hl, a pending
+    // step's head, or none (zeros)
+    const T* qsrc = nullptr;
+    if (hl < G && prev != 2)
+      qsrc = (const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + hl) * D;
+    else if (DEF && prev != 0 && hl >= G && hl < 2 * G)
+      qsrc = (const T*)a.qprev + (qrow + hl - G) * D;
+    else if (two && hl >= 2 * G && hl < 3 * G)
+      qsrc = (const T*)a.qprev2 + (qrow + hl - 2 * G) * D;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (hl < G && prev != 2)
-        u = load16((const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + hl) * D + 32 * kc + 8 * kq);
-      else if (DEF && prev != 0 && hl >= G && hl < 2 * G)
-        u = load16((const T*)a.qprev + (qrow + hl - G) * D + 32 * kc + 8 * kq);
+      const uint4 u = qsrc ? load16(qsrc + 32 * kc + 8 * kq) : make_uint4(0, 0, 0, 0);
       if (DEF && prev != 2 && c == 0 && hl < G)
         *reinterpret_cast<uint4*>((T*)a.qsave + (qrow + hl) * D + 32 * kc + 8 * kq) = u;
       qa[kc] = as_bf16x8(u);
     }
-    // the previous step's (M, 1/L) of the heads this lane receives in rows G..2G-1
-    bool vp[4];
+    // the pending steps' (M, 1/L) of the heads this lane receives: tile rows
+    // G..2G-1 the last pending step, rows 2G..3G-1 the one before it (v2)
     float pM[4], piL[4];
+    bool vp[4], v2[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hp = 4 * kq + i - G;
-      vp[i] = DEF && prev != 0 && hp >= 0 && hp < G;
-      pM[i] = vp[i] ? a.mlprev[(qrow + hp) * 2] : 0.f;
-      piL[i] = vp[i] ? a.mlprev[(qrow + hp) * 2 + 1] : 0.f;
+      const int h = 4 * kq + i;
+      v2[i] = two && h >= 2 * G && h < 3 * G;
+      vp[i] = v2[i] || (DEF && prev != 0 && h >= G && h < 2 * G);
+      const float* ml = v2[i] ? a.mlprev2 + (qrow + h - 2 * G) * 2 : a.mlprev + (qrow + (vp[i] ? h - G : 0)) * 2;
+      pM[i] = vp[i] ? ml[0] : 0.f;
+      piL[i] = vp[i] ? ml[1] : 0.f;
     }
     float* sp = DEF ? a.spart + (((int64_t)l * a.kv_heads + kvh) * a.batch + b) * a.lstride + j0 : nullptr;
     float mx[4];
@@ -431,12 +451,15 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const AttnArgs a, const Step
           }
         }
         if (DEF && prev != 0) {
-          // sum of the previous step's weights of row r over the group's heads:
+          // sum of the pending steps' weights of row r over the group's heads:
           // this lane's heads, then the four lanes that hold row r, in a fixed order
+          // (the earlier of two pending steps lacks the later one's new row,
+          // live index nprev - 1)
+          const bool row2 = j0 + r < nprev - 1;
           float e = 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (vp[i]) e += exp2f(acc[i] * a.qscale - pM[i]) * piL[i];
+            if (vp[i] && (row2 || !v2[i])) e += exp2f(acc[i] * a.qscale - pM[i]) * piL[i];
           e += __shfl_xor(e, 16);
           e += __shfl_xor(e, 32);
           if (kq == 0) es[r] = e;

@@ -99,17 +99,24 @@ struct tkv {
   int pending_tiles = 0;
   // Deferred Eq. 1 (bf16 grouped-query heads on the matrix cores, resident
   // staging): a step's weights are recomputed, from its queries and its
-  // heads' (M, 1/L), by the next step's attention launch, which streams the
-  // same K rows anyway, and folded into s by that step's merge pass; a
-  // score-only pass over K does it when s is needed first.  No logits are
-  // stored.
+  // heads' (M, 1/L), by a later step's attention launch, which streams the
+  // same K rows anyway, and folded into s by that step's merge pass.  With
+  // g <= 5 two steps' queries fit the logits tile's padded rows, so every
+  // other launch forms the last two steps' weights at once and writes one
+  // sum per row and kv head for both (pair).  A reassignment first runs a
+  // score-only pass over K for the pending steps and folds them into s; a
+  // score read folds them into a copy of s only, so that reads never change
+  // which steps are summed together.  No logits are stored.
   bool defer = false;
-  bool prev_pending = false;        // the last step's weights are not in s yet
-  std::vector<int32_t> prev_nlive;  // [B] live rows of that step
-  int qcur = 0;                        // qbuf[qcur], mlbuf[qcur]: that step's queries and (M, 1/L)
-  void* qbuf[2] = {nullptr, nullptr};  // [L][B][Hq][D] each
-  float* mlbuf[2] = {nullptr, nullptr};  // [L][B][Hq][2] each
+  bool pair = false;                // two pending steps per launch (3 g <= 16)
+  int pend = 0;                     // steps whose weights are not in s yet (0..2)
+  std::vector<int32_t> prev_nlive;  // [B] live rows of the last of them
+  int qcur = 0;  // qbuf[qcur], mlbuf[qcur]: the last completed step's queries and (M, 1/L); the one
+                 // before it at (qcur + 2) % 3; the running step's go to (qcur + 1) % 3
+  void* qbuf[3] = {nullptr, nullptr, nullptr};     // [L][B][Hq][D] each
+  float* mlbuf[3] = {nullptr, nullptr, nullptr};   // [L][B][Hq][2] each
   float* spart = nullptr;              // [L][Hkv][B][lstride]
+  float* s_view = nullptr;             // [B][nmax]: s with the pending steps folded in, for reads
   std::vector<int32_t> nlive;                 // [B] live rows
   std::vector<std::vector<int32_t>> free0;    // [B] free T0 slots (back = next to use); [1] when shared
   bool shared_hbm = false;                    // one T0 slot space and budget for the batch

@@ -69,15 +69,19 @@ struct AttnArgs {
   float* part_o;             // [layers][batch][q_heads][max_chunks][head_dim]
   float qscale;              // log2(e) / sqrt(head_dim)
   int32_t layer_begin, batch, q_heads, kv_heads, nmax, max_chunks, lstride;
-  // Deferred Eq. 1 (matrix-core path, resident staging): the previous step's
-  // weights are recomputed from its queries while this launch streams K.
-  //   prev_mode 0: none; 1: this step's launch, previous step's rows are live
-  //   indices < nlive - 1; 2: score only (flush), rows < nlive, no attention.
-  int32_t prev_mode;
-  const void* qprev;   // [layers][batch][q_heads][head_dim]: the previous step's q
-  void* qsave;         // [layers][batch][q_heads][head_dim]: this step's q, kept for the next
-  const float* mlprev; // [layers][batch][q_heads][2]: the previous step's (M, 1/L), log2 units
-  float* spart;        // [layers][kv_heads][batch][lstride]: sum over the group's heads of alpha
+  // Deferred Eq. 1 (matrix-core path, resident staging): the weights of the
+  // last one or two steps (prev_steps) are recomputed from their queries
+  // while this launch streams K.
+  //   prev_mode 0: none; 1: this step's launch, the last pending step's rows
+  //   are live indices < nlive - 1; 2: score only (flush), rows < nlive, no
+  //   attention.  With two steps, the earlier one has one row fewer.
+  int32_t prev_mode, prev_steps;
+  const void* qprev;    // [layers][batch][q_heads][head_dim]: the last pending step's q
+  const void* qprev2;   // the same for the step before it (prev_steps 2)
+  void* qsave;          // [layers][batch][q_heads][head_dim]: this step's q, kept for later
+  const float* mlprev;  // [layers][batch][q_heads][2]: the last pending step's (M, 1/L), log2 units
+  const float* mlprev2; // the same for the step before it (prev_steps 2)
+  float* spart;         // [layers][kv_heads][batch][lstride]: sum over the group's heads of alpha
   int32_t nlive[kMaxBatch];
 };
 

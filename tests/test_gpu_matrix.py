@@ -44,3 +44,18 @@ def test_most_query_heads():
     w = tkvsynth.CONFIGS["tiny"].replace(dtype="bf16", head_dim=64, kv_heads=32, q_heads=256, layers=1, batch=1,
                                          prefill=300, steps=9, delta=8, prompt=8, recent=16)
     run_parity(w, Inputs(w), w.steps)
+
+
+@pytest.mark.parametrize("group,delta", [(4, 5), (5, 7), (8, 5)])
+def test_deferred_pairs_odd_delta(group, delta):
+    """The matrix-core path over resident staging forms Eq. 1 of the last two
+    steps together every other launch when both fit the logits tile (g <= 5;
+    g = 8 one step per launch).  With an odd Delta the reassignments find one
+    pending step and two in turn, and the scores read at every step come from
+    a copy; scores, outputs and labels still follow the oracle (Method §2 and
+    §4)."""
+    w = tkvsynth.CONFIGS["tiny"].replace(dtype="bf16", head_dim=128, kv_heads=2, q_heads=2 * group, layers=3,
+                                         batch=2, prefill=400, steps=3 * delta + 2, delta=delta, prompt=16,
+                                         recent=24, hbm_ratio=0.4, evict_ratio=0.05)
+    outs, s, tiers, st, o, nr = run_parity(w, Inputs(w), w.steps, check_every=1)
+    assert nr == 3

@@ -1,10 +1,13 @@
 """The Eq. 1 update of a step is applied in stream order before the scores
-are next read or written ("Not All Thoughts Need HBM", gist.science summary,
-Method §2): whether it runs inside the next append's launch or is flushed by
-a score read, a score write or a reassignment, the scores are the same bits.
-For bf16 grouped-query heads over resident staging the next step's attention
-launch recomputes the step's weights (no logits are stored); a flush then
-runs a score-only pass over K, with the same bits again."""
+are next read or ranked ("Not All Thoughts Need HBM", gist.science summary,
+Method §2): whether it runs inside the next append's launch or is applied
+for a score read, the scores are the same bits.
+For bf16 grouped-query heads over resident staging a later step's attention
+launch recomputes the step's weights (no logits are stored), two steps at a
+time when both fit the logits tile (g <= 5); a score read then forms the
+pending steps in a score-only pass over K into a copy of the scores, which
+changes nothing later, and a reassignment folds them into the scores first
+(an odd Delta leaves one step pending there, an even one two)."""
 import numpy as np
 import pytest
 import torch
@@ -55,12 +58,16 @@ SHAPES = {
     # bf16 grouped-query heads: the next step's launch recomputes the weights
     # (or a score-only pass over K does, when the scores are read first)
     "14b": dict(layers=4, batch=2, prefill=300, steps=40, delta=16, prompt=20, recent=16),
+    # an odd Delta: reassignments find one pending step, then two, in turn
+    "14b-delta7": dict(layers=4, batch=2, prefill=300, steps=40, delta=7, prompt=20, recent=16),
+    # g = 8: one pending step per launch (two do not fit the tile)
+    "70b": dict(layers=3, batch=2, prefill=300, steps=40, delta=16, prompt=20, recent=16),
 }
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_fold_placement_does_not_change_scores(name):
-    w = tkvsynth.CONFIGS[name].replace(**SHAPES[name])
+    w = tkvsynth.CONFIGS[name.split("-")[0]].replace(**SHAPES[name])
     inp = Inputs(w)
     a, ta = _run(w, inp, read_every_step=False)
     b, tb = _run(w, inp, read_every_step=True)
@@ -69,10 +76,16 @@ def test_fold_placement_does_not_change_scores(name):
     assert np.array_equal(ta[:, :n], tb[:, :n])
 
 
-def test_write_scores_replaces_pending_update():
-    w = tkvsynth.CONFIGS["tiny"].replace(prefill=64, steps=20, delta=8)
+@pytest.mark.parametrize("name,write_at", [("tiny", 9), ("14b", 9), ("14b", 10)])
+def test_write_scores_replaces_pending_update(name, write_at):
+    """Written scores replace s with every pending update (one or two deferred
+    steps on the matrix-core path); later steps add to the written values."""
+    w = tkvsynth.CONFIGS[name].replace(prefill=64, steps=20, delta=8, prompt=min(tkvsynth.CONFIGS[name].prompt, 20),
+                                       recent=min(tkvsynth.CONFIGS[name].recent, 16))
+    if name == "14b":
+        w = w.replace(layers=3, batch=2)
     inp = Inputs(w)
-    _run(w, inp, read_every_step=False, write_at=9)
+    _run(w, inp, read_every_step=False, write_at=write_at)
 
 
 def test_scores_read_between_layer_groups():
