@@ -1,6 +1,6 @@
 """Full-size workloads on the GPU, checked against the oracle.
 
-The 14B, 32B, 32B with the 8-bit tier, and 70B workloads run at their real
+The 7B, 14B, 32B, 32B with the 8-bit tier, and 70B workloads run at their real
 shapes and cache sizes through one reassignment; the 70B one also in its
 defining mode, stream staging, where about two thirds of the rows live in
 pinned host memory and every step copies each layer's T1 rows to the GPU
@@ -103,6 +103,16 @@ def run_full(w, layers, seqs, sample_every, staging_layers=0, full_seq=None):
     assert worst <= 5e-3 and worst_full <= 5e-3
     assert s_rel <= 1e-4
     return st
+
+
+@pytest.mark.timeout(900)
+def test_7b_full_size():
+    """The 7B workload at its real shape (32 layers x 32 kv heads: each row's
+    deferred weight sums form a list of 1024 entries, folded with 16 partial
+    sums), its one sequence followed by the oracle in every layer."""
+    w = tkvsynth.CONFIGS["7b"].replace(steps=66)
+    st = run_full(w, layers=(0, 31), seqs=(0,), sample_every=16, full_seq=0)
+    assert st["reassigns"] == 1 and st["tier_count"][3] > 0
 
 
 @pytest.mark.timeout(900)
