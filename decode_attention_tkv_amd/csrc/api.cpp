@@ -227,13 +227,10 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   dev((void**)&t->loc, B * nmax * 4);
   dev((void**)&t->s, B * nmax * 4);
   t->vector_pass = (o.flags & TKV_FLAG_VECTOR_PASS) != 0 && s.dtype == TKV_BF16 && group >= 4;
-  // deferred Eq. 1 (bf16 over resident staging): the matrix-core path, and
-  // the vector path with one or two query heads per kv head
-  t->defer = resident && s.dtype == TKV_BF16 && ((group >= 4 && !t->vector_pass) || group <= 2);
+  // the matrix-core path over resident staging
+  t->defer = resident && s.dtype == TKV_BF16 && group >= 4 && !t->vector_pass;
   if (t->defer) {
-    // two pending steps per launch: on the matrix cores when both steps'
-    // queries fit beside this step's in the 16-row tile; always on the vector path
-    t->pair = group <= 2 || 3 * group <= 16;
+    t->pair = 3 * group <= 16;  // two steps' queries beside this step's in the 16-row tile
     for (int i = 0; i < 3; ++i) {
       dev(&t->qbuf[i], L * B * Hq * t->D * t->esz);
       dev((void**)&t->mlbuf[i], L * B * Hq * 2 * 4);
@@ -675,11 +672,7 @@ static int drain_events(tkv* t) {
   return TKV_OK;
 }
 
-// Deferred fold: partial sums per row, 16 when a row's list (layers x kv
-// heads) is longer than 640 entries, else 4.
-static int fold_parts(const tkv* t) { return t->L * t->Hkv > 640 ? 16 : 4; }
-
-// Deferred Eq. 1: the fold of the pending steps' per-group sums into s.
+// Deferred Eq. 1: the fold of the pending step's per-group sums into s.
 static ScoreArgs defer_fold_args(const tkv* t) {
   ScoreArgs sa{};
   sa.layer_score = t->spart;  // rows [layer][kv head], summed in that order
@@ -690,17 +683,15 @@ static ScoreArgs defer_fold_args(const tkv* t) {
   sa.batch = t->B;
   sa.nmax = t->nmax;
   sa.lstride = t->lstride;
-  sa.parts = fold_parts(t);
   for (int b = 0; b < t->B; ++b) sa.nlive[b] = t->prev_nlive[b];
   return sa;
 }
 
-// tiles of the deferred fold (256 / parts rows each)
+// tiles of 64 rows of the deferred fold
 static int prev_tiles(const tkv* t) {
   int m = 0;
   for (int b = 0; b < t->B; ++b) m = std::max(m, t->prev_nlive[b]);
-  const int rows = 256 / fold_parts(t);
-  return (m + rows - 1) / rows;
+  return (m + 63) / 64;
 }
 
 // Deferred Eq. 1: how many pending steps the running step's launches form
@@ -829,7 +820,7 @@ static int flush_deferred(tkv* t, hipStream_t st, bool commit) {
   }
   if (chunks > 0) {
     HIP_TRY(t, launch_attn(a, none, t->dtype, t->D, t->group, t->chunk, false, t->L, chunks, nullptr, nullptr, st));
-    HIP_TRY(t, launch_fold(fold, prev_tiles(t), st));
+    HIP_TRY(t, launch_fold64(fold, prev_tiles(t), st));
   }
   if (commit) t->pend = 0;
   return TKV_OK;

@@ -34,7 +34,7 @@
 //                 logits are stored; the next step's k_attn_chunk recomputes
 //                 the step's weights in the padded rows of its logits tile and
 //                 writes their sum over each group's heads, and its
-//                 k_finalize folds those sums into s (k_fold when a
+//                 k_finalize folds those sums into s (k_fold64 when a
 //                 score-only pass flushes a step).
 //                 No atomics anywhere, so every result is bitwise
 //                 reproducible.
@@ -79,12 +79,6 @@ __device__ __forceinline__ float group_max(float x) {
 }
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-// acc + x0 * y0 + x1 * y1 over two packed bf16 pairs (element 0 in the low half)
-__device__ __forceinline__ float dot2bf(uint32_t x, uint32_t y, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), acc, false);
-}
 
 // A result the merge pass or Eq. 1 reads later, written through to memory
 // (a relaxed store at system scope: global_store sc0 sc1) rather than held
@@ -199,43 +193,31 @@ __device__ __forceinline__ void score_rows(const ScoreArgs& a, int tile, int b) 
   a.s[p] += acc * a.inv_lh;
 }
 
-// Deferred Eq. 1 fold for live rows [R tile, R tile + R) of sequence b,
-// R = 256 / P: s[pos(j)] += (sum over the f.layers rows [layer][kv head] of
-// f.layer_score) * 1/(L*H).  P partial sums per row: partial k adds every
-// P-th entry of the row's list from k, in order, and the P partials are then
-// added in order.  The lists are long (layers x kv heads), so one thread per
-// row would wait on one long load chain; P = 4 (64 rows per block, each load
-// reading 256 contiguous bytes) up to 640 entries, 16 beyond that (16 rows
-// per block, 64 entries per thread).  Every thread of the block calls it.
-template <int P>
-__device__ __forceinline__ void fold_rows(const ScoreArgs& f, int tile, int b, float* red) {
-  constexpr int R = 256 / P;
-  const int r = threadIdx.x % R, k = threadIdx.x / R;
-  const int j = tile * R + r;
+// Deferred Eq. 1 fold for live rows [64 tile, 64 tile + 64) of sequence b:
+// s[pos(j)] += (sum over the f.layers rows [layer][kv head] of f.layer_score)
+// * 1/(L*H).  Wave k of the block adds every fourth row of that list from
+// row k, in order, for 64 consecutive live rows (256 contiguous bytes per
+// load); the four partials are added in order.  The sums are long (layers x
+// kv heads), so one thread per row would wait on one long load chain.
+// Every thread of the block calls it.
+__device__ __forceinline__ void fold_rows64(const ScoreArgs& f, int tile, int b, float (*red)[64]) {
+  const int r = threadIdx.x & 63, k = threadIdx.x >> 6;
+  const int j = tile * 64 + r;
   const bool live = j < f.nlive[b];
   float acc = 0.f;
   if (live) {
     const float* p = f.layer_score + (int64_t)b * f.lstride + j;
     const int64_t step = (int64_t)f.batch * f.lstride;
 #pragma unroll 16
-    for (int l = k; l < f.layers; l += P) acc += p[l * step];
+    for (int l = k; l < f.layers; l += 4) acc += p[l * step];
   }
-  red[k * R + r] = acc;
+  red[k][r] = acc;
   __syncthreads();
   if (k == 0 && live) {
-    float t = red[r];
-#pragma unroll
-    for (int q = 1; q < P; ++q) t += red[q * R + r];
+    const float t = ((red[0][r] + red[1][r]) + red[2][r]) + red[3][r];
     const int64_t pos = (int64_t)b * f.nmax + f.live_pos[(int64_t)b * f.nmax + j];
     f.s[pos] += t * f.inv_lh;
   }
-}
-
-__device__ __forceinline__ void fold_tile(const ScoreArgs& f, int tile, int b, float* red) {
-  if (f.parts == 16)
-    fold_rows<16>(f, tile, b, red);
-  else
-    fold_rows<4>(f, tile, b, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -295,21 +277,15 @@ __global__ __launch_bounds__(256) void k_append(const AppendArgs a, const ScoreA
 // group's heads (and both steps) and one value per row and kv head leaves the
 // block, in place of G logits per step.  The host asks for two steps every
 // other launch when they fit, and for none in between.  Chunk-0 blocks keep
-// this step's queries for later.  The bf16 vector path with G <= 2 does the
-// same with packed bf16 dot products (the pending steps' products are
-// per-lane, like this step's).  DEF 1 is a deferred launch with nothing
-// pending (no logits, no weight sums: the lean form); DEF 2 forms the pending
-// steps' weights (or, prev_mode 2, only those: the score-only pass).
+// this step's queries for later.
 //
 // At least four waves per SIMD: without that bound the compiler puts the
 // matrix-core accumulators in AGPRs and, at G = 5 with two pending steps,
 // needs 132 registers, one wave fewer; with it, the same code fits in VGPRs
 // alone (no spills).  The vector path's allocation is unchanged.
-template <typename T, int D, int G, int CHUNK, bool MK, bool QT, int DEF>
+template <typename T, int D, int G, int CHUNK, bool MK, bool QT, bool DEF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void k_attn_chunk(const AttnArgs a, const StepArgs n) {
-  constexpr bool DF = DEF != 0;  // deferred Eq. 1: no logits stored, this step's queries kept
-  constexpr bool PV = DEF == 2;  // this launch forms pending steps' weights (DEF 1: none pending)
   constexpr int LPR = D * (int)sizeof(T) / 16;  // lanes per row
   constexpr int EPL = 16 / (int)sizeof(T);      // elements per lane
   constexpr int RPI = 64 / LPR;                 // rows per wave load
@@ -318,17 +294,15 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   constexpr int ITERS = RPW / RPI;
   // loads in flight per lane per batch: 16 for one query head per kv head
   // (1.2% faster than 8 at the 7B shape, though it leaves 5 waves per SIMD
-  // instead of 8), fewer as the G query heads' accumulators take registers,
-  // and half as many with deferred Eq. 1 on the vector path, whose pending
-  // steps' products keep more registers (still 5 waves per SIMD at G = 1)
-  constexpr int UB = (PV && !MK) ? (G == 1 ? 8 : 4) : (G == 1) ? 16 : (G == 2) ? 8 : 4;
+  // instead of 8), fewer as the G query heads' accumulators take registers
+  constexpr int UB = (G == 1) ? 16 : (G == 2) ? 8 : 4;
   constexpr int U = ITERS < UB ? ITERS : UB;    // loads in flight per lane per batch
   static_assert(RPW % RPI == 0 && ITERS % U == 0, "chunk shape");
 
   // logits (log2 units), kept to the end unless Eq. 1 is deferred; then the
   // per-wave partial outputs reuse their space once p is formed (one more
   // work-group per CU at G = 8)
-  constexpr bool OSUM_IN_ZS = DF && NW * D <= CHUNK;
+  constexpr bool OSUM_IN_ZS = DEF && NW * D <= CHUNK;
   __shared__ float zs_store[G * CHUNK + (OSUM_IN_ZS ? 0 : NW * G * D)];
   float (*zs)[CHUNK] = reinterpret_cast<float (*)[CHUNK]>(zs_store);
   float (*osum)[G][D] = reinterpret_cast<float (*)[G][D]>(zs_store + (OSUM_IN_ZS ? 0 : G * CHUNK));
@@ -338,7 +312,7 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   // deferred Eq. 1: the previous step's weight sums of the chunk's rows, held
   // here until the block's last barrier is behind it (a global store ahead of
   // a barrier holds the wave there until the store is acknowledged)
-  __shared__ float es[PV ? CHUNK : 1];
+  __shared__ float es[DEF ? CHUNK : 1];
   // matrix-core p.V: P as three bf16 terms (hi, mid, lo), G heads x CHUNK rows
   __shared__ __attribute__((aligned(16))) bf16_t pt[MK ? 3 : 1][MK ? G : 1][MK ? CHUNK : 1];
 
@@ -389,9 +363,9 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
     // live indices below the new row's; 2, score only over every live row.
     // With two pending steps the earlier one had one row fewer (each step
     // appends one row per sequence and nothing leaves between reassignments).
-    const int prev = PV ? a.prev_mode : 0;
+    const int prev = DEF ? a.prev_mode : 0;
     const int nprev = prev == 1 ? nl - 1 : nl;
-    const bool two = PV && prev != 0 && a.prev_steps == 2;
+    const bool two = DEF && prev != 0 && a.prev_steps == 2;
     // ---- phase 1 on the matrix cores: Z[16 heads x 16 rows] += Q[16 x 32] K^T[32 x 16],
     // D/32 steps per tile of 16 rows (v_mfma_f32_16x16x32_bf16).  Lane l feeds
     // head / row (l % 16) and the 8 elements 8*(l/16) of each 32-wide slice;
@@ -406,14 +380,14 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
     const T* qsrc = nullptr;
     if (hl < G && prev != 2)
       qsrc = (const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + hl) * D;
-    else if (PV && prev != 0 && hl >= G && hl < 2 * G)
+    else if (DEF && prev != 0 && hl >= G && hl < 2 * G)
       qsrc = (const T*)a.qprev + (qrow + hl - G) * D;
     else if (two && hl >= 2 * G && hl < 3 * G)
       qsrc = (const T*)a.qprev2 + (qrow + hl - 2 * G) * D;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const uint4 u = qsrc ? load16(qsrc + 32 * kc + 8 * kq) : make_uint4(0, 0, 0, 0);
-      if (DF && prev != 2 && c == 0 && hl < G)
+      if (DEF && prev != 2 && c == 0 && hl < G)
         *reinterpret_cast<uint4*>((T*)a.qsave + (qrow + hl) * D + 32 * kc + 8 * kq) = u;
       qa[kc] = as_bf16x8(u);
     }
@@ -425,12 +399,12 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * kq + i;
       v2[i] = two && h >= 2 * G && h < 3 * G;
-      vp[i] = v2[i] || (PV && prev != 0 && h >= G && h < 2 * G);
+      vp[i] = v2[i] || (DEF && prev != 0 && h >= G && h < 2 * G);
       const float* ml = v2[i] ? a.mlprev2 + (qrow + h - 2 * G) * 2 : a.mlprev + (qrow + (vp[i] ? h - G : 0)) * 2;
       pM[i] = vp[i] ? ml[0] : 0.f;
       piL[i] = vp[i] ? ml[1] : 0.f;
     }
-    float* sp = PV ? a.spart + (((int64_t)l * a.kv_heads + kvh) * a.batch + b) * a.lstride + j0 : nullptr;
+    float* sp = DEF ? a.spart + (((int64_t)l * a.kv_heads + kvh) * a.batch + b) * a.lstride + j0 : nullptr;
     float mx[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) mx[i] = -INFINITY;
@@ -476,7 +450,7 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
             mx[i] = fmaxf(mx[i], z);
           }
         }
-        if (PV && prev != 0) {
+        if (DEF && prev != 0) {
           // sum of the pending steps' weights of row r over the group's heads:
           // this lane's heads, then the four lanes that hold row r, in a fixed order
           // (the earlier of two pending steps lacks the later one's new row,
@@ -506,39 +480,14 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
 #pragma unroll
     for (int g = 0; g < G; ++g) mc[g] = fmaxf(fmaxf(red[0][g], red[1][g]), fmaxf(red[2][g], red[3][g]));
   } else {
-    // deferred Eq. 1 on the vector path (bf16, G <= 2): the pending steps'
-    // queries stay packed as bf16 pairs (four registers per head and step) and
-    // are unpacked at each product; their heads' (M, 1/L) are the block's own
-    static_assert(!DF || (std::is_same<T, bf16_t>::value && G <= 2), "deferred vector path: bf16, G <= 2");
-    const int prev = PV ? a.prev_mode : 0;
-    const int nprev = prev == 1 ? nl - 1 : nl;
-    const bool two = PV && prev != 0 && a.prev_steps == 2;
-    const int64_t qrow = ((int64_t)l * a.batch + b) * a.q_heads + kvh * G;  // head 0 of the group, layer l
     float qv[G][EPL];
   #pragma unroll
     for (int g = 0; g < G; ++g) {
       const T* qp = (const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + g) * D + part * EPL;
-      const uint4 u = prev != 2 ? load16(qp) : make_uint4(0, 0, 0, 0);
-      if (DF && prev != 2 && c == 0 && wave == 0 && rg == 0)
-        *reinterpret_cast<uint4*>((T*)a.qsave + (qrow + g) * D + part * EPL) = u;
-      unpack<T>(u, qv[g]);
+      unpack<T>(load16(qp), qv[g]);
   #pragma unroll
       for (int e = 0; e < EPL; ++e) qv[g][e] *= a.qscale;
     }
-    constexpr int NP = PV ? 2 : 1;  // pending steps: [0] the last, [1] the one before it
-    uint4 qd[NP][G];
-    float dM[NP][G], diL[NP][G];
-  #pragma unroll
-    for (int sp2 = 0; sp2 < NP; ++sp2)
-  #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const bool on = PV && prev != 0 && (sp2 == 0 || two);
-        const T* src = (const T*)(sp2 == 0 ? a.qprev : a.qprev2);
-        const float* ml = sp2 == 0 ? a.mlprev : a.mlprev2;
-        qd[sp2][g] = on ? load16(src + (qrow + g) * D + part * EPL) : make_uint4(0, 0, 0, 0);
-        dM[sp2][g] = on ? ml[(qrow + g) * 2] : 0.f;
-        diL[sp2][g] = on ? ml[(qrow + g) * 2 + 1] : 0.f;
-      }
 
     // ---- phase 1: logits and the chunk max
     float mx[G];
@@ -567,52 +516,18 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
         const int r = wave * RPW + (it0 + u) * RPI + rg;
         float kf[EPL];
         unpack<T>(kd[u], kf);
-        if (prev != 2) {
   #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            float acc = 0.f;
+        for (int g = 0; g < G; ++g) {
+          float acc = 0.f;
   #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc = fmaf(qv[g][e], kf[e], acc);
-            const float z = group_sum<LPR>(acc);
-            if (r < nrows) {
-              if (part == 0) zs[g][r] = z;
-              mx[g] = fmaxf(mx[g], z);
-            }
-          }
-        }
-        if constexpr (PV) {
-          if (prev != 0) {
-            // the pending steps' weights of row r, summed over the heads of
-            // the last pending step, then of the one before it (which lacks
-            // the last one's new row, live index nprev - 1)
-            float e = 0.f;
-  #pragma unroll
-            for (int sp2 = 0; sp2 < NP; ++sp2) {
-              if (sp2 == 1 && !two) break;
-              const bool ok = j0 + r < (sp2 == 0 ? nprev : nprev - 1);
-  #pragma unroll
-              for (int g = 0; g < G; ++g) {
-                // packed bf16 pairs of q and K straight into the dot product
-                // (v_dot2c_f32_bf16: both products are exact in fp32)
-                float acc = 0.f;
-                acc = dot2bf(qd[sp2][g].x, kd[u].x, acc);
-                acc = dot2bf(qd[sp2][g].y, kd[u].y, acc);
-                acc = dot2bf(qd[sp2][g].z, kd[u].z, acc);
-                acc = dot2bf(qd[sp2][g].w, kd[u].w, acc);
-                const float z = group_sum<LPR>(acc) * a.qscale;
-                if (ok) e += exp2f(z - dM[sp2][g]) * diL[sp2][g];
-              }
-            }
-            if (part == 0 && r < nrows) es[r] = e;
+          for (int e = 0; e < EPL; ++e) acc = fmaf(qv[g][e], kf[e], acc);
+          const float z = group_sum<LPR>(acc);
+          if (r < nrows) {
+            if (part == 0) zs[g][r] = z;
+            mx[g] = fmaxf(mx[g], z);
           }
         }
       }
-    }
-    if (PV && prev == 2) {  // score only: the sums leave, and so does the whole block
-      float* sp = a.spart + (((int64_t)l * a.kv_heads + kvh) * a.batch + b) * a.lstride + j0;
-      __syncthreads();
-      for (int r = tid; r < nrows && j0 + r < nprev; r += 256) store_through(sp + r, es[r]);
-      return;
     }
   #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -794,7 +709,7 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
     const float v = (tid & 1) ? ((red[0][g] + red[1][g]) + red[2][g]) + red[3][g] : mc[g];
     store_through(a.part_ml + ((hbase + g) * a.max_chunks + c) * 2 + (tid & 1), v);
   }
-  if constexpr (PV) {
+  if constexpr (MK && DEF) {
     if (a.prev_mode != 0) {
       // the previous step's rows: live indices below the new row's (all of them in a score-only pass)
       const int nprev = a.prev_mode == 1 ? nl - 1 : nl;
@@ -804,7 +719,7 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   }
   // logits, padded with zeros to the line that holds the chunk's last row
   // (none when Eq. 1 is deferred)
-  const int nw = DF ? 0 : min(CHUNK, (nrows + 31) / 32 * 32);
+  const int nw = DEF ? 0 : min(CHUNK, (nrows + 31) / 32 * 32);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float* lg = a.logits + (hbase + g) * a.lstride + j0;
@@ -854,7 +769,7 @@ template <int D, int RPT>
 __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a, const ScoreArgs fold) {
   __shared__ float Ms[kMaxQHeads];
   __shared__ float iLs[kMaxQHeads];
-  __shared__ float fold_red[256];
+  __shared__ float fold_red[4][64];
   constexpr int TILE = 256 * RPT;
   const int tid = threadIdx.x;
   const int x = blockIdx.x, b = blockIdx.y, ll = blockIdx.z;
@@ -912,7 +827,7 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a, const Sc
       // fold tiles are dealt over the layer slices: ceil(fold_tiles / slices) per slice
       const int per = (a.fold_tiles + gridDim.z - 1) / gridDim.z;
       const int ft = ll * per + (x - tiles_grid - hblocks);
-      if (ft < a.fold_tiles) fold_tile(fold, ft, b, fold_red);
+      if (ft < a.fold_tiles) fold_rows64(fold, ft, b, fold_red);
       return;
     }
     const int h = (x - tiles_grid) * HPB + tid / TPH, ev = tid % TPH;
@@ -1005,9 +920,9 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a, const Sc
 __global__ __launch_bounds__(256) void k_score(const ScoreArgs a) { score_rows(a, blockIdx.x, blockIdx.y); }
 
 // Deferred Eq. 1 fold on its own: grid (tiles of 64 rows, batch).
-__global__ __launch_bounds__(256) void k_fold(const ScoreArgs a) {
-  __shared__ float red[256];
-  fold_tile(a, blockIdx.x, blockIdx.y, red);
+__global__ __launch_bounds__(256) void k_fold64(const ScoreArgs a) {
+  __shared__ float red[4][64];
+  fold_rows64(a, blockIdx.x, blockIdx.y, red);
 }
 
 // Grouped-query heads (G >= 4) of bf16 caches take the matrix-core logits.
@@ -1019,7 +934,7 @@ struct AttnLaunch {
   hipStream_t s;
 };
 
-template <typename T, int D, int G, bool QT, int DEF, bool MK>
+template <typename T, int D, int G, bool QT, bool DEF, bool MK>
 const void* attn_fn(int chunk) {
   switch (chunk) {
     case 128: return (const void*)&k_attn_chunk<T, D, G, 128, MK, QT, DEF>;
@@ -1029,30 +944,24 @@ const void* attn_fn(int chunk) {
   }
 }
 
-// a.spart set: deferred Eq. 1, which the matrix-core path and the bf16
-// vector path with one or two query heads per kv head have, without 8-bit
-// staging (the launcher checks this before it sets a.spart).  vec: bf16
+// a.spart set: deferred Eq. 1, which only the matrix-core path without 8-bit
+// staging has (the launcher checks this before it sets a.spart).  vec: bf16
 // grouped-query heads on the vector path instead of the matrix cores (not
 // with 8-bit staging).
 template <typename T, int D, int G, bool QT>
 hipError_t launch_attn_t(const AttnArgs& a, const StepArgs& n, int chunk, bool vec, const AttnLaunch& L) {
   constexpr bool MK = std::is_same<T, bf16_t>::value && G >= 4;
-  constexpr bool VDEF = std::is_same<T, bf16_t>::value && G <= 2 && !QT;  // deferred vector path
   const void* fn = nullptr;
   if constexpr (MK && !QT) {
     if (vec) {
       if (a.spart) return hipErrorInvalidValue;
-      fn = attn_fn<T, D, G, QT, 0, false>(chunk);
+      fn = attn_fn<T, D, G, QT, false, false>(chunk);
     } else {
-      fn = !a.spart ? attn_fn<T, D, G, QT, 0, true>(chunk)
-           : a.prev_mode ? attn_fn<T, D, G, QT, 2, true>(chunk) : attn_fn<T, D, G, QT, 1, true>(chunk);
+      fn = a.spart ? attn_fn<T, D, G, QT, true, true>(chunk) : attn_fn<T, D, G, QT, false, true>(chunk);
     }
-  } else if constexpr (VDEF) {
-    fn = !a.spart ? attn_fn<T, D, G, QT, 0, false>(chunk)
-         : a.prev_mode ? attn_fn<T, D, G, QT, 2, false>(chunk) : attn_fn<T, D, G, QT, 1, false>(chunk);
   } else {
     if (a.spart || (vec && MK)) return hipErrorInvalidValue;
-    fn = attn_fn<T, D, G, QT, 0, MK>(chunk);
+    fn = attn_fn<T, D, G, QT, false, MK>(chunk);
   }
   if (!fn) return hipErrorInvalidValue;
   AttnArgs ac = a;
@@ -1140,9 +1049,8 @@ hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fold(const ScoreArgs& a, int tiles, hipStream_t s) {
-  if (a.parts != 4 && a.parts != 16) return hipErrorInvalidValue;
-  k_fold<<<dim3(tiles, a.batch), 256, 0, s>>>(a);
+hipError_t launch_fold64(const ScoreArgs& a, int tiles64, hipStream_t s) {
+  k_fold64<<<dim3(tiles64, a.batch), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -104,7 +104,6 @@ struct ScoreArgs {
   float* s;                  // [batch][nmax] by position
   float inv_lh;              // 1 / (layers * q_heads)
   int32_t layers, batch, nmax, lstride;
-  int32_t parts;             // deferred fold: partial sums per row (4, or 16 for lists over 640 rows)
   int32_t nlive[kMaxBatch];
 };
 
@@ -313,8 +312,7 @@ hipError_t launch_finalize(const FinalizeArgs& a, const ScoreArgs* fold, int fol
                            int layer_count, int max_live, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s);
 // deferred Eq. 1 fold (a.layers rows [layer][kv head]), tiles of 64 live rows
-// Deferred fold of a.layer_score into s: tiles of 256 / a.parts live rows.
-hipError_t launch_fold(const ScoreArgs& a, int tiles, hipStream_t s);
+hipError_t launch_fold64(const ScoreArgs& a, int tiles64, hipStream_t s);
 
 // ---- launchers (move.hip) -------------------------------------------------
 hipError_t launch_place_rows(const PlaceArgs& a, int layers, hipStream_t s);

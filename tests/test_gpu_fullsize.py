@@ -107,9 +107,9 @@ def run_full(w, layers, seqs, sample_every, staging_layers=0, full_seq=None):
 
 @pytest.mark.timeout(900)
 def test_7b_full_size():
-    """The 7B workload at its real shape (32 layers x 32 kv heads: each row's
-    deferred weight sums form a list of 1024 entries, folded with 16 partial
-    sums), its one sequence followed by the oracle in every layer."""
+    """The 7B workload at its real shape (32 layers, 32 kv heads, one query
+    head each, logits summed over 32 heads per layer), its one sequence
+    followed by the oracle in every layer."""
     w = tkvsynth.CONFIGS["7b"].replace(steps=66)
     st = run_full(w, layers=(0, 31), seqs=(0,), sample_every=16, full_seq=0)
     assert st["reassigns"] == 1 and st["tier_count"][3] > 0
