@@ -111,3 +111,20 @@ def test_random_scored_prefill(i):
         w = w.replace(prefill=40 + 7 * i, prompt=min(w.prompt, 20))
     print("[scored %d] %s staging %d chunk %d" % (i, w, staging, chunk), flush=True)
     run_scored(w, w.steps, check_every=3, staging_layers=staging, chunk=chunk)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_odd_delta(i):
+    """Draws with an odd Delta (5, 7, 9 or 11), so that on the paths that
+    defer Eq. 1 two steps at a time (bf16, 4 or 5 query heads per kv head,
+    resident staging) the reassignments find one pending step and then two in
+    turn; every other path runs them as usual (Method §4)."""
+    w, staging, chunk, calls, groups, static = _draw(200 + i)
+    r = np.random.default_rng(7000 + i)
+    delta = int(r.choice([5, 7, 9, 11]))
+    w = w.replace(delta=delta, steps=int(r.integers(3, 5)) * delta + int(r.integers(0, delta)))
+    print("[odd-delta %d] %s staging %d chunk %d calls %s %s static %s" % (i, w, staging, chunk, calls, groups,
+                                                                         static), flush=True)
+    outs, s, tiers, st, o, n_reassign = run_parity(w, Inputs(w), w.steps, check_every=2, staging_layers=staging,
+                                                   chunk=chunk, calls=calls, groups=groups, static=static)
+    assert n_reassign == w.steps // w.delta
