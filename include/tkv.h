@@ -226,15 +226,18 @@ int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream);
  * out: device fp32 [layer_count][batch][q_heads][head_dim].  Layer groups of
  * one step must be called in order and cover every layer once.  The step's
  * Eq. 1 increment of the scores (Method §2) is applied in stream order before
- * anything that reads or writes them: it runs inside the next tkv_append's
- * launch, or first thing in tkv_reassign, tkv_read_scores or tkv_write_scores
- * on the stream given to that call.  bf16 caches with 4 or more query heads
- * per kv head and resident staging (staging_layers 0 or layers) defer it
- * further: the next step's attention launch recomputes the step's weights
- * from its queries while it streams the same K rows, and the next step's last
- * layer group adds them; a score read or write, or tkv_reassign, first runs a
- * score-only pass over K (half a step's reads) when a step is still pending.
- * The scores are the same either way (tested bit for bit). */
+ * anything that reads them: it runs inside the next tkv_append's launch, or
+ * first thing in tkv_reassign or tkv_read_scores on the stream given to that
+ * call.  bf16 caches with 4 or more query heads per kv head and resident
+ * staging (staging_layers 0 or layers) defer it further: a later step's
+ * attention launch recomputes the step's weights from its queries while it
+ * streams the same K rows, and that step's last layer group adds them; with 4
+ * or 5 query heads per kv head every other launch does so for the last two
+ * steps at once.  tkv_reassign first runs a score-only pass over K (half a
+ * step's reads) for the steps still pending and adds them; tkv_read_scores
+ * does the same into a copy that it returns, leaving them pending, so reads
+ * never change the scores' bits.  tkv_write_scores replaces the scores and
+ * drops every pending increment. */
 int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_count, const void* q, float* out,
                     tkv_stream_t stream);
 
@@ -282,7 +285,10 @@ int tkv_reassign_static(tkv_t* t, tkv_stream_t stream);
 int tkv_stats(tkv_t* t, tkv_stats_t* out);
 
 /* Test and inspection hooks (synchronise `stream`).  Arrays are host
- * [batch][max_tokens]; entries at positions >= n_tokens are unspecified. */
+ * [batch][max_tokens]; entries at positions >= n_tokens are unspecified.
+ * tkv_read_scores returns the scores with every completed step's Eq. 1
+ * increment in them; tkv_write_scores replaces them (pending increments are
+ * dropped). */
 int tkv_read_scores(tkv_t* t, float* scores, tkv_stream_t stream);
 int tkv_write_scores(tkv_t* t, const float* scores, tkv_stream_t stream);
 int tkv_read_tiers(tkv_t* t, uint8_t* tiers, tkv_stream_t stream);
