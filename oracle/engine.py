@@ -204,3 +204,94 @@ class OracleTKV:
             self.tier[b, :n] = new
             new_all[b] = new
         return new_all, deltas
+
+
+def layer_groups(layer_hbm):
+    """Consecutive layers with the same HBM ratio, as [(first layer, end, ratio)]."""
+    out = []
+    for l, h in enumerate(layer_hbm):
+        if out and out[-1][2] == h:
+            out[-1] = (out[-1][0], l + 1, h)
+        else:
+            out.append((l, l + 1, h))
+    return out
+
+
+class OracleLayerGroups:
+    """Per-layer HBM budgets (the budget variant in the spirit of ARKV's
+    per-layer ratios, gist.science ARKV summary, Method; tiers and Eq. 1 from
+    "Not All Thoughts Need HBM", Method §1, §2 and §4).  Reading: layer l
+    keeps floor(h_l N) rows in HBM.  Consecutive layers with one ratio form a
+    group, and each group places its rows by the rules of Method §1 with its
+    own ratio.  Every group ranks by the one Eq. 1 score, which averages over
+    all layers, and shares the eviction and T2 ratios.  So every group evicts
+    the same rows, and a group's T0 holds the protected rows and its best
+    candidates.  Each group is an OracleTKV over its layers.  They hold one
+    score array, to which each step adds the all-layer increment once."""
+
+    def __init__(self, layer_hbm, q_heads, kv_heads, head_dim, batch, max_tokens, delta, evict_ratio, t2_ratio,
+                 prompt, sinks, recent, bf16, t2_fp8=False, t2_head_scales=False):
+        self.groups = layer_groups(list(layer_hbm))
+        self.L, self.B, self.Hq = len(layer_hbm), batch, q_heads
+        self.parts = [OracleTKV(l1 - l0, q_heads, kv_heads, head_dim, batch, max_tokens, delta, h, evict_ratio,
+                                t2_ratio, prompt, sinks, recent, bf16, t2_fp8=t2_fp8, t2_head_scales=t2_head_scales)
+                      for (l0, l1, h) in self.groups]
+        self.s = self.parts[0].s
+        for p in self.parts:
+            p.s = self.s  # one score array for every group
+
+    @classmethod
+    def for_workload(cls, w, layer_hbm, max_tokens=None):
+        assert len(layer_hbm) == w.layers
+        return cls(layer_hbm, w.q_heads, w.kv_heads, w.head_dim, w.batch, max_tokens or w.n_final, w.delta,
+                   w.evict_ratio, w.t2_ratio, w.prompt, w.sinks, w.recent, w.dtype == "bf16", w.t2_fp8,
+                   w.t2_head_scales)
+
+    @property
+    def n(self):
+        return self.parts[0].n
+
+    def part_of(self, layer):
+        """(group index, layer within the group) of a layer."""
+        for g, (l0, l1, _) in enumerate(self.groups):
+            if l0 <= layer < l1:
+                return g, layer - l0
+        raise IndexError(layer)
+
+    def tier_of(self, layer):
+        return self.parts[self.part_of(layer)[0]].tier
+
+    def live(self):
+        return self.parts[0].live()
+
+    def prefill(self, K, V):
+        """K, V: float32 values [L][B][n0][Hkv][d]."""
+        for (l0, l1, _), p in zip(self.groups, self.parts):
+            p.prefill(K[l0:l1], V[l0:l1])
+
+    def append(self, k, v):
+        for (l0, l1, _), p in zip(self.groups, self.parts):
+            p.append(k[l0:l1], v[l0:l1])
+
+    def attend(self, q):
+        """q: [L][B][Hq][d] values.  Returns out [L][B][Hq][d] and adds the
+        step's Eq. 1 increment over all L layers to the shared scores."""
+        live = self.live()
+        outs, inc = [], 0.0
+        for (l0, l1, _), p in zip(self.groups, self.parts):
+            assert np.array_equal(p.live(), live), "groups disagree on the evicted rows"
+            outs.append(p.attend(q[l0:l1], update_scores=False))
+            # (1/L_g) sum over the group's layers, weighted L_g / L: (1/L) sum over all layers
+            inc = inc + eq1_increment(p.last_alpha[..., : self.n]) * ((l1 - l0) / self.L)
+        self.s[:, : self.n] += np.where(live[:, : self.n], inc, 0.0)
+        for p in self.parts:
+            p.step += 1
+        return np.concatenate(outs, axis=0)
+
+    def reassign(self, rank_scores=None, adopt=None):
+        """Every group re-placed by the shared scores with its own ratio.
+        adopt: optional per-group tiers [G][B][n].  Returns [(tiers, deltas)]
+        per group."""
+        scores = self.s[:, : self.n] if rank_scores is None else rank_scores
+        return [p.reassign(rank_scores=scores, adopt=None if adopt is None else adopt[g])
+                for g, p in enumerate(self.parts)]
