@@ -53,7 +53,8 @@ class tkv_protect(ctypes.Structure):
 
 class tkv_options(ctypes.Structure):
     _fields_ = [("t2_ratio", ctypes.c_double), ("staging_layers", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("flags", ctypes.c_uint64), ("mem_cap_bytes", ctypes.c_int64)]
+                ("chunk", ctypes.c_int32), ("flags", ctypes.c_uint64), ("mem_cap_bytes", ctypes.c_int64),
+                ("layer_hbm", ctypes.POINTER(ctypes.c_double))]
 
 
 class tkv_delta(ctypes.Structure):
@@ -94,6 +95,7 @@ _SIGS = {
     "tkv_read_scores": [_vp, _vp, _vp],
     "tkv_write_scores": [_vp, _vp, _vp],
     "tkv_read_tiers": [_vp, _vp, _vp],
+    "tkv_read_layer_tiers": [_vp, _i32, _vp, _vp],
     "tkv_read_deltas": [_vp, _vp, _vp, _vp],
     "tkv_read_kv": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
     "tkv_read_t2": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
@@ -146,9 +148,15 @@ def _dev_ptr(x: torch.Tensor, shape, dtype, name):
 
 def tkv_create(layers, q_heads, kv_heads, head_dim, batch, max_tokens, dtype, delta, hbm_ratio,
                evict_ratio, prompt, sinks, recent, t2_ratio=0.0, staging_layers=0, chunk=0, flags=0,
-               mem_cap_bytes=0):
+               mem_cap_bytes=0, layer_hbm=None):
     shape = tkv_shape(layers, q_heads, kv_heads, head_dim, batch, max_tokens, dtype)
-    opts = tkv_options(t2_ratio, staging_layers, chunk, flags, mem_cap_bytes)
+    lh = None
+    if layer_hbm is not None:
+        if len(layer_hbm) != layers:
+            raise ValueError("layer_hbm has %d ratios for %d layers" % (len(layer_hbm), layers))
+        lh = (ctypes.c_double * len(layer_hbm))(*[float(x) for x in layer_hbm])
+    opts = tkv_options(t2_ratio, staging_layers, chunk, flags, mem_cap_bytes,
+                       ctypes.cast(lh, ctypes.POINTER(ctypes.c_double)) if lh is not None else None)
     h = _vp()
     rc = lib().tkv_create(ctypes.byref(shape), delta, hbm_ratio, evict_ratio,
                           tkv_protect(prompt, sinks, recent), ctypes.byref(opts), ctypes.byref(h))
@@ -213,6 +221,12 @@ def tkv_read_tiers(h, batch, max_tokens, stream=None) -> np.ndarray:
     return out
 
 
+def tkv_read_layer_tiers(h, layer, batch, max_tokens, stream=None) -> np.ndarray:
+    out = np.empty((batch, max_tokens), np.uint8)
+    _check(lib().tkv_read_layer_tiers(h, layer, out.ctypes.data, _stream(stream)), h)
+    return out
+
+
 def tkv_read_deltas(h, batch, max_tokens):
     promote = np.zeros((batch, max_tokens), DELTA_DTYPE)
     demote = np.zeros((batch, max_tokens), DELTA_DTYPE)
@@ -246,7 +260,7 @@ class TieredKV:
     def __init__(self, layers, q_heads, kv_heads, head_dim, batch, max_tokens, dtype="bf16", delta=64,
                  hbm_ratio=0.5, evict_ratio=0.03, prompt=0, sinks=4, recent=128, t2_ratio=0.0,
                  staging_layers=0, chunk=0, time_kernels=False, no_t1=False, t2_fp8=False, shared_hbm=False,
-                 t2_head_scales=False, extra_flags=0, mem_cap_bytes=0):
+                 t2_head_scales=False, extra_flags=0, mem_cap_bytes=0, layer_hbm=None):
         self.L, self.Hq, self.Hkv, self.D, self.B, self.nmax = layers, q_heads, kv_heads, head_dim, batch, max_tokens
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -255,7 +269,8 @@ class TieredKV:
                             prompt, sinks, recent, t2_ratio, staging_layers, chunk,
                             (TKV_FLAG_TIME_KERNELS if time_kernels else 0) | (TKV_FLAG_NO_T1 if no_t1 else 0)
                             | (TKV_FLAG_T2_FP8 if t2_fp8 else 0) | (TKV_FLAG_SHARED_HBM if shared_hbm else 0)
-                            | (TKV_FLAG_T2_HEAD_SCALES if t2_head_scales else 0) | extra_flags, mem_cap_bytes)
+                            | (TKV_FLAG_T2_HEAD_SCALES if t2_head_scales else 0) | extra_flags, mem_cap_bytes,
+                            layer_hbm)
         self.n_scales = kv_heads if t2_head_scales else 1
 
     @classmethod
@@ -321,6 +336,9 @@ class TieredKV:
 
     def read_tiers(self, stream=None):
         return tkv_read_tiers(self.h, self.B, self.nmax, stream)
+
+    def read_layer_tiers(self, layer, stream=None):
+        return tkv_read_layer_tiers(self.h, layer, self.B, self.nmax, stream)
 
     def read_deltas(self):
         return tkv_read_deltas(self.h, self.B, self.nmax)

@@ -65,6 +65,11 @@ static int host_alloc(tkv* t, void** p, size_t bytes) {
 }
 
 static void release(tkv* t) {
+  for (tkv* p : t->parts) {
+    release(p);
+    delete p;
+  }
+  t->parts.clear();
   if (t->side) (void)hipStreamSynchronize(t->side);
   if (t->side_v) (void)hipStreamSynchronize(t->side_v);
   if (t->wb) (void)hipStreamSynchronize(t->wb);
@@ -107,17 +112,63 @@ static int arena_settled(tkv* t) {
   return TKV_OK;
 }
 
-// A handle whose last reassignment failed part way is unusable.
+// A handle whose last reassignment failed part way is unusable (with
+// per-layer budgets: any of its parts).
 static int usable(tkv* t) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  for (const tkv* p : t->parts) t->failed = t->failed || p->failed;
   if (t->failed) return tkv_fail(t, TKV_ESTATE, "handle unusable: an earlier reassignment failed part way");
   return TKV_OK;
 }
 
+// The result of a call on part i of a handle with per-layer budgets: its
+// error message, and whether it left the part unusable, pass to the handle.
+static int part_rc(tkv* t, size_t i, int rc) {
+  if (rc != TKV_OK) {
+    t->err = t->parts[i]->err;
+    t->failed = t->failed || t->parts[i]->failed;
+  }
+  return rc;
+}
+
+// The part of a handle with per-layer budgets that holds `layer`.
+static size_t part_of(const tkv* t, int layer) {
+  size_t i = 0;
+  while (i + 1 < t->parts.size() && t->part_l0[i + 1] <= layer) ++i;
+  return i;
+}
+
+// The step state of a handle with per-layer budgets, from its parts: a step
+// is in progress while any part has layers left.
+static void mirror_parts(tkv* t) {
+  const tkv* p0 = t->parts[0];
+  t->n = p0->n;
+  t->step = p0->step;
+  t->state = p0->state;
+  for (const tkv* p : t->parts)
+    if (p->state == TkvState::InStep) t->state = TkvState::InStep;
+}
+
+// A layer's slice of a [layers][...] device array whose layers are
+// `layer_bytes` apart.
+static const void* layer_slice(const void* base, int layer, size_t layer_bytes) {
+  return (const char*)base + (size_t)layer * layer_bytes;
+}
+
 extern "C" const char* tkv_last_error(const tkv_t* t) { return t ? t->err.c_str() : g_create_err.c_str(); }
 
+// A part of a handle with per-layer budgets: the handle's score array and
+// the layer count Eq. 1 averages over.
+struct PartOf {
+  float* s;
+  int score_layers;
+};
+
+static int create_groups(const tkv_shape& s, int32_t delta, double evict_ratio, tkv_protect protect,
+                         const tkv_options& o, tkv_t** out);
+
 static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, double evict_ratio,
-                          tkv_protect protect, const tkv_options* opts, tkv_t** out) {
+                          tkv_protect protect, const tkv_options* opts, tkv_t** out, const PartOf* part = nullptr) {
   if (!out) return tkv_fail(nullptr, TKV_EINVAL, "out is NULL");
   *out = nullptr;
   if (!shape) return tkv_fail(nullptr, TKV_EINVAL, "shape is NULL");
@@ -155,6 +206,19 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
     return tkv_fail(nullptr, TKV_EINVAL, "TKV_FLAG_VECTOR_PASS does not combine with an 8-bit tier in stream staging");
   if ((o.flags & TKV_FLAG_SHARED_HBM) && s.max_tokens >= (1 << 26))
     return tkv_fail(nullptr, TKV_EINVAL, "TKV_FLAG_SHARED_HBM needs max_tokens < 2^26 (joint ranking keys)");
+  if (o.layer_hbm) {
+    // per-layer budgets: groups of consecutive layers with one ratio
+    int groups = 1;
+    for (int l = 0; l < s.layers; ++l) {
+      if (!ratio_ok(o.layer_hbm[l])) return tkv_fail(nullptr, TKV_EINVAL, "layer_hbm[%d] must be in [0, 1]", l);
+      if (l > 0 && o.layer_hbm[l] != o.layer_hbm[l - 1]) ++groups;
+    }
+    if (o.flags & (TKV_FLAG_NO_T1 | TKV_FLAG_SHARED_HBM))
+      return tkv_fail(nullptr, TKV_EINVAL, "layer_hbm does not combine with TKV_FLAG_NO_T1 or TKV_FLAG_SHARED_HBM");
+    if (groups > 1) return create_groups(s, delta, evict_ratio, protect, o, out);
+    hbm_ratio = o.layer_hbm[0];  // one ratio: a plain handle
+    o.layer_hbm = nullptr;
+  }
   const bool resident = o.staging_layers == 0 || o.staging_layers >= s.layers;
 
   tkv* t = new tkv();
@@ -225,12 +289,21 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   dev((void**)&t->live_pos, B * nmax * 4);
   dev((void**)&t->tier, B * nmax);
   dev((void**)&t->loc, B * nmax * 4);
-  dev((void**)&t->s, B * nmax * 4);
+  if (part) {
+    t->s = part->s;  // the handle of the parts holds the scores
+    t->s_shared = true;
+    t->score_layers = part->score_layers;
+  } else {
+    dev((void**)&t->s, B * nmax * 4);
+  }
   t->vector_pass = (o.flags & TKV_FLAG_VECTOR_PASS) != 0 && s.dtype == TKV_BF16 && group >= 4;
   // the matrix-core path over resident staging
   t->defer = resident && s.dtype == TKV_BF16 && group >= 4 && !t->vector_pass;
   if (t->defer) {
-    t->pair = 3 * group <= 16;  // two steps' queries beside this step's in the 16-row tile
+    // two steps' queries beside this step's in the 16-row tile; a part of a
+    // handle with per-layer budgets takes one step per launch, so that reads
+    // may apply its pending step without changing the scores' bits
+    t->pair = 3 * group <= 16 && !part;
     for (int i = 0; i < 3; ++i) {
       dev(&t->qbuf[i], L * B * Hq * t->D * t->esz);
       dev((void**)&t->mlbuf[i], L * B * Hq * 2 * 4);
@@ -312,7 +385,7 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
     if (e == hipSuccess) e = hipMemset(t->tier, kUnused, B * nmax);
     if (e == hipSuccess) e = hipMemset(t->tier_alt, kUnused, B * nmax);  // the two swap at each reassignment
     if (e == hipSuccess) e = hipMemset(t->loc, 0xFF, B * nmax * 4);
-    if (e == hipSuccess) e = hipMemset(t->s, 0, B * nmax * 4);
+    if (e == hipSuccess && !t->s_shared) e = hipMemset(t->s, 0, B * nmax * 4);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) rc = tkv_fail(t, TKV_EHIP, "initialising device state: %s", hipGetErrorString(e));
   }
@@ -358,6 +431,95 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   *out = t;
   return TKV_OK;
 }
+// Per-layer budgets: the handle the caller holds keeps the shape, the scores
+// and the step state; each group of consecutive layers with one ratio is a
+// part, a whole handle over its layers that shares those scores.  With stream
+// staging each part streams its own layers, so each needs more layers than
+// staging slots.  The memory cap is split over the parts by layer count.
+static int create_groups(const tkv_shape& s, int32_t delta, double evict_ratio, tkv_protect protect,
+                         const tkv_options& o, tkv_t** out) {
+  std::vector<std::pair<int, int>> groups;  // [first layer, end)
+  for (int l = 0; l < s.layers; ++l) {
+    if (l > 0 && o.layer_hbm[l] == o.layer_hbm[l - 1])
+      groups.back().second = l + 1;
+    else
+      groups.emplace_back(l, l + 1);
+  }
+  const bool stream = o.staging_layers >= 2 && o.staging_layers < s.layers;
+  for (const auto& g : groups)
+    if (stream && g.second - g.first <= o.staging_layers)
+      return tkv_fail(nullptr, TKV_EINVAL,
+                      "layer_hbm with stream staging: layer group [%d, %d) has no more layers than staging_layers %d",
+                      g.first, g.second, o.staging_layers);
+  tkv* t = new tkv();
+  struct Owner {
+    tkv* t;
+    ~Owner() {
+      if (t) {
+        release(t);
+        delete t;
+      }
+    }
+  } owner{t};
+  t->L = s.layers;
+  t->Hq = s.q_heads;
+  t->Hkv = s.kv_heads;
+  t->D = s.head_dim;
+  t->B = s.batch;
+  t->nmax = s.max_tokens;
+  t->dtype = s.dtype;
+  t->esz = s.dtype == TKV_BF16 ? 2 : 4;
+  t->group = s.q_heads / s.kv_heads;
+  t->delta = delta;
+  t->resident = !stream;
+  t->evict = evict_ratio;
+  t->t2 = o.t2_ratio;
+  t->prompt = protect.prompt;
+  t->sinks = protect.sinks;
+  t->recent = protect.recent;
+  t->flags = o.flags;
+  t->mem_cap = o.mem_cap_bytes;
+  t->row_elems = (int64_t)s.kv_heads * s.head_dim;
+  t->row_bytes = t->row_elems * t->esz;
+  {
+    const hipError_t e = hipGetDevice(&t->device);
+    if (e != hipSuccess) return tkv_fail(nullptr, TKV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  }
+  const size_t sbytes = (size_t)s.batch * s.max_tokens * 4;
+  int rc = device_alloc(t, (void**)&t->s, sbytes);
+  if (rc == TKV_OK) {
+    hipError_t e = hipMemset(t->s, 0, sbytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) rc = tkv_fail(t, TKV_EHIP, "initialising the scores: %s", hipGetErrorString(e));
+  }
+  if (rc != TKV_OK) {
+    g_create_err = t->err;
+    return rc;
+  }
+  const PartOf pof{t->s, s.layers};
+  for (const auto& g : groups) {
+    tkv_shape ps = s;
+    ps.layers = g.second - g.first;
+    tkv_options po = o;
+    po.layer_hbm = nullptr;
+    if (o.mem_cap_bytes > 0) po.mem_cap_bytes = std::max<int64_t>(1, o.mem_cap_bytes / s.layers * ps.layers);
+    tkv* part = nullptr;
+    rc = create_impl(&ps, delta, o.layer_hbm[g.first], evict_ratio, protect, &po, &part, &pof);
+    if (rc != TKV_OK) return rc;  // g_create_err holds the part's message
+    t->parts.push_back(part);
+    t->part_l0.push_back(g.first);
+  }
+  t->st.hbm_bytes = t->st.host_bytes = t->st.full_cache_bytes = 0;
+  for (const tkv* p : t->parts) {
+    t->st.hbm_bytes += p->st.hbm_bytes;
+    t->st.host_bytes += p->st.host_bytes;
+    t->st.full_cache_bytes += p->st.full_cache_bytes;
+  }
+  owner.t = nullptr;
+  *out = t;
+  return TKV_OK;
+}
+
 extern "C" int tkv_create(const tkv_shape* shape, int32_t delta, double hbm_ratio, double evict_ratio,
                           tkv_protect protect, const tkv_options* opts, tkv_t** out) {
   return guarded(nullptr, [&] { return create_impl(shape, delta, hbm_ratio, evict_ratio, protect, opts, out); });
@@ -381,6 +543,17 @@ static int prefill_impl(tkv_t* t, const void* k, const void* v, int32_t n_tokens
   if (misaligned(k) || misaligned(v)) return tkv_fail(t, TKV_EINVAL, "k/v not 16-byte aligned");
   if (n_tokens < 1) return tkv_fail(t, TKV_EINVAL, "n_tokens must be >= 1");
   if (n_tokens > t->nmax) return tkv_fail(t, TKV_ECAPACITY, "n_tokens %d > max_tokens %d", n_tokens, t->nmax);
+  if (!t->parts.empty()) {
+    // per-layer budgets: each part places its layers' rows by its own ratio
+    const size_t lb = (size_t)t->B * n_tokens * t->row_bytes;  // one layer of k: [batch][n_tokens][kv_heads][head_dim]
+    for (size_t i = 0; i < t->parts.size(); ++i) {
+      const int l0 = t->part_l0[i];
+      const int rc = prefill_impl(t->parts[i], layer_slice(k, l0, lb), layer_slice(v, l0, lb), n_tokens, stream);
+      if (part_rc(t, i, rc)) return rc;
+    }
+    mirror_parts(t);
+    return TKV_OK;
+  }
   hipStream_t st = (hipStream_t)stream;
   const int n0 = n_tokens;
 
@@ -551,7 +724,7 @@ static int prefill_scored_impl(tkv_t* t, const void* k, const void* v, const voi
   a.q = q;
   a.s = t->s;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)t->D));
-  a.inv_lh = (float)(1.0 / ((double)t->L * t->Hq));
+  a.inv_lh = (float)t->inv_lh();
   a.layers = t->L;
   a.batch = t->B;
   a.q_heads = t->Hq;
@@ -615,6 +788,24 @@ static void append_commit(tkv* t, const int32_t* slot) {
 }
 
 static int append_impl(tkv_t* t, const void* k, const void* v, tkv_stream_t stream) {
+  if (t && !t->parts.empty()) {
+    // per-layer budgets: every part must take the row before any does
+    if (int rc = usable(t)) return rc;
+    for (size_t i = 0; i < t->parts.size(); ++i)
+      if (int rc = part_rc(t, i, append_check(t->parts[i], k, v))) return rc;
+    const size_t lb = (size_t)t->B * t->row_bytes;  // one layer of k: [batch][kv_heads][head_dim]
+    for (size_t i = 0; i < t->parts.size(); ++i) {
+      const int l0 = t->part_l0[i];
+      const int rc = append_impl(t->parts[i], layer_slice(k, l0, lb), layer_slice(v, l0, lb), stream);
+      if (rc) {
+        t->failed = i > 0;  // earlier parts hold the row already
+        return part_rc(t, i, rc);
+      }
+    }
+    t->layers_done = 0;
+    mirror_parts(t);
+    return TKV_OK;
+  }
   int rc = append_check(t, k, v);
   if (rc) return rc;
   AppendArgs a{};
@@ -678,7 +869,7 @@ static ScoreArgs defer_fold_args(const tkv* t) {
   sa.layer_score = t->spart;  // rows [layer][kv head], summed in that order
   sa.live_pos = t->live_pos;
   sa.s = t->s;
-  sa.inv_lh = (float)(1.0 / ((double)t->L * t->Hq));
+  sa.inv_lh = (float)t->inv_lh();
   sa.layers = t->L * t->Hkv;
   sa.batch = t->B;
   sa.nmax = t->nmax;
@@ -905,7 +1096,7 @@ static void end_step(tkv* t, int max_live) {
   sa.layer_score = t->layer_score;
   sa.live_pos = t->live_pos;
   sa.s = t->s;
-  sa.inv_lh = (float)(1.0 / ((double)t->L * t->Hq));
+  sa.inv_lh = (float)t->inv_lh();
   sa.layers = t->L;
   sa.batch = t->B;
   sa.nmax = t->nmax;
@@ -935,6 +1126,22 @@ static int decode_attn_impl(tkv_t* t, int32_t layer_begin, int32_t layer_count, 
   if (layer_begin != t->layers_done)
     return tkv_fail(t, TKV_ESTATE, "layer groups must come in order: expected layer %d", t->layers_done);
   if (layer_count < 1 || layer_begin + layer_count > t->L) return tkv_fail(t, TKV_EINVAL, "bad layer range");
+  if (!t->parts.empty()) {
+    // per-layer budgets: each part runs its share of the range, in layer order
+    const size_t ql = (size_t)t->B * t->Hq * t->D * t->esz, ol = (size_t)t->B * t->Hq * t->D;
+    const int end = layer_begin + layer_count;
+    for (size_t i = 0; i < t->parts.size(); ++i) {
+      const int p0 = t->part_l0[i], p1 = p0 + t->parts[i]->L;
+      const int a = std::max(layer_begin, p0), e = std::min(end, p1);
+      if (a >= e) continue;
+      const int rc = decode_attn_impl(t->parts[i], a - p0, e - a, layer_slice(q, a - layer_begin, ql),
+                                      out + (size_t)(a - layer_begin) * ol, stream);
+      if (part_rc(t, i, rc)) return rc;
+    }
+    t->layers_done += layer_count;
+    mirror_parts(t);
+    return TKV_OK;
+  }
   hipStream_t st = (hipStream_t)stream;
   int max_live = 0;
   for (int b = 0; b < t->B; ++b) max_live = std::max(max_live, t->nlive[b]);
@@ -970,6 +1177,28 @@ extern "C" int tkv_decode_attn(tkv_t* t, int32_t layer_begin, int32_t layer_coun
 
 static int decode_step_impl(tkv_t* t, const void* k, const void* v, const void* q, float* out,
                                tkv_stream_t stream) {
+  if (t && !t->parts.empty()) {
+    // per-layer budgets: every part must take the row, then each runs its step
+    if (int rc = usable(t)) return rc;
+    if (!q || !out) return tkv_fail(t, TKV_EINVAL, "q/out is NULL");
+    if (misaligned(q) || misaligned(out)) return tkv_fail(t, TKV_EINVAL, "q/out not 16-byte aligned");
+    for (size_t i = 0; i < t->parts.size(); ++i)
+      if (int rc = part_rc(t, i, append_check(t->parts[i], k, v))) return rc;
+    const size_t kl = (size_t)t->B * t->row_bytes;
+    const size_t ql = (size_t)t->B * t->Hq * t->D * t->esz, ol = (size_t)t->B * t->Hq * t->D;
+    for (size_t i = 0; i < t->parts.size(); ++i) {
+      const int l0 = t->part_l0[i];
+      const int rc = decode_step_impl(t->parts[i], layer_slice(k, l0, kl), layer_slice(v, l0, kl),
+                                      layer_slice(q, l0, ql), out + (size_t)l0 * ol, stream);
+      if (rc) {
+        t->failed = i > 0;  // earlier parts hold the row already
+        return part_rc(t, i, rc);
+      }
+    }
+    t->layers_done = 0;
+    mirror_parts(t);
+    return TKV_OK;
+  }
   int rc = append_check(t, k, v);
   if (rc) return rc;
   if (!q || !out) return tkv_fail(t, TKV_EINVAL, "q/out is NULL");
@@ -1006,6 +1235,39 @@ extern "C" int tkv_decode_step(tkv_t* t, const void* k, const void* v, const voi
 
 static int stats_impl(tkv_t* t, tkv_stats_t* out) {
   if (!t || !out) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (!t->parts.empty()) {
+    // per-layer budgets: pools, traffic and time summed over the parts; the
+    // tier counts weighted by each part's layers; the evictions (the same rows
+    // in every part) and the reassignments counted once
+    tkv_stats_t a{};
+    for (size_t i = 0; i < t->parts.size(); ++i) {
+      tkv_stats_t ps{};
+      if (int rc = part_rc(t, i, stats_impl(t->parts[i], &ps))) return rc;
+      const int64_t lw = t->parts[i]->L;
+      for (int x = 0; x < 4; ++x) a.tier_count[x] += ps.tier_count[x] * lw;
+      a.hbm_bytes += ps.hbm_bytes;
+      a.host_bytes += ps.host_bytes;
+      a.full_cache_bytes += ps.full_cache_bytes;
+      a.promotions += ps.promotions;
+      a.demotions += ps.demotions;
+      a.h2d_bytes += ps.h2d_bytes;
+      a.d2h_bytes += ps.d2h_bytes;
+      a.attn_kernel_ms += ps.attn_kernel_ms;
+      a.attn_kernel_launches += ps.attn_kernel_launches;
+      a.attn_kv_bytes += ps.attn_kv_bytes;
+      a.reassign_ms += ps.reassign_ms;
+      a.mem_bytes += ps.mem_bytes;
+      if (i == 0) {
+        a.step = ps.step;
+        a.n_tokens = ps.n_tokens;
+        a.evictions = ps.evictions;
+        a.reassigns = ps.reassigns;
+      }
+    }
+    a.mem_bytes += t->mem_held;
+    *out = a;
+    return TKV_OK;
+  }
   if (int rc = arena_settled(t)) return rc;
   HIP_TRY(t, hipStreamSynchronize(t->side));
   if (t->side_v) HIP_TRY(t, hipStreamSynchronize(t->side_v));
@@ -1029,6 +1291,8 @@ extern "C" int tkv_stats(tkv_t* t, tkv_stats_t* out) {
 }
 
 int tkv_flush_score(tkv* t, hipStream_t stream) {
+  for (size_t i = 0; i < t->parts.size(); ++i)  // per-layer budgets: every part's pending increment
+    if (int rc = part_rc(t, i, tkv_flush_score(t->parts[i], stream))) return rc;
   if (t->defer) return t->pend ? flush_deferred(t, stream, true) : TKV_OK;
   if (!t->score_pending) return TKV_OK;
   HIP_TRY(t, launch_score(t->pending_score, t->pending_tiles, stream));
@@ -1040,7 +1304,11 @@ static int read_scores_impl(tkv_t* t, float* scores, tkv_stream_t stream) {
   if (int rc = usable(t)) return rc;
   if (!scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   const float* src = t->s;
-  if (t->defer && t->pend) {
+  if (!t->parts.empty()) {
+    // per-layer budgets: every part's pending increment goes into s (the parts
+    // apply one step at a time, so this changes no bits)
+    if (int rc = tkv_flush_score(t, (hipStream_t)stream)) return rc;
+  } else if (t->defer && t->pend) {
     // the pending steps into a copy of s: they stay pending, so a read never
     // changes which steps a later launch sums together
     if (int rc = flush_deferred(t, (hipStream_t)stream, false)) return rc;
@@ -1061,6 +1329,11 @@ static int write_scores_impl(tkv_t* t, const float* scores, tkv_stream_t stream)
   if (!scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "step in progress");
   // the written scores replace s with every pending update: those are dropped
+  for (tkv* p : t->parts) {
+    if (p->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "step in progress");
+    p->pend = 0;
+    p->score_pending = false;
+  }
   if (t->defer) {
     t->pend = 0;
   } else {
@@ -1077,6 +1350,7 @@ extern "C" int tkv_write_scores(tkv_t* t, const float* scores, tkv_stream_t stre
 static int read_tiers_impl(tkv_t* t, uint8_t* tiers, tkv_stream_t stream) {
   if (int rc = usable(t)) return rc;
   if (!tiers) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (!t->parts.empty()) return part_rc(t, 0, read_tiers_impl(t->parts[0], tiers, stream));  // layer 0's
   HIP_TRY(t, hipMemcpyAsync(tiers, t->tier, (size_t)t->B * t->nmax, hipMemcpyDeviceToHost, (hipStream_t)stream));
   HIP_TRY(t, hipStreamSynchronize((hipStream_t)stream));
   return TKV_OK;
@@ -1085,9 +1359,21 @@ extern "C" int tkv_read_tiers(tkv_t* t, uint8_t* tiers, tkv_stream_t stream) {
   return guarded(t, [&] { return read_tiers_impl(t, tiers, stream); });
 }
 
+static int read_layer_tiers_impl(tkv_t* t, int32_t layer, uint8_t* tiers, tkv_stream_t stream) {
+  if (int rc = usable(t)) return rc;
+  if (layer < 0 || layer >= t->L) return tkv_fail(t, TKV_EINVAL, "layer %d out of range", layer);
+  if (t->parts.empty()) return read_tiers_impl(t, tiers, stream);
+  const size_t i = part_of(t, layer);
+  return part_rc(t, i, read_tiers_impl(t->parts[i], tiers, stream));
+}
+extern "C" int tkv_read_layer_tiers(tkv_t* t, int32_t layer, uint8_t* tiers, tkv_stream_t stream) {
+  return guarded(t, [&] { return read_layer_tiers_impl(t, layer, tiers, stream); });
+}
+
 static int read_deltas_impl(tkv_t* t, tkv_delta* promote, tkv_delta* demote, int32_t* counts) {
   if (int rc = usable(t)) return rc;
   if (!promote || !demote || !counts) return tkv_fail(t, TKV_EINVAL, "NULL argument");
+  if (!t->parts.empty()) return part_rc(t, 0, read_deltas_impl(t->parts[0], promote, demote, counts));
   const size_t nd = (size_t)t->B * t->nmax;
   std::memcpy(promote, t->h_promote, nd * sizeof(tkv_delta));
   std::memcpy(demote, t->h_demote, nd * sizeof(tkv_delta));
@@ -1104,6 +1390,10 @@ static int read_kv_impl(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, void*
   if (!k || !v) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (layer < 0 || layer >= t->L || seq < 0 || seq >= t->B || pos < 0 || pos >= t->n)
     return tkv_fail(t, TKV_EINVAL, "layer/seq/pos out of range");
+  if (!t->parts.empty()) {
+    const size_t i = part_of(t, layer);
+    return part_rc(t, i, read_kv_impl(t->parts[i], layer - t->part_l0[i], seq, pos, k, v, stream));
+  }
   if (int rc = arena_settled(t)) return rc;
   const size_t at = (size_t)seq * t->nmax + pos;
   const uint8_t tier = t->h_tier[at];
@@ -1153,6 +1443,10 @@ static int read_t2_impl(tkv_t* t, int32_t layer, int32_t seq, int32_t pos, int8_
   if (!k_codes || !v_codes || !scales) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   if (layer < 0 || layer >= t->L || seq < 0 || seq >= t->B || pos < 0 || pos >= t->n)
     return tkv_fail(t, TKV_EINVAL, "layer/seq/pos out of range");
+  if (!t->parts.empty()) {
+    const size_t i = part_of(t, layer);
+    return part_rc(t, i, read_t2_impl(t->parts[i], layer - t->part_l0[i], seq, pos, k_codes, v_codes, scales));
+  }
   if (int rc = arena_settled(t)) return rc;
   const size_t at = (size_t)seq * t->nmax + pos;
   if (t->h_tier[at] != TKV_T2) return tkv_fail(t, TKV_ESTATE, "position %d is not in T2", pos);

@@ -159,6 +159,19 @@ struct tkv {
 
   std::string err;
 
+  // ---- per-layer HBM budgets
+  // The handle the caller holds: one part per group of consecutive layers with
+  // one ratio, each a whole handle over its layers (empty otherwise).  The
+  // parts share this handle's score array s.
+  std::vector<tkv*> parts;
+  std::vector<int> part_l0;   // first layer of each part
+  // In a part: s belongs to the handle of the parts (not freed here), and
+  // Eq. 1 averages over score_layers layers (all of that handle's).
+  bool s_shared = false;
+  int score_layers = 0;
+  // Eq. 1's 1 / (layers * q_heads) over the layers the scores average over
+  double inv_lh() const { return 1.0 / ((double)(score_layers ? score_layers : L) * Hq); }
+
   tkvd::ArenaSpace arenaspace() const {
     tkvd::ArenaSpace a{};
     a.a1_k = d_arena1_k;

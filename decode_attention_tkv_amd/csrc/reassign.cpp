@@ -118,9 +118,26 @@ static DeltaTotals delta_totals(const tkv* t) {
 // kernel reads the scratch any more.
 static int reassign_impl(tkv_t* t, tkv_stream_t stream, bool use_static) {
   if (!t) return tkv_fail(nullptr, TKV_EINVAL, "handle is NULL");
+  for (const tkv* p : t->parts) t->failed = t->failed || p->failed;
   if (t->failed) return tkv_fail(t, TKV_ESTATE, "handle unusable: an earlier reassignment failed part way");
   if (t->state == TkvState::InStep) return tkv_fail(t, TKV_ESTATE, "reassign between the layer groups of a step");
   if (t->n == 0) return TKV_OK;
+  if (!t->parts.empty()) {
+    // Per-layer budgets: each part ranks the scores of all layers, so every
+    // part's pending Eq. 1 increment goes in first; then each part re-places
+    // its layers with its own ratio.  A part that fails after an earlier one
+    // was re-placed leaves the parts disagreeing: the handle is then failed.
+    if (int rc = tkv_flush_score(t, (hipStream_t)stream)) return rc;
+    for (size_t i = 0; i < t->parts.size(); ++i) {
+      const int rc = reassign_impl(t->parts[i], stream, use_static);
+      if (rc != TKV_OK) {
+        t->err = t->parts[i]->err;
+        t->failed = t->failed || i > 0 || t->parts[i]->failed;
+        return rc;
+      }
+    }
+    return TKV_OK;
+  }
   const auto wall0 = std::chrono::steady_clock::now();
   hipStream_t st = (hipStream_t)stream;
   if (int rc = tkv_flush_score(t, st)) return rc;  // ranking reads s

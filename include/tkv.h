@@ -91,7 +91,31 @@ typedef struct {
                              arenas, scratch, the buffers a reassignment grows); an
                              allocation past it fails with TKV_ENOMEM as a failed hipMalloc
                              would.  0 = no cap. */
+  const double* layer_hbm; /* per-layer HBM budgets: `layers` ratios in [0,1] (host
+                             memory, read during tkv_create only), or NULL for hbm_ratio
+                             in every layer.  See "Per-layer HBM budgets" below. */
 } tkv_options;
+
+/* Per-layer HBM budgets (the budget variant in the spirit of ARKV's per-layer
+ * ratios, gist.science ARKV summary, Method; tiers and budgets from "Not All
+ * Thoughts Need HBM", Method §1): layer l keeps floor(layer_hbm[l] * N) rows
+ * in HBM.  Consecutive layers with the same ratio form a group, and each group
+ * places its rows by Method §1 with its own ratio: its T0 holds the protected
+ * rows and its best candidates.  Every group ranks by the one Eq. 1 score,
+ * averaged over all layers, and shares evict_ratio and t2_ratio.  So every
+ * group evicts the same rows and the outputs do not depend on the ratios
+ * (Method §3, Proposition 1).  A group's T2 count can be smaller than
+ * floor(t2_ratio * N) when its HBM share leaves fewer candidates.  Each group
+ * holds its own T0 pool, staging and arenas, sized by its own ratio; with
+ * stream staging every group needs more than staging_layers layers.  Calls take
+ * every layer as usual (each group runs on its own slice, in layer order, on
+ * the caller's stream); tkv_read_tiers and tkv_read_deltas report layer 0's
+ * group, tkv_read_layer_tiers any layer's.  hbm_ratio is then unused; one
+ * distinct ratio is the same as no layer_hbm.  Deferred Eq. 1 runs one step
+ * per launch.  A reassignment first applies every group's pending Eq. 1
+ * increment, then re-places each group.  Not with TKV_FLAG_NO_T1 or
+ * TKV_FLAG_SHARED_HBM (TKV_EINVAL).  tkv_stats sums pools and traffic over
+ * the groups; tier_count then counts (layer, position) rows of the batch. */
 
 /* Record HIP events around the attention kernels; tkv_stats reports their time. */
 #define TKV_FLAG_TIME_KERNELS 1ull
@@ -292,6 +316,10 @@ int tkv_stats(tkv_t* t, tkv_stats_t* out);
 int tkv_read_scores(tkv_t* t, float* scores, tkv_stream_t stream);
 int tkv_write_scores(tkv_t* t, const float* scores, tkv_stream_t stream);
 int tkv_read_tiers(tkv_t* t, uint8_t* tiers, tkv_stream_t stream);
+/* The tiers of layer `layer`'s rows (host [batch][max_tokens]); with
+ * per-layer budgets each layer group has its own, otherwise every layer has
+ * the handle's.  TKV_EINVAL for a layer out of range. */
+int tkv_read_layer_tiers(tkv_t* t, int32_t layer, uint8_t* tiers, tkv_stream_t stream);
 /* Changed rows of the last tkv_reassign: promote/demote are host
  * [batch][max_tokens], ascending by position per sequence; counts is host
  * [batch][2] = {promotions, demotions}. */

@@ -269,6 +269,14 @@ class OracleLayerGroups:
         for (l0, l1, _), p in zip(self.groups, self.parts):
             p.prefill(K[l0:l1], V[l0:l1])
 
+    def prefill_scored(self, K, V, Q):
+        """The scored prefill: each group places its rows as prefill() does,
+        the prompt's causal attention weights over all layers become the shared
+        scores (prefill.py), then every group is re-placed by them."""
+        self.prefill(K, V)
+        self.s[:, : self.n] = _prefill.prefill_scores(K, Q, self.n)
+        return self.reassign()
+
     def append(self, k, v):
         for (l0, l1, _), p in zip(self.groups, self.parts):
             p.append(k[l0:l1], v[l0:l1])

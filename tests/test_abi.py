@@ -71,3 +71,29 @@ def test_null_handle_calls_fail_cleanly(tkv):
     assert lib.tkv_decode_step(None, None, None, None, None, None) == tkv.TKV_EINVAL
     assert lib.tkv_prefill_scored(None, None, None, None, 1, None) == tkv.TKV_EINVAL
     assert lib.tkv_stats(None, None) == tkv.TKV_EINVAL
+
+
+@pytest.mark.parametrize("layer_hbm,kw", [
+    ([0.2, float("nan"), 0.5, 0.5], {}),
+    ([0.2, 0.3, 1.5, 0.5], {}),
+    ([0.2, 0.2, 0.5, 0.5], dict(flags=2)),       # TKV_FLAG_NO_T1
+    ([0.2, 0.2, 0.5, 0.5], dict(flags=8)),       # TKV_FLAG_SHARED_HBM
+    ([0.2, 0.2, 0.5, 0.5], dict(staging_layers=2)),  # stream staging: a group of 2 layers, not more than S
+])
+def test_create_rejects_bad_layer_budgets(tkv, layer_hbm, kw):
+    """Per-layer HBM budgets: every ratio in [0, 1]; not with the eviction-only
+    policy or the batch-shared budget; with stream staging every layer group
+    has more layers than staging slots."""
+    args = dict(layers=4, q_heads=8, kv_heads=4, head_dim=64, batch=1, max_tokens=64, dtype=tkv.TKV_F32,
+                delta=16, hbm_ratio=0.5, evict_ratio=0.1, prompt=4, sinks=4, recent=8, layer_hbm=layer_hbm)
+    args.update(kw)
+    with pytest.raises(tkv.TkvError) as e:
+        tkv.tkv_create(**args)
+    assert e.value.code == tkv.TKV_EINVAL
+    assert tkv.lib().tkv_last_error(None)
+
+
+def test_layer_budgets_length_checked(tkv):
+    with pytest.raises(ValueError):
+        tkv.tkv_create(layers=4, q_heads=8, kv_heads=4, head_dim=64, batch=1, max_tokens=64, dtype=tkv.TKV_F32,
+                       delta=16, hbm_ratio=0.5, evict_ratio=0.1, prompt=4, sinks=4, recent=8, layer_hbm=[0.5, 0.5])

@@ -123,3 +123,16 @@ def test_t2_clipped_per_group():
         assert int((tier == T2).sum()) == min(c - n0c, math.floor(0.25 * n))
         counts.append(int((tier == T2).sum()))
     assert counts[0] == math.floor(0.25 * n) and counts[1] < counts[0]
+
+
+def test_scored_prefill_equal_ratios_is_the_one_budget_oracle():
+    w = _small(hbm_ratio=0.4, prefill=64)
+    K, V = w.values(w.kv(0, 0, w.prefill)), w.values(w.kv(1, 0, w.prefill))
+    Q = w.values(w.q(0, w.prefill)).transpose(1, 2, 0, 3, 4).copy()  # [L][B][n][Hq][d]
+    a = oracle.OracleTKV.for_workload(w)
+    a.prefill_scored(K, V, Q)
+    b = oracle.OracleLayerGroups.for_workload(w, [0.4] * 2 + [0.4000001] * 3)
+    b.prefill_scored(K, V, Q)
+    assert np.array_equal(a.s, b.s)
+    for l in range(w.layers):
+        assert np.array_equal(a.tier, b.tier_of(l))
