@@ -128,3 +128,41 @@ def test_random_odd_delta(i):
     outs, s, tiers, st, o, n_reassign = run_parity(w, Inputs(w), w.steps, check_every=2, staging_layers=staging,
                                                    chunk=chunk, calls=calls, groups=groups, static=static)
     assert n_reassign == w.steps // w.delta
+
+
+def _draw_layers(i):
+    """A random workload with per-layer HBM budgets: two to four groups of
+    consecutive layers, each with its own ratio (stream staging only where
+    every group has more layers than staging slots)."""
+    r = np.random.default_rng(9000 + i)
+    dtype = "bf16" if r.random() < 0.6 else "f32"
+    group = int(r.choice([1, 2, 4, 5, 8]))
+    kv_heads = int(r.choice([1, 2]))
+    ngroups = int(r.integers(2, 5))
+    sizes = [int(x) for x in r.integers(1, 4, ngroups)]
+    staging = 0
+    if min(sizes) >= 3 and r.random() < 0.5:
+        staging = int(r.integers(2, min(sizes)))
+    layer_hbm = []
+    for sz in sizes:
+        layer_hbm += [float(np.round(r.uniform(0.0, 1.0), 2))] * sz
+    prefill = int(r.integers(60, 400))
+    delta = int(r.choice([7, 8, 16]))
+    t2 = float(r.choice([0.0, 0.0, 0.1, 0.2]))
+    w = tkvsynth.CONFIGS["tiny"].replace(
+        name="layers%d" % i, dtype=dtype, head_dim=int(r.choice([64, 128])), kv_heads=kv_heads,
+        q_heads=kv_heads * group, layers=len(layer_hbm), batch=int(r.integers(1, 4)), prefill=prefill,
+        steps=int(r.integers(2, 4)) * delta + int(r.integers(0, delta)), delta=delta,
+        evict_ratio=float(np.round(r.uniform(0.0, 0.4), 2)), t2_ratio=t2,
+        prompt=int(r.integers(0, min(prefill, 48) + 1)), sinks=int(r.integers(0, 6)), recent=int(r.integers(0, 40)),
+        seed=int(r.integers(0, 1 << 20)), t2_fp8=bool(t2 > 0 and r.random() < 0.5))
+    calls = str(r.choice(["one", "two"]))
+    return w, layer_hbm, staging, calls
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_layer_budgets(i):
+    from test_gpu_layer_budgets import run_layers
+    w, layer_hbm, staging, calls = _draw_layers(i)
+    st, o, n_reassign = run_layers(w, layer_hbm, staging_layers=staging, calls=calls, check_every=3)
+    assert n_reassign == w.steps // w.delta
