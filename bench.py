@@ -74,7 +74,7 @@ EXTRA_FLAGS = 0  # TKV_FLAG_* added to every handle (e.g. the vector pass for gr
 
 
 def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kernels=True, sync_reassign=False,
-               samples=(), scored_prefill=None):
+               samples=(), scored_prefill=None, layer_hbm=None):
     """Prefill, `warmup` untimed steps, then `steps` timed steps.  Returns
     (seconds, stats before, stats after).  sync_reassign: drain the stream
     before and after every reassignment of the timed steps and put the
@@ -82,10 +82,11 @@ def run_decode(w, inputs, warmup, steps, torch, tkv, staging_layers=0, time_kern
     0-based steps whose outputs are copied to the host (a synchronisation
     each; for untimed runs), under after["samples"]; the last step's output
     is always under after["last_out"].  scored_prefill: the prompt's queries
-    [L][B][n][Hq][d] to prefill with scores instead of the plain placement."""
+    [L][B][n][Hq][d] to prefill with scores instead of the plain placement.
+    layer_hbm: per-layer HBM ratios (tkv_options.layer_hbm), or None."""
     k0, v0, kn, vn, q = inputs
     c = tkv.TieredKV.for_workload(w, staging_layers=staging_layers, time_kernels=time_kernels, chunk=CHUNK,
-                                  extra_flags=EXTRA_FLAGS)
+                                  extra_flags=EXTRA_FLAGS, layer_hbm=layer_hbm)
     if scored_prefill is not None:
         c.prefill_scored(k0, v0, scored_prefill)
     else:
@@ -559,28 +560,37 @@ def main():
     if args.baseline_steps > 0:
         # the same engine under other policies, same inputs and step window
         result["baselines"] = {}
-        policies = (("full cache (all rows in T0)", dict(hbm_ratio=1.0, evict_ratio=0.0)),
-                    ("eviction only, heavy hitters (no T1)", dict(no_t1=True)),
-                    ("sinks + recent window", dict(hbm_ratio=0.0, no_t1=True, prompt=0)))
+        policies = (("full cache (all rows in T0)", dict(hbm_ratio=1.0, evict_ratio=0.0), None),
+                    ("eviction only, heavy hitters (no T1)", dict(no_t1=True), None),
+                    ("sinks + recent window", dict(hbm_ratio=0.0, no_t1=True, prompt=0), None))
         if w.batch > 1:
-            policies += (("one HBM budget for the batch", dict(shared_hbm=True)),)
+            policies += (("one HBM budget for the batch", dict(shared_hbm=True), None),)
+        # per-layer budgets: the first half of the layers 0.2 below the workload's ratio, the
+        # rest 0.2 above (the same mean; the same rows evicted)
+        half = w.layers // 2
+        lo, hi = max(0.0, w.hbm_ratio - 0.2), min(1.0, w.hbm_ratio + 0.2)
+        policies += (("per-layer HBM budgets (%d layers at %.2f, %d at %.2f)" % (half, lo, w.layers - half, hi), {},
+                      [lo] * half + [hi] * (w.layers - half)),)
         result["baselines"]["tiered (this line)"] = {
             "steps_per_s": steps_per_s, "live_rows_per_seq_at_end":
                 (after["tier_count"][0] + after["tier_count"][1] + after["tier_count"][2]) / w.batch,
             "t0_rows_at_end": after["tier_count"][0],
             "hbm_ratio": w.hbm_ratio, "evict_ratio": w.evict_ratio, "no_t1": False,
             "kernel_gbs": achieved, "host_bytes": after["host_bytes"]}
-        for name, kw in policies:
+        for name, kw, layer_hbm in policies:
             print("[bench] baseline %s: %d timed steps" % (name, args.baseline_steps), file=sys.stderr, flush=True)
             wb = w.replace(**kw)
-            bsecs, bb, ba = run_decode(wb, inputs, args.warmup, args.baseline_steps, torch, tkv)
-            live = (ba["tier_count"][0] + ba["tier_count"][1] + ba["tier_count"][2]) / w.batch
+            bsecs, bb, ba = run_decode(wb, inputs, args.warmup, args.baseline_steps, torch, tkv, layer_hbm=layer_hbm)
+            # (with per-layer budgets tier_count counts (layer, position) rows)
+            per = w.batch * (w.layers if layer_hbm else 1)
+            live = (ba["tier_count"][0] + ba["tier_count"][1] + ba["tier_count"][2]) / per
             kb = ba["attn_kv_bytes"] - bb["attn_kv_bytes"]
             km = ba["attn_kernel_ms"] - bb["attn_kernel_ms"]
             result["baselines"][name] = {
                 "steps_per_s": args.baseline_steps / bsecs, "live_rows_per_seq_at_end": live,
-                "t0_rows_at_end": ba["tier_count"][0],
-                "hbm_ratio": wb.hbm_ratio, "evict_ratio": wb.evict_ratio, "no_t1": wb.no_t1,
+                "t0_rows_at_end": ba["tier_count"][0] / (w.layers if layer_hbm else 1),
+                "hbm_ratio": wb.hbm_ratio if not layer_hbm else sum(layer_hbm) / len(layer_hbm),
+                "evict_ratio": wb.evict_ratio, "no_t1": wb.no_t1,
                 "kernel_gbs": kb / (km / 1e3) / 1e9 if km > 0 else None,
                 "host_bytes": ba["host_bytes"]}
 
