@@ -298,9 +298,12 @@ int tkv_reassign(tkv_t* t, tkv_stream_t stream);
  * holds -- 2 * layers * kv_heads * head_dim * element bytes per moved row
  * (rows entering T1 or T2; promotions too outside positional staging) plus
  * about 100 bytes per changed row -- returns TKV_ECAPACITY and changes
- * nothing.  The array is shared by every handle on that GPU and keeps the
- * last call's contents: calls that overlap on one GPU (other host threads)
- * race.  The call returns only once no kernel reads the array any more. */
+ * nothing (with per-layer budgets the layer groups are re-placed one after
+ * another, each within the array; if a later group does not fit, the earlier
+ * ones are already re-placed and the handle is marked failed).  The array is
+ * shared by every handle on that GPU and keeps the last call's contents:
+ * calls that overlap on one GPU (other host threads) race.  The call returns
+ * only once no kernel reads the array any more. */
 int tkv_reassign_static(tkv_t* t, tkv_stream_t stream);
 
 /* Counters and sizes (the HBM the tiers save and the traffic they cost: the
