@@ -205,3 +205,55 @@ def test_layer_budgets_errors():
     c.decode_attn(dq, out)
     c.reassign()
     c.close()
+
+
+@pytest.mark.timeout(900)
+def test_layer_budgets_14b_full_shape():
+    """The 14B shape (48 layers, 40 q / 8 kv heads, bf16, 4 sequences, 4096
+    prefilled positions) with three groups of 16 layers at HBM ratios 0.3,
+    0.5 and 0.7, through one reassignment.  Sequences are independent (Method
+    §1, §2), so an oracle over every layer of one sequence is exact for it:
+    its outputs and scores are compared every 16 steps.  Every sequence's
+    labels in every group are re-derived from the GPU's fp32 scores."""
+    import decode_attention_tkv_amd as tkv
+    w = tkvsynth.CONFIGS["14b"].replace(steps=65)
+    ratios = [0.3] * 16 + [0.5] * 16 + [0.7] * 16
+    seq = 1
+    print("[layer budgets 14b] drawing inputs", flush=True)
+    inp = Inputs(w)
+    c = tkv.TieredKV.for_workload(w, layer_hbm=ratios)
+    c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
+    o = oracle.OracleLayerGroups(ratios, w.q_heads, w.kv_heads, w.head_dim, 1, w.n_final, w.delta, w.evict_ratio,
+                                 w.t2_ratio, w.prompt, w.sinks, w.recent, True)
+    o.prefill(w.values(inp.k0[:, [seq]]), w.values(inp.v0[:, [seq]]))
+    out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    worst = 0.0
+    for t in range(w.steps):
+        k, v = inp.step_kv(t)
+        c.decode_step(to_device(k, w.dtype), to_device(v, w.dtype), to_device(inp.q[t], w.dtype), out)
+        o.append(w.values(k[:, [seq]]), w.values(v[:, [seq]]))
+        ref = o.attend(w.values(inp.q[t][:, [seq]]))
+        if t % 16 == 0 or t == w.steps - 1:
+            worst = max(worst, float(np.max(np.abs(out.cpu().numpy()[:, [seq]] - ref))))
+            print("[layer budgets 14b] step %d: max |out - oracle| %.3g" % (t + 1, worst), flush=True)
+        if (t + 1) % w.delta == 0:
+            n = o.n
+            g_s = c.read_scores()[:, :n]
+            assert max_rel(g_s[[seq]], o.s[:, :n]) <= 1e-4
+            old = [c.read_layer_tiers(l0)[:, :n] for (l0, _, _) in o.groups]
+            c.reassign()
+            new = []
+            for g, (l0, l1, h) in enumerate(o.groups):
+                got = c.read_layer_tiers(l0)[:, :n]
+                for b in range(w.batch):
+                    ref_t = tiering.reassign(old[g][b], g_s[b], n, w.prompt, w.sinks, w.recent, h, w.evict_ratio,
+                                             w.t2_ratio)
+                    assert np.array_equal(got[b], ref_t), "labels of group %d, sequence %d" % (g, b)
+                new.append(got)
+                assert np.array_equal(got == T3, new[0] == T3)
+            o.reassign(rank_scores=g_s[[seq]], adopt=[x[[seq]] for x in new])
+    rel = max_rel(c.read_scores()[[seq], : o.n], o.s[:, : o.n])
+    st = c.stats()
+    c.close()
+    assert worst <= 5e-3 and rel <= 1e-4, (worst, rel)
+    assert st["reassigns"] == 1 and st["evictions"] > 0
