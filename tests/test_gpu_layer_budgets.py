@@ -91,6 +91,19 @@ def run_layers(w, layer_hbm, staging_layers=0, calls="one", groups=None, check_e
                 new.append(got)
             o.reassign(rank_scores=g_s, adopt=new)
             n_reassign += 1
+            # the values attention reads for sampled live rows of every layer (T2 rows as their
+            # dequantised values; with stream staging those exist only as codes) are the oracle's,
+            # bit for bit
+            rng = np.random.default_rng(t)
+            for l in range(w.layers):
+                g, ll = o.part_of(l)
+                tier = o.parts[g].tier
+                for b in range(w.batch):
+                    live = np.nonzero(tier[b, :n] < (2 if staging_layers else 3))[0]
+                    for pos in rng.choice(live, size=min(4, len(live)), replace=False):
+                        gk, gv = c.read_kv(l, b, int(pos))
+                        assert np.array_equal(w.values(gk), o.parts[g].K[ll, b, pos])
+                        assert np.array_equal(w.values(gv), o.parts[g].V[ll, b, pos])
     rel = max_rel(c.read_scores()[:, : o.n], o.s[:, : o.n])
     st = c.stats()
     c.close()
