@@ -114,8 +114,9 @@ typedef struct {
  * distinct ratio is the same as no layer_hbm.  Deferred Eq. 1 runs one step
  * per launch.  A reassignment first applies every group's pending Eq. 1
  * increment, then re-places each group.  Not with TKV_FLAG_NO_T1 or
- * TKV_FLAG_SHARED_HBM (TKV_EINVAL).  tkv_stats sums pools and traffic over
- * the groups; tier_count then counts (layer, position) rows of the batch. */
+ * TKV_FLAG_SHARED_HBM (TKV_EINVAL).  mem_cap_bytes is split over the groups
+ * by their layer counts.  tkv_stats sums pools and traffic over the groups;
+ * tier_count then counts (layer, position) rows of the batch. */
 
 /* Record HIP events around the attention kernels; tkv_stats reports their time. */
 #define TKV_FLAG_TIME_KERNELS 1ull
@@ -179,7 +180,8 @@ typedef struct {
 typedef struct {
   int64_t step;              /* decode steps completed */
   int64_t n_tokens;          /* positions appended per sequence (incl. evicted) */
-  int64_t tier_count[4];     /* positions per tier, summed over the batch */
+  int64_t tier_count[4];     /* positions per tier, summed over the batch (with per-layer
+                                budgets: (layer, position) rows) */
   int64_t hbm_bytes;         /* K/V bytes allocated in HBM (T0 pool + staging) */
   int64_t host_bytes;        /* pinned host K/V bytes (T1 + T2 arenas) */
   int64_t full_cache_bytes;  /* K/V bytes an all-HBM cache of max_tokens would take */
