@@ -38,9 +38,10 @@ STAGING_LAYERS = 4  # HBM slots of the stream-staging leg (two layers per copy)
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_tkv_amd", "csrc", "attn.hip")
 def attention_kernel(w, args):
     """Which pass of the split-K kernel a workload's decode steps take: bf16
-    caches with four or more query heads per kv head use the matrix cores
-    unless the vector pass is asked for; every other shape the vector units."""
-    if w.dtype == "bf16" and w.q_heads >= 4 * w.kv_heads and not args.vector_pass:
+    caches with one query head per kv head, or four or more (unless the
+    vector pass is asked for), use the matrix cores; every other shape the
+    vector units."""
+    if w.dtype == "bf16" and (w.q_heads == w.kv_heads or (w.q_heads >= 4 * w.kv_heads and not args.vector_pass)):
         return "k_attn_chunk (split-K attention, matrix-core pass)"
     return "k_attn_chunk (split-K attention, vector pass)"
 

@@ -297,17 +297,17 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
     dev((void**)&t->s, B * nmax * 4);
   }
   t->vector_pass = (o.flags & TKV_FLAG_VECTOR_PASS) != 0 && s.dtype == TKV_BF16 && group >= 4;
-  // the matrix-core path over resident staging
-  t->defer = resident && s.dtype == TKV_BF16 && group >= 4 && !t->vector_pass;
+  // the matrix-core path (bf16, g >= 4 or g == 1) over resident staging
+  t->defer = resident && s.dtype == TKV_BF16 && ((group >= 4 && !t->vector_pass) || group == 1);
   if (t->defer) {
-    // two steps' queries beside this step's in the 16-row tile; a part of a
-    // handle with per-layer budgets takes one step per launch, so that reads
-    // may apply its pending step without changing the scores' bits
-    t->pair = 3 * group <= 16 && !part;
-    for (int i = 0; i < 3; ++i) {
-      dev(&t->qbuf[i], L * B * Hq * t->D * t->esz);
-      dev((void**)&t->mlbuf[i], L * B * Hq * 2 * 4);
-    }
+    // as many pending steps per forming launch as fit beside this step's
+    // queries in the 16-row tile; a part of a handle with per-layer budgets
+    // takes one step per launch, so that reads may apply its pending step
+    // without changing the scores' bits
+    t->kmax = part ? 1 : 16 / group - 1;
+    t->ring = t->kmax + 1;
+    dev(&t->qring, (size_t)t->ring * L * B * Hq * t->D * t->esz);
+    dev((void**)&t->mlring, (size_t)t->ring * L * B * Hq * 2 * 4);
     dev((void**)&t->s_view, B * nmax * 4);
     dev((void**)&t->spart, L * t->Hkv * B * t->lstride * 4);
   } else {
@@ -863,7 +863,11 @@ static int drain_events(tkv* t) {
   return TKV_OK;
 }
 
-// Deferred Eq. 1: the fold of the pending step's per-group sums into s.
+// Deferred fold: partial sums per row, 16 when a row's list (layers x kv
+// heads) is longer than 640 entries, else 4.
+static int fold_parts(const tkv* t) { return t->L * t->Hkv > 640 ? 16 : 4; }
+
+// Deferred Eq. 1: the fold of the pending steps' sums into s.
 static ScoreArgs defer_fold_args(const tkv* t) {
   ScoreArgs sa{};
   sa.layer_score = t->spart;  // rows [layer][kv head], summed in that order
@@ -874,24 +878,37 @@ static ScoreArgs defer_fold_args(const tkv* t) {
   sa.batch = t->B;
   sa.nmax = t->nmax;
   sa.lstride = t->lstride;
+  sa.parts = fold_parts(t);
   for (int b = 0; b < t->B; ++b) sa.nlive[b] = t->prev_nlive[b];
   return sa;
 }
 
-// tiles of 64 rows of the deferred fold
+// tiles of the deferred fold (256 / parts rows each)
 static int prev_tiles(const tkv* t) {
   int m = 0;
   for (int b = 0; b < t->B; ++b) m = std::max(m, t->prev_nlive[b]);
-  return (m + 63) / 64;
+  const int rows = 256 / fold_parts(t);
+  return (m + rows - 1) / rows;
+}
+
+// The deferral's ring arguments of an attention launch.
+static void ring_args(const tkv* t, AttnArgs* a) {
+  a->ring = t->ring;
+  a->qcur = t->qcur;
+  a->qring = t->qring;
+  a->mlring = t->mlring;
+  a->qslot = (int64_t)t->L * t->B * t->Hq * t->D;
+  a->mlslot = (int64_t)t->L * t->B * t->Hq * 2;
+  a->spart = t->spart;
 }
 
 // Deferred Eq. 1: how many pending steps the running step's launches form
-// (and its merge pass folds): both once two are pending, or the one pending
-// step when two do not fit the logits tile.  Fixed for the whole step: pend
-// changes only when a step ends or a reassignment commits.
+// (and its merge pass folds): all of them once kmax are pending, else none.
+// Fixed for the whole step: pend changes only when a step ends or a
+// reassignment commits.
 static int defer_now(const tkv* t) {
   if (!t->defer) return 0;
-  return t->pend == 2 ? 2 : (t->pend == 1 && !t->pair) ? 1 : 0;
+  return t->pend >= t->kmax ? t->pend : 0;
 }
 
 // Split-K attention + chunk merge for layers [lb, lb + lc) whose q/out start at q, out.
@@ -903,12 +920,7 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
   if (t->defer) {
     a.prev_mode = now ? 1 : 0;
     a.prev_steps = now;
-    a.qprev = t->qbuf[t->qcur];
-    a.qprev2 = t->qbuf[(t->qcur + 2) % 3];
-    a.qsave = t->qbuf[(t->qcur + 1) % 3];
-    a.mlprev = t->mlbuf[t->qcur];
-    a.mlprev2 = t->mlbuf[(t->qcur + 2) % 3];
-    a.spart = t->spart;
+    ring_args(t, &a);
   }
   a.rows = t->rowspace();
   a.live_loc = t->live_loc;
@@ -962,7 +974,7 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
   ScoreArgs fold{};
   int fold_tiles = 0;
   if (t->defer) {
-    f.mlprev = t->mlbuf[(t->qcur + 1) % 3];
+    f.mlprev = t->mlring + (size_t)((t->qcur + 1) % t->ring) * t->L * t->B * t->Hq * 2;
     if (now && lb + lc == t->L) {
       fold = defer_fold_args(t);
       fold_tiles = prev_tiles(t);
@@ -992,11 +1004,7 @@ static int flush_deferred(tkv* t, hipStream_t st, bool commit) {
   a.lstride = t->lstride;
   a.prev_mode = 2;
   a.prev_steps = t->pend;
-  a.qprev = t->qbuf[t->qcur];
-  a.qprev2 = t->qbuf[(t->qcur + 2) % 3];
-  a.mlprev = t->mlbuf[t->qcur];
-  a.mlprev2 = t->mlbuf[(t->qcur + 2) % 3];
-  a.spart = t->spart;
+  ring_args(t, &a);
   int m = 0;
   for (int b = 0; b < t->B; ++b) {
     a.nlive[b] = t->prev_nlive[b];  // the last pending step's rows (the live list only grew since)
@@ -1011,7 +1019,7 @@ static int flush_deferred(tkv* t, hipStream_t st, bool commit) {
   }
   if (chunks > 0) {
     HIP_TRY(t, launch_attn(a, none, t->dtype, t->D, t->group, t->chunk, false, t->L, chunks, nullptr, nullptr, st));
-    HIP_TRY(t, launch_fold64(fold, prev_tiles(t), st));
+    HIP_TRY(t, launch_fold(fold, prev_tiles(t), st));
   }
   if (commit) t->pend = 0;
   return TKV_OK;
@@ -1106,7 +1114,7 @@ static void end_step(tkv* t, int max_live) {
     // computed and folded by the next step's launches (or by tkv_flush_score)
     t->pend = t->pend - defer_now(t) + (max_live > 0 ? 1 : 0);
     t->prev_nlive = t->nlive;
-    t->qcur = (t->qcur + 1) % 3;
+    t->qcur = (t->qcur + 1) % t->ring;
   } else {
     // applied by the next append's launch (or by tkv_flush_score)
     t->pending_score = sa;

@@ -17,9 +17,9 @@
 //                 (quad_perm, row_half_mirror, row_mirror), the chunk max and
 //                 sums with DPP + LDS in a fixed order.  Phase 1 keeps the
 //                 log2-scaled logits in LDS; phase 2 forms p = 2^(z - m_chunk)
-//                 once per (head, row) and accumulates p * V.  Grouped-query
-//                 heads (G >= 4) of bf16 caches do both contractions on the
-//                 matrix cores instead.  The block's outputs (logits, chunk
+//                 once per (head, row) and accumulates p * V.  bf16 caches
+//                 with G >= 4 or G == 1 do both contractions on the matrix
+//                 cores instead.  The block's outputs (logits, chunk
 //                 max/sum, partial o) leave last, written through to memory:
 //                 writes mixed into the read stream cost the HBM far more
 //                 than their size, so the kernel writes only what Eq. 1 and
@@ -30,12 +30,12 @@
 //   k_score       one thread per live row: adds the layers' sums (layer
 //                 order) times 1/(L*H) to s.  The same code normally runs in
 //                 the next step's append launch, saving a launch per step.
-//   Deferred Eq. 1 (bf16 grouped-query heads over resident staging): no
-//                 logits are stored; the next step's k_attn_chunk recomputes
-//                 the step's weights in the padded rows of its logits tile and
-//                 writes their sum over each group's heads, and its
-//                 k_finalize folds those sums into s (k_fold64 when a
-//                 score-only pass flushes a step).
+//   Deferred Eq. 1 (the matrix-core path over resident staging): no
+//                 logits are stored; a later step's k_attn_chunk recomputes
+//                 the pending steps' weights in the padded rows of its logits
+//                 tile and writes their sum over the pending heads, and its
+//                 k_finalize folds those sums into s (k_fold when a
+//                 score-only pass applies pending steps).
 //                 No atomics anywhere, so every result is bitwise
 //                 reproducible.
 #include <hip/hip_ext.h>
@@ -193,31 +193,43 @@ __device__ __forceinline__ void score_rows(const ScoreArgs& a, int tile, int b) 
   a.s[p] += acc * a.inv_lh;
 }
 
-// Deferred Eq. 1 fold for live rows [64 tile, 64 tile + 64) of sequence b:
-// s[pos(j)] += (sum over the f.layers rows [layer][kv head] of f.layer_score)
-// * 1/(L*H).  Wave k of the block adds every fourth row of that list from
-// row k, in order, for 64 consecutive live rows (256 contiguous bytes per
-// load); the four partials are added in order.  The sums are long (layers x
-// kv heads), so one thread per row would wait on one long load chain.
-// Every thread of the block calls it.
-__device__ __forceinline__ void fold_rows64(const ScoreArgs& f, int tile, int b, float (*red)[64]) {
-  const int r = threadIdx.x & 63, k = threadIdx.x >> 6;
-  const int j = tile * 64 + r;
+// Deferred Eq. 1 fold for live rows [R tile, R tile + R) of sequence b,
+// R = 256 / P: s[pos(j)] += (sum over the f.layers rows [layer][kv head] of
+// f.layer_score) * 1/(L*H).  P partial sums per row: partial k adds every
+// P-th entry of the row's list from k, in order, and the P partials are then
+// added in order.  The lists are long (layers x kv heads), so one thread per
+// row would wait on one long load chain; P = 4 (64 rows per block, each load
+// reading 256 contiguous bytes) up to 640 entries, 16 beyond that (16 rows
+// per block, 64 entries per thread at 1024).  Every thread of the block calls it.
+template <int P>
+__device__ __forceinline__ void fold_rows(const ScoreArgs& f, int tile, int b, float* red) {
+  constexpr int R = 256 / P;
+  const int r = threadIdx.x % R, k = threadIdx.x / R;
+  const int j = tile * R + r;
   const bool live = j < f.nlive[b];
   float acc = 0.f;
   if (live) {
     const float* p = f.layer_score + (int64_t)b * f.lstride + j;
     const int64_t step = (int64_t)f.batch * f.lstride;
 #pragma unroll 16
-    for (int l = k; l < f.layers; l += 4) acc += p[l * step];
+    for (int l = k; l < f.layers; l += P) acc += p[l * step];
   }
-  red[k][r] = acc;
+  red[k * R + r] = acc;
   __syncthreads();
   if (k == 0 && live) {
-    const float t = ((red[0][r] + red[1][r]) + red[2][r]) + red[3][r];
+    float t = red[r];
+#pragma unroll
+    for (int q = 1; q < P; ++q) t += red[q * R + r];
     const int64_t pos = (int64_t)b * f.nmax + f.live_pos[(int64_t)b * f.nmax + j];
     f.s[pos] += t * f.inv_lh;
   }
+}
+
+__device__ __forceinline__ void fold_tile(const ScoreArgs& f, int tile, int b, float* red) {
+  if (f.parts == 16)
+    fold_rows<16>(f, tile, b, red);
+  else
+    fold_rows<4>(f, tile, b, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -270,17 +282,18 @@ __global__ __launch_bounds__(256) void k_append(const AppendArgs a, const ScoreA
 // positions and live indices below the new row's.
 //
 // DEF (matrix-core path, resident staging): Eq. 1 for pending steps runs
-// here instead of from stored logits.  Their queries fill the padded rows of
-// the logits tile (G..2G-1 the last pending step, 2G..3G-1 the one before it
-// when 3G <= 16), so each K tile gives every step's logits in the same MFMAs;
-// with each pending step's (M, 1/L) a row's weights are summed over the
-// group's heads (and both steps) and one value per row and kv head leaves the
-// block, in place of G logits per step.  The host asks for two steps every
-// other launch when they fit, and for none in between.  Chunk-0 blocks keep
-// this step's queries for later.
+// here instead of from stored logits.  The 16-row logits tile holds this
+// step's G query heads in rows 0..G-1; pending step s (1 = the last completed
+// step) fills rows sG..sG+G-1, up to 16/G - 1 steps.  Each K tile thus gives
+// every step's logits in the same MFMAs; with each pending step's (M, 1/L) a
+// row's weights are summed over all pending heads, and one value per row and
+// kv head leaves the block, in place of G logits per step.  The host asks for
+// 16/G - 1 steps once that many are pending (15 at G = 1, 3 at G = 4, 2 at
+// G = 5, 1 at G = 8) and for none in between.  Chunk-0 blocks keep this
+// step's queries for later.
 //
 // At least four waves per SIMD: without that bound the compiler puts the
-// matrix-core accumulators in AGPRs and, at G = 5 with two pending steps,
+// matrix-core accumulators in AGPRs and, at G = 5 with pending steps,
 // needs 132 registers, one wave fewer; with it, the same code fits in VGPRs
 // alone (no spills).  The vector path's allocation is unchanged.
 template <typename T, int D, int G, int CHUNK, bool MK, bool QT, bool DEF>
@@ -361,11 +374,16 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   if constexpr (MK) {
     // deferred Eq. 1 (DEF): prev_mode 1, the last pending step's rows are the
     // live indices below the new row's; 2, score only over every live row.
-    // With two pending steps the earlier one had one row fewer (each step
-    // appends one row per sequence and nothing leaves between reassignments).
+    // Pending step s (1 = the last completed step) had s - 1 rows fewer (each
+    // step appends one row per sequence and nothing leaves between
+    // reassignments); its queries fill tile rows sG..sG+G-1.
     const int prev = DEF ? a.prev_mode : 0;
     const int nprev = prev == 1 ? nl - 1 : nl;
-    const bool two = DEF && prev != 0 && a.prev_steps == 2;
+    const int nps = (DEF && prev != 0) ? a.prev_steps : 0;  // pending steps formed here
+    auto slot = [&](int st) {  // ring slot of pending step st (0: this step)
+      const int x = (a.qcur + 1 - st) % a.ring;
+      return x < 0 ? x + a.ring : x;
+    };
     // ---- phase 1 on the matrix cores: Z[16 heads x 16 rows] += Q[16 x 32] K^T[32 x 16],
     // D/32 steps per tile of 16 rows (v_mfma_f32_16x16x32_bf16).  Lane l feeds
     // head / row (l % 16) and the 8 elements 8*(l/16) of each 32-wide slice;
@@ -375,34 +393,31 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
     const int hl = lane & 15, kq = lane >> 4;
     bf16x8 qa[KC];
     const int64_t qrow = ((int64_t)l * a.batch + b) * a.q_heads + kvh * G;  // head 0 of the group, layer l
-    // this lane's query row of the tile: this step's head hl, a pending
-    // step's head, or none (zeros)
+    // this lane's query row of the tile: step hl / G (0: this step), head
+    // hl % G, or none (zeros)
+    const int qs = hl / G, qh = hl % G;
     const T* qsrc = nullptr;
-    if (hl < G && prev != 2)
-      qsrc = (const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + hl) * D;
-    else if (DEF && prev != 0 && hl >= G && hl < 2 * G)
-      qsrc = (const T*)a.qprev + (qrow + hl - G) * D;
-    else if (two && hl >= 2 * G && hl < 3 * G)
-      qsrc = (const T*)a.qprev2 + (qrow + hl - 2 * G) * D;
+    if (qs == 0 && prev != 2)
+      qsrc = (const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + qh) * D;
+    else if (qs >= 1 && qs <= nps)
+      qsrc = (const T*)a.qring + slot(qs) * a.qslot + (qrow + qh) * D;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const uint4 u = qsrc ? load16(qsrc + 32 * kc + 8 * kq) : make_uint4(0, 0, 0, 0);
-      if (DEF && prev != 2 && c == 0 && hl < G)
-        *reinterpret_cast<uint4*>((T*)a.qsave + (qrow + hl) * D + 32 * kc + 8 * kq) = u;
+      if (DEF && prev != 2 && c == 0 && qs == 0)
+        *reinterpret_cast<uint4*>((T*)a.qring + slot(0) * a.qslot + (qrow + qh) * D + 32 * kc + 8 * kq) = u;
       qa[kc] = as_bf16x8(u);
     }
-    // the pending steps' (M, 1/L) of the heads this lane receives: tile rows
-    // G..2G-1 the last pending step, rows 2G..3G-1 the one before it (v2)
+    // the pending steps' (M, 1/L) of the heads this lane receives (tile rows
+    // 4 kq .. 4 kq + 3: step h / G, head h % G)
     float pM[4], piL[4];
-    bool vp[4], v2[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = 4 * kq + i;
-      v2[i] = two && h >= 2 * G && h < 3 * G;
-      vp[i] = v2[i] || (DEF && prev != 0 && h >= G && h < 2 * G);
-      const float* ml = v2[i] ? a.mlprev2 + (qrow + h - 2 * G) * 2 : a.mlprev + (qrow + (vp[i] ? h - G : 0)) * 2;
-      pM[i] = vp[i] ? ml[0] : 0.f;
-      piL[i] = vp[i] ? ml[1] : 0.f;
+      const int h = 4 * kq + i, st = h / G;
+      const bool on = st >= 1 && st <= nps;
+      const float* ml = a.mlring + (on ? slot(st) * a.mlslot + (qrow + h % G) * 2 : 0);
+      pM[i] = on ? ml[0] : 0.f;
+      piL[i] = on ? ml[1] : 0.f;
     }
     float* sp = DEF ? a.spart + (((int64_t)l * a.kv_heads + kvh) * a.batch + b) * a.lstride + j0 : nullptr;
     float mx[4];
@@ -451,15 +466,15 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
           }
         }
         if (DEF && prev != 0) {
-          // sum of the pending steps' weights of row r over the group's heads:
-          // this lane's heads, then the four lanes that hold row r, in a fixed order
-          // (the earlier of two pending steps lacks the later one's new row,
-          // live index nprev - 1)
-          const bool row2 = j0 + r < nprev - 1;
+          // sum of the pending steps' weights of row r over their heads: this
+          // lane's four tile rows, then the four lanes that hold row r, in a
+          // fixed order (pending step st holds live indices < nprev - (st - 1))
           float e = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (vp[i] && (row2 || !v2[i])) e += exp2f(acc[i] * a.qscale - pM[i]) * piL[i];
+          for (int i = 0; i < 4; ++i) {
+            const int st = (4 * kq + i) / G;
+            if (st >= 1 && st <= nps && j0 + r < nprev - (st - 1)) e += exp2f(acc[i] * a.qscale - pM[i]) * piL[i];
+          }
           e += __shfl_xor(e, 16);
           e += __shfl_xor(e, 32);
           if (kq == 0) es[r] = e;
@@ -769,7 +784,7 @@ template <int D, int RPT>
 __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a, const ScoreArgs fold) {
   __shared__ float Ms[kMaxQHeads];
   __shared__ float iLs[kMaxQHeads];
-  __shared__ float fold_red[4][64];
+  __shared__ float fold_red[256];
   constexpr int TILE = 256 * RPT;
   const int tid = threadIdx.x;
   const int x = blockIdx.x, b = blockIdx.y, ll = blockIdx.z;
@@ -827,7 +842,7 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a, const Sc
       // fold tiles are dealt over the layer slices: ceil(fold_tiles / slices) per slice
       const int per = (a.fold_tiles + gridDim.z - 1) / gridDim.z;
       const int ft = ll * per + (x - tiles_grid - hblocks);
-      if (ft < a.fold_tiles) fold_rows64(fold, ft, b, fold_red);
+      if (ft < a.fold_tiles) fold_tile(fold, ft, b, fold_red);
       return;
     }
     const int h = (x - tiles_grid) * HPB + tid / TPH, ev = tid % TPH;
@@ -919,10 +934,10 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a, const Sc
 // Eq. 1 update on its own: grid (tiles, batch).
 __global__ __launch_bounds__(256) void k_score(const ScoreArgs a) { score_rows(a, blockIdx.x, blockIdx.y); }
 
-// Deferred Eq. 1 fold on its own: grid (tiles of 64 rows, batch).
-__global__ __launch_bounds__(256) void k_fold64(const ScoreArgs a) {
-  __shared__ float red[4][64];
-  fold_rows64(a, blockIdx.x, blockIdx.y, red);
+// Deferred Eq. 1 fold on its own: grid (tiles of 256 / a.parts rows, batch).
+__global__ __launch_bounds__(256) void k_fold(const ScoreArgs a) {
+  __shared__ float red[256];
+  fold_tile(a, blockIdx.x, blockIdx.y, red);
 }
 
 // Grouped-query heads (G >= 4) of bf16 caches take the matrix-core logits.
@@ -950,7 +965,9 @@ const void* attn_fn(int chunk) {
 // with 8-bit staging).
 template <typename T, int D, int G, bool QT>
 hipError_t launch_attn_t(const AttnArgs& a, const StepArgs& n, int chunk, bool vec, const AttnLaunch& L) {
-  constexpr bool MK = std::is_same<T, bf16_t>::value && G >= 4;
+  // the matrix cores for bf16 with 4 or more query heads per kv head, and with
+  // one (whose tile then has room for 15 pending steps of deferred Eq. 1)
+  constexpr bool MK = std::is_same<T, bf16_t>::value && (G >= 4 || G == 1);
   const void* fn = nullptr;
   if constexpr (MK && !QT) {
     if (vec) {
@@ -1049,8 +1066,9 @@ hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fold64(const ScoreArgs& a, int tiles64, hipStream_t s) {
-  k_fold64<<<dim3(tiles64, a.batch), 256, 0, s>>>(a);
+hipError_t launch_fold(const ScoreArgs& a, int tiles, hipStream_t s) {
+  if (a.parts != 4 && a.parts != 16) return hipErrorInvalidValue;
+  k_fold<<<dim3(tiles, a.batch), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -97,24 +97,27 @@ struct tkv {
   bool score_pending = false;
   tkvd::ScoreArgs pending_score{};
   int pending_tiles = 0;
-  // Deferred Eq. 1 (bf16 grouped-query heads on the matrix cores, resident
-  // staging): a step's weights are recomputed, from its queries and its
-  // heads' (M, 1/L), by a later step's attention launch, which streams the
-  // same K rows anyway, and folded into s by that step's merge pass.  With
-  // g <= 5 two steps' queries fit the logits tile's padded rows, so every
-  // other launch forms the last two steps' weights at once and writes one
-  // sum per row and kv head for both (pair).  A reassignment first runs a
-  // score-only pass over K for the pending steps and folds them into s; a
-  // score read folds them into a copy of s only, so that reads never change
-  // which steps are summed together.  No logits are stored.
+  // Deferred Eq. 1 (bf16 on the matrix cores, resident staging): a step's
+  // weights are recomputed, from its queries and its heads' (M, 1/L), by a
+  // later step's attention launch, which streams the same K rows anyway, and
+  // folded into s by that step's merge pass.  The logits tile has room for
+  // kmax = 16/g - 1 pending steps beside the running one, so a launch forms
+  // the pending steps' weights once kmax are pending and writes one sum per
+  // row and kv head for all of them; the launches in between form none.  A
+  // reassignment first runs a score-only pass over K for the pending steps
+  // and folds them into s; a score read folds them into a copy of s only, so
+  // that reads never change which steps are summed together.  No logits are
+  // stored.
   bool defer = false;
-  bool pair = false;                // two pending steps per launch (3 g <= 16)
-  int pend = 0;                     // steps whose weights are not in s yet (0..2)
+  int kmax = 1;                     // pending steps per forming launch
+  int pend = 0;                     // steps whose weights are not in s yet (0..kmax)
   std::vector<int32_t> prev_nlive;  // [B] live rows of the last of them
-  int qcur = 0;  // qbuf[qcur], mlbuf[qcur]: the last completed step's queries and (M, 1/L); the one
-                 // before it at (qcur + 2) % 3; the running step's go to (qcur + 1) % 3
-  void* qbuf[3] = {nullptr, nullptr, nullptr};     // [L][B][Hq][D] each
-  float* mlbuf[3] = {nullptr, nullptr, nullptr};   // [L][B][Hq][2] each
+  // rings of kmax + 1 slots: the last completed step's queries and (M, 1/L)
+  // at slot qcur, the one before it at qcur - 1 (mod ring); the running
+  // step's go to (qcur + 1) mod ring
+  int ring = 2, qcur = 0;
+  void* qring = nullptr;     // [ring][L][B][Hq][D]
+  float* mlring = nullptr;   // [ring][L][B][Hq][2]
   float* spart = nullptr;              // [L][Hkv][B][lstride]
   float* s_view = nullptr;             // [B][nmax]: s with the pending steps folded in, for reads
   std::vector<int32_t> nlive;                 // [B] live rows

@@ -70,18 +70,20 @@ struct AttnArgs {
   float qscale;              // log2(e) / sqrt(head_dim)
   int32_t layer_begin, batch, q_heads, kv_heads, nmax, max_chunks, lstride;
   // Deferred Eq. 1 (matrix-core path, resident staging): the weights of the
-  // last one or two steps (prev_steps) are recomputed from their queries
-  // while this launch streams K.
+  // last prev_steps steps are recomputed from their queries while this launch
+  // streams K.
   //   prev_mode 0: none; 1: this step's launch, the last pending step's rows
   //   are live indices < nlive - 1; 2: score only (flush), rows < nlive, no
-  //   attention.  With two steps, the earlier one has one row fewer.
+  //   attention.  Each earlier pending step has one row fewer.
+  // Queries and (M, 1/L) of recent steps sit in rings of `ring` slots: the
+  // last completed step in slot qcur, the one before it in qcur - 1 (mod
+  // ring), and so on; this step's go to slot (qcur + 1) mod ring.
   int32_t prev_mode, prev_steps;
-  const void* qprev;    // [layers][batch][q_heads][head_dim]: the last pending step's q
-  const void* qprev2;   // the same for the step before it (prev_steps 2)
-  void* qsave;          // [layers][batch][q_heads][head_dim]: this step's q, kept for later
-  const float* mlprev;  // [layers][batch][q_heads][2]: the last pending step's (M, 1/L), log2 units
-  const float* mlprev2; // the same for the step before it (prev_steps 2)
-  float* spart;         // [layers][kv_heads][batch][lstride]: sum over the group's heads of alpha
+  int32_t ring, qcur;
+  void* qring;          // [ring][layers][batch][q_heads][head_dim]
+  float* mlring;        // [ring][layers][batch][q_heads][2], log2 units
+  int64_t qslot, mlslot; // elements per slot
+  float* spart;         // [layers][kv_heads][batch][lstride]: sum over the pending heads of alpha
   int32_t nlive[kMaxBatch];
 };
 
@@ -93,7 +95,7 @@ struct FinalizeArgs {
   float* layer_score;  // [layers][batch][lstride]: sum over heads of alpha, per live index
   int32_t layer_begin, batch, q_heads, nmax, max_chunks, chunk, lstride;
   int32_t tiles_grid;  // score blocks in the grid (tiles of the longest sequence; set by the launcher)
-  float* mlprev;       // deferred Eq. 1: (M, 1/L) of every head kept for the next step, or null
+  float* mlprev;       // deferred Eq. 1: (M, 1/L) of every head kept for later steps (a ring slot), or null
   int32_t fold_tiles;  // deferred Eq. 1: tiles of the fold of `fold` run by layer-0 blocks (0: none)
   int32_t nlive[kMaxBatch];
 };
@@ -104,6 +106,7 @@ struct ScoreArgs {
   float* s;                  // [batch][nmax] by position
   float inv_lh;              // 1 / (layers * q_heads)
   int32_t layers, batch, nmax, lstride;
+  int32_t parts;             // deferred fold: partial sums per row (4, or 16 for lists over 640 rows)
   int32_t nlive[kMaxBatch];
 };
 
@@ -312,7 +315,8 @@ hipError_t launch_finalize(const FinalizeArgs& a, const ScoreArgs* fold, int fol
                            int layer_count, int max_live, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int tiles_now, hipStream_t s);
 // deferred Eq. 1 fold (a.layers rows [layer][kv head]), tiles of 64 live rows
-hipError_t launch_fold64(const ScoreArgs& a, int tiles64, hipStream_t s);
+// Deferred fold of a.layer_score into s: tiles of 256 / a.parts live rows.
+hipError_t launch_fold(const ScoreArgs& a, int tiles, hipStream_t s);
 
 // ---- launchers (move.hip) -------------------------------------------------
 hipError_t launch_place_rows(const PlaceArgs& a, int layers, hipStream_t s);
