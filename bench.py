@@ -41,7 +41,7 @@ def attention_kernel(w, args):
     caches with one query head per kv head, or four or more (unless the
     vector pass is asked for), use the matrix cores; every other shape the
     vector units."""
-    if w.dtype == "bf16" and (w.q_heads == w.kv_heads or (w.q_heads >= 4 * w.kv_heads and not args.vector_pass)):
+    if w.dtype == "bf16" and (w.q_heads == w.kv_heads or w.q_heads >= 4 * w.kv_heads) and not args.vector_pass:
         return "k_attn_chunk (split-K attention, matrix-core pass)"
     return "k_attn_chunk (split-K attention, vector pass)"
 
@@ -354,7 +354,7 @@ def main():
     ap.add_argument("--workload", default="7b")
     ap.add_argument("--chunk", type=int, default=0, help="split-K rows per work-group: 128, 256 or 512 (0: default)")
     ap.add_argument("--vector-pass", action="store_true",
-                    help="grouped-query bf16 heads on the vector units instead of the matrix cores")
+                    help="bf16 heads (one, or 4 or more, per kv head) on the vector units instead of the matrix cores")
     ap.add_argument("--stream-steps", type=int, default=64, help="timed steps of the stream-staging leg (0: skip)")
     ap.add_argument("--staging-layers", type=int, default=STAGING_LAYERS,
                     help="HBM staging slots S of the stream-staging leg (2 .. layers - 1)")

@@ -296,9 +296,9 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   } else {
     dev((void**)&t->s, B * nmax * 4);
   }
-  t->vector_pass = (o.flags & TKV_FLAG_VECTOR_PASS) != 0 && s.dtype == TKV_BF16 && group >= 4;
+  t->vector_pass = (o.flags & TKV_FLAG_VECTOR_PASS) != 0 && s.dtype == TKV_BF16 && (group >= 4 || group == 1);
   // the matrix-core path (bf16, g >= 4 or g == 1) over resident staging
-  t->defer = resident && s.dtype == TKV_BF16 && ((group >= 4 && !t->vector_pass) || group == 1);
+  t->defer = resident && s.dtype == TKV_BF16 && (group >= 4 || group == 1) && !t->vector_pass;
   if (t->defer) {
     // as many pending steps per forming launch as fit beside this step's
     // queries in the 16-row tile; a part of a handle with per-layer budgets

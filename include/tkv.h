@@ -152,11 +152,11 @@ typedef struct {
  * next to heads of large ones.  Combines with TKV_FLAG_T2_FP8.  tkv_read_t2
  * then returns kv_heads scales for K followed by kv_heads for V. */
 #define TKV_FLAG_T2_HEAD_SCALES 16ull
-/* bf16 caches with 4 or more query heads per kv head: run the split-K pass on
- * the vector units (as for fewer heads per kv head) instead of the matrix
- * cores; the logits are then stored and Eq. 1 is never deferred.  Outputs
- * agree with the matrix-core pass to rounding.  Not with an 8-bit tier in
- * stream staging (TKV_EINVAL).  No effect on other shapes. */
+/* bf16 caches with one, or 4 or more, query heads per kv head: run the
+ * split-K pass on the vector units (as for 2 heads per kv head and fp32)
+ * instead of the matrix cores; the logits are then stored and Eq. 1 is never
+ * deferred.  Outputs agree with the matrix-core pass to rounding.  Not with an
+ * 8-bit tier in stream staging (TKV_EINVAL).  No effect on other shapes. */
 #define TKV_FLAG_VECTOR_PASS 32ull
 /* Test hooks, off in normal use.  TKV_FLAG_TEST_DELAY_COPIES: stream staging
  * enqueues a bounded delay kernel (a fixed number of sleep iterations, then
@@ -254,12 +254,12 @@ int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream);
  * Eq. 1 increment of the scores (Method §2) is applied in stream order before
  * anything that reads them: it runs inside the next tkv_append's launch, or
  * first thing in tkv_reassign or tkv_read_scores on the stream given to that
- * call.  bf16 caches with 4 or more query heads per kv head and resident
- * staging (staging_layers 0 or layers) defer it further: a later step's
- * attention launch recomputes the step's weights from its queries while it
- * streams the same K rows, and that step's last layer group adds them; with 4
- * or 5 query heads per kv head every other launch does so for the last two
- * steps at once.  tkv_reassign first runs a score-only pass over K (half a
+ * call.  bf16 caches with one, or 4 or more, query heads per kv head and
+ * resident staging (staging_layers 0 or layers) defer it further: a later
+ * step's attention launch recomputes the pending steps' weights from their
+ * queries while it streams the same K rows, and that step's last layer group
+ * adds them; it does so once 16/g - 1 steps are pending (g query heads per kv
+ * head: 15 at g = 1, 3 at g = 4, 2 at g = 5, 1 at g = 8).  tkv_reassign first runs a score-only pass over K (half a
  * step's reads) for the steps still pending and adds them; tkv_read_scores
  * does the same into a copy that it returns, leaving them pending, so reads
  * never change the scores' bits.  tkv_write_scores replaces the scores and

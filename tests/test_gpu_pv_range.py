@@ -1,5 +1,6 @@
-"""The matrix-core p.V of grouped-query bf16 heads against the oracle on
-large values, and the vector pass of the same heads.
+"""The matrix-core p.V of bf16 heads (one, five or eight query heads per kv
+head) against the oracle on large values, and the vector pass of the same
+heads.
 
 Attention output is the weighted sum of the live V rows ("Not All Thoughts
 Need HBM", gist.science summary, Method §3: every live row contributes at
@@ -40,7 +41,7 @@ def _loud_v(inp, w, seed=3):
     return float(max(np.abs(tkvsynth.bf16_to_f32(inp.v0)).max(), np.abs(tkvsynth.bf16_to_f32(inp.vn)).max()))
 
 
-@pytest.mark.parametrize("heads", ["14b", "70b"])
+@pytest.mark.parametrize("heads", ["7b", "14b", "70b"])
 @pytest.mark.parametrize("staging", [0, 2], ids=["resident", "stream"])
 def test_matrix_core_pv_large_values(heads, staging):
     w = tkvsynth.CONFIGS[heads].replace(layers=3, batch=2, prefill=900, steps=40, delta=32, prompt=40, recent=32)
@@ -50,11 +51,11 @@ def test_matrix_core_pv_large_values(heads, staging):
     run_parity(w, inp, w.steps, check_every=3, staging_layers=staging)
 
 
-@pytest.mark.parametrize("heads", ["14b", "70b"])
+@pytest.mark.parametrize("heads", ["7b", "14b", "70b"])
 def test_vector_pass_grouped_query(heads):
-    """TKV_FLAG_VECTOR_PASS: the same heads on the vector units (stored
-    logits, Eq. 1 not deferred) match the oracle, and the matrix-core pass's
-    outputs to within rounding."""
+    """TKV_FLAG_VECTOR_PASS: the same heads (one, five or eight query heads
+    per kv head) on the vector units (stored logits, Eq. 1 not deferred) match
+    the oracle, and the matrix-core pass's outputs to within rounding."""
     import decode_attention_tkv_amd as tkv
     w = tkvsynth.CONFIGS[heads].replace(layers=3, batch=2, prefill=900, steps=70, delta=32, prompt=40, recent=32)
     inp = Inputs(w)
