@@ -8,8 +8,12 @@ fp64 scores (relative 1e-4) after 256 steps and at the end, with outputs
 within 5e-3 on the way and every reassignment's labels and changed-row
 lists bit-exact.
 
-  * 7B heads (32 query / 32 kv heads, head_dim 128): the vector pass, which
-    stores the logits and sums each layer's weights in its merge pass.
+  * 7B heads (32 query / 32 kv heads, head_dim 128) on the matrix cores,
+    Eq. 1 deferred up to fifteen steps (the pending steps' queries fill rows
+    1..15 of the logits tile), so a reassignment every 64 steps finds
+    pending steps of several counts; and the same heads on the vector pass
+    (TKV_FLAG_VECTOR_PASS), which stores the logits and sums each layer's
+    weights in its merge pass.
   * 14B heads (40 query / 8 kv heads): the matrix-core pass with Eq. 1
     deferred to the next step's launch (the previous step's queries ride in
     the padded rows of the logits tile).
@@ -28,6 +32,14 @@ pytestmark = pytest.mark.gpu
 def test_7b_heads_320_steps():
     w = tkvsynth.CONFIGS["7b"].replace(layers=4, prefill=2200, steps=320)
     out = run_parity(w, Inputs(w), w.steps, check_every=8, score_at=(256,))
+    assert out[5] == 5
+
+
+@pytest.mark.timeout(600)
+def test_7b_heads_vector_pass_320_steps():
+    import decode_attention_tkv_amd as tkv
+    w = tkvsynth.CONFIGS["7b"].replace(layers=4, prefill=2200, steps=320)
+    out = run_parity(w, Inputs(w), w.steps, check_every=8, score_at=(256,), extra_flags=tkv.TKV_FLAG_VECTOR_PASS)
     assert out[5] == 5
 
 
