@@ -301,10 +301,9 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   t->defer = resident && s.dtype == TKV_BF16 && (group >= 4 || group == 1) && !t->vector_pass;
   if (t->defer) {
     // as many pending steps per forming launch as fit beside this step's
-    // queries in the 16-row tile; a part of a handle with per-layer budgets
-    // takes one step per launch, so that reads may apply its pending step
-    // without changing the scores' bits
-    t->kmax = part ? 1 : 16 / group - 1;
+    // queries in the 16-row tile (the parts of a handle with per-layer
+    // budgets run in step, so they form the same steps together)
+    t->kmax = 16 / group - 1;
     t->ring = t->kmax + 1;
     dev(&t->qring, (size_t)t->ring * L * B * Hq * t->D * t->esz);
     dev((void**)&t->mlring, (size_t)t->ring * L * B * Hq * 2 * 4);
@@ -989,8 +988,10 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
 // their rows' K in every layer, then the fold, into s (commit: nothing is
 // pending afterwards) or into a copy of s that a score read returns (the
 // steps stay pending and are later formed and folded exactly as without the
-// read).
-static int flush_deferred(tkv* t, hipStream_t st, bool commit) {
+// read).  view: the copy to fold into when not committing, already holding s
+// (the parts of a handle with per-layer budgets fold into one), or nullptr
+// for this handle's own copy.
+static int flush_deferred(tkv* t, hipStream_t st, bool commit, float* view = nullptr) {
   AttnArgs a{};
   a.rows = t->rowspace();
   a.live_loc = t->live_loc;
@@ -1014,8 +1015,11 @@ static int flush_deferred(tkv* t, hipStream_t st, bool commit) {
   StepArgs none{};
   ScoreArgs fold = defer_fold_args(t);
   if (!commit) {
-    HIP_TRY(t, hipMemcpyAsync(t->s_view, t->s, (size_t)t->B * t->nmax * 4, hipMemcpyDeviceToDevice, st));
-    fold.s = t->s_view;
+    if (!view) {
+      HIP_TRY(t, hipMemcpyAsync(t->s_view, t->s, (size_t)t->B * t->nmax * 4, hipMemcpyDeviceToDevice, st));
+      view = t->s_view;
+    }
+    fold.s = view;
   }
   if (chunks > 0) {
     HIP_TRY(t, launch_attn(a, none, t->dtype, t->D, t->group, t->chunk, false, t->L, chunks, nullptr, nullptr, st));
@@ -1312,9 +1316,22 @@ static int read_scores_impl(tkv_t* t, float* scores, tkv_stream_t stream) {
   if (int rc = usable(t)) return rc;
   if (!scores) return tkv_fail(t, TKV_EINVAL, "NULL argument");
   const float* src = t->s;
-  if (!t->parts.empty()) {
-    // per-layer budgets: every part's pending increment goes into s (the parts
-    // apply one step at a time, so this changes no bits)
+  if (!t->parts.empty() && t->parts[0]->defer) {
+    // per-layer budgets with deferred Eq. 1: every part's pending steps into
+    // one copy of the shared s (the first part's), which the read returns
+    tkv* p0 = t->parts[0];
+    if (p0->pend) {
+      HIP_TRY(t, hipMemcpyAsync(p0->s_view, t->s, (size_t)t->B * t->nmax * 4, hipMemcpyDeviceToDevice,
+                                (hipStream_t)stream));
+      for (size_t i = 0; i < t->parts.size(); ++i)
+        if (t->parts[i]->pend)
+          if (int rc = part_rc(t, i, flush_deferred(t->parts[i], (hipStream_t)stream, false, p0->s_view)))
+            return rc;
+      src = p0->s_view;
+    }
+  } else if (!t->parts.empty()) {
+    // per-layer budgets with stored logits: each part's pending score launch
+    // (one step's) goes into s, as the next launch would apply it
     if (int rc = tkv_flush_score(t, (hipStream_t)stream)) return rc;
   } else if (t->defer && t->pend) {
     // the pending steps into a copy of s: they stay pending, so a read never

@@ -2,12 +2,15 @@
 are next read or ranked ("Not All Thoughts Need HBM", gist.science summary,
 Method §2): whether it runs inside the next append's launch or is applied
 for a score read, the scores are the same bits.
-For bf16 grouped-query heads over resident staging a later step's attention
-launch recomputes the step's weights (no logits are stored), two steps at a
-time when both fit the logits tile (g <= 5); a score read then forms the
-pending steps in a score-only pass over K into a copy of the scores, which
-changes nothing later, and a reassignment folds them into the scores first
-(an odd Delta leaves one step pending there, an even one two)."""
+For bf16 heads on the matrix cores over resident staging (one query head per
+kv head, or four and more) a later step's attention launch recomputes the
+step's weights (no logits are stored), as many steps at a time as fit the
+16-row logits tile beside the running step's queries (16/g - 1); a score
+read then forms the pending steps in a score-only pass over K into a copy of
+the scores, which changes nothing later, and a reassignment folds them into
+the scores first (Delta decides how many are pending there).  With per-layer
+HBM budgets every group of layers defers its own part of Eq. 1 and a read
+folds all of them into one copy."""
 import numpy as np
 import pytest
 import torch
@@ -18,9 +21,9 @@ from harness import Inputs, to_device
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, inp, read_every_step, write_at=None, groups=None, read_mid_step=False):
+def _run(w, inp, read_every_step, write_at=None, groups=None, read_mid_step=False, layer_hbm=None, **kw):
     import decode_attention_tkv_amd as tkv
-    c = tkv.TieredKV.for_workload(w)
+    c = tkv.TieredKV.for_workload(w, layer_hbm=layer_hbm, **kw)
     c.prefill(to_device(inp.k0, w.dtype), to_device(inp.v0, w.dtype))
     out = torch.empty((w.layers, w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     written = None
@@ -53,33 +56,45 @@ def _run(w, inp, read_every_step, write_at=None, groups=None, read_mid_step=Fals
 
 
 SHAPES = {
-    # one query head per kv head: the update is summed from stored logits
+    # one query head per kv head: up to 15 pending steps per forming launch
+    # (Delta 16 forms them once between reassignments, Delta 20 leaves 4)
     "7b": dict(layers=4, prefill=300, steps=40, delta=16, prompt=20, recent=16),
-    # bf16 grouped-query heads: the next step's launch recomputes the weights
+    "7b-delta20": dict(layers=4, prefill=300, steps=45, delta=20, prompt=20, recent=16),
+    # bf16 grouped-query heads (g = 5): two pending steps per forming launch
     # (or a score-only pass over K does, when the scores are read first)
     "14b": dict(layers=4, batch=2, prefill=300, steps=40, delta=16, prompt=20, recent=16),
-    # an odd Delta: reassignments find one pending step, then two, in turn
+    # an odd Delta: reassignments find other counts of pending steps
     "14b-delta7": dict(layers=4, batch=2, prefill=300, steps=40, delta=7, prompt=20, recent=16),
     # g = 8: one pending step per launch (two do not fit the tile)
     "70b": dict(layers=3, batch=2, prefill=300, steps=40, delta=16, prompt=20, recent=16),
+    # per-layer HBM budgets: three groups of layers, each deferring its part
+    "7b-layers": dict(layers=6, prefill=300, steps=45, delta=20, prompt=20, recent=16),
+    "14b-layers": dict(layers=5, batch=2, prefill=300, steps=40, delta=7, prompt=20, recent=16),
+    # the vector pass stores logits and sums each step from them
+    "7b-vector": dict(layers=4, prefill=300, steps=40, delta=16, prompt=20, recent=16),
 }
+LAYER_HBM = {"7b-layers": [0.2, 0.2, 0.5, 0.5, 0.9, 0.9], "14b-layers": [0.3, 0.3, 0.8, 0.8, 0.8]}
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_fold_placement_does_not_change_scores(name):
+    import decode_attention_tkv_amd as tkv
     w = tkvsynth.CONFIGS[name.split("-")[0]].replace(**SHAPES[name])
     inp = Inputs(w)
-    a, ta = _run(w, inp, read_every_step=False)
-    b, tb = _run(w, inp, read_every_step=True)
+    kw = dict(layer_hbm=LAYER_HBM.get(name))
+    if name.endswith("vector"):
+        kw["extra_flags"] = tkv.TKV_FLAG_VECTOR_PASS
+    a, ta = _run(w, inp, read_every_step=False, **kw)
+    b, tb = _run(w, inp, read_every_step=True, **kw)
     n = w.n_final
     assert np.array_equal(a[:, :n], b[:, :n])
     assert np.array_equal(ta[:, :n], tb[:, :n])
 
 
-@pytest.mark.parametrize("name,write_at", [("tiny", 9), ("14b", 9), ("14b", 10)])
+@pytest.mark.parametrize("name,write_at", [("tiny", 9), ("14b", 9), ("14b", 10), ("7b", 13)])
 def test_write_scores_replaces_pending_update(name, write_at):
-    """Written scores replace s with every pending update (one or two deferred
-    steps on the matrix-core path); later steps add to the written values."""
+    """Written scores replace s with every pending update (the deferred steps
+    on the matrix-core path); later steps add to the written values."""
     w = tkvsynth.CONFIGS[name].replace(prefill=64, steps=20, delta=8, prompt=min(tkvsynth.CONFIGS[name].prompt, 20),
                                        recent=min(tkvsynth.CONFIGS[name].recent, 16))
     if name == "14b":
