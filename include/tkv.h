@@ -111,9 +111,11 @@ typedef struct {
  * every layer as usual (each group runs on its own slice, in layer order, on
  * the caller's stream); tkv_read_tiers and tkv_read_deltas report layer 0's
  * group, tkv_read_layer_tiers any layer's.  hbm_ratio is then unused; one
- * distinct ratio is the same as no layer_hbm.  Deferred Eq. 1 runs one step
- * per launch.  A reassignment first applies every group's pending Eq. 1
- * increment, then re-places each group.  Not with TKV_FLAG_NO_T1 or
+ * distinct ratio is the same as no layer_hbm.  Deferred Eq. 1 defers as many
+ * steps as without groups (the groups run in step); tkv_read_scores folds
+ * every group's pending steps into one copy of the scores.  A reassignment
+ * first applies every group's pending Eq. 1 increment, then re-places each
+ * group.  Not with TKV_FLAG_NO_T1 or
  * TKV_FLAG_SHARED_HBM (TKV_EINVAL).  mem_cap_bytes is split over the groups
  * by their layer counts.  tkv_stats sums pools and traffic over the groups;
  * tier_count then counts (layer, position) rows of the batch. */
