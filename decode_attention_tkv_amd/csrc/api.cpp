@@ -301,9 +301,10 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   t->defer = resident && s.dtype == TKV_BF16 && (group >= 4 || group == 1) && !t->vector_pass;
   if (t->defer) {
     // as many pending steps per forming launch as fit beside this step's
-    // queries in the 16-row tile (the parts of a handle with per-layer
-    // budgets run in step, so they form the same steps together)
-    t->kmax = 16 / group - 1;
+    // queries in the 16-row tile and in the forming launch's extra tiles (the
+    // parts of a handle with per-layer budgets run in step, so they form the
+    // same steps together)
+    t->kmax = tkvd::defer_max_pending(group);
     t->ring = t->kmax + 1;
     dev(&t->qring, (size_t)t->ring * L * B * Hq * t->D * t->esz);
     dev((void**)&t->mlring, (size_t)t->ring * L * B * Hq * 2 * 4);

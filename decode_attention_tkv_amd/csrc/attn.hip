@@ -33,7 +33,9 @@
 //   Deferred Eq. 1 (the matrix-core path over resident staging): no
 //                 logits are stored; a later step's k_attn_chunk recomputes
 //                 the pending steps' weights in the padded rows of its logits
-//                 tile and writes their sum over the pending heads, and its
+//                 tile (and, with G >= 4, in two more tiles of pending
+//                 queries held in LDS, against the same K fragments) and
+//                 writes their sum over the pending heads, and its
 //                 k_finalize folds those sums into s (k_fold when a
 //                 score-only pass applies pending steps).
 //                 No atomics anywhere, so every result is bitwise
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(256) void k_append(const AppendArgs a, const ScoreA
 // matrix-core accumulators in AGPRs and, at G = 5 with pending steps,
 // needs 132 registers, one wave fewer; with it, the same code fits in VGPRs
 // alone (no spills).  The vector path's allocation is unchanged.
-template <typename T, int D, int G, int CHUNK, bool MK, bool QT, bool DEF>
+template <typename T, int D, int G, int CHUNK, bool MK, bool QT, bool DEF, int XT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   constexpr int LPR = D * (int)sizeof(T) / 16;  // lanes per row
@@ -328,6 +330,13 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   __shared__ float es[DEF ? CHUNK : 1];
   // matrix-core p.V: P as three bf16 terms (hi, mid, lo), G heads x CHUNK rows
   __shared__ __attribute__((aligned(16))) bf16_t pt[MK ? 3 : 1][MK ? G : 1][MK ? CHUNK : 1];
+  // deferred Eq. 1, forming launches: XT more logits tiles of pending steps,
+  // each lane's A operand (tile row l % 16, elements 32 kc + 8 (l / 16) ..+7)
+  // and each tile row's (M, 1/L)
+  constexpr int XQ = (MK && DEF) ? XT : 0;
+  constexpr int SPT = 16 / G;  // steps per tile
+  __shared__ uint4 qx[XQ ? XQ : 1][XQ ? D / 32 : 1][XQ ? 64 : 1];
+  __shared__ float2 mlx[XQ ? XQ : 1][XQ ? 16 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = lane % LPR, rg = lane / LPR;
@@ -368,6 +377,33 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   const T* newV = n.k ? (const T*)n.v + noff : poolV;
   const uint32_t* locs = a.live_loc + (int64_t)b * a.nmax + j0;
   for (int r = tid; r < CHUNK; r += 256) codes_s[r] = r < nrows ? (j0 + r == jn ? kNewRow : locs[r]) : 0u;
+  if constexpr (XQ > 0) {
+    // extra tile x, row h: head h % G of pending step SPT (x + 1) + h / G, if
+    // that step is formed here; zeros otherwise
+    const int nps = a.prev_mode != 0 ? a.prev_steps : 0;
+    const int64_t qrow = ((int64_t)l * a.batch + b) * a.q_heads + kvh * G;
+    auto slot_of = [&](int st) {
+      const int x = (a.qcur + 1 - st) % a.ring;
+      return x < 0 ? x + a.ring : x;
+    };
+    for (int i = tid; i < XQ * (D / 32) * 64; i += 256) {
+      const int x = i / ((D / 32) * 64), kc = (i / 64) % (D / 32), ln = i % 64;
+      const int h = ln & 15, st = SPT * (x + 1) + h / G;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (h < SPT * G && st <= nps)
+        u = load16((const T*)a.qring + slot_of(st) * a.qslot + (qrow + h % G) * D + 32 * kc + 8 * (ln >> 4));
+      qx[x][kc][ln] = u;
+    }
+    for (int i = tid; i < XQ * 16; i += 256) {
+      const int x = i / 16, h = i % 16, st = SPT * (x + 1) + h / G;
+      float2 m = make_float2(0.f, 0.f);
+      if (h < SPT * G && st <= nps) {
+        const float* ml = a.mlring + slot_of(st) * a.mlslot + (qrow + h % G) * 2;
+        m = make_float2(ml[0], ml[1]);
+      }
+      mlx[x][h] = m;
+    }
+  }
   __syncthreads();
 
   float mc[G];
@@ -376,7 +412,8 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
     // live indices below the new row's; 2, score only over every live row.
     // Pending step s (1 = the last completed step) had s - 1 rows fewer (each
     // step appends one row per sequence and nothing leaves between
-    // reassignments); its queries fill tile rows sG..sG+G-1.
+    // reassignments); its queries fill tile rows sG..sG+G-1 for s < 16 / G,
+    // else rows of the extra tiles (XT of them, forming launches only).
     const int prev = DEF ? a.prev_mode : 0;
     const int nprev = prev == 1 ? nl - 1 : nl;
     const int nps = (DEF && prev != 0) ? a.prev_steps : 0;  // pending steps formed here
@@ -399,7 +436,7 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
     const T* qsrc = nullptr;
     if (qs == 0 && prev != 2)
       qsrc = (const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + qh) * D;
-    else if (qs >= 1 && qs <= nps)
+    else if (qs >= 1 && qs <= nps && qs < SPT)
       qsrc = (const T*)a.qring + slot(qs) * a.qslot + (qrow + qh) * D;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
@@ -414,7 +451,7 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * kq + i, st = h / G;
-      const bool on = st >= 1 && st <= nps;
+      const bool on = st >= 1 && st <= nps && st < SPT;
       const float* ml = a.mlring + (on ? slot(st) * a.mlslot + (qrow + h % G) * 2 : 0);
       pM[i] = on ? ml[0] : 0.f;
       piL[i] = on ? ml[1] : 0.f;
@@ -473,7 +510,26 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int st = (4 * kq + i) / G;
-            if (st >= 1 && st <= nps && j0 + r < nprev - (st - 1)) e += exp2f(acc[i] * a.qscale - pM[i]) * piL[i];
+            if (st >= 1 && st <= nps && st < SPT && j0 + r < nprev - (st - 1))
+              e += exp2f(acc[i] * a.qscale - pM[i]) * piL[i];
+          }
+          if constexpr (XQ > 0) {
+            // the extra tiles: the same K fragments against queries from LDS
+#pragma unroll
+            for (int x = 0; x < XQ; ++x) {
+              f32x4 ax = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int kc = 0; kc < KC; ++kc)
+                ax = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qx[x][kc][lane]), as_bf16x8(kd[tt][kc]), ax, 0, 0, 0);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int h = 4 * kq + i, st = SPT * (x + 1) + h / G;
+                if (h < SPT * G && st <= nps && j0 + r < nprev - (st - 1)) {
+                  const float2 m = mlx[x][h];
+                  e += exp2f(ax[i] * a.qscale - m.x) * m.y;
+                }
+              }
+            }
           }
           e += __shfl_xor(e, 16);
           e += __shfl_xor(e, 32);
@@ -949,12 +1005,12 @@ struct AttnLaunch {
   hipStream_t s;
 };
 
-template <typename T, int D, int G, bool QT, bool DEF, bool MK>
+template <typename T, int D, int G, bool QT, bool DEF, bool MK, int XT = 0>
 const void* attn_fn(int chunk) {
   switch (chunk) {
-    case 128: return (const void*)&k_attn_chunk<T, D, G, 128, MK, QT, DEF>;
-    case 256: return (const void*)&k_attn_chunk<T, D, G, 256, MK, QT, DEF>;
-    case 512: return (const void*)&k_attn_chunk<T, D, G, 512, MK, QT, DEF>;
+    case 128: return (const void*)&k_attn_chunk<T, D, G, 128, MK, QT, DEF, XT>;
+    case 256: return (const void*)&k_attn_chunk<T, D, G, 256, MK, QT, DEF, XT>;
+    case 512: return (const void*)&k_attn_chunk<T, D, G, 512, MK, QT, DEF, XT>;
     default: return nullptr;
   }
 }
@@ -974,7 +1030,15 @@ hipError_t launch_attn_t(const AttnArgs& a, const StepArgs& n, int chunk, bool v
       if (a.spart) return hipErrorInvalidValue;
       fn = attn_fn<T, D, G, QT, false, false>(chunk);
     } else {
-      fn = a.spart ? attn_fn<T, D, G, QT, true, true>(chunk) : attn_fn<T, D, G, QT, false, true>(chunk);
+      // launches that form pending steps (or score them only) take the
+      // form with the extra logits tiles; the others the lean one
+      constexpr int XT = defer_extra_tiles(G);
+      if (!a.spart)
+        fn = attn_fn<T, D, G, QT, false, true>(chunk);
+      else if (a.prev_mode != 0)
+        fn = attn_fn<T, D, G, QT, true, true, XT>(chunk);
+      else
+        fn = attn_fn<T, D, G, QT, true, true, 0>(chunk);
     }
   } else {
     if (a.spart || (vec && MK)) return hipErrorInvalidValue;

@@ -100,10 +100,12 @@ struct tkv {
   // Deferred Eq. 1 (bf16 on the matrix cores, resident staging): a step's
   // weights are recomputed, from its queries and its heads' (M, 1/L), by a
   // later step's attention launch, which streams the same K rows anyway, and
-  // folded into s by that step's merge pass.  The logits tile has room for
-  // kmax = 16/g - 1 pending steps beside the running one, so a launch forms
-  // the pending steps' weights once kmax are pending and writes one sum per
-  // row and kv head for all of them; the launches in between form none.  A
+  // folded into s by that step's merge pass.  The logits tile and the
+  // forming launch's extra tiles have room for kmax = defer_max_pending(g)
+  // pending steps beside the running one (15 at g = 1, 11 at g = 4, 8 at
+  // g = 5, 5 at g = 8), so a launch forms the pending steps' weights once
+  // kmax are pending and writes one sum per row and kv head for all of them;
+  // the launches in between form none.  A
   // reassignment first runs a score-only pass over K for the pending steps
   // and folds them into s; a score read folds them into a copy of s only, so
   // that reads never change which steps are summed together.  No logits are

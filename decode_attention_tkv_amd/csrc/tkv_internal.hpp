@@ -60,6 +60,16 @@ __host__ __device__ inline int64_t q_scale_at(const RowSpace& r, int l, int b, u
 // chunk's stores start on a line boundary.
 constexpr int kLogitAlign = 64;
 
+// Deferred Eq. 1 on the matrix cores: a 16-row logits tile holds 16 / g
+// steps' query heads (g per step).  The running step's tile holds it and
+// 16 / g - 1 pending steps; a launch that forms pending steps (or a
+// score-only pass) adds defer_extra_tiles(g) more tiles of 16 / g pending
+// steps each, their queries staged in LDS, so that with few steps per tile
+// the weight sums are still written only once per several steps.
+constexpr int defer_steps_per_tile(int g) { return 16 / g; }
+constexpr int defer_extra_tiles(int g) { return g >= 4 ? 2 : 0; }
+constexpr int defer_max_pending(int g) { return defer_steps_per_tile(g) * (1 + defer_extra_tiles(g)) - 1; }
+
 struct AttnArgs {
   RowSpace rows;
   const uint32_t* live_loc;  // [batch][nmax] loc code of live index j (ascending position)

@@ -260,8 +260,10 @@ int tkv_append(tkv_t* t, const void* k, const void* v, tkv_stream_t stream);
  * resident staging (staging_layers 0 or layers) defer it further: a later
  * step's attention launch recomputes the pending steps' weights from their
  * queries while it streams the same K rows, and that step's last layer group
- * adds them; it does so once 16/g - 1 steps are pending (g query heads per kv
- * head: 15 at g = 1, 3 at g = 4, 2 at g = 5, 1 at g = 8).  tkv_reassign first runs a score-only pass over K (half a
+ * adds them; it does so once 15 steps are pending at g = 1 (g query heads per
+ * kv head), 11 at g = 4, 8 at g = 5 and 5 at g = 8 (the running step's logits
+ * tile holds 16/g - 1 of them, and a forming launch adds two tiles of 16/g
+ * steps each at g >= 4).  tkv_reassign first runs a score-only pass over K (half a
  * step's reads) for the steps still pending and adds them; tkv_read_scores
  * does the same into a copy that it returns, leaving them pending, so reads
  * never change the scores' bits.  tkv_write_scores replaces the scores and

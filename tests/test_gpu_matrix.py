@@ -46,14 +46,16 @@ def test_most_query_heads():
     run_parity(w, Inputs(w), w.steps)
 
 
-@pytest.mark.parametrize("group,delta", [(4, 5), (5, 7), (8, 5)])
+@pytest.mark.parametrize("group,delta", [(4, 5), (4, 13), (5, 7), (5, 11), (8, 5), (8, 7)])
 def test_deferred_pairs_odd_delta(group, delta):
-    """The matrix-core path over resident staging forms Eq. 1 of the last two
-    steps together every other launch when both fit the logits tile (g <= 5;
-    g = 8 one step per launch).  With an odd Delta the reassignments find one
-    pending step and two in turn, and the scores read at every step come from
-    a copy; scores, outputs and labels still follow the oracle (Method §2 and
-    §4)."""
+    """The matrix-core path over resident staging forms Eq. 1 of several
+    pending steps together in one launch (11 at g = 4, 8 at g = 5, 5 at g = 8:
+    16/g - 1 of them in the running step's logits tile, the rest in two extra
+    tiles).  A Delta below that count leaves every step pending until the
+    reassignment's score-only pass; a larger one prime to the cadence has
+    forming launches and finds a different count pending at each
+    reassignment.  The scores read at every step come from a copy; scores,
+    outputs and labels still follow the oracle (Method §2 and §4)."""
     w = tkvsynth.CONFIGS["tiny"].replace(dtype="bf16", head_dim=128, kv_heads=2, q_heads=2 * group, layers=3,
                                          batch=2, prefill=400, steps=3 * delta + 2, delta=delta, prompt=16,
                                          recent=24, hbm_ratio=0.4, evict_ratio=0.05)

@@ -116,9 +116,9 @@ def test_random_scored_prefill(i):
 @pytest.mark.parametrize("i", range(24))
 def test_random_odd_delta(i):
     """Draws with an odd Delta (5, 7, 9 or 11), so that on the paths that
-    defer Eq. 1 two steps at a time (bf16, 4 or 5 query heads per kv head,
-    resident staging) the reassignments find one pending step and then two in
-    turn; every other path runs them as usual (Method §4)."""
+    defer Eq. 1 several steps at a time (bf16, one or 4 and more query heads
+    per kv head, resident staging) the reassignments find different counts of
+    pending steps in turn; every other path runs them as usual (Method §4)."""
     w, staging, chunk, calls, groups, static = _draw(200 + i)
     r = np.random.default_rng(7000 + i)
     delta = int(r.choice([5, 7, 9, 11]))

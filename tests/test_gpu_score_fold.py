@@ -5,7 +5,8 @@ for a score read, the scores are the same bits.
 For bf16 heads on the matrix cores over resident staging (one query head per
 kv head, or four and more) a later step's attention launch recomputes the
 step's weights (no logits are stored), as many steps at a time as fit the
-16-row logits tile beside the running step's queries (16/g - 1); a score
+16-row logits tile beside the running step's queries (16/g - 1), and with
+four and more query heads per kv head two more tiles of 16/g steps; a score
 read then forms the pending steps in a score-only pass over K into a copy of
 the scores, which changes nothing later, and a reassignment folds them into
 the scores first (Delta decides how many are pending there).  With per-layer
@@ -60,12 +61,13 @@ SHAPES = {
     # (Delta 16 forms them once between reassignments, Delta 20 leaves 4)
     "7b": dict(layers=4, prefill=300, steps=40, delta=16, prompt=20, recent=16),
     "7b-delta20": dict(layers=4, prefill=300, steps=45, delta=20, prompt=20, recent=16),
-    # bf16 grouped-query heads (g = 5): two pending steps per forming launch
+    # bf16 grouped-query heads (g = 5): eight pending steps per forming launch
     # (or a score-only pass over K does, when the scores are read first)
     "14b": dict(layers=4, batch=2, prefill=300, steps=40, delta=16, prompt=20, recent=16),
     # an odd Delta: reassignments find other counts of pending steps
     "14b-delta7": dict(layers=4, batch=2, prefill=300, steps=40, delta=7, prompt=20, recent=16),
-    # g = 8: one pending step per launch (two do not fit the tile)
+    # g = 8: five pending steps per forming launch (one in the running step's
+    # tile, two in each extra tile)
     "70b": dict(layers=3, batch=2, prefill=300, steps=40, delta=16, prompt=20, recent=16),
     # per-layer HBM budgets: three groups of layers, each deferring its part
     "7b-layers": dict(layers=6, prefill=300, steps=45, delta=20, prompt=20, recent=16),
