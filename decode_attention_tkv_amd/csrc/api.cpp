@@ -975,6 +975,8 @@ static int launch_layers(tkv* t, int lb, int lc, const void* q, float* out, int 
   int fold_tiles = 0;
   if (t->defer) {
     f.mlprev = t->mlring + (size_t)((t->qcur + 1) % t->ring) * t->L * t->B * t->Hq * 2;
+    f.q = q;
+    f.qsave = (char*)t->qring + (size_t)((t->qcur + 1) % t->ring) * t->L * t->B * t->Hq * t->D * t->esz;
     if (now && lb + lc == t->L) {
       fold = defer_fold_args(t);
       fold_tiles = prev_tiles(t);

@@ -376,33 +376,80 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   const T* newK = n.k ? (const T*)n.k + noff : poolK;
   const T* newV = n.k ? (const T*)n.v + noff : poolV;
   const uint32_t* locs = a.live_loc + (int64_t)b * a.nmax + j0;
-  for (int r = tid; r < CHUNK; r += 256) codes_s[r] = r < nrows ? (j0 + r == jn ? kNewRow : locs[r]) : 0u;
+  // Set-up: every global load of the block is issued before the first LDS
+  // store, so their latencies overlap (a store that waits on its load ahead
+  // of the next load would serialise them): the chunk's location codes and,
+  // on the matrix cores, the tile's queries, the pending steps' (M, 1/L) and
+  // the extra tiles' queries.
+  constexpr int CPT = (CHUNK + 255) / 256;  // codes per thread
+  uint32_t cr[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int r = tid + 256 * k;
+    cr[k] = (r < CHUNK && r < nrows) ? (j0 + r == jn ? kNewRow : locs[r]) : 0u;
+  }
+  // matrix cores: lane l feeds tile row l % 16 (pending step (l % 16) / G,
+  // 0 = this step, head (l % 16) % G; zeros past the steps formed here) and
+  // receives rows 4 (l / 16) .. +3
+  constexpr int KQ = MK ? D / 32 : 1;
+  const int mprev = (MK && DEF) ? a.prev_mode : 0;
+  const int mnps = mprev != 0 ? a.prev_steps : 0;  // pending steps formed here
+  auto slot = [&](int st) {  // ring slot of pending step st (0: this step)
+    const int x = (a.qcur + 1 - st) % a.ring;
+    return x < 0 ? x + a.ring : x;
+  };
+  const int64_t qrow = ((int64_t)l * a.batch + b) * a.q_heads + kvh * G;  // head 0 of the group, layer l
+  uint4 qu[KQ];
+  float pM[4], piL[4];
+  if constexpr (MK) {
+    const int hl = lane & 15, kq = lane >> 4, qs = hl / G, qh = hl % G;
+    const T* qsrc = nullptr;
+    if (qs == 0 && mprev != 2)
+      qsrc = (const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + qh) * D;
+    else if (qs >= 1 && qs <= mnps && qs < SPT)
+      qsrc = (const T*)a.qring + slot(qs) * a.qslot + (qrow + qh) * D;
+#pragma unroll
+    for (int kc = 0; kc < KQ; ++kc) qu[kc] = qsrc ? load16(qsrc + 32 * kc + 8 * kq) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * kq + i, st = h / G;
+      const bool on = st >= 1 && st <= mnps && st < SPT;
+      const float* ml = a.mlring + (on ? slot(st) * a.mlslot + (qrow + h % G) * 2 : 0);
+      pM[i] = on ? ml[0] : 0.f;
+      piL[i] = on ? ml[1] : 0.f;
+    }
+  }
+  // extra tile x, row h: head h % G of pending step SPT (x + 1) + h / G, if
+  // that step is formed here; zeros otherwise
+  constexpr int XPT = XQ ? (XQ * (D / 32) * 64 + 255) / 256 : 1;  // A-operand pieces per thread
+  uint4 xr[XPT];
+  float2 xm = make_float2(0.f, 0.f);
   if constexpr (XQ > 0) {
-    // extra tile x, row h: head h % G of pending step SPT (x + 1) + h / G, if
-    // that step is formed here; zeros otherwise
-    const int nps = a.prev_mode != 0 ? a.prev_steps : 0;
-    const int64_t qrow = ((int64_t)l * a.batch + b) * a.q_heads + kvh * G;
-    auto slot_of = [&](int st) {
-      const int x = (a.qcur + 1 - st) % a.ring;
-      return x < 0 ? x + a.ring : x;
-    };
-    for (int i = tid; i < XQ * (D / 32) * 64; i += 256) {
+#pragma unroll
+    for (int k = 0; k < XPT; ++k) {
+      const int i = tid + 256 * k;
       const int x = i / ((D / 32) * 64), kc = (i / 64) % (D / 32), ln = i % 64;
       const int h = ln & 15, st = SPT * (x + 1) + h / G;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (h < SPT * G && st <= nps)
-        u = load16((const T*)a.qring + slot_of(st) * a.qslot + (qrow + h % G) * D + 32 * kc + 8 * (ln >> 4));
-      qx[x][kc][ln] = u;
+      xr[k] = make_uint4(0, 0, 0, 0);
+      if (i < XQ * (D / 32) * 64 && h < SPT * G && st <= mnps)
+        xr[k] = load16((const T*)a.qring + slot(st) * a.qslot + (qrow + h % G) * D + 32 * kc + 8 * (ln >> 4));
     }
-    for (int i = tid; i < XQ * 16; i += 256) {
-      const int x = i / 16, h = i % 16, st = SPT * (x + 1) + h / G;
-      float2 m = make_float2(0.f, 0.f);
-      if (h < SPT * G && st <= nps) {
-        const float* ml = a.mlring + slot_of(st) * a.mlslot + (qrow + h % G) * 2;
-        m = make_float2(ml[0], ml[1]);
-      }
-      mlx[x][h] = m;
+    const int x = tid / 16, h = tid % 16, st = SPT * (x + 1) + h / G;
+    if (tid < XQ * 16 && h < SPT * G && st <= mnps) {
+      const float* ml = a.mlring + slot(st) * a.mlslot + (qrow + h % G) * 2;
+      xm = make_float2(ml[0], ml[1]);
     }
+  }
+#pragma unroll
+  for (int k = 0; k < CPT; ++k)
+    if (tid + 256 * k < CHUNK) codes_s[tid + 256 * k] = cr[k];
+  if constexpr (XQ > 0) {
+#pragma unroll
+    for (int k = 0; k < XPT; ++k) {
+      const int i = tid + 256 * k;
+      if (i < XQ * (D / 32) * 64) qx[i / ((D / 32) * 64)][(i / 64) % (D / 32)][i % 64] = xr[k];
+    }
+    if (tid < XQ * 16) mlx[tid / 16][tid % 16] = xm;
   }
   __syncthreads();
 
@@ -414,13 +461,9 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
     // step appends one row per sequence and nothing leaves between
     // reassignments); its queries fill tile rows sG..sG+G-1 for s < 16 / G,
     // else rows of the extra tiles (XT of them, forming launches only).
-    const int prev = DEF ? a.prev_mode : 0;
+    const int prev = mprev;
     const int nprev = prev == 1 ? nl - 1 : nl;
-    const int nps = (DEF && prev != 0) ? a.prev_steps : 0;  // pending steps formed here
-    auto slot = [&](int st) {  // ring slot of pending step st (0: this step)
-      const int x = (a.qcur + 1 - st) % a.ring;
-      return x < 0 ? x + a.ring : x;
-    };
+    const int nps = mnps;
     // ---- phase 1 on the matrix cores: Z[16 heads x 16 rows] += Q[16 x 32] K^T[32 x 16],
     // D/32 steps per tile of 16 rows (v_mfma_f32_16x16x32_bf16).  Lane l feeds
     // head / row (l % 16) and the 8 elements 8*(l/16) of each 32-wide slice;
@@ -428,34 +471,11 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
     constexpr int KC = D / 32;
     constexpr int TILES = RPW / 16;
     const int hl = lane & 15, kq = lane >> 4;
+    // the tile's queries (loaded in the set-up) and, in pM / piL, the pending
+    // steps' (M, 1/L) of the tile rows this lane receives
     bf16x8 qa[KC];
-    const int64_t qrow = ((int64_t)l * a.batch + b) * a.q_heads + kvh * G;  // head 0 of the group, layer l
-    // this lane's query row of the tile: step hl / G (0: this step), head
-    // hl % G, or none (zeros)
-    const int qs = hl / G, qh = hl % G;
-    const T* qsrc = nullptr;
-    if (qs == 0 && prev != 2)
-      qsrc = (const T*)a.q + (((int64_t)ll * a.batch + b) * a.q_heads + kvh * G + qh) * D;
-    else if (qs >= 1 && qs <= nps && qs < SPT)
-      qsrc = (const T*)a.qring + slot(qs) * a.qslot + (qrow + qh) * D;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const uint4 u = qsrc ? load16(qsrc + 32 * kc + 8 * kq) : make_uint4(0, 0, 0, 0);
-      if (DEF && prev != 2 && c == 0 && qs == 0)
-        *reinterpret_cast<uint4*>((T*)a.qring + slot(0) * a.qslot + (qrow + qh) * D + 32 * kc + 8 * kq) = u;
-      qa[kc] = as_bf16x8(u);
-    }
-    // the pending steps' (M, 1/L) of the heads this lane receives (tile rows
-    // 4 kq .. 4 kq + 3: step h / G, head h % G)
-    float pM[4], piL[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * kq + i, st = h / G;
-      const bool on = st >= 1 && st <= nps && st < SPT;
-      const float* ml = a.mlring + (on ? slot(st) * a.mlslot + (qrow + h % G) * 2 : 0);
-      pM[i] = on ? ml[0] : 0.f;
-      piL[i] = on ? ml[1] : 0.f;
-    }
+    for (int kc = 0; kc < KC; ++kc) qa[kc] = as_bf16x8(qu[kc]);
     float* sp = DEF ? a.spart + (((int64_t)l * a.kv_heads + kvh) * a.batch + b) * a.lstride + j0 : nullptr;
     float mx[4];
 #pragma unroll
@@ -903,6 +923,13 @@ __global__ __launch_bounds__(256) void k_finalize(const FinalizeArgs a, const Sc
     }
     const int h = (x - tiles_grid) * HPB + tid / TPH, ev = tid % TPH;
     if (h >= a.q_heads || nl == 0) return;
+    if (a.qsave && ev < D / 8) {
+      // deferred Eq. 1: the head's query row into the ring, for the later
+      // launches that form this step's weights (bf16, 16 B per thread)
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
+                                                        (((int64_t)ll * a.batch + b) * a.q_heads + h) * D);
+      reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.qsave) + (hbase + h) * D)[ev] = src[ev];
+    }
     const float* ml = a.part_ml + (hbase + h) * a.max_chunks * 2;
     const outv* po = reinterpret_cast<const outv*>(a.part_o + (hbase + h) * a.max_chunks * D) + ev;
     outv acc = {};

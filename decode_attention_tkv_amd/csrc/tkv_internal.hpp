@@ -87,7 +87,8 @@ struct AttnArgs {
   //   attention.  Each earlier pending step has one row fewer.
   // Queries and (M, 1/L) of recent steps sit in rings of `ring` slots: the
   // last completed step in slot qcur, the one before it in qcur - 1 (mod
-  // ring), and so on; this step's go to slot (qcur + 1) mod ring.
+  // ring), and so on; the merge pass puts this step's in slot
+  // (qcur + 1) mod ring.
   int32_t prev_mode, prev_steps;
   int32_t ring, qcur;
   void* qring;          // [ring][layers][batch][q_heads][head_dim]
@@ -106,6 +107,8 @@ struct FinalizeArgs {
   int32_t layer_begin, batch, q_heads, nmax, max_chunks, chunk, lstride;
   int32_t tiles_grid;  // score blocks in the grid (tiles of the longest sequence; set by the launcher)
   float* mlprev;       // deferred Eq. 1: (M, 1/L) of every head kept for later steps (a ring slot), or null
+  const void* q;       // deferred Eq. 1: the step's queries [layer_count][batch][q_heads][head_dim] (bf16)
+  void* qsave;         // deferred Eq. 1: their ring slot [layers][batch][q_heads][head_dim], or null
   int32_t fold_tiles;  // deferred Eq. 1: tiles of the fold of `fold` run by layer-0 blocks (0: none)
   int32_t nlive[kMaxBatch];
 };
