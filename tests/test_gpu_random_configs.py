@@ -166,3 +166,42 @@ def test_random_layer_budgets(i):
     w, layer_hbm, staging, calls = _draw_layers(i)
     st, o, n_reassign = run_layers(w, layer_hbm, staging_layers=staging, calls=calls, check_every=3)
     assert n_reassign == w.steps // w.delta
+
+
+def _draw_deferral(i):
+    """A bf16 workload on the matrix-core path over resident staging (one, 4, 5
+    or 8 query heads per kv head), with a Delta that leaves every count of
+    pending steps at some reassignment (15 formed together at g = 1, 11 at
+    g = 4, 8 at g = 5, 5 at g = 8), scores read against the oracle at random
+    steps between reassignments (a read folds the pending steps into a copy),
+    and the calls of a step drawn as in the general draws."""
+    r = np.random.default_rng(11000 + i)
+    group = int(r.choice([1, 4, 5, 8]))
+    kv_heads = int(r.choice([1, 2]))
+    layers = int(r.integers(1, 5))
+    delta = int(r.choice([6, 9, 12, 17, 20]))
+    steps = int(r.integers(2, 4)) * delta + int(r.integers(0, delta))
+    prefill = int(r.integers(40, 400))
+    w = tkvsynth.CONFIGS["tiny"].replace(
+        name="deferral%d" % i, dtype="bf16", head_dim=int(r.choice([64, 128])), kv_heads=kv_heads,
+        q_heads=kv_heads * group, layers=layers, batch=int(r.integers(1, 4)), prefill=prefill, steps=steps,
+        delta=delta, hbm_ratio=float(np.round(r.uniform(0.1, 0.9), 2)),
+        evict_ratio=float(np.round(r.uniform(0.0, 0.4), 2)), t2_ratio=float(r.choice([0.0, 0.1])),
+        prompt=int(r.integers(0, min(prefill, 48) + 1)), sinks=int(r.integers(0, 6)), recent=int(r.integers(0, 40)),
+        seed=int(r.integers(0, 1 << 20)))
+    calls = str(r.choice(["two", "one", "groups"])) if layers > 1 else str(r.choice(["two", "one"]))
+    groups = None
+    if calls == "groups":
+        cut = sorted(r.choice(np.arange(1, layers), size=int(r.integers(1, layers)), replace=False).tolist())
+        groups = [b - a for a, b in zip([0] + cut, cut + [layers])]
+    score_at = tuple(sorted(set(int(x) for x in r.integers(1, steps + 1, 3))))
+    return w, calls, groups, score_at
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_deferral(i):
+    w, calls, groups, score_at = _draw_deferral(i)
+    print("[deferral %d] %s calls %s %s scores at %s" % (i, w, calls, groups, score_at), flush=True)
+    outs, s, tiers, st, o, n_reassign = run_parity(w, Inputs(w), w.steps, check_every=2, calls=calls, groups=groups,
+                                                   score_at=score_at)
+    assert n_reassign == w.steps // w.delta
