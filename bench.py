@@ -194,9 +194,9 @@ def summarize_pmc(fetch_dir, write_dir):
     kv = sum((w.prefill + 1 + t) * w.kv_bytes_per_token() * w.batch for t in range(n_disp)) / n_disp
     lines = ["# k_attn_chunk HBM traffic, 7b workload (rocprofv3 counters)", "",
              "Commands (one MI355X, repo root; each counter in its own run):", "",
-             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o pmc -- python bench.py --pmc-probe",
-             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o pmc -- python bench.py --pmc-probe",
-             "    python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write", "",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o pmc -- python bench.py --pmc-probe" % fetch_dir,
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o pmc -- python bench.py --pmc-probe" % write_dir,
+             "    python bench.py --summarize-pmc %s %s" % (fetch_dir, write_dir), "",
              "`--pmc-probe` runs 8 warmup + 24 decode steps of the 7b workload, then one plain 1 GiB device",
              "copy (torch copy_) whose counter reading scales KiB to bytes (factor = 1 GiB / counted).", "",
              "| Counter | attention dispatches | mean KiB / dispatch | copy KiB (1 GiB copy) | scale | bytes / launch |",
