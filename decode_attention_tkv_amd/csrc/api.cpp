@@ -193,10 +193,18 @@ static int create_impl(const tkv_shape* shape, int32_t delta, double hbm_ratio, 
   tkv_options o{};
   if (opts) o = *opts;
   if (!ratio_ok(o.t2_ratio)) return tkv_fail(nullptr, TKV_EINVAL, "t2_ratio must be in [0, 1]");
-  // grouped-query heads (q_heads >= 4 kv_heads) move more partials per row: larger chunks
-  if (o.chunk == 0) o.chunk = (s.q_heads >= 4 * s.kv_heads) ? 512 : 256;
-  if (o.chunk != 128 && o.chunk != 256 && o.chunk != 512)
-    return tkv_fail(nullptr, TKV_EINVAL, "chunk must be 128, 256 or 512");
+  // grouped-query heads (q_heads >= 4 kv_heads) write more partials per row
+  // read, so they take larger chunks: 1024 rows on the matrix cores (bf16),
+  // whose logits tile needs no LDS for P, 512 on the vector path
+  if (o.chunk == 0) {
+    const bool mk = s.dtype == TKV_BF16 && (o.flags & TKV_FLAG_VECTOR_PASS) == 0;
+    o.chunk = s.q_heads >= 4 * s.kv_heads ? (mk ? 1024 : 512) : 256;
+  }
+  if (o.chunk != 128 && o.chunk != 256 && o.chunk != 512 && o.chunk != 1024)
+    return tkv_fail(nullptr, TKV_EINVAL, "chunk must be 128, 256, 512 or 1024");
+  if (o.chunk == 1024 && !(s.dtype == TKV_BF16 && (s.q_heads == s.kv_heads || s.q_heads >= 4 * s.kv_heads) &&
+                           (o.flags & TKV_FLAG_VECTOR_PASS) == 0))
+    return tkv_fail(nullptr, TKV_EINVAL, "chunk 1024 needs the matrix-core path (bf16, 1 or >= 4 query heads per kv head)");
   if (o.mem_cap_bytes < 0) return tkv_fail(nullptr, TKV_EINVAL, "mem_cap_bytes must be >= 0");
   if (o.staging_layers < 0 || o.staging_layers == 1)
     return tkv_fail(nullptr, TKV_EINVAL, "staging_layers must be 0 or >= 2");

@@ -318,7 +318,7 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   // per-wave partial outputs reuse their space once p is formed (one more
   // work-group per CU at G = 8)
   constexpr bool OSUM_IN_ZS = DEF && NW * D <= CHUNK;
-  __shared__ float zs_store[G * CHUNK + (OSUM_IN_ZS ? 0 : NW * G * D)];
+  __shared__ __attribute__((aligned(16))) float zs_store[G * CHUNK + (OSUM_IN_ZS ? 0 : NW * G * D)];
   float (*zs)[CHUNK] = reinterpret_cast<float (*)[CHUNK]>(zs_store);
   float (*osum)[G][D] = reinterpret_cast<float (*)[G][D]>(zs_store + (OSUM_IN_ZS ? 0 : G * CHUNK));
   __shared__ float ps[MK ? 1 : G][MK ? 1 : CHUNK];     // p = 2^(z - m) of the vector path
@@ -328,8 +328,9 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   // here until the block's last barrier is behind it (a global store ahead of
   // a barrier holds the wave there until the store is acknowledged)
   __shared__ float es[DEF ? CHUNK : 1];
-  // matrix-core p.V: P as three bf16 terms (hi, mid, lo), G heads x CHUNK rows
-  __shared__ __attribute__((aligned(16))) bf16_t pt[MK ? 3 : 1][MK ? G : 1][MK ? CHUNK : 1];
+  // matrix-core p.V: each wave's sums of p per head (the lanes form p from
+  // the logits as they build the MFMA operands)
+  __shared__ float redL[MK ? NW : 1][MK ? G : 1];
   // deferred Eq. 1, forming launches: XT more logits tiles of pending steps,
   // each lane's A operand (tile row l % 16, elements 32 kc + 8 (l / 16) ..+7)
   // and each tile row's (M, 1/L)
@@ -634,38 +635,26 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   // ---- p = 2^(z - m) and the chunk sums.  The logits go out at the very end:
   // a global store ahead of a barrier would hold every wave at that barrier
   // until the store is acknowledged.
-  float ls[G];
+  if constexpr (!MK) {
+    float ls[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    ls[g] = 0.f;
-    for (int r = tid; r < CHUNK; r += 256) {
-      float p = 0.f;
-      if (r < nrows) p = exp2f(zs[g][r] - mc[g]);
-      if constexpr (MK) {
-        // p = hi + mid + lo, each a bf16 value (each term takes the next 8 of
-        // p's 24 significant bits; the remainders are exact in fp32), so the
-        // bf16 matrix cores weigh V by p itself, as the vector path does
-        const uint32_t hi = bf16_bits(p);
-        const float r1 = p - __uint_as_float(hi << 16);
-        const uint32_t mid = bf16_bits(r1);
-        const uint32_t lo = bf16_bits(r1 - __uint_as_float(mid << 16));
-        pt[0][g][r] = (bf16_t)hi;
-        pt[1][g][r] = (bf16_t)mid;
-        pt[2][g][r] = (bf16_t)lo;
-        ls[g] += p;
-      } else {
+    for (int g = 0; g < G; ++g) {
+      ls[g] = 0.f;
+      for (int r = tid; r < CHUNK; r += 256) {
+        float p = 0.f;
+        if (r < nrows) p = exp2f(zs[g][r] - mc[g]);
         ps[g][r] = p;
         ls[g] += p;
       }
     }
-  }
-  // all reads of red[] (maxima) and of zs (when osum reuses it) are done
-  // before either is written again below
-  __syncthreads();
+    // all reads of red[] (maxima) and of zs (when osum reuses it) are done
+    // before either is written again below
+    __syncthreads();
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float s = group_sum<64>(ls[g]);
-    if (lane == 0) red[wave][g] = s;
+    for (int g = 0; g < G; ++g) {
+      const float s = group_sum<64>(ls[g]);
+      if (lane == 0) red[wave][g] = s;
+    }
   }
 
   // ---- phase 2: o = sum_r p_r * v_r
@@ -688,6 +677,7 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
     f32x4 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;  // this lane's p of head hl, over its rows
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
       const int rb = wave * RPW + st * 32 + 8 * kq;
@@ -706,10 +696,34 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
           vr[i] = ok ? load16nt(p) : make_uint4(0, 0, 0, 0);
         }
       }
+      // P of head hl, rows rb..rb+7: p = 2^(z - m) = hi + mid + lo, each a
+      // bf16 value (each term takes the next 8 of p's 24 significant bits; the
+      // remainders are exact in fp32), so the bf16 matrix cores weigh V by p
+      // itself, as the vector path does.  Each (head, row) is formed by one
+      // lane only, which also adds p to its head's sum.
+      uint32_t pw[3][4] = {};
+      if (hl < G) {
+        float mh = mc[0];
+#pragma unroll
+        for (int g = 1; g < G; ++g) mh = hl == g ? mc[g] : mh;
+        const f32x4 z0 = *reinterpret_cast<const f32x4*>(&zs[hl][rb]);
+        const f32x4 z1 = *reinterpret_cast<const f32x4*>(&zs[hl][rb + 4]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = rb + i < nrows ? exp2f((i < 4 ? z0[i] : z1[i - 4]) - mh) : 0.f;
+          const uint32_t hi = bf16_bits(p);
+          const float r1 = p - __uint_as_float(hi << 16);
+          const uint32_t mid = bf16_bits(r1);
+          const uint32_t lo = bf16_bits(r1 - __uint_as_float(mid << 16));
+          pw[0][i >> 1] |= hi << (16 * (i & 1));
+          pw[1][i >> 1] |= mid << (16 * (i & 1));
+          pw[2][i >> 1] |= lo << (16 * (i & 1));
+          lsum += p;
+        }
+      }
       bf16x8 pa[3];
 #pragma unroll
-      for (int k = 0; k < 3; ++k)
-        pa[k] = hl < G ? *reinterpret_cast<const bf16x8*>(&pt[k][hl < G ? hl : 0][rb]) : as_bf16x8(make_uint4(0, 0, 0, 0));
+      for (int k = 0; k < 3; ++k) pa[k] = as_bf16x8(make_uint4(pw[k][0], pw[k][1], pw[k][2], pw[k][3]));
       uint32_t vh[8][4];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -731,6 +745,13 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
         for (int k = 0; k < 3; ++k) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[k], vb, acc[j], 0, 0, 0);
       }
     }
+    // the wave's sum of p per head: the four lanes of head hl, in a fixed order
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (kq == 0 && hl < G) redL[wave][hl] = lsum;
+    // every wave's reads of the logits are done before osum, which may share
+    // their space, is written
+    if constexpr (OSUM_IN_ZS) __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * kq + i;
@@ -797,7 +818,12 @@ void k_attn_chunk(const AttnArgs a, const StepArgs n) {
   }
   if (tid < 2 * G) {
     const int g = tid >> 1;
-    const float v = (tid & 1) ? ((red[0][g] + red[1][g]) + red[2][g]) + red[3][g] : mc[g];
+    float v = mc[g];
+    if constexpr (MK) {
+      if (tid & 1) v = ((redL[0][g] + redL[1][g]) + redL[2][g]) + redL[3][g];
+    } else {
+      if (tid & 1) v = ((red[0][g] + red[1][g]) + red[2][g]) + red[3][g];
+    }
     store_through(a.part_ml + ((hbase + g) * a.max_chunks + c) * 2 + (tid & 1), v);
   }
   if constexpr (MK && DEF) {
@@ -1038,6 +1064,9 @@ const void* attn_fn(int chunk) {
     case 128: return (const void*)&k_attn_chunk<T, D, G, 128, MK, QT, DEF, XT>;
     case 256: return (const void*)&k_attn_chunk<T, D, G, 256, MK, QT, DEF, XT>;
     case 512: return (const void*)&k_attn_chunk<T, D, G, 512, MK, QT, DEF, XT>;
+    case 1024:  // the matrix-core path only
+      if constexpr (MK) return (const void*)&k_attn_chunk<T, D, G, 1024, MK, QT, DEF, XT>;
+      return nullptr;
     default: return nullptr;
   }
 }

@@ -84,8 +84,11 @@ typedef struct {
                              from pinned host memory into slot (layer mod S), ahead of the
                              attention that reads it (S - 1 layers ahead at most; with an
                              even S >= 4, S/2 consecutive layers per copy). */
-  int32_t chunk;          /* split-K rows per work-group: 128, 256 or 512; 0 = 512 when
-                             q_heads >= 4 * kv_heads, else 256 */
+  int32_t chunk;          /* split-K rows per work-group: 128, 256, 512 or 1024 (1024 on
+                             the matrix-core path only: bf16 with 1 or >= 4 query heads
+                             per kv head, no TKV_FLAG_VECTOR_PASS; TKV_EINVAL otherwise);
+                             0 = 1024 for bf16 with q_heads >= 4 * kv_heads (512 with
+                             TKV_FLAG_VECTOR_PASS or fp32), else 256 */
   uint64_t flags;         /* TKV_FLAG_* */
   int64_t mem_cap_bytes;  /* most device + pinned host bytes the handle may hold (pools,
                              arenas, scratch, the buffers a reassignment grows); an

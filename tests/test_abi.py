@@ -62,6 +62,24 @@ def test_create_rejects_bad_policy(tkv, kw):
     assert tkv.lib().tkv_last_error(None)
 
 
+@pytest.mark.parametrize("case", ["f32_g4", "bf16_g2", "bf16_g4_vector_pass"])
+def test_chunk_1024_needs_the_matrix_cores(tkv, case):
+    """1024-row chunks exist on the matrix-core path only (bf16, one or 4 and
+    more query heads per kv head, no vector pass); elsewhere TKV_EINVAL."""
+    args = dict(layers=2, q_heads=16, kv_heads=4, head_dim=64, batch=1, max_tokens=64, dtype=tkv.TKV_BF16,
+                delta=16, hbm_ratio=0.5, evict_ratio=0.1, prompt=4, sinks=4, recent=8, chunk=1024)
+    if case == "f32_g4":
+        args["dtype"] = tkv.TKV_F32
+    elif case == "bf16_g2":
+        args["q_heads"] = 8
+    else:
+        args["flags"] = tkv.TKV_FLAG_VECTOR_PASS
+    with pytest.raises(tkv.TkvError) as e:
+        tkv.tkv_create(**args)
+    assert e.value.code == tkv.TKV_EINVAL
+    assert b"1024" in tkv.lib().tkv_last_error(None)
+
+
 def test_null_handle_calls_fail_cleanly(tkv):
     lib = tkv.lib()
     assert lib.tkv_destroy(None) == tkv.TKV_OK
